@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the KDA training path.
+
+This module draws random numbers and rounds them to the storage dtypes; it
+holds none of the method's arithmetic. Both the GPU path's tests/bench and
+the oracle consume the arrays it returns, so the two sides always see the
+same bits.
+
+Workloads. The deterministic KDA package's timing rows (flashinfer PR #8909,
+timing tables and their row-key paragraph) are named 1doc (one 16384-token
+document, 64 heads), 4doc (8192/4096/3072/1024 tokens, 64 heads), R2 (16384
+tokens in 3 unequal documents, 4 heads) and m2 (2048/1500 tokens, 4 heads),
+with bf16 q/k/v/beta, an fp32 gate and head dim 128. The pages give no value
+distributions; the ones below are the recipe this repository fixes:
+
+* q, k, v, dO: standard normal, drawn as float32, rounded to bf16 (RNE).
+  With the L2 norm off, q and k are first normalised per (token, head) in
+  float32, then rounded once to bf16 (so they are only nearly unit-norm).
+  With the fused L2 norm, q and k are raw N(0,1) values.
+* beta: sigmoid of a standard normal, rounded to bf16.
+* gate form g: logsigmoid(x)/16 of a standard normal x, in float64, stored
+  as float32.
+* gate form raw: a = bf16(N(0,1)); A_log ~ U(lo, hi) float32 per head;
+  dt_bias ~ N(0, 0.5) float32 per (head, channel), 0.5 being the std.
+* draw order from numpy.random.default_rng(seed): q, k, v, beta-x, gate-x,
+  dO, then A_log and dt_bias for the raw form.
+
+bf16 values are returned as uint16 bit patterns (numpy has no bf16 dtype);
+``bf16_to_f32`` widens them exactly.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+HEAD_DIM = 128
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 with round-to-nearest-even; returns uint16 bits."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    b = x.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    rounded = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    if nan.any():
+        out = np.where(nan, np.uint16(0x7FC0), out)
+    return out
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 exactly."""
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    doc_lens: tuple
+    H: int
+    gate: str                 # "g" or "raw"
+    l2norm: bool              # fused in-kernel L2 norm on raw q, k
+    alog_range: tuple = (0.0, float(np.log(16.0)))
+    seed: int = 0
+    backward: tuple = ("saved",)
+    D: int = HEAD_DIM
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.doc_lens))
+
+    @property
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.doc_lens)]).astype(np.int32)
+
+    @property
+    def key(self) -> str:
+        return f"{self.name}:{self.gate}:{'fused' if self.l2norm else 'off'}"
+
+
+# The five workloads, in order: tiny, m2, R2, 1doc, 4doc fast-decay.
+WORKLOADS = [
+    Workload("tiny", (200, 56), 2, "g", False, seed=0),
+    Workload("m2", (2048, 1500), 4, "g", False, seed=1),
+    Workload("R2", (9001, 5120, 2263), 4, "raw", False, (0.0, float(np.log(16.0))), seed=2),
+    Workload("1doc", (16384,), 64, "g", True, seed=3),
+    Workload("4doc", (8192, 4096, 3072, 1024), 64, "raw", False,
+             (float(np.log(4.0)), float(np.log(32.0))), seed=4, backward=("saved", "replay")),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def _normalise_rows(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / n).astype(np.float32)
+
+
+def make_inputs(w: Workload, seed: int | None = None) -> dict:
+    """Draw the inputs of workload ``w``. Returns numpy arrays:
+    q, k, v, beta, dO (uint16 bf16 bits), gate (float32 g, or uint16 bf16 a),
+    A_log, dt_bias (float32, raw form only), cu_seqlens (int32)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    T, H, D = w.T, w.H, w.D
+    q = rng.standard_normal((T, H, D), dtype=np.float32)
+    k = rng.standard_normal((T, H, D), dtype=np.float32)
+    v = rng.standard_normal((T, H, D), dtype=np.float32)
+    bx = rng.standard_normal((T, H), dtype=np.float32)
+    gx = rng.standard_normal((T, H, D), dtype=np.float32)
+    dO = rng.standard_normal((T, H, D), dtype=np.float32)
+    if not w.l2norm:
+        q = _normalise_rows(q)
+        k = _normalise_rows(k)
+    out = {
+        "cu_seqlens": w.cu_seqlens,
+        "q": f32_to_bf16(q),
+        "k": f32_to_bf16(k),
+        "v": f32_to_bf16(v),
+        "beta": f32_to_bf16((1.0 / (1.0 + np.exp(-bx.astype(np.float64)))).astype(np.float32)),
+        "dO": f32_to_bf16(dO),
+    }
+    if w.gate == "g":
+        x = gx.astype(np.float64)
+        logsig = np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+        out["gate"] = (logsig / 16.0).astype(np.float32)
+    else:
+        out["gate"] = f32_to_bf16(gx)
+        lo, hi = w.alog_range
+        out["A_log"] = rng.uniform(lo, hi, H).astype(np.float32)
+        out["dt_bias"] = rng.normal(0.0, 0.5, (H, D)).astype(np.float32)
+    return out
+
+
+def custom(doc_lens, H, gate="g", l2norm=False, alog_range=(0.0, float(np.log(16.0))),
+           seed=0, D=HEAD_DIM, name="custom") -> Workload:
+    """A workload of arbitrary document lengths with the same distributions."""
+    return Workload(name, tuple(int(x) for x in doc_lens), int(H), gate, bool(l2norm),
+                    tuple(alog_range), int(seed), D=int(D))
+
+
+def as_f64(inp: dict) -> dict:
+    """Exact float64 copies of every floating input (for the oracle)."""
+    out = {}
+    for key in ("q", "k", "v", "beta", "dO"):
+        out[key] = bf16_to_f32(inp[key]).astype(np.float64)
+    g = inp["gate"]
+    out["gate"] = (bf16_to_f32(g) if g.dtype == np.uint16 else g).astype(np.float64)
+    for key in ("A_log", "dt_bias"):
+        if key in inp:
+            out[key] = inp[key].astype(np.float64)
+    out["cu_seqlens"] = inp["cu_seqlens"].astype(np.int64)
+    return out
