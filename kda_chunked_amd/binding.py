@@ -1,0 +1,179 @@
+"""Python binding of libkda.so (see include/kda.h for the contract).
+
+Argument marshalling only: every step of the KDA path runs in the library's
+HIP kernels. torch supplies device memory and the current stream. There is
+no CPU fallback: if the library is missing, loading fails with an error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_GATE_G = 0
+KDA_GATE_RAW = 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
+          4: "device error"}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class kda_problem(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("H", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("dk", ctypes.c_int32),
+        ("dv", ctypes.c_int32),
+        ("gate", ctypes.c_int32),
+        ("l2norm", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("l2_eps", ctypes.c_float),
+    ]
+
+
+_lib = None
+EXPORTS = ("kda_saved_bytes", "kda_workspace_bytes", "kda_fwd", "kda_bwd",
+           "kda_status_string", "kda_last_error", "kda_abi_version")
+
+
+def lib():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m kda_chunked_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        pp = ctypes.POINTER(kda_problem)
+        L.kda_saved_bytes.argtypes = [pp]
+        L.kda_saved_bytes.restype = sz
+        L.kda_workspace_bytes.argtypes = [pp, ctypes.c_int, ctypes.c_int]
+        L.kda_workspace_bytes.restype = sz
+        L.kda_fwd.argtypes = [pp] + [vp] * 10 + [vp, sz, vp]
+        L.kda_fwd.restype = ctypes.c_int
+        L.kda_bwd.argtypes = [pp] + [vp] * 16 + [vp, sz, vp]
+        L.kda_bwd.restype = ctypes.c_int
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_last_error.argtypes = []
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_abi_version.argtypes = []
+        L.kda_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def problem(T, H, num_seqs, gate="g", l2norm=False, scale=None, l2_eps=1e-6, dk=128, dv=128):
+    if gate not in ("g", "raw"):
+        raise ValueError(f"gate must be 'g' or 'raw', got {gate!r}")
+    if scale is None:
+        scale = dk ** -0.5
+    return kda_problem(int(T), int(H), int(num_seqs), int(dk), int(dv),
+                       KDA_GATE_RAW if gate == "raw" else KDA_GATE_G, int(bool(l2norm)),
+                       float(scale), float(l2_eps))
+
+
+def saved_bytes(p: kda_problem) -> int:
+    return int(lib().kda_saved_bytes(ctypes.byref(p)))
+
+
+def workspace_bytes(p: kda_problem, backward: bool, replay: bool = False) -> int:
+    return int(lib().kda_workspace_bytes(ctypes.byref(p), int(bool(backward)), int(bool(replay))))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _check(rc):
+    if rc != 0:
+        raise KdaError(rc, lib().kda_last_error().decode())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t):
+    return t.device if t.is_cuda else None
+
+
+def kda_fwd(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, o, saved, workspace):
+    """Enqueue the forward on the current stream of q's device (made current)."""
+    dev = _dev(q)
+    with torch.cuda.device(dev):
+        rc = lib().kda_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g_or_a),
+                           _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(o), _ptr(saved),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(dev))
+    _check(rc)
+
+
+def kda_bwd(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, dO, saved, dq, dk, dv,
+            dbeta, dg_or_da, dA_log, ddt_bias, workspace):
+    """Enqueue the backward on the current stream of q's device (made current).
+    saved=None selects the replay backward."""
+    dev = _dev(q)
+    with torch.cuda.device(dev):
+        rc = lib().kda_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                           _ptr(g_or_a), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(dO),
+                           _ptr(saved), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta),
+                           _ptr(dg_or_da), _ptr(dA_log), _ptr(ddt_bias), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+
+
+class KDA:
+    """Holds the buffers of one problem shape and runs forward / backward.
+
+    Inputs are torch tensors on one GPU: q, k, v [T,H,128] bf16; beta [T,H]
+    bf16; gate g [T,H,128] fp32 or a [T,H,128] bf16 with A_log [H] and
+    dt_bias [H,128] fp32; cu_seqlens [N+1] int32."""
+
+    def __init__(self, T, H, num_seqs, gate="g", l2norm=False, scale=None, l2_eps=1e-6,
+                 device="cuda"):
+        self.p = problem(T, H, num_seqs, gate, l2norm, scale, l2_eps)
+        self.gate = gate
+        self.device = torch.device(device)
+        nbytes = max(workspace_bytes(self.p, False), workspace_bytes(self.p, True, True))
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(max(nbytes, 1), **u8)
+        self.saved = torch.empty(max(saved_bytes(self.p), 1), **u8)
+
+    def forward(self, q, k, v, beta, gate, cu_seqlens, A_log=None, dt_bias=None, save=True,
+                o=None):
+        if o is None:
+            o = torch.empty_like(v)
+        kda_fwd(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, o,
+                self.saved if save else None, self.workspace)
+        return o
+
+    def backward(self, q, k, v, beta, gate, cu_seqlens, dO, A_log=None, dt_bias=None,
+                 replay=False, out=None):
+        if out is None:
+            out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                       dbeta=torch.empty_like(beta), dgate=torch.empty_like(gate))
+            if self.gate == "raw":
+                out["dA_log"] = torch.empty_like(A_log)
+                out["ddt_bias"] = torch.empty_like(dt_bias)
+        kda_bwd(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, dO,
+                None if replay else self.saved, out["dq"], out["dk"], out["dv"], out["dbeta"],
+                out["dgate"], out.get("dA_log"), out.get("ddt_bias"), self.workspace)
+        return out

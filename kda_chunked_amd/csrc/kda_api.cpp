@@ -1,0 +1,306 @@
+// Host side of the C ABI declared in include/kda.h: argument validation,
+// buffer sizing, workspace carving and the stream-ordered launch sequence.
+// Nothing here reads device memory or synchronises with the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+// Message of the calling thread's last failed call (plain storage: no
+// dynamic initialisation or destructor in the thread-local block).
+thread_local char g_last_error[512];
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carving of a byte buffer into aligned regions.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct Sizes {
+  int64_t T, H, N, NC;
+};
+
+Sizes sizes_of(const kda_problem* p) {
+  Sizes s;
+  s.T = p->T;
+  s.H = p->H;
+  s.N = p->num_seqs;
+  s.NC = p->T / 64 + p->num_seqs;
+  return s;
+}
+
+kda::ChunkTable carve_table(Carver& c, const Sizes& s) {
+  kda::ChunkTable ct;
+  ct.doc_c0 = c.take<int32_t>(s.N + 1);
+  ct.tok = c.take<int32_t>(s.NC);
+  ct.len = c.take<int32_t>(s.NC);
+  return ct;
+}
+
+// with_states = 0 leaves out S_in and R (a forward that saves nothing).
+kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states, float** G) {
+  kda::SavedSet sv{};
+  const size_t mat = (size_t)s.NC * s.H * 64 * 64;
+  sv.Tm = c.take<float>(mat);
+  sv.Aqk = c.take<float>(mat);
+  sv.Akk = c.take<float>(mat);
+  sv.rq = c.take<float>((size_t)s.T * s.H);
+  sv.rk = c.take<float>((size_t)s.T * s.H);
+  *G = c.take<float>((size_t)s.T * s.H * 128);
+  if (with_states) {
+    sv.S_in = c.take<float>((size_t)s.NC * s.H * 128 * 128);
+    sv.R = c.take<float>((size_t)s.T * s.H * 128);
+  }
+  return sv;
+}
+
+kda::BwdWork carve_bwd(Carver& c, const Sizes& s) {
+  kda::BwdWork bw;
+  bw.dS = c.take<float>((size_t)s.NC * s.H * 128 * 128);
+  bw.dU = c.take<float>((size_t)s.T * s.H * 128);
+  bw.part_A = c.take<float>((size_t)s.NC * s.H);
+  bw.part_dt = c.take<float>((size_t)s.NC * s.H * 128);
+  return bw;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+kda_status check_problem(const kda_problem* p) {
+  if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "T = %lld is negative", (long long)p->T);
+  if (p->T > (int64_t)1 << 30)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "T = %lld exceeds 2^30 tokens", (long long)p->T);
+  if (p->H < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "H = %d: need at least one head", p->H);
+  if (p->num_seqs < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = %d: need at least one document",
+                p->num_seqs);
+  if (p->num_seqs > (1 << 24))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = %d is too large", p->num_seqs);
+  if (p->dk != 128 || p->dv != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "dk = %d, dv = %d: this build serves 128, 128", p->dk,
+                p->dv);
+  if (p->gate != KDA_GATE_G && p->gate != KDA_GATE_RAW)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "unknown gate form %d", p->gate);
+  if (p->l2norm != 0 && p->l2norm != 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "l2norm must be 0 or 1, got %d", p->l2norm);
+  if (!std::isfinite(p->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!std::isfinite(p->l2_eps) || p->l2_eps < 0.f)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "l2_eps must be finite and >= 0");
+  return KDA_OK;
+}
+
+#define REQUIRE_PTR(ptr, name)                                                         \
+  do {                                                                                 \
+    if (!(ptr)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", name);             \
+    if (!aligned(ptr)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+kda::Dims dims_of(const kda_problem* p) {
+  kda::Dims d;
+  d.T = p->T;
+  d.H = p->H;
+  d.N = p->num_seqs;
+  d.NC = (int)(p->T / 64 + p->num_seqs);
+  d.raw = p->gate == KDA_GATE_RAW;
+  d.l2norm = p->l2norm;
+  d.scale = p->scale;
+  d.l2_eps = p->l2_eps;
+  return d;
+}
+
+size_t fwd_ws_bytes(const Sizes& s) {
+  Carver c(nullptr);
+  carve_table(c, s);
+  float* G;
+  carve_saved(c, s, 0, &G);
+  return c.off;
+}
+
+size_t bwd_ws_bytes(const Sizes& s, int replay) {
+  Carver c(nullptr);
+  carve_table(c, s);
+  carve_bwd(c, s);
+  if (replay) {
+    float* G;
+    carve_saved(c, s, 1, &G);
+  }
+  return c.off;
+}
+
+#define LAUNCH(call)                                                                    \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(KDA_ERR_DEVICE, "%s failed: %s", #call, hipGetErrorString(e_));       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_saved_bytes(const kda_problem* p) {
+  if (check_problem(p) != KDA_OK) return 0;
+  Carver c(nullptr);
+  float* G;
+  carve_saved(c, sizes_of(p), 1, &G);
+  return c.off;
+}
+
+size_t kda_workspace_bytes(const kda_problem* p, int backward, int replay) {
+  if (check_problem(p) != KDA_OK) return 0;
+  const Sizes s = sizes_of(p);
+  return backward ? bwd_ws_bytes(s, replay) : fwd_ws_bytes(s);
+}
+
+kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                   const void* beta, const void* g_or_a, const float* A_log,
+                   const float* dt_bias, const int32_t* cu_seqlens, void* o, void* saved,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  kda_status st = check_problem(p);
+  if (st != KDA_OK) return st;
+  if (p->T == 0) return KDA_OK;
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(beta, "beta");
+  REQUIRE_PTR(g_or_a, "g_or_a");
+  REQUIRE_PTR(cu_seqlens, "cu_seqlens");
+  REQUIRE_PTR(o, "o");
+  if (p->gate == KDA_GATE_RAW) {
+    REQUIRE_PTR(A_log, "A_log");
+    REQUIRE_PTR(dt_bias, "dt_bias");
+  }
+  if (saved && !aligned(saved)) return fail(KDA_ERR_INVALID_ARGUMENT, "saved is not 16-byte aligned");
+  REQUIRE_PTR(workspace, "workspace");
+  const Sizes s = sizes_of(p);
+  const size_t need = fwd_ws_bytes(s);
+  if (workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+                workspace_bytes, need);
+
+  const kda::Dims d = dims_of(p);
+  const kda::Inputs in{q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens};
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carver wc(workspace);
+  const kda::ChunkTable ct = carve_table(wc, s);
+  float* G = nullptr;
+  kda::SavedSet sv;
+  if (saved) {
+    Carver sc(saved);
+    sv = carve_saved(sc, s, 1, &G);
+  } else {
+    sv = carve_saved(wc, s, 0, &G);
+  }
+  LAUNCH(kda::launch_chunk_map(d, cu_seqlens, ct, hs));
+  LAUNCH(kda::launch_fwd_prep(d, in, ct, G, sv, hs));
+  LAUNCH(kda::launch_fwd_scan(d, in, ct, G, sv, o, saved != nullptr, hs));
+  return KDA_OK;
+}
+
+kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                   const void* beta, const void* g_or_a, const float* A_log,
+                   const float* dt_bias, const int32_t* cu_seqlens, const void* dO,
+                   const void* saved, void* dq, void* dk, void* dv, void* dbeta,
+                   void* dg_or_da, float* dA_log, float* ddt_bias, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  kda_status st = check_problem(p);
+  if (st != KDA_OK) return st;
+  if (p->T == 0) {
+    // no tokens: the parameter gradients are zero sums; leave them to the caller
+    return KDA_OK;
+  }
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(beta, "beta");
+  REQUIRE_PTR(g_or_a, "g_or_a");
+  REQUIRE_PTR(cu_seqlens, "cu_seqlens");
+  REQUIRE_PTR(dO, "dO");
+  REQUIRE_PTR(dq, "dq");
+  REQUIRE_PTR(dk, "dk");
+  REQUIRE_PTR(dv, "dv");
+  REQUIRE_PTR(dbeta, "dbeta");
+  REQUIRE_PTR(dg_or_da, "dg_or_da");
+  if (p->gate == KDA_GATE_RAW) {
+    REQUIRE_PTR(A_log, "A_log");
+    REQUIRE_PTR(dt_bias, "dt_bias");
+    REQUIRE_PTR(dA_log, "dA_log");
+    REQUIRE_PTR(ddt_bias, "ddt_bias");
+  }
+  if (saved && !aligned(saved)) return fail(KDA_ERR_INVALID_ARGUMENT, "saved is not 16-byte aligned");
+  REQUIRE_PTR(workspace, "workspace");
+  const Sizes s = sizes_of(p);
+  const int replay = saved == nullptr;
+  const size_t need = bwd_ws_bytes(s, replay);
+  if (workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+                workspace_bytes, need);
+
+  const kda::Dims d = dims_of(p);
+  const kda::Inputs in{q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens};
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carver wc(workspace);
+  const kda::ChunkTable ct = carve_table(wc, s);
+  const kda::BwdWork bw = carve_bwd(wc, s);
+  float* G = nullptr;
+  kda::SavedSet sv;
+  if (replay) {
+    sv = carve_saved(wc, s, 1, &G);
+  } else {
+    Carver sc(const_cast<void*>(saved));
+    sv = carve_saved(sc, s, 1, &G);
+  }
+  const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
+  LAUNCH(kda::launch_chunk_map(d, cu_seqlens, ct, hs));
+  if (replay) {
+    LAUNCH(kda::launch_fwd_prep(d, in, ct, G, sv, hs));
+    LAUNCH(kda::launch_fwd_scan(d, in, ct, G, sv, nullptr, 1, hs));
+  }
+  LAUNCH(kda::launch_bwd_scan(d, in, ct, G, sv, dO, dv, bw, hs));
+  LAUNCH(kda::launch_bwd_intra(d, in, ct, G, sv, dO, out, bw, hs));
+  if (p->gate == KDA_GATE_RAW) LAUNCH(kda::launch_finalize(d, ct, out, bw, hs));
+  return KDA_OK;
+}
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KDA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Device-side building blocks shared by the gfx950 KDA kernels.
+//
+// Matrix products run on the CDNA4 MFMA unit as v_mfma_f32_16x16x32_bf16
+// (16x16 output tile, K step 32, fp32 accumulation). Operands that are not
+// exact bf16 inputs are carried as an fp32 value split into two bf16 parts
+// x = hi + lo (hi = RNE(x), lo = RNE(x - hi)); a product of two split operands
+// is hi*hi + hi*lo + lo*hi (the BF16x3 split product named on flashinfer
+// PR #7176, opening section), which keeps fp32-grade accuracy on bf16 MFMA.
+//
+// Lane layout of v_mfma_f32_16x16x32_bf16 (wave64, lane l):
+//   A (16 x 32): lane l holds A[l % 16][8 * (l / 16) + 0..7]
+//   B (32 x 16): lane l holds B[8 * (l / 16) + 0..7][l % 16]
+//   D (16 x 16): lane l holds D[4 * (l / 16) + 0..3][l % 16]
+// Operands are staged in LDS "panels": row-major bf16 tiles whose rows run
+// along the product's K dimension (so one 16-byte read fills a fragment);
+// a B operand is stored as its transpose (rows = N).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CL = 64;    // chunk length (tokens)
+constexpr int HD = 128;   // head dimension (dk = dv)
+constexpr float LOG2E = 1.4426950408889634f;
+
+#define KDA_DEV __device__ __forceinline__
+
+KDA_DEV int lane_id() { return threadIdx.x & 63; }
+KDA_DEV int wave_id() { return threadIdx.x >> 6; }
+
+KDA_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+KDA_DEV f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+KDA_DEV float bf2f(bf16 x) { return (float)x; }
+KDA_DEV bf16 f2bf(float x) { return (bf16)x; }  // round to nearest even
+
+// exp(x) through the hardware base-2 exponential.
+KDA_DEV float fexp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+
+// An LDS operand panel: hi and lo bf16 planes, `ld` elements per row.
+struct Panel {
+  bf16* hi;
+  bf16* lo;
+  int ld;
+};
+
+// Which operands of a product carry their lo part.
+enum : int { SPLIT_NONE = 0, SPLIT_A = 1, SPLIT_B = 2, SPLIT_AB = 3 };
+
+KDA_DEV bf16x8 frag(const bf16* p, int ld, int row0, int k) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(p + (row0 + (l & 15)) * ld + k + ((l >> 4) << 3));
+}
+
+// acc += A[m0:m0+16, k0:k1] * B[n0:n0+16, k0:k1]^T  (both panels K-contiguous).
+// Terms are added small-first: lo*hi, hi*lo, then hi*hi.
+template <int SPLIT>
+KDA_DEV void mma(f32x4& acc, const Panel& A, int m0, const Panel& B, int n0, int k0, int k1) {
+  for (int k = k0; k < k1; k += 32) {
+    const bf16x8 ah = frag(A.hi, A.ld, m0, k);
+    const bf16x8 bh = frag(B.hi, B.ld, n0, k);
+    if (SPLIT & SPLIT_A) acc = mfma16(frag(A.lo, A.ld, m0, k), bh, acc);
+    if (SPLIT & SPLIT_B) acc = mfma16(ah, frag(B.lo, B.ld, n0, k), acc);
+    acc = mfma16(ah, bh, acc);
+  }
+}
+
+template <int SPLIT, int KLEN>
+KDA_DEV void mma_k(f32x4& acc, const Panel& A, int m0, const Panel& B, int n0) {
+#pragma unroll
+  for (int k = 0; k < KLEN; k += 32) {
+    const bf16x8 ah = frag(A.hi, A.ld, m0, k);
+    const bf16x8 bh = frag(B.hi, B.ld, n0, k);
+    if (SPLIT & SPLIT_A) acc = mfma16(frag(A.lo, A.ld, m0, k), bh, acc);
+    if (SPLIT & SPLIT_B) acc = mfma16(ah, frag(B.lo, B.ld, n0, k), acc);
+    acc = mfma16(ah, bh, acc);
+  }
+}
+
+// Split-store one fp32 value into a panel.
+KDA_DEV void put(const Panel& P, int row, int col, float x) {
+  const bf16 h = f2bf(x);
+  P.hi[row * P.ld + col] = h;
+  if (P.lo) P.lo[row * P.ld + col] = f2bf(x - bf2f(h));
+}
+
+// Split-store 8 consecutive fp32 values (16-byte aligned destination).
+KDA_DEV void put8(const Panel& P, int row, int col, const float* x) {
+  bf16x8 h, w;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = f2bf(x[i]);
+    w[i] = f2bf(x[i] - bf2f(h[i]));
+  }
+  *reinterpret_cast<bf16x8*>(P.hi + row * P.ld + col) = h;
+  if (P.lo) *reinterpret_cast<bf16x8*>(P.lo + row * P.ld + col) = w;
+}
+
+// D tile at (m0, n0) -> panel laid out [n][m] (the tile's rows become the
+// panel's contiguous K axis): one 8-byte write per plane and lane.
+KDA_DEV void store_tile_t(const f32x4& acc, const Panel& P, int m0, int n0) {
+  const int l = lane_id();
+  bf16x4 h, w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = f2bf(acc[i]);
+    w[i] = f2bf(acc[i] - bf2f(h[i]));
+  }
+  const int off = (n0 + (l & 15)) * P.ld + m0 + 4 * (l >> 4);
+  *reinterpret_cast<bf16x4*>(P.hi + off) = h;
+  if (P.lo) *reinterpret_cast<bf16x4*>(P.lo + off) = w;
+}
+
+// D tile at (m0, n0) -> panel laid out [m][n].
+KDA_DEV void store_tile_n(const f32x4& acc, const Panel& P, int m0, int n0) {
+  const int l = lane_id();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) put(P, m0 + 4 * (l >> 4) + i, n0 + (l & 15), acc[i]);
+}
+
+// Row / column of element i (0..3) of this lane's D tile.
+KDA_DEV int drow(int i) { return 4 * (lane_id() >> 4) + i; }
+KDA_DEV int dcol() { return lane_id() & 15; }
+
+// softplus(x) = log(1 + e^x), stable for large |x|.
+KDA_DEV float softplus(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
+KDA_DEV float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// The per-token log forget gate g for (token t, head h, channel c).
+KDA_DEV float gate_value(const void* gate, int raw, const float* A_log, const float* dt_bias,
+                         int64_t t, int h, int H, int c) {
+  const int64_t idx = (t * H + h) * HD + c;
+  if (!raw) return reinterpret_cast<const float*>(gate)[idx];
+  const float a = bf2f(reinterpret_cast<const bf16*>(gate)[idx]);
+  return -__expf(A_log[h]) * softplus(a + dt_bias[h * HD + c]);
+}
+
+}  // namespace kda

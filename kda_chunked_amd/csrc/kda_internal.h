@@ -1,0 +1,88 @@
+// Internal interface between the host API (kda_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Device-side chunk table built from cu_seqlens by the chunk-map kernel.
+// Chunks are 64 tokens long and restart at every document start; chunk ids
+// are assigned in document order. n_chunks_max = floor(T/64) + num_seqs is an
+// upper bound on the number of chunks that the host can compute without
+// reading cu_seqlens.
+struct ChunkTable {
+  int32_t* doc_c0;   // [N+1]: chunks of document d are [doc_c0[d], doc_c0[d+1])
+  int32_t* tok;      // [n_chunks_max]: first token of the chunk
+  int32_t* len;      // [n_chunks_max]: tokens in the chunk (1..64)
+};
+
+// Per-chunk matrices and states (the saved forward set), all fp32. The gate
+// cumsum G [T, H, 128] is carved right after rk.
+struct SavedSet {
+  float* S_in;   // [NC, H, 128, 128] state before each chunk
+  float* Tm;     // [NC, H, 64, 64]  (I + Diag(beta) A_kk)^-1, zero above the diagonal
+  float* Aqk;    // [NC, H, 64, 64]  decayed q.k products, zero above the diagonal
+  float* Akk;    // [NC, H, 64, 64]  decayed k.k products, zero on and above the diagonal
+  float* R;      // [T, H, 128]      V - (K*e^G) S_in, per token
+  float* rq;     // [T, H]           L2 scalars (1 without the fused norm)
+  float* rk;     // [T, H]
+};
+
+struct Dims {
+  int64_t T;
+  int H;
+  int N;        // documents
+  int NC;       // n_chunks_max
+  int raw;      // gate form raw
+  int l2norm;
+  float scale;
+  float l2_eps;
+};
+
+struct Inputs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* gate;   // g (fp32) or a (bf16)
+  const float* A_log;
+  const float* dt_bias;
+  const int32_t* cu;
+};
+
+struct BwdOut {
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dbeta;
+  void* dgate;        // dg (fp32) or da (bf16)
+  float* dA_log;
+  float* ddt_bias;
+};
+
+struct BwdWork {
+  float* dS;          // [NC, H, 128, 128] gradient w.r.t. the state after each chunk
+  float* dU;          // [T, H, 128] gradient w.r.t. U~ (the chunk's transformed values)
+  float* part_A;      // [NC, H]      raw form: per-chunk sum of dg*g
+  float* part_dt;     // [NC, H, 128] raw form: per-chunk sum of dz
+};
+
+hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
+                            hipStream_t s);
+hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
+                           const SavedSet& sv, hipStream_t s);
+hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
+                           const float* G, const SavedSet& sv, void* o, int save_states,
+                           hipStream_t s);
+hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
+                           const float* G, const SavedSet& sv, const void* dO, void* dv,
+                           const BwdWork& bw, hipStream_t s);
+hipError_t launch_bwd_intra(const Dims& d, const Inputs& in, const ChunkTable& ct,
+                            const float* G, const SavedSet& sv, const void* dO,
+                            const BwdOut& out, const BwdWork& bw, hipStream_t s);
+hipError_t launch_finalize(const Dims& d, const ChunkTable& ct, const BwdOut& out,
+                           const BwdWork& bw, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,116 @@
+"""The C-ABI library: it loads, exports every symbol include/kda.h declares,
+and validates arguments on the host before touching the device (no GPU needed)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kda_chunked_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(kda_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert header_symbols() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_header_symbol():
+    lib = B.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b(kda_[a-z_]+)$", out, flags=re.M))
+    for sym in header_symbols():
+        assert sym in exported, sym
+        assert getattr(lib, sym) is not None
+    assert lib.kda_abi_version() == 1
+
+
+def test_library_is_built_for_gfx950_only(tmp_path):
+    fatbin = tmp_path / "fatbin.bin"
+    # objcopy with one file argument rewrites that file: always name the output
+    r = subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", B.LIB_PATH,
+                        str(fatbin)], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("objcopy cannot extract the device code section here")
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          f"--input={fatbin}"], capture_output=True, text=True, check=True)
+    targets = [t for t in out.stdout.split() if "amdgcn" in t]
+    assert targets and all("gfx950" in t for t in targets)
+
+
+def _p(**kw):
+    base = dict(T=1000, H=4, num_seqs=2, gate="g", l2norm=False)
+    base.update(kw)
+    return B.problem(**base)
+
+
+def test_sizes():
+    p = _p()
+    nc = 1000 // 64 + 2
+    s = B.saved_bytes(p)
+    assert s >= nc * 4 * 128 * 128 * 4 + 3 * nc * 4 * 64 * 64 * 4
+    assert B.workspace_bytes(p, True, True) > B.workspace_bytes(p, True, False)
+    assert B.workspace_bytes(p, False) > 0
+    # invalid problems size to zero
+    assert B.saved_bytes(_p(H=0)) == 0
+    assert B.workspace_bytes(_p(dk=64), False) == 0
+
+
+def _fwd_status(p, **ptrs):
+    lib = B.lib()
+    args = dict(q=16, k=16, v=16, beta=16, g=16, A_log=None, dt_bias=None, cu=16, o=16,
+                saved=None, ws=16, ws_bytes=1 << 40)
+    args.update(ptrs)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    rc = lib.kda_fwd(ctypes.byref(p), vp(args["q"]), vp(args["k"]), vp(args["v"]),
+                     vp(args["beta"]), vp(args["g"]), vp(args["A_log"]), vp(args["dt_bias"]),
+                     vp(args["cu"]), vp(args["o"]), vp(args["saved"]), vp(args["ws"]),
+                     args["ws_bytes"], None)
+    return rc, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H=0), 1, "head"),
+    (dict(num_seqs=0), 1, "document"),
+    (dict(T=-1), 1, "negative"),
+    (dict(dk=64), 2, "128"),
+    (dict(dv=256), 2, "128"),
+])
+def test_invalid_problem_rejected_before_launch(kw, status, msg):
+    rc, err = _fwd_status(_p(**kw))
+    assert rc == status and msg in err
+
+
+def test_null_and_misaligned_pointers_rejected():
+    rc, err = _fwd_status(_p(), q=None)
+    assert rc == 1 and "q is NULL" in err
+    rc, err = _fwd_status(_p(), k=18)
+    assert rc == 1 and "aligned" in err
+    rc, err = _fwd_status(_p(gate="raw"))
+    assert rc == 1 and "A_log" in err
+
+
+def test_small_workspace_rejected():
+    rc, err = _fwd_status(_p(), ws_bytes=100)
+    assert rc == 3 and "workspace" in err
+
+
+def test_zero_tokens_is_a_no_op():
+    rc, _ = _fwd_status(_p(T=0), q=None, k=None, v=None)
+    assert rc == 0
+
+
+def test_status_strings():
+    lib = B.lib()
+    lib.kda_status_string.restype = ctypes.c_char_p
+    assert lib.kda_status_string(0) == b"ok"
+    assert lib.kda_status_string(3) == b"workspace too small"
