@@ -118,6 +118,14 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
                    void* dg_or_da, float* dA_log, float* ddt_bias, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* Instrumentation for callers that time the library's kernels (for example
+ * with HIP events): when set, `hook` is called on the host immediately before
+ * (end = 0) and after (end = 1) every kernel launch, with the kernel's name
+ * and the stream it is enqueued on. Process-wide; set it while no other
+ * thread is calling the library. NULL removes it. */
+typedef void (*kda_launch_hook)(void* user, const char* kernel, int end, void* stream);
+void kda_set_launch_hook(kda_launch_hook hook, void* user);
+
 const char* kda_status_string(kda_status s);
 const char* kda_last_error(void);   /* thread-local; "" if none */
 int kda_abi_version(void);          /* KDA_ABI_VERSION */

@@ -43,7 +43,9 @@ class kda_problem(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("kda_saved_bytes", "kda_workspace_bytes", "kda_fwd", "kda_bwd",
-           "kda_status_string", "kda_last_error", "kda_abi_version")
+           "kda_set_launch_hook", "kda_status_string", "kda_last_error", "kda_abi_version")
+LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int,
+                               ctypes.c_void_p)
 
 
 def lib():
@@ -60,9 +62,9 @@ def lib():
         L.kda_saved_bytes.restype = sz
         L.kda_workspace_bytes.argtypes = [pp, ctypes.c_int, ctypes.c_int]
         L.kda_workspace_bytes.restype = sz
-        L.kda_fwd.argtypes = [pp] + [vp] * 10 + [vp, sz, vp]
+        L.kda_fwd.argtypes = [pp] + [vp] * 11 + [sz, vp]
         L.kda_fwd.restype = ctypes.c_int
-        L.kda_bwd.argtypes = [pp] + [vp] * 16 + [vp, sz, vp]
+        L.kda_bwd.argtypes = [pp] + [vp] * 18 + [sz, vp]
         L.kda_bwd.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
@@ -70,8 +72,25 @@ def lib():
         L.kda_last_error.restype = ctypes.c_char_p
         L.kda_abi_version.argtypes = []
         L.kda_abi_version.restype = ctypes.c_int
+        L.kda_set_launch_hook.argtypes = [LAUNCH_HOOK, ctypes.c_void_p]
+        L.kda_set_launch_hook.restype = None
         _lib = L
     return _lib
+
+
+_hook_ref = None
+
+
+def set_launch_hook(fn):
+    """Install fn(kernel_name: str, end: bool, stream: int) as the library's
+    launch hook (None removes it)."""
+    global _hook_ref
+    if fn is None:
+        _hook_ref = None
+        lib().kda_set_launch_hook(LAUNCH_HOOK(), None)
+        return
+    _hook_ref = LAUNCH_HOOK(lambda user, name, end, stream: fn(name.decode(), bool(end), stream))
+    lib().kda_set_launch_hook(_hook_ref, None)
 
 
 def problem(T, H, num_seqs, gate="g", l2norm=False, scale=None, l2_eps=1e-6, dk=128, dv=128):
@@ -108,17 +127,39 @@ def _check(rc):
 
 
 def _stream(device):
+    if device is None:
+        return None
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _dev(t):
-    return t.device if t.is_cuda else None
+def _dev(p, tensors):
+    """The device of the call. Host tensors are refused for a valid problem (the
+    library would hand host addresses to its kernels); for an invalid problem
+    the library's own validation reports the error before any launch."""
+    ts = [t for t in tensors if t is not None]
+    if all(t.is_cuda for t in ts):
+        return ts[0].device
+    if lib().kda_saved_bytes(ctypes.byref(p)) != 0:
+        raise ValueError("every tensor passed to the KDA library must be on the GPU")
+    return None
+
+
+class _nullctx:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+def _device_ctx(dev):
+    return torch.cuda.device(dev) if dev is not None else _nullctx()
 
 
 def kda_fwd(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, o, saved, workspace):
     """Enqueue the forward on the current stream of q's device (made current)."""
-    dev = _dev(q)
-    with torch.cuda.device(dev):
+    dev = _dev(p, (q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, o, saved, workspace))
+    with _device_ctx(dev):
         rc = lib().kda_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g_or_a),
                            _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(o), _ptr(saved),
                            _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -130,8 +171,9 @@ def kda_bwd(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, dO, saved, dq,
             dbeta, dg_or_da, dA_log, ddt_bias, workspace):
     """Enqueue the backward on the current stream of q's device (made current).
     saved=None selects the replay backward."""
-    dev = _dev(q)
-    with torch.cuda.device(dev):
+    dev = _dev(p, (q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, dO, saved, dq, dk, dv,
+                   dbeta, dg_or_da, dA_log, ddt_bias, workspace))
+    with _device_ctx(dev):
         rc = lib().kda_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                            _ptr(g_or_a), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(dO),
                            _ptr(saved), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta),

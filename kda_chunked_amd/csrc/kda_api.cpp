@@ -151,9 +151,14 @@ size_t bwd_ws_bytes(const Sizes& s, int replay) {
   return c.off;
 }
 
-#define LAUNCH(call)                                                                    \
+kda_launch_hook g_hook = nullptr;
+void* g_hook_user = nullptr;
+
+#define LAUNCH(name, call)                                                              \
   do {                                                                                  \
+    if (g_hook) g_hook(g_hook_user, name, 0, hs);                                       \
     hipError_t e_ = (call);                                                             \
+    if (g_hook) g_hook(g_hook_user, name, 1, hs);                                       \
     if (e_ != hipSuccess)                                                               \
       return fail(KDA_ERR_DEVICE, "%s failed: %s", #call, hipGetErrorString(e_));       \
   } while (0)
@@ -216,9 +221,9 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   } else {
     sv = carve_saved(wc, s, 0, &G);
   }
-  LAUNCH(kda::launch_chunk_map(d, cu_seqlens, ct, hs));
-  LAUNCH(kda::launch_fwd_prep(d, in, ct, G, sv, hs));
-  LAUNCH(kda::launch_fwd_scan(d, in, ct, G, sv, o, saved != nullptr, hs));
+  LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
+  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, hs));
+  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, G, sv, o, saved != nullptr, hs));
   return KDA_OK;
 }
 
@@ -277,14 +282,14 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
     sv = carve_saved(sc, s, 1, &G);
   }
   const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
-  LAUNCH(kda::launch_chunk_map(d, cu_seqlens, ct, hs));
+  LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   if (replay) {
-    LAUNCH(kda::launch_fwd_prep(d, in, ct, G, sv, hs));
-    LAUNCH(kda::launch_fwd_scan(d, in, ct, G, sv, nullptr, 1, hs));
+    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, hs));
+    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, G, sv, nullptr, 1, hs));
   }
-  LAUNCH(kda::launch_bwd_scan(d, in, ct, G, sv, dO, dv, bw, hs));
-  LAUNCH(kda::launch_bwd_intra(d, in, ct, G, sv, dO, out, bw, hs));
-  if (p->gate == KDA_GATE_RAW) LAUNCH(kda::launch_finalize(d, ct, out, bw, hs));
+  LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, G, sv, dO, dv, bw, hs));
+  LAUNCH("bwd_intra", kda::launch_bwd_intra(d, in, ct, G, sv, dO, out, bw, hs));
+  if (p->gate == KDA_GATE_RAW) LAUNCH("finalize", kda::launch_finalize(d, ct, out, bw, hs));
   return KDA_OK;
 }
 
@@ -300,6 +305,11 @@ const char* kda_status_string(kda_status s) {
 }
 
 const char* kda_last_error(void) { return g_last_error; }
+
+void kda_set_launch_hook(kda_launch_hook hook, void* user) {
+  g_hook = hook;
+  g_hook_user = user;
+}
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 

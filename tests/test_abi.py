@@ -114,3 +114,25 @@ def test_status_strings():
     lib.kda_status_string.restype = ctypes.c_char_p
     assert lib.kda_status_string(0) == b"ok"
     assert lib.kda_status_string(3) == b"workspace too small"
+
+
+def test_bwd_binding_signature_and_validation():
+    """kda_bwd through the Python binding: an invalid problem is rejected on
+    the host (so no tensor memory is touched and no GPU is needed)."""
+    import torch
+    p = B.problem(100, 0, 1)
+    t = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(B.KdaError) as e:
+        B.kda_bwd(p, t, t, t, t, t, None, None, t, t, None, t, t, t, t, t, None, None, t)
+    assert e.value.status == 1 and "head" in str(e.value)
+    with pytest.raises(B.KdaError) as e:
+        B.kda_fwd(p, t, t, t, t, t, None, None, t, t, None, t)
+    assert e.value.status == 1
+
+
+def test_host_tensors_refused_for_a_valid_problem():
+    import torch
+    p = B.problem(100, 2, 1)
+    t = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        B.kda_fwd(p, t, t, t, t, t, None, None, t, t, None, t)
