@@ -9,33 +9,43 @@
 //   dA_qk = scale dO U~^T (i <= r),  dTb = dU~ R^T (i <= r)
 //   dT = dTb Diag(beta),  dX = -T^T dT T^T (i < r),  dA_kk = Diag(beta) dX
 //   dbeta_i = sum_r dTb[r,i] T[r,i] + sum_i' dX[i,i'] A_kk[i,i']
-// then pushes dA_qk, dA_kk through the decayed products (same fast-decay-safe
-// references as the forward), accumulates dq, dk and dG (the gradient of the
-// chunk-local cumsum G) per element, and finishes with
-//   dg_j = sum_{r >= j} dG_r   (reverse cumsum inside the chunk)
-// and the chain rules of the fused L2 norm and of the raw gate
-//   g = -exp(A_log) softplus(a + dt_bias).
-// Each pair term of dG enters dG_r with + and dG_i with - from products on the
-// same rounded operands (the diagonal pair rule of PR #8909's accuracy fix).
+// then pushes dA_qk, dA_kk through the decayed products, accumulates dq, dk
+// and dG (the gradient of the chunk-local cumsum G) per element, and finishes
+// with dg_j = sum_{r >= j} dG_r (reverse cumsum inside the chunk) and the chain
+// rules of the fused L2 norm and of the raw gate g = -exp(A_log) softplus(a +
+// dt_bias). Each pair term of dG enters dG_r with + and dG_i with - from
+// products of the same rounded operands (the diagonal pair rule of PR #8909's
+// accuracy fix).
+//
+// Decayed products. When the chunk's total decay span is at most CALM_SPAN in
+// every channel, one reference (the chunk start) serves every (r, i) pair:
+// x_r e^(G_r - G_i) k_i = (x_r e^(G_r)) (k_i e^(-G_i)), all factors <= e^40.
+// Otherwise each 16-row block I uses the reference rho_I = G before the block
+// (both factors <= 1 for columns before the block) and a diagonal block whose
+// own span is too wide is summed element by element in fp32.
+//
+// Work layout: 512 threads (8 waves). Wave w owns rows 16*(w&3).. of the
+// chunk and channels 64*(w>>2).. of every 64 x 128 per-element quantity; the
+// thread keeps its 16 elements' G, q^, k^ in registers, so epilogues read no
+// memory.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
+constexpr int NTHR = 512;
 constexpr int K1_LD = HD + 8;
 constexpr int K2_LD = CL + 8;
 constexpr int X_LD = 32 + 8;
 constexpr int GS_LD = HD + 4;
-constexpr int AK_LD = CL + 4;
+constexpr int F_LD = CL + 1;        // fp32 64x64 matrices
 constexpr float CALM_SPAN_B = 40.f;
 
 struct BwdIntraSmem {
   union {
     struct {
-      bf16 tb_hi[CL][K2_LD], tb_lo[CL][K2_LD];     // Tb   [r][i]
-      bf16 tbt_hi[CL][K2_LD], tbt_lo[CL][K2_LD];   // Tb^T [i][r]
-      bf16 rt_hi[HD][K2_LD], rt_lo[HD][K2_LD];     // R^T  [j][i]
-      bf16 dut_hi[HD][K2_LD], dut_lo[HD][K2_LD];   // dU~^T [j][r]
+      bf16 a_hi[CL][K2_LD], a_lo[CL][K2_LD];       // Tb [r][i], then Tb^T [i][r]
+      bf16 b_hi[HD][K2_LD], b_lo[HD][K2_LD];       // R^T [j][i], then dU~^T [j][r]
     } p1;
     struct {
       bf16 s_hi[HD][K1_LD], s_lo[HD][K1_LD];       // S_in [c][j], then dS_out [c][j]
@@ -43,45 +53,63 @@ struct BwdIntraSmem {
       bf16 do_hi[CL][K1_LD];                       // dO [r][j]
     } p2;
     struct {
-      bf16 du_hi[CL][K1_LD], du_lo[CL][K1_LD];     // dU~ [r][j]
-      bf16 r_hi[CL][K1_LD], r_lo[CL][K1_LD];       // R [i][j]
+      bf16 a_hi[CL][K1_LD], a_lo[CL][K1_LD];       // dU~ [r][j]
+      bf16 b_hi[CL][K1_LD], b_lo[CL][K1_LD];       // R [i][j]
     } p4;
     struct {
-      float T[CL][AK_LD], Akk[CL][AK_LD], dT[CL][AK_LD], tmp[CL][AK_LD];
+      float dAqk[CL][F_LD], dAkk[CL][F_LD];        // shared with p6
+      float T[CL][F_LD], dT[CL][F_LD], tmp[CL][F_LD];
     } p5;
     struct {
-      float G[CL][GS_LD];
-      bf16 yt_hi[HD][K2_LD], yt_lo[HD][K2_LD];     // Y^T [c][i]
-      bf16 xt_hi[HD][X_LD], xt_lo[HD][X_LD];       // [Xq ; Xk]^T [c][32]
-      bf16 dq_hi[16][K2_LD], dq_lo[16][K2_LD];     // dA_qk rows of block I [r][i]
-      bf16 dk_hi[16][K2_LD], dk_lo[16][K2_LD];     // dA_kk rows of block I
-      bf16 dat_hi[CL][X_LD], dat_lo[CL][X_LD];     // [dA_qk^T | dA_kk^T] [i][32]
-      float rho[HD];
+      float dAqk[CL][F_LD], dAkk[CL][F_LD];
+      union {
+        struct {                                   // single-reference path, part 1
+          bf16 dq_hi[CL][K2_LD], dq_lo[CL][K2_LD]; // dA_qk [r][i]
+          bf16 dk_hi[CL][K2_LD], dk_lo[CL][K2_LD]; // dA_kk [r][i]
+          bf16 yt_hi[HD][K2_LD], yt_lo[HD][K2_LD]; // (k^ e^-G)^T [c][i]
+        } a;
+        struct {                                   // single-reference path, part 2
+          bf16 dat_hi[CL][K1_LD], dat_lo[CL][K1_LD];   // [dA_qk^T | dA_kk^T] [i][128]
+          bf16 xt_hi[HD][K1_LD], xt_lo[HD][K1_LD];     // [q^ e^G ; k^ e^G]^T [c][128]
+        } b;
+        struct {                                   // per-block path
+          bf16 yt_hi[HD][K2_LD], yt_lo[HD][K2_LD];
+          bf16 xt_hi[HD][X_LD], xt_lo[HD][X_LD];
+          bf16 dq_hi[16][K2_LD], dq_lo[16][K2_LD];
+          bf16 dk_hi[16][K2_LD], dk_lo[16][K2_LD];
+          bf16 dat_hi[CL][X_LD], dat_lo[CL][X_LD];
+          float Gb[16][HD], qb[16][HD], kb[16][HD];  // one diagonal block, fp32
+        } g;
+      } u;
     } p6;
     struct {
       float dG[CL][GS_LD];
-      float red[HD];
+      bf16 a[CL][HD];
+      float tot[HD];
+      float red[2][2][HD];
+      float rowp[2][2][CL];
     } p7;
   } u;
-  float dAqk[CL][AK_LD];
-  float dAkk[CL][AK_LD];
   float beta[CL], rq[CL], rk[CL], db[CL];
   float GL[HD], gam[HD], dGL[HD];
+  float Gref[5][HD];       // G before block I (I = 0..3) and G_last (I = 4)
   float dGLw[4][HD];
-  int calm[4];
+  int calm_blk[4];
+  int calm_chunk;
 };
 
-__global__ __launch_bounds__(256) void bwd_intra_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                         const float* __restrict__ G,
-                                                         SavedSet sv,
-                                                         const bf16* __restrict__ dO,
-                                                         BwdOut out, BwdWork bw) {
+__global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, ChunkTable ct,
+                                                          const float* __restrict__ G,
+                                                          SavedSet sv,
+                                                          const bf16* __restrict__ dO,
+                                                          BwdOut out, BwdWork bw) {
   __shared__ BwdIntraSmem sm;
   const int ci = blockIdx.x, h = blockIdx.y;
   if (ci >= ct.doc_c0[d.N]) return;
   const int64_t t0 = ct.tok[ci];
   const int n = ct.len[ci];
   const int t = threadIdx.x, w = wave_id(), l = lane_id();
+  const int rb = w & 3, chh = w >> 2;          // row block, channel half
   const int64_t ch = (int64_t)ci * d.H + h;
   const int H = d.H;
   const bf16* q = reinterpret_cast<const bf16*>(in.q);
@@ -89,251 +117,315 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(Dims d, Inputs in, Chunk
   const bf16* beta = reinterpret_cast<const bf16*>(in.beta);
   const float* Tg = sv.Tm + ch * CL * CL;
   const float* Akk_g = sv.Akk + ch * CL * CL;
-
-  // element (r, c) of this lane's accumulators: r = 16w + drow(i), c = 16nt + dcol()
-  f32x4 adq[8], adk[8], adG[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) adq[nt] = adk[nt] = adG[nt] = zero4();
-
   auto rowidx = [&](int r) -> int64_t { return (t0 + r) * H + h; };
+  auto clampr = [&](int r) -> int { return r < n ? r : n - 1; };
 
-  if (t < CL) {
-    const bool ok = t < n;
-    sm.beta[t] = ok ? bf2f(beta[rowidx(t)]) : 0.f;
-    sm.rq[t] = ok ? sv.rq[rowidx(t)] : 0.f;
-    sm.rk[t] = ok ? sv.rk[rowidx(t)] : 0.f;
-  } else if (t < CL + HD) {
-    const int c = t - CL;
-    const float gl = G[rowidx(n - 1) * HD + c];
-    sm.GL[c] = gl;
-    sm.gam[c] = fexp(gl);
-  }
-  for (int e = t; e < CL * AK_LD; e += 256) {
-    (&sm.dAqk[0][0])[e] = 0.f;
-    (&sm.dAkk[0][0])[e] = 0.f;
-  }
-  __syncthreads();
-
-  // ------------------------------------------------ P1: U~ = Tb R, dR = Tb^T dU~
-  f32x4 U[8], dR[8];
+  // ------------------------------------------------------------ P0: setup
+  // this thread's elements: rows er(i) = 16 rb + drow(i), channels ec(nt) = 64 chh + 16 nt + dcol()
+  float eG[4][4];
+  bf16 eqb[4][4], ekb[4][4];       // raw q, k (bf16); q^ = q * rqr[i], zero on padded rows
+  float rqr[4], rkr[4];
   {
-    const Panel TB{&sm.u.p1.tb_hi[0][0], &sm.u.p1.tb_lo[0][0], K2_LD};
-    const Panel TBT{&sm.u.p1.tbt_hi[0][0], &sm.u.p1.tbt_lo[0][0], K2_LD};
-    const Panel RT{&sm.u.p1.rt_hi[0][0], &sm.u.p1.rt_lo[0][0], K2_LD};
-    const Panel DUT{&sm.u.p1.dut_hi[0][0], &sm.u.p1.dut_lo[0][0], K2_LD};
-    for (int e = t; e < CL * (CL / 8); e += 256) {
-      const int r = e >> 3, i8 = (e & 7) * 8;
-      float tb[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) tb[j] = Tg[r * CL + i8 + j] * sm.beta[i8 + j];
-      put8(TB, r, i8, tb);
+    for (int i = 0; i < 4; ++i) {
+      const int r0 = 16 * rb + drow(i), r = clampr(r0);
+      const float a = sv.rq[rowidx(r)], b = sv.rk[rowidx(r)];
+      rqr[i] = r0 < n ? a : 0.f;
+      rkr[i] = r0 < n ? b : 0.f;
     }
-    for (int e = t; e < CL * (CL / 8); e += 256) {
-      const int i = e & (CL - 1), r8 = (e >> 6) * 8;
-      float tb[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) tb[j] = Tg[(r8 + j) * CL + i] * sm.beta[i];
-      put8(TBT, i, r8, tb);
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = clampr(16 * rb + drow(i));
+        const int64_t idx = rowidx(r) * HD + 64 * chh + 16 * nt + dcol();
+        eG[nt][i] = G[idx];
+        eqb[nt][i] = q[idx];
+        ekb[nt][i] = k[idx];
+      }
+  }
+#define EQ(nt, i) (bf2f(eqb[nt][i]) * rqr[i])
+#define EK(nt, i) (bf2f(ekb[nt][i]) * rkr[i])
+  if (t < CL) {
+    const int r = clampr(t);
+    const bool ok = t < n;
+    const float b = bf2f(beta[rowidx(r)]), a = sv.rq[rowidx(r)], c = sv.rk[rowidx(r)];
+    sm.beta[t] = ok ? b : 0.f;
+    sm.rq[t] = ok ? a : 0.f;
+    sm.rk[t] = ok ? c : 0.f;
+  }
+  for (int e = t; e < 5 * HD; e += NTHR) {
+    const int I = e >> 7, c = e & 127;
+    const float v = I == 0 ? 0.f : G[rowidx(clampr(16 * I - 1)) * HD + c];
+    sm.Gref[I][c] = v;
+    if (I == 4) {
+      sm.GL[c] = v;
+      sm.gam[c] = fexp(v);
     }
-    for (int e = t; e < HD * (CL / 8); e += 256) {
-      const int j = e & (HD - 1), r8 = (e >> 7) * 8;
-      float rv[8], du[8];
+  }
+  if (t < 4) sm.calm_blk[t] = 1;
+  if (t == 4) sm.calm_chunk = 1;
+  __syncthreads();
+  if (t < HD) {
+    if (-sm.Gref[4][t] > CALM_SPAN_B) sm.calm_chunk = 0;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      if (sm.Gref[I][t] - sm.Gref[I + 1][t] > CALM_SPAN_B) sm.calm_blk[I] = 0;
+  }
+
+  f32x4 adq[4], adk[4], adG[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) adq[nt] = adk[nt] = adG[nt] = zero4();
+
+  // ------------------------------------------------------------ P1: U~ and dR
+  f32x4 U[4], dR[4];
+  {
+    const Panel A{&sm.u.p1.a_hi[0][0], &sm.u.p1.a_lo[0][0], K2_LD};
+    const Panel B{&sm.u.p1.b_hi[0][0], &sm.u.p1.b_lo[0][0], K2_LD};
+    // Tb [r][i]
+    {
+      const int r = t >> 3, i8 = (t & 7) * 8;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(Tg + r * CL + i8);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(Tg + r * CL + i8 + 4);
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = a0[j] * sm.beta[i8 + j];
+        x[j + 4] = a1[j] * sm.beta[i8 + 4 + j];
+      }
+      put8(A, r, i8, x);
+    }
+    // R^T [j][i]
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int e = t + NTHR * rep, j = e & 127, i8 = (e >> 7) * 8;
+      float x[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int i = i8 + jj;
+        const float v = sv.R[rowidx(clampr(i)) * HD + j];
+        x[jj] = i < n ? v : 0.f;
+      }
+      put8(B, j, i8, x);
+    }
+    __syncthreads();
+    const int kend = ((16 * rb + 16 + 31) / 32) * 32;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) U[nt] = zero4();
+    mma_row<SPLIT_AB, 4>(U, A, 16 * rb, B, 64 * chh, 0, kend);
+    __syncthreads();
+    // Tb^T [i][r]
+    {
+      const int i = t & 63, r8 = (t >> 6) * 8;
+      float x[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) x[jj] = Tg[(r8 + jj) * CL + i] * sm.beta[i];
+      put8(A, i, r8, x);
+    }
+    // dU~^T [j][r]
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int e = t + NTHR * rep, j = e & 127, r8 = (e >> 7) * 8;
+      float x[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int r = r8 + jj;
-        rv[jj] = r < n ? sv.R[rowidx(r) * HD + j] : 0.f;
-        du[jj] = r < n ? bw.dU[rowidx(r) * HD + j] : 0.f;
+        const float v = bw.dU[rowidx(clampr(r)) * HD + j];
+        x[jj] = r < n ? v : 0.f;
       }
-      put8(RT, j, r8, rv);
-      put8(DUT, j, r8, du);
+      put8(B, j, r8, x);
     }
     __syncthreads();
-    const int kend = ((16 * w + 16 + 31) / 32) * 32;
-    const int kbeg = (16 * w / 32) * 32;
+    const int kbeg = (16 * rb / 32) * 32;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      U[nt] = zero4();
-      dR[nt] = zero4();
-      mma<SPLIT_AB>(U[nt], TB, 16 * w, RT, 16 * nt, 0, kend);
-      mma<SPLIT_AB>(dR[nt], TBT, 16 * w, DUT, 16 * nt, kbeg, CL);
-    }
+    for (int nt = 0; nt < 4; ++nt) dR[nt] = zero4();
+    mma_row<SPLIT_AB, 4>(dR, A, 16 * rb, B, 64 * chh, kbeg, CL);
     __syncthreads();
   }
 
-  // ------------------------------------------------ P2: dQd and dKd against S_in
+  // ------------------------------------------------------------ P2: dQd, dKd
   const Panel SP{&sm.u.p2.s_hi[0][0], &sm.u.p2.s_lo[0][0], K1_LD};
   const Panel AP{&sm.u.p2.a_hi[0][0], &sm.u.p2.a_lo[0][0], K1_LD};
   const Panel DOP{&sm.u.p2.do_hi[0][0], nullptr, K1_LD};
-  {
-    const float* Sg = sv.S_in + ch * HD * HD;
-    for (int e = t; e < HD * (HD / 8); e += 256) {
-      const int c = e >> 4, j8 = (e & 15) * 8;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(Sg + c * HD + j8);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(Sg + c * HD + j8 + 4);
-      const float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      put8(SP, c, j8, x);
+  auto load_state_panel = [&](const float* src) {
+    // 128 x 128 fp32 -> split panel [c][j]; 8 float4 per thread, all issued first
+    f32x4 v[8];
+#pragma unroll
+    for (int rep = 0; rep < 8; ++rep) {
+      const int e = t + NTHR * rep, c = e >> 5, j4 = (e & 31) * 4;
+      v[rep] = *reinterpret_cast<const f32x4*>(src + c * HD + j4);
     }
-    for (int e = t; e < CL * (HD / 8); e += 256) {
-      const int r = e >> 4, j8 = (e & 15) * 8;
-      bf16x8 x;
-      if (r < n) {
-        x = *reinterpret_cast<const bf16x8*>(dO + rowidx(r) * HD + j8);
-      } else {
+#pragma unroll
+    for (int rep = 0; rep < 8; ++rep) {
+      const int e = t + NTHR * rep, c = e >> 5, j4 = (e & 31) * 4;
+      put4(SP, c, j4, v[rep]);
+    }
+  };
+  {
+    load_state_panel(sv.S_in + ch * HD * HD);
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int e = t + NTHR * rep, r = e >> 4, j8 = (e & 15) * 8;
+      bf16x8 x = *reinterpret_cast<const bf16x8*>(dO + rowidx(clampr(r)) * HD + j8);
+      if (r >= n) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) x[jj] = f2bf(0.f);
       }
       *reinterpret_cast<bf16x8*>(&sm.u.p2.do_hi[r][j8]) = x;
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) store_tile_n(dR[nt], AP, 16 * w, 16 * nt);
+    for (int nt = 0; nt < 4; ++nt) store_tile_n(dR[nt], AP, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
+    {
+      f32x4 a[4];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      f32x4 a = zero4(), b = zero4();
-      mma_k<SPLIT_B, HD>(a, DOP, 16 * w, SP, 16 * nt);
-      mma_k<SPLIT_AB, HD>(b, AP, 16 * w, SP, 16 * nt);
+      for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
+      mma_row<SPLIT_B, 4>(a, DOP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i), c = 16 * nt + dcol();
-        if (r < n) {
-          const int64_t idx = rowidx(r) * HD + c;
-          const float e1 = fexp(G[idx]);
-          const float qh = bf2f(q[idx]) * sm.rq[r], kh = bf2f(k[idx]) * sm.rk[r];
-          const float p = d.scale * a[i] * e1;
-          const float p2 = -b[i] * e1;
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = d.scale * a[nt][i] * fexp(eG[nt][i]);
           adq[nt][i] += p;
-          adk[nt][i] += p2;
-          adG[nt][i] += p * qh + p2 * kh;
+          adG[nt][i] += p * EQ(nt, i);
         }
-      }
+    }
+    {
+      f32x4 b[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) b[nt] = zero4();
+      mma_row<SPLIT_AB, 4>(b, AP, 16 * rb, SP, 64 * chh, 0, HD);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p2 = -b[nt][i] * fexp(eG[nt][i]);
+          adk[nt][i] += p2;
+          adG[nt][i] += p2 * EK(nt, i);
+        }
     }
     __syncthreads();
   }
 
-  // ------------------------------------------------ P3: dKe, dA_qk, dgamma
+  // ------------------------------------------------------------ P3: dKe, dA_qk, dgamma
+  f32x4 dAq[2];
   {
-    const float* dSg = bw.dS + ch * HD * HD;
-    for (int e = t; e < HD * (HD / 8); e += 256) {
-      const int c = e >> 4, j8 = (e & 15) * 8;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(dSg + c * HD + j8);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(dSg + c * HD + j8 + 4);
-      const float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      put8(SP, c, j8, x);
-    }
+    load_state_panel(bw.dS + ch * HD * HD);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) store_tile_n(U[nt], AP, 16 * w, 16 * nt);
+    for (int nt = 0; nt < 4; ++nt) store_tile_n(U[nt], AP, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
-    float colp[8];
+    f32x4 a[4];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      f32x4 a = zero4();
-      mma_k<SPLIT_AB, HD>(a, AP, 16 * w, SP, 16 * nt);
-      colp[nt] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i), c = 16 * nt + dcol();
-        if (r < n) {
-          const int64_t idx = rowidx(r) * HD + c;
-          const float kh = bf2f(k[idx]) * sm.rk[r];
-          const float p3 = a[i] * fexp(sm.GL[c] - G[idx]);
-          adk[nt][i] += p3;
-          adG[nt][i] -= p3 * kh;
-          colp[nt] += p3 * kh;
-        }
-      }
-    }
-    // column sums of the Ke term -> dG at the chunk's last row
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      float s = colp[nt];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      if (l < 16) sm.dGLw[w][16 * nt + l] = s;
-    }
-    // dA_qk = scale dO U~^T, lower triangle including the diagonal
+    for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
+    mma_row<SPLIT_AB, 4>(a, AP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      f32x4 a = zero4();
-      mma_k<SPLIT_B, HD>(a, DOP, 16 * w, AP, 16 * nt);
+      const int c = 64 * chh + 16 * nt + dcol();
+      float colp = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i), c = 16 * nt + dcol();
-        sm.dAqk[r][c] = (c <= r) ? d.scale * a[i] : 0.f;
+        const float p3 = a[nt][i] * fexp(sm.GL[c] - eG[nt][i]);
+        adk[nt][i] += p3;
+        adG[nt][i] -= p3 * EK(nt, i);
+        colp += p3 * EK(nt, i);
       }
+      colp += __shfl_xor(colp, 16);
+      colp += __shfl_xor(colp, 32);
+      if (l < 16) sm.dGLw[rb][c] = colp;
     }
-    __syncthreads();
-    // dgamma[c] = sum_j dS_out[c][j] S_in[c][j]; dG_last += dgamma * gamma
+    // dA_qk = scale dO U~^T: rows 16 rb, columns i in tiles 2 chh, 2 chh + 1
+    dAq[0] = dAq[1] = zero4();
+    mma_row<SPLIT_B, 2>(dAq, DOP, 16 * rb, AP, 32 * chh, 0, HD);
+    // dgamma[c] = sum_j dS_out[c][j] S_in[c][j]; four threads per channel
     {
-      const float* Sg = sv.S_in + ch * HD * HD;
-      const int c = t >> 1, half = t & 1;
+      const int c = t >> 2, part = t & 3;
+      const float* dSg = bw.dS + ch * HD * HD + c * HD + 32 * part;
+      const float* Sg = sv.S_in + ch * HD * HD + c * HD + 32 * part;
+      f32x4 xa[8], xb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xa[j] = *reinterpret_cast<const f32x4*>(dSg + 4 * j);
+        xb[j] = *reinterpret_cast<const f32x4*>(Sg + 4 * j);
+      }
       float s = 0.f;
-      for (int j = 64 * half; j < 64 * half + 64; ++j) s += dSg[c * HD + j] * Sg[c * HD + j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += xa[j][0] * xb[j][0] + xa[j][1] * xb[j][1] + xa[j][2] * xb[j][2] + xa[j][3] * xb[j][3];
       s += __shfl_xor(s, 1);
-      if (half == 0)
+      s += __shfl_xor(s, 2);
+      __syncthreads();
+      if (part == 0)
         sm.dGL[c] = s * sm.gam[c] + ((sm.dGLw[0][c] + sm.dGLw[1][c]) + (sm.dGLw[2][c] + sm.dGLw[3][c]));
     }
     __syncthreads();
   }
 
-  // ------------------------------------------------ P4: dTb = dU~ R^T
-  f32x4 dTb[4];
+  // ------------------------------------------------------------ P4: dTb = dU~ R^T
+  f32x4 dTb[2];
   {
-    const Panel DU{&sm.u.p4.du_hi[0][0], &sm.u.p4.du_lo[0][0], K1_LD};
-    const Panel RP{&sm.u.p4.r_hi[0][0], &sm.u.p4.r_lo[0][0], K1_LD};
-    for (int e = t; e < CL * (HD / 8); e += 256) {
-      const int r = e >> 4, j8 = (e & 15) * 8;
-      float a[8], b[8];
+    const Panel DU{&sm.u.p4.a_hi[0][0], &sm.u.p4.a_lo[0][0], K1_LD};
+    const Panel RP{&sm.u.p4.b_hi[0][0], &sm.u.p4.b_lo[0][0], K1_LD};
+    f32x4 va[4], vb[4];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        a[jj] = r < n ? bw.dU[rowidx(r) * HD + j8 + jj] : 0.f;
-        b[jj] = r < n ? sv.R[rowidx(r) * HD + j8 + jj] : 0.f;
-      }
-      put8(DU, r, j8, a);
-      put8(RP, r, j8, b);
+    for (int rep = 0; rep < 4; ++rep) {
+      const int e = t + NTHR * rep, r = e >> 5, j4 = (e & 31) * 4;
+      va[rep] = *reinterpret_cast<const f32x4*>(bw.dU + rowidx(clampr(r)) * HD + j4);
+      vb[rep] = *reinterpret_cast<const f32x4*>(sv.R + rowidx(clampr(r)) * HD + j4);
+    }
+#pragma unroll
+    for (int rep = 0; rep < 4; ++rep) {
+      const int e = t + NTHR * rep, r = e >> 5, j4 = (e & 31) * 4;
+      const f32x4 z = zero4();
+      put4(DU, r, j4, r < n ? va[rep] : z);
+      put4(RP, r, j4, r < n ? vb[rep] : z);
     }
     __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      dTb[nt] = zero4();
-      mma_k<SPLIT_AB, HD>(dTb[nt], DU, 16 * w, RP, 16 * nt);
-    }
+    dTb[0] = dTb[1] = zero4();
+    mma_row<SPLIT_AB, 2>(dTb, DU, 16 * rb, RP, 32 * chh, 0, HD);
     __syncthreads();
   }
 
-  // ------------------------------------------------ P5: WY / UT backward (fp32)
+  // ------------------------------------------------------------ P5: WY / UT backward (fp32)
   {
-    float (*Tm)[AK_LD] = sm.u.p5.T;
-    float (*Ak)[AK_LD] = sm.u.p5.Akk;
-    float (*dT)[AK_LD] = sm.u.p5.dT;
-    float (*tmp)[AK_LD] = sm.u.p5.tmp;
-    for (int e = t; e < CL * CL; e += 256) {
-      const int r = e >> 6, i = e & 63;
-      Tm[r][i] = Tg[e];
-      Ak[r][i] = Akk_g[e];
+    float (*dAqk)[F_LD] = sm.u.p5.dAqk;
+    float (*dAkk)[F_LD] = sm.u.p5.dAkk;
+    float (*Tm)[F_LD] = sm.u.p5.T;
+    float (*dT)[F_LD] = sm.u.p5.dT;
+    float (*tmp)[F_LD] = sm.u.p5.tmp;
+    {
+      f32x4 a0 = *reinterpret_cast<const f32x4*>(Tg + 8 * t);
+      f32x4 a1 = *reinterpret_cast<const f32x4*>(Tg + 8 * t + 4);
+      const int r = t >> 3, i8 = (t & 7) * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Tm[r][i8 + j] = a0[j];
+        Tm[r][i8 + 4 + j] = a1[j];
+      }
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i), c = 16 * nt + dcol();
+        const int r = 16 * rb + drow(i), c = 32 * chh + 16 * nt + dcol();
         dT[r][c] = (c <= r) ? dTb[nt][i] : 0.f;
+        dAqk[r][c] = (c <= r) ? d.scale * dAq[nt][i] : 0.f;
       }
     __syncthreads();
     if (t < CL) {
-      // dbeta from Tb = T Diag(beta): column sums, fixed order
       float s = 0.f;
       for (int r = t; r < CL; ++r) s += dT[r][t] * Tm[r][t];
       sm.db[t] = s;
     }
     __syncthreads();
-    for (int e = t; e < CL * CL; e += 256) {
-      const int r = e >> 6, m = e & 63;
+#pragma unroll
+    for (int rep = 0; rep < 8; ++rep) {
+      const int e = t + NTHR * rep, r = e >> 6, m = e & 63;
       dT[r][m] *= sm.beta[m];
     }
     __syncthreads();
     // tmp = dT T^T : tmp[r][i] = sum_{m <= min(r, i)} dT[r][m] T[i][m]
-    for (int e = t; e < CL * CL; e += 256) {
-      const int r = e >> 6, i = e & 63;
+#pragma unroll
+    for (int rep = 0; rep < 8; ++rep) {
+      const int e = t + NTHR * rep, r = e >> 6, i = e & 63;
       const int mmax = min(r, i);
       float s = 0.f;
       for (int m = 0; m <= mmax; ++m) s += dT[r][m] * Tm[i][m];
@@ -341,269 +433,368 @@ __global__ __launch_bounds__(256) void bwd_intra_kernel(Dims d, Inputs in, Chunk
     }
     __syncthreads();
     {
-      // dX[r][i] = -sum_{m >= r} T[m][r] tmp[m][i]  (i < r); four threads per row
-      const int r = t >> 2, part = t & 3;
+      // dX[r][i] = -sum_{m >= r} T[m][r] tmp[m][i] (i < r); eight threads per row
+      const int r = t >> 3, part = t & 7;
+      const f32x4 ak0 = *reinterpret_cast<const f32x4*>(Akk_g + r * CL + 8 * part);
+      const f32x4 ak1 = *reinterpret_cast<const f32x4*>(Akk_g + r * CL + 8 * part + 4);
       float dbr = 0.f;
-      for (int i = 16 * part; i < 16 * part + 16; ++i) {
-        if (i >= r) break;
-        float s = 0.f;
-        for (int m = r; m < CL; ++m) s += Tm[m][r] * tmp[m][i];
-        const float dx = -s;
-        sm.dAkk[r][i] = sm.beta[r] * dx;
-        dbr += dx * Ak[r][i];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int i = 8 * part + jj;
+        float dx = 0.f;
+        if (i < r) {
+          float s = 0.f;
+          for (int m = r; m < CL; ++m) s += Tm[m][r] * tmp[m][i];
+          dx = -s;
+        }
+        dAkk[r][i] = sm.beta[r] * dx;
+        dbr += dx * (jj < 4 ? ak0[jj] : ak1[jj - 4]);
       }
       dbr += __shfl_xor(dbr, 1);
       dbr += __shfl_xor(dbr, 2);
+      dbr += __shfl_xor(dbr, 4);
+      __syncthreads();
       if (part == 0) sm.db[r] += dbr;
     }
     __syncthreads();
   }
 
-  // ------------------------------------------------ P6: decayed-product backward
+  // ------------------------------------------------------------ P6: decayed-product backward
   {
-    float (*Gs)[GS_LD] = sm.u.p6.G;
-    for (int e = t; e < CL * HD; e += 256) {
-      const int r = e >> 7, c = e & 127;
-      Gs[r][c] = r < n ? G[rowidx(r) * HD + c] : sm.GL[c];
-    }
-    if (t < 4) sm.calm[t] = 1;
-    __syncthreads();
-    if (t < HD) {
+    float (*dAqk)[F_LD] = sm.u.p6.dAqk;
+    float (*dAkk)[F_LD] = sm.u.p6.dAkk;
+    if (sm.calm_chunk) {
+      // single reference at the chunk start
+      const Panel DQ{&sm.u.p6.u.a.dq_hi[0][0], &sm.u.p6.u.a.dq_lo[0][0], K2_LD};
+      const Panel DK{&sm.u.p6.u.a.dk_hi[0][0], &sm.u.p6.u.a.dk_lo[0][0], K2_LD};
+      const Panel YT{&sm.u.p6.u.a.yt_hi[0][0], &sm.u.p6.u.a.yt_lo[0][0], K2_LD};
+      {
+        const int r = t >> 3, i8 = (t & 7) * 8;
+        put8(DQ, r, i8, &dAqk[r][i8]);
+        put8(DK, r, i8, &dAkk[r][i8]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = EK(nt, i) * fexp(-eG[nt][i]);
+        put4(YT, 64 * chh + 16 * nt + dcol(), 16 * rb + 4 * (l >> 4), y);
+      }
+      __syncthreads();
+      const int kend = ((16 * rb + 16 + 31) / 32) * 32;
+      f32x4 aq[4], ak[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aq[nt] = ak[nt] = zero4();
+      mma_row<SPLIT_AB, 4>(aq, DQ, 16 * rb, YT, 64 * chh, 0, kend);
+      mma_row<SPLIT_AB, 4>(ak, DK, 16 * rb, YT, 64 * chh, 0, kend);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e1 = fexp(eG[nt][i]);
+          const float dqa = aq[nt][i] * e1, dka = ak[nt][i] * e1;
+          adq[nt][i] += dqa;
+          adk[nt][i] += dka;
+          adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
+        }
+      __syncthreads();
+      const Panel DAT{&sm.u.p6.u.b.dat_hi[0][0], &sm.u.p6.u.b.dat_lo[0][0], K1_LD};
+      const Panel XT{&sm.u.p6.u.b.xt_hi[0][0], &sm.u.p6.u.b.xt_lo[0][0], K1_LD};
+      {
+        const int i = t & 63, part = t >> 6;           // part: 8 groups of 8 rows (qk 0-3, kk 4-7)
+        const int r8 = (part & 3) * 16, isk = part >> 2;
+        float x[8], y[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          x[jj] = isk ? dAkk[r8 + jj][i] : dAqk[r8 + jj][i];
+          y[jj] = isk ? dAkk[r8 + 8 + jj][i] : dAqk[r8 + 8 + jj][i];
+        }
+        put8(DAT, i, 64 * isk + r8, x);
+        put8(DAT, i, 64 * isk + r8 + 8, y);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 xq, xk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e1 = fexp(eG[nt][i]);
+          xq[i] = EQ(nt, i) * e1;
+          xk[i] = EK(nt, i) * e1;
+        }
+        const int c = 64 * chh + 16 * nt + dcol(), r0 = 16 * rb + 4 * (l >> 4);
+        put4(XT, c, r0, xq);
+        put4(XT, c, 64 + r0, xk);
+      }
+      __syncthreads();
+      f32x4 ac[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
+      const int kb = (16 * rb / 32) * 32;
+      mma_row<SPLIT_AB, 4>(ac, DAT, 16 * rb, XT, 64 * chh, kb, CL);
+      mma_row<SPLIT_AB, 4>(ac, DAT, 16 * rb, XT, 64 * chh, CL + kb, 2 * CL);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float dka = ac[nt][i] * fexp(-eG[nt][i]);
+          adk[nt][i] += dka;
+          adG[nt][i] -= dka * EK(nt, i);
+        }
+      __syncthreads();
+    } else {
+      // one reference per 16-row block
+      const Panel YT{&sm.u.p6.u.g.yt_hi[0][0], &sm.u.p6.u.g.yt_lo[0][0], K2_LD};
+      const Panel XT{&sm.u.p6.u.g.xt_hi[0][0], &sm.u.p6.u.g.xt_lo[0][0], X_LD};
+      const Panel DQ{&sm.u.p6.u.g.dq_hi[0][0], &sm.u.p6.u.g.dq_lo[0][0], K2_LD};
+      const Panel DK{&sm.u.p6.u.g.dk_hi[0][0], &sm.u.p6.u.g.dk_lo[0][0], K2_LD};
+      const Panel DAT{&sm.u.p6.u.g.dat_hi[0][0], &sm.u.p6.u.g.dat_lo[0][0], X_LD};
       for (int I = 0; I < 4; ++I) {
-        const float ref = I == 0 ? 0.f : Gs[16 * I - 1][t];
-        if (ref - Gs[16 * I + 15][t] > CALM_SPAN_B) sm.calm[I] = 0;
-      }
-    }
-    const Panel YT{&sm.u.p6.yt_hi[0][0], &sm.u.p6.yt_lo[0][0], K2_LD};
-    const Panel XT{&sm.u.p6.xt_hi[0][0], &sm.u.p6.xt_lo[0][0], X_LD};
-    const Panel DQ{&sm.u.p6.dq_hi[0][0], &sm.u.p6.dq_lo[0][0], K2_LD};
-    const Panel DK{&sm.u.p6.dk_hi[0][0], &sm.u.p6.dk_lo[0][0], K2_LD};
-    const Panel DAT{&sm.u.p6.dat_hi[0][0], &sm.u.p6.dat_lo[0][0], X_LD};
-    float* rho = sm.u.p6.rho;
-    for (int I = 0; I < 4; ++I) {
-      __syncthreads();
-      if (t < HD) rho[t] = I == 0 ? 0.f : Gs[16 * I - 1][t];
-      __syncthreads();
-      const int calm = sm.calm[I];
-      const int ny = 16 * I + 16;           // columns i of this row block
-      const int nyk = ((ny + 31) / 32) * 32;
-      // Y^T [c][i] = k^_i e^(rho - G_i), zero for i >= ny and for block I when not calm
-      for (int e = t; e < HD * (CL / 8); e += 256) {
-        const int c = e & (HD - 1), i8 = (e >> 7) * 8;
-        float y[8];
+        const int calm = sm.calm_blk[I];
+        const int ny = 16 * I + 16;
+        const int nyk = ((ny + 31) / 32) * 32;
+        // Y^T [c][i]: rows of this thread's block, zero unless before block I
+        // (or block I itself when its span is narrow)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = i8 + j;
-          const bool on = i < 16 * I || (i < ny && calm);
-          y[j] = (on && i < n) ? bf2f(k[rowidx(i) * HD + c]) * sm.rk[i] * fexp(rho[c] - Gs[i][c]) : 0.f;
-        }
-        put8(YT, c, i8, y);
-      }
-      // X^T [c][rr] (q) and [c][16 + rr] (k) for rows of block I
-      for (int e = t; e < HD * 4; e += 256) {
-        const int c = e & (HD - 1), part = e >> 7;   // part: 0,1 -> q rows 0-7, 8-15; 2,3 -> k
-        const int isk = part >> 1, rr0 = (part & 1) * 8;
-        float x[8];
+        for (int nt = 0; nt < 4; ++nt) {
+          const int c = 64 * chh + 16 * nt + dcol();
+          const float rho = sm.Gref[I][c];
+          const bool on = rb < I || (rb == I && calm);
+          f32x4 y;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 16 * I + rr0 + j;
-          float v = 0.f;
-          if (r < n) {
-            const int64_t idx = rowidx(r) * HD + c;
-            v = isk ? bf2f(k[idx]) * sm.rk[r] : bf2f(q[idx]) * sm.rq[r];
-            v *= fexp(Gs[r][c] - rho[c]);
+          for (int i = 0; i < 4; ++i) y[i] = on ? EK(nt, i) * fexp(rho - eG[nt][i]) : 0.f;
+          put4(YT, c, 16 * rb + 4 * (l >> 4), y);
+          if (rb == I) {
+            f32x4 xq, xk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float e1 = fexp(eG[nt][i] - rho);
+              xq[i] = EQ(nt, i) * e1;
+              xk[i] = EK(nt, i) * e1;
+            }
+            put4(XT, c, 4 * (l >> 4), xq);
+            put4(XT, c, 16 + 4 * (l >> 4), xk);
           }
-          x[j] = v;
         }
-        put8(XT, c, 16 * isk + rr0, x);
-      }
-      // dA rows of block I, and [dA_qk^T | dA_kk^T]
-      for (int e = t; e < 16 * (CL / 8); e += 256) {
-        const int rr = e >> 3, i8 = (e & 7) * 8;
-        put8(DQ, rr, i8, &sm.dAqk[16 * I + rr][i8]);
-        put8(DK, rr, i8, &sm.dAkk[16 * I + rr][i8]);
-      }
-      for (int e = t; e < CL * 4; e += 256) {
-        const int i = e & (CL - 1), part = e >> 6;
-        const int isk = part >> 1, rr0 = (part & 1) * 8;
-        float x[8];
+        if (t < 128) {
+          const int rr = t >> 3, i8 = (t & 7) * 8;
+          put8(DQ, rr, i8, &dAqk[16 * I + rr][i8]);
+          put8(DK, rr, i8, &dAkk[16 * I + rr][i8]);
+        } else if (t < 128 + 256) {
+          const int e = t - 128, i = e & 63, part = e >> 6;   // 4 parts of 8
+          const int isk = part >> 1, rr0 = (part & 1) * 8;
+          float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 16 * I + rr0 + j;
-          x[j] = isk ? sm.dAkk[r][i] : sm.dAqk[r][i];
+          for (int jj = 0; jj < 8; ++jj)
+            x[jj] = isk ? dAkk[16 * I + rr0 + jj][i] : dAqk[16 * I + rr0 + jj][i];
+          put8(DAT, i, 16 * isk + rr0, x);
         }
-        put8(DAT, i, 16 * isk + rr0, x);
-      }
-      __syncthreads();
-      if (w == I) {
-        // row side: rows of block I
+        __syncthreads();
+        if (rb == I) {
+          f32x4 aq[4], ak[4];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          f32x4 aq = zero4(), ak = zero4();
-          mma<SPLIT_AB>(aq, DQ, 0, YT, 16 * nt, 0, nyk);
-          mma<SPLIT_AB>(ak, DK, 0, YT, 16 * nt, 0, nyk);
+          for (int nt = 0; nt < 4; ++nt) aq[nt] = ak[nt] = zero4();
+          mma_row<SPLIT_AB, 4>(aq, DQ, 0, YT, 64 * chh, 0, nyk);
+          mma_row<SPLIT_AB, 4>(ak, DK, 0, YT, 64 * chh, 0, nyk);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * I + drow(i), c = 16 * nt + dcol();
-            if (r < n) {
-              const int64_t idx = rowidx(r) * HD + c;
-              const float e1 = fexp(Gs[r][c] - rho[c]);
-              const float qh = bf2f(q[idx]) * sm.rq[r], kh = bf2f(k[idx]) * sm.rk[r];
-              const float dqa = aq[i] * e1, dka = ak[i] * e1;
+          for (int nt = 0; nt < 4; ++nt) {
+            const float rho = sm.Gref[I][64 * chh + 16 * nt + dcol()];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float e1 = fexp(eG[nt][i] - rho);
+              const float dqa = aq[nt][i] * e1, dka = ak[nt][i] * e1;
               adq[nt][i] += dqa;
               adk[nt][i] += dka;
-              adG[nt][i] += dqa * qh + dka * kh;
+              adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
             }
           }
         }
-      }
-      if (w < I || (w == I && calm)) {
-        // column side: columns i of block w from rows of block I
+        if (rb < I || (rb == I && calm)) {
+          f32x4 ac[4];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          f32x4 a = zero4();
-          mma_k<SPLIT_AB, 32>(a, DAT, 16 * w, XT, 16 * nt);
+          for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
+          mma_row<SPLIT_AB, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 0, 32);
 #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int i = 16 * w + drow(i4), c = 16 * nt + dcol();
-            if (i < n) {
-              const float kh = bf2f(k[rowidx(i) * HD + c]) * sm.rk[i];
-              const float dka = a[i4] * fexp(rho[c] - Gs[i][c]);
-              adk[nt][i4] += dka;
-              adG[nt][i4] -= dka * kh;
+          for (int nt = 0; nt < 4; ++nt) {
+            const float rho = sm.Gref[I][64 * chh + 16 * nt + dcol()];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float dka = ac[nt][i] * fexp(rho - eG[nt][i]);
+              adk[nt][i] += dka;
+              adG[nt][i] -= dka * EK(nt, i);
             }
           }
         }
+        __syncthreads();
+        if (!calm) {
+          // exact fp32 sums for the pairs inside block I
+          if (rb == I) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int rl = drow(i), c = 64 * chh + 16 * nt + dcol();
+                sm.u.p6.u.g.Gb[rl][c] = eG[nt][i];
+                sm.u.p6.u.g.qb[rl][c] = EQ(nt, i);
+                sm.u.p6.u.g.kb[rl][c] = EK(nt, i);
+              }
+          }
+          __syncthreads();
+          if (rb == I) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int rl = drow(i), r = 16 * I + rl, c = 64 * chh + 16 * nt + dcol();
+                const float gr = eG[nt][i], qr = EQ(nt, i), kr = EK(nt, i);
+                float dq_s = 0.f, dk_s = 0.f, dG_s = 0.f;
+                for (int il = 0; il <= rl; ++il) {
+                  const float kk = sm.u.p6.u.g.kb[il][c] * fexp(gr - sm.u.p6.u.g.Gb[il][c]);
+                  const float a = dAqk[r][16 * I + il], b = dAkk[r][16 * I + il];
+                  dq_s += a * kk;
+                  dk_s += b * kk;
+                  dG_s += (a * qr + b * kr) * kk;
+                }
+                for (int r2 = rl; r2 < 16; ++r2) {
+                  const float E = fexp(sm.u.p6.u.g.Gb[r2][c] - gr);
+                  const float s = (dAqk[16 * I + r2][r] * sm.u.p6.u.g.qb[r2][c] +
+                                   dAkk[16 * I + r2][r] * sm.u.p6.u.g.kb[r2][c]) * E;
+                  dk_s += s;
+                  dG_s -= s * kr;
+                }
+                adq[nt][i] += dq_s;
+                adk[nt][i] += dk_s;
+                adG[nt][i] += dG_s;
+              }
+          }
+          __syncthreads();
+        }
       }
     }
-    // Diagonal tiles of blocks whose decay span is too wide: element-wise fp32.
-    if (!sm.calm[w]) {
-      const int I = w;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int r = 16 * I + drow(i4), c = 16 * nt + dcol();
-          if (r >= n) continue;
-          const float qr = bf2f(q[rowidx(r) * HD + c]) * sm.rq[r];
-          const float kr = bf2f(k[rowidx(r) * HD + c]) * sm.rk[r];
-          float dq_s = 0.f, dk_s = 0.f, dG_s = 0.f;
-          // as a row r: pairs (r, i), i <= r
-          for (int i = 16 * I; i <= r; ++i) {
-            const float kk = bf2f(k[rowidx(i) * HD + c]) * sm.rk[i] * fexp(Gs[r][c] - Gs[i][c]);
-            const float a = sm.dAqk[r][i], b = sm.dAkk[r][i];
-            dq_s += a * kk;
-            dk_s += b * kk;
-            dG_s += (a * qr + b * kr) * kk;
-          }
-          // as a column i = r: pairs (r2, r), r2 >= r
-          for (int r2 = r; r2 < 16 * I + 16 && r2 < n; ++r2) {
-            const float E = fexp(Gs[r2][c] - Gs[r][c]);
-            const float q2 = bf2f(q[rowidx(r2) * HD + c]) * sm.rq[r2];
-            const float k2 = bf2f(k[rowidx(r2) * HD + c]) * sm.rk[r2];
-            const float s = (sm.dAqk[r2][r] * q2 + sm.dAkk[r2][r] * k2) * E;
-            dk_s += s;
-            dG_s -= s * kr;
-          }
-          adq[nt][i4] += dq_s;
-          adk[nt][i4] += dk_s;
-          adG[nt][i4] += dG_s;
-        }
-    }
-    __syncthreads();
   }
 
-  // ------------------------------------------------ P7: dg, L2 chain, outputs
+  // ------------------------------------------------------------ P7: dg, L2 chain, outputs
   {
     float (*dG)[GS_LD] = sm.u.p7.dG;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i), c = 16 * nt + dcol();
+        const int r = 16 * rb + drow(i), c = 64 * chh + 16 * nt + dcol();
         dG[r][c] = adG[nt][i] + (r == CL - 1 ? sm.dGL[c] : 0.f);
       }
-    __syncthreads();
-    if (t < HD) {
-      const int c = t;
-      float run = 0.f, pdt = 0.f, pA = 0.f;
-      const float ea = d.raw ? __expf(in.A_log[h]) : 0.f;
-      const float dtb = d.raw ? in.dt_bias[h * HD + c] : 0.f;
-      for (int r = CL - 1; r >= 0; --r) {
-        run += dG[r][c];
-        if (r < n) {
-          const int64_t idx = rowidx(r) * HD + c;
-          if (d.raw) {
-            const float z = bf2f(reinterpret_cast<const bf16*>(in.gate)[idx]) + dtb;
-            const float dz = run * (-ea) * sigmoid(z);
-            reinterpret_cast<bf16*>(out.dgate)[idx] = f2bf(dz);
-            pdt += dz;
-            pA += run * (-ea * softplus(z));
-          } else {
-            reinterpret_cast<float*>(out.dgate)[idx] = run;
-          }
-        }
-      }
-      if (d.raw) {
-        bw.part_dt[ch * HD + c] = pdt;
-        sm.u.p7.red[c] = pA;
+    const bf16* araw = reinterpret_cast<const bf16*>(in.gate);
+    if (d.raw) {
+#pragma unroll
+      for (int rep = 0; rep < 2; ++rep) {
+        const int e = t + NTHR * rep, r = e >> 4, c8 = (e & 15) * 8;
+        *reinterpret_cast<bf16x8*>(&sm.u.p7.a[r][c8]) =
+            *reinterpret_cast<const bf16x8*>(araw + rowidx(clampr(r)) * HD + c8);
       }
     }
-    __syncthreads();
-    if (d.raw && t == 0) {
-      float s = 0.f;
-      for (int c = 0; c < HD; ++c) s += sm.u.p7.red[c];
-      bw.part_A[ch] = s;
-    }
-    // L2 chain and the bf16 outputs
-    bf16* dq = reinterpret_cast<bf16*>(out.dq);
-    bf16* dk = reinterpret_cast<bf16*>(out.dk);
+    // L2 row dot products <x^, dx^> over the 128 channels
     float pq[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
     if (d.l2norm) {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + drow(i), c = 16 * nt + dcol();
-          if (r < n) {
-            const int64_t idx = rowidx(r) * HD + c;
-            pq[i] += bf2f(q[idx]) * sm.rq[r] * adq[nt][i];
-            pk[i] += bf2f(k[idx]) * sm.rk[r] * adk[nt][i];
-          }
+          pq[i] += EQ(nt, i) * adq[nt][i];
+          pk[i] += EK(nt, i) * adk[nt][i];
         }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
         for (int m = 1; m < 16; m <<= 1) {
           pq[i] += __shfl_xor(pq[i], m);
           pk[i] += __shfl_xor(pk[i], m);
         }
+      if (dcol() == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm.u.p7.rowp[0][chh][16 * rb + drow(i)] = pq[i];
+          sm.u.p7.rowp[1][chh][16 * rb + drow(i)] = pk[i];
+        }
       }
     }
+    __syncthreads();
+    // reverse cumsum within the chunk; two threads per channel (rows 32-63, 0-31)
+    const int cc = t & 127, half = (t >> 7) & 1;
+    const bool active = t < 256;
+    if (active) {
+      float run = 0.f;
+      for (int r = 32 * half + 31; r >= 32 * half; --r) {
+        run += dG[r][cc];
+        dG[r][cc] = run;
+      }
+      if (half == 1) sm.u.p7.tot[cc] = run;
+    }
+    __syncthreads();
+    float pdt = 0.f, pA = 0.f;
+    if (active) {
+      const float base = half == 0 ? sm.u.p7.tot[cc] : 0.f;
+      const float ea = d.raw ? __expf(in.A_log[h]) : 0.f;
+      const float dtb = d.raw ? in.dt_bias[h * HD + cc] : 0.f;
+      for (int r = 32 * half; r < 32 * half + 32 && r < n; ++r) {
+        const float dg = dG[r][cc] + base;
+        const int64_t idx = rowidx(r) * HD + cc;
+        if (d.raw) {
+          const float z = bf2f(sm.u.p7.a[r][cc]) + dtb;
+          const float dz = dg * (-ea) * sigmoid(z);
+          reinterpret_cast<bf16*>(out.dgate)[idx] = f2bf(dz);
+          pdt += dz;
+          pA += dg * (-ea * softplus(z));
+        } else {
+          reinterpret_cast<float*>(out.dgate)[idx] = dg;
+        }
+      }
+      sm.u.p7.red[0][half][cc] = pdt;
+      sm.u.p7.red[1][half][cc] = pA;
+    }
+    __syncthreads();
+    if (d.raw) {
+      if (t < HD) bw.part_dt[ch * HD + t] = sm.u.p7.red[0][0][t] + sm.u.p7.red[0][1][t];
+      if (t == HD) {
+        float s = 0.f;
+        for (int c2 = 0; c2 < HD; ++c2) s += sm.u.p7.red[1][0][c2] + sm.u.p7.red[1][1][c2];
+        bw.part_A[ch] = s;
+      }
+    }
+    // dq, dk (L2 chain) and dbeta
+    bf16* dq = reinterpret_cast<bf16*>(out.dq);
+    bf16* dk = reinterpret_cast<bf16*>(out.dk);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + drow(i);
+      float tq = 0.f, tk = 0.f;
+      if (d.l2norm) {
+        tq = sm.u.p7.rowp[0][0][r] + sm.u.p7.rowp[0][1][r];
+        tk = sm.u.p7.rowp[1][0][r] + sm.u.p7.rowp[1][1][r];
+      }
+      if (r < n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i), c = 16 * nt + dcol();
-        if (r < n) {
-          const int64_t idx = rowidx(r) * HD + c;
+        for (int nt = 0; nt < 4; ++nt) {
+          const int64_t idx = rowidx(r) * HD + 64 * chh + 16 * nt + dcol();
           float gq = adq[nt][i], gk = adk[nt][i];
           if (d.l2norm) {
-            const float rq = sm.rq[r], rk = sm.rk[r];
-            gq = rq * (gq - bf2f(q[idx]) * rq * pq[i]);
-            gk = rk * (gk - bf2f(k[idx]) * rk * pk[i]);
+            gq = sm.rq[r] * (gq - EQ(nt, i) * tq);
+            gk = sm.rk[r] * (gk - EK(nt, i) * tk);
           }
           dq[idx] = f2bf(gq);
           dk[idx] = f2bf(gk);
         }
       }
+    }
     if (t < n) reinterpret_cast<bf16*>(out.dbeta)[rowidx(t)] = f2bf(sm.db[t]);
   }
 }
 
+#undef EQ
+#undef EK
+
 hipError_t launch_bwd_intra(const Dims& d, const Inputs& in, const ChunkTable& ct,
                             const float* G, const SavedSet& sv, const void* dO,
                             const BwdOut& out, const BwdWork& bw, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_intra_kernel, dim3(d.NC, d.H), dim3(256), 0, s, d, in, ct, G, sv,
+  hipLaunchKernelGGL(bwd_intra_kernel, dim3(d.NC, d.H), dim3(NTHR), 0, s, d, in, ct, G, sv,
                      reinterpret_cast<const bf16*>(dO), out, bw);
   return hipGetLastError();
 }

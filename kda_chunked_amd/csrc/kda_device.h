@@ -88,6 +88,58 @@ KDA_DEV void mma_k(f32x4& acc, const Panel& A, int m0, const Panel& B, int n0) {
   }
 }
 
+// Register-blocked product over an MT x NT block of 16x16 tiles:
+// acc[mt][nt] += A[m0 + 16 mt, k0:k1] * B[n0 + 16 nt, k0:k1]^T.
+// Each fragment is read from LDS once per K step and reused across the block.
+template <int SPLIT, int MT, int NT>
+KDA_DEV void mma_blk(f32x4 (&acc)[MT][NT], const Panel& A, int m0, const Panel& B, int n0,
+                     int k0, int k1) {
+  for (int k = k0; k < k1; k += 32) {
+    bf16x8 ah[MT], al[MT], bh[NT], bl[NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      ah[mt] = frag(A.hi, A.ld, m0 + 16 * mt, k);
+      if (SPLIT & SPLIT_A) al[mt] = frag(A.lo, A.ld, m0 + 16 * mt, k);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bh[nt] = frag(B.hi, B.ld, n0 + 16 * nt, k);
+      if (SPLIT & SPLIT_B) bl[nt] = frag(B.lo, B.ld, n0 + 16 * nt, k);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (SPLIT & SPLIT_A) acc[mt][nt] = mfma16(al[mt], bh[nt], acc[mt][nt]);
+        if (SPLIT & SPLIT_B) acc[mt][nt] = mfma16(ah[mt], bl[nt], acc[mt][nt]);
+        acc[mt][nt] = mfma16(ah[mt], bh[nt], acc[mt][nt]);
+      }
+  }
+}
+
+// One row of tiles: acc[nt] += A[m0:m0+16] * B[n0 + 16 nt]^T.
+template <int SPLIT, int NT>
+KDA_DEV void mma_row(f32x4 (&acc)[NT], const Panel& A, int m0, const Panel& B, int n0, int k0,
+                     int k1) {
+  for (int k = k0; k < k1; k += 32) {
+    const bf16x8 ah = frag(A.hi, A.ld, m0, k);
+    bf16x8 al;
+    if (SPLIT & SPLIT_A) al = frag(A.lo, A.ld, m0, k);
+    bf16x8 bh[NT], bl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bh[nt] = frag(B.hi, B.ld, n0 + 16 * nt, k);
+      if (SPLIT & SPLIT_B) bl[nt] = frag(B.lo, B.ld, n0 + 16 * nt, k);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (SPLIT & SPLIT_A) acc[nt] = mfma16(al, bh[nt], acc[nt]);
+      if (SPLIT & SPLIT_B) acc[nt] = mfma16(ah, bl[nt], acc[nt]);
+      acc[nt] = mfma16(ah, bh[nt], acc[nt]);
+    }
+  }
+}
+
 // Split-store one fp32 value into a panel.
 KDA_DEV void put(const Panel& P, int row, int col, float x) {
   const bf16 h = f2bf(x);
@@ -127,6 +179,23 @@ KDA_DEV void store_tile_n(const f32x4& acc, const Panel& P, int m0, int n0) {
   const int l = lane_id();
 #pragma unroll
   for (int i = 0; i < 4; ++i) put(P, m0 + 4 * (l >> 4) + i, n0 + (l & 15), acc[i]);
+}
+
+// D tile at (m0, n0) -> panel [m][n] (row-major), hi and lo planes.
+KDA_DEV void store_tile_rowmajor(const f32x4& acc, const Panel& P, int m0, int n0) {
+  store_tile_n(acc, P, m0, n0);
+}
+
+// Split-store 4 consecutive fp32 values (8-byte aligned destination).
+KDA_DEV void put4(const Panel& P, int row, int col, f32x4 x) {
+  bf16x4 h, w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = f2bf(x[i]);
+    w[i] = f2bf(x[i] - bf2f(h[i]));
+  }
+  *reinterpret_cast<bf16x4*>(P.hi + row * P.ld + col) = h;
+  if (P.lo) *reinterpret_cast<bf16x4*>(P.lo + row * P.ld + col) = w;
 }
 
 // Row / column of element i (0..3) of this lane's D tile.
