@@ -16,22 +16,46 @@
 // walk on PR #7176, opening section) and walks the document's chunks in
 // order; the 4 tiles of a head are mapped to one XCD so that they share the
 // chunk operands through that XCD's L2.
+//
+// Pipelining: the raw inputs of the next chunk (q, k, G, v, T, A_qk, ...)
+// are loaded into registers while the current chunk's products run, so the
+// only memory latency on the sequential path is the first chunk's.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
+constexpr int NT_SCAN = 512;        // threads per scan workgroup (8 waves)
 constexpr int VT = 32;              // state columns per workgroup
 constexpr int NTILE = HD / VT;      // workgroups per (document, head)
 constexpr int K1_LD = HD + 8;       // panels with K = 128
 constexpr int K2_LD = CL + 8;       // panels with K = 64
 
-// Split terms per product (see the precision notes in the design document).
-constexpr int SPLIT_KS = SPLIT_AB;   // Kd S
-constexpr int SPLIT_TR = SPLIT_AB;   // Tb R
-constexpr int SPLIT_QS = SPLIT_AB;   // Qd S
-constexpr int SPLIT_AU = SPLIT_AB;   // A_qk U~
-constexpr int SPLIT_KU = SPLIT_AB;   // Ke^T U~
+// Split terms per product (SPLIT_A: first operand carries its lo part, ...).
+#ifndef KDA_SPLIT_KS
+#define KDA_SPLIT_KS SPLIT_AB
+#endif
+#ifndef KDA_SPLIT_TR
+#define KDA_SPLIT_TR SPLIT_AB
+#endif
+#ifndef KDA_SPLIT_QS
+#define KDA_SPLIT_QS SPLIT_AB
+#endif
+#ifndef KDA_SPLIT_AU
+#define KDA_SPLIT_AU SPLIT_AB
+#endif
+#ifndef KDA_SPLIT_KU
+#define KDA_SPLIT_KU SPLIT_AB
+#endif
+#ifndef KDA_SPLIT_BW
+#define KDA_SPLIT_BW SPLIT_AB
+#endif
+constexpr int SPLIT_KS = KDA_SPLIT_KS;   // Kd S          (forward)
+constexpr int SPLIT_TR = KDA_SPLIT_TR;   // Tb R          (forward)
+constexpr int SPLIT_QS = KDA_SPLIT_QS;   // Qd S          (forward)
+constexpr int SPLIT_AU = KDA_SPLIT_AU;   // A_qk U~       (forward)
+constexpr int SPLIT_KU = KDA_SPLIT_KU;   // Ke^T U~       (forward)
+constexpr int SPLIT_BW = KDA_SPLIT_BW;   // reverse-scan products with two computed operands
 
 // blockIdx -> (pair = document * H + head, tile). Consecutive workgroups are
 // dealt to the 8 XCDs round robin; the 4 tiles of a pair get ids 8 apart.
@@ -43,6 +67,8 @@ KDA_DEV bool scan_coords(int P, int& pair, int& tile) {
 }
 
 static int scan_grid(int P) { return ((P + 7) / 8) * 8 * NTILE; }
+
+KDA_DEV float bsel(bool ok, bf16 x) { return ok ? bf2f(x) : 0.f; }
 
 // ------------------------------------------------------------------ forward
 struct FwdScanSmem {
@@ -57,27 +83,44 @@ struct FwdScanSmem {
   bf16 rr_hi[VT][K2_LD], rr_lo[VT][K2_LD];                 // R^T [j][r]
   bf16 u_hi[VT][K2_LD], u_lo[VT][K2_LD];                   // U~^T [j][r]
   float gam[HD];
-  float GL[HD];
   float rk[CL], rq[CL], beta[CL];
 };
 
-__global__ __launch_bounds__(256) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                        const float* __restrict__ G,
-                                                        SavedSet sv, bf16* __restrict__ o,
-                                                        int save) {
+// Registers holding one chunk's raw inputs for this thread.
+struct FwdPref {
+  bf16x8 k0, k1, q0, q1;     // row rA = t>>3, channels cA .. cA+15 (cA = 16*(t&7))
+  f32x4 g[4];                // G at the same elements
+  f32x4 T0, T1, A0, A1;      // T and A_qk: row rA, columns 8*(t&7) .. +7
+  bf16x8 kt[2];              // k at channel cB = t&127, rows 16*(t>>7) .. +15
+  float gt[16];              // G at the same elements
+  float gl;                  // G_last[cB]
+  bf16 v[4];                 // V at this lane's R-tile elements
+  float sb, sq, sk;          // beta, rq, rk of row t (t < 64)
+  int64_t t0;
+  int n;
+};
+
+__global__ __launch_bounds__(NT_SCAN) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
+                                                            const float* __restrict__ G,
+                                                            SavedSet sv, bf16* __restrict__ o,
+                                                            int save) {
   __shared__ FwdScanSmem sm;
   int pair, tile;
   if (!scan_coords(d.N * d.H, pair, tile)) return;
   const int doc = pair / d.H, h = pair % d.H;
   const int c0 = ct.doc_c0[doc], c1 = ct.doc_c0[doc + 1];
   const int t = threadIdx.x, w = wave_id();
+  const int rb = w & 3, nw = w >> 2;       // R / U~ / O tile of this wave: rows 16 rb, cols 16 nw
   const int j0 = tile * VT;
+  const int H = d.H;
   const bf16* q = reinterpret_cast<const bf16*>(in.q);
   const bf16* k = reinterpret_cast<const bf16*>(in.k);
   const bf16* v = reinterpret_cast<const bf16*>(in.v);
   const bf16* beta = reinterpret_cast<const bf16*>(in.beta);
+  const int rA = t >> 3, cA = 16 * (t & 7), i8 = 8 * (t & 7);
+  const int cB = t & 127, rB = 16 * (t >> 7);
 
-  const Panel KD{&sm.r1.kd.hi[0][0], &sm.r1.kd.lo[0][0], K1_LD};
+  const Panel KD{&sm.r1.kd.hi[0][0], (SPLIT_KS & SPLIT_A) ? &sm.r1.kd.lo[0][0] : nullptr, K1_LD};
   const Panel KE{&sm.r1.ke.hi[0][0], &sm.r1.ke.lo[0][0], K2_LD};
   const Panel QD{&sm.qd_hi[0][0], &sm.qd_lo[0][0], K1_LD};
   const Panel TB{&sm.tb_hi[0][0], &sm.tb_lo[0][0], K2_LD};
@@ -86,166 +129,169 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(Dims d, Inputs in, ChunkT
   const Panel RP{&sm.rr_hi[0][0], &sm.rr_lo[0][0], K2_LD};
   const Panel UP{&sm.u_hi[0][0], &sm.u_lo[0][0], K2_LD};
 
-  // state tile: wave w owns state rows [32w, 32w+32) x 32 columns
-  f32x4 S[2][2];
+  FwdPref pf;
+  auto prefetch_main = [&](int cn) {
+    pf.t0 = ct.tok[cn];
+    pf.n = ct.len[cn];
+    const int64_t ch = (int64_t)cn * H + h;
+    const int r = rA < pf.n ? rA : pf.n - 1;
+    const int64_t base = ((pf.t0 + r) * H + h) * HD + cA;
+    pf.k0 = *reinterpret_cast<const bf16x8*>(k + base);
+    pf.k1 = *reinterpret_cast<const bf16x8*>(k + base + 8);
+    pf.q0 = *reinterpret_cast<const bf16x8*>(q + base);
+    pf.q1 = *reinterpret_cast<const bf16x8*>(q + base + 8);
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int j = 0; j < 4; ++j) pf.g[j] = *reinterpret_cast<const f32x4*>(G + base + 4 * j);
+    const float* Tr = sv.Tm + ch * CL * CL + rA * CL + i8;
+    const float* Ar = sv.Aqk + ch * CL * CL + rA * CL + i8;
+    pf.T0 = *reinterpret_cast<const f32x4*>(Tr);
+    pf.T1 = *reinterpret_cast<const f32x4*>(Tr + 4);
+    pf.A0 = *reinterpret_cast<const f32x4*>(Ar);
+    pf.A1 = *reinterpret_cast<const f32x4*>(Ar + 4);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) S[a][b] = zero4();
-  for (int e = t; e < VT * K1_LD; e += 256) {
-    sm.s_hi[0][e] = f2bf(0.f);
-    sm.s_lo[0][e] = f2bf(0.f);
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 16 * rb + drow(i), rc = rr < pf.n ? rr : pf.n - 1;
+      pf.v[i] = v[((pf.t0 + rc) * H + h) * HD + j0 + 16 * nw + dcol()];
+    }
+    if (t < CL) {
+      const int rt = t < pf.n ? t : pf.n - 1;
+      const int64_t ri = (pf.t0 + rt) * H + h;
+      pf.sb = bf2f(beta[ri]);
+      pf.sq = sv.rq[ri];
+      pf.sk = sv.rk[ri];
+    }
+  };
+  auto prefetch_ke = [&](int cn) {
+    const int64_t tt = ct.tok[cn];
+    const int nn = ct.len[cn];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = rB + j, rc = r < nn ? r : nn - 1;
+      const int64_t idx = ((tt + rc) * H + h) * HD + cB;
+      pf.kt[j >> 3][j & 7] = k[idx];
+      pf.gt[j] = G[idx];
+    }
+    pf.gl = G[((tt + nn - 1) * H + h) * HD + cB];
+  };
+
+  // state: wave w owns state rows [16w, 16w+16) x 32 columns
+  f32x4 S[2];
+  S[0] = S[1] = zero4();
+  for (int e = t; e < VT * K1_LD; e += NT_SCAN) {
+    (&sm.s_hi[0][0])[e] = f2bf(0.f);
+    (&sm.s_lo[0][0])[e] = f2bf(0.f);
+  }
+  if (c0 < c1) {
+    prefetch_main(c0);
+    prefetch_ke(c0);
   }
 
   for (int ci = c0; ci < c1; ++ci) {
-    const int64_t t0 = ct.tok[ci];
-    const int n = ct.len[ci];
-    const int64_t ch = (int64_t)ci * d.H + h;
-    __syncthreads();
-    // ---- A. chunk operands
+    const int64_t t0 = pf.t0;
+    const int n = pf.n;
+    const int64_t ch = (int64_t)ci * H + h;
+    // ---- A. small vectors and the panels that do not depend on R
     if (t < CL) {
-      const bool in_chunk = t < n;
-      sm.rk[t] = in_chunk ? sv.rk[(t0 + t) * d.H + h] : 0.f;
-      sm.rq[t] = in_chunk ? sv.rq[(t0 + t) * d.H + h] : 0.f;
-      sm.beta[t] = in_chunk ? bf2f(beta[(t0 + t) * d.H + h]) : 0.f;
-    } else if (t < CL + HD) {
-      const int c = t - CL;
-      const float gl = G[((t0 + n - 1) * d.H + h) * HD + c];
-      sm.GL[c] = gl;
-      sm.gam[c] = fexp(gl);
+      const bool ok = t < n;
+      sm.beta[t] = ok ? pf.sb : 0.f;
+      sm.rq[t] = ok ? pf.sq : 0.f;
+      sm.rk[t] = ok ? pf.sk : 0.f;
     }
+    if (t < HD) sm.gam[t] = fexp(pf.gl);   // thread t < 128 has cB = t
     __syncthreads();
-    for (int e = t; e < CL * (HD / 8); e += 256) {
-      const int r = e >> 4, c8 = (e & 15) * 8;
-      float kd[8], qd[8];
-      if (r < n) {
-        const int64_t base = ((t0 + r) * d.H + h) * HD + c8;
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(k + base);
-        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(q + base);
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(G + base);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(G + base + 4);
+    {
+      const bool ok = rA < n;
+      const float rk = sm.rk[rA], rq = sm.rq[rA];
+      float kd[16], qd[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e1 = fexp(j < 4 ? g0[j] : g1[j - 4]);
-          kd[j] = -bf2f(kv[j]) * sm.rk[r] * e1;
-          qd[j] = bf2f(qv[j]) * sm.rq[r] * e1 * d.scale;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kd[j] = qd[j] = 0.f;
+      for (int j = 0; j < 16; ++j) {
+        const float e1 = fexp(pf.g[j >> 2][j & 3]);
+        const bf16 kb = j < 8 ? pf.k0[j] : pf.k1[j - 8];
+        const bf16 qb = j < 8 ? pf.q0[j] : pf.q1[j - 8];
+        kd[j] = ok ? -bf2f(kb) * rk * e1 : 0.f;
+        qd[j] = ok ? bf2f(qb) * rq * e1 * d.scale : 0.f;
       }
-      put8(KD, r, c8, kd);
-      put8(QD, r, c8, qd);
-    }
-    for (int e = t; e < CL * (CL / 8); e += 256) {
-      const int r = e >> 3, i8 = (e & 7) * 8;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(sv.Tm + ch * CL * CL + r * CL + i8);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(sv.Tm + ch * CL * CL + r * CL + i8 + 4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(sv.Aqk + ch * CL * CL + r * CL + i8);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(sv.Aqk + ch * CL * CL + r * CL + i8 + 4);
+      put8(KD, rA, cA, kd);
+      put8(KD, rA, cA + 8, kd + 8);
+      put8(QD, rA, cA, qd);
+      put8(QD, rA, cA + 8, qd + 8);
       float tb[8], aq[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        tb[j] = (j < 4 ? a0[j] : a1[j - 4]) * sm.beta[i8 + j];
-        aq[j] = (j < 4 ? b0[j] : b1[j - 4]) * d.scale;
+        tb[j] = (j < 4 ? pf.T0[j] : pf.T1[j - 4]) * sm.beta[i8 + j];
+        aq[j] = (j < 4 ? pf.A0[j] : pf.A1[j - 4]) * d.scale;
       }
-      put8(TB, r, i8, tb);
-      put8(AQ, r, i8, aq);
+      put8(TB, rA, i8, tb);
+      put8(AQ, rA, i8, aq);
     }
-    // V tile as the accumulator of R = V - Kd S (wave w: rows 16w.., 2 column tiles)
-    f32x4 R[2];
+    f32x4 R;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int i = 0; i < 4; ++i) R[i] = bsel(16 * rb + drow(i) < n, pf.v[i]);
+    if (ci + 1 < c1) prefetch_main(ci + 1);
+    __syncthreads();
+    // ---- B. R = V - Kd S_in (tile rows 16 rb, cols 16 nw)
+    mma_k<SPLIT_KS, HD>(R, KD, 16 * rb, SP, 16 * nw);
+    if (save) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i);
-        R[nt][i] = r < n ? bf2f(v[((t0 + r) * d.H + h) * HD + j0 + 16 * nt + dcol()]) : 0.f;
+        const int r = 16 * rb + drow(i);
+        if (r < n) sv.R[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = R[i];
       }
-    __syncthreads();
-    // ---- B. R = V - Kd S_in
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      mma_k<SPLIT_KS, HD>(R[nt], KD, 16 * w, SP, 16 * nt);
-      if (save) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + drow(i);
-          if (r < n) sv.R[((t0 + r) * d.H + h) * HD + j0 + 16 * nt + dcol()] = R[nt][i];
-        }
-      }
-      store_tile_t(R[nt], RP, 16 * w, 16 * nt);
-    }
-    if (save) {
-      // S_in of this chunk
       float* Sg = sv.S_in + ch * HD * HD;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            Sg[(32 * w + 16 * mt + drow(i)) * HD + j0 + 16 * nt + dcol()] = S[mt][nt][i];
+        for (int i = 0; i < 4; ++i)
+          Sg[(16 * w + drow(i)) * HD + j0 + 16 * nt + dcol()] = S[nt][i];
     }
+    store_tile_t(R, RP, 16 * rb, 16 * nw);
     __syncthreads();
-    // ---- C. U~ = Tb R; then Ke^T into the Kd space
-    const int kend = ((16 * w + 16 + 31) / 32) * 32;
-    f32x4 U[2];
+    // ---- C. U~ = Tb R; Ke^T into the Kd space
+    const int kend = ((16 * rb + 16 + 31) / 32) * 32;
+    f32x4 U = zero4();
+    mma<SPLIT_TR>(U, TB, 16 * rb, RP, 16 * nw, 0, kend);
+    store_tile_t(U, UP, 16 * rb, 16 * nw);
+    {
+      const float gl = pf.gl;
+      float ke[16];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      U[nt] = zero4();
-      mma<SPLIT_TR>(U[nt], TB, 16 * w, RP, 16 * nt, 0, kend);
-      store_tile_t(U[nt], UP, 16 * w, 16 * nt);
-    }
-    for (int e = t; e < HD * (CL / 8); e += 256) {
-      const int c = e & (HD - 1), r8 = (e >> 7) * 8;
-      float ke[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = r8 + j;
-        if (r < n) {
-          const int64_t idx = ((t0 + r) * d.H + h) * HD + c;
-          ke[j] = bf2f(k[idx]) * sm.rk[r] * fexp(sm.GL[c] - G[idx]);
-        } else {
-          ke[j] = 0.f;
-        }
+      for (int j = 0; j < 16; ++j) {
+        const int r = rB + j;
+        ke[j] = r < n ? bf2f(pf.kt[j >> 3][j & 7]) * sm.rk[r] * fexp(gl - pf.gt[j]) : 0.f;
       }
-      put8(KE, c, r8, ke);
+      put8(KE, cB, rB, ke);
+      put8(KE, cB, rB + 8, ke + 8);
     }
+    if (ci + 1 < c1) prefetch_ke(ci + 1);
     __syncthreads();
     // ---- D. O = scale (Qd S_in + A_qk U~)   (skipped when replaying)
-#pragma unroll
-    for (int nt = 0; nt < 2 && o != nullptr; ++nt) {
+    if (o != nullptr) {
       f32x4 acc = zero4();
-      mma_k<SPLIT_QS, HD>(acc, QD, 16 * w, SP, 16 * nt);
-      mma<SPLIT_AU>(acc, AQ, 16 * w, UP, 16 * nt, 0, kend);
+      mma_k<SPLIT_QS, HD>(acc, QD, 16 * rb, SP, 16 * nw);
+      mma<SPLIT_AU>(acc, AQ, 16 * rb, UP, 16 * nw, 0, kend);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i);
-        if (r < n) o[((t0 + r) * d.H + h) * HD + j0 + 16 * nt + dcol()] = f2bf(acc[i]);
+        const int r = 16 * rb + drow(i);
+        if (r < n) o[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = f2bf(acc[i]);
       }
     }
     // ---- E. S_out = Diag(e^G_last) S_in + Ke^T U~
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[mt][nt][i] *= sm.gam[32 * w + 16 * mt + drow(i)];
-        mma_k<SPLIT_KU, CL>(S[mt][nt], KE, 32 * w + 16 * mt, UP, 16 * nt);
-      }
+      for (int i = 0; i < 4; ++i) S[nt][i] *= sm.gam[16 * w + drow(i)];
+    mma_row<SPLIT_KU, 2>(S, KE, 16 * w, UP, 0, 0, CL);
     __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) store_tile_t(S[mt][nt], SP, 32 * w + 16 * mt, 16 * nt);
+    for (int nt = 0; nt < 2; ++nt) store_tile_t(S[nt], SP, 16 * w, 16 * nt);
   }
 }
 
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const float* G, const SavedSet& sv, void* o, int save_states,
                            hipStream_t s) {
-  hipLaunchKernelGGL(fwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(256), 0, s, d, in, ct,
-                     G, sv, reinterpret_cast<bf16*>(o), save_states);
+  hipLaunchKernelGGL(fwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(NT_SCAN), 0, s, d, in,
+                     ct, G, sv, reinterpret_cast<bf16*>(o), save_states);
   return hipGetLastError();
 }
 
@@ -267,21 +313,40 @@ struct BwdScanSmem {
   float rk[CL], rq[CL], beta[CL];
 };
 
-__global__ __launch_bounds__(256) void bwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                        const float* __restrict__ G,
-                                                        SavedSet sv,
-                                                        const bf16* __restrict__ dO,
-                                                        bf16* __restrict__ dv, BwdWork bw) {
+struct BwdPref {
+  bf16x8 k0, k1;             // row rA, channels cA .. cA+15 (for Ke)
+  f32x4 g[4];
+  float at[8], tt[8];        // A_qk and T at rows 8*(t>>6) .. +7, column t&63
+  bf16x8 qt[2], kt[2];       // q, k at channel cB, rows rB .. rB+15 (for Qd^T, Kd^T)
+  float gt[16];
+  float gl;                  // G_last of channel cB
+  bf16 dov[4];               // dO^T tile: column t&31, rows 4*(t>>5) .. +3
+  float sb, sq, sk;
+  int64_t t0;
+  int n;
+};
+
+__global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
+                                                            const float* __restrict__ G,
+                                                            SavedSet sv,
+                                                            const bf16* __restrict__ dO,
+                                                            bf16* __restrict__ dv, BwdWork bw) {
   __shared__ BwdScanSmem sm;
   int pair, tile;
   if (!scan_coords(d.N * d.H, pair, tile)) return;
   const int doc = pair / d.H, h = pair % d.H;
   const int c0 = ct.doc_c0[doc], c1 = ct.doc_c0[doc + 1];
   const int t = threadIdx.x, w = wave_id();
+  const int rb = w & 3, nw = w >> 2;
   const int j0 = tile * VT;
+  const int H = d.H;
   const bf16* q = reinterpret_cast<const bf16*>(in.q);
   const bf16* k = reinterpret_cast<const bf16*>(in.k);
   const bf16* beta = reinterpret_cast<const bf16*>(in.beta);
+  const int rA = t >> 3, cA = 16 * (t & 7);
+  const int cB = t & 127, rB = 16 * (t >> 7);
+  const int iC = t & 63, rC = 8 * (t >> 6);
+  const int jD = t & 31, rD = 4 * (t >> 5);
 
   const Panel KE{&sm.r1.ke.hi[0][0], &sm.r1.ke.lo[0][0], K1_LD};
   const Panel QD{&sm.r1.qd.hi[0][0], &sm.r1.qd.lo[0][0], K2_LD};
@@ -293,148 +358,166 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(Dims d, Inputs in, ChunkT
   const Panel DU{&sm.du_hi[0][0], &sm.du_lo[0][0], K2_LD};
   const Panel DR{&sm.dr_hi[0][0], &sm.dr_lo[0][0], K2_LD};
 
-  f32x4 dS[2][2];
+  BwdPref pf;
+  auto prefetch_main = [&](int cn) {
+    pf.t0 = ct.tok[cn];
+    pf.n = ct.len[cn];
+    const int64_t ch = (int64_t)cn * H + h;
+    const int r = rA < pf.n ? rA : pf.n - 1;
+    const int64_t base = ((pf.t0 + r) * H + h) * HD + cA;
+    pf.k0 = *reinterpret_cast<const bf16x8*>(k + base);
+    pf.k1 = *reinterpret_cast<const bf16x8*>(k + base + 8);
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int j = 0; j < 4; ++j) pf.g[j] = *reinterpret_cast<const f32x4*>(G + base + 4 * j);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) dS[a][b] = zero4();
-  for (int e = t; e < VT * K1_LD; e += 256) {
-    sm.ds_hi[0][e] = f2bf(0.f);
-    sm.ds_lo[0][e] = f2bf(0.f);
+    for (int j = 0; j < 8; ++j) {
+      pf.at[j] = sv.Aqk[ch * CL * CL + (rC + j) * CL + iC];
+      pf.tt[j] = sv.Tm[ch * CL * CL + (rC + j) * CL + iC];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = rD + j, rc = rr < pf.n ? rr : pf.n - 1;
+      pf.dov[j] = dO[((pf.t0 + rc) * H + h) * HD + j0 + jD];
+    }
+    if (t < CL) {
+      const int rt = t < pf.n ? t : pf.n - 1;
+      const int64_t ri = (pf.t0 + rt) * H + h;
+      pf.sb = bf2f(beta[ri]);
+      pf.sq = sv.rq[ri];
+      pf.sk = sv.rk[ri];
+    }
+    pf.gl = G[((pf.t0 + pf.n - 1) * H + h) * HD + cB];
+  };
+  auto prefetch_t = [&](int cn) {
+    const int64_t tt = ct.tok[cn];
+    const int nn = ct.len[cn];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = rB + j, rc = r < nn ? r : nn - 1;
+      const int64_t idx = ((tt + rc) * H + h) * HD + cB;
+      pf.qt[j >> 3][j & 7] = q[idx];
+      pf.kt[j >> 3][j & 7] = k[idx];
+      pf.gt[j] = G[idx];
+    }
+  };
+
+  f32x4 dS[2];
+  dS[0] = dS[1] = zero4();
+  for (int e = t; e < VT * K1_LD; e += NT_SCAN) {
+    (&sm.ds_hi[0][0])[e] = f2bf(0.f);
+    (&sm.ds_lo[0][0])[e] = f2bf(0.f);
+  }
+  if (c0 < c1) {
+    prefetch_main(c1 - 1);
+    prefetch_t(c1 - 1);
   }
 
   for (int ci = c1 - 1; ci >= c0; --ci) {
-    const int64_t t0 = ct.tok[ci];
-    const int n = ct.len[ci];
-    const int64_t ch = (int64_t)ci * d.H + h;
-    __syncthreads();
+    const int64_t t0 = pf.t0;
+    const int n = pf.n;
+    const int64_t ch = (int64_t)ci * H + h;
     // ---- A. operands
     if (t < CL) {
-      const bool in_chunk = t < n;
-      sm.rk[t] = in_chunk ? sv.rk[(t0 + t) * d.H + h] : 0.f;
-      sm.rq[t] = in_chunk ? sv.rq[(t0 + t) * d.H + h] : 0.f;
-      sm.beta[t] = in_chunk ? bf2f(beta[(t0 + t) * d.H + h]) : 0.f;
-    } else if (t < CL + HD) {
-      const int c = t - CL;
-      const float gl = G[((t0 + n - 1) * d.H + h) * HD + c];
-      sm.GL[c] = gl;
-      sm.gam[c] = fexp(gl);
+      const bool ok = t < n;
+      sm.beta[t] = ok ? pf.sb : 0.f;
+      sm.rq[t] = ok ? pf.sq : 0.f;
+      sm.rk[t] = ok ? pf.sk : 0.f;
+    }
+    if (t < HD) {
+      sm.GL[t] = pf.gl;
+      sm.gam[t] = fexp(pf.gl);
     }
     __syncthreads();
-    for (int e = t; e < CL * (HD / 8); e += 256) {
-      const int r = e >> 4, c8 = (e & 15) * 8;
-      float ke[8];
-      if (r < n) {
-        const int64_t base = ((t0 + r) * d.H + h) * HD + c8;
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(k + base);
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(G + base);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(G + base + 4);
+    {
+      const bool ok = rA < n;
+      const float rk = sm.rk[rA];
+      float ke[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          ke[j] = bf2f(kv[j]) * sm.rk[r] * fexp(sm.GL[c8 + j] - (j < 4 ? g0[j] : g1[j - 4]));
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ke[j] = 0.f;
+      for (int j = 0; j < 16; ++j) {
+        const bf16 kb = j < 8 ? pf.k0[j] : pf.k1[j - 8];
+        ke[j] = ok ? bf2f(kb) * rk * fexp(sm.GL[cA + j] - pf.g[j >> 2][j & 3]) : 0.f;
       }
-      put8(KE, r, c8, ke);
-    }
-    // A_qk^T and Tb^T: transposed loads, 8 rows r per task
-    for (int e = t; e < CL * (CL / 8); e += 256) {
-      const int i = e & (CL - 1), r8 = (e >> 6) * 8;
+      put8(KE, rA, cA, ke);
+      put8(KE, rA, cA + 8, ke + 8);
       float aq[8], tb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int r = r8 + j;
-        aq[j] = sv.Aqk[ch * CL * CL + r * CL + i] * d.scale;
-        tb[j] = sv.Tm[ch * CL * CL + r * CL + i] * sm.beta[i];
+        aq[j] = pf.at[j] * d.scale;
+        tb[j] = pf.tt[j] * sm.beta[iC];
       }
-      put8(AQ, i, r8, aq);
-      put8(TB, i, r8, tb);
-    }
-    // dO^T tile [j][r]
-    for (int e = t; e < VT * CL; e += 256) {
-      const int j = e & (VT - 1), r = e >> 5;
-      sm.do_hi[j][r] = r < n ? dO[((t0 + r) * d.H + h) * HD + j0 + j] : f2bf(0.f);
-    }
-    __syncthreads();
-    // ---- B. dU~ = scale A_qk^T dO + Ke dS_out   (rows = token i of the chunk)
+      put8(AQ, iC, rC, aq);
+      put8(TB, iC, rC, tb);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+      for (int j = 0; j < 4; ++j)
+        sm.do_hi[jD][rD + j] = (rD + j < n) ? pf.dov[j] : f2bf(0.f);
+    }
+    if (ci - 1 >= c0) prefetch_main(ci - 1);
+    __syncthreads();
+    // ---- B. dU~ = scale A_qk^T dO + Ke dS_out   (tile rows 16 rb, cols 16 nw)
+    f32x4 dU = zero4();
+    mma<SPLIT_A>(dU, AQ, 16 * rb, DO, 16 * nw, (16 * rb / 32) * 32, CL);
+    mma_k<SPLIT_BW, HD>(dU, KE, 16 * rb, DS, 16 * nw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + drow(i);
+      if (r < n) bw.dU[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = dU[i];
+    }
+    store_tile_t(dU, DU, 16 * rb, 16 * nw);
+    __syncthreads();
+    // ---- C. dR = Tb^T dU~ (= dv); Qd^T and -Kd^T panels
+    {
       f32x4 acc = zero4();
-      mma<SPLIT_A>(acc, AQ, 16 * w, DO, 16 * nt, 0, CL);
-      mma_k<SPLIT_AB, HD>(acc, KE, 16 * w, DS, 16 * nt);
+      mma<SPLIT_BW>(acc, TB, 16 * rb, DU, 16 * nw, (16 * rb / 32) * 32, CL);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i);
-        if (r < n) bw.dU[((t0 + r) * d.H + h) * HD + j0 + 16 * nt + dcol()] = acc[i];
+        const int r = 16 * rb + drow(i);
+        if (r < n) dv[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = f2bf(acc[i]);
       }
-      store_tile_t(acc, DU, 16 * w, 16 * nt);
+      store_tile_t(acc, DR, 16 * rb, 16 * nw);
     }
-    __syncthreads();
-    // ---- C. dR = Tb^T dU~  (= dv); then the Qd^T / -Kd^T panels
     {
-      const int kbeg = (16 * w / 32) * 32;
+      float qd[16], kd[16];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4 acc = zero4();
-        mma<SPLIT_AB>(acc, TB, 16 * w, DU, 16 * nt, kbeg, CL);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + drow(i);
-          if (r < n) dv[((t0 + r) * d.H + h) * HD + j0 + 16 * nt + dcol()] = f2bf(acc[i]);
-        }
-        store_tile_t(acc, DR, 16 * w, 16 * nt);
+      for (int j = 0; j < 16; ++j) {
+        const int r = rB + j;
+        const bool ok = r < n;
+        const float e1 = fexp(pf.gt[j]);
+        qd[j] = ok ? bf2f(pf.qt[j >> 3][j & 7]) * sm.rq[r] * e1 * d.scale : 0.f;
+        kd[j] = ok ? -bf2f(pf.kt[j >> 3][j & 7]) * sm.rk[r] * e1 : 0.f;
       }
+      put8(QD, cB, rB, qd);
+      put8(QD, cB, rB + 8, qd + 8);
+      put8(KD, cB, rB, kd);
+      put8(KD, cB, rB + 8, kd + 8);
     }
-    for (int e = t; e < HD * (CL / 8); e += 256) {
-      const int c = e & (HD - 1), r8 = (e >> 7) * 8;
-      float qd[8], kd[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = r8 + j;
-        if (r < n) {
-          const int64_t idx = ((t0 + r) * d.H + h) * HD + c;
-          const float e1 = fexp(G[idx]);
-          qd[j] = bf2f(q[idx]) * sm.rq[r] * e1 * d.scale;
-          kd[j] = -bf2f(k[idx]) * sm.rk[r] * e1;
-        } else {
-          qd[j] = kd[j] = 0.f;
-        }
-      }
-      put8(QD, c, r8, qd);
-      put8(KD, c, r8, kd);
-    }
+    if (ci - 1 >= c0) prefetch_t(ci - 1);
     __syncthreads();
     // ---- D. dS_in = Diag(e^G_last) dS_out + scale Qd^T dO - Kd^T dR
     {
       float* dSg = bw.dS + ch * HD * HD;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = 32 * w + 16 * mt + drow(i);
-            dSg[c * HD + j0 + 16 * nt + dcol()] = dS[mt][nt][i];
-            dS[mt][nt][i] *= sm.gam[c];
-          }
-          mma<SPLIT_A>(dS[mt][nt], QD, 32 * w + 16 * mt, DO, 16 * nt, 0, CL);
-          mma_k<SPLIT_AB, CL>(dS[mt][nt], KD, 32 * w + 16 * mt, DR, 16 * nt);
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * w + drow(i);
+          dSg[c * HD + j0 + 16 * nt + dcol()] = dS[nt][i];
+          dS[nt][i] *= sm.gam[c];
         }
+      mma_row<SPLIT_A, 2>(dS, QD, 16 * w, DO, 0, 0, CL);
+      mma_row<SPLIT_BW, 2>(dS, KD, 16 * w, DR, 0, 0, CL);
     }
     __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) store_tile_t(dS[mt][nt], DS, 32 * w + 16 * mt, 16 * nt);
+    for (int nt = 0; nt < 2; ++nt) store_tile_t(dS[nt], DS, 16 * w, 16 * nt);
   }
 }
 
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const float* G, const SavedSet& sv, const void* dO, void* dv,
                            const BwdWork& bw, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(256), 0, s, d, in, ct, G,
-                     sv, reinterpret_cast<const bf16*>(dO), reinterpret_cast<bf16*>(dv), bw);
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(NT_SCAN), 0, s, d, in,
+                     ct, G, sv, reinterpret_cast<const bf16*>(dO), reinterpret_cast<bf16*>(dv),
+                     bw);
   return hipGetLastError();
 }
 
