@@ -41,6 +41,29 @@ constexpr int GS_LD = HD + 4;
 constexpr int F_LD = CL + 1;        // fp32 64x64 matrices
 constexpr float CALM_SPAN_B = 40.f;
 
+// Split terms per product (SPLIT_A: first operand carries its lo part, ...).
+#ifndef KDA_SPLIT_B1
+#define KDA_SPLIT_B1 SPLIT_B     // U~ = Tb R, dR = Tb^T dU~
+#endif
+#ifndef KDA_SPLIT_B2
+#define KDA_SPLIT_B2 SPLIT_B     // dKd = dR S_in^T
+#endif
+#ifndef KDA_SPLIT_B3
+#define KDA_SPLIT_B3 SPLIT_B     // dQd = dO S_in^T (dO exact)
+#endif
+#ifndef KDA_SPLIT_B4
+#define KDA_SPLIT_B4 SPLIT_AB    // dKe = U~ dS_out^T
+#endif
+#ifndef KDA_SPLIT_B5
+#define KDA_SPLIT_B5 SPLIT_B     // dA_qk = dO U~^T (dO exact)
+#endif
+#ifndef KDA_SPLIT_B6
+#define KDA_SPLIT_B6 SPLIT_AB    // dTb = dU~ R^T
+#endif
+#ifndef KDA_SPLIT_B7
+#define KDA_SPLIT_B7 SPLIT_AB    // decayed-product backward: dA Y, dA^T X
+#endif
+
 struct BwdIntraSmem {
   union {
     struct {
@@ -180,7 +203,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   // ------------------------------------------------------------ P1: U~ and dR
   f32x4 U[4], dR[4];
   {
-    const Panel A{&sm.u.p1.a_hi[0][0], &sm.u.p1.a_lo[0][0], K2_LD};
+    const Panel A{&sm.u.p1.a_hi[0][0], (KDA_SPLIT_B1 & SPLIT_A) ? &sm.u.p1.a_lo[0][0] : nullptr, K2_LD};
     const Panel B{&sm.u.p1.b_hi[0][0], &sm.u.p1.b_lo[0][0], K2_LD};
     // Tb [r][i]
     {
@@ -212,7 +235,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     const int kend = ((16 * rb + 16 + 31) / 32) * 32;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) U[nt] = zero4();
-    mma_row<SPLIT_AB, 4>(U, A, 16 * rb, B, 64 * chh, 0, kend);
+    mma_row<KDA_SPLIT_B1, 4>(U, A, 16 * rb, B, 64 * chh, 0, kend);
     __syncthreads();
     // Tb^T [i][r]
     {
@@ -239,7 +262,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     const int kbeg = (16 * rb / 32) * 32;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) dR[nt] = zero4();
-    mma_row<SPLIT_AB, 4>(dR, A, 16 * rb, B, 64 * chh, kbeg, CL);
+    mma_row<KDA_SPLIT_B1, 4>(dR, A, 16 * rb, B, 64 * chh, kbeg, CL);
     __syncthreads();
   }
 
@@ -273,14 +296,15 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       }
       *reinterpret_cast<bf16x8*>(&sm.u.p2.do_hi[r][j8]) = x;
     }
+    const Panel APd{AP.hi, (KDA_SPLIT_B2 & SPLIT_A) ? AP.lo : nullptr, K1_LD};
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) store_tile_n(dR[nt], AP, 16 * rb, 64 * chh + 16 * nt);
+    for (int nt = 0; nt < 4; ++nt) store_tile_n(dR[nt], APd, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
     {
       f32x4 a[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
-      mma_row<SPLIT_B, 4>(a, DOP, 16 * rb, SP, 64 * chh, 0, HD);
+      mma_row<KDA_SPLIT_B3, 4>(a, DOP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -294,7 +318,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       f32x4 b[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) b[nt] = zero4();
-      mma_row<SPLIT_AB, 4>(b, AP, 16 * rb, SP, 64 * chh, 0, HD);
+      mma_row<KDA_SPLIT_B2, 4>(b, AP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -317,7 +341,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     f32x4 a[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
-    mma_row<SPLIT_AB, 4>(a, AP, 16 * rb, SP, 64 * chh, 0, HD);
+    mma_row<KDA_SPLIT_B4, 4>(a, AP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int c = 64 * chh + 16 * nt + dcol();
@@ -335,7 +359,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     }
     // dA_qk = scale dO U~^T: rows 16 rb, columns i in tiles 2 chh, 2 chh + 1
     dAq[0] = dAq[1] = zero4();
-    mma_row<SPLIT_B, 2>(dAq, DOP, 16 * rb, AP, 32 * chh, 0, HD);
+    mma_row<KDA_SPLIT_B5, 2>(dAq, DOP, 16 * rb, AP, 32 * chh, 0, HD);
     // dgamma[c] = sum_j dS_out[c][j] S_in[c][j]; four threads per channel
     {
       const int c = t >> 2, part = t & 3;
@@ -380,7 +404,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     }
     __syncthreads();
     dTb[0] = dTb[1] = zero4();
-    mma_row<SPLIT_AB, 2>(dTb, DU, 16 * rb, RP, 32 * chh, 0, HD);
+    mma_row<KDA_SPLIT_B6, 2>(dTb, DU, 16 * rb, RP, 32 * chh, 0, HD);
     __syncthreads();
   }
 
@@ -485,8 +509,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       f32x4 aq[4], ak[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) aq[nt] = ak[nt] = zero4();
-      mma_row<SPLIT_AB, 4>(aq, DQ, 16 * rb, YT, 64 * chh, 0, kend);
-      mma_row<SPLIT_AB, 4>(ak, DK, 16 * rb, YT, 64 * chh, 0, kend);
+      mma_row<KDA_SPLIT_B7, 4>(aq, DQ, 16 * rb, YT, 64 * chh, 0, kend);
+      mma_row<KDA_SPLIT_B7, 4>(ak, DK, 16 * rb, YT, 64 * chh, 0, kend);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -530,8 +554,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
       const int kb = (16 * rb / 32) * 32;
-      mma_row<SPLIT_AB, 4>(ac, DAT, 16 * rb, XT, 64 * chh, kb, CL);
-      mma_row<SPLIT_AB, 4>(ac, DAT, 16 * rb, XT, 64 * chh, CL + kb, 2 * CL);
+      mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, kb, CL);
+      mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, CL + kb, 2 * CL);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -593,8 +617,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           f32x4 aq[4], ak[4];
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) aq[nt] = ak[nt] = zero4();
-          mma_row<SPLIT_AB, 4>(aq, DQ, 0, YT, 64 * chh, 0, nyk);
-          mma_row<SPLIT_AB, 4>(ak, DK, 0, YT, 64 * chh, 0, nyk);
+          mma_row<KDA_SPLIT_B7, 4>(aq, DQ, 0, YT, 64 * chh, 0, nyk);
+          mma_row<KDA_SPLIT_B7, 4>(ak, DK, 0, YT, 64 * chh, 0, nyk);
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
             const float rho = sm.Gref[I][64 * chh + 16 * nt + dcol()];
@@ -612,7 +636,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           f32x4 ac[4];
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
-          mma_row<SPLIT_AB, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 0, 32);
+          mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 0, 32);
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
             const float rho = sm.Gref[I][64 * chh + 16 * nt + dcol()];

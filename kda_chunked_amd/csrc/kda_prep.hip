@@ -22,6 +22,10 @@ namespace kda {
 
 constexpr float CALM_SPAN = 40.f;
 
+#ifndef KDA_SPLIT_P1
+#define KDA_SPLIT_P1 SPLIT_AB    // A_kk = X_k Y^T, A_qk = X_q Y^T
+#endif
+
 __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
                                                         int64_t T, int NC, ChunkTable ct) {
   __shared__ int32_t scan[256];
@@ -69,264 +73,329 @@ hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& 
 }
 
 // ---------------------------------------------------------------------------
-// Shared-memory layout of the prep kernel.
-constexpr int GS_LD = HD + 4;     // fp32 row stride of G
-constexpr int XS_LD = HD + 8;     // bf16 row stride of q, k and the K=128 panels
-constexpr int AK_LD = CL + 4;     // fp32 row stride of 64x64 matrices
+// The prep kernel: 512 threads (8 waves). Thread t owns row rA = t >> 3 and
+// channels cA .. cA+15 (cA = 16 (t & 7)) of every 64 x 128 chunk quantity.
+constexpr int NT_PREP = 512;
+constexpr int GS_LD = HD + 1;     // fp32 row stride of G (scalar accesses only)
+constexpr int XS_LD = HD + 8;     // bf16 row stride of the K = 128 panels
+constexpr int F_LD = CL + 1;      // fp32 64 x 64 matrices
 
 struct PrepSmem {
   float G[CL][GS_LD];
-  bf16 qs[CL][XS_LD];
-  bf16 ks[CL][XS_LD];
+  float qtot[4][HD];
+  float nrm[2][8][CL];
   float rq[CL], rk[CL], beta[CL];
-  float rho[HD];
-  float half_tot[HD];
-  int calm[4];
-  bf16 xk_hi[16][XS_LD], xk_lo[16][XS_LD];
-  bf16 xq_hi[16][XS_LD], xq_lo[16][XS_LD];
+  float rho[4][HD];
+  int calm_blk[4];
+  int calm_chunk;
   union {
-    struct {
+    struct {                                   // single reference: Kd, Qd, Y = k^ e^-G
+      bf16 xk_hi[CL][XS_LD], xk_lo[CL][XS_LD];
+      bf16 xq_hi[CL][XS_LD], xq_lo[CL][XS_LD];
       bf16 y_hi[CL][XS_LD], y_lo[CL][XS_LD];
-    } p;
+    } a;
+    struct {                                   // one reference per 16-row block
+      bf16 xk_hi[16][XS_LD], xk_lo[16][XS_LD];
+      bf16 xq_hi[16][XS_LD], xq_lo[16][XS_LD];
+      bf16 y_hi[CL][XS_LD], y_lo[CL][XS_LD];
+      bf16 qs[CL][XS_LD], ks[CL][XS_LD];       // raw q, k for the exact diagonal sums
+    } b;
     struct {
-      float Tm[CL][AK_LD];
-      float Z[16][17];
+      float Tm[CL][F_LD];
+      float Z[3][16][17];
     } s;
   } u;
-  float Akk[CL][AK_LD];
+  float Akk[CL][F_LD];
 };
 
-// Loads the chunk's gate, forms G = cumsum(g) in LDS (rows >= n hold G[n-1])
-// and, when G_out is non-null, writes G for the chunk's tokens.
-KDA_DEV void load_gate_cumsum(float (*Gs)[GS_LD], float* half_tot, const Dims& d, const Inputs& in,
-                              int64_t t0, int n, int h, float* G_out) {
-  const int t = threadIdx.x;
-  for (int e = t; e < CL * HD; e += 256) {
-    const int r = e / HD, c = e % HD;
-    Gs[r][c] = r < n ? gate_value(in.gate, d.raw, in.A_log, in.dt_bias, t0 + r, h, d.H, c) : 0.f;
-  }
-  __syncthreads();
-  // Two threads per channel: rows 0-31 and 32-63, then the upper half adds
-  // the lower half's total (a fixed order, so every kernel that recomputes G
-  // gets the same bits).
-  const int c = t & (HD - 1), half = t >> 7;
-  float run = 0.f;
-  for (int r = 32 * half; r < 32 * half + 32; ++r) {
-    run += Gs[r][c];
-    Gs[r][c] = run;
-  }
-  if (half == 0) half_tot[c] = run;
-  __syncthreads();
-  if (half == 1) {
-    const float base = half_tot[c];
-    for (int r = 32; r < 64; ++r) Gs[r][c] += base;
-  }
-  __syncthreads();
-  if (G_out) {
-    for (int e = t; e < n * HD; e += 256) {
-      const int r = e / HD, c2 = e % HD;
-      G_out[((t0 + r) * d.H + h) * HD + c2] = Gs[r][c2];
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void fwd_prep_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                        float* __restrict__ G_out, SavedSet sv) {
+__global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, ChunkTable ct,
+                                                            float* __restrict__ G_out,
+                                                            SavedSet sv) {
   __shared__ PrepSmem sm;
   const int ci = blockIdx.x, h = blockIdx.y;
   if (ci >= ct.doc_c0[d.N]) return;
   const int64_t t0 = ct.tok[ci];
   const int n = ct.len[ci];
   const int t = threadIdx.x, w = wave_id(), l = lane_id();
-  const int64_t ch = (int64_t)ci * d.H + h;
+  const int H = d.H;
+  const int64_t ch = (int64_t)ci * H + h;
   const bf16* q = reinterpret_cast<const bf16*>(in.q);
   const bf16* k = reinterpret_cast<const bf16*>(in.k);
   const bf16* beta = reinterpret_cast<const bf16*>(in.beta);
+  const int rA = t >> 3, cA = 16 * (t & 7);
+  const bool okA = rA < n;
+  const int64_t baseA = ((t0 + (okA ? rA : n - 1)) * H + h) * HD + cA;
 
-  // 1. q, k rows (zero padded), beta, L2 scalars.
-  for (int e = t; e < CL * (HD / 8); e += 256) {
-    const int r = e / (HD / 8), c8 = (e % (HD / 8)) * 8;
-    bf16x8 qv, kv;
-    if (r < n) {
-      qv = *reinterpret_cast<const bf16x8*>(q + ((t0 + r) * d.H + h) * HD + c8);
-      kv = *reinterpret_cast<const bf16x8*>(k + ((t0 + r) * d.H + h) * HD + c8);
-    } else {
+  // ---- 1. loads (all issued before use): q, k, gate of this thread's 16 elements
+  bf16x8 q0 = *reinterpret_cast<const bf16x8*>(q + baseA);
+  bf16x8 q1 = *reinterpret_cast<const bf16x8*>(q + baseA + 8);
+  bf16x8 k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
+  bf16x8 k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
+  float g[16];
+  if (!d.raw) {
+    const float* gp = reinterpret_cast<const float*>(in.gate) + baseA;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qv[i] = kv[i] = f2bf(0.f);
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(gp + 4 * j);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) g[4 * j + u] = x[u];
     }
-    *reinterpret_cast<bf16x8*>(&sm.qs[r][c8]) = qv;
-    *reinterpret_cast<bf16x8*>(&sm.ks[r][c8]) = kv;
+  } else {
+    const bf16* ap = reinterpret_cast<const bf16*>(in.gate) + baseA;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + 8);
+    const float ea = __expf(in.A_log[h]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      g[j] = -ea * softplus(bf2f(j < 8 ? a0[j] : a1[j - 8]) + in.dt_bias[h * HD + cA + j]);
   }
-  for (int e = t; e < CL * AK_LD; e += 256) (&sm.Akk[0][0])[e] = 0.f;
-  if (t < CL) sm.beta[t] = t < n ? bf2f(beta[(t0 + t) * d.H + h]) : 0.f;
-  __syncthreads();
+  if (t < CL) sm.beta[t] = t < n ? bf2f(beta[(t0 + (t < n ? t : n - 1)) * H + h]) : 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sm.G[rA][cA + j] = okA ? g[j] : 0.f;
+  // L2 row sums: partial over this thread's 16 channels
   {
-    // four threads per row, 32 channels each
-    const int r = t >> 2, part = t & 3;
     float sq = 0.f, sk = 0.f;
-    for (int c = 32 * part; c < 32 * part + 32; ++c) {
-      const float a = bf2f(sm.qs[r][c]), b = bf2f(sm.ks[r][c]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float a = bf2f(j < 8 ? q0[j] : q1[j - 8]), b = bf2f(j < 8 ? k0[j] : k1[j - 8]);
       sq += a * a;
       sk += b * b;
     }
-    sq += __shfl_xor(sq, 1);
-    sk += __shfl_xor(sk, 1);
-    sq += __shfl_xor(sq, 2);
-    sk += __shfl_xor(sk, 2);
-    if (part == 0) {
-      const float a = d.l2norm ? 1.f / sqrtf(sq + d.l2_eps) : 1.f;
-      const float b = d.l2norm ? 1.f / sqrtf(sk + d.l2_eps) : 1.f;
-      sm.rq[r] = a;
-      sm.rk[r] = b;
-      if (r < n) {
-        sv.rq[(t0 + r) * d.H + h] = a;
-        sv.rk[(t0 + r) * d.H + h] = b;
-      }
-    }
-  }
-
-  // 2. Gate cumsum.
-  load_gate_cumsum(sm.G, sm.half_tot, d, in, t0, n, h, G_out);
-
-  // 3. Calm flags: decay span of each 16-row block, per channel.
-  if (t < 4) sm.calm[t] = 1;
-  __syncthreads();
-  if (t < HD) {
-    for (int I = 0; I < 4; ++I) {
-      const float ref = I == 0 ? 0.f : sm.G[16 * I - 1][t];
-      if (ref - sm.G[16 * I + 15][t] > CALM_SPAN) sm.calm[I] = 0;
-    }
+    sm.nrm[0][t & 7][rA] = sq;
+    sm.nrm[1][t & 7][rA] = sk;
   }
   __syncthreads();
 
-  const Panel XK{&sm.xk_hi[0][0], &sm.xk_lo[0][0], XS_LD};
-  const Panel XQ{&sm.xq_hi[0][0], &sm.xq_lo[0][0], XS_LD};
-  const Panel Y{&sm.u.p.y_hi[0][0], &sm.u.p.y_lo[0][0], XS_LD};
-  float* Aqk_g = sv.Aqk + ch * CL * CL;
-
-  // 4. Off-diagonal and calm diagonal tiles on MFMA, one row block at a time.
-  for (int I = 0; I < 4; ++I) {
-    if (t < HD) sm.rho[t] = I == 0 ? 0.f : sm.G[16 * I - 1][t];
-    __syncthreads();
-    const int calm = sm.calm[I];
-    const int ny = 16 * I + 16;
-    // X rows of block I (q and k), 8 channels per task.
-    for (int e = t; e < 16 * (HD / 8); e += 256) {
-      const int rl = e / (HD / 8), c8 = (e % (HD / 8)) * 8;
-      const int r = 16 * I + rl;
-      float xk[8], xq[8];
+  // ---- 2. chunk-local cumsum of g: four threads per channel (16 rows each)
+  {
+    const int c = t & 127, qr = t >> 7;
+    float run = 0.f;
+    for (int r = 16 * qr; r < 16 * qr + 16; ++r) {
+      run += sm.G[r][c];
+      sm.G[r][c] = run;
+    }
+    sm.qtot[qr][c] = run;
+    if (t < CL) {
+      float a = 0.f, b = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float f = fexp(sm.G[r][c8 + j] - sm.rho[c8 + j]);
-        xk[j] = bf2f(sm.ks[r][c8 + j]) * sm.rk[r] * f;
-        xq[j] = bf2f(sm.qs[r][c8 + j]) * sm.rq[r] * f;
+        a += sm.nrm[0][j][t];
+        b += sm.nrm[1][j][t];
       }
-      put8(XK, rl, c8, xk);
-      put8(XQ, rl, c8, xq);
-    }
-    // Y rows 0 .. 16I+15 (block I's own rows only when calm).
-    for (int e = t; e < ny * (HD / 8); e += 256) {
-      const int i = e / (HD / 8), c8 = (e % (HD / 8)) * 8;
-      float y[8];
-      const bool on = i < 16 * I || calm;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        y[j] = on ? bf2f(sm.ks[i][c8 + j]) * sm.rk[i] * fexp(sm.rho[c8 + j] - sm.G[i][c8 + j]) : 0.f;
-      put8(Y, i, c8, y);
+      const float rq = d.l2norm ? 1.f / sqrtf(a + d.l2_eps) : 1.f;
+      const float rk = d.l2norm ? 1.f / sqrtf(b + d.l2_eps) : 1.f;
+      sm.rq[t] = t < n ? rq : 0.f;
+      sm.rk[t] = t < n ? rk : 0.f;
+      if (t < n) {
+        sv.rq[(t0 + t) * H + h] = rq;
+        sv.rk[(t0 + t) * H + h] = rk;
+      }
     }
     __syncthreads();
-    // tile-products: (matrix, J) for J = 0..I; wave w takes every 4th.
-    for (int p = w; p < 2 * (I + 1); p += 4) {
-      const int J = p >> 1, isq = p & 1;
-      if (J == I && !calm) continue;
-      f32x4 acc = zero4();
-      mma_k<SPLIT_AB, HD>(acc, isq ? XQ : XK, 0, Y, 16 * J);
+    float carry = 0.f;
+    for (int j = 0; j < qr; ++j) carry += sm.qtot[j][c];
+    if (qr > 0)
+      for (int r = 16 * qr; r < 16 * qr + 16; ++r) sm.G[r][c] += carry;
+  }
+  if (t < 4) sm.calm_blk[t] = 1;
+  if (t == 4) sm.calm_chunk = 1;
+  __syncthreads();
+  // this thread's G (rows >= n hold G[n-1] because their g is 0)
+  float Gv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) Gv[j] = sm.G[rA][cA + j];
+  if (okA) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4*>(G_out + baseA + 4 * j) =
+          f32x4{Gv[4 * j], Gv[4 * j + 1], Gv[4 * j + 2], Gv[4 * j + 3]};
+  }
+  if (t < HD) {
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const float ref = I == 0 ? 0.f : sm.G[16 * I - 1][t];
+      sm.rho[I][t] = ref;
+      if (ref - sm.G[16 * I + 15][t] > CALM_SPAN) sm.calm_blk[I] = 0;
+    }
+    if (-sm.G[CL - 1][t] > CALM_SPAN) sm.calm_chunk = 0;
+  }
+  __syncthreads();
+
+  const float rqA = sm.rq[rA], rkA = sm.rk[rA];
+  float* Aqk_g = sv.Aqk + ch * CL * CL;
+  const int rb = w & 3, isq = w >> 2;         // MFMA role: row block rb of A_kk (isq = 0) or A_qk
+  if (sm.calm_chunk) {
+    // ---- 3a. single reference at the chunk start: A = X Y^T with X = x^ e^G, Y = k^ e^-G
+    const Panel XK{&sm.u.a.xk_hi[0][0], &sm.u.a.xk_lo[0][0], XS_LD};
+    const Panel XQ{&sm.u.a.xq_hi[0][0], &sm.u.a.xq_lo[0][0], XS_LD};
+    const Panel Y{&sm.u.a.y_hi[0][0], &sm.u.a.y_lo[0][0], XS_LD};
+    float xk[16], xq[16], y[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float e1 = fexp(Gv[j]);
+      const float kh = bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA;
+      const float qh = bf2f(j < 8 ? q0[j] : q1[j - 8]) * rqA;
+      xk[j] = kh * e1;
+      xq[j] = qh * e1;
+      y[j] = kh * fexp(-Gv[j]);
+    }
+    put8(XK, rA, cA, xk);
+    put8(XK, rA, cA + 8, xk + 8);
+    put8(XQ, rA, cA, xq);
+    put8(XQ, rA, cA + 8, xq + 8);
+    put8(Y, rA, cA, y);
+    put8(Y, rA, cA + 8, y + 8);
+    __syncthreads();
+    f32x4 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+    mma_row<KDA_SPLIT_P1, 4>(acc, isq ? XQ : XK, 16 * rb, Y, 0, 0, HD);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int r = 16 * I + drow(i4), i = 16 * J + dcol();
-        if (isq) {
-          Aqk_g[r * CL + i] = (i <= r) ? acc[i4] : 0.f;
-        } else {
-          sm.Akk[r][i] = (i < r) ? acc[i4] : 0.f;
+        const int r = 16 * rb + drow(i4), i = 16 * nt + dcol();
+        if (isq)
+          Aqk_g[r * CL + i] = (i <= r) ? acc[nt][i4] : 0.f;
+        else
+          sm.Akk[r][i] = (i < r) ? acc[nt][i4] : 0.f;
+      }
+    __syncthreads();
+  } else {
+    // ---- 3b. one reference per 16-row block; exact sums for wide diagonal blocks
+    const Panel XK{&sm.u.b.xk_hi[0][0], &sm.u.b.xk_lo[0][0], XS_LD};
+    const Panel XQ{&sm.u.b.xq_hi[0][0], &sm.u.b.xq_lo[0][0], XS_LD};
+    const Panel Y{&sm.u.b.y_hi[0][0], &sm.u.b.y_lo[0][0], XS_LD};
+    *reinterpret_cast<bf16x8*>(&sm.u.b.qs[rA][cA]) = q0;
+    *reinterpret_cast<bf16x8*>(&sm.u.b.qs[rA][cA + 8]) = q1;
+    *reinterpret_cast<bf16x8*>(&sm.u.b.ks[rA][cA]) = k0;
+    *reinterpret_cast<bf16x8*>(&sm.u.b.ks[rA][cA + 8]) = k1;
+    for (int I = 0; I < 4; ++I) {
+      const int calm = sm.calm_blk[I];
+      const int bA = rA >> 4;
+      float y[16];
+      const bool on = bA < I || (bA == I && calm);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float kh = bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA;
+        y[j] = on ? kh * fexp(sm.rho[I][cA + j] - Gv[j]) : 0.f;
+      }
+      put8(Y, rA, cA, y);
+      put8(Y, rA, cA + 8, y + 8);
+      if (bA == I) {
+        float xk[16], xq[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float e1 = fexp(Gv[j] - sm.rho[I][cA + j]);
+          xk[j] = bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA * e1;
+          xq[j] = bf2f(j < 8 ? q0[j] : q1[j - 8]) * rqA * e1;
+        }
+        put8(XK, rA & 15, cA, xk);
+        put8(XK, rA & 15, cA + 8, xk + 8);
+        put8(XQ, rA & 15, cA, xq);
+        put8(XQ, rA & 15, cA + 8, xq + 8);
+      }
+      __syncthreads();
+      // tile-products (matrix, J) for J = 0..I, one per wave
+      {
+        const int J = w >> 1, pq = w & 1;
+        if (J <= I) {
+          f32x4 acc = zero4();
+          if (J < I || calm) mma_k<KDA_SPLIT_P1, HD>(acc, pq ? XQ : XK, 0, Y, 16 * J);
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int r = 16 * I + drow(i4), i = 16 * J + dcol();
+            if (pq)
+              Aqk_g[r * CL + i] = (i <= r) ? acc[i4] : 0.f;
+            else
+              sm.Akk[r][i] = (i < r) ? acc[i4] : 0.f;
+          }
+        }
+        // zero the strictly-upper tiles of A_qk and A_kk for this row block
+        for (int e = t; e < 16 * (CL - 16 * (I + 1)); e += NT_PREP) {
+          const int rl = e / (CL - 16 * (I + 1)), i = 16 * (I + 1) + e % (CL - 16 * (I + 1));
+          Aqk_g[(16 * I + rl) * CL + i] = 0.f;
+          sm.Akk[16 * I + rl][i] = 0.f;
         }
       }
+      __syncthreads();
     }
-    // zero the strictly-upper tiles of A_qk for this row block
-    for (int e = t; e < 16 * (CL - ny); e += 256) {
-      const int rl = e / (CL - ny), i = ny + e % (CL - ny);
-      Aqk_g[(16 * I + rl) * CL + i] = 0.f;
+    // exact fp32 sums on the diagonal tiles of blocks whose span is too wide
+    for (int p = t; p < 4 * 256; p += NT_PREP) {
+      const int I = p >> 8;
+      if (sm.calm_blk[I]) continue;
+      const int r = 16 * I + ((p >> 4) & 15), i = 16 * I + (p & 15);
+      if (i > r) continue;
+      float skk = 0.f, sqk = 0.f;
+      for (int c = 0; c < HD; ++c) {
+        const float e = fexp(sm.G[r][c] - sm.G[i][c]) * bf2f(sm.u.b.ks[i][c]);
+        skk += bf2f(sm.u.b.ks[r][c]) * e;
+        sqk += bf2f(sm.u.b.qs[r][c]) * e;
+      }
+      Aqk_g[r * CL + i] = sqk * sm.rq[r] * sm.rk[i];
+      if (i < r) sm.Akk[r][i] = skk * sm.rk[r] * sm.rk[i];
     }
     __syncthreads();
   }
 
-  // 5. Diagonal tiles of blocks whose decay span is too wide: exact fp32 sums,
-  //    one (r, i) entry per task over the 4 x 256 entries of the diagonal tiles.
-  for (int p = t; p < 4 * 256; p += 256) {
-    const int I = p >> 8;
-    if (sm.calm[I]) continue;
-    const int r = 16 * I + ((p >> 4) & 15), i = 16 * I + (p & 15);
-    if (i > r) {
-      Aqk_g[r * CL + i] = 0.f;
-      continue;
-    }
-    float skk = 0.f, sqk = 0.f;
-    for (int c = 0; c < HD; ++c) {
-      const float e = fexp(sm.G[r][c] - sm.G[i][c]) * bf2f(sm.ks[i][c]);
-      skk += bf2f(sm.ks[r][c]) * e;
-      sqk += bf2f(sm.qs[r][c]) * e;
-    }
-    Aqk_g[r * CL + i] = sqk * sm.rq[r] * sm.rk[i];
-    if (i < r) sm.Akk[r][i] = skk * sm.rk[r] * sm.rk[i];
-  }
+  // ---- 4. T = (I + Diag(beta) A_kk)^-1 by 16x16 blocks, fp32
+  float (*Tm)[F_LD] = sm.u.s.Tm;
+  for (int e = t; e < CL * F_LD; e += NT_PREP) (&Tm[0][0])[e] = 0.f;
   __syncthreads();
-
-  // 6. T = (I + Diag(beta) A_kk)^-1 by 16x16 blocks, fp32.
-  float (*Tm)[AK_LD] = sm.u.s.Tm;
-  for (int e = t; e < CL * AK_LD; e += 256) (&Tm[0][0])[e] = 0.f;
-  __syncthreads();
-  if (l < 16) {
+  if (w < 4 && l < 16) {
     // wave w inverts diagonal block w; lane = column j
     const int I = w, j = l;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float s = (r == j) ? 1.f : 0.f;
+      float s2 = (r == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s -= sm.beta[16 * I + r] * sm.Akk[16 * I + r][16 * I + i] * x[i];
-      x[r] = s;
+      for (int i = 0; i < r; ++i) s2 -= sm.beta[16 * I + r] * sm.Akk[16 * I + r][16 * I + i] * x[i];
+      x[r] = s2;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) Tm[16 * I + r][16 * I + j] = x[r];
   }
   __syncthreads();
   for (int dist = 1; dist < 4; ++dist) {
-    for (int J = 0; J + dist < 4; ++J) {
+    // the (4 - dist) blocks of this distance in parallel, 256 threads each
+    const int nb = 4 - dist;
+    const int bsel = t >> 8, r = (t >> 4) & 15, j = t & 15;
+    for (int J0 = 0; J0 < nb; J0 += 2) {
+      const int J = J0 + bsel;
       const int I = J + dist;
-      const int r = t >> 4, j = t & 15;
-      // Z = sum_{m in blocks J..I-1} X[I-row r][m] T[m][J-col j]
-      float z = 0.f;
-      for (int m = 16 * J; m < 16 * I; ++m)
-        z += sm.beta[16 * I + r] * sm.Akk[16 * I + r][m] * Tm[m][16 * J + j];
-      sm.u.s.Z[r][j] = z;
+      if (J < nb) {
+        float z = 0.f;
+        for (int m = 16 * J; m < 16 * I; ++m)
+          z += sm.beta[16 * I + r] * sm.Akk[16 * I + r][m] * Tm[m][16 * J + j];
+        sm.u.s.Z[bsel][r][j] = z;
+      }
       __syncthreads();
-      float s = 0.f;
-      for (int m = 0; m < 16; ++m) s += Tm[16 * I + r][16 * I + m] * sm.u.s.Z[m][j];
-      Tm[16 * I + r][16 * J + j] = -s;
+      if (J < nb) {
+        float s2 = 0.f;
+        for (int m = 0; m < 16; ++m) s2 += Tm[16 * I + r][16 * I + m] * sm.u.s.Z[bsel][m][j];
+        Tm[16 * I + r][16 * J + j] = -s2;
+      }
       __syncthreads();
     }
   }
   float* Tg = sv.Tm + ch * CL * CL;
   float* Akk_g = sv.Akk + ch * CL * CL;
-  for (int e = t; e < CL * CL; e += 256) {
-    const int r = e / CL, i = e % CL;
-    Tg[e] = Tm[r][i];
-    Akk_g[e] = sm.Akk[r][i];
+  {
+    const int r = t >> 3, i8 = 8 * (t & 7);
+    *reinterpret_cast<f32x4*>(Tg + r * CL + i8) = f32x4{Tm[r][i8], Tm[r][i8 + 1], Tm[r][i8 + 2], Tm[r][i8 + 3]};
+    *reinterpret_cast<f32x4*>(Tg + r * CL + i8 + 4) =
+        f32x4{Tm[r][i8 + 4], Tm[r][i8 + 5], Tm[r][i8 + 6], Tm[r][i8 + 7]};
+    *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8) =
+        f32x4{sm.Akk[r][i8], sm.Akk[r][i8 + 1], sm.Akk[r][i8 + 2], sm.Akk[r][i8 + 3]};
+    *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8 + 4) =
+        f32x4{sm.Akk[r][i8 + 4], sm.Akk[r][i8 + 5], sm.Akk[r][i8 + 6], sm.Akk[r][i8 + 7]};
   }
 }
 
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
                            const SavedSet& sv, hipStream_t s) {
-  hipLaunchKernelGGL(fwd_prep_kernel, dim3(d.NC, d.H), dim3(256), 0, s, d, in, ct, G, sv);
+  hipLaunchKernelGGL(fwd_prep_kernel, dim3(d.NC, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv);
   return hipGetLastError();
 }
 

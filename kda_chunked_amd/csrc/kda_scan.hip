@@ -33,10 +33,10 @@ constexpr int K2_LD = CL + 8;       // panels with K = 64
 
 // Split terms per product (SPLIT_A: first operand carries its lo part, ...).
 #ifndef KDA_SPLIT_KS
-#define KDA_SPLIT_KS SPLIT_AB
+#define KDA_SPLIT_KS SPLIT_NONE
 #endif
 #ifndef KDA_SPLIT_TR
-#define KDA_SPLIT_TR SPLIT_AB
+#define KDA_SPLIT_TR SPLIT_B
 #endif
 #ifndef KDA_SPLIT_QS
 #define KDA_SPLIT_QS SPLIT_AB
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(NT_SCAN) void fwd_scan_kernel(Dims d, Inputs in, Ch
   const Panel KD{&sm.r1.kd.hi[0][0], (SPLIT_KS & SPLIT_A) ? &sm.r1.kd.lo[0][0] : nullptr, K1_LD};
   const Panel KE{&sm.r1.ke.hi[0][0], &sm.r1.ke.lo[0][0], K2_LD};
   const Panel QD{&sm.qd_hi[0][0], &sm.qd_lo[0][0], K1_LD};
-  const Panel TB{&sm.tb_hi[0][0], &sm.tb_lo[0][0], K2_LD};
+  const Panel TB{&sm.tb_hi[0][0], (SPLIT_TR & SPLIT_A) ? &sm.tb_lo[0][0] : nullptr, K2_LD};
   const Panel AQ{&sm.aq_hi[0][0], &sm.aq_lo[0][0], K2_LD};
   const Panel SP{&sm.s_hi[0][0], &sm.s_lo[0][0], K1_LD};
   const Panel RP{&sm.rr_hi[0][0], &sm.rr_lo[0][0], K2_LD};
