@@ -12,14 +12,29 @@ step), the roofline of the dominant kernel (timed live with HIP events on
 the stream the library launches on, through the library's launch hook), and
 the FP64 oracle timed on the host on a bounded sample of the same workload.
 
+Besides the timed steps it times, outside the timed region, the units of the
+deterministic package's protocol: fwd alone, bwd alone and the replay pair
+(forward without saving, backward recomputing the forward), each the median
+of 15 samples of 20 back-to-back calls.
+
+HBM traffic and MFMA utilisation come from rocprofv3 counter runs whose
+summaries sit in profiles/; they are reported only while the kernel sources
+still hash to the fingerprint recorded with them (else null).
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 1doc]
-                       [--no-cpu] [--extra]
+                       [--no-cpu] [--no-units] [--calibrate-copy MIB]
+       python bench.py --pmc-summary DIR     (tabulate a rocprofv3 --pmc run)
+       python bench.py --trace-summary DIR   (tabulate a rocprofv3 --kernel-trace run)
+       python bench.py --fingerprint         (hash of the kernel sources)
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import os
 import statistics
@@ -31,6 +46,13 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+METRIC = "KDA fwd+bwd ms & tokens/s, 16384 tok x 64 heads, d=128; MFMA util %"
+CSRC = os.path.join(ROOT, "kda_chunked_amd", "csrc")
+# fwd+bwd ms per row on NVIDIA GB300 ("after head" column of the GB300 timing
+# table on flashinfer PR #8909): another machine's numbers, context only.
+PAGE_FWD_BWD_MS = {"1doc:g:fused": 4.4696, "4doc:raw:off": 4.2789, "R2:raw:off": 0.6658,
+                   "m2:g:off": 0.5285}
+PROFILES = os.path.join(ROOT, "profiles")
 
 # Algorithmic multiply-adds per full 64-token chunk and head, per kernel: the
 # products the method defines (triangular products counted on their nonzero
@@ -88,6 +110,96 @@ class HipEvents:
         return out
 
 
+def fingerprint() -> str:
+    """sha256 (16 hex digits) over the kernel sources; counter figures taken
+    on other sources are stale."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if p.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(p).encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _short(kernel_name: str) -> str:
+    for k in ("chunk_map", "fwd_prep", "fwd_scan", "bwd_scan", "bwd_intra", "finalize"):
+        if k + "_kernel" in kernel_name:
+            return k
+    return "copy" if "copyBuffer" in kernel_name else kernel_name[:40]
+
+
+def _rocprof_rows(folder: str, query_db: str, csv_name: str):
+    """Rows of a rocprofv3 output folder, from its SQLite results (the default
+    output format) or its CSV files."""
+    import sqlite3
+    dbs = glob.glob(os.path.join(folder, "**", "*_results.db"), recursive=True)
+    for f in dbs:
+        con = sqlite3.connect(f)
+        con.row_factory = sqlite3.Row
+        yield from (dict(r) for r in con.execute(query_db))
+        con.close()
+    if not dbs:
+        for f in glob.glob(os.path.join(folder, "**", csv_name), recursive=True):
+            yield from csv.DictReader(open(f))
+
+
+def pmc_summary(folder: str) -> dict:
+    """Mean per dispatch of every counter in a rocprofv3 --pmc run:
+    {kernel: {counter: (dispatches, mean, grid_size)}}."""
+    acc = {}
+    q = ("select kernel_name as Kernel_Name, counter_name as Counter_Name, "
+         "value as Counter_Value, grid_size as Grid_Size from counters_collection")
+    for r in _rocprof_rows(folder, q, "*counter_collection.csv"):
+        key = (_short(r["Kernel_Name"]), r["Counter_Name"], int(r["Grid_Size"]))
+        acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    if not acc:
+        raise SystemExit(f"no counter records under {folder}")
+    out = {}
+    for (k, c, grid), v in sorted(acc.items()):
+        out.setdefault(k, {})[c] = (len(v), statistics.fmean(v), grid)
+    return out
+
+
+def trace_summary(folder: str) -> dict:
+    """Per-kernel dispatch count, total and mean duration (us) of a rocprofv3
+    --kernel-trace run."""
+    acc = {}
+    q = "select name as Kernel_Name, start as Start_Timestamp, end as End_Timestamp from kernels"
+    for r in _rocprof_rows(folder, q, "*kernel_trace.csv"):
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        acc.setdefault(_short(r["Kernel_Name"]), []).append(dur)
+    if not acc:
+        raise SystemExit(f"no kernel records under {folder}")
+    return {k: (len(v), sum(v), statistics.fmean(v)) for k, v in acc.items()}
+
+
+def profile_figures(workload: str, kernel: str, fp: str):
+    """Counter figures recorded in profiles/ for this workload and kernel
+    (a `figures:` JSON line in the summary), if taken on these sources."""
+    for p in sorted(glob.glob(os.path.join(PROFILES, f"*{workload}*.md"))):
+        for line in open(p):
+            if line.startswith("figures: "):
+                fig = json.loads(line[len("figures: "):])
+                if fig.get("kernel") == kernel and fig.get("workload") == workload:
+                    if fig.get("fingerprint") == fp:
+                        return fig
+    return None
+
+
+def time_unit(torch, fn, samples=15, calls=20):
+    """Median over `samples` of (HIP-event time of `calls` back-to-back calls) / calls."""
+    out = []
+    for _ in range(samples):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(calls):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / calls)
+    return statistics.median(out)
+
+
 def make_device_inputs(w, torch):
     import numpy as np
     from kda_chunked_amd import inputs as I
@@ -107,11 +219,11 @@ def make_device_inputs(w, torch):
 
 def cpu_baseline(w, inp, threads):
     """The FP64 oracle (as it stands) on a bounded sample of the workload:
-    2 heads per host thread of the same document(s), fwd + bwd."""
+    4 heads per host thread of the same document(s), fwd + bwd."""
     import numpy as np
     from kda_chunked_amd import inputs as I
     from oracle import kda_oracle as ko
-    nh = min(w.H, 2 * threads)
+    nh = min(w.H, 4 * threads)
     hs = list(range(nh))
     f = I.as_f64({k: (v[:, hs] if k in ("q", "k", "v", "beta", "dO", "gate") else v)
                   for k, v in inp.items()})
@@ -136,9 +248,36 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="1doc")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--extra", action="store_true", help="also time fwd and bwd alone")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-units", action="store_true",
+                    help="skip the fwd / bwd / replay unit timings")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the steps, copy MIB MiB device to device once (a plain copy "
+                         "kernel of known size, for scaling HBM byte counters)")
+    ap.add_argument("--pmc-summary", metavar="DIR", help="tabulate a rocprofv3 --pmc run and exit")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="tabulate a rocprofv3 --kernel-trace run and exit")
+    ap.add_argument("--fingerprint", action="store_true", help="print the source hash and exit")
     args = ap.parse_args()
+    if args.fingerprint:
+        print(fingerprint())
+        return
+    if args.trace_summary:
+        summ = trace_summary(args.trace_summary)
+        tot = sum(v[1] for v in summ.values())
+        print("| kernel | dispatches | total us | mean us | % |")
+        print("|---|---:|---:|---:|---:|")
+        for k, (n, t, m) in sorted(summ.items(), key=lambda kv: -kv[1][1]):
+            print(f"| {k} | {n} | {t:.1f} | {m:.1f} | {100 * t / tot:.1f} |")
+        return
+    if args.pmc_summary:
+        summ = pmc_summary(args.pmc_summary)
+        print("| kernel | counter | dispatches | mean per dispatch | grid |")
+        print("|---|---|---:|---:|---:|")
+        for k, cs in summ.items():
+            for c, (n, m, grid) in cs.items():
+                print(f"| {k} | {c} | {n} | {m:.6g} | {grid} |")
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU "
               "(heads or sequence shards would split across GPUs; see the design notes)",
@@ -160,18 +299,21 @@ def main():
     if w.gate == "raw":
         grads.update(dA_log=torch.empty_like(A_log), ddt_bias=torch.empty_like(dt_bias))
     o = torch.empty_like(dev["v"])
+    args_in = (dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], dev["cu"])
 
-    def fwd():
-        kda.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], dev["cu"], A_log,
-                    dt_bias, save=True, o=o)
+    def fwd(save=True):
+        kda.forward(*args_in, A_log, dt_bias, save=save, o=o)
 
-    def bwd():
-        kda.backward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], dev["cu"],
-                     dev["dO"], A_log, dt_bias, out=grads)
+    def bwd(replay=False):
+        kda.backward(*args_in, dev["dO"], A_log, dt_bias, replay=replay, out=grads)
 
     def step():
         fwd()
         bwd()
+
+    def replay_pair():
+        fwd(save=False)
+        bwd(replay=True)
 
     for _ in range(args.warmup):
         step()
@@ -194,32 +336,42 @@ def main():
     kern = ev.durations_ms()
     kern_avg = {k: statistics.fmean(v) for k, v in kern.items()}
 
-    extra = {}
-    if args.extra:
-        for name, fn in (("fwd", fwd), ("bwd", bwd)):
-            samples = []
-            for _ in range(5):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                for _ in range(5):
-                    fn()
-                b.record()
-                torch.cuda.synchronize()
-                samples.append(a.elapsed_time(b) / 5)
-            extra[f"{name}_ms"] = round(statistics.median(samples), 4)
+    units = {}
+    if not args.no_units:
+        units["fwd_ms"] = time_unit(torch, fwd)
+        units["bwd_ms"] = time_unit(torch, bwd)
+        units["fwd_bwd_ms"] = time_unit(torch, step)
+        units["replay_fwd_bwd_ms"] = time_unit(torch, replay_pair)
+        units = {k: round(v, 4) for k, v in units.items()}
 
-    units = w.T * w.H / 64.0    # chunk-head equivalents per launch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    chunk_heads = w.T * w.H / 64.0    # chunk-head equivalents per launch
     dom = max((k for k in kern_avg if k in MAC_PER_CHUNK_HEAD), key=lambda k: kern_avg[k])
-    flop = 2.0 * MAC_PER_CHUNK_HEAD[dom] * units
+    flop = 2.0 * MAC_PER_CHUNK_HEAD[dom] * chunk_heads
     achieved = flop / (kern_avg[dom] * 1e-3) / 1e12
+    fp = fingerprint()
+    fig = profile_figures(w.name, dom, fp)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": fig["traffic_bytes"] if fig else None,
                 "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(kern_avg[dom], 4)}
+    if fig:
+        roofline["mfma_busy_pct"] = fig.get("mfma_busy_pct")
+        roofline["executed_mfma_tflops"] = round(
+            fig["mfma_flop"] / (kern_avg[dom] * 1e-3) / 1e12, 2) if "mfma_flop" in fig else None
 
-    total_flop = 2.0 * sum(MAC_PER_CHUNK_HEAD.values()) * units
+    total_flop = 2.0 * sum(MAC_PER_CHUNK_HEAD.values()) * chunk_heads
     line = {
-        "metric": "KDA fwd+bwd tokens/s (16384 tok x 64 heads, d=128)",
+        "metric": METRIC,
         "value": round(w.T / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -228,17 +380,22 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": (round(w.T / (ms_step * 1e-3) / (w.T / (PAGE_FWD_BWD_MS[w.key] * 1e-3)), 4)
+                        if w.key in PAGE_FWD_BWD_MS else None),
+        "vs_baseline_note": ("ratio to the GB300 fwd+bwd figure of this row on flashinfer PR "
+                             "#8909 (other hardware, context only)"),
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.key + ":saved", "tokens": w.T, "heads": w.H, "head_dim": 128,
                    "docs": list(w.doc_lens), "chunk": 64},
         "roofline": roofline,
+        "token_heads_per_s": round(w.T * w.H / (ms_step * 1e-3), 1),
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kern_avg.items())},
         "algorithmic_tflops": round(total_flop / (ms_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
+        "source_fingerprint": fp,
     }
-    line.update(extra)
+    line.update(units)
     if not args.no_cpu:
         from oracle import kda_oracle as ko
         line["cpu_baseline"] = cpu_baseline(w, inp, ko.default_threads())
