@@ -64,6 +64,10 @@ constexpr float CALM_SPAN_B = 40.f;
 #define KDA_SPLIT_B7 SPLIT_AB    // decayed-product backward: dA Y, dA^T X
 #endif
 
+#ifndef KDA_SPLIT_B8
+#define KDA_SPLIT_B8 SPLIT_AB    // WY / UT backward: dT T^T, T^T tmp
+#endif
+
 struct BwdIntraSmem {
   union {
     struct {
@@ -80,41 +84,41 @@ struct BwdIntraSmem {
       bf16 b_hi[CL][K1_LD], b_lo[CL][K1_LD];       // R [i][j]
     } p4;
     struct {
-      float dAqk[CL][F_LD], dAkk[CL][F_LD];        // shared with p6
-      float T[CL][F_LD], dT[CL][F_LD], tmp[CL][F_LD];
+      bf16 dt_hi[CL][K2_LD], dt_lo[CL][K2_LD];     // dT = dTb Diag(beta) [r][m]
+      bf16 tn_hi[CL][K2_LD], tn_lo[CL][K2_LD];     // T [i][m]
+      bf16 tt_hi[CL][K2_LD], tt_lo[CL][K2_LD];     // T^T [r][m]
+      bf16 mt_hi[CL][K2_LD], mt_lo[CL][K2_LD];     // (dT T^T)^T [i][m]
     } p5;
-    struct {
-      float dAqk[CL][F_LD], dAkk[CL][F_LD];
-      union {
-        struct {                                   // single-reference path, part 1
-          bf16 dq_hi[CL][K2_LD], dq_lo[CL][K2_LD]; // dA_qk [r][i]
-          bf16 dk_hi[CL][K2_LD], dk_lo[CL][K2_LD]; // dA_kk [r][i]
-          bf16 yt_hi[HD][K2_LD], yt_lo[HD][K2_LD]; // (k^ e^-G)^T [c][i]
-        } a;
-        struct {                                   // single-reference path, part 2
-          bf16 dat_hi[CL][K1_LD], dat_lo[CL][K1_LD];   // [dA_qk^T | dA_kk^T] [i][128]
-          bf16 xt_hi[HD][K1_LD], xt_lo[HD][K1_LD];     // [q^ e^G ; k^ e^G]^T [c][128]
-        } b;
-        struct {                                   // per-block path
-          bf16 yt_hi[HD][K2_LD], yt_lo[HD][K2_LD];
-          bf16 xt_hi[HD][X_LD], xt_lo[HD][X_LD];
-          bf16 dq_hi[16][K2_LD], dq_lo[16][K2_LD];
-          bf16 dk_hi[16][K2_LD], dk_lo[16][K2_LD];
-          bf16 dat_hi[CL][X_LD], dat_lo[CL][X_LD];
-          float Gb[16][HD], qb[16][HD], kb[16][HD];  // one diagonal block, fp32
-        } g;
-      } u;
+    union {
+      struct {
+        union {
+          struct {                                 // part 1
+            bf16 dq_hi[CL][K2_LD], dq_lo[CL][K2_LD];   // dA_qk [r][i]
+            bf16 dk_hi[CL][K2_LD], dk_lo[CL][K2_LD];   // dA_kk [r][i]
+            bf16 yt_hi[HD][K2_LD], yt_lo[HD][K2_LD];   // Y^T [c][i], Y = k^ times a decay factor
+          } a;
+          struct {                                 // part 2
+            bf16 xt_hi[HD][K1_LD], xt_lo[HD][K1_LD];   // X^T [c][32 I + (q rows | k rows)]
+          } b;
+        } u;
+        bf16 dat_hi[CL][K1_LD], dat_lo[CL][K1_LD]; // [i][32 I + (dA_qk^T | dA_kk^T of block I)]
+      } m;
+      struct {                                     // exact diagonal sums (column layout)
+        float g[CL][GS_LD], q[CL][GS_LD], k[CL][GS_LD];
+      } x;
     } p6;
     struct {
       float dG[CL][GS_LD];
-      bf16 a[CL][HD];
-      float tot[HD];
-      float red[2][2][HD];
+      float tot[4][HD];
+      float red[2][4][HD];
       float rowp[2][2][CL];
     } p7;
   } u;
+  // diagonal 16 x 16 tiles of dA_qk, dA_kk, fp32: [block][row][col]
+  float dqN[4][16][16], dkN[4][16][16];
   float beta[CL], rq[CL], rk[CL], db[CL];
-  float GL[HD], gam[HD], dGL[HD];
+  float dbc[4][CL], dbr[2][CL];
+  float GL[HD], gam[HD], dGL[HD], dgam[HD];
   float Gref[5][HD];       // G before block I (I = 0..3) and G_last (I = 4)
   float dGLw[4][HD];
   int calm_blk[4];
@@ -334,7 +338,59 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   // ------------------------------------------------------------ P3: dKe, dA_qk, dgamma
   f32x4 dAq[2];
   {
-    load_state_panel(bw.dS + ch * HD * HD);
+    // dS_out replaces S_in in the panel. dgamma[c] = sum_j dS_out[c][j] S_in[c][j]
+    // takes S_in from the split panel (hi + lo) just before it is overwritten:
+    // each thread rewrites exactly the elements it reads.
+    {
+      const float* src = bw.dS + ch * HD * HD;
+      f32x4 v[8];
+#pragma unroll
+      for (int rep = 0; rep < 8; ++rep) {
+        const int e = t + NTHR * rep, c = e >> 5, j4 = (e & 31) * 4;
+        v[rep] = *reinterpret_cast<const f32x4*>(src + c * HD + j4);
+      }
+      float part[8];
+#pragma unroll
+      for (int rep = 0; rep < 8; ++rep) {
+        const int e = t + NTHR * rep, c = e >> 5, j4 = (e & 31) * 4;
+        const bf16x4 sh = *reinterpret_cast<const bf16x4*>(SP.hi + c * K1_LD + j4);
+        const bf16x4 sl = *reinterpret_cast<const bf16x4*>(SP.lo + c * K1_LD + j4);
+        float acc = 0.f;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) acc += v[rep][q4] * (bf2f(sh[q4]) + bf2f(sl[q4]));
+        part[rep] = acc;
+        put4(SP, c, j4, v[rep]);
+      }
+      // sum each part[rep] over the 32 lanes that share its channel: halving
+      // exchanges leave lane l with the total of rep = 4 b4 + 2 b3 + b2
+      // (b_k = bit k of l)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const bool up = l & 16;
+        const float send = up ? part[k4] : part[k4 + 4];
+        const float keep = up ? part[k4 + 4] : part[k4];
+        part[k4] = keep + __shfl_xor(send, 16);
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const bool up = l & 8;
+        const float send = up ? part[k2] : part[k2 + 2];
+        const float keep = up ? part[k2 + 2] : part[k2];
+        part[k2] = keep + __shfl_xor(send, 8);
+      }
+      {
+        const bool up = l & 4;
+        const float send = up ? part[0] : part[1];
+        const float keep = up ? part[1] : part[0];
+        part[0] = keep + __shfl_xor(send, 4);
+      }
+      part[0] += __shfl_xor(part[0], 2);
+      part[0] += __shfl_xor(part[0], 1);
+      if ((l & 3) == 0) {
+        const int rep = 4 * ((l >> 4) & 1) + 2 * ((l >> 3) & 1) + ((l >> 2) & 1);
+        sm.dgam[(t >> 5) + 16 * rep] = part[0];
+      }
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_tile_n(U[nt], AP, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
@@ -360,27 +416,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     // dA_qk = scale dO U~^T: rows 16 rb, columns i in tiles 2 chh, 2 chh + 1
     dAq[0] = dAq[1] = zero4();
     mma_row<KDA_SPLIT_B5, 2>(dAq, DOP, 16 * rb, AP, 32 * chh, 0, HD);
-    // dgamma[c] = sum_j dS_out[c][j] S_in[c][j]; four threads per channel
-    {
-      const int c = t >> 2, part = t & 3;
-      const float* dSg = bw.dS + ch * HD * HD + c * HD + 32 * part;
-      const float* Sg = sv.S_in + ch * HD * HD + c * HD + 32 * part;
-      f32x4 xa[8], xb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        xa[j] = *reinterpret_cast<const f32x4*>(dSg + 4 * j);
-        xb[j] = *reinterpret_cast<const f32x4*>(Sg + 4 * j);
-      }
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s += xa[j][0] * xb[j][0] + xa[j][1] * xb[j][1] + xa[j][2] * xb[j][2] + xa[j][3] * xb[j][3];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      __syncthreads();
-      if (part == 0)
-        sm.dGL[c] = s * sm.gam[c] + ((sm.dGLw[0][c] + sm.dGLw[1][c]) + (sm.dGLw[2][c] + sm.dGLw[3][c]));
-    }
     __syncthreads();
+    if (t < HD)
+      sm.dGL[t] = sm.dgam[t] * sm.gam[t] + ((sm.dGLw[0][t] + sm.dGLw[1][t]) + (sm.dGLw[2][t] + sm.dGLw[3][t]));
   }
 
   // ------------------------------------------------------------ P4: dTb = dU~ R^T
@@ -408,103 +446,127 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     __syncthreads();
   }
 
-  // ------------------------------------------------------------ P5: WY / UT backward (fp32)
+  // ------------------------------------------------------------ P5: WY / UT backward
+  // tmp = dT T^T (tmp[r][i] = sum_{m <= min(r, i)} dT[r][m] T[i][m]) and
+  // dX = -T^T tmp (i < r) as split MFMA products; dA_kk = Diag(beta) dX.
+  f32x4 dAk[2];
   {
-    float (*dAqk)[F_LD] = sm.u.p5.dAqk;
-    float (*dAkk)[F_LD] = sm.u.p5.dAkk;
-    float (*Tm)[F_LD] = sm.u.p5.T;
-    float (*dT)[F_LD] = sm.u.p5.dT;
-    float (*tmp)[F_LD] = sm.u.p5.tmp;
+    const Panel DT{&sm.u.p5.dt_hi[0][0], &sm.u.p5.dt_lo[0][0], K2_LD};
+    const Panel TN{&sm.u.p5.tn_hi[0][0], &sm.u.p5.tn_lo[0][0], K2_LD};
+    const Panel TT{&sm.u.p5.tt_hi[0][0], &sm.u.p5.tt_lo[0][0], K2_LD};
+    const Panel MT{&sm.u.p5.mt_hi[0][0], &sm.u.p5.mt_lo[0][0], K2_LD};
     {
-      f32x4 a0 = *reinterpret_cast<const f32x4*>(Tg + 8 * t);
-      f32x4 a1 = *reinterpret_cast<const f32x4*>(Tg + 8 * t + 4);
-      const int r = t >> 3, i8 = (t & 7) * 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Tm[r][i8 + j] = a0[j];
-        Tm[r][i8 + 4 + j] = a1[j];
-      }
+      const int r = t >> 3, m8 = (t & 7) * 8;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(Tg + r * CL + m8);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(Tg + r * CL + m8 + 4);
+      const float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      put8(TN, r, m8, x);
     }
+    {
+      const int r = t & 63, m8 = (t >> 6) * 8;
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = Tg[(m8 + j) * CL + r];
+      put8(TT, r, m8, x);
+    }
+    // dT = dTb Diag(beta) (m <= r), and dbeta_m += sum_r dTb[r][m] T[r][m]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int m = 32 * chh + 16 * nt + dcol();
+      const float bm = sm.beta[m];
+      f32x4 x;
+      float cp = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + drow(i);
+        const float v = m <= r ? dTb[nt][i] : 0.f;
+        x[i] = v * bm;
+        cp += v * Tg[r * CL + m];
+      }
+      store_tile_n(x, DT, 16 * rb, 32 * chh + 16 * nt);
+      cp += __shfl_xor(cp, 16);
+      cp += __shfl_xor(cp, 32);
+      if (l < 16) sm.dbc[rb][m] = cp;
+    }
+    __syncthreads();
+    f32x4 tm[2];
+    tm[0] = tm[1] = zero4();
+    const int kend = ((min(16 * rb + 16, 32 * chh + 32) + 31) / 32) * 32;
+    mma_row<KDA_SPLIT_B8, 2>(tm, DT, 16 * rb, TN, 32 * chh, 0, kend);
+    store_tile_t(tm[0], MT, 16 * rb, 32 * chh);
+    store_tile_t(tm[1], MT, 16 * rb, 32 * chh + 16);
+    __syncthreads();
+    f32x4 dx[2];
+    dx[0] = dx[1] = zero4();
+    mma_row<KDA_SPLIT_B8, 2>(dx, TT, 16 * rb, MT, 32 * chh, (16 * rb / 32) * 32, CL);
+    // dA_kk = beta_r dX (i < r); dbeta_r += sum_i dX[r][i] A_kk[r][i]; dA_qk scaled and masked
+    float rp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + drow(i), c = 32 * chh + 16 * nt + dcol();
-        dT[r][c] = (c <= r) ? dTb[nt][i] : 0.f;
-        dAqk[r][c] = (c <= r) ? d.scale * dAq[nt][i] : 0.f;
+        const float v = c < r ? -dx[nt][i] : 0.f;
+        rp[i] += v * Akk_g[r * CL + c];
+        dAk[nt][i] = sm.beta[r] * v;
+        dAq[nt][i] = c <= r ? d.scale * dAq[nt][i] : 0.f;
       }
-    __syncthreads();
-    if (t < CL) {
-      float s = 0.f;
-      for (int r = t; r < CL; ++r) s += dT[r][t] * Tm[r][t];
-      sm.db[t] = s;
-    }
-    __syncthreads();
 #pragma unroll
-    for (int rep = 0; rep < 8; ++rep) {
-      const int e = t + NTHR * rep, r = e >> 6, m = e & 63;
-      dT[r][m] *= sm.beta[m];
-    }
-    __syncthreads();
-    // tmp = dT T^T : tmp[r][i] = sum_{m <= min(r, i)} dT[r][m] T[i][m]
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int rep = 0; rep < 8; ++rep) {
-      const int e = t + NTHR * rep, r = e >> 6, i = e & 63;
-      const int mmax = min(r, i);
-      float s = 0.f;
-      for (int m = 0; m <= mmax; ++m) s += dT[r][m] * Tm[i][m];
-      tmp[r][i] = s;
-    }
-    __syncthreads();
-    {
-      // dX[r][i] = -sum_{m >= r} T[m][r] tmp[m][i] (i < r); eight threads per row
-      const int r = t >> 3, part = t & 7;
-      const f32x4 ak0 = *reinterpret_cast<const f32x4*>(Akk_g + r * CL + 8 * part);
-      const f32x4 ak1 = *reinterpret_cast<const f32x4*>(Akk_g + r * CL + 8 * part + 4);
-      float dbr = 0.f;
+      for (int m = 1; m < 16; m <<= 1) rp[i] += __shfl_xor(rp[i], m);
+    if (dcol() == 0) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int i = 8 * part + jj;
-        float dx = 0.f;
-        if (i < r) {
-          float s = 0.f;
-          for (int m = r; m < CL; ++m) s += Tm[m][r] * tmp[m][i];
-          dx = -s;
-        }
-        dAkk[r][i] = sm.beta[r] * dx;
-        dbr += dx * (jj < 4 ? ak0[jj] : ak1[jj - 4]);
-      }
-      dbr += __shfl_xor(dbr, 1);
-      dbr += __shfl_xor(dbr, 2);
-      dbr += __shfl_xor(dbr, 4);
-      __syncthreads();
-      if (part == 0) sm.db[r] += dbr;
+      for (int i = 0; i < 4; ++i) sm.dbr[chh][16 * rb + drow(i)] = rp[i];
     }
     __syncthreads();
+    if (t < CL)
+      sm.db[t] = ((sm.dbc[0][t] + sm.dbc[1][t]) + (sm.dbc[2][t] + sm.dbc[3][t])) +
+                 (sm.dbr[0][t] + sm.dbr[1][t]);
   }
 
   // ------------------------------------------------------------ P6: decayed-product backward
+  // dq_r += sum_i dA_qk[r][i] k^_i e^(G_r - G_i),  dk_r += sum_i dA_kk[r][i] k^_i e^(G_r - G_i),
+  // dk_i += sum_r (dA_qk[r][i] q^_r + dA_kk[r][i] k^_r) e^(G_r - G_i), with the matching
+  // + / - pair terms of dG.
   {
-    float (*dAqk)[F_LD] = sm.u.p6.dAqk;
-    float (*dAkk)[F_LD] = sm.u.p6.dAkk;
-    if (sm.calm_chunk) {
-      // single reference at the chunk start
-      const Panel DQ{&sm.u.p6.u.a.dq_hi[0][0], &sm.u.p6.u.a.dq_lo[0][0], K2_LD};
-      const Panel DK{&sm.u.p6.u.a.dk_hi[0][0], &sm.u.p6.u.a.dk_lo[0][0], K2_LD};
-      const Panel YT{&sm.u.p6.u.a.yt_hi[0][0], &sm.u.p6.u.a.yt_lo[0][0], K2_LD};
-      {
-        const int r = t >> 3, i8 = (t & 7) * 8;
-        put8(DQ, r, i8, &dAqk[r][i8]);
-        put8(DK, r, i8, &dAkk[r][i8]);
-      }
+    const Panel DQ{&sm.u.p6.m.u.a.dq_hi[0][0], &sm.u.p6.m.u.a.dq_lo[0][0], K2_LD};
+    const Panel DK{&sm.u.p6.m.u.a.dk_hi[0][0], &sm.u.p6.m.u.a.dk_lo[0][0], K2_LD};
+    const Panel YT{&sm.u.p6.m.u.a.yt_hi[0][0], &sm.u.p6.m.u.a.yt_lo[0][0], K2_LD};
+    const Panel XT{&sm.u.p6.m.u.b.xt_hi[0][0], &sm.u.p6.m.u.b.xt_lo[0][0], K1_LD};
+    const Panel DAT{&sm.u.p6.m.dat_hi[0][0], &sm.u.p6.m.dat_lo[0][0], K1_LD};
+    const bool calm = sm.calm_chunk;
+    const bool blk_calm = sm.calm_blk[rb];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        f32x4 y;
+    for (int nt = 0; nt < 2; ++nt) {
+      store_tile_n(dAq[nt], DQ, 16 * rb, 32 * chh + 16 * nt);
+      store_tile_n(dAk[nt], DK, 16 * rb, 32 * chh + 16 * nt);
+      store_tile_t(dAq[nt], DAT, 32 * rb, 32 * chh + 16 * nt);
+      store_tile_t(dAk[nt], DAT, 32 * rb + 16, 32 * chh + 16 * nt);
+    }
+    if (!calm && chh == (rb >> 1)) {
+      // this wave holds the diagonal tile (rb, rb) of both matrices
+      const f32x4 aq = (rb & 1) ? dAq[1] : dAq[0];
+      const f32x4 ak = (rb & 1) ? dAk[1] : dAk[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = EK(nt, i) * fexp(-eG[nt][i]);
-        put4(YT, 64 * chh + 16 * nt + dcol(), 16 * rb + 4 * (l >> 4), y);
+      for (int i = 0; i < 4; ++i) {
+        sm.dqN[rb][drow(i)][dcol()] = aq[i];
+        sm.dkN[rb][drow(i)][dcol()] = ak[i];
       }
-      __syncthreads();
+    }
+    // Y^T [c][i]: k^_i e^(-G_i) (one reference at the chunk start), or
+    // k^_i e^(rho_end(J) - G_i) with rho_end(J) = G at the end of i's block J
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int c = 64 * chh + 16 * nt + dcol();
+      const float ref = calm ? 0.f : sm.Gref[rb + 1][c];
+      f32x4 y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = EK(nt, i) * fexp(ref - eG[nt][i]);
+      put4(YT, c, 16 * rb + 4 * (l >> 4), y);
+    }
+    __syncthreads();
+    if (calm) {
       const int kend = ((16 * rb + 16 + 31) / 32) * 32;
       f32x4 aq[4], ak[4];
 #pragma unroll
@@ -521,41 +583,55 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           adk[nt][i] += dka;
           adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
         }
-      __syncthreads();
-      const Panel DAT{&sm.u.p6.u.b.dat_hi[0][0], &sm.u.p6.u.b.dat_lo[0][0], K1_LD};
-      const Panel XT{&sm.u.p6.u.b.xt_hi[0][0], &sm.u.p6.u.b.xt_lo[0][0], K1_LD};
-      {
-        const int i = t & 63, part = t >> 6;           // part: 8 groups of 8 rows (qk 0-3, kk 4-7)
-        const int r8 = (part & 3) * 16, isk = part >> 2;
-        float x[8], y[8];
+    } else {
+      // block J of the columns: sum over i in J on MFMA, then the factor
+      // e^(G_r - rho_end(J)) <= 1 (J < rb); the diagonal block only when calm
+      const int jend = blk_calm ? rb : rb - 1;
+      for (int J = 0; J <= jend; ++J) {
+        f32x4 aq[4], ak[4];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          x[jj] = isk ? dAkk[r8 + jj][i] : dAqk[r8 + jj][i];
-          y[jj] = isk ? dAkk[r8 + 8 + jj][i] : dAqk[r8 + 8 + jj][i];
+        for (int nt = 0; nt < 4; ++nt) {
+          aq[nt] = ak[nt] = zero4();
+          mma_k16<KDA_SPLIT_B7>(aq[nt], DQ, 16 * rb, YT, 64 * chh + 16 * nt, 16 * J);
+          mma_k16<KDA_SPLIT_B7>(ak[nt], DK, 16 * rb, YT, 64 * chh + 16 * nt, 16 * J);
         }
-        put8(DAT, i, 64 * isk + r8, x);
-        put8(DAT, i, 64 * isk + r8 + 8, y);
-      }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        f32x4 xq, xk;
+        for (int nt = 0; nt < 4; ++nt) {
+          const float ref = sm.Gref[J + 1][64 * chh + 16 * nt + dcol()];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e1 = fexp(eG[nt][i]);
-          xq[i] = EQ(nt, i) * e1;
-          xk[i] = EK(nt, i) * e1;
+          for (int i = 0; i < 4; ++i) {
+            const float e1 = fexp(eG[nt][i] - ref);
+            const float dqa = aq[nt][i] * e1, dka = ak[nt][i] * e1;
+            adq[nt][i] += dqa;
+            adk[nt][i] += dka;
+            adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
+          }
         }
-        const int c = 64 * chh + 16 * nt + dcol(), r0 = 16 * rb + 4 * (l >> 4);
-        put4(XT, c, r0, xq);
-        put4(XT, c, 64 + r0, xk);
       }
-      __syncthreads();
+    }
+    __syncthreads();
+    // X^T [c][32 I + ...]: q^_r, k^_r times e^(G_r) or e^(G_r - rho_start(I)),
+    // rho_start(I) = G before block I
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int c = 64 * chh + 16 * nt + dcol();
+      const float ref = calm ? 0.f : sm.Gref[rb][c];
+      f32x4 xq, xk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e1 = fexp(eG[nt][i] - ref);
+        xq[i] = EQ(nt, i) * e1;
+        xk[i] = EK(nt, i) * e1;
+      }
+      put4(XT, c, 32 * rb + 4 * (l >> 4), xq);
+      put4(XT, c, 32 * rb + 16 + 4 * (l >> 4), xk);
+    }
+    __syncthreads();
+    if (calm) {
       f32x4 ac[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
-      const int kb = (16 * rb / 32) * 32;
-      mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, kb, CL);
-      mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, CL + kb, 2 * CL);
+      mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 32 * rb, 2 * CL);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -564,135 +640,91 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           adk[nt][i] += dka;
           adG[nt][i] -= dka * EK(nt, i);
         }
-      __syncthreads();
     } else {
-      // one reference per 16-row block
-      const Panel YT{&sm.u.p6.u.g.yt_hi[0][0], &sm.u.p6.u.g.yt_lo[0][0], K2_LD};
-      const Panel XT{&sm.u.p6.u.g.xt_hi[0][0], &sm.u.p6.u.g.xt_lo[0][0], X_LD};
-      const Panel DQ{&sm.u.p6.u.g.dq_hi[0][0], &sm.u.p6.u.g.dq_lo[0][0], K2_LD};
-      const Panel DK{&sm.u.p6.u.g.dk_hi[0][0], &sm.u.p6.u.g.dk_lo[0][0], K2_LD};
-      const Panel DAT{&sm.u.p6.u.g.dat_hi[0][0], &sm.u.p6.u.g.dat_lo[0][0], X_LD};
-      for (int I = 0; I < 4; ++I) {
-        const int calm = sm.calm_blk[I];
-        const int ny = 16 * I + 16;
-        const int nyk = ((ny + 31) / 32) * 32;
-        // Y^T [c][i]: rows of this thread's block, zero unless before block I
-        // (or block I itself when its span is narrow)
+      // block I of the rows r: factor e^(rho_start(I) - G_i) <= 1 (I > rb)
+      for (int I = blk_calm ? rb : rb + 1; I < 4; ++I) {
+        f32x4 ac[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
+        mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 32 * I, 32 * I + 32);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const int c = 64 * chh + 16 * nt + dcol();
-          const float rho = sm.Gref[I][c];
-          const bool on = rb < I || (rb == I && calm);
-          f32x4 y;
+          const float ref = sm.Gref[I][64 * chh + 16 * nt + dcol()];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = on ? EK(nt, i) * fexp(rho - eG[nt][i]) : 0.f;
-          put4(YT, c, 16 * rb + 4 * (l >> 4), y);
-          if (rb == I) {
-            f32x4 xq, xk;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float e1 = fexp(eG[nt][i] - rho);
-              xq[i] = EQ(nt, i) * e1;
-              xk[i] = EK(nt, i) * e1;
-            }
-            put4(XT, c, 4 * (l >> 4), xq);
-            put4(XT, c, 16 + 4 * (l >> 4), xk);
+          for (int i = 0; i < 4; ++i) {
+            const float dka = ac[nt][i] * fexp(ref - eG[nt][i]);
+            adk[nt][i] += dka;
+            adG[nt][i] -= dka * EK(nt, i);
           }
-        }
-        if (t < 128) {
-          const int rr = t >> 3, i8 = (t & 7) * 8;
-          put8(DQ, rr, i8, &dAqk[16 * I + rr][i8]);
-          put8(DK, rr, i8, &dAkk[16 * I + rr][i8]);
-        } else if (t < 128 + 256) {
-          const int e = t - 128, i = e & 63, part = e >> 6;   // 4 parts of 8
-          const int isk = part >> 1, rr0 = (part & 1) * 8;
-          float x[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            x[jj] = isk ? dAkk[16 * I + rr0 + jj][i] : dAqk[16 * I + rr0 + jj][i];
-          put8(DAT, i, 16 * isk + rr0, x);
-        }
-        __syncthreads();
-        if (rb == I) {
-          f32x4 aq[4], ak[4];
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) aq[nt] = ak[nt] = zero4();
-          mma_row<KDA_SPLIT_B7, 4>(aq, DQ, 0, YT, 64 * chh, 0, nyk);
-          mma_row<KDA_SPLIT_B7, 4>(ak, DK, 0, YT, 64 * chh, 0, nyk);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const float rho = sm.Gref[I][64 * chh + 16 * nt + dcol()];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float e1 = fexp(eG[nt][i] - rho);
-              const float dqa = aq[nt][i] * e1, dka = ak[nt][i] * e1;
-              adq[nt][i] += dqa;
-              adk[nt][i] += dka;
-              adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
-            }
-          }
-        }
-        if (rb < I || (rb == I && calm)) {
-          f32x4 ac[4];
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
-          mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 0, 32);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const float rho = sm.Gref[I][64 * chh + 16 * nt + dcol()];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float dka = ac[nt][i] * fexp(rho - eG[nt][i]);
-              adk[nt][i] += dka;
-              adG[nt][i] -= dka * EK(nt, i);
-            }
-          }
-        }
-        __syncthreads();
-        if (!calm) {
-          // exact fp32 sums for the pairs inside block I
-          if (rb == I) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int rl = drow(i), c = 64 * chh + 16 * nt + dcol();
-                sm.u.p6.u.g.Gb[rl][c] = eG[nt][i];
-                sm.u.p6.u.g.qb[rl][c] = EQ(nt, i);
-                sm.u.p6.u.g.kb[rl][c] = EK(nt, i);
-              }
-          }
-          __syncthreads();
-          if (rb == I) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int rl = drow(i), r = 16 * I + rl, c = 64 * chh + 16 * nt + dcol();
-                const float gr = eG[nt][i], qr = EQ(nt, i), kr = EK(nt, i);
-                float dq_s = 0.f, dk_s = 0.f, dG_s = 0.f;
-                for (int il = 0; il <= rl; ++il) {
-                  const float kk = sm.u.p6.u.g.kb[il][c] * fexp(gr - sm.u.p6.u.g.Gb[il][c]);
-                  const float a = dAqk[r][16 * I + il], b = dAkk[r][16 * I + il];
-                  dq_s += a * kk;
-                  dk_s += b * kk;
-                  dG_s += (a * qr + b * kr) * kk;
-                }
-                for (int r2 = rl; r2 < 16; ++r2) {
-                  const float E = fexp(sm.u.p6.u.g.Gb[r2][c] - gr);
-                  const float s = (dAqk[16 * I + r2][r] * sm.u.p6.u.g.qb[r2][c] +
-                                   dAkk[16 * I + r2][r] * sm.u.p6.u.g.kb[r2][c]) * E;
-                  dk_s += s;
-                  dG_s -= s * kr;
-                }
-                adq[nt][i] += dq_s;
-                adk[nt][i] += dk_s;
-                adG[nt][i] += dG_s;
-              }
-          }
-          __syncthreads();
         }
       }
+    }
+    __syncthreads();
+    if (!calm && !(sm.calm_blk[0] & sm.calm_blk[1] & sm.calm_blk[2] & sm.calm_blk[3])) {
+      // Diagonal blocks too wide for one reference: every pair (r, i) of the
+      // block is summed with its exact factor e^(G_r - G_i) <= 1 in fp32.
+      // Column layout: thread (I, c) holds rows 16 I .. 16 I + 15 of channel c.
+      float (*Xg)[GS_LD] = sm.u.p6.x.g;
+      float (*Xq)[GS_LD] = sm.u.p6.x.q;
+      float (*Xk)[GS_LD] = sm.u.p6.x.k;
+      if (!blk_calm) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rb + drow(i), c = 64 * chh + 16 * nt + dcol();
+            Xg[r][c] = eG[nt][i];
+            Xq[r][c] = EQ(nt, i);
+            Xk[r][c] = EK(nt, i);
+          }
+      }
+      __syncthreads();
+      const int I = t >> 7, c = t & 127;
+      if (!sm.calm_blk[I]) {
+        float g[16], qv[16], kv[16], sq[16], sk[16], sg[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          g[j] = Xg[16 * I + j][c];
+          qv[j] = Xq[16 * I + j][c];
+          kv[j] = Xk[16 * I + j][c];
+          sq[j] = sk[j] = sg[j] = 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+          for (int i = 0; i <= r; ++i) {
+            const float E = fexp(g[r] - g[i]);
+            const float a = sm.dqN[I][r][i], b = sm.dkN[I][r][i];
+            const float ke = kv[i] * E;
+            const float wgt = a * qv[r] + b * kv[r];
+            sq[r] += a * ke;
+            sk[r] += b * ke;
+            sg[r] += wgt * ke;
+            const float s2 = wgt * E;
+            sk[i] += s2;
+            sg[i] -= s2 * kv[i];
+          }
+        // each thread overwrites only the entries it read
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          Xg[16 * I + j][c] = sg[j];
+          Xq[16 * I + j][c] = sq[j];
+          Xk[16 * I + j][c] = sk[j];
+        }
+      }
+      __syncthreads();
+      if (!blk_calm) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rb + drow(i), c2 = 64 * chh + 16 * nt + dcol();
+            adq[nt][i] += Xq[r][c2];
+            adk[nt][i] += Xk[r][c2];
+            adG[nt][i] += Xg[r][c2];
+          }
+      }
+      __syncthreads();
     }
   }
 
@@ -706,18 +738,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         const int r = 16 * rb + drow(i), c = 64 * chh + 16 * nt + dcol();
         dG[r][c] = adG[nt][i] + (r == CL - 1 ? sm.dGL[c] : 0.f);
       }
-    const bf16* araw = reinterpret_cast<const bf16*>(in.gate);
-    if (d.raw) {
-#pragma unroll
-      for (int rep = 0; rep < 2; ++rep) {
-        const int e = t + NTHR * rep, r = e >> 4, c8 = (e & 15) * 8;
-        *reinterpret_cast<bf16x8*>(&sm.u.p7.a[r][c8]) =
-            *reinterpret_cast<const bf16x8*>(araw + rowidx(clampr(r)) * HD + c8);
-      }
-    }
     // L2 row dot products <x^, dx^> over the 128 channels
-    float pq[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
     if (d.l2norm) {
+      float pq[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -740,29 +763,38 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         }
       }
     }
-    __syncthreads();
-    // reverse cumsum within the chunk; two threads per channel (rows 32-63, 0-31)
-    const int cc = t & 127, half = (t >> 7) & 1;
-    const bool active = t < 256;
-    if (active) {
-      float run = 0.f;
-      for (int r = 32 * half + 31; r >= 32 * half; --r) {
-        run += dG[r][cc];
-        dG[r][cc] = run;
-      }
-      if (half == 1) sm.u.p7.tot[cc] = run;
+    // column layout: thread (I, c) owns rows 16 I .. 16 I + 15 of channel c
+    const int I = t >> 7, cc = t & 127;
+    const bf16* araw = reinterpret_cast<const bf16*>(in.gate);
+    float av[16];
+    if (d.raw) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) av[j] = bf2f(araw[rowidx(clampr(16 * I + j)) * HD + cc]);
     }
     __syncthreads();
+    // reverse cumsum inside the chunk: dg_j = sum_{r >= j} dG_r
+    float v[16];
+    float run = 0.f;
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      run += dG[16 * I + j][cc];
+      v[j] = run;
+    }
+    sm.u.p7.tot[I][cc] = run;
+    __syncthreads();
+    float carry = 0.f;
+    for (int I2 = 3; I2 > I; --I2) carry += sm.u.p7.tot[I2][cc];
     float pdt = 0.f, pA = 0.f;
-    if (active) {
-      const float base = half == 0 ? sm.u.p7.tot[cc] : 0.f;
-      const float ea = d.raw ? __expf(in.A_log[h]) : 0.f;
-      const float dtb = d.raw ? in.dt_bias[h * HD + cc] : 0.f;
-      for (int r = 32 * half; r < 32 * half + 32 && r < n; ++r) {
-        const float dg = dG[r][cc] + base;
+    const float ea = d.raw ? __expf(in.A_log[h]) : 0.f;
+    const float dtb = d.raw ? in.dt_bias[h * HD + cc] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * I + j;
+      if (r < n) {
+        const float dg = v[j] + carry;
         const int64_t idx = rowidx(r) * HD + cc;
         if (d.raw) {
-          const float z = bf2f(sm.u.p7.a[r][cc]) + dtb;
+          const float z = av[j] + dtb;
           const float dz = dg * (-ea) * sigmoid(z);
           reinterpret_cast<bf16*>(out.dgate)[idx] = f2bf(dz);
           pdt += dz;
@@ -771,15 +803,21 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           reinterpret_cast<float*>(out.dgate)[idx] = dg;
         }
       }
-      sm.u.p7.red[0][half][cc] = pdt;
-      sm.u.p7.red[1][half][cc] = pA;
+    }
+    if (d.raw) {
+      sm.u.p7.red[0][I][cc] = pdt;
+      sm.u.p7.red[1][I][cc] = pA;
     }
     __syncthreads();
     if (d.raw) {
-      if (t < HD) bw.part_dt[ch * HD + t] = sm.u.p7.red[0][0][t] + sm.u.p7.red[0][1][t];
+      if (t < HD)
+        bw.part_dt[ch * HD + t] = (sm.u.p7.red[0][0][t] + sm.u.p7.red[0][1][t]) +
+                                  (sm.u.p7.red[0][2][t] + sm.u.p7.red[0][3][t]);
       if (t == HD) {
         float s = 0.f;
-        for (int c2 = 0; c2 < HD; ++c2) s += sm.u.p7.red[1][0][c2] + sm.u.p7.red[1][1][c2];
+        for (int c2 = 0; c2 < HD; ++c2)
+          s += (sm.u.p7.red[1][0][c2] + sm.u.p7.red[1][1][c2]) +
+               (sm.u.p7.red[1][2][c2] + sm.u.p7.red[1][3][c2]);
         bw.part_A[ch] = s;
       }
     }

@@ -140,6 +140,29 @@ KDA_DEV void mma_row(f32x4 (&acc)[NT], const Panel& A, int m0, const Panel& B, i
   }
 }
 
+// acc += A[m0:m0+16, k0:k0+16] * B[n0:n0+16, k0:k0+16]^T: a K = 16 product on
+// the K = 32 instruction. Lanes 32..63 carry K = 16..31, which is zeroed (they
+// read the same in-range elements as lanes 0..31, then drop them).
+template <int SPLIT>
+KDA_DEV void mma_k16(f32x4& acc, const Panel& A, int m0, const Panel& B, int n0, int k0) {
+  const int l = lane_id();
+  const bool on = l < 32;
+  const int ko = k0 + ((l >> 4) & 1) * 8;
+  const int ar = (m0 + (l & 15)) * A.ld + ko, br = (n0 + (l & 15)) * B.ld + ko;
+  const bf16x8 z = {};
+  const bf16x8 ah = on ? *reinterpret_cast<const bf16x8*>(A.hi + ar) : z;
+  const bf16x8 bh = on ? *reinterpret_cast<const bf16x8*>(B.hi + br) : z;
+  if (SPLIT & SPLIT_A) {
+    const bf16x8 al = on ? *reinterpret_cast<const bf16x8*>(A.lo + ar) : z;
+    acc = mfma16(al, bh, acc);
+  }
+  if (SPLIT & SPLIT_B) {
+    const bf16x8 bl = on ? *reinterpret_cast<const bf16x8*>(B.lo + br) : z;
+    acc = mfma16(ah, bl, acc);
+  }
+  acc = mfma16(ah, bh, acc);
+}
+
 // Split-store one fp32 value into a panel.
 KDA_DEV void put(const Panel& P, int row, int col, float x) {
   const bf16 h = f2bf(x);
