@@ -78,6 +78,11 @@ kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states, float** G)
   return sv;
 }
 
+// Operand panels of the forward scan (bf16, fwd_panel layout per chunk-head).
+void* carve_panels(Carver& c, const Sizes& s) {
+  return c.take<uint16_t>((size_t)s.NC * s.H * kda::fwd_panel::ELEMS);
+}
+
 kda::BwdWork carve_bwd(Carver& c, const Sizes& s) {
   kda::BwdWork bw;
   bw.dS = c.take<float>((size_t)s.NC * s.H * 128 * 128);
@@ -137,6 +142,7 @@ size_t fwd_ws_bytes(const Sizes& s) {
   carve_table(c, s);
   float* G;
   carve_saved(c, s, 0, &G);
+  carve_panels(c, s);
   return c.off;
 }
 
@@ -147,6 +153,7 @@ size_t bwd_ws_bytes(const Sizes& s, int replay) {
   if (replay) {
     float* G;
     carve_saved(c, s, 1, &G);
+    carve_panels(c, s);
   }
   return c.off;
 }
@@ -214,16 +221,15 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   Carver wc(workspace);
   const kda::ChunkTable ct = carve_table(wc, s);
   float* G = nullptr;
-  kda::SavedSet sv;
+  kda::SavedSet sv = carve_saved(wc, s, 0, &G);   // used when nothing is saved
+  void* panels = carve_panels(wc, s);
   if (saved) {
     Carver sc(saved);
     sv = carve_saved(sc, s, 1, &G);
-  } else {
-    sv = carve_saved(wc, s, 0, &G);
   }
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
-  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, hs));
-  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, G, sv, o, saved != nullptr, hs));
+  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, hs));
+  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, o, saved != nullptr, hs));
   return KDA_OK;
 }
 
@@ -275,8 +281,10 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   const kda::BwdWork bw = carve_bwd(wc, s);
   float* G = nullptr;
   kda::SavedSet sv;
+  void* panels = nullptr;
   if (replay) {
     sv = carve_saved(wc, s, 1, &G);
+    panels = carve_panels(wc, s);
   } else {
     Carver sc(const_cast<void*>(saved));
     sv = carve_saved(sc, s, 1, &G);
@@ -284,8 +292,8 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   if (replay) {
-    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, hs));
-    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, G, sv, nullptr, 1, hs));
+    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, hs));
+    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, nullptr, 1, hs));
   }
   LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, G, sv, dO, dv, bw, hs));
   LAUNCH("bwd_intra", kda::launch_bwd_intra(d, in, ct, G, sv, dO, out, bw, hs));

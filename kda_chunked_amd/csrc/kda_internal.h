@@ -69,12 +69,26 @@ struct BwdWork {
   float* part_dt;     // [NC, H, 128] raw form: per-chunk sum of dz
 };
 
+// Per chunk-head operand panels of the forward scan, written by the prep
+// kernel as bf16 planes (hi = RNE(x), lo = RNE(x - hi)) in the row-major
+// layout the scan stages into LDS. Offsets in bf16 elements.
+namespace fwd_panel {
+constexpr int KD = 0;                        // -Kd hi            [64][128]
+constexpr int QD = KD + 64 * 128;            // scale Qd hi, lo   [2][64][128]
+constexpr int KE = QD + 2 * 64 * 128;        // Ke^T hi, lo       [2][128][64]
+constexpr int TB = KE + 2 * 128 * 64;        // Tb hi             [64][64]
+constexpr int AQ = TB + 64 * 64;             // scale A_qk hi, lo [2][64][64]
+constexpr int GAM = AQ + 2 * 64 * 64;        // e^(G_last), fp32  [128]
+constexpr int ELEMS = GAM + 2 * 128;         // bf16 elements per chunk-head
+constexpr size_t BYTES = (size_t)ELEMS * 2;  // 107008, a multiple of 16
+}  // namespace fwd_panel
+
 hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
                             hipStream_t s);
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
-                           const SavedSet& sv, hipStream_t s);
+                           const SavedSet& sv, void* panels, hipStream_t s);
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                           const float* G, const SavedSet& sv, void* o, int save_states,
+                           const SavedSet& sv, const void* panels, void* o, int save_states,
                            hipStream_t s);
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const float* G, const SavedSet& sv, const void* dO, void* dv,

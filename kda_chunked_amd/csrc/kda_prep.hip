@@ -9,12 +9,16 @@
 //   T = (I + Diag(beta) A_kk)^-1                          (UT/WY solve)
 //
 // Fast-decay safety. e^(G_r - G_i) is formed from two factors that never
-// overflow: rows of block I (16 rows) use the reference rho_I = G at the row
-// before the block, X_r = x_r e^(G_r - rho_I) <= 1 and, for columns i before
-// the block, Y_i = k_i e^(rho_I - G_i) <= 1. For columns inside the block the
-// second factor exceeds 1; it is used only when the block's own decay span is
-// at most CALM_SPAN in every channel, otherwise that diagonal tile is summed
-// element by element in fp32.
+// overflow. A tile of rows in block I and columns in block J < I uses the
+// reference rho = G at the end of block J: x_r e^(G_r - rho) <= 1 and
+// k_i e^(rho - G_i) <= 1. A diagonal tile uses rho = G before the block, so the
+// second factor is at most e^(span of the block); it is used only when that
+// span is at most CALM_SPAN in every channel, otherwise the tile is summed
+// element by element in fp32 with the exact factor.
+//
+// Besides the saved fp32 matrices, the kernel writes the forward scan's
+// operand panels (-Kd, scale Qd, Ke^T, Tb, scale A_qk as bf16 hi/lo planes and
+// e^(G_last)), so that the sequential scan only streams them.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -73,44 +77,54 @@ hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& 
 }
 
 // ---------------------------------------------------------------------------
-// The prep kernel: 512 threads (8 waves). Thread t owns row rA = t >> 3 and
-// channels cA .. cA+15 (cA = 16 (t & 7)) of every 64 x 128 chunk quantity.
+// The prep kernel: 512 threads (8 waves). For loads and the elementwise
+// panels, thread t owns row rA = t >> 3 and channels cA .. cA+15 (cA = 16 (t & 7)).
 constexpr int NT_PREP = 512;
-constexpr int GS_LD = HD + 1;     // fp32 row stride of G (scalar accesses only)
-constexpr int XS_LD = HD + 8;     // bf16 row stride of the K = 128 panels
+constexpr int GP_LD = HD + 4;     // fp32 rows of G (16-byte aligned rows)
+constexpr int XS_LD = HD + 8;     // bf16 rows of the raw q, k
 constexpr int F_LD = CL + 1;      // fp32 64 x 64 matrices
 
 struct PrepSmem {
-  float G[CL][GS_LD];
+  float G[CL][GP_LD];
+  bf16 qs[CL][XS_LD], ks[CL][XS_LD];   // raw q, k (rows >= n repeat row n - 1)
+  float Akk[CL][F_LD], Aqk[CL][F_LD];
+  float Tm[CL][F_LD];
+  float Z[3][16][17];
+  float Gref[5][HD];       // G before block I (I = 0..3) and G_last (I = 4)
   float qtot[4][HD];
   float nrm[2][8][CL];
   float rq[CL], rk[CL], beta[CL];
-  float rho[4][HD];
   int calm_blk[4];
-  int calm_chunk;
-  union {
-    struct {                                   // single reference: Kd, Qd, Y = k^ e^-G
-      bf16 xk_hi[CL][XS_LD], xk_lo[CL][XS_LD];
-      bf16 xq_hi[CL][XS_LD], xq_lo[CL][XS_LD];
-      bf16 y_hi[CL][XS_LD], y_lo[CL][XS_LD];
-    } a;
-    struct {                                   // one reference per 16-row block
-      bf16 xk_hi[16][XS_LD], xk_lo[16][XS_LD];
-      bf16 xq_hi[16][XS_LD], xq_lo[16][XS_LD];
-      bf16 y_hi[CL][XS_LD], y_lo[CL][XS_LD];
-      bf16 qs[CL][XS_LD], ks[CL][XS_LD];       // raw q, k for the exact diagonal sums
-    } b;
-    struct {
-      float Tm[CL][F_LD];
-      float Z[3][16][17];
-    } s;
-  } u;
-  float Akk[CL][F_LD];
 };
+
+// Tile (I, J), J <= I, of the lower triangle of 16 x 16 blocks.
+KDA_DEV void tile_of(int item, int& I, int& J) {
+  I = item < 1 ? 0 : item < 3 ? 1 : item < 6 ? 2 : 3;
+  J = item - I * (I + 1) / 2;
+}
+
+// One 8-channel MFMA fragment of x e^(+-(G - ref)) for row `row`, channels
+// c .. c+7, split into hi and lo planes. sgn = +1: x e^(G - ref); -1: x e^(ref - G).
+KDA_DEV void decayed_frag(const PrepSmem& sm, const bf16 (*x)[XS_LD], float rx, int row, int c,
+                          const float* ref, float sgn, bf16x8& hi, bf16x8& lo) {
+  const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.G[row][c]);
+  const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.G[row][c + 4]);
+  const f32x4 r0 = *reinterpret_cast<const f32x4*>(ref + c);
+  const f32x4 r1 = *reinterpret_cast<const f32x4*>(ref + c + 4);
+  const bf16x8 xv = *reinterpret_cast<const bf16x8*>(&x[row][c]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float gj = j < 4 ? g0[j] : g1[j - 4];
+    const float rj = j < 4 ? r0[j] : r1[j - 4];
+    const float v = bf2f(xv[j]) * rx * fexp(sgn * (gj - rj));
+    hi[j] = f2bf(v);
+    lo[j] = f2bf(v - bf2f(hi[j]));
+  }
+}
 
 __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, ChunkTable ct,
                                                             float* __restrict__ G_out,
-                                                            SavedSet sv) {
+                                                            SavedSet sv, bf16* __restrict__ panels) {
   __shared__ PrepSmem sm;
   const int ci = blockIdx.x, h = blockIdx.y;
   if (ci >= ct.doc_c0[d.N]) return;
@@ -127,10 +141,10 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   const int64_t baseA = ((t0 + (okA ? rA : n - 1)) * H + h) * HD + cA;
 
   // ---- 1. loads (all issued before use): q, k, gate of this thread's 16 elements
-  bf16x8 q0 = *reinterpret_cast<const bf16x8*>(q + baseA);
-  bf16x8 q1 = *reinterpret_cast<const bf16x8*>(q + baseA + 8);
-  bf16x8 k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
-  bf16x8 k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
+  const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(q + baseA);
+  const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(q + baseA + 8);
+  const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
+  const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
   float g[16];
   if (!d.raw) {
     const float* gp = reinterpret_cast<const float*>(in.gate) + baseA;
@@ -150,8 +164,14 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       g[j] = -ea * softplus(bf2f(j < 8 ? a0[j] : a1[j - 8]) + in.dt_bias[h * HD + cA + j]);
   }
   if (t < CL) sm.beta[t] = t < n ? bf2f(beta[(t0 + (t < n ? t : n - 1)) * H + h]) : 0.f;
+  *reinterpret_cast<bf16x8*>(&sm.qs[rA][cA]) = q0;
+  *reinterpret_cast<bf16x8*>(&sm.qs[rA][cA + 8]) = q1;
+  *reinterpret_cast<bf16x8*>(&sm.ks[rA][cA]) = k0;
+  *reinterpret_cast<bf16x8*>(&sm.ks[rA][cA + 8]) = k1;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) sm.G[rA][cA + j] = okA ? g[j] : 0.f;
+  for (int j = 0; j < 16; j += 4)
+    *reinterpret_cast<f32x4*>(&sm.G[rA][cA + j]) =
+        okA ? f32x4{g[j], g[j + 1], g[j + 2], g[j + 3]} : zero4();
   // L2 row sums: partial over this thread's 16 channels
   {
     float sq = 0.f, sk = 0.f;
@@ -191,16 +211,34 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
         sv.rk[(t0 + t) * H + h] = rk;
       }
     }
+    if (t < 4) sm.calm_blk[t] = 1;
     __syncthreads();
     float carry = 0.f;
     for (int j = 0; j < qr; ++j) carry += sm.qtot[j][c];
     if (qr > 0)
       for (int r = 16 * qr; r < 16 * qr + 16; ++r) sm.G[r][c] += carry;
   }
-  if (t < 4) sm.calm_blk[t] = 1;
-  if (t == 4) sm.calm_chunk = 1;
   __syncthreads();
-  // this thread's G (rows >= n hold G[n-1] because their g is 0)
+  // references: G before each 16-row block and G_last (rows >= n hold G[n-1],
+  // their g being 0); a block is calm when its own decay span is <= CALM_SPAN
+  if (t < HD) {
+    sm.Gref[0][t] = 0.f;
+#pragma unroll
+    for (int I = 1; I <= 4; ++I) sm.Gref[I][t] = sm.G[16 * I - 1][t];
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      if ((I == 0 ? 0.f : sm.G[16 * I - 1][t]) - sm.G[16 * I + 15][t] > CALM_SPAN)
+        sm.calm_blk[I] = 0;
+  }
+  // zero the strictly-upper 16 x 16 tiles of A_kk and A_qk
+  for (int e = t; e < 6 * 256; e += NT_PREP) {
+    const int tile = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+    const int I = tile < 3 ? 0 : tile < 5 ? 1 : 2;
+    const int J = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
+    sm.Akk[16 * I + rr][16 * J + cc] = 0.f;
+    sm.Aqk[16 * I + rr][16 * J + cc] = 0.f;
+  }
+  // this thread's G; G into the saved set
   float Gv[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) Gv[j] = sm.G[rA][cA + j];
@@ -210,136 +248,92 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       *reinterpret_cast<f32x4*>(G_out + baseA + 4 * j) =
           f32x4{Gv[4 * j], Gv[4 * j + 1], Gv[4 * j + 2], Gv[4 * j + 3]};
   }
-  if (t < HD) {
+  __syncthreads();
+
+  // ---- 3. decayed products, tile (I, J) of A_kk and A_qk per wave item.
+  // Off-diagonal tiles (J < I) use rho = G at the end of block J: both
+  // x_r e^(G_r - rho) and k_i e^(rho - G_i) are <= 1. A calm diagonal tile
+  // uses rho = G before the block (the second factor is <= e^CALM_SPAN).
+  for (int item = w; item < 10; item += 8) {
+    int I, J;
+    tile_of(item, I, J);
+    const bool diag = I == J;
+    if (diag && !sm.calm_blk[I]) continue;
+    const float* ref = diag ? sm.Gref[I] : sm.Gref[J + 1];
+    const int ra = 16 * I + (l & 15), rbw = 16 * J + (l & 15);
+    const float rqa = sm.rq[ra], rka = sm.rk[ra], rkb = sm.rk[rbw];
+    f32x4 akk = zero4(), aqk = zero4();
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const float ref = I == 0 ? 0.f : sm.G[16 * I - 1][t];
-      sm.rho[I][t] = ref;
-      if (ref - sm.G[16 * I + 15][t] > CALM_SPAN) sm.calm_blk[I] = 0;
+    for (int ks = 0; ks < HD / 32; ++ks) {
+      const int c = 32 * ks + 8 * (l >> 4);
+      bf16x8 xk_h, xk_l, xq_h, xq_l, y_h, y_l;
+      decayed_frag(sm, sm.ks, rka, ra, c, ref, 1.f, xk_h, xk_l);
+      decayed_frag(sm, sm.qs, rqa, ra, c, ref, 1.f, xq_h, xq_l);
+      decayed_frag(sm, sm.ks, rkb, rbw, c, ref, -1.f, y_h, y_l);
+      if (KDA_SPLIT_P1 & SPLIT_A) {
+        akk = mfma16(xk_l, y_h, akk);
+        aqk = mfma16(xq_l, y_h, aqk);
+      }
+      if (KDA_SPLIT_P1 & SPLIT_B) {
+        akk = mfma16(xk_h, y_l, akk);
+        aqk = mfma16(xq_h, y_l, aqk);
+      }
+      akk = mfma16(xk_h, y_h, akk);
+      aqk = mfma16(xq_h, y_h, aqk);
     }
-    if (-sm.G[CL - 1][t] > CALM_SPAN) sm.calm_chunk = 0;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int r = 16 * I + drow(i4), i = 16 * J + dcol();
+      sm.Akk[r][i] = (i < r) ? akk[i4] : 0.f;
+      sm.Aqk[r][i] = (i <= r) ? aqk[i4] : 0.f;
+    }
+  }
+  // Diagonal blocks whose span is too wide: every pair (r, i <= r) of the
+  // block with its exact factor e^(G_r - G_i) <= 1, in fp32. Thread (I, p, cg)
+  // takes the 17 pairs of rows p and 15 - p over channels 8 cg .. 8 cg + 7;
+  // the 16 channel groups are summed across lanes.
+  {
+    const int I = t >> 7, p = (t >> 4) & 7, cg = t & 15, c = 8 * cg;
+    if (!sm.calm_blk[I]) {
+      for (int e = 0; e < 17; ++e) {
+        const int rl = e <= p ? p : 15 - p;
+        const int il = e <= p ? e : e - p - 1;
+        const int r = 16 * I + rl, i = 16 * I + il;
+        const f32x4 gr0 = *reinterpret_cast<const f32x4*>(&sm.G[r][c]);
+        const f32x4 gr1 = *reinterpret_cast<const f32x4*>(&sm.G[r][c + 4]);
+        const f32x4 gi0 = *reinterpret_cast<const f32x4*>(&sm.G[i][c]);
+        const f32x4 gi1 = *reinterpret_cast<const f32x4*>(&sm.G[i][c + 4]);
+        const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&sm.ks[r][c]);
+        const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&sm.qs[r][c]);
+        const bf16x8 ki = *reinterpret_cast<const bf16x8*>(&sm.ks[i][c]);
+        float skk = 0.f, sqk = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float dg = j < 4 ? gr0[j] - gi0[j] : gr1[j - 4] - gi1[j - 4];
+          const float e1 = fexp(dg) * bf2f(ki[j]);
+          skk += bf2f(kr[j]) * e1;
+          sqk += bf2f(qr[j]) * e1;
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+          skk += __shfl_xor(skk, m);
+          sqk += __shfl_xor(sqk, m);
+        }
+        if (cg == 0) {
+          sm.Akk[r][i] = il < rl ? skk * sm.rk[r] * sm.rk[i] : 0.f;
+          sm.Aqk[r][i] = sqk * sm.rq[r] * sm.rk[i];
+          if (il < rl) {               // the mirrored entry above the diagonal
+            sm.Akk[i][r] = 0.f;
+            sm.Aqk[i][r] = 0.f;
+          }
+        }
+      }
+    }
   }
   __syncthreads();
 
-  const float rqA = sm.rq[rA], rkA = sm.rk[rA];
-  float* Aqk_g = sv.Aqk + ch * CL * CL;
-  const int rb = w & 3, isq = w >> 2;         // MFMA role: row block rb of A_kk (isq = 0) or A_qk
-  if (sm.calm_chunk) {
-    // ---- 3a. single reference at the chunk start: A = X Y^T with X = x^ e^G, Y = k^ e^-G
-    const Panel XK{&sm.u.a.xk_hi[0][0], &sm.u.a.xk_lo[0][0], XS_LD};
-    const Panel XQ{&sm.u.a.xq_hi[0][0], &sm.u.a.xq_lo[0][0], XS_LD};
-    const Panel Y{&sm.u.a.y_hi[0][0], &sm.u.a.y_lo[0][0], XS_LD};
-    float xk[16], xq[16], y[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float e1 = fexp(Gv[j]);
-      const float kh = bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA;
-      const float qh = bf2f(j < 8 ? q0[j] : q1[j - 8]) * rqA;
-      xk[j] = kh * e1;
-      xq[j] = qh * e1;
-      y[j] = kh * fexp(-Gv[j]);
-    }
-    put8(XK, rA, cA, xk);
-    put8(XK, rA, cA + 8, xk + 8);
-    put8(XQ, rA, cA, xq);
-    put8(XQ, rA, cA + 8, xq + 8);
-    put8(Y, rA, cA, y);
-    put8(Y, rA, cA + 8, y + 8);
-    __syncthreads();
-    f32x4 acc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
-    mma_row<KDA_SPLIT_P1, 4>(acc, isq ? XQ : XK, 16 * rb, Y, 0, 0, HD);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r = 16 * rb + drow(i4), i = 16 * nt + dcol();
-        if (isq)
-          Aqk_g[r * CL + i] = (i <= r) ? acc[nt][i4] : 0.f;
-        else
-          sm.Akk[r][i] = (i < r) ? acc[nt][i4] : 0.f;
-      }
-    __syncthreads();
-  } else {
-    // ---- 3b. one reference per 16-row block; exact sums for wide diagonal blocks
-    const Panel XK{&sm.u.b.xk_hi[0][0], &sm.u.b.xk_lo[0][0], XS_LD};
-    const Panel XQ{&sm.u.b.xq_hi[0][0], &sm.u.b.xq_lo[0][0], XS_LD};
-    const Panel Y{&sm.u.b.y_hi[0][0], &sm.u.b.y_lo[0][0], XS_LD};
-    *reinterpret_cast<bf16x8*>(&sm.u.b.qs[rA][cA]) = q0;
-    *reinterpret_cast<bf16x8*>(&sm.u.b.qs[rA][cA + 8]) = q1;
-    *reinterpret_cast<bf16x8*>(&sm.u.b.ks[rA][cA]) = k0;
-    *reinterpret_cast<bf16x8*>(&sm.u.b.ks[rA][cA + 8]) = k1;
-    for (int I = 0; I < 4; ++I) {
-      const int calm = sm.calm_blk[I];
-      const int bA = rA >> 4;
-      float y[16];
-      const bool on = bA < I || (bA == I && calm);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float kh = bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA;
-        y[j] = on ? kh * fexp(sm.rho[I][cA + j] - Gv[j]) : 0.f;
-      }
-      put8(Y, rA, cA, y);
-      put8(Y, rA, cA + 8, y + 8);
-      if (bA == I) {
-        float xk[16], xq[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float e1 = fexp(Gv[j] - sm.rho[I][cA + j]);
-          xk[j] = bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA * e1;
-          xq[j] = bf2f(j < 8 ? q0[j] : q1[j - 8]) * rqA * e1;
-        }
-        put8(XK, rA & 15, cA, xk);
-        put8(XK, rA & 15, cA + 8, xk + 8);
-        put8(XQ, rA & 15, cA, xq);
-        put8(XQ, rA & 15, cA + 8, xq + 8);
-      }
-      __syncthreads();
-      // tile-products (matrix, J) for J = 0..I, one per wave
-      {
-        const int J = w >> 1, pq = w & 1;
-        if (J <= I) {
-          f32x4 acc = zero4();
-          if (J < I || calm) mma_k<KDA_SPLIT_P1, HD>(acc, pq ? XQ : XK, 0, Y, 16 * J);
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int r = 16 * I + drow(i4), i = 16 * J + dcol();
-            if (pq)
-              Aqk_g[r * CL + i] = (i <= r) ? acc[i4] : 0.f;
-            else
-              sm.Akk[r][i] = (i < r) ? acc[i4] : 0.f;
-          }
-        }
-        // zero the strictly-upper tiles of A_qk and A_kk for this row block
-        for (int e = t; e < 16 * (CL - 16 * (I + 1)); e += NT_PREP) {
-          const int rl = e / (CL - 16 * (I + 1)), i = 16 * (I + 1) + e % (CL - 16 * (I + 1));
-          Aqk_g[(16 * I + rl) * CL + i] = 0.f;
-          sm.Akk[16 * I + rl][i] = 0.f;
-        }
-      }
-      __syncthreads();
-    }
-    // exact fp32 sums on the diagonal tiles of blocks whose span is too wide
-    for (int p = t; p < 4 * 256; p += NT_PREP) {
-      const int I = p >> 8;
-      if (sm.calm_blk[I]) continue;
-      const int r = 16 * I + ((p >> 4) & 15), i = 16 * I + (p & 15);
-      if (i > r) continue;
-      float skk = 0.f, sqk = 0.f;
-      for (int c = 0; c < HD; ++c) {
-        const float e = fexp(sm.G[r][c] - sm.G[i][c]) * bf2f(sm.u.b.ks[i][c]);
-        skk += bf2f(sm.u.b.ks[r][c]) * e;
-        sqk += bf2f(sm.u.b.qs[r][c]) * e;
-      }
-      Aqk_g[r * CL + i] = sqk * sm.rq[r] * sm.rk[i];
-      if (i < r) sm.Akk[r][i] = skk * sm.rk[r] * sm.rk[i];
-    }
-    __syncthreads();
-  }
-
   // ---- 4. T = (I + Diag(beta) A_kk)^-1 by 16x16 blocks, fp32
-  float (*Tm)[F_LD] = sm.u.s.Tm;
+  float (*Tm)[F_LD] = sm.Tm;
   for (int e = t; e < CL * F_LD; e += NT_PREP) (&Tm[0][0])[e] = 0.f;
   __syncthreads();
   if (w < 4 && l < 16) {
@@ -368,34 +362,97 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
         float z = 0.f;
         for (int m = 16 * J; m < 16 * I; ++m)
           z += sm.beta[16 * I + r] * sm.Akk[16 * I + r][m] * Tm[m][16 * J + j];
-        sm.u.s.Z[bsel][r][j] = z;
+        sm.Z[bsel][r][j] = z;
       }
       __syncthreads();
       if (J < nb) {
         float s2 = 0.f;
-        for (int m = 0; m < 16; ++m) s2 += Tm[16 * I + r][16 * I + m] * sm.u.s.Z[bsel][m][j];
+        for (int m = 0; m < 16; ++m) s2 += Tm[16 * I + r][16 * I + m] * sm.Z[bsel][m][j];
         Tm[16 * I + r][16 * J + j] = -s2;
       }
       __syncthreads();
     }
   }
+
+  // ---- 5. saved matrices (fp32) and the forward scan's operand panels
   float* Tg = sv.Tm + ch * CL * CL;
   float* Akk_g = sv.Akk + ch * CL * CL;
+  float* Aqk_g = sv.Aqk + ch * CL * CL;
+  bf16* P = panels ? panels + ch * (int64_t)fwd_panel::ELEMS : nullptr;
   {
     const int r = t >> 3, i8 = 8 * (t & 7);
-    *reinterpret_cast<f32x4*>(Tg + r * CL + i8) = f32x4{Tm[r][i8], Tm[r][i8 + 1], Tm[r][i8 + 2], Tm[r][i8 + 3]};
-    *reinterpret_cast<f32x4*>(Tg + r * CL + i8 + 4) =
-        f32x4{Tm[r][i8 + 4], Tm[r][i8 + 5], Tm[r][i8 + 6], Tm[r][i8 + 7]};
-    *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8) =
-        f32x4{sm.Akk[r][i8], sm.Akk[r][i8 + 1], sm.Akk[r][i8 + 2], sm.Akk[r][i8 + 3]};
-    *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8 + 4) =
-        f32x4{sm.Akk[r][i8 + 4], sm.Akk[r][i8 + 5], sm.Akk[r][i8 + 6], sm.Akk[r][i8 + 7]};
+    float tv[8], kv[8], qv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      tv[j] = Tm[r][i8 + j];
+      kv[j] = sm.Akk[r][i8 + j];
+      qv[j] = sm.Aqk[r][i8 + j];
+    }
+    *reinterpret_cast<f32x4*>(Tg + r * CL + i8) = f32x4{tv[0], tv[1], tv[2], tv[3]};
+    *reinterpret_cast<f32x4*>(Tg + r * CL + i8 + 4) = f32x4{tv[4], tv[5], tv[6], tv[7]};
+    *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8) = f32x4{kv[0], kv[1], kv[2], kv[3]};
+    *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8 + 4) = f32x4{kv[4], kv[5], kv[6], kv[7]};
+    *reinterpret_cast<f32x4*>(Aqk_g + r * CL + i8) = f32x4{qv[0], qv[1], qv[2], qv[3]};
+    *reinterpret_cast<f32x4*>(Aqk_g + r * CL + i8 + 4) = f32x4{qv[4], qv[5], qv[6], qv[7]};
+    if (P) {
+      bf16x8 tb, ah, al;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tb[j] = f2bf(tv[j] * sm.beta[i8 + j]);
+        const float a = qv[j] * d.scale;
+        ah[j] = f2bf(a);
+        al[j] = f2bf(a - bf2f(ah[j]));
+      }
+      *reinterpret_cast<bf16x8*>(P + fwd_panel::TB + r * CL + i8) = tb;
+      *reinterpret_cast<bf16x8*>(P + fwd_panel::AQ + r * CL + i8) = ah;
+      *reinterpret_cast<bf16x8*>(P + fwd_panel::AQ + CL * CL + r * CL + i8) = al;
+    }
+  }
+  if (P) {
+    // -Kd = -k^ e^G (hi) and scale Qd = scale q^ e^G (hi, lo): this thread's row
+    const float rqA = sm.rq[rA], rkA = sm.rk[rA];
+    bf16x8 kd[2], qh[2], ql[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float e1 = fexp(Gv[j]);
+      const float kx = -bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA * e1;
+      const float qx = bf2f(j < 8 ? q0[j] : q1[j - 8]) * rqA * e1 * d.scale;
+      kd[j >> 3][j & 7] = f2bf(kx);
+      const bf16 hq = f2bf(qx);
+      qh[j >> 3][j & 7] = hq;
+      ql[j >> 3][j & 7] = f2bf(qx - bf2f(hq));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<bf16x8*>(P + fwd_panel::KD + rA * HD + cA + 8 * u) = kd[u];
+      *reinterpret_cast<bf16x8*>(P + fwd_panel::QD + rA * HD + cA + 8 * u) = qh[u];
+      *reinterpret_cast<bf16x8*>(P + fwd_panel::QD + CL * HD + rA * HD + cA + 8 * u) = ql[u];
+    }
+    // Ke^T [c][r] = k^_r e^(G_last - G_r): thread (c, rows 16 b .. 16 b + 15)
+    const int c = t & 127, b = t >> 7;
+    const float gl = sm.Gref[4][c];
+    bf16x8 eh[2], el[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * b + j;
+      const float x = bf2f(sm.ks[r][c]) * sm.rk[r] * fexp(gl - sm.G[r][c]);
+      const bf16 hx = f2bf(x);
+      eh[j >> 3][j & 7] = hx;
+      el[j >> 3][j & 7] = f2bf(x - bf2f(hx));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<bf16x8*>(P + fwd_panel::KE + c * CL + 16 * b + 8 * u) = eh[u];
+      *reinterpret_cast<bf16x8*>(P + fwd_panel::KE + HD * CL + c * CL + 16 * b + 8 * u) = el[u];
+    }
+    if (t < HD) reinterpret_cast<float*>(P + fwd_panel::GAM)[t] = fexp(sm.Gref[4][t]);
   }
 }
 
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
-                           const SavedSet& sv, hipStream_t s) {
-  hipLaunchKernelGGL(fwd_prep_kernel, dim3(d.NC, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv);
+                           const SavedSet& sv, void* panels, hipStream_t s) {
+  hipLaunchKernelGGL(fwd_prep_kernel, dim3(d.NC, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
+                     reinterpret_cast<bf16*>(panels));
   return hipGetLastError();
 }
 

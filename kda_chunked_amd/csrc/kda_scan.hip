@@ -71,39 +71,59 @@ static int scan_grid(int P) { return ((P + 7) / 8) * 8 * NTILE; }
 KDA_DEV float bsel(bool ok, bf16 x) { return ok ? bf2f(x) : 0.f; }
 
 // ------------------------------------------------------------------ forward
+// The chunk's operands arrive ready-made from the prep kernel (fwd_panel
+// layout): -Kd, scale Qd, Ke^T, Tb, scale A_qk and e^(G_last). Each step
+// stages them into LDS with 16-byte copies (prefetched into registers during
+// the previous step), so the sequential path holds only the S-dependent
+// products and their epilogues.
 struct FwdScanSmem {
-  union {
-    struct { bf16 hi[CL][K1_LD], lo[CL][K1_LD]; } kd;      // -Kd   [r][c]
-    struct { bf16 hi[HD][K2_LD], lo[HD][K2_LD]; } ke;      // Ke^T  [c][r]
-  } r1;
-  bf16 qd_hi[CL][K1_LD], qd_lo[CL][K1_LD];                 // scale*Qd [r][c]
-  bf16 tb_hi[CL][K2_LD], tb_lo[CL][K2_LD];                 // Tb [r][i]
-  bf16 aq_hi[CL][K2_LD], aq_lo[CL][K2_LD];                 // scale*A_qk [r][i]
-  bf16 s_hi[VT][K1_LD], s_lo[VT][K1_LD];                   // S^T [j][c]
-  bf16 rr_hi[VT][K2_LD], rr_lo[VT][K2_LD];                 // R^T [j][r]
-  bf16 u_hi[VT][K2_LD], u_lo[VT][K2_LD];                   // U~^T [j][r]
-  float gam[HD];
-  float rk[CL], rq[CL], beta[CL];
+  bf16 kd_hi[CL][K1_LD];                         // -Kd        [r][c]
+  bf16 qd_hi[CL][K1_LD], qd_lo[CL][K1_LD];       // scale Qd   [r][c]
+  bf16 ke_hi[HD][K2_LD], ke_lo[HD][K2_LD];       // Ke^T       [c][r]
+  bf16 tb_hi[CL][K2_LD];                         // Tb         [r][i]
+  bf16 aq_hi[CL][K2_LD], aq_lo[CL][K2_LD];       // scale A_qk [r][i]
+  float gam[HD];                                 // e^(G_last)
+  bf16 s_hi[VT][K1_LD], s_lo[VT][K1_LD];         // S^T        [j][c]
+  bf16 rr_hi[VT][K2_LD], rr_lo[VT][K2_LD];       // R^T        [j][r]
+  bf16 u_hi[VT][K2_LD], u_lo[VT][K2_LD];         // U~^T       [j][r]
 };
 
-// Registers holding one chunk's raw inputs for this thread.
-struct FwdPref {
-  bf16x8 k0, k1, q0, q1;     // row rA = t>>3, channels cA .. cA+15 (cA = 16*(t&7))
-  f32x4 g[4];                // G at the same elements
-  f32x4 T0, T1, A0, A1;      // T and A_qk: row rA, columns 8*(t&7) .. +7
-  bf16x8 kt[2];              // k at channel cB = t&127, rows 16*(t>>7) .. +15
-  float gt[16];              // G at the same elements
-  float gl;                  // G_last[cB]
-  bf16 v[4];                 // V at this lane's R-tile elements
-  float sb, sq, sk;          // beta, rq, rk of row t (t < 64)
-  int64_t t0;
-  int n;
-};
+constexpr int FP_UNITS = fwd_panel::ELEMS / 8;           // 16-byte units per chunk-head
+constexpr int FP_PER_THREAD = (FP_UNITS + NT_SCAN - 1) / NT_SCAN;
+static_assert(fwd_panel::KD == 0 && fwd_panel::QD == 1024 * 8 && fwd_panel::KE == 3072 * 8 &&
+                  fwd_panel::TB == 5120 * 8 && fwd_panel::AQ == 5632 * 8 &&
+                  fwd_panel::GAM == 6656 * 8 && FP_UNITS == 6688,
+              "staging map below assumes this panel layout");
+
+// LDS destination of 16-byte unit u = t + 512 k of a chunk's panels.
+KDA_DEV void stage_unit(FwdScanSmem& sm, int k, int t, const bf16x8& x) {
+  const int u = t + NT_SCAN * k;
+  bf16* dst;
+  if (k < 2) {                       // -Kd hi
+    dst = &sm.kd_hi[u >> 4][(u & 15) << 3];
+  } else if (k < 6) {                // Qd hi, lo
+    const int v = u - 1024;
+    dst = (v >> 10 ? &sm.qd_lo[0][0] : &sm.qd_hi[0][0]) + ((v >> 4) & 63) * K1_LD + ((v & 15) << 3);
+  } else if (k < 10) {               // Ke^T hi, lo
+    const int v = u - 3072;
+    dst = (v >> 10 ? &sm.ke_lo[0][0] : &sm.ke_hi[0][0]) + ((v >> 3) & 127) * K2_LD + ((v & 7) << 3);
+  } else if (k < 11) {               // Tb hi
+    const int v = u - 5120;
+    dst = &sm.tb_hi[v >> 3][(v & 7) << 3];
+  } else if (k < 13) {               // A_qk hi, lo
+    const int v = u - 5632;
+    dst = (v >> 9 ? &sm.aq_lo[0][0] : &sm.aq_hi[0][0]) + ((v >> 3) & 63) * K2_LD + ((v & 7) << 3);
+  } else {                           // e^(G_last), fp32 (32 units)
+    *reinterpret_cast<bf16x8*>(&sm.gam[4 * (u - 6656)]) = x;
+    return;
+  }
+  *reinterpret_cast<bf16x8*>(dst) = x;
+}
 
 __global__ __launch_bounds__(NT_SCAN) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                            const float* __restrict__ G,
-                                                            SavedSet sv, bf16* __restrict__ o,
-                                                            int save) {
+                                                            SavedSet sv,
+                                                            const bf16* __restrict__ panels,
+                                                            bf16* __restrict__ o, int save) {
   __shared__ FwdScanSmem sm;
   int pair, tile;
   if (!scan_coords(d.N * d.H, pair, tile)) return;
@@ -113,130 +133,57 @@ __global__ __launch_bounds__(NT_SCAN) void fwd_scan_kernel(Dims d, Inputs in, Ch
   const int rb = w & 3, nw = w >> 2;       // R / U~ / O tile of this wave: rows 16 rb, cols 16 nw
   const int j0 = tile * VT;
   const int H = d.H;
-  const bf16* q = reinterpret_cast<const bf16*>(in.q);
-  const bf16* k = reinterpret_cast<const bf16*>(in.k);
   const bf16* v = reinterpret_cast<const bf16*>(in.v);
-  const bf16* beta = reinterpret_cast<const bf16*>(in.beta);
-  const int rA = t >> 3, cA = 16 * (t & 7), i8 = 8 * (t & 7);
-  const int cB = t & 127, rB = 16 * (t >> 7);
 
-  const Panel KD{&sm.r1.kd.hi[0][0], (SPLIT_KS & SPLIT_A) ? &sm.r1.kd.lo[0][0] : nullptr, K1_LD};
-  const Panel KE{&sm.r1.ke.hi[0][0], &sm.r1.ke.lo[0][0], K2_LD};
+  const Panel KD{&sm.kd_hi[0][0], nullptr, K1_LD};
   const Panel QD{&sm.qd_hi[0][0], &sm.qd_lo[0][0], K1_LD};
-  const Panel TB{&sm.tb_hi[0][0], (SPLIT_TR & SPLIT_A) ? &sm.tb_lo[0][0] : nullptr, K2_LD};
+  const Panel KE{&sm.ke_hi[0][0], &sm.ke_lo[0][0], K2_LD};
+  const Panel TB{&sm.tb_hi[0][0], nullptr, K2_LD};
   const Panel AQ{&sm.aq_hi[0][0], &sm.aq_lo[0][0], K2_LD};
   const Panel SP{&sm.s_hi[0][0], &sm.s_lo[0][0], K1_LD};
   const Panel RP{&sm.rr_hi[0][0], &sm.rr_lo[0][0], K2_LD};
   const Panel UP{&sm.u_hi[0][0], &sm.u_lo[0][0], K2_LD};
 
-  FwdPref pf;
-  auto prefetch_main = [&](int cn) {
-    pf.t0 = ct.tok[cn];
-    pf.n = ct.len[cn];
-    const int64_t ch = (int64_t)cn * H + h;
-    const int r = rA < pf.n ? rA : pf.n - 1;
-    const int64_t base = ((pf.t0 + r) * H + h) * HD + cA;
-    pf.k0 = *reinterpret_cast<const bf16x8*>(k + base);
-    pf.k1 = *reinterpret_cast<const bf16x8*>(k + base + 8);
-    pf.q0 = *reinterpret_cast<const bf16x8*>(q + base);
-    pf.q1 = *reinterpret_cast<const bf16x8*>(q + base + 8);
+  // next chunk's panels and V tile, held in registers
+  bf16x8 pu[FP_PER_THREAD];
+  bf16 pv[4];
+  int64_t pt0 = 0;
+  int pn = 0;
+  auto prefetch = [&](int cn) {
+    pt0 = ct.tok[cn];
+    pn = ct.len[cn];
+    const bf16* src = panels + ((int64_t)cn * H + h) * fwd_panel::ELEMS;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pf.g[j] = *reinterpret_cast<const f32x4*>(G + base + 4 * j);
-    const float* Tr = sv.Tm + ch * CL * CL + rA * CL + i8;
-    const float* Ar = sv.Aqk + ch * CL * CL + rA * CL + i8;
-    pf.T0 = *reinterpret_cast<const f32x4*>(Tr);
-    pf.T1 = *reinterpret_cast<const f32x4*>(Tr + 4);
-    pf.A0 = *reinterpret_cast<const f32x4*>(Ar);
-    pf.A1 = *reinterpret_cast<const f32x4*>(Ar + 4);
+    for (int k = 0; k < FP_PER_THREAD; ++k)
+      if (k < FP_PER_THREAD - 1 || t < FP_UNITS - NT_SCAN * (FP_PER_THREAD - 1))
+        pu[k] = *reinterpret_cast<const bf16x8*>(src + 8 * (t + NT_SCAN * k));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * rb + drow(i), rc = rr < pf.n ? rr : pf.n - 1;
-      pf.v[i] = v[((pf.t0 + rc) * H + h) * HD + j0 + 16 * nw + dcol()];
+      const int rr = 16 * rb + drow(i), rc = rr < pn ? rr : pn - 1;
+      pv[i] = v[((pt0 + rc) * H + h) * HD + j0 + 16 * nw + dcol()];
     }
-    if (t < CL) {
-      const int rt = t < pf.n ? t : pf.n - 1;
-      const int64_t ri = (pf.t0 + rt) * H + h;
-      pf.sb = bf2f(beta[ri]);
-      pf.sq = sv.rq[ri];
-      pf.sk = sv.rk[ri];
-    }
-  };
-  auto prefetch_ke = [&](int cn) {
-    const int64_t tt = ct.tok[cn];
-    const int nn = ct.len[cn];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = rB + j, rc = r < nn ? r : nn - 1;
-      const int64_t idx = ((tt + rc) * H + h) * HD + cB;
-      pf.kt[j >> 3][j & 7] = k[idx];
-      pf.gt[j] = G[idx];
-    }
-    pf.gl = G[((tt + nn - 1) * H + h) * HD + cB];
   };
 
   // state: wave w owns state rows [16w, 16w+16) x 32 columns
   f32x4 S[2];
   S[0] = S[1] = zero4();
-  for (int e = t; e < VT * K1_LD; e += NT_SCAN) {
-    (&sm.s_hi[0][0])[e] = f2bf(0.f);
-    (&sm.s_lo[0][0])[e] = f2bf(0.f);
-  }
-  if (c0 < c1) {
-    prefetch_main(c0);
-    prefetch_ke(c0);
-  }
+  if (c0 < c1) prefetch(c0);
 
   for (int ci = c0; ci < c1; ++ci) {
-    const int64_t t0 = pf.t0;
-    const int n = pf.n;
+    const int64_t t0 = pt0;
+    const int n = pn;
     const int64_t ch = (int64_t)ci * H + h;
-    // ---- A. small vectors and the panels that do not depend on R
-    if (t < CL) {
-      const bool ok = t < n;
-      sm.beta[t] = ok ? pf.sb : 0.f;
-      sm.rq[t] = ok ? pf.sq : 0.f;
-      sm.rk[t] = ok ? pf.sk : 0.f;
-    }
-    if (t < HD) sm.gam[t] = fexp(pf.gl);   // thread t < 128 has cB = t
-    __syncthreads();
-    {
-      const bool ok = rA < n;
-      const float rk = sm.rk[rA], rq = sm.rq[rA];
-      float kd[16], qd[16];
+    __syncthreads();                       // the previous chunk's operands are consumed
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e1 = fexp(pf.g[j >> 2][j & 3]);
-        const bf16 kb = j < 8 ? pf.k0[j] : pf.k1[j - 8];
-        const bf16 qb = j < 8 ? pf.q0[j] : pf.q1[j - 8];
-        kd[j] = ok ? -bf2f(kb) * rk * e1 : 0.f;
-        qd[j] = ok ? bf2f(qb) * rq * e1 * d.scale : 0.f;
-      }
-      put8(KD, rA, cA, kd);
-      put8(KD, rA, cA + 8, kd + 8);
-      put8(QD, rA, cA, qd);
-      put8(QD, rA, cA + 8, qd + 8);
-      float tb[8], aq[8];
+    for (int k = 0; k < FP_PER_THREAD; ++k)
+      if (k < FP_PER_THREAD - 1 || t < FP_UNITS - NT_SCAN * (FP_PER_THREAD - 1))
+        stage_unit(sm, k, t, pu[k]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        tb[j] = (j < 4 ? pf.T0[j] : pf.T1[j - 4]) * sm.beta[i8 + j];
-        aq[j] = (j < 4 ? pf.A0[j] : pf.A1[j - 4]) * d.scale;
-      }
-      put8(TB, rA, i8, tb);
-      put8(AQ, rA, i8, aq);
-    }
+    for (int nt = 0; nt < 2; ++nt) store_tile_t(S[nt], SP, 16 * w, 16 * nt);
     f32x4 R;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) R[i] = bsel(16 * rb + drow(i) < n, pf.v[i]);
-    if (ci + 1 < c1) prefetch_main(ci + 1);
-    __syncthreads();
-    // ---- B. R = V - Kd S_in (tile rows 16 rb, cols 16 nw)
-    mma_k<SPLIT_KS, HD>(R, KD, 16 * rb, SP, 16 * nw);
+    for (int i = 0; i < 4; ++i) R[i] = bsel(16 * rb + drow(i) < n, pv[i]);
     if (save) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + drow(i);
-        if (r < n) sv.R[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = R[i];
-      }
       float* Sg = sv.S_in + ch * HD * HD;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
@@ -244,27 +191,26 @@ __global__ __launch_bounds__(NT_SCAN) void fwd_scan_kernel(Dims d, Inputs in, Ch
         for (int i = 0; i < 4; ++i)
           Sg[(16 * w + drow(i)) * HD + j0 + 16 * nt + dcol()] = S[nt][i];
     }
+    if (ci + 1 < c1) prefetch(ci + 1);
+    __syncthreads();
+    // ---- R = V - Kd S_in (the panel holds -Kd)
+    mma_k<SPLIT_KS, HD>(R, KD, 16 * rb, SP, 16 * nw);
+    if (save) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + drow(i);
+        if (r < n) sv.R[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = R[i];
+      }
+    }
     store_tile_t(R, RP, 16 * rb, 16 * nw);
     __syncthreads();
-    // ---- C. U~ = Tb R; Ke^T into the Kd space
+    // ---- U~ = Tb R
     const int kend = ((16 * rb + 16 + 31) / 32) * 32;
     f32x4 U = zero4();
     mma<SPLIT_TR>(U, TB, 16 * rb, RP, 16 * nw, 0, kend);
     store_tile_t(U, UP, 16 * rb, 16 * nw);
-    {
-      const float gl = pf.gl;
-      float ke[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = rB + j;
-        ke[j] = r < n ? bf2f(pf.kt[j >> 3][j & 7]) * sm.rk[r] * fexp(gl - pf.gt[j]) : 0.f;
-      }
-      put8(KE, cB, rB, ke);
-      put8(KE, cB, rB + 8, ke + 8);
-    }
-    if (ci + 1 < c1) prefetch_ke(ci + 1);
     __syncthreads();
-    // ---- D. O = scale (Qd S_in + A_qk U~)   (skipped when replaying)
+    // ---- O = scale (Qd S_in + A_qk U~)   (skipped when replaying)
     if (o != nullptr) {
       f32x4 acc = zero4();
       mma_k<SPLIT_QS, HD>(acc, QD, 16 * rb, SP, 16 * nw);
@@ -275,23 +221,21 @@ __global__ __launch_bounds__(NT_SCAN) void fwd_scan_kernel(Dims d, Inputs in, Ch
         if (r < n) o[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = f2bf(acc[i]);
       }
     }
-    // ---- E. S_out = Diag(e^G_last) S_in + Ke^T U~
+    // ---- S_out = Diag(e^G_last) S_in + Ke^T U~
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[nt][i] *= sm.gam[16 * w + drow(i)];
     mma_row<SPLIT_KU, 2>(S, KE, 16 * w, UP, 0, 0, CL);
-    __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) store_tile_t(S[nt], SP, 16 * w, 16 * nt);
   }
 }
 
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                           const float* G, const SavedSet& sv, void* o, int save_states,
+                           const SavedSet& sv, const void* panels, void* o, int save_states,
                            hipStream_t s) {
   hipLaunchKernelGGL(fwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(NT_SCAN), 0, s, d, in,
-                     ct, G, sv, reinterpret_cast<bf16*>(o), save_states);
+                     ct, sv, reinterpret_cast<const bf16*>(panels), reinterpret_cast<bf16*>(o),
+                     save_states);
   return hipGetLastError();
 }
 
