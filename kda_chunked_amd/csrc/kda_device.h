@@ -225,9 +225,15 @@ KDA_DEV void put4(const Panel& P, int row, int col, f32x4 x) {
 KDA_DEV int drow(int i) { return 4 * (lane_id() >> 4) + i; }
 KDA_DEV int dcol() { return lane_id() & 15; }
 
-// softplus(x) = log(1 + e^x), stable for large |x|.
-KDA_DEV float softplus(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
-KDA_DEV float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^-|x|), on the hardware
+// base-2 exponential and logarithm.
+KDA_DEV float softplus(float x) {
+  const float y = __builtin_amdgcn_exp2f(-fabsf(x) * LOG2E);
+  return fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + y) * 0.6931471805599453f;
+}
+KDA_DEV float sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * LOG2E));
+}
 
 // The per-token log forget gate g for (token t, head h, channel c).
 KDA_DEV float gate_value(const void* gate, int raw, const float* A_log, const float* dt_bias,

@@ -140,38 +140,34 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   const bool okA = rA < n;
   const int64_t baseA = ((t0 + (okA ? rA : n - 1)) * H + h) * HD + cA;
 
-  // ---- 1. loads (all issued before use): q, k, gate of this thread's 16 elements
+  // ---- 1. loads (all issued before use). Thread t: q, k of row rA, channels
+  // cA .. cA+15; the gate of channel cG = t & 127, rows 16 qG .. 16 qG + 15.
   const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(q + baseA);
   const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(q + baseA + 8);
   const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
   const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
+  const int cG = t & 127, qG = t >> 7;
   float g[16];
   if (!d.raw) {
-    const float* gp = reinterpret_cast<const float*>(in.gate) + baseA;
+    const float* gp = reinterpret_cast<const float*>(in.gate);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(gp + 4 * j);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) g[4 * j + u] = x[u];
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * qG + j;
+      g[j] = gp[((t0 + (r < n ? r : n - 1)) * H + h) * HD + cG];
     }
   } else {
-    const bf16* ap = reinterpret_cast<const bf16*>(in.gate) + baseA;
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + 8);
-    const float ea = __expf(in.A_log[h]);
+    const bf16* ap = reinterpret_cast<const bf16*>(in.gate);
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      g[j] = -ea * softplus(bf2f(j < 8 ? a0[j] : a1[j - 8]) + in.dt_bias[h * HD + cA + j]);
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * qG + j;
+      g[j] = bf2f(ap[((t0 + (r < n ? r : n - 1)) * H + h) * HD + cG]);
+    }
   }
   if (t < CL) sm.beta[t] = t < n ? bf2f(beta[(t0 + (t < n ? t : n - 1)) * H + h]) : 0.f;
   *reinterpret_cast<bf16x8*>(&sm.qs[rA][cA]) = q0;
   *reinterpret_cast<bf16x8*>(&sm.qs[rA][cA + 8]) = q1;
   *reinterpret_cast<bf16x8*>(&sm.ks[rA][cA]) = k0;
   *reinterpret_cast<bf16x8*>(&sm.ks[rA][cA + 8]) = k1;
-#pragma unroll
-  for (int j = 0; j < 16; j += 4)
-    *reinterpret_cast<f32x4*>(&sm.G[rA][cA + j]) =
-        okA ? f32x4{g[j], g[j + 1], g[j + 2], g[j + 3]} : zero4();
   // L2 row sums: partial over this thread's 16 channels
   {
     float sq = 0.f, sk = 0.f;
@@ -184,17 +180,33 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     sm.nrm[0][t & 7][rA] = sq;
     sm.nrm[1][t & 7][rA] = sk;
   }
-  __syncthreads();
-
-  // ---- 2. chunk-local cumsum of g: four threads per channel (16 rows each)
+  // ---- 2. chunk-local cumsum of g in registers (16 rows per thread), then
+  // the carry of the earlier row quarters
   {
-    const int c = t & 127, qr = t >> 7;
+    const float ea = d.raw ? __expf(in.A_log[h]) : 0.f;
+    const float dtb = d.raw ? in.dt_bias[h * HD + cG] : 0.f;
     float run = 0.f;
-    for (int r = 16 * qr; r < 16 * qr + 16; ++r) {
-      run += sm.G[r][c];
-      sm.G[r][c] = run;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float x = g[j];
+      if (d.raw) x = -ea * softplus(x + dtb);
+      run += (16 * qG + j < n) ? x : 0.f;
+      g[j] = run;
     }
-    sm.qtot[qr][c] = run;
+    sm.qtot[qG][cG] = run;
+  }
+  if (t < 4) sm.calm_blk[t] = 1;
+  __syncthreads();
+  {
+    float carry = 0.f;
+    for (int j = 0; j < qG; ++j) carry += sm.qtot[j][cG];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 16 * qG + j;
+      const float Gx = g[j] + carry;
+      sm.G[r][cG] = Gx;               // rows >= n hold G[n-1] (their g is 0)
+      if (r < n) G_out[((t0 + r) * H + h) * HD + cG] = Gx;
+    }
     if (t < CL) {
       float a = 0.f, b = 0.f;
 #pragma unroll
@@ -211,16 +223,10 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
         sv.rk[(t0 + t) * H + h] = rk;
       }
     }
-    if (t < 4) sm.calm_blk[t] = 1;
-    __syncthreads();
-    float carry = 0.f;
-    for (int j = 0; j < qr; ++j) carry += sm.qtot[j][c];
-    if (qr > 0)
-      for (int r = 16 * qr; r < 16 * qr + 16; ++r) sm.G[r][c] += carry;
   }
   __syncthreads();
-  // references: G before each 16-row block and G_last (rows >= n hold G[n-1],
-  // their g being 0); a block is calm when its own decay span is <= CALM_SPAN
+  // references: G before each 16-row block and G_last; a block is calm when
+  // its own decay span is <= CALM_SPAN in every channel
   if (t < HD) {
     sm.Gref[0][t] = 0.f;
 #pragma unroll
@@ -238,16 +244,10 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     sm.Akk[16 * I + rr][16 * J + cc] = 0.f;
     sm.Aqk[16 * I + rr][16 * J + cc] = 0.f;
   }
-  // this thread's G; G into the saved set
+  // this thread's G (row rA, channels cA ..)
   float Gv[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) Gv[j] = sm.G[rA][cA + j];
-  if (okA) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<f32x4*>(G_out + baseA + 4 * j) =
-          f32x4{Gv[4 * j], Gv[4 * j + 1], Gv[4 * j + 2], Gv[4 * j + 3]};
-  }
   __syncthreads();
 
   // ---- 3. decayed products, tile (I, J) of A_kk and A_qk per wave item.
@@ -289,43 +289,58 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     }
   }
   // Diagonal blocks whose span is too wide: every pair (r, i <= r) of the
-  // block with its exact factor e^(G_r - G_i) <= 1, in fp32. Thread (I, p, cg)
-  // takes the 17 pairs of rows p and 15 - p over channels 8 cg .. 8 cg + 7;
+  // block with its exact factor e^(G_r - G_i) <= 1, in fp32. Wave p takes the
+  // 17 pairs of rows p and 15 - p; lane (I, cg) block I, channels 8 cg .. + 7;
   // the 16 channel groups are summed across lanes.
-  {
-    const int I = t >> 7, p = (t >> 4) & 7, cg = t & 15, c = 8 * cg;
-    if (!sm.calm_blk[I]) {
-      for (int e = 0; e < 17; ++e) {
-        const int rl = e <= p ? p : 15 - p;
-        const int il = e <= p ? e : e - p - 1;
-        const int r = 16 * I + rl, i = 16 * I + il;
-        const f32x4 gr0 = *reinterpret_cast<const f32x4*>(&sm.G[r][c]);
-        const f32x4 gr1 = *reinterpret_cast<const f32x4*>(&sm.G[r][c + 4]);
-        const f32x4 gi0 = *reinterpret_cast<const f32x4*>(&sm.G[i][c]);
-        const f32x4 gi1 = *reinterpret_cast<const f32x4*>(&sm.G[i][c + 4]);
-        const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&sm.ks[r][c]);
-        const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&sm.qs[r][c]);
-        const bf16x8 ki = *reinterpret_cast<const bf16x8*>(&sm.ks[i][c]);
-        float skk = 0.f, sqk = 0.f;
+  if (!(sm.calm_blk[0] & sm.calm_blk[1] & sm.calm_blk[2] & sm.calm_blk[3])) {
+    const int p = w, I = (l >> 4) & 3, cg = l & 15, c = 8 * cg;
+    const bool on = !sm.calm_blk[I];
+    float ga[8], gb[8];
+    {
+      const int ra = 16 * I + p, rz = 16 * I + 15 - p;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float dg = j < 4 ? gr0[j] - gi0[j] : gr1[j - 4] - gi1[j - 4];
-          const float e1 = fexp(dg) * bf2f(ki[j]);
-          skk += bf2f(kr[j]) * e1;
-          sqk += bf2f(qr[j]) * e1;
-        }
+      for (int j = 0; j < 8; j += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.G[ra][c + j]);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.G[rz][c + j]);
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-          skk += __shfl_xor(skk, m);
-          sqk += __shfl_xor(sqk, m);
+        for (int u = 0; u < 4; ++u) {
+          ga[j + u] = x[u];
+          gb[j + u] = y[u];
         }
-        if (cg == 0) {
-          sm.Akk[r][i] = il < rl ? skk * sm.rk[r] * sm.rk[i] : 0.f;
-          sm.Aqk[r][i] = sqk * sm.rq[r] * sm.rk[i];
-          if (il < rl) {               // the mirrored entry above the diagonal
-            sm.Akk[i][r] = 0.f;
-            sm.Aqk[i][r] = 0.f;
-          }
+      }
+    }
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.ks[16 * I + p][c]);
+    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.qs[16 * I + p][c]);
+    const bf16x8 kz = *reinterpret_cast<const bf16x8*>(&sm.ks[16 * I + 15 - p][c]);
+    const bf16x8 qz = *reinterpret_cast<const bf16x8*>(&sm.qs[16 * I + 15 - p][c]);
+#pragma unroll
+    for (int e = 0; e < 17; ++e) {
+      const bool first = e <= p;                // wave-uniform
+      const int rl = first ? p : 15 - p;
+      const int il = first ? e : e - p - 1;
+      const int r = 16 * I + rl, i = 16 * I + il;
+      const f32x4 gi0 = *reinterpret_cast<const f32x4*>(&sm.G[i][c]);
+      const f32x4 gi1 = *reinterpret_cast<const f32x4*>(&sm.G[i][c + 4]);
+      const bf16x8 ki = *reinterpret_cast<const bf16x8*>(&sm.ks[i][c]);
+      float skk = 0.f, sqk = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float gi = j < 4 ? gi0[j] : gi1[j - 4];
+        const float e1 = fexp((first ? ga[j] : gb[j]) - gi) * bf2f(ki[j]);
+        skk += bf2f(first ? ka[j] : kz[j]) * e1;
+        sqk += bf2f(first ? qa[j] : qz[j]) * e1;
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        skk += __shfl_xor(skk, m);
+        sqk += __shfl_xor(sqk, m);
+      }
+      if (on && cg == 0) {
+        sm.Akk[r][i] = il < rl ? skk * sm.rk[r] * sm.rk[i] : 0.f;
+        sm.Aqk[r][i] = sqk * sm.rq[r] * sm.rk[i];
+        if (il < rl) {                 // the mirrored entry above the diagonal
+          sm.Akk[i][r] = 0.f;
+          sm.Aqk[i][r] = 0.f;
         }
       }
     }
