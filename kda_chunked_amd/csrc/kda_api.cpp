@@ -74,6 +74,7 @@ kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states, float** G)
   if (with_states) {
     sv.S_in = c.take<float>((size_t)s.NC * s.H * 128 * 128);
     sv.R = c.take<float>((size_t)s.T * s.H * 128);
+    sv.U = c.take<float>((size_t)s.T * s.H * 128);
   }
   return sv;
 }
@@ -87,6 +88,7 @@ kda::BwdWork carve_bwd(Carver& c, const Sizes& s) {
   kda::BwdWork bw;
   bw.dS = c.take<float>((size_t)s.NC * s.H * 128 * 128);
   bw.dU = c.take<float>((size_t)s.T * s.H * 128);
+  bw.dR = c.take<float>((size_t)s.T * s.H * 128);
   bw.part_A = c.take<float>((size_t)s.NC * s.H);
   bw.part_dt = c.take<float>((size_t)s.NC * s.H * 128);
   return bw;

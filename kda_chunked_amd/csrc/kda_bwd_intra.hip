@@ -2,11 +2,10 @@
 // flashinfer PR #8909, opening section and commit notes) plus the parameter
 // reduction of the raw gate.
 //
-// Given the saved state S_in, the state gradient dS_out and dU~ (both from the
-// reverse scan), one workgroup per (chunk, head) forms
-//   U~ = Tb R,  dR = Tb^T dU~                      (Tb = T Diag(beta))
+// Given the saved state S_in and U~ = Tb R (forward scan), and dS_out,
+// dU~ and dR = Tb^T dU~ (reverse scan), one workgroup per (chunk, head) forms
 //   dQd = scale dO S_in^T,  dKd = -dR S_in^T,  dKe = U~ dS_out^T
-//   dA_qk = scale dO U~^T (i <= r),  dTb = dU~ R^T (i <= r)
+//   dA_qk = scale dO U~^T (i <= r),  dTb = dU~ R^T (i <= r)   (Tb = T Diag(beta))
 //   dT = dTb Diag(beta),  dX = -T^T dT T^T (i < r),  dA_kk = Diag(beta) dX
 //   dbeta_i = sum_r dTb[r,i] T[r,i] + sum_i' dX[i,i'] A_kk[i,i']
 // then pushes dA_qk, dA_kk through the decayed products, accumulates dq, dk
@@ -42,9 +41,6 @@ constexpr int F_LD = CL + 1;        // fp32 64x64 matrices
 constexpr float CALM_SPAN_B = 40.f;
 
 // Split terms per product (SPLIT_A: first operand carries its lo part, ...).
-#ifndef KDA_SPLIT_B1
-#define KDA_SPLIT_B1 SPLIT_B     // U~ = Tb R, dR = Tb^T dU~
-#endif
 #ifndef KDA_SPLIT_B2
 #define KDA_SPLIT_B2 SPLIT_B     // dKd = dR S_in^T
 #endif
@@ -70,10 +66,6 @@ constexpr float CALM_SPAN_B = 40.f;
 
 struct BwdIntraSmem {
   union {
-    struct {
-      bf16 a_hi[CL][K2_LD], a_lo[CL][K2_LD];       // Tb [r][i], then Tb^T [i][r]
-      bf16 b_hi[HD][K2_LD], b_lo[HD][K2_LD];       // R^T [j][i], then dU~^T [j][r]
-    } p1;
     struct {
       bf16 s_hi[HD][K1_LD], s_lo[HD][K1_LD];       // S_in [c][j], then dS_out [c][j]
       bf16 a_hi[CL][K1_LD], a_lo[CL][K1_LD];       // dR [r][j], then U~ [r][j]
@@ -150,29 +142,41 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   // ------------------------------------------------------------ P0: setup
   // this thread's elements: rows er(i) = 16 rb + drow(i), channels ec(nt) = 64 chh + 16 nt + dcol()
   float eG[4][4];
-  bf16 eqb[4][4], ekb[4][4];       // raw q, k (bf16); q^ = q * rqr[i], zero on padded rows
+  bf16x2 eq2[4][2], ek2[4][2];     // raw q, k (bf16 pairs i = 2 m, 2 m + 1); q^ = q * rqr[i]
   float rqr[4], rkr[4];
-  {
+  // (re)load G, q, k at this thread's elements: called where a phase needs
+  // them, so that they are not held in registers across the phases between
+  auto load_epi = [&]() {
+    // addresses rebuilt from an opaque copy of the thread id, and pointers
+    // made opaque, so that a reload is neither merged with the previous one
+    // nor served from addresses kept live in between
+    int tt = t;
+    int64_t base = (t0 * H + h) * HD, rbase = t0 * H + h;
+    asm volatile("" : "+v"(tt), "+s"(base), "+s"(rbase));
+    const float* Gp = G + base;
+    const bf16* qp = q + base;
+    const bf16* kp = k + base;
+    const float* rqp = sv.rq + rbase;
+    const float* rkp = sv.rk + rbase;
+    const int ll = tt & 63, rbb = (tt >> 6) & 3, cb = 64 * (tt >> 8) + (ll & 15);
+    const int rstride = H * HD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r0 = 16 * rb + drow(i), r = clampr(r0);
-      const float a = sv.rq[rowidx(r)], b = sv.rk[rowidx(r)];
+      const int r0 = 16 * rbb + 4 * (ll >> 4) + i, r = r0 < n ? r0 : n - 1;
+      const int ro = r * rstride + cb;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        eG[nt][i] = Gp[ro + 16 * nt];
+        eq2[nt][i >> 1][i & 1] = qp[ro + 16 * nt];
+        ek2[nt][i >> 1][i & 1] = kp[ro + 16 * nt];
+      }
+      const float a = rqp[r * H], b = rkp[r * H];
       rqr[i] = r0 < n ? a : 0.f;
       rkr[i] = r0 < n ? b : 0.f;
     }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = clampr(16 * rb + drow(i));
-        const int64_t idx = rowidx(r) * HD + 64 * chh + 16 * nt + dcol();
-        eG[nt][i] = G[idx];
-        eqb[nt][i] = q[idx];
-        ekb[nt][i] = k[idx];
-      }
-  }
-#define EQ(nt, i) (bf2f(eqb[nt][i]) * rqr[i])
-#define EK(nt, i) (bf2f(ekb[nt][i]) * rkr[i])
+  };
+#define EQ(nt, i) (bf2f(eq2[nt][(i) >> 1][(i) & 1]) * rqr[i])
+#define EK(nt, i) (bf2f(ek2[nt][(i) >> 1][(i) & 1]) * rkr[i])
   if (t < CL) {
     const int r = clampr(t);
     const bool ok = t < n;
@@ -204,73 +208,20 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) adq[nt] = adk[nt] = adG[nt] = zero4();
 
-  // ------------------------------------------------------------ P1: U~ and dR
-  f32x4 U[4], dR[4];
-  {
-    const Panel A{&sm.u.p1.a_hi[0][0], (KDA_SPLIT_B1 & SPLIT_A) ? &sm.u.p1.a_lo[0][0] : nullptr, K2_LD};
-    const Panel B{&sm.u.p1.b_hi[0][0], &sm.u.p1.b_lo[0][0], K2_LD};
-    // Tb [r][i]
-    {
-      const int r = t >> 3, i8 = (t & 7) * 8;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(Tg + r * CL + i8);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(Tg + r * CL + i8 + 4);
-      float x[8];
+  // fp32 [T, H, 128] values at this thread's 16 elements (zero on padded rows)
+  auto load_elems = [&](const float* src, f32x4 (&x)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = a0[j] * sm.beta[i8 + j];
-        x[j + 4] = a1[j] * sm.beta[i8 + 4 + j];
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + drow(i);
+        const float v = src[rowidx(clampr(r)) * HD + 64 * chh + 16 * nt + dcol()];
+        x[nt][i] = r < n ? v : 0.f;
       }
-      put8(A, r, i8, x);
-    }
-    // R^T [j][i]
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int e = t + NTHR * rep, j = e & 127, i8 = (e >> 7) * 8;
-      float x[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int i = i8 + jj;
-        const float v = sv.R[rowidx(clampr(i)) * HD + j];
-        x[jj] = i < n ? v : 0.f;
-      }
-      put8(B, j, i8, x);
-    }
-    __syncthreads();
-    const int kend = ((16 * rb + 16 + 31) / 32) * 32;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) U[nt] = zero4();
-    mma_row<KDA_SPLIT_B1, 4>(U, A, 16 * rb, B, 64 * chh, 0, kend);
-    __syncthreads();
-    // Tb^T [i][r]
-    {
-      const int i = t & 63, r8 = (t >> 6) * 8;
-      float x[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) x[jj] = Tg[(r8 + jj) * CL + i] * sm.beta[i];
-      put8(A, i, r8, x);
-    }
-    // dU~^T [j][r]
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int e = t + NTHR * rep, j = e & 127, r8 = (e >> 7) * 8;
-      float x[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int r = r8 + jj;
-        const float v = bw.dU[rowidx(clampr(r)) * HD + j];
-        x[jj] = r < n ? v : 0.f;
-      }
-      put8(B, j, r8, x);
-    }
-    __syncthreads();
-    const int kbeg = (16 * rb / 32) * 32;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) dR[nt] = zero4();
-    mma_row<KDA_SPLIT_B1, 4>(dR, A, 16 * rb, B, 64 * chh, kbeg, CL);
-    __syncthreads();
-  }
+  };
 
   // ------------------------------------------------------------ P2: dQd, dKd
+  // dR (= dv, fp32) from the reverse scan
   const Panel SP{&sm.u.p2.s_hi[0][0], &sm.u.p2.s_lo[0][0], K1_LD};
   const Panel AP{&sm.u.p2.a_hi[0][0], &sm.u.p2.a_lo[0][0], K1_LD};
   const Panel DOP{&sm.u.p2.do_hi[0][0], nullptr, K1_LD};
@@ -289,6 +240,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     }
   };
   {
+    f32x4 dR[4];
+    load_elems(bw.dR, dR);
     load_state_panel(sv.S_in + ch * HD * HD);
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
@@ -304,6 +257,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_tile_n(dR[nt], APd, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
+    load_epi();
     {
       f32x4 a[4];
 #pragma unroll
@@ -338,6 +292,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   // ------------------------------------------------------------ P3: dKe, dA_qk, dgamma
   f32x4 dAq[2];
   {
+    f32x4 U[4];                                   // U~ from the forward scan
+    load_elems(sv.U, U);
     // dS_out replaces S_in in the panel. dgamma[c] = sum_j dS_out[c][j] S_in[c][j]
     // takes S_in from the split panel (hi + lo) just before it is overwritten:
     // each thread rewrites exactly the elements it reads.
@@ -394,6 +350,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_tile_n(U[nt], AP, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
+    load_epi();
     f32x4 a[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
@@ -535,6 +492,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     const Panel YT{&sm.u.p6.m.u.a.yt_hi[0][0], &sm.u.p6.m.u.a.yt_lo[0][0], K2_LD};
     const Panel XT{&sm.u.p6.m.u.b.xt_hi[0][0], &sm.u.p6.m.u.b.xt_lo[0][0], K1_LD};
     const Panel DAT{&sm.u.p6.m.dat_hi[0][0], &sm.u.p6.m.dat_lo[0][0], K1_LD};
+    load_epi();
     const bool calm = sm.calm_chunk;
     const bool blk_calm = sm.calm_blk[rb];
 #pragma unroll

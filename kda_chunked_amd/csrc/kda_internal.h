@@ -26,6 +26,7 @@ struct SavedSet {
   float* Aqk;    // [NC, H, 64, 64]  decayed q.k products, zero above the diagonal
   float* Akk;    // [NC, H, 64, 64]  decayed k.k products, zero on and above the diagonal
   float* R;      // [T, H, 128]      V - (K*e^G) S_in, per token
+  float* U;      // [T, H, 128]      U~ = Tb R, per token
   float* rq;     // [T, H]           L2 scalars (1 without the fused norm)
   float* rk;     // [T, H]
 };
@@ -65,6 +66,7 @@ struct BwdOut {
 struct BwdWork {
   float* dS;          // [NC, H, 128, 128] gradient w.r.t. the state after each chunk
   float* dU;          // [T, H, 128] gradient w.r.t. U~ (the chunk's transformed values)
+  float* dR;          // [T, H, 128] gradient w.r.t. R (= dv in fp32)
   float* part_A;      // [NC, H]      raw form: per-chunk sum of dg*g
   float* part_dt;     // [NC, H, 128] raw form: per-chunk sum of dz
 };

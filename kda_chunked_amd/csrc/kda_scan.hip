@@ -208,6 +208,13 @@ __global__ __launch_bounds__(NT_SCAN) void fwd_scan_kernel(Dims d, Inputs in, Ch
     const int kend = ((16 * rb + 16 + 31) / 32) * 32;
     f32x4 U = zero4();
     mma<SPLIT_TR>(U, TB, 16 * rb, RP, 16 * nw, 0, kend);
+    if (save) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + drow(i);
+        if (r < n) sv.U[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = U[i];
+      }
+    }
     store_tile_t(U, UP, 16 * rb, 16 * nw);
     __syncthreads();
     // ---- O = scale (Qd S_in + A_qk U~)   (skipped when replaying)
@@ -415,7 +422,11 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + drow(i);
-        if (r < n) dv[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = f2bf(acc[i]);
+        if (r < n) {
+          const int64_t idx = ((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol();
+          dv[idx] = f2bf(acc[i]);
+          bw.dR[idx] = acc[i];
+        }
       }
       store_tile_t(acc, DR, 16 * rb, 16 * nw);
     }
