@@ -73,8 +73,8 @@ kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states, float** G)
   *G = c.take<float>((size_t)s.T * s.H * 128);
   if (with_states) {
     sv.S_in = c.take<float>((size_t)s.NC * s.H * 128 * 128);
-    sv.R = c.take<float>((size_t)s.T * s.H * 128);
-    sv.U = c.take<float>((size_t)s.T * s.H * 128);
+    sv.R = c.take<float>((size_t)s.NC * s.H * 64 * 128);
+    sv.U = c.take<float>((size_t)s.NC * s.H * 64 * 128);
   }
   return sv;
 }
@@ -143,7 +143,7 @@ size_t fwd_ws_bytes(const Sizes& s) {
   Carver c(nullptr);
   carve_table(c, s);
   float* G;
-  carve_saved(c, s, 0, &G);
+  carve_saved(c, s, 1, &G);   // used when the caller saves nothing
   carve_panels(c, s);
   return c.off;
 }
@@ -223,7 +223,7 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   Carver wc(workspace);
   const kda::ChunkTable ct = carve_table(wc, s);
   float* G = nullptr;
-  kda::SavedSet sv = carve_saved(wc, s, 0, &G);   // used when nothing is saved
+  kda::SavedSet sv = carve_saved(wc, s, 1, &G);   // used when nothing is saved
   void* panels = carve_panels(wc, s);
   if (saved) {
     Carver sc(saved);
@@ -231,7 +231,8 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   }
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, hs));
-  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, o, saved != nullptr, hs));
+  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, saved != nullptr, hs));
+  LAUNCH("fwd_out", kda::launch_fwd_out(d, ct, sv, panels, o, hs));
   return KDA_OK;
 }
 
@@ -295,7 +296,7 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   if (replay) {
     LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, hs));
-    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, nullptr, 1, hs));
+    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, 1, hs));
   }
   LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, G, sv, dO, dv, bw, hs));
   LAUNCH("bwd_intra", kda::launch_bwd_intra(d, in, ct, G, sv, dO, out, bw, hs));

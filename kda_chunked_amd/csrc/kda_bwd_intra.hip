@@ -226,18 +226,13 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   const Panel AP{&sm.u.p2.a_hi[0][0], &sm.u.p2.a_lo[0][0], K1_LD};
   const Panel DOP{&sm.u.p2.do_hi[0][0], nullptr, K1_LD};
   auto load_state_panel = [&](const float* src) {
-    // 128 x 128 fp32 -> split panel [c][j]; 8 float4 per thread, all issued first
+    // 128 x 128 fp32, tile order -> split panel [c][j]: wave w takes row
+    // block w, 8 tiles, all loads issued first
     f32x4 v[8];
 #pragma unroll
-    for (int rep = 0; rep < 8; ++rep) {
-      const int e = t + NTHR * rep, c = e >> 5, j4 = (e & 31) * 4;
-      v[rep] = *reinterpret_cast<const f32x4*>(src + c * HD + j4);
-    }
+    for (int jb = 0; jb < 8; ++jb) v[jb] = *reinterpret_cast<const f32x4*>(src + tile_off(w, jb));
 #pragma unroll
-    for (int rep = 0; rep < 8; ++rep) {
-      const int e = t + NTHR * rep, c = e >> 5, j4 = (e & 31) * 4;
-      put4(SP, c, j4, v[rep]);
-    }
+    for (int jb = 0; jb < 8; ++jb) store_tile_n(v[jb], SP, 16 * w, 16 * jb);
   };
   {
     f32x4 dR[4];
@@ -292,8 +287,10 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   // ------------------------------------------------------------ P3: dKe, dA_qk, dgamma
   f32x4 dAq[2];
   {
-    f32x4 U[4];                                   // U~ from the forward scan
-    load_elems(sv.U, U);
+    f32x4 U[4];                                   // U~ from the forward scan (tile order)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      U[nt] = *reinterpret_cast<const f32x4*>(sv.U + ch * CL * HD + tile_off(rb, 4 * chh + nt));
     // dS_out replaces S_in in the panel. dgamma[c] = sum_j dS_out[c][j] S_in[c][j]
     // takes S_in from the split panel (hi + lo) just before it is overwritten:
     // each thread rewrites exactly the elements it reads.
@@ -388,14 +385,14 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     for (int rep = 0; rep < 4; ++rep) {
       const int e = t + NTHR * rep, r = e >> 5, j4 = (e & 31) * 4;
       va[rep] = *reinterpret_cast<const f32x4*>(bw.dU + rowidx(clampr(r)) * HD + j4);
-      vb[rep] = *reinterpret_cast<const f32x4*>(sv.R + rowidx(clampr(r)) * HD + j4);
+      // R, tile order: wave w takes row block w & 3, column blocks 4 (w >> 2) + rep
+      vb[rep] = *reinterpret_cast<const f32x4*>(sv.R + ch * CL * HD + tile_off(rb, 4 * chh + rep));
     }
 #pragma unroll
     for (int rep = 0; rep < 4; ++rep) {
       const int e = t + NTHR * rep, r = e >> 5, j4 = (e & 31) * 4;
-      const f32x4 z = zero4();
-      put4(DU, r, j4, r < n ? va[rep] : z);
-      put4(RP, r, j4, r < n ? vb[rep] : z);
+      put4(DU, r, j4, r < n ? va[rep] : zero4());
+      store_tile_n(vb[rep], RP, 16 * rb, 64 * chh + 16 * rep);
     }
     __syncthreads();
     dTb[0] = dTb[1] = zero4();

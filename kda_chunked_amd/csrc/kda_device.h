@@ -221,6 +221,10 @@ KDA_DEV void put4(const Panel& P, int row, int col, f32x4 x) {
   if (P.lo) *reinterpret_cast<bf16x4*>(P.lo + row * P.ld + col) = w;
 }
 
+// Offset of this lane's 4 values of tile (rb, cb) in a tile-ordered matrix
+// with 8 column blocks (128 columns): one 16-byte vector per lane.
+KDA_DEV int tile_off(int rb, int cb) { return (rb * 8 + cb) * 256 + 4 * lane_id(); }
+
 // Row / column of element i (0..3) of this lane's D tile.
 KDA_DEV int drow(int i) { return 4 * (lane_id() >> 4) + i; }
 KDA_DEV int dcol() { return lane_id() & 15; }

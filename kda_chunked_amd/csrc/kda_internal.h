@@ -20,13 +20,20 @@ struct ChunkTable {
 
 // Per-chunk matrices and states (the saved forward set), all fp32. The gate
 // cumsum G [T, H, 128] is carved right after rk.
+//
+// S_in, R and U~ are stored per chunk-head in MFMA tile order: a 16 x 16 tile
+// (row block rb, column block cb) is 256 contiguous floats at
+// (rb * 8 + cb) * 256, and within it the element (4 (l / 16) + i, l % 16)
+// sits at 4 l + i, i.e. each lane of the producing or consuming MFMA reads
+// or writes its four values as one 16-byte vector. Rows past the chunk's end
+// hold zeros.
 struct SavedSet {
-  float* S_in;   // [NC, H, 128, 128] state before each chunk
+  float* S_in;   // [NC, H, 128 x 128] state before each chunk (tile order)
   float* Tm;     // [NC, H, 64, 64]  (I + Diag(beta) A_kk)^-1, zero above the diagonal
   float* Aqk;    // [NC, H, 64, 64]  decayed q.k products, zero above the diagonal
   float* Akk;    // [NC, H, 64, 64]  decayed k.k products, zero on and above the diagonal
-  float* R;      // [T, H, 128]      V - (K*e^G) S_in, per token
-  float* U;      // [T, H, 128]      U~ = Tb R, per token
+  float* R;      // [NC, H, 64 x 128] V - (K*e^G) S_in (tile order)
+  float* U;      // [NC, H, 64 x 128] U~ = Tb R (tile order)
   float* rq;     // [T, H]           L2 scalars (1 without the fused norm)
   float* rk;     // [T, H]
 };
@@ -71,17 +78,19 @@ struct BwdWork {
   float* part_dt;     // [NC, H, 128] raw form: per-chunk sum of dz
 };
 
-// Per chunk-head operand panels of the forward scan, written by the prep
-// kernel as bf16 planes (hi = RNE(x), lo = RNE(x - hi)) in the row-major
-// layout the scan stages into LDS. Offsets in bf16 elements.
+// Per chunk-head operand panels of the forward pass, written by the prep
+// kernel as bf16 planes (hi = RNE(x), lo = RNE(x - hi)), row-major. The first
+// CHAIN elements are what the sequential state scan needs; the rest feed the
+// output kernel. Offsets in bf16 elements.
 namespace fwd_panel {
 constexpr int KD = 0;                        // -Kd hi            [64][128]
-constexpr int QD = KD + 64 * 128;            // scale Qd hi, lo   [2][64][128]
-constexpr int KE = QD + 2 * 64 * 128;        // Ke^T hi, lo       [2][128][64]
-constexpr int TB = KE + 2 * 128 * 64;        // Tb hi             [64][64]
-constexpr int AQ = TB + 64 * 64;             // scale A_qk hi, lo [2][64][64]
-constexpr int GAM = AQ + 2 * 64 * 64;        // e^(G_last), fp32  [128]
-constexpr int ELEMS = GAM + 2 * 128;         // bf16 elements per chunk-head
+constexpr int TB = KD + 64 * 128;            // Tb hi             [64][64]
+constexpr int KE = TB + 64 * 64;             // Ke^T hi, lo       [2][128][64]
+constexpr int GAM = KE + 2 * 128 * 64;       // e^(G_last), fp32  [128]
+constexpr int CHAIN = GAM + 2 * 128;         // end of the scan's part
+constexpr int QD = CHAIN;                    // scale Qd hi, lo   [2][64][128]
+constexpr int AQ = QD + 2 * 64 * 128;        // scale A_qk hi, lo [2][64][64]
+constexpr int ELEMS = AQ + 2 * 64 * 64;      // bf16 elements per chunk-head
 constexpr size_t BYTES = (size_t)ELEMS * 2;  // 107008, a multiple of 16
 }  // namespace fwd_panel
 
@@ -90,8 +99,9 @@ hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& 
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
                            const SavedSet& sv, void* panels, hipStream_t s);
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                           const SavedSet& sv, const void* panels, void* o, int save_states,
-                           hipStream_t s);
+                           const SavedSet& sv, const void* panels, int save_R, hipStream_t s);
+hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& sv,
+                          const void* panels, void* o, hipStream_t s);
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const float* G, const SavedSet& sv, const void* dO, void* dv,
                            const BwdWork& bw, hipStream_t s);

@@ -71,178 +71,317 @@ static int scan_grid(int P) { return ((P + 7) / 8) * 8 * NTILE; }
 KDA_DEV float bsel(bool ok, bf16 x) { return ok ? bf2f(x) : 0.f; }
 
 // ------------------------------------------------------------------ forward
-// The chunk's operands arrive ready-made from the prep kernel (fwd_panel
-// layout): -Kd, scale Qd, Ke^T, Tb, scale A_qk and e^(G_last). Each step
-// stages them into LDS with 16-byte copies (prefetched into registers during
-// the previous step), so the sequential path holds only the S-dependent
-// products and their epilogues.
-struct FwdScanSmem {
-  bf16 kd_hi[CL][K1_LD];                         // -Kd        [r][c]
-  bf16 qd_hi[CL][K1_LD], qd_lo[CL][K1_LD];       // scale Qd   [r][c]
-  bf16 ke_hi[HD][K2_LD], ke_lo[HD][K2_LD];       // Ke^T       [c][r]
-  bf16 tb_hi[CL][K2_LD];                         // Tb         [r][i]
-  bf16 aq_hi[CL][K2_LD], aq_lo[CL][K2_LD];       // scale A_qk [r][i]
-  float gam[HD];                                 // e^(G_last)
-  bf16 s_hi[VT][K1_LD], s_lo[VT][K1_LD];         // S^T        [j][c]
-  bf16 rr_hi[VT][K2_LD], rr_lo[VT][K2_LD];       // R^T        [j][r]
-  bf16 u_hi[VT][K2_LD], u_lo[VT][K2_LD];         // U~^T       [j][r]
+// The sequential state chain of one (document, head) and 32 state columns.
+// Two waves, one per 16-column slice: each wave runs the whole chain of its
+// slice by itself,
+//   R = V - Kd S_in,  U~ = Tb R,  S_out = e^(G_last) * S_in + Ke^T U~,
+// exchanging operands only through its own LDS area (no barrier). The
+// chunk's shared operands (-Kd, Tb, Ke^T, e^(G_last): the first
+// fwd_panel::CHAIN elements of its panels) are copied global -> LDS with
+// asynchronous 16-byte DMA, one chunk ahead into the other of two buffers,
+// so the only barrier per chunk is the one that hands a buffer over.
+// S_in, R (when saving for the backward) and U~ go to memory; the output
+// O = Qd S_in + A_qk U~ is formed afterwards by fwd_out_kernel, in parallel
+// over chunks.
+constexpr int FS_THREADS = 128;
+constexpr int FS_UNITS = fwd_panel::CHAIN / 8;          // 16-byte units: 3616
+constexpr int FS_PER_THREAD = (FS_UNITS + FS_THREADS - 1) / FS_THREADS;   // 29
+static_assert(fwd_panel::KD == 0 && fwd_panel::TB == 1024 * 8 && fwd_panel::KE == 1536 * 8 &&
+                  fwd_panel::GAM == 3584 * 8 && FS_UNITS == 3616,
+              "DMA map below assumes this panel layout");
+
+// One chunk's shared operands in LDS, unpadded; 16-byte chunks of each row
+// are XOR-swizzled so that 16 rows read at one K offset hit distinct banks.
+struct __attribute__((aligned(16))) ChainBuf {
+  bf16 kd[CL * HD];          // -Kd  [r][c], row 256 B, chunk ^= r & 15
+  bf16 tb[CL * CL];          // Tb   [r][i], row 128 B, chunk ^= (r >> 1) & 7
+  bf16 ke[2][HD * CL];       // Ke^T [c][r] hi, lo, as tb
+  float gam[HD];
+};
+struct __attribute__((aligned(16))) SliceBuf {            // one wave's B operands
+  bf16 s_hi[16][K1_LD];                      // S^T [j][c]
+  bf16 r_hi[16][K2_LD], r_lo[16][K2_LD];     // R^T [j][r]
+  bf16 u_hi[16][K2_LD], u_lo[16][K2_LD];     // U~^T [j][r]
 };
 
-constexpr int FP_UNITS = fwd_panel::ELEMS / 8;           // 16-byte units per chunk-head
-constexpr int FP_PER_THREAD = (FP_UNITS + NT_SCAN - 1) / NT_SCAN;
-static_assert(fwd_panel::KD == 0 && fwd_panel::QD == 1024 * 8 && fwd_panel::KE == 3072 * 8 &&
-                  fwd_panel::TB == 5120 * 8 && fwd_panel::AQ == 5632 * 8 &&
-                  fwd_panel::GAM == 6656 * 8 && FP_UNITS == 6688,
-              "staging map below assumes this panel layout");
+KDA_DEV int swz256(int row, int kc) { return row * 128 + ((kc ^ (row & 15)) << 3); }
+KDA_DEV int swz128(int row, int kc) { return row * 64 + ((kc ^ ((row >> 1) & 7)) << 3); }
 
-// LDS destination of 16-byte unit u = t + 512 k of a chunk's panels.
-KDA_DEV void stage_unit(FwdScanSmem& sm, int k, int t, const bf16x8& x) {
-  const int u = t + NT_SCAN * k;
-  bf16* dst;
-  if (k < 2) {                       // -Kd hi
-    dst = &sm.kd_hi[u >> 4][(u & 15) << 3];
-  } else if (k < 6) {                // Qd hi, lo
-    const int v = u - 1024;
-    dst = (v >> 10 ? &sm.qd_lo[0][0] : &sm.qd_hi[0][0]) + ((v >> 4) & 63) * K1_LD + ((v & 15) << 3);
-  } else if (k < 10) {               // Ke^T hi, lo
-    const int v = u - 3072;
-    dst = (v >> 10 ? &sm.ke_lo[0][0] : &sm.ke_hi[0][0]) + ((v >> 3) & 127) * K2_LD + ((v & 7) << 3);
-  } else if (k < 11) {               // Tb hi
-    const int v = u - 5120;
-    dst = &sm.tb_hi[v >> 3][(v & 7) << 3];
-  } else if (k < 13) {               // A_qk hi, lo
-    const int v = u - 5632;
-    dst = (v >> 9 ? &sm.aq_lo[0][0] : &sm.aq_hi[0][0]) + ((v >> 3) & 63) * K2_LD + ((v & 7) << 3);
-  } else {                           // e^(G_last), fp32 (32 units)
-    *reinterpret_cast<bf16x8*>(&sm.gam[4 * (u - 6656)]) = x;
-    return;
-  }
-  *reinterpret_cast<bf16x8*>(dst) = x;
+// A fragment (16 rows from m0, K = 32 from k) of a swizzled panel.
+KDA_DEV bf16x8 frag256(const bf16* p, int m0, int k) {
+  const int l = lane_id(), row = m0 + (l & 15);
+  return *reinterpret_cast<const bf16x8*>(p + swz256(row, (k >> 3) + (l >> 4)));
+}
+KDA_DEV bf16x8 frag128(const bf16* p, int m0, int k) {
+  const int l = lane_id(), row = m0 + (l & 15);
+  return *reinterpret_cast<const bf16x8*>(p + swz128(row, (k >> 3) + (l >> 4)));
 }
 
-__global__ __launch_bounds__(NT_SCAN) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                            SavedSet sv,
-                                                            const bf16* __restrict__ panels,
-                                                            bf16* __restrict__ o, int save) {
-  __shared__ FwdScanSmem sm;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous copy of chunk `src`'s chain operands into `dst` (this thread's
+// share: units t + 128 k). Lane l of each instruction lands at 16 l.
+KDA_DEV void chain_dma(ChainBuf& dst, const bf16* __restrict__ src, int t) {
+  char* base = reinterpret_cast<char*>(&dst);
+  const int w = t >> 6;
+#pragma unroll
+  for (int k = 0; k < FS_PER_THREAD; ++k) {
+    const int u = t + FS_THREADS * k;
+    int e;                                   // source element of the unit
+    if (k < 8) {
+      const int row = u >> 4;
+      e = fwd_panel::KD + row * 128 + (((u & 15) ^ (row & 15)) << 3);
+    } else if (k < 12) {
+      const int v = u - 1024, row = v >> 3;
+      e = fwd_panel::TB + row * 64 + (((v & 7) ^ ((row >> 1) & 7)) << 3);
+    } else if (k < 28) {
+      const int v = u - 1536, pl = v >> 10, row = (v >> 3) & 127;
+      e = fwd_panel::KE + pl * (HD * CL) + row * 64 + (((v & 7) ^ ((row >> 1) & 7)) << 3);
+    } else {
+      e = fwd_panel::GAM + (u - 3584) * 8;
+    }
+    if (k < FS_PER_THREAD - 1 || u < FS_UNITS)
+      __builtin_amdgcn_global_load_lds(src + e,
+                                       (lds_void*)(base + 16 * (FS_THREADS * k + 64 * w)), 16, 0,
+                                       0);
+  }
+}
+
+__global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
+                                                               SavedSet sv,
+                                                               const bf16* __restrict__ panels,
+                                                               int save_R) {
+  __shared__ ChainBuf bufA;
+  __shared__ ChainBuf bufB;
+  __shared__ SliceBuf slice[2];
   int pair, tile;
   if (!scan_coords(d.N * d.H, pair, tile)) return;
   const int doc = pair / d.H, h = pair % d.H;
   const int c0 = ct.doc_c0[doc], c1 = ct.doc_c0[doc + 1];
   const int t = threadIdx.x, w = wave_id();
-  const int rb = w & 3, nw = w >> 2;       // R / U~ / O tile of this wave: rows 16 rb, cols 16 nw
-  const int j0 = tile * VT;
+  const int jv = tile * VT + 16 * w;          // this wave's 16 state columns
   const int H = d.H;
   const bf16* v = reinterpret_cast<const bf16*>(in.v);
+  SliceBuf& sb = slice[w];
+  const Panel SB{&sb.s_hi[0][0], nullptr, K1_LD};
+  const Panel RB{&sb.r_hi[0][0], &sb.r_lo[0][0], K2_LD};
+  const Panel UB{&sb.u_hi[0][0], &sb.u_lo[0][0], K2_LD};
 
-  const Panel KD{&sm.kd_hi[0][0], nullptr, K1_LD};
-  const Panel QD{&sm.qd_hi[0][0], &sm.qd_lo[0][0], K1_LD};
-  const Panel KE{&sm.ke_hi[0][0], &sm.ke_lo[0][0], K2_LD};
-  const Panel TB{&sm.tb_hi[0][0], nullptr, K2_LD};
-  const Panel AQ{&sm.aq_hi[0][0], &sm.aq_lo[0][0], K2_LD};
-  const Panel SP{&sm.s_hi[0][0], &sm.s_lo[0][0], K1_LD};
-  const Panel RP{&sm.rr_hi[0][0], &sm.rr_lo[0][0], K2_LD};
-  const Panel UP{&sm.u_hi[0][0], &sm.u_lo[0][0], K2_LD};
-
-  // next chunk's panels and V tile, held in registers
-  bf16x8 pu[FP_PER_THREAD];
-  bf16 pv[4];
+  // state slice: tile m holds rows 16 m .. 16 m + 15 (D layout)
+  f32x4 S[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) S[m] = zero4();
+  // V of the next chunk at this lane's R elements (rows 16 rb + drow(i))
+  bf16 pv[4][4];
   int64_t pt0 = 0;
   int pn = 0;
-  auto prefetch = [&](int cn) {
-    pt0 = ct.tok[cn];
-    pn = ct.len[cn];
-    const bf16* src = panels + ((int64_t)cn * H + h) * fwd_panel::ELEMS;
+  // V loads of chunk cn; its table entry (pt0, pn) must be in registers already
+  auto prefetch_v = [&](int cn) {
 #pragma unroll
-    for (int k = 0; k < FP_PER_THREAD; ++k)
-      if (k < FP_PER_THREAD - 1 || t < FP_UNITS - NT_SCAN * (FP_PER_THREAD - 1))
-        pu[k] = *reinterpret_cast<const bf16x8*>(src + 8 * (t + NT_SCAN * k));
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * rb + drow(i), rc = rr < pn ? rr : pn - 1;
-      pv[i] = v[((pt0 + rc) * H + h) * HD + j0 + 16 * nw + dcol()];
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + drow(i), rc = r < pn ? r : pn - 1;
+        pv[rb][i] = v[((pt0 + rc) * H + h) * HD + jv + dcol()];
+      }
   };
+  auto panel_of = [&](int cn) { return panels + ((int64_t)cn * H + h) * fwd_panel::ELEMS; };
 
-  // state: wave w owns state rows [16w, 16w+16) x 32 columns
-  f32x4 S[2];
-  S[0] = S[1] = zero4();
-  if (c0 < c1) prefetch(c0);
-
-  for (int ci = c0; ci < c1; ++ci) {
+  auto step = [&](ChainBuf& cur, ChainBuf& nxt, int ci) {
     const int64_t t0 = pt0;
     const int n = pn;
     const int64_t ch = (int64_t)ci * H + h;
-    __syncthreads();                       // the previous chunk's operands are consumed
+    f32x4 R[4];
 #pragma unroll
-    for (int k = 0; k < FP_PER_THREAD; ++k)
-      if (k < FP_PER_THREAD - 1 || t < FP_UNITS - NT_SCAN * (FP_PER_THREAD - 1))
-        stage_unit(sm, k, t, pu[k]);
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) store_tile_t(S[nt], SP, 16 * w, 16 * nt);
-    f32x4 R;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) R[i] = bsel(16 * rb + drow(i) < n, pv[i]);
-    if (save) {
+      for (int i = 0; i < 4; ++i) R[rb][i] = bsel(16 * rb + drow(i) < n, pv[rb][i]);
+    // the next chunk's table entry, read before the wait below so that no later
+    // wait for it also waits for the next chunk's copies
+    if (ci + 1 < c1) {
+      pt0 = ct.tok[ci + 1];
+      pn = ct.len[ci + 1];
+    }
+    __builtin_amdgcn_s_waitcnt(0);     // this thread's copies of `cur` have landed
+    __syncthreads();                   // ... and the other wave's; `nxt` is free
+    if (ci + 1 < c1) {
+      chain_dma(nxt, panel_of(ci + 1), t);
+      prefetch_v(ci + 1);
+    }
+    // S_in: to memory and, as B operand, to this wave's LDS
+    {
       float* Sg = sv.S_in + ch * HD * HD;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Sg[(16 * w + drow(i)) * HD + j0 + 16 * nt + dcol()] = S[nt][i];
-    }
-    if (ci + 1 < c1) prefetch(ci + 1);
-    __syncthreads();
-    // ---- R = V - Kd S_in (the panel holds -Kd)
-    mma_k<SPLIT_KS, HD>(R, KD, 16 * rb, SP, 16 * nw);
-    if (save) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + drow(i);
-        if (r < n) sv.R[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = R[i];
+      for (int m = 0; m < 8; ++m) {
+        *reinterpret_cast<f32x4*>(Sg + tile_off(m, jv >> 4)) = S[m];
+        store_tile_t(S[m], SB, 16 * m, 0);
       }
     }
-    store_tile_t(R, RP, 16 * rb, 16 * nw);
-    __syncthreads();
-    // ---- U~ = Tb R
-    const int kend = ((16 * rb + 16 + 31) / 32) * 32;
-    f32x4 U = zero4();
-    mma<SPLIT_TR>(U, TB, 16 * rb, RP, 16 * nw, 0, kend);
-    if (save) {
+    // R = V - Kd S_in (the panel holds -Kd)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + drow(i);
-        if (r < n) sv.U[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = U[i];
+    for (int k = 0; k < HD; k += 32) {
+      const bf16x8 b = frag(SB.hi, SB.ld, 0, k);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) R[rb] = mfma16(frag256(cur.kd, 16 * rb, k), b, R[rb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (save_R) *reinterpret_cast<f32x4*>(sv.R + ch * CL * HD + tile_off(rb, jv >> 4)) = R[rb];
+      store_tile_t(R[rb], RB, 16 * rb, 0);
+    }
+    // U~ = Tb R (Tb lower triangular: K up to the end of the row block)
+    f32x4 U[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) U[rb] = zero4();
+#pragma unroll
+    for (int k = 0; k < CL; k += 32) {
+      const bf16x8 bh = frag(RB.hi, RB.ld, 0, k);
+      const bf16x8 bl = frag(RB.lo, RB.ld, 0, k);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (k < 16 * rb + 16) {
+          const bf16x8 a = frag128(cur.tb, 16 * rb, k);
+          U[rb] = mfma16(a, bl, U[rb]);
+          U[rb] = mfma16(a, bh, U[rb]);
+        }
       }
     }
-    store_tile_t(U, UP, 16 * rb, 16 * nw);
-    __syncthreads();
-    // ---- O = scale (Qd S_in + A_qk U~)   (skipped when replaying)
-    if (o != nullptr) {
-      f32x4 acc = zero4();
-      mma_k<SPLIT_QS, HD>(acc, QD, 16 * rb, SP, 16 * nw);
-      mma<SPLIT_AU>(acc, AQ, 16 * rb, UP, 16 * nw, 0, kend);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + drow(i);
-        if (r < n) o[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = f2bf(acc[i]);
+    for (int rb = 0; rb < 4; ++rb) {
+      *reinterpret_cast<f32x4*>(sv.U + ch * CL * HD + tile_off(rb, jv >> 4)) = U[rb];
+      store_tile_t(U[rb], UB, 16 * rb, 0);
+    }
+    // S_out = e^(G_last) * S_in + Ke^T U~
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[m][i] *= cur.gam[16 * m + drow(i)];
+#pragma unroll
+    for (int k = 0; k < CL; k += 32) {
+      const bf16x8 bh = frag(UB.hi, UB.ld, 0, k);
+      const bf16x8 bl = frag(UB.lo, UB.ld, 0, k);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const bf16x8 ah = frag128(cur.ke[0], 16 * m, k);
+        const bf16x8 al = frag128(cur.ke[1], 16 * m, k);
+        S[m] = mfma16(al, bh, S[m]);
+        S[m] = mfma16(ah, bl, S[m]);
+        S[m] = mfma16(ah, bh, S[m]);
       }
     }
-    // ---- S_out = Diag(e^G_last) S_in + Ke^T U~
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[nt][i] *= sm.gam[16 * w + drow(i)];
-    mma_row<SPLIT_KU, 2>(S, KE, 16 * w, UP, 0, 0, CL);
+  };
+
+  if (c0 < c1) {
+    pt0 = ct.tok[c0];
+    pn = ct.len[c0];
+    chain_dma(bufA, panel_of(c0), t);
+    prefetch_v(c0);
+  }
+  for (int ci = c0; ci < c1; ci += 2) {
+    step(bufA, bufB, ci);
+    if (ci + 1 < c1) step(bufB, bufA, ci + 1);
   }
 }
 
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                           const SavedSet& sv, const void* panels, void* o, int save_states,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(fwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(NT_SCAN), 0, s, d, in,
-                     ct, sv, reinterpret_cast<const bf16*>(panels), reinterpret_cast<bf16*>(o),
-                     save_states);
+                           const SavedSet& sv, const void* panels, int save_R, hipStream_t s) {
+  hipLaunchKernelGGL(fwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(FS_THREADS), 0, s, d, in,
+                     ct, sv, reinterpret_cast<const bf16*>(panels), save_R);
+  return hipGetLastError();
+}
+
+// O = scale (Qd S_in + A_qk U~) per (chunk, head), from the saved S_in and U~
+// and the output panels (scale folded in). 8 waves: rows 16 (w & 3), columns
+// 64 (w >> 2) .. + 63. A operands are read from memory as MFMA fragments; the
+// B operands S_in^T and U~^T are split into LDS panels.
+struct FwdOutSmem {
+  bf16 s_hi[HD][K1_LD], s_lo[HD][K1_LD];     // S_in^T [j][c]
+  bf16 u_hi[HD][K2_LD], u_lo[HD][K2_LD];     // U~^T   [j][i]
+};
+
+KDA_DEV bf16x8 gfrag(const bf16* p, int ld, int m0, int k) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(p + (m0 + (l & 15)) * ld + k + ((l >> 4) << 3));
+}
+
+__global__ __launch_bounds__(512) void fwd_out_kernel(Dims d, ChunkTable ct,
+                                                       SavedSet sv,
+                                                       const bf16* __restrict__ panels,
+                                                       bf16* __restrict__ o) {
+  __shared__ FwdOutSmem sm;
+  const int ci = blockIdx.x, h = blockIdx.y;
+  if (ci >= ct.doc_c0[d.N]) return;
+  const int64_t t0 = ct.tok[ci];
+  const int n = ct.len[ci];
+  const int t = threadIdx.x, w = wave_id();
+  const int rb = w & 3, chh = w >> 2;
+  const int H = d.H;
+  const int64_t ch = (int64_t)ci * H + h;
+  const bf16* P = panels + ch * fwd_panel::ELEMS;
+  const Panel SP{&sm.s_hi[0][0], &sm.s_lo[0][0], K1_LD};
+  const Panel UP{&sm.u_hi[0][0], &sm.u_lo[0][0], K2_LD};
+  // S_in [c][j] -> S_in^T panel: wave w stores tiles (c block w, all 8 j blocks)
+  {
+    const float* Sg = sv.S_in + ch * HD * HD;
+    const float* Ug = sv.U + ch * CL * HD;
+    f32x4 xs[8], xu[4];
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) xs[jb] = *reinterpret_cast<const f32x4*>(Sg + tile_off(w, jb));
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) xu[ib] = *reinterpret_cast<const f32x4*>(Ug + tile_off(ib, w));
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) store_tile_t(xs[jb], SP, 16 * w, 16 * jb);
+    // U~ [i][j] -> U~^T panel: wave w: j block w, i blocks 0..3
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) store_tile_t(xu[ib], UP, 16 * ib, 16 * w);
+  }
+  __syncthreads();
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+  const bf16* qh = P + fwd_panel::QD;
+  const bf16* ql = qh + CL * HD;
+#pragma unroll
+  for (int k = 0; k < HD; k += 32) {
+    const bf16x8 ah = gfrag(qh, HD, 16 * rb, k), al = gfrag(ql, HD, 16 * rb, k);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n0 = 64 * chh + 16 * nt;
+      const bf16x8 bh = frag(SP.hi, SP.ld, n0, k), bl = frag(SP.lo, SP.ld, n0, k);
+      acc[nt] = mfma16(al, bh, acc[nt]);
+      acc[nt] = mfma16(ah, bl, acc[nt]);
+      acc[nt] = mfma16(ah, bh, acc[nt]);
+    }
+  }
+  const bf16* aqh = P + fwd_panel::AQ;
+  const bf16* aql = aqh + CL * CL;
+  const int kend = ((16 * rb + 16 + 31) / 32) * 32;
+  for (int k = 0; k < kend; k += 32) {
+    const bf16x8 ah = gfrag(aqh, CL, 16 * rb, k), al = gfrag(aql, CL, 16 * rb, k);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n0 = 64 * chh + 16 * nt;
+      const bf16x8 bh = frag(UP.hi, UP.ld, n0, k), bl = frag(UP.lo, UP.ld, n0, k);
+      acc[nt] = mfma16(al, bh, acc[nt]);
+      acc[nt] = mfma16(ah, bl, acc[nt]);
+      acc[nt] = mfma16(ah, bh, acc[nt]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * rb + drow(i);
+    if (r < n) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        o[((t0 + r) * H + h) * HD + 64 * chh + 16 * nt + dcol()] = f2bf(acc[nt][i]);
+    }
+  }
+}
+
+hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& sv,
+                          const void* panels, void* o, hipStream_t s) {
+  hipLaunchKernelGGL(fwd_out_kernel, dim3(d.NC, d.H), dim3(512), 0, s, d, ct, sv,
+                     reinterpret_cast<const bf16*>(panels), reinterpret_cast<bf16*>(o));
   return hipGetLastError();
 }
 
