@@ -75,6 +75,7 @@ kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states, float** G)
     sv.S_in = c.take<float>((size_t)s.NC * s.H * 128 * 128);
     sv.R = c.take<float>((size_t)s.NC * s.H * 64 * 128);
     sv.U = c.take<float>((size_t)s.NC * s.H * 64 * 128);
+    sv.bwd_panels = c.take<uint16_t>((size_t)s.NC * s.H * kda::bwd_panel::ELEMS);
   }
   return sv;
 }
@@ -87,8 +88,8 @@ void* carve_panels(Carver& c, const Sizes& s) {
 kda::BwdWork carve_bwd(Carver& c, const Sizes& s) {
   kda::BwdWork bw;
   bw.dS = c.take<float>((size_t)s.NC * s.H * 128 * 128);
-  bw.dU = c.take<float>((size_t)s.T * s.H * 128);
-  bw.dR = c.take<float>((size_t)s.T * s.H * 128);
+  bw.dU = c.take<float>((size_t)s.NC * s.H * 64 * 128);
+  bw.dR = c.take<float>((size_t)s.NC * s.H * 64 * 128);
   bw.part_A = c.take<float>((size_t)s.NC * s.H);
   bw.part_dt = c.take<float>((size_t)s.NC * s.H * 128);
   return bw;
@@ -230,7 +231,7 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
     sv = carve_saved(sc, s, 1, &G);
   }
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
-  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, hs));
+  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, saved != nullptr, hs));
   LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, saved != nullptr, hs));
   LAUNCH("fwd_out", kda::launch_fwd_out(d, ct, sv, panels, o, hs));
   return KDA_OK;
@@ -295,7 +296,7 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   if (replay) {
-    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, hs));
+    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, 1, hs));
     LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, 1, hs));
   }
   LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, G, sv, dO, dv, bw, hs));

@@ -208,18 +208,6 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) adq[nt] = adk[nt] = adG[nt] = zero4();
 
-  // fp32 [T, H, 128] values at this thread's 16 elements (zero on padded rows)
-  auto load_elems = [&](const float* src, f32x4 (&x)[4]) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + drow(i);
-        const float v = src[rowidx(clampr(r)) * HD + 64 * chh + 16 * nt + dcol()];
-        x[nt][i] = r < n ? v : 0.f;
-      }
-  };
-
   // ------------------------------------------------------------ P2: dQd, dKd
   // dR (= dv, fp32) from the reverse scan
   const Panel SP{&sm.u.p2.s_hi[0][0], &sm.u.p2.s_lo[0][0], K1_LD};
@@ -236,7 +224,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   };
   {
     f32x4 dR[4];
-    load_elems(bw.dR, dR);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)   // dR from the reverse scan (tile order)
+      dR[nt] = *reinterpret_cast<const f32x4*>(bw.dR + ch * CL * HD + tile_off(rb, 4 * chh + nt));
     load_state_panel(sv.S_in + ch * HD * HD);
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
@@ -291,57 +281,29 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
       U[nt] = *reinterpret_cast<const f32x4*>(sv.U + ch * CL * HD + tile_off(rb, 4 * chh + nt));
-    // dS_out replaces S_in in the panel. dgamma[c] = sum_j dS_out[c][j] S_in[c][j]
-    // takes S_in from the split panel (hi + lo) just before it is overwritten:
-    // each thread rewrites exactly the elements it reads.
+    // dS_out replaces S_in in the panel; dgamma[c] = sum_j dS_out[c][j] S_in[c][j]
+    // in fp32 from both matrices in tile order (wave w: row block w, 8 tiles)
     {
-      const float* src = bw.dS + ch * HD * HD;
+      const float* dSg = bw.dS + ch * HD * HD;
+      const float* Sg = sv.S_in + ch * HD * HD;
       f32x4 v[8];
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rep = 0; rep < 8; ++rep) {
-        const int e = t + NTHR * rep, c = e >> 5, j4 = (e & 31) * 4;
-        v[rep] = *reinterpret_cast<const f32x4*>(src + c * HD + j4);
-      }
-      float part[8];
+      for (int jb = 0; jb < 8; ++jb) v[jb] = *reinterpret_cast<const f32x4*>(dSg + tile_off(w, jb));
 #pragma unroll
-      for (int rep = 0; rep < 8; ++rep) {
-        const int e = t + NTHR * rep, c = e >> 5, j4 = (e & 31) * 4;
-        const bf16x4 sh = *reinterpret_cast<const bf16x4*>(SP.hi + c * K1_LD + j4);
-        const bf16x4 sl = *reinterpret_cast<const bf16x4*>(SP.lo + c * K1_LD + j4);
-        float acc = 0.f;
+      for (int jb = 0; jb < 8; ++jb) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(Sg + tile_off(w, jb));
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) acc += v[rep][q4] * (bf2f(sh[q4]) + bf2f(sl[q4]));
-        part[rep] = acc;
-        put4(SP, c, j4, v[rep]);
-      }
-      // sum each part[rep] over the 32 lanes that share its channel: halving
-      // exchanges leave lane l with the total of rep = 4 b4 + 2 b3 + b2
-      // (b_k = bit k of l)
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const bool up = l & 16;
-        const float send = up ? part[k4] : part[k4 + 4];
-        const float keep = up ? part[k4 + 4] : part[k4];
-        part[k4] = keep + __shfl_xor(send, 16);
+        for (int i = 0; i < 4; ++i) part[i] += v[jb][i] * x[i];
+        store_tile_n(v[jb], SP, 16 * w, 16 * jb);
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const bool up = l & 8;
-        const float send = up ? part[k2] : part[k2 + 2];
-        const float keep = up ? part[k2 + 2] : part[k2];
-        part[k2] = keep + __shfl_xor(send, 8);
-      }
-      {
-        const bool up = l & 4;
-        const float send = up ? part[0] : part[1];
-        const float keep = up ? part[1] : part[0];
-        part[0] = keep + __shfl_xor(send, 4);
-      }
-      part[0] += __shfl_xor(part[0], 2);
-      part[0] += __shfl_xor(part[0], 1);
-      if ((l & 3) == 0) {
-        const int rep = 4 * ((l >> 4) & 1) + 2 * ((l >> 3) & 1) + ((l >> 2) & 1);
-        sm.dgam[(t >> 5) + 16 * rep] = part[0];
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) part[i] += __shfl_xor(part[i], m);
+      if (dcol() == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.dgam[16 * w + drow(i)] = part[i];
       }
     }
 #pragma unroll
@@ -380,18 +342,16 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   {
     const Panel DU{&sm.u.p4.a_hi[0][0], &sm.u.p4.a_lo[0][0], K1_LD};
     const Panel RP{&sm.u.p4.b_hi[0][0], &sm.u.p4.b_lo[0][0], K1_LD};
+    // dU~ and R, tile order: wave w takes row block w & 3, column blocks 4 (w >> 2) ..
     f32x4 va[4], vb[4];
 #pragma unroll
     for (int rep = 0; rep < 4; ++rep) {
-      const int e = t + NTHR * rep, r = e >> 5, j4 = (e & 31) * 4;
-      va[rep] = *reinterpret_cast<const f32x4*>(bw.dU + rowidx(clampr(r)) * HD + j4);
-      // R, tile order: wave w takes row block w & 3, column blocks 4 (w >> 2) + rep
+      va[rep] = *reinterpret_cast<const f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, 4 * chh + rep));
       vb[rep] = *reinterpret_cast<const f32x4*>(sv.R + ch * CL * HD + tile_off(rb, 4 * chh + rep));
     }
 #pragma unroll
     for (int rep = 0; rep < 4; ++rep) {
-      const int e = t + NTHR * rep, r = e >> 5, j4 = (e & 31) * 4;
-      put4(DU, r, j4, r < n ? va[rep] : zero4());
+      store_tile_n(va[rep], DU, 16 * rb, 64 * chh + 16 * rep);
       store_tile_n(vb[rep], RP, 16 * rb, 64 * chh + 16 * rep);
     }
     __syncthreads();

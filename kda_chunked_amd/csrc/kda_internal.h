@@ -36,6 +36,7 @@ struct SavedSet {
   float* U;      // [NC, H, 64 x 128] U~ = Tb R (tile order)
   float* rq;     // [T, H]           L2 scalars (1 without the fused norm)
   float* rk;     // [T, H]
+  void* bwd_panels;   // [NC, H, bwd_panel::ELEMS] bf16: the reverse scan's operands
 };
 
 struct Dims {
@@ -71,9 +72,9 @@ struct BwdOut {
 };
 
 struct BwdWork {
-  float* dS;          // [NC, H, 128, 128] gradient w.r.t. the state after each chunk
-  float* dU;          // [T, H, 128] gradient w.r.t. U~ (the chunk's transformed values)
-  float* dR;          // [T, H, 128] gradient w.r.t. R (= dv in fp32)
+  float* dS;          // [NC, H, 128 x 128] gradient w.r.t. the state after each chunk (tile order)
+  float* dU;          // [NC, H, 64 x 128] gradient w.r.t. U~ (tile order, as SavedSet::R)
+  float* dR;          // [NC, H, 64 x 128] gradient w.r.t. R (= dv in fp32; tile order)
   float* part_A;      // [NC, H]      raw form: per-chunk sum of dg*g
   float* part_dt;     // [NC, H, 128] raw form: per-chunk sum of dz
 };
@@ -94,10 +95,22 @@ constexpr int ELEMS = AQ + 2 * 64 * 64;      // bf16 elements per chunk-head
 constexpr size_t BYTES = (size_t)ELEMS * 2;  // 107008, a multiple of 16
 }  // namespace fwd_panel
 
+// Per chunk-head operand panels of the reverse state scan, written by the prep
+// kernel into the saved set: bf16 hi, lo planes, row-major, K contiguous.
+namespace bwd_panel {
+constexpr int KE = 0;                        // Ke = k^ e^(G_last - G)     [2][64][128]  rows r
+constexpr int AQT = KE + 2 * 64 * 128;       // scale A_qk^T                [2][64][64]   rows r, K = i
+constexpr int TBT = AQT + 2 * 64 * 64;       // Tb^T                        [2][64][64]   rows i, K = r
+constexpr int QDT = TBT + 2 * 64 * 64;       // scale Qd^T                  [2][128][64]  rows c, K = r
+constexpr int KDT = QDT + 2 * 128 * 64;      // -Kd^T                       [2][128][64]  rows c, K = r
+constexpr int GAM = KDT + 2 * 128 * 64;      // e^(G_last), fp32            [128]
+constexpr int ELEMS = GAM + 2 * 128;         // 65792 bf16 elements (a multiple of 8)
+}  // namespace bwd_panel
+
 hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
                             hipStream_t s);
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
-                           const SavedSet& sv, void* panels, hipStream_t s);
+                           const SavedSet& sv, void* panels, int with_bwd, hipStream_t s);
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, const void* panels, int save_R, hipStream_t s);
 hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& sv,

@@ -124,7 +124,8 @@ KDA_DEV void decayed_frag(const PrepSmem& sm, const bf16 (*x)[XS_LD], float rx, 
 
 __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, ChunkTable ct,
                                                             float* __restrict__ G_out,
-                                                            SavedSet sv, bf16* __restrict__ panels) {
+                                                            SavedSet sv, bf16* __restrict__ panels,
+                                                            bf16* __restrict__ bwd_panels) {
   __shared__ PrepSmem sm;
   const int ci = blockIdx.x, h = blockIdx.y;
   if (ci >= ct.doc_c0[d.N]) return;
@@ -462,12 +463,72 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     }
     if (t < HD) reinterpret_cast<float*>(P + fwd_panel::GAM)[t] = fexp(sm.Gref[4][t]);
   }
+  if (bwd_panels) {
+    // the reverse scan's operands (bwd_panel layout)
+    bf16* B = bwd_panels + ch * (int64_t)bwd_panel::ELEMS;
+    auto put8g = [](bf16* hi, bf16* lo, const float* x) {
+      bf16x8 a, b;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        a[j] = f2bf(x[j]);
+        b[j] = f2bf(x[j] - bf2f(a[j]));
+      }
+      *reinterpret_cast<bf16x8*>(hi) = a;
+      *reinterpret_cast<bf16x8*>(lo) = b;
+    };
+    {
+      // Ke [r][c] = k^_r e^(G_last - G_r): this thread's row rA, channels cA ..
+      const float rkA = sm.rk[rA];
+      float x[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        x[j] = bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA * fexp(sm.Gref[4][cA + j] - Gv[j]);
+      bf16* hi = B + bwd_panel::KE + rA * HD + cA;
+      put8g(hi, hi + CL * HD, x);
+      put8g(hi + 8, hi + 8 + CL * HD, x + 8);
+    }
+    {
+      // scale A_qk^T [r][i] = scale A_qk[i][r];  Tb^T [i][r] = T[r][i] beta_i
+      const int r = t >> 3, i8 = 8 * (t & 7);
+      float a[8], b[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        a[j] = sm.Aqk[i8 + j][r] * d.scale;
+        b[j] = Tm[i8 + j][r] * sm.beta[r];
+      }
+      bf16* ah = B + bwd_panel::AQT + r * CL + i8;
+      bf16* bh = B + bwd_panel::TBT + r * CL + i8;
+      put8g(ah, ah + CL * CL, a);
+      put8g(bh, bh + CL * CL, b);
+    }
+    {
+      // scale Qd^T [c][r] = scale q^_r e^(G_r), -Kd^T [c][r] = -k^_r e^(G_r):
+      // thread (channel c, rows 16 b .. 16 b + 15)
+      const int c = t & 127, b = t >> 7;
+      float xq[16], xk[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 16 * b + j;
+        const float e1 = fexp(sm.G[r][c]);
+        xq[j] = bf2f(sm.qs[r][c]) * sm.rq[r] * e1 * d.scale;
+        xk[j] = -bf2f(sm.ks[r][c]) * sm.rk[r] * e1;
+      }
+      bf16* qh = B + bwd_panel::QDT + c * CL + 16 * b;
+      bf16* kh = B + bwd_panel::KDT + c * CL + 16 * b;
+      put8g(qh, qh + HD * CL, xq);
+      put8g(qh + 8, qh + 8 + HD * CL, xq + 8);
+      put8g(kh, kh + HD * CL, xk);
+      put8g(kh + 8, kh + 8 + HD * CL, xk + 8);
+    }
+    if (t < HD) reinterpret_cast<float*>(B + bwd_panel::GAM)[t] = fexp(sm.Gref[4][t]);
+  }
 }
 
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
-                           const SavedSet& sv, void* panels, hipStream_t s) {
+                           const SavedSet& sv, void* panels, int with_bwd, hipStream_t s) {
   hipLaunchKernelGGL(fwd_prep_kernel, dim3(d.NC, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
-                     reinterpret_cast<bf16*>(panels));
+                     reinterpret_cast<bf16*>(panels),
+                     with_bwd ? reinterpret_cast<bf16*>(sv.bwd_panels) : nullptr);
   return hipGetLastError();
 }
 

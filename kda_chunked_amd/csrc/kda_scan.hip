@@ -386,38 +386,60 @@ hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& s
 }
 
 // ------------------------------------------------------------------ reverse
+// Operands come ready-made from the saved set (bwd_panel layout, written by
+// the prep kernel) and are staged into LDS with 16-byte copies prefetched
+// into registers one chunk ahead; scale Qd^T shares its LDS space with Ke and
+// is staged once Ke has been consumed.
 struct BwdScanSmem {
   union {
-    struct { bf16 hi[CL][K1_LD], lo[CL][K1_LD]; } ke;      // Ke    [r][c]
-    struct { bf16 hi[HD][K2_LD], lo[HD][K2_LD]; } qd;      // scale*Qd^T [c][r]
+    struct { bf16 hi[CL][K1_LD], lo[CL][K1_LD]; } ke;      // Ke           [r][c]
+    struct { bf16 hi[HD][K2_LD], lo[HD][K2_LD]; } qd;      // scale*Qd^T   [c][r]
   } r1;
-  bf16 kd_hi[HD][K2_LD], kd_lo[HD][K2_LD];                 // -Kd^T [c][r]
-  bf16 aq_hi[CL][K2_LD], aq_lo[CL][K2_LD];                 // scale*A_qk^T [i][r]
-  bf16 tb_hi[CL][K2_LD], tb_lo[CL][K2_LD];                 // Tb^T [i][r]
+  bf16 kd_hi[HD][K2_LD], kd_lo[HD][K2_LD];                 // -Kd^T        [c][r]
+  bf16 aq_hi[CL][K2_LD], aq_lo[CL][K2_LD];                 // scale*A_qk^T [r][i]
+  bf16 tb_hi[CL][K2_LD], tb_lo[CL][K2_LD];                 // Tb^T         [i][r]
   bf16 do_hi[VT][K2_LD];                                   // dO^T [j][r] (exact bf16)
   bf16 ds_hi[VT][K1_LD], ds_lo[VT][K1_LD];                 // dS^T [j][c]
   bf16 du_hi[VT][K2_LD], du_lo[VT][K2_LD];                 // dU~^T [j][r]
   bf16 dr_hi[VT][K2_LD], dr_lo[VT][K2_LD];                 // dR^T [j][r]
   float gam[HD];
-  float GL[HD];
-  float rk[CL], rq[CL], beta[CL];
 };
 
-struct BwdPref {
-  bf16x8 k0, k1;             // row rA, channels cA .. cA+15 (for Ke)
-  f32x4 g[4];
-  float at[8], tt[8];        // A_qk and T at rows 8*(t>>6) .. +7, column t&63
-  bf16x8 qt[2], kt[2];       // q, k at channel cB, rows rB .. rB+15 (for Qd^T, Kd^T)
-  float gt[16];
-  float gl;                  // G_last of channel cB
-  bf16 dov[4];               // dO^T tile: column t&31, rows 4*(t>>5) .. +3
-  float sb, sq, sk;
-  int64_t t0;
-  int n;
-};
+constexpr int BP_UNITS = bwd_panel::ELEMS / 8;           // 8224
+constexpr int BP_PER_THREAD = (BP_UNITS + NT_SCAN - 1) / NT_SCAN;   // 17
+static_assert(bwd_panel::KE == 0 && bwd_panel::AQT == 2048 * 8 && bwd_panel::TBT == 3072 * 8 &&
+                  bwd_panel::QDT == 4096 * 8 && bwd_panel::KDT == 6144 * 8 &&
+                  bwd_panel::GAM == 8192 * 8 && BP_UNITS == 8224,
+              "staging map below assumes this panel layout");
+
+// LDS destination of unit u = t + 512 k (k != 8..11: those are scale Qd^T,
+// staged separately into the Ke space).
+KDA_DEV void bstage_unit(BwdScanSmem& sm, int k, int t, const bf16x8& x) {
+  const int u = t + NT_SCAN * k;
+  bf16* dst;
+  if (k < 4) {                       // Ke hi, lo
+    const int v = u;
+    dst = (v >> 10 ? &sm.r1.ke.lo[0][0] : &sm.r1.ke.hi[0][0]) + ((v >> 4) & 63) * K1_LD + ((v & 15) << 3);
+  } else if (k < 6) {                // A_qk^T hi, lo
+    const int v = u - 2048;
+    dst = (v >> 9 ? &sm.aq_lo[0][0] : &sm.aq_hi[0][0]) + ((v >> 3) & 63) * K2_LD + ((v & 7) << 3);
+  } else if (k < 8) {                // Tb^T hi, lo
+    const int v = u - 3072;
+    dst = (v >> 9 ? &sm.tb_lo[0][0] : &sm.tb_hi[0][0]) + ((v >> 3) & 63) * K2_LD + ((v & 7) << 3);
+  } else if (k < 12) {               // scale Qd^T hi, lo (into the Ke space)
+    const int v = u - 4096;
+    dst = (v >> 10 ? &sm.r1.qd.lo[0][0] : &sm.r1.qd.hi[0][0]) + ((v >> 3) & 127) * K2_LD + ((v & 7) << 3);
+  } else if (k < 16) {               // -Kd^T hi, lo
+    const int v = u - 6144;
+    dst = (v >> 10 ? &sm.kd_lo[0][0] : &sm.kd_hi[0][0]) + ((v >> 3) & 127) * K2_LD + ((v & 7) << 3);
+  } else {                           // e^(G_last), fp32 (32 units)
+    *reinterpret_cast<bf16x8*>(&sm.gam[4 * (u - 8192)]) = x;
+    return;
+  }
+  *reinterpret_cast<bf16x8*>(dst) = x;
+}
 
 __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                            const float* __restrict__ G,
                                                             SavedSet sv,
                                                             const bf16* __restrict__ dO,
                                                             bf16* __restrict__ dv, BwdWork bw) {
@@ -430,13 +452,8 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   const int rb = w & 3, nw = w >> 2;
   const int j0 = tile * VT;
   const int H = d.H;
-  const bf16* q = reinterpret_cast<const bf16*>(in.q);
-  const bf16* k = reinterpret_cast<const bf16*>(in.k);
-  const bf16* beta = reinterpret_cast<const bf16*>(in.beta);
-  const int rA = t >> 3, cA = 16 * (t & 7);
-  const int cB = t & 127, rB = 16 * (t >> 7);
-  const int iC = t & 63, rC = 8 * (t >> 6);
   const int jD = t & 31, rD = 4 * (t >> 5);
+  const bf16* BP = reinterpret_cast<const bf16*>(sv.bwd_panels);
 
   const Panel KE{&sm.r1.ke.hi[0][0], &sm.r1.ke.lo[0][0], K1_LD};
   const Panel QD{&sm.r1.qd.hi[0][0], &sm.r1.qd.lo[0][0], K2_LD};
@@ -448,46 +465,22 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   const Panel DU{&sm.du_hi[0][0], &sm.du_lo[0][0], K2_LD};
   const Panel DR{&sm.dr_hi[0][0], &sm.dr_lo[0][0], K2_LD};
 
-  BwdPref pf;
-  auto prefetch_main = [&](int cn) {
-    pf.t0 = ct.tok[cn];
-    pf.n = ct.len[cn];
-    const int64_t ch = (int64_t)cn * H + h;
-    const int r = rA < pf.n ? rA : pf.n - 1;
-    const int64_t base = ((pf.t0 + r) * H + h) * HD + cA;
-    pf.k0 = *reinterpret_cast<const bf16x8*>(k + base);
-    pf.k1 = *reinterpret_cast<const bf16x8*>(k + base + 8);
+  bf16x8 pu[BP_PER_THREAD];
+  bf16 pdo[4];
+  int64_t pt0 = 0;
+  int pn = 0;
+  auto prefetch = [&](int cn) {
+    pt0 = ct.tok[cn];
+    pn = ct.len[cn];
+    const bf16* src = BP + ((int64_t)cn * H + h) * bwd_panel::ELEMS;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pf.g[j] = *reinterpret_cast<const f32x4*>(G + base + 4 * j);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pf.at[j] = sv.Aqk[ch * CL * CL + (rC + j) * CL + iC];
-      pf.tt[j] = sv.Tm[ch * CL * CL + (rC + j) * CL + iC];
-    }
+    for (int k = 0; k < BP_PER_THREAD; ++k)
+      if (k < BP_PER_THREAD - 1 || t < BP_UNITS - NT_SCAN * (BP_PER_THREAD - 1))
+        pu[k] = *reinterpret_cast<const bf16x8*>(src + 8 * (t + NT_SCAN * k));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int rr = rD + j, rc = rr < pf.n ? rr : pf.n - 1;
-      pf.dov[j] = dO[((pf.t0 + rc) * H + h) * HD + j0 + jD];
-    }
-    if (t < CL) {
-      const int rt = t < pf.n ? t : pf.n - 1;
-      const int64_t ri = (pf.t0 + rt) * H + h;
-      pf.sb = bf2f(beta[ri]);
-      pf.sq = sv.rq[ri];
-      pf.sk = sv.rk[ri];
-    }
-    pf.gl = G[((pf.t0 + pf.n - 1) * H + h) * HD + cB];
-  };
-  auto prefetch_t = [&](int cn) {
-    const int64_t tt = ct.tok[cn];
-    const int nn = ct.len[cn];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = rB + j, rc = r < nn ? r : nn - 1;
-      const int64_t idx = ((tt + rc) * H + h) * HD + cB;
-      pf.qt[j >> 3][j & 7] = q[idx];
-      pf.kt[j >> 3][j & 7] = k[idx];
-      pf.gt[j] = G[idx];
+      const int rr = rD + j, rc = rr < pn ? rr : pn - 1;
+      pdo[j] = dO[((pt0 + rc) * H + h) * HD + j0 + jD];
     }
   };
 
@@ -497,106 +490,55 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     (&sm.ds_hi[0][0])[e] = f2bf(0.f);
     (&sm.ds_lo[0][0])[e] = f2bf(0.f);
   }
-  if (c0 < c1) {
-    prefetch_main(c1 - 1);
-    prefetch_t(c1 - 1);
-  }
+  if (c0 < c1) prefetch(c1 - 1);
 
   for (int ci = c1 - 1; ci >= c0; --ci) {
-    const int64_t t0 = pf.t0;
-    const int n = pf.n;
+    const int64_t t0 = pt0;
+    const int n = pn;
     const int64_t ch = (int64_t)ci * H + h;
-    // ---- A. operands
-    if (t < CL) {
-      const bool ok = t < n;
-      sm.beta[t] = ok ? pf.sb : 0.f;
-      sm.rq[t] = ok ? pf.sq : 0.f;
-      sm.rk[t] = ok ? pf.sk : 0.f;
-    }
-    if (t < HD) {
-      sm.GL[t] = pf.gl;
-      sm.gam[t] = fexp(pf.gl);
-    }
-    __syncthreads();
-    {
-      const bool ok = rA < n;
-      const float rk = sm.rk[rA];
-      float ke[16];
+    // ---- A. operands of this chunk (scale Qd^T waits in registers)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bf16 kb = j < 8 ? pf.k0[j] : pf.k1[j - 8];
-        ke[j] = ok ? bf2f(kb) * rk * fexp(sm.GL[cA + j] - pf.g[j >> 2][j & 3]) : 0.f;
-      }
-      put8(KE, rA, cA, ke);
-      put8(KE, rA, cA + 8, ke + 8);
-      float aq[8], tb[8];
+    for (int k = 0; k < BP_PER_THREAD; ++k)
+      if ((k < 8 || k >= 12) && (k < BP_PER_THREAD - 1 || t < BP_UNITS - NT_SCAN * (BP_PER_THREAD - 1)))
+        bstage_unit(sm, k, t, pu[k]);
+    bf16x8 qdt[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        aq[j] = pf.at[j] * d.scale;
-        tb[j] = pf.tt[j] * sm.beta[iC];
-      }
-      put8(AQ, iC, rC, aq);
-      put8(TB, iC, rC, tb);
+    for (int k = 0; k < 4; ++k) qdt[k] = pu[8 + k];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sm.do_hi[jD][rD + j] = (rD + j < n) ? pf.dov[j] : f2bf(0.f);
-    }
-    if (ci - 1 >= c0) prefetch_main(ci - 1);
+    for (int j = 0; j < 4; ++j) sm.do_hi[jD][rD + j] = (rD + j < n) ? pdo[j] : f2bf(0.f);
+    if (ci - 1 >= c0) prefetch(ci - 1);
     __syncthreads();
     // ---- B. dU~ = scale A_qk^T dO + Ke dS_out   (tile rows 16 rb, cols 16 nw)
     f32x4 dU = zero4();
     mma<SPLIT_A>(dU, AQ, 16 * rb, DO, 16 * nw, (16 * rb / 32) * 32, CL);
     mma_k<SPLIT_BW, HD>(dU, KE, 16 * rb, DS, 16 * nw);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rb + drow(i);
-      if (r < n) bw.dU[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = dU[i];
-    }
+    *reinterpret_cast<f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)) = dU;
     store_tile_t(dU, DU, 16 * rb, 16 * nw);
     __syncthreads();
-    // ---- C. dR = Tb^T dU~ (= dv); Qd^T and -Kd^T panels
+    // ---- C. dR = Tb^T dU~ (= dv); scale Qd^T into the Ke space
     {
       f32x4 acc = zero4();
       mma<SPLIT_BW>(acc, TB, 16 * rb, DU, 16 * nw, (16 * rb / 32) * 32, CL);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + drow(i);
-        if (r < n) {
-          const int64_t idx = ((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol();
-          dv[idx] = f2bf(acc[i]);
-          bw.dR[idx] = acc[i];
-        }
+        if (r < n) dv[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = f2bf(acc[i]);
       }
+      *reinterpret_cast<f32x4*>(bw.dR + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)) = acc;
       store_tile_t(acc, DR, 16 * rb, 16 * nw);
     }
-    {
-      float qd[16], kd[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = rB + j;
-        const bool ok = r < n;
-        const float e1 = fexp(pf.gt[j]);
-        qd[j] = ok ? bf2f(pf.qt[j >> 3][j & 7]) * sm.rq[r] * e1 * d.scale : 0.f;
-        kd[j] = ok ? -bf2f(pf.kt[j >> 3][j & 7]) * sm.rk[r] * e1 : 0.f;
-      }
-      put8(QD, cB, rB, qd);
-      put8(QD, cB, rB + 8, qd + 8);
-      put8(KD, cB, rB, kd);
-      put8(KD, cB, rB + 8, kd + 8);
-    }
-    if (ci - 1 >= c0) prefetch_t(ci - 1);
+    for (int k = 0; k < 4; ++k) bstage_unit(sm, 8 + k, t, qdt[k]);
     __syncthreads();
     // ---- D. dS_in = Diag(e^G_last) dS_out + scale Qd^T dO - Kd^T dR
     {
       float* dSg = bw.dS + ch * HD * HD;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt) {
+        *reinterpret_cast<f32x4*>(dSg + tile_off(w, (j0 >> 4) + nt)) = dS[nt];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * w + drow(i);
-          dSg[c * HD + j0 + 16 * nt + dcol()] = dS[nt][i];
-          dS[nt][i] *= sm.gam[c];
-        }
+        for (int i = 0; i < 4; ++i) dS[nt][i] *= sm.gam[16 * w + drow(i)];
+      }
       mma_row<SPLIT_A, 2>(dS, QD, 16 * w, DO, 0, 0, CL);
       mma_row<SPLIT_BW, 2>(dS, KD, 16 * w, DR, 0, 0, CL);
     }
@@ -609,9 +551,9 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const float* G, const SavedSet& sv, const void* dO, void* dv,
                            const BwdWork& bw, hipStream_t s) {
+  (void)G;
   hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(NT_SCAN), 0, s, d, in,
-                     ct, G, sv, reinterpret_cast<const bf16*>(dO), reinterpret_cast<bf16*>(dv),
-                     bw);
+                     ct, sv, reinterpret_cast<const bf16*>(dO), reinterpret_cast<bf16*>(dv), bw);
   return hipGetLastError();
 }
 
