@@ -66,7 +66,6 @@ kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states, float** G)
   kda::SavedSet sv{};
   const size_t mat = (size_t)s.NC * s.H * 64 * 64;
   sv.Tm = c.take<float>(mat);
-  sv.Aqk = c.take<float>(mat);
   sv.Akk = c.take<float>(mat);
   sv.rq = c.take<float>((size_t)s.T * s.H);
   sv.rk = c.take<float>((size_t)s.T * s.H);

@@ -30,7 +30,6 @@ struct ChunkTable {
 struct SavedSet {
   float* S_in;   // [NC, H, 128 x 128] state before each chunk (tile order)
   float* Tm;     // [NC, H, 64, 64]  (I + Diag(beta) A_kk)^-1, zero above the diagonal
-  float* Aqk;    // [NC, H, 64, 64]  decayed q.k products, zero above the diagonal
   float* Akk;    // [NC, H, 64, 64]  decayed k.k products, zero on and above the diagonal
   float* R;      // [NC, H, 64 x 128] V - (K*e^G) S_in (tile order)
   float* U;      // [NC, H, 64 x 128] U~ = Tb R (tile order)

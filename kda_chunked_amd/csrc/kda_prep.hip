@@ -393,7 +393,6 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   // ---- 5. saved matrices (fp32) and the forward scan's operand panels
   float* Tg = sv.Tm + ch * CL * CL;
   float* Akk_g = sv.Akk + ch * CL * CL;
-  float* Aqk_g = sv.Aqk + ch * CL * CL;
   bf16* P = panels ? panels + ch * (int64_t)fwd_panel::ELEMS : nullptr;
   {
     const int r = t >> 3, i8 = 8 * (t & 7);
@@ -408,8 +407,6 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     *reinterpret_cast<f32x4*>(Tg + r * CL + i8 + 4) = f32x4{tv[4], tv[5], tv[6], tv[7]};
     *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8) = f32x4{kv[0], kv[1], kv[2], kv[3]};
     *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8 + 4) = f32x4{kv[4], kv[5], kv[6], kv[7]};
-    *reinterpret_cast<f32x4*>(Aqk_g + r * CL + i8) = f32x4{qv[0], qv[1], qv[2], qv[3]};
-    *reinterpret_cast<f32x4*>(Aqk_g + r * CL + i8 + 4) = f32x4{qv[4], qv[5], qv[6], qv[7]};
     if (P) {
       bf16x8 tb, ah, al;
 #pragma unroll
