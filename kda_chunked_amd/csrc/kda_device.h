@@ -229,6 +229,49 @@ KDA_DEV int tile_off(int rb, int cb) { return (rb * 8 + cb) * 256 + 4 * lane_id(
 KDA_DEV int drow(int i) { return 4 * (lane_id() >> 4) + i; }
 KDA_DEV int dcol() { return lane_id() & 15; }
 
+// Cross-lane exchange inside a 16-lane row by DPP (no LDS traffic): lane j
+// receives the value of lane j ^ M for M = 1 (quad swap), 3 (quad reverse),
+// 7 (half-row mirror) and 15 (row mirror).
+template <int M>
+KDA_DEV float row_xor(float v) {
+  static_assert(M == 1 || M == 3 || M == 7 || M == 15, "row_xor mask");
+  constexpr int ctrl = M == 1 ? 0xB1 : M == 3 ? 0x1B : M == 7 ? 0x141 : 0x140;
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a row (every lane gets the total).
+KDA_DEV float row_sum16(float v) {
+  v += row_xor<1>(v);
+  v += row_xor<3>(v);
+  v += row_xor<7>(v);
+  return v + row_xor<15>(v);
+}
+
+template <int M, int HALF>
+KDA_DEV void row_transpose_level(float* x, bool up) {
+#pragma unroll
+  for (int k = 0; k < HALF; ++k) {
+    // opaque copies: a select between two array elements would otherwise be
+    // folded into a dynamically indexed read of the whole array
+    float lo = x[k], hi = x[HALF + k];
+    asm("" : "+v"(lo), "+v"(hi));
+    x[k] = (up ? hi : lo) + row_xor<M>(up ? lo : hi);
+  }
+}
+
+// Transposing sum over a 16-lane row: each lane enters with 16 partial values
+// x[0..15]; lane j (j = lane & 15) returns the row total of value j. Each
+// level pairs lanes that differ in one more bit of j and halves the values a
+// lane keeps (15 exchanges in all).
+KDA_DEV float row_transpose_sum16(float* x, int j) {
+  row_transpose_level<15, 8>(x, j & 8);
+  row_transpose_level<7, 4>(x, j & 4);
+  row_transpose_level<3, 2>(x, j & 2);
+  row_transpose_level<1, 1>(x, j & 1);
+  return x[0];
+}
+
 // softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^-|x|), on the hardware
 // base-2 exponential and logarithm.
 KDA_DEV float softplus(float x) {

@@ -8,13 +8,17 @@
 //   A_qk[r,i] = sum_c q_r[c] k_i[c] e^(G_r[c] - G_i[c])   (i <= r)
 //   T = (I + Diag(beta) A_kk)^-1                          (UT/WY solve)
 //
-// Fast-decay safety. e^(G_r - G_i) is formed from two factors that never
-// overflow. A tile of rows in block I and columns in block J < I uses the
-// reference rho = G at the end of block J: x_r e^(G_r - rho) <= 1 and
-// k_i e^(rho - G_i) <= 1. A diagonal tile uses rho = G before the block, so the
-// second factor is at most e^(span of the block); it is used only when that
-// span is at most CALM_SPAN in every channel, otherwise the tile is summed
-// element by element in fp32 with the exact factor.
+// Fast-decay safety (g <= 0, so G falls along the chunk). e^(G_r - G_i) is
+// formed from two factors that never overflow. A tile of rows in block I and
+// columns in block J < I uses the reference rho = G at the end of block J:
+// x_r e^(G_r - rho) <= 1 and k_i e^(rho - G_i) <= 1. A diagonal tile whose
+// decay span (G before the block minus G at its last row) is at most SPAN_MAX
+// in every channel uses the midpoint of that range as rho, so both factors lie
+// within e^(+-SPAN_MAX/2) and their bf16 lo planes stay normal. A wider
+// diagonal tile is summed in fp32 without exponentials of differences: down
+// column i the factor e^(G_r - G_i) is the running product of the per-step
+// decays e^(g_r), r = i+1 .. 15, which never exceeds 1 and underflows
+// gracefully.
 //
 // Besides the saved fp32 matrices, the kernel writes the forward scan's
 // operand panels (-Kd, scale Qd, Ke^T, Tb, scale A_qk as bf16 hi/lo planes and
@@ -24,7 +28,7 @@
 
 namespace kda {
 
-constexpr float CALM_SPAN = 40.f;
+constexpr float SPAN_MAX = 120.f;
 
 #ifndef KDA_SPLIT_P1
 #define KDA_SPLIT_P1 SPLIT_AB    // A_kk = X_k Y^T, A_qk = X_q Y^T
@@ -91,31 +95,39 @@ struct PrepSmem {
   float Tm[CL][F_LD];
   float Z[3][16][17];
   float Gref[5][HD];       // G before block I (I = 0..3) and G_last (I = 4)
-  float qtot[4][HD];
-  float nrm[2][8][CL];
+  union {
+    struct {
+      float qtot[4][HD];   // cumsum carries of the row quarters
+      float nrm[2][8][CL]; // L2 partial sums
+    } s;
+    float E[CL][HD];       // e^(g) per row and channel, once the above are dead
+  } u;
   float rq[CL], rk[CL], beta[CL];
-  int calm_blk[4];
+  int wide[4];             // diagonal block I has a span > SPAN_MAX
 };
 
-// Tile (I, J), J <= I, of the lower triangle of 16 x 16 blocks.
-KDA_DEV void tile_of(int item, int& I, int& J) {
-  I = item < 1 ? 0 : item < 3 ? 1 : item < 6 ? 2 : 3;
-  J = item - I * (I + 1) / 2;
+// Off-diagonal tile (I, J), J < I, of the lower triangle of 16 x 16 blocks.
+KDA_DEV void offdiag_tile(int item, int& I, int& J) {
+  I = item < 1 ? 1 : item < 3 ? 2 : 3;
+  J = item - I * (I - 1) / 2;
 }
 
-// One 8-channel MFMA fragment of x e^(+-(G - ref)) for row `row`, channels
-// c .. c+7, split into hi and lo planes. sgn = +1: x e^(G - ref); -1: x e^(ref - G).
+// One 8-channel MFMA fragment of x e^(+-(G - rho)) for row `row`, channels
+// c .. c+7, split into hi and lo planes, with rho = (ra + rb) / 2 (exactly ra
+// when ra == rb). sgn = +1: x e^(G - rho); -1: x e^(rho - G).
 KDA_DEV void decayed_frag(const PrepSmem& sm, const bf16 (*x)[XS_LD], float rx, int row, int c,
-                          const float* ref, float sgn, bf16x8& hi, bf16x8& lo) {
+                          const float* ra, const float* rb, float sgn, bf16x8& hi, bf16x8& lo) {
   const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.G[row][c]);
   const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.G[row][c + 4]);
-  const f32x4 r0 = *reinterpret_cast<const f32x4*>(ref + c);
-  const f32x4 r1 = *reinterpret_cast<const f32x4*>(ref + c + 4);
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(ra + c);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(ra + c + 4);
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(rb + c);
+  const f32x4 b1 = *reinterpret_cast<const f32x4*>(rb + c + 4);
   const bf16x8 xv = *reinterpret_cast<const bf16x8*>(&x[row][c]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float gj = j < 4 ? g0[j] : g1[j - 4];
-    const float rj = j < 4 ? r0[j] : r1[j - 4];
+    const float rj = 0.5f * ((j < 4 ? a0[j] : a1[j - 4]) + (j < 4 ? b0[j] : b1[j - 4]));
     const float v = bf2f(xv[j]) * rx * fexp(sgn * (gj - rj));
     hi[j] = f2bf(v);
     lo[j] = f2bf(v - bf2f(hi[j]));
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
   const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
   const int cG = t & 127, qG = t >> 7;
-  float g[16];
+  float g[16], eg[16];
   if (!d.raw) {
     const float* gp = reinterpret_cast<const float*>(in.gate);
 #pragma unroll
@@ -178,8 +190,8 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       sq += a * a;
       sk += b * b;
     }
-    sm.nrm[0][t & 7][rA] = sq;
-    sm.nrm[1][t & 7][rA] = sk;
+    sm.u.s.nrm[0][t & 7][rA] = sq;
+    sm.u.s.nrm[1][t & 7][rA] = sk;
   }
   // ---- 2. chunk-local cumsum of g in registers (16 rows per thread), then
   // the carry of the earlier row quarters
@@ -191,16 +203,18 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     for (int j = 0; j < 16; ++j) {
       float x = g[j];
       if (d.raw) x = -ea * softplus(x + dtb);
-      run += (16 * qG + j < n) ? x : 0.f;
+      x = (16 * qG + j < n) ? x : 0.f;
+      run += x;
       g[j] = run;
+      eg[j] = fexp(x);
     }
-    sm.qtot[qG][cG] = run;
+    sm.u.s.qtot[qG][cG] = run;
   }
-  if (t < 4) sm.calm_blk[t] = 1;
+  if (t < 4) sm.wide[t] = 0;
   __syncthreads();
   {
     float carry = 0.f;
-    for (int j = 0; j < qG; ++j) carry += sm.qtot[j][cG];
+    for (int j = 0; j < qG; ++j) carry += sm.u.s.qtot[j][cG];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = 16 * qG + j;
@@ -212,8 +226,8 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       float a = 0.f, b = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        a += sm.nrm[0][j][t];
-        b += sm.nrm[1][j][t];
+        a += sm.u.s.nrm[0][j][t];
+        b += sm.u.s.nrm[1][j][t];
       }
       const float rq = d.l2norm ? 1.f / sqrtf(a + d.l2_eps) : 1.f;
       const float rk = d.l2norm ? 1.f / sqrtf(b + d.l2_eps) : 1.f;
@@ -226,17 +240,18 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     }
   }
   __syncthreads();
-  // references: G before each 16-row block and G_last; a block is calm when
-  // its own decay span is <= CALM_SPAN in every channel
+  // references: G before each 16-row block and G_last; the decay span of each
+  // diagonal block; the per-step decays (qtot and nrm are dead now)
   if (t < HD) {
     sm.Gref[0][t] = 0.f;
 #pragma unroll
     for (int I = 1; I <= 4; ++I) sm.Gref[I][t] = sm.G[16 * I - 1][t];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
-      if ((I == 0 ? 0.f : sm.G[16 * I - 1][t]) - sm.G[16 * I + 15][t] > CALM_SPAN)
-        sm.calm_blk[I] = 0;
+      if ((I == 0 ? 0.f : sm.G[16 * I - 1][t]) - sm.G[16 * I + 15][t] > SPAN_MAX) sm.wide[I] = 1;
   }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sm.u.E[16 * qG + j][cG] = eg[j];
   // zero the strictly-upper 16 x 16 tiles of A_kk and A_qk
   for (int e = t; e < 6 * 256; e += NT_PREP) {
     const int tile = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
@@ -251,98 +266,133 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   for (int j = 0; j < 16; ++j) Gv[j] = sm.G[rA][cA + j];
   __syncthreads();
 
-  // ---- 3. decayed products, tile (I, J) of A_kk and A_qk per wave item.
-  // Off-diagonal tiles (J < I) use rho = G at the end of block J: both
-  // x_r e^(G_r - rho) and k_i e^(rho - G_i) are <= 1. A calm diagonal tile
-  // uses rho = G before the block (the second factor is <= e^CALM_SPAN).
-  for (int item = w; item < 10; item += 8) {
-    int I, J;
-    tile_of(item, I, J);
-    const bool diag = I == J;
-    if (diag && !sm.calm_blk[I]) continue;
-    const float* ref = diag ? sm.Gref[I] : sm.Gref[J + 1];
-    const int ra = 16 * I + (l & 15), rbw = 16 * J + (l & 15);
-    const float rqa = sm.rq[ra], rka = sm.rk[ra], rkb = sm.rk[rbw];
-    f32x4 akk = zero4(), aqk = zero4();
+  // ---- 3. decayed products of A_kk and A_qk, as work items spread over the
+  // 8 waves: each off-diagonal tile and each calm diagonal tile is one MFMA
+  // product of bf16 hi/lo operands; each wide diagonal tile is two
+  // running-product units (unit u: columns p and 15 - p, p = 4u .. 4u + 3).
+  int wide[4], n_wide = 0;
 #pragma unroll
-    for (int ks = 0; ks < HD / 32; ++ks) {
-      const int c = 32 * ks + 8 * (l >> 4);
-      bf16x8 xk_h, xk_l, xq_h, xq_l, y_h, y_l;
-      decayed_frag(sm, sm.ks, rka, ra, c, ref, 1.f, xk_h, xk_l);
-      decayed_frag(sm, sm.qs, rqa, ra, c, ref, 1.f, xq_h, xq_l);
-      decayed_frag(sm, sm.ks, rkb, rbw, c, ref, -1.f, y_h, y_l);
-      if (KDA_SPLIT_P1 & SPLIT_A) {
-        akk = mfma16(xk_l, y_h, akk);
-        aqk = mfma16(xq_l, y_h, aqk);
-      }
-      if (KDA_SPLIT_P1 & SPLIT_B) {
-        akk = mfma16(xk_h, y_l, akk);
-        aqk = mfma16(xq_h, y_l, aqk);
-      }
-      akk = mfma16(xk_h, y_h, akk);
-      aqk = mfma16(xq_h, y_h, aqk);
-    }
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int r = 16 * I + drow(i4), i = 16 * J + dcol();
-      sm.Akk[r][i] = (i < r) ? akk[i4] : 0.f;
-      sm.Aqk[r][i] = (i <= r) ? aqk[i4] : 0.f;
-    }
+  for (int I = 0; I < 4; ++I) {
+    wide[I] = __builtin_amdgcn_readfirstlane(sm.wide[I]);
+    n_wide += wide[I];
   }
-  // Diagonal blocks whose span is too wide: every pair (r, i <= r) of the
-  // block with its exact factor e^(G_r - G_i) <= 1, in fp32. Wave p takes the
-  // 17 pairs of rows p and 15 - p; lane (I, cg) block I, channels 8 cg .. + 7;
-  // the 16 channel groups are summed across lanes.
-  if (!(sm.calm_blk[0] & sm.calm_blk[1] & sm.calm_blk[2] & sm.calm_blk[3])) {
-    const int p = w, I = (l >> 4) & 3, cg = l & 15, c = 8 * cg;
-    const bool on = !sm.calm_blk[I];
-    float ga[8], gb[8];
-    {
-      const int ra = 16 * I + p, rz = 16 * I + 15 - p;
+  for (int item = w; item < 10 + n_wide; item += 8) {
+    int I = 3, J, unit = -1;
+    if (item < 6) {
+      offdiag_tile(item, I, J);
+    } else {
+      int rem = item - 6;
+      bool found = false;
 #pragma unroll
-      for (int j = 0; j < 8; j += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.G[ra][c + j]);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.G[rz][c + j]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ga[j + u] = x[u];
-          gb[j + u] = y[u];
+      for (int b = 0; b < 4; ++b) {
+        const int cnt = 1 + wide[b];
+        if (!found && rem < cnt) {
+          I = b;
+          unit = wide[b] ? rem : -1;
+          found = true;
+        } else if (!found) {
+          rem -= cnt;
         }
       }
+      J = I;
     }
-    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.ks[16 * I + p][c]);
-    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.qs[16 * I + p][c]);
-    const bf16x8 kz = *reinterpret_cast<const bf16x8*>(&sm.ks[16 * I + 15 - p][c]);
-    const bf16x8 qz = *reinterpret_cast<const bf16x8*>(&sm.qs[16 * I + 15 - p][c]);
+    if (unit < 0) {
+      // rho: G at the end of block J (off-diagonal), else the midpoint of G
+      // before block I and G at its last row
+      const bool diag = I == J;
+      const float* refa = diag ? sm.Gref[I] : sm.Gref[J + 1];
+      const float* refb = sm.Gref[J + 1];
+      const int ra = 16 * I + (l & 15), rbw = 16 * J + (l & 15);
+      const float rqa = sm.rq[ra], rka = sm.rk[ra], rkb = sm.rk[rbw];
+      f32x4 akk = zero4(), aqk = zero4();
 #pragma unroll
-    for (int e = 0; e < 17; ++e) {
-      const bool first = e <= p;                // wave-uniform
-      const int rl = first ? p : 15 - p;
-      const int il = first ? e : e - p - 1;
-      const int r = 16 * I + rl, i = 16 * I + il;
-      const f32x4 gi0 = *reinterpret_cast<const f32x4*>(&sm.G[i][c]);
-      const f32x4 gi1 = *reinterpret_cast<const f32x4*>(&sm.G[i][c + 4]);
-      const bf16x8 ki = *reinterpret_cast<const bf16x8*>(&sm.ks[i][c]);
-      float skk = 0.f, sqk = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float gi = j < 4 ? gi0[j] : gi1[j - 4];
-        const float e1 = fexp((first ? ga[j] : gb[j]) - gi) * bf2f(ki[j]);
-        skk += bf2f(first ? ka[j] : kz[j]) * e1;
-        sqk += bf2f(first ? qa[j] : qz[j]) * e1;
-      }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        skk += __shfl_xor(skk, m);
-        sqk += __shfl_xor(sqk, m);
-      }
-      if (on && cg == 0) {
-        sm.Akk[r][i] = il < rl ? skk * sm.rk[r] * sm.rk[i] : 0.f;
-        sm.Aqk[r][i] = sqk * sm.rq[r] * sm.rk[i];
-        if (il < rl) {                 // the mirrored entry above the diagonal
-          sm.Akk[i][r] = 0.f;
-          sm.Aqk[i][r] = 0.f;
+      for (int ks = 0; ks < HD / 32; ++ks) {
+        const int c = 32 * ks + 8 * (l >> 4);
+        bf16x8 xk_h, xk_l, xq_h, xq_l, y_h, y_l;
+        decayed_frag(sm, sm.ks, rka, ra, c, refa, refb, 1.f, xk_h, xk_l);
+        decayed_frag(sm, sm.qs, rqa, ra, c, refa, refb, 1.f, xq_h, xq_l);
+        decayed_frag(sm, sm.ks, rkb, rbw, c, refa, refb, -1.f, y_h, y_l);
+        if (KDA_SPLIT_P1 & SPLIT_A) {
+          akk = mfma16(xk_l, y_h, akk);
+          aqk = mfma16(xq_l, y_h, aqk);
         }
+        if (KDA_SPLIT_P1 & SPLIT_B) {
+          akk = mfma16(xk_h, y_l, akk);
+          aqk = mfma16(xq_h, y_l, aqk);
+        }
+        akk = mfma16(xk_h, y_h, akk);
+        aqk = mfma16(xq_h, y_h, aqk);
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r = 16 * I + drow(i4), i = 16 * J + dcol();
+        sm.Akk[r][i] = (i < r) ? akk[i4] : 0.f;
+        sm.Aqk[r][i] = (i <= r) ? aqk[i4] : 0.f;
+      }
+    } else {
+      // Lane (lg, cg): column pair p = 4 unit + lg, channels 8 cg .. + 7.
+      // Step st walks column p for rows p .. 15 (st = 0 .. 15 - p), then
+      // column 15 - p for rows 15 - p .. 15: 17 (r, i) pairs per lane group.
+      const int lg = l >> 4, cg = l & 15, c = 8 * cg, b0 = 16 * I;
+      const int p = 4 * unit + lg;
+      auto pair_of = [&](int st, int& r, int& i) {
+        const bool second = st > 15 - p;
+        i = second ? 15 - p : p;
+        r = second ? st - 1 : p + st;
+      };
+      float f[8];    // k_i rk_i e^(G_r - G_i), channels c .. c+7
+      auto step = [&](int st, float& skk, float& sqk) {
+        int r, i;
+        pair_of(st, r, i);
+        if (st == 0 || st == 16 - p) {
+          const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + i][c]);
+          const float rki = sm.rk[b0 + i];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = bf2f(kv[j]) * rki;
+        } else {
+          const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c]);
+          const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + 4]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] *= j < 4 ? e0[j] : e1[j - 4];
+        }
+        const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + r][c]);
+        const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&sm.qs[b0 + r][c]);
+        skk = sqk = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          skk += bf2f(kr[j]) * f[j];
+          sqk += bf2f(qr[j]) * f[j];
+        }
+      };
+      // the sums of step st (kind 0: A_kk, 1: A_qk), mirrored zero above the diagonal
+      auto store = [&](int st, int kind, float v) {
+        int r, i;
+        pair_of(st, r, i);
+        if (kind == 0) {
+          sm.Akk[b0 + r][b0 + i] = r > i ? v * sm.rk[b0 + r] : 0.f;
+          if (r > i) sm.Akk[b0 + i][b0 + r] = 0.f;
+        } else {
+          sm.Aqk[b0 + r][b0 + i] = v * sm.rq[b0 + r];
+          if (r > i) sm.Aqk[b0 + i][b0 + r] = 0.f;
+        }
+      };
+      // steps 0..15 in two groups of 8: the 16 sums of a group are reduced
+      // over the 16 channel-group lanes (one DPP row), after which lane cg
+      // holds the total of value cg (step cg / 2, kind cg % 2)
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq) {
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) step(8 * gq + e, x[2 * e], x[2 * e + 1]);
+        store(8 * gq + (cg >> 1), cg & 1, row_transpose_sum16(x, cg));
+      }
+      float skk, sqk;
+      step(16, skk, sqk);
+      skk = row_sum16(skk);
+      sqk = row_sum16(sqk);
+      if (cg == 0) {
+        store(16, 0, skk);
+        store(16, 1, sqk);
       }
     }
   }
