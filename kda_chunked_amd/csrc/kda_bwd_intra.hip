@@ -298,9 +298,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         store_tile_n(v[jb], SP, 16 * w, 16 * jb);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) part[i] += __shfl_xor(part[i], m);
+      for (int i = 0; i < 4; ++i) part[i] = row_sum16(part[i]);
       if (dcol() == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.dgam[16 * w + drow(i)] = part[i];
@@ -426,9 +424,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         dAq[nt][i] = c <= r ? d.scale * dAq[nt][i] : 0.f;
       }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) rp[i] += __shfl_xor(rp[i], m);
+    for (int i = 0; i < 4; ++i) rp[i] = row_sum16(rp[i]);
     if (dcol() == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.dbr[chh][16 * rb + drow(i)] = rp[i];
@@ -498,29 +494,41 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           adk[nt][i] += dka;
           adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
         }
-    } else {
-      // block J of the columns: sum over i in J on MFMA, then the factor
-      // e^(G_r - rho_end(J)) <= 1 (J < rb); the diagonal block only when calm
+    } else if (rb > 0 || blk_calm) {
+      // Column blocks J = 0 .. jend (the diagonal block only when calm): the
+      // product over block J carries e^(rho_end(J) - G_i); a Horner sweep
+      // rescales the running sum by e^(rho_end(J) - rho_end(J-1)) <= 1 before
+      // adding block J, so that one factor e^(G_r - rho_end(jend)) finishes it.
       const int jend = blk_calm ? rb : rb - 1;
+      f32x4 aq[4], ak[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) aq[nt] = ak[nt] = zero4();
       for (int J = 0; J <= jend; ++J) {
-        f32x4 aq[4], ak[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          aq[nt] = ak[nt] = zero4();
+          if (J > 0) {
+            const int c = 64 * chh + 16 * nt + dcol();
+            const float dj = fexp(sm.Gref[J + 1][c] - sm.Gref[J][c]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              aq[nt][i] *= dj;
+              ak[nt][i] *= dj;
+            }
+          }
           mma_k16<KDA_SPLIT_B7>(aq[nt], DQ, 16 * rb, YT, 64 * chh + 16 * nt, 16 * J);
           mma_k16<KDA_SPLIT_B7>(ak[nt], DK, 16 * rb, YT, 64 * chh + 16 * nt, 16 * J);
         }
+      }
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float ref = sm.Gref[J + 1][64 * chh + 16 * nt + dcol()];
+      for (int nt = 0; nt < 4; ++nt) {
+        const float ref = sm.Gref[jend + 1][64 * chh + 16 * nt + dcol()];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e1 = fexp(eG[nt][i] - ref);
-            const float dqa = aq[nt][i] * e1, dka = ak[nt][i] * e1;
-            adq[nt][i] += dqa;
-            adk[nt][i] += dka;
-            adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const float e1 = fexp(eG[nt][i] - ref);
+          const float dqa = aq[nt][i] * e1, dka = ak[nt][i] * e1;
+          adq[nt][i] += dqa;
+          adk[nt][i] += dka;
+          adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
         }
       }
     }
@@ -555,29 +563,43 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           adk[nt][i] += dka;
           adG[nt][i] -= dka * EK(nt, i);
         }
-    } else {
-      // block I of the rows r: factor e^(rho_start(I) - G_i) <= 1 (I > rb)
-      for (int I = blk_calm ? rb : rb + 1; I < 4; ++I) {
-        f32x4 ac[4];
+    } else if (rb < 3 || blk_calm) {
+      // Row blocks I = 3 down to istart (the diagonal block only when calm):
+      // the product over block I carries e^(G_r - rho_start(I)); the Horner
+      // sweep rescales by e^(rho_start(I+1) - rho_start(I)) <= 1 before adding
+      // block I, and e^(rho_start(istart) - G_i) finishes it.
+      const int istart = blk_calm ? rb : rb + 1;
+      f32x4 ac[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
-        mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 32 * I, 32 * I + 32);
+      for (int nt = 0; nt < 4; ++nt) ac[nt] = zero4();
+      for (int I = 3; I >= istart; --I) {
+        if (I < 3) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float ref = sm.Gref[I][64 * chh + 16 * nt + dcol()];
+          for (int nt = 0; nt < 4; ++nt) {
+            const int c = 64 * chh + 16 * nt + dcol();
+            const float di = fexp(sm.Gref[I + 1][c] - sm.Gref[I][c]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float dka = ac[nt][i] * fexp(ref - eG[nt][i]);
-            adk[nt][i] += dka;
-            adG[nt][i] -= dka * EK(nt, i);
+            for (int i = 0; i < 4; ++i) ac[nt][i] *= di;
           }
+        }
+        mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 32 * I, 32 * I + 32);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float ref = sm.Gref[istart][64 * chh + 16 * nt + dcol()];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float dka = ac[nt][i] * fexp(ref - eG[nt][i]);
+          adk[nt][i] += dka;
+          adG[nt][i] -= dka * EK(nt, i);
         }
       }
     }
     __syncthreads();
     if (!calm && !(sm.calm_blk[0] & sm.calm_blk[1] & sm.calm_blk[2] & sm.calm_blk[3])) {
       // Diagonal blocks too wide for one reference: every pair (r, i) of the
-      // block is summed with its exact factor e^(G_r - G_i) <= 1 in fp32.
+      // block is summed with its exact factor e^(G_r - G_i) <= 1 in fp32, the
+      // running product of the per-step decays e^(G_m - G_(m-1)), m = i+1 .. r.
       // Column layout: thread (I, c) holds rows 16 I .. 16 I + 15 of channel c.
       float (*Xg)[GS_LD] = sm.u.p6.x.g;
       float (*Xq)[GS_LD] = sm.u.p6.x.q;
@@ -604,11 +626,18 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           kv[j] = Xk[16 * I + j][c];
           sq[j] = sk[j] = sg[j] = 0.f;
         }
+        float P[16];    // P[i] = e^(G_r - G_i) for the current row r
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 16; ++r) {
+          if (r > 0) {
+            const float er = fexp(g[r] - g[r - 1]);
+#pragma unroll
+            for (int i = 0; i < r; ++i) P[i] *= er;
+          }
+          P[r] = 1.f;
 #pragma unroll
           for (int i = 0; i <= r; ++i) {
-            const float E = fexp(g[r] - g[i]);
+            const float E = P[i];
             const float a = sm.dqN[I][r][i], b = sm.dkN[I][r][i];
             const float ke = kv[i] * E;
             const float wgt = a * qv[r] + b * kv[r];
@@ -619,6 +648,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
             sk[i] += s2;
             sg[i] -= s2 * kv[i];
           }
+        }
         // each thread overwrites only the entries it read
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -664,12 +694,10 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           pk[i] += EK(nt, i) * adk[nt][i];
         }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-          pq[i] += __shfl_xor(pq[i], m);
-          pk[i] += __shfl_xor(pk[i], m);
-        }
+      for (int i = 0; i < 4; ++i) {
+        pq[i] = row_sum16(pq[i]);
+        pk[i] = row_sum16(pk[i]);
+      }
       if (dcol() == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -728,12 +756,16 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       if (t < HD)
         bw.part_dt[ch * HD + t] = (sm.u.p7.red[0][0][t] + sm.u.p7.red[0][1][t]) +
                                   (sm.u.p7.red[0][2][t] + sm.u.p7.red[0][3][t]);
-      if (t == HD) {
+      if (w == 2) {                 // channels l and l + 64, then the 64 lanes
         float s = 0.f;
-        for (int c2 = 0; c2 < HD; ++c2)
+#pragma unroll
+        for (int c2 = l; c2 < HD; c2 += 64)
           s += (sm.u.p7.red[1][0][c2] + sm.u.p7.red[1][1][c2]) +
                (sm.u.p7.red[1][2][c2] + sm.u.p7.red[1][3][c2]);
-        bw.part_A[ch] = s;
+        s = row_sum16(s);
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (l == 0) bw.part_A[ch] = s;
       }
     }
     // dq, dk (L2 chain) and dbeta
