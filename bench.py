@@ -62,10 +62,59 @@ _TRI_S = 64 * 63 // 2 * 128        # strictly lower
 _SQ = 64 * 128 * 128               # 64 x 128 x 128
 MAC_PER_CHUNK_HEAD = {
     "fwd_prep": _TRI_S + _TRI + 64 ** 3 // 6,
-    "fwd_scan": 3 * _SQ + 2 * _TRI,
+    "fwd_scan": 2 * _SQ + _TRI,        # R = V - Kd S_in, U~ = Tb R, Ke^T U~
+    "fwd_out": _SQ + _TRI,             # Qd S_in, A_qk U~
     "bwd_scan": 3 * _SQ + 2 * _TRI,
     "bwd_intra": 3 * _SQ + 6 * _TRI + 2 * _TRI_S + 64 ** 3 // 2,
 }
+
+# Algorithmic bytes per full chunk and head, per kernel: every tensor the
+# kernel reads or writes in this design's data flow, counted once at its
+# stored precision (a panel read by several workgroups counts once). Gate
+# form g stores an fp32 g / dg; the raw form a bf16 a / da plus fp32 partials.
+_X = 64 * 128                      # elements of a 64 x 128 per-chunk tensor
+_FWD_PANEL_B = 107008              # forward operand panels (bf16 hi/lo planes)
+_FWD_CHAIN_B = 57856               # their chain part: -Kd, Tb, Ke^T hi/lo, e^(G_last)
+_BWD_PANEL_B = 131584              # reverse-scan operand panels
+
+
+def algo_bytes_per_chunk_head(kernel: str, raw: bool) -> int:
+    gate_in = 2 * _X if raw else 4 * _X            # a (bf16) or g (fp32)
+    gate_out = 2 * _X + 512 + 4 if raw else 4 * _X  # da + part_dt + part_A, or dg
+    return {
+        # q, k, gate, beta -> G, rq, rk, T, A_kk, both panel sets
+        "fwd_prep": 2 * 2 * _X + gate_in + 128 + 4 * _X + 512 + 2 * 4 * 64 * 64
+                    + _FWD_PANEL_B + _BWD_PANEL_B,
+        # chain panels, v -> S_in, R, U~ (fp32)
+        "fwd_scan": _FWD_CHAIN_B + 2 * _X + 4 * 128 * 128 + 2 * 4 * _X,
+        # S_in, U~, scale Qd, scale A_qk -> o
+        "fwd_out": 4 * 128 * 128 + 4 * _X + 2 * 2 * _X + 2 * 2 * 64 * 64 + 2 * _X,
+        # panels, dO -> dv, dU~, dR, dS (fp32)
+        "bwd_scan": _BWD_PANEL_B + 2 * _X + 2 * _X + 2 * 4 * _X + 4 * 128 * 128,
+        # q, k, G, dO, beta, rq, rk, S_in, dS, U~, R, dU~, dR, T, A_kk (+ a) -> dq, dk, dbeta, dgate
+        "bwd_intra": 2 * 2 * _X + 4 * _X + 2 * _X + 128 + 512 + 2 * 4 * 128 * 128 + 4 * 4 * _X
+                     + 2 * 4 * 64 * 64 + (2 * _X if raw else 0)
+                     + 2 * 2 * _X + 128 + gate_out,
+    }[kernel]
+
+
+def kernel_roofline(kernel: str, ms: float, chunk_heads: float, raw: bool) -> dict:
+    """The kernel's bound (whichever of its algorithmic FLOP at the bf16 MFMA
+    peak or its algorithmic bytes at the HBM peak takes longer) and the
+    fraction of that peak it reaches."""
+    flop = 2.0 * MAC_PER_CHUNK_HEAD[kernel] * chunk_heads
+    nbytes = float(algo_bytes_per_chunk_head(kernel, raw)) * chunk_heads
+    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        ach = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": nbytes,
+                "algorithmic_flop_per_launch": flop}
+    ach = flop / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_bytes_per_launch": nbytes, "algorithmic_flop_per_launch": flop}
 
 
 class HipEvents:
@@ -122,7 +171,7 @@ def fingerprint() -> str:
 
 
 def _short(kernel_name: str) -> str:
-    for k in ("chunk_map", "fwd_prep", "fwd_scan", "bwd_scan", "bwd_intra", "finalize"):
+    for k in ("chunk_map", "fwd_prep", "fwd_scan", "fwd_out", "bwd_scan", "bwd_intra", "finalize"):
         if k + "_kernel" in kernel_name:
             return k
     return "copy" if "copyBuffer" in kernel_name else kernel_name[:40]
@@ -354,16 +403,22 @@ def main():
         torch.cuda.synchronize()
 
     chunk_heads = w.T * w.H / 64.0    # chunk-head equivalents per launch
-    dom = max((k for k in kern_avg if k in MAC_PER_CHUNK_HEAD), key=lambda k: kern_avg[k])
-    flop = 2.0 * MAC_PER_CHUNK_HEAD[dom] * chunk_heads
-    achieved = flop / (kern_avg[dom] * 1e-3) / 1e12
+    raw = w.gate == "raw"
+    per_kernel = {k: kernel_roofline(k, kern_avg[k], chunk_heads, raw)
+                  for k in kern_avg if k in MAC_PER_CHUNK_HEAD}
+    dom = max(per_kernel, key=lambda k: kern_avg[k])
     fp = fingerprint()
     fig = profile_figures(w.name, dom, fp)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+    r = per_kernel[dom]
+    roofline = {"bound": r["bound"], "kernel": dom, "achieved": r["achieved"], "peak": r["peak"],
+                "unit": r["unit"], "frac": r["frac"],
                 "traffic": fig["traffic_bytes"] if fig else None,
-                "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(kern_avg[dom], 4)}
+                "algorithmic_bytes_per_launch": r["algorithmic_bytes_per_launch"],
+                "algorithmic_flop_per_launch": r["algorithmic_flop_per_launch"],
+                "avg_launch_ms": round(kern_avg[dom], 4)}
+    # the MFMA view of the same kernel (its algorithmic FLOP at the bf16 peak)
+    roofline["mfma_frac"] = round(r["algorithmic_flop_per_launch"] / (kern_avg[dom] * 1e-3)
+                                  / 1e12 / PEAK_BF16_TFLOPS, 4)
     if fig:
         roofline["mfma_busy_pct"] = fig.get("mfma_busy_pct")
         roofline["executed_mfma_tflops"] = round(
@@ -391,6 +446,8 @@ def main():
         "roofline": roofline,
         "token_heads_per_s": round(w.T * w.H / (ms_step * 1e-3), 1),
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kern_avg.items())},
+        "kernels_roofline": {k: {"bound": v["bound"], "frac": v["frac"]}
+                             for k, v in sorted(per_kernel.items())},
         "algorithmic_tflops": round(total_flop / (ms_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
         "source_fingerprint": fp,

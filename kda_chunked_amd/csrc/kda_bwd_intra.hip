@@ -281,28 +281,20 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
       U[nt] = *reinterpret_cast<const f32x4*>(sv.U + ch * CL * HD + tile_off(rb, 4 * chh + nt));
-    // dS_out replaces S_in in the panel; dgamma[c] = sum_j dS_out[c][j] S_in[c][j]
-    // in fp32 from both matrices in tile order (wave w: row block w, 8 tiles)
+    // dS_out replaces S_in in the panel (wave w: row block w, 8 tiles);
+    // dgamma[c] = sum_j dS_out[c][j] S_in[c][j], from the reverse scan's
+    // partial sums over its four 32-column tiles
     {
       const float* dSg = bw.dS + ch * HD * HD;
-      const float* Sg = sv.S_in + ch * HD * HD;
       f32x4 v[8];
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) v[jb] = *reinterpret_cast<const f32x4*>(dSg + tile_off(w, jb));
-#pragma unroll
-      for (int jb = 0; jb < 8; ++jb) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(Sg + tile_off(w, jb));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[i] += v[jb][i] * x[i];
-        store_tile_n(v[jb], SP, 16 * w, 16 * jb);
+      if (t < HD) {
+        const float* pg = bw.dgam_part + ch * 4 * HD + t;
+        sm.dgam[t] = (pg[0] + pg[HD]) + (pg[2 * HD] + pg[3 * HD]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] = row_sum16(part[i]);
-      if (dcol() == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.dgam[16 * w + drow(i)] = part[i];
-      }
+      for (int jb = 0; jb < 8; ++jb) store_tile_n(v[jb], SP, 16 * w, 16 * jb);
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_tile_n(U[nt], AP, 16 * rb, 64 * chh + 16 * nt);

@@ -467,6 +467,7 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
 
   bf16x8 pu[BP_PER_THREAD];
   bf16 pdo[4];
+  f32x4 pS[2];         // S_in tiles (rows 16 w, this workgroup's 32 columns)
   int64_t pt0 = 0;
   int pn = 0;
   auto prefetch = [&](int cn) {
@@ -482,6 +483,10 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
       const int rr = rD + j, rc = rr < pn ? rr : pn - 1;
       pdo[j] = dO[((pt0 + rc) * H + h) * HD + j0 + jD];
     }
+    const float* Sg = sv.S_in + ((int64_t)cn * H + h) * HD * HD;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      pS[nt] = *reinterpret_cast<const f32x4*>(Sg + tile_off(w, (j0 >> 4) + nt));
   };
 
   f32x4 dS[2];
@@ -504,6 +509,7 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     bf16x8 qdt[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) qdt[k] = pu[8 + k];
+    const f32x4 Sc0 = pS[0], Sc1 = pS[1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sm.do_hi[jD][rD + j] = (rD + j < n) ? pdo[j] : f2bf(0.f);
     if (ci - 1 >= c0) prefetch(ci - 1);
@@ -533,6 +539,12 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     // ---- D. dS_in = Diag(e^G_last) dS_out + scale Qd^T dO - Kd^T dR
     {
       float* dSg = bw.dS + ch * HD * HD;
+      // d/d e^(G_last)[c] of this workgroup's columns: sum_j dS_out[c][j] S_in[c][j]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = row_sum16(dS[0][i] * Sc0[i] + dS[1][i] * Sc1[i]);
+        if (dcol() == 0) bw.dgam_part[(ch * NTILE + tile) * HD + 16 * w + drow(i)] = p;
+      }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         *reinterpret_cast<f32x4*>(dSg + tile_off(w, (j0 >> 4) + nt)) = dS[nt];
