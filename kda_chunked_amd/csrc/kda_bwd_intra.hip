@@ -144,12 +144,12 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   float eG[4][4];
   bf16x2 eq2[4][2], ek2[4][2];     // raw q, k (bf16 pairs i = 2 m, 2 m + 1); q^ = q * rqr[i]
   float rqr[4], rkr[4];
-  // (re)load G, q, k at this thread's elements: called where a phase needs
-  // them, so that they are not held in registers across the phases between
+  // load G, q, k at this thread's elements once the first phase's panels
+  // are staged (they stay in registers through the epilogues of P2 .. P7)
   auto load_epi = [&]() {
     // addresses rebuilt from an opaque copy of the thread id, and pointers
-    // made opaque, so that a reload is neither merged with the previous one
-    // nor served from addresses kept live in between
+    // made opaque, so that the loads are issued here and not hoisted above
+    // the staging of the first phase
     int tt = t;
     int64_t base = (t0 * H + h) * HD, rbase = t0 * H + h;
     asm volatile("" : "+v"(tt), "+s"(base), "+s"(rbase));
@@ -299,7 +299,6 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) store_tile_n(U[nt], AP, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
-    load_epi();
     f32x4 a[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
@@ -437,7 +436,6 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     const Panel YT{&sm.u.p6.m.u.a.yt_hi[0][0], &sm.u.p6.m.u.a.yt_lo[0][0], K2_LD};
     const Panel XT{&sm.u.p6.m.u.b.xt_hi[0][0], &sm.u.p6.m.u.b.xt_lo[0][0], K1_LD};
     const Panel DAT{&sm.u.p6.m.dat_hi[0][0], &sm.u.p6.m.dat_lo[0][0], K1_LD};
-    load_epi();
     const bool calm = sm.calm_chunk;
     const bool blk_calm = sm.calm_blk[rb];
 #pragma unroll
