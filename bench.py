@@ -73,24 +73,22 @@ MAC_PER_CHUNK_HEAD = {
 # stored precision (a panel read by several workgroups counts once). Gate
 # form g stores an fp32 g / dg; the raw form a bf16 a / da plus fp32 partials.
 _X = 64 * 128                      # elements of a 64 x 128 per-chunk tensor
-_FWD_PANEL_B = 107008              # forward operand panels (bf16 hi/lo planes)
+_PANEL_B = 131584                  # operand panels (bf16 hi/lo planes), read by all three scans
 _FWD_CHAIN_B = 57856               # their chain part: -Kd, Tb, Ke^T hi/lo, e^(G_last)
-_BWD_PANEL_B = 131584              # reverse-scan operand panels
 
 
 def algo_bytes_per_chunk_head(kernel: str, raw: bool) -> int:
     gate_in = 2 * _X if raw else 4 * _X            # a (bf16) or g (fp32)
     gate_out = 2 * _X + 512 + 4 if raw else 4 * _X  # da + part_dt + part_A, or dg
     return {
-        # q, k, gate, beta -> G, rq, rk, T, A_kk, both panel sets
-        "fwd_prep": 2 * 2 * _X + gate_in + 128 + 4 * _X + 512 + 2 * 4 * 64 * 64
-                    + _FWD_PANEL_B + _BWD_PANEL_B,
+        # q, k, gate, beta -> G, rq, rk, T, A_kk, operand panels
+        "fwd_prep": 2 * 2 * _X + gate_in + 128 + 4 * _X + 512 + 2 * 4 * 64 * 64 + _PANEL_B,
         # chain panels, v -> S_in, R, U~ (fp32)
         "fwd_scan": _FWD_CHAIN_B + 2 * _X + 4 * 128 * 128 + 2 * 4 * _X,
         # S_in, U~, scale Qd, scale A_qk -> o
         "fwd_out": 4 * 128 * 128 + 4 * _X + 2 * 2 * _X + 2 * 2 * 64 * 64 + 2 * _X,
         # panels, dO, S_in -> dv, dU~, dR, dS (fp32), e^(G_last) gradient partials
-        "bwd_scan": _BWD_PANEL_B + 2 * _X + 4 * 128 * 128
+        "bwd_scan": _PANEL_B + 2 * _X + 4 * 128 * 128
                     + 2 * _X + 2 * 4 * _X + 4 * 128 * 128 + 4 * 4 * 128,
         # q, k, G, dO, beta, rq, rk, S_in, dS, U~, R, dU~, dR, T, A_kk, e^(G_last)
         # gradient partials (+ a) -> dq, dk, dbeta, dgate

@@ -74,14 +74,9 @@ kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states, float** G)
     sv.S_in = c.take<float>((size_t)s.NC * s.H * 128 * 128);
     sv.R = c.take<float>((size_t)s.NC * s.H * 64 * 128);
     sv.U = c.take<float>((size_t)s.NC * s.H * 64 * 128);
-    sv.bwd_panels = c.take<uint16_t>((size_t)s.NC * s.H * kda::bwd_panel::ELEMS);
+    sv.panels = c.take<uint16_t>((size_t)s.NC * s.H * kda::fwd_panel::ELEMS);
   }
   return sv;
-}
-
-// Operand panels of the forward scan (bf16, fwd_panel layout per chunk-head).
-void* carve_panels(Carver& c, const Sizes& s) {
-  return c.take<uint16_t>((size_t)s.NC * s.H * kda::fwd_panel::ELEMS);
 }
 
 kda::BwdWork carve_bwd(Carver& c, const Sizes& s) {
@@ -145,7 +140,6 @@ size_t fwd_ws_bytes(const Sizes& s) {
   carve_table(c, s);
   float* G;
   carve_saved(c, s, 1, &G);   // used when the caller saves nothing
-  carve_panels(c, s);
   return c.off;
 }
 
@@ -156,7 +150,6 @@ size_t bwd_ws_bytes(const Sizes& s, int replay) {
   if (replay) {
     float* G;
     carve_saved(c, s, 1, &G);
-    carve_panels(c, s);
   }
   return c.off;
 }
@@ -225,15 +218,14 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   const kda::ChunkTable ct = carve_table(wc, s);
   float* G = nullptr;
   kda::SavedSet sv = carve_saved(wc, s, 1, &G);   // used when nothing is saved
-  void* panels = carve_panels(wc, s);
   if (saved) {
     Carver sc(saved);
     sv = carve_saved(sc, s, 1, &G);
   }
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
-  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, saved != nullptr, hs));
-  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, saved != nullptr, hs));
-  LAUNCH("fwd_out", kda::launch_fwd_out(d, ct, sv, panels, o, hs));
+  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, saved != nullptr, hs));
+  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, saved != nullptr, hs));
+  LAUNCH("fwd_out", kda::launch_fwd_out(d, ct, sv, sv.panels, o, hs));
   return KDA_OK;
 }
 
@@ -285,10 +277,8 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   const kda::BwdWork bw = carve_bwd(wc, s);
   float* G = nullptr;
   kda::SavedSet sv;
-  void* panels = nullptr;
   if (replay) {
     sv = carve_saved(wc, s, 1, &G);
-    panels = carve_panels(wc, s);
   } else {
     Carver sc(const_cast<void*>(saved));
     sv = carve_saved(sc, s, 1, &G);
@@ -296,8 +286,8 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   if (replay) {
-    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, panels, 1, hs));
-    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, panels, 1, hs));
+    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, 1, hs));
+    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, 1, hs));
   }
   LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, G, sv, dO, dv, bw, hs));
   LAUNCH("bwd_intra", kda::launch_bwd_intra(d, in, ct, G, sv, dO, out, bw, hs));

@@ -63,26 +63,49 @@ KDA_DEV bf16x8 frag(const bf16* p, int ld, int row0, int k) {
   return *reinterpret_cast<const bf16x8*>(p + (row0 + (l & 15)) * ld + k + ((l >> 4) << 3));
 }
 
-// acc += A[m0:m0+16, k0:k1] * B[n0:n0+16, k0:k1]^T  (both panels K-contiguous).
-// Terms are added small-first: lo*hi, hi*lo, then hi*hi.
-template <int SPLIT>
+// The same fragment of A[m][k] from a panel that stores A transposed, as
+// [k][m] (row k, ld elements per row), by two LDS transpose loads. Within each
+// 16-lane group the load gives lane j the j-th column of the 4 x 16 block whose
+// rows the group's lanes address: lane s (of 16) supplies row s / 4 and
+// columns 4 (s % 4) .. + 3, so lane j receives rows 0..3 of column j. The
+// panel must live in LDS with 8-byte aligned rows.
+KDA_DEV bf16x8 fragT(const bf16* p, int ld, int m0, int k) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int l = lane_id(), s = l & 15;
+  const bf16* a = p + (k + 8 * (l >> 4) + (s >> 2)) * ld + m0 + 4 * (s & 3);
+  const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+  const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 4 * ld));
+  // whole-vector concatenation and one 16-byte bit cast (no per-element casts)
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A operand fragment: K-contiguous panel (AT = false) or transposed panel.
+template <bool AT>
+KDA_DEV bf16x8 afrag(const bf16* p, int ld, int m0, int k) {
+  return AT ? fragT(p, ld, m0, k) : frag(p, ld, m0, k);
+}
+
+// acc += A[m0:m0+16, k0:k1] * B[n0:n0+16, k0:k1]^T  (B K-contiguous; A too, or
+// stored transposed when AT). Terms are added small-first: lo*hi, hi*lo, hi*hi.
+template <int SPLIT, bool AT = false>
 KDA_DEV void mma(f32x4& acc, const Panel& A, int m0, const Panel& B, int n0, int k0, int k1) {
   for (int k = k0; k < k1; k += 32) {
-    const bf16x8 ah = frag(A.hi, A.ld, m0, k);
+    const bf16x8 ah = afrag<AT>(A.hi, A.ld, m0, k);
     const bf16x8 bh = frag(B.hi, B.ld, n0, k);
-    if (SPLIT & SPLIT_A) acc = mfma16(frag(A.lo, A.ld, m0, k), bh, acc);
+    if (SPLIT & SPLIT_A) acc = mfma16(afrag<AT>(A.lo, A.ld, m0, k), bh, acc);
     if (SPLIT & SPLIT_B) acc = mfma16(ah, frag(B.lo, B.ld, n0, k), acc);
     acc = mfma16(ah, bh, acc);
   }
 }
 
-template <int SPLIT, int KLEN>
+template <int SPLIT, int KLEN, bool AT = false>
 KDA_DEV void mma_k(f32x4& acc, const Panel& A, int m0, const Panel& B, int n0) {
 #pragma unroll
   for (int k = 0; k < KLEN; k += 32) {
-    const bf16x8 ah = frag(A.hi, A.ld, m0, k);
+    const bf16x8 ah = afrag<AT>(A.hi, A.ld, m0, k);
     const bf16x8 bh = frag(B.hi, B.ld, n0, k);
-    if (SPLIT & SPLIT_A) acc = mfma16(frag(A.lo, A.ld, m0, k), bh, acc);
+    if (SPLIT & SPLIT_A) acc = mfma16(afrag<AT>(A.lo, A.ld, m0, k), bh, acc);
     if (SPLIT & SPLIT_B) acc = mfma16(ah, frag(B.lo, B.ld, n0, k), acc);
     acc = mfma16(ah, bh, acc);
   }
@@ -118,13 +141,13 @@ KDA_DEV void mma_blk(f32x4 (&acc)[MT][NT], const Panel& A, int m0, const Panel& 
 }
 
 // One row of tiles: acc[nt] += A[m0:m0+16] * B[n0 + 16 nt]^T.
-template <int SPLIT, int NT>
+template <int SPLIT, int NT, bool AT = false>
 KDA_DEV void mma_row(f32x4 (&acc)[NT], const Panel& A, int m0, const Panel& B, int n0, int k0,
                      int k1) {
   for (int k = k0; k < k1; k += 32) {
-    const bf16x8 ah = frag(A.hi, A.ld, m0, k);
+    const bf16x8 ah = afrag<AT>(A.hi, A.ld, m0, k);
     bf16x8 al;
-    if (SPLIT & SPLIT_A) al = frag(A.lo, A.ld, m0, k);
+    if (SPLIT & SPLIT_A) al = afrag<AT>(A.lo, A.ld, m0, k);
     bf16x8 bh[NT], bl[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {

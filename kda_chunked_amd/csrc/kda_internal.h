@@ -35,7 +35,7 @@ struct SavedSet {
   float* U;      // [NC, H, 64 x 128] U~ = Tb R (tile order)
   float* rq;     // [T, H]           L2 scalars (1 without the fused norm)
   float* rk;     // [T, H]
-  void* bwd_panels;   // [NC, H, bwd_panel::ELEMS] bf16: the reverse scan's operands
+  void* panels;  // [NC, H, fwd_panel::ELEMS] bf16 operand panels (also the reverse scan's)
 };
 
 struct Dims {
@@ -79,10 +79,12 @@ struct BwdWork {
   float* part_dt;     // [NC, H, 128] raw form: per-chunk sum of dz
 };
 
-// Per chunk-head operand panels of the forward pass, written by the prep
-// kernel as bf16 planes (hi = RNE(x), lo = RNE(x - hi)), row-major. The first
-// CHAIN elements are what the sequential state scan needs; the rest feed the
-// output kernel. Offsets in bf16 elements.
+// Per chunk-head operand panels, written by the prep kernel as bf16 planes
+// (hi = RNE(x), lo = RNE(x - hi)), row-major. The first CHAIN elements are
+// what the sequential state scan needs; QD and AQ feed the output kernel; the
+// reverse scan reads Ke^T, A_qk, Tb, Qd and -Kd transposed (LDS transpose
+// loads), for which the lo planes of -Kd and Tb follow at the end (written only
+// when a backward will use them). Offsets in bf16 elements.
 namespace fwd_panel {
 constexpr int KD = 0;                        // -Kd hi            [64][128]
 constexpr int TB = KD + 64 * 128;            // Tb hi             [64][64]
@@ -91,26 +93,16 @@ constexpr int GAM = KE + 2 * 128 * 64;       // e^(G_last), fp32  [128]
 constexpr int CHAIN = GAM + 2 * 128;         // end of the scan's part
 constexpr int QD = CHAIN;                    // scale Qd hi, lo   [2][64][128]
 constexpr int AQ = QD + 2 * 64 * 128;        // scale A_qk hi, lo [2][64][64]
-constexpr int ELEMS = AQ + 2 * 64 * 64;      // bf16 elements per chunk-head
-constexpr size_t BYTES = (size_t)ELEMS * 2;  // 107008, a multiple of 16
+constexpr int KDL = AQ + 2 * 64 * 64;        // -Kd lo            [64][128]
+constexpr int TBL = KDL + 64 * 128;          // Tb lo             [64][64]
+constexpr int ELEMS = TBL + 64 * 64;         // 65792 bf16 elements per chunk-head
+constexpr size_t BYTES = (size_t)ELEMS * 2;  // 131584, a multiple of 16
 }  // namespace fwd_panel
-
-// Per chunk-head operand panels of the reverse state scan, written by the prep
-// kernel into the saved set: bf16 hi, lo planes, row-major, K contiguous.
-namespace bwd_panel {
-constexpr int KE = 0;                        // Ke = k^ e^(G_last - G)     [2][64][128]  rows r
-constexpr int AQT = KE + 2 * 64 * 128;       // scale A_qk^T                [2][64][64]   rows r, K = i
-constexpr int TBT = AQT + 2 * 64 * 64;       // Tb^T                        [2][64][64]   rows i, K = r
-constexpr int QDT = TBT + 2 * 64 * 64;       // scale Qd^T                  [2][128][64]  rows c, K = r
-constexpr int KDT = QDT + 2 * 128 * 64;      // -Kd^T                       [2][128][64]  rows c, K = r
-constexpr int GAM = KDT + 2 * 128 * 64;      // e^(G_last), fp32            [128]
-constexpr int ELEMS = GAM + 2 * 128;         // 65792 bf16 elements (a multiple of 8)
-}  // namespace bwd_panel
 
 hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
                             hipStream_t s);
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
-                           const SavedSet& sv, void* panels, int with_bwd, hipStream_t s);
+                           const SavedSet& sv, int with_bwd, hipStream_t s);
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, const void* panels, int save_R, hipStream_t s);
 hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& sv,

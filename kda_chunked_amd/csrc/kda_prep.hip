@@ -20,9 +20,10 @@
 // decays e^(g_r), r = i+1 .. 15, which never exceeds 1 and underflows
 // gracefully.
 //
-// Besides the saved fp32 matrices, the kernel writes the forward scan's
-// operand panels (-Kd, scale Qd, Ke^T, Tb, scale A_qk as bf16 hi/lo planes and
-// e^(G_last)), so that the sequential scan only streams them.
+// Besides the saved fp32 matrices, the kernel writes the operand panels (-Kd,
+// scale Qd, Ke^T, Tb, scale A_qk as bf16 hi/lo planes and e^(G_last)) that the
+// two state scans and the output kernel stream; the lo planes of -Kd and Tb
+// only when a backward will read them.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -137,7 +138,7 @@ KDA_DEV void decayed_frag(const PrepSmem& sm, const bf16 (*x)[XS_LD], float rx, 
 __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, ChunkTable ct,
                                                             float* __restrict__ G_out,
                                                             SavedSet sv, bf16* __restrict__ panels,
-                                                            bf16* __restrict__ bwd_panels) {
+                                                            int with_lo) {
   __shared__ PrepSmem sm;
   const int ci = blockIdx.x, h = blockIdx.y;
   if (ci >= ct.doc_c0[d.N]) return;
@@ -458,15 +459,18 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8) = f32x4{kv[0], kv[1], kv[2], kv[3]};
     *reinterpret_cast<f32x4*>(Akk_g + r * CL + i8 + 4) = f32x4{kv[4], kv[5], kv[6], kv[7]};
     if (P) {
-      bf16x8 tb, ah, al;
+      bf16x8 tb, tl, ah, al;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        tb[j] = f2bf(tv[j] * sm.beta[i8 + j]);
+        const float b = tv[j] * sm.beta[i8 + j];
+        tb[j] = f2bf(b);
+        tl[j] = f2bf(b - bf2f(tb[j]));
         const float a = qv[j] * d.scale;
         ah[j] = f2bf(a);
         al[j] = f2bf(a - bf2f(ah[j]));
       }
       *reinterpret_cast<bf16x8*>(P + fwd_panel::TB + r * CL + i8) = tb;
+      if (with_lo) *reinterpret_cast<bf16x8*>(P + fwd_panel::TBL + r * CL + i8) = tl;
       *reinterpret_cast<bf16x8*>(P + fwd_panel::AQ + r * CL + i8) = ah;
       *reinterpret_cast<bf16x8*>(P + fwd_panel::AQ + CL * CL + r * CL + i8) = al;
     }
@@ -474,13 +478,15 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   if (P) {
     // -Kd = -k^ e^G (hi) and scale Qd = scale q^ e^G (hi, lo): this thread's row
     const float rqA = sm.rq[rA], rkA = sm.rk[rA];
-    bf16x8 kd[2], qh[2], ql[2];
+    bf16x8 kd[2], kl[2], qh[2], ql[2];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float e1 = fexp(Gv[j]);
       const float kx = -bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA * e1;
       const float qx = bf2f(j < 8 ? q0[j] : q1[j - 8]) * rqA * e1 * d.scale;
-      kd[j >> 3][j & 7] = f2bf(kx);
+      const bf16 hk = f2bf(kx);
+      kd[j >> 3][j & 7] = hk;
+      kl[j >> 3][j & 7] = f2bf(kx - bf2f(hk));
       const bf16 hq = f2bf(qx);
       qh[j >> 3][j & 7] = hq;
       ql[j >> 3][j & 7] = f2bf(qx - bf2f(hq));
@@ -488,6 +494,7 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       *reinterpret_cast<bf16x8*>(P + fwd_panel::KD + rA * HD + cA + 8 * u) = kd[u];
+      if (with_lo) *reinterpret_cast<bf16x8*>(P + fwd_panel::KDL + rA * HD + cA + 8 * u) = kl[u];
       *reinterpret_cast<bf16x8*>(P + fwd_panel::QD + rA * HD + cA + 8 * u) = qh[u];
       *reinterpret_cast<bf16x8*>(P + fwd_panel::QD + CL * HD + rA * HD + cA + 8 * u) = ql[u];
     }
@@ -510,72 +517,12 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     }
     if (t < HD) reinterpret_cast<float*>(P + fwd_panel::GAM)[t] = fexp(sm.Gref[4][t]);
   }
-  if (bwd_panels) {
-    // the reverse scan's operands (bwd_panel layout)
-    bf16* B = bwd_panels + ch * (int64_t)bwd_panel::ELEMS;
-    auto put8g = [](bf16* hi, bf16* lo, const float* x) {
-      bf16x8 a, b;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        a[j] = f2bf(x[j]);
-        b[j] = f2bf(x[j] - bf2f(a[j]));
-      }
-      *reinterpret_cast<bf16x8*>(hi) = a;
-      *reinterpret_cast<bf16x8*>(lo) = b;
-    };
-    {
-      // Ke [r][c] = k^_r e^(G_last - G_r): this thread's row rA, channels cA ..
-      const float rkA = sm.rk[rA];
-      float x[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        x[j] = bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA * fexp(sm.Gref[4][cA + j] - Gv[j]);
-      bf16* hi = B + bwd_panel::KE + rA * HD + cA;
-      put8g(hi, hi + CL * HD, x);
-      put8g(hi + 8, hi + 8 + CL * HD, x + 8);
-    }
-    {
-      // scale A_qk^T [r][i] = scale A_qk[i][r];  Tb^T [i][r] = T[r][i] beta_i
-      const int r = t >> 3, i8 = 8 * (t & 7);
-      float a[8], b[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        a[j] = sm.Aqk[i8 + j][r] * d.scale;
-        b[j] = Tm[i8 + j][r] * sm.beta[r];
-      }
-      bf16* ah = B + bwd_panel::AQT + r * CL + i8;
-      bf16* bh = B + bwd_panel::TBT + r * CL + i8;
-      put8g(ah, ah + CL * CL, a);
-      put8g(bh, bh + CL * CL, b);
-    }
-    {
-      // scale Qd^T [c][r] = scale q^_r e^(G_r), -Kd^T [c][r] = -k^_r e^(G_r):
-      // thread (channel c, rows 16 b .. 16 b + 15)
-      const int c = t & 127, b = t >> 7;
-      float xq[16], xk[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = 16 * b + j;
-        const float e1 = fexp(sm.G[r][c]);
-        xq[j] = bf2f(sm.qs[r][c]) * sm.rq[r] * e1 * d.scale;
-        xk[j] = -bf2f(sm.ks[r][c]) * sm.rk[r] * e1;
-      }
-      bf16* qh = B + bwd_panel::QDT + c * CL + 16 * b;
-      bf16* kh = B + bwd_panel::KDT + c * CL + 16 * b;
-      put8g(qh, qh + HD * CL, xq);
-      put8g(qh + 8, qh + 8 + HD * CL, xq + 8);
-      put8g(kh, kh + HD * CL, xk);
-      put8g(kh + 8, kh + 8 + HD * CL, xk + 8);
-    }
-    if (t < HD) reinterpret_cast<float*>(B + bwd_panel::GAM)[t] = fexp(sm.Gref[4][t]);
-  }
 }
 
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
-                           const SavedSet& sv, void* panels, int with_bwd, hipStream_t s) {
+                           const SavedSet& sv, int with_bwd, hipStream_t s) {
   hipLaunchKernelGGL(fwd_prep_kernel, dim3(d.NC, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
-                     reinterpret_cast<bf16*>(panels),
-                     with_bwd ? reinterpret_cast<bf16*>(sv.bwd_panels) : nullptr);
+                     reinterpret_cast<bf16*>(sv.panels), with_bwd);
   return hipGetLastError();
 }
 

@@ -386,18 +386,22 @@ hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& s
 }
 
 // ------------------------------------------------------------------ reverse
-// Operands come ready-made from the saved set (bwd_panel layout, written by
-// the prep kernel) and are staged into LDS with 16-byte copies prefetched
-// into registers one chunk ahead; scale Qd^T shares its LDS space with Ke and
-// is staged once Ke has been consumed.
+// LDS of the reverse scan. The chunk's operands are the forward panels in
+// their stored (row-major, natural) orientation; every product here needs
+// them transposed (K along the stored rows), which the LDS transpose loads of
+// fragT provide. Rows are padded to 72 or 144 elements so that those loads
+// are free of bank conflicts. The panels arrive through 16-byte copies
+// prefetched into registers one chunk ahead; scale Qd shares its LDS space
+// with Ke^T and is staged once Ke^T has been consumed.
+constexpr int QD_LD = HD + 16;       // 144: rows of 288 bytes
 struct BwdScanSmem {
   union {
-    struct { bf16 hi[CL][K1_LD], lo[CL][K1_LD]; } ke;      // Ke           [r][c]
-    struct { bf16 hi[HD][K2_LD], lo[HD][K2_LD]; } qd;      // scale*Qd^T   [c][r]
+    struct { bf16 hi[HD][K2_LD], lo[HD][K2_LD]; } ke;      // Ke^T         [c][r]
+    struct { bf16 hi[CL][QD_LD], lo[CL][QD_LD]; } qd;      // scale*Qd     [r][c]
   } r1;
-  bf16 kd_hi[HD][K2_LD], kd_lo[HD][K2_LD];                 // -Kd^T        [c][r]
-  bf16 aq_hi[CL][K2_LD], aq_lo[CL][K2_LD];                 // scale*A_qk^T [r][i]
-  bf16 tb_hi[CL][K2_LD], tb_lo[CL][K2_LD];                 // Tb^T         [i][r]
+  bf16 kd_hi[CL][QD_LD], kd_lo[CL][QD_LD];                 // -Kd          [r][c]
+  bf16 aq_hi[CL][K2_LD], aq_lo[CL][K2_LD];                 // scale*A_qk   [r][i]
+  bf16 tb_hi[CL][K2_LD], tb_lo[CL][K2_LD];                 // Tb           [r][i]
   bf16 do_hi[VT][K2_LD];                                   // dO^T [j][r] (exact bf16)
   bf16 ds_hi[VT][K1_LD], ds_lo[VT][K1_LD];                 // dS^T [j][c]
   bf16 du_hi[VT][K2_LD], du_lo[VT][K2_LD];                 // dU~^T [j][r]
@@ -405,35 +409,45 @@ struct BwdScanSmem {
   float gam[HD];
 };
 
-constexpr int BP_UNITS = bwd_panel::ELEMS / 8;           // 8224
+// The operands as 8224 16-byte units u = t + 512 k, k = 0..16, read from the
+// chunk's forward panels: k 0-3 Ke^T (hi, lo), 4-5 A_qk (hi, lo), 6 Tb hi,
+// 7 Tb lo, 8-11 Qd (hi, lo; staged after Ke^T is consumed), 12-13 -Kd hi,
+// 14-15 -Kd lo, 16 e^(G_last) (32 units).
+constexpr int BP_UNITS = 8224;
 constexpr int BP_PER_THREAD = (BP_UNITS + NT_SCAN - 1) / NT_SCAN;   // 17
-static_assert(bwd_panel::KE == 0 && bwd_panel::AQT == 2048 * 8 && bwd_panel::TBT == 3072 * 8 &&
-                  bwd_panel::QDT == 4096 * 8 && bwd_panel::KDT == 6144 * 8 &&
-                  bwd_panel::GAM == 8192 * 8 && BP_UNITS == 8224,
+static_assert(fwd_panel::KE + 2 * 128 * 64 == fwd_panel::GAM &&
+                  fwd_panel::QD + 2 * 64 * 128 == fwd_panel::AQ,
               "staging map below assumes this panel layout");
 
-// LDS destination of unit u = t + 512 k (k != 8..11: those are scale Qd^T,
-// staged separately into the Ke space).
+// Panel offset (bf16 elements) of unit t + 512 k at t = 0.
+KDA_DEV constexpr int bunit_src(int k) {
+  return k < 4 ? fwd_panel::KE + 4096 * k
+       : k < 6 ? fwd_panel::AQ + 4096 * (k - 4)
+       : k == 6 ? fwd_panel::TB
+       : k == 7 ? fwd_panel::TBL
+       : k < 12 ? fwd_panel::QD + 4096 * (k - 8)
+       : k < 14 ? fwd_panel::KD + 4096 * (k - 12)
+       : k < 16 ? fwd_panel::KDL + 4096 * (k - 14)
+       : fwd_panel::GAM;
+}
+
+// LDS destination of unit u = t + 512 k.
 KDA_DEV void bstage_unit(BwdScanSmem& sm, int k, int t, const bf16x8& x) {
-  const int u = t + NT_SCAN * k;
+  const int v = t + NT_SCAN * (k < 4 ? k : k < 6 ? k - 4 : k < 8 ? 0 : k < 12 ? k - 8
+                                     : k < 14 ? k - 12 : k < 16 ? k - 14 : 0);
   bf16* dst;
-  if (k < 4) {                       // Ke hi, lo
-    const int v = u;
-    dst = (v >> 10 ? &sm.r1.ke.lo[0][0] : &sm.r1.ke.hi[0][0]) + ((v >> 4) & 63) * K1_LD + ((v & 15) << 3);
-  } else if (k < 6) {                // A_qk^T hi, lo
-    const int v = u - 2048;
+  if (k < 4) {                       // Ke^T [c][r] hi, lo
+    dst = (v >> 10 ? &sm.r1.ke.lo[0][0] : &sm.r1.ke.hi[0][0]) + ((v >> 3) & 127) * K2_LD + ((v & 7) << 3);
+  } else if (k < 6) {                // A_qk [r][i] hi, lo
     dst = (v >> 9 ? &sm.aq_lo[0][0] : &sm.aq_hi[0][0]) + ((v >> 3) & 63) * K2_LD + ((v & 7) << 3);
-  } else if (k < 8) {                // Tb^T hi, lo
-    const int v = u - 3072;
-    dst = (v >> 9 ? &sm.tb_lo[0][0] : &sm.tb_hi[0][0]) + ((v >> 3) & 63) * K2_LD + ((v & 7) << 3);
-  } else if (k < 12) {               // scale Qd^T hi, lo (into the Ke space)
-    const int v = u - 4096;
-    dst = (v >> 10 ? &sm.r1.qd.lo[0][0] : &sm.r1.qd.hi[0][0]) + ((v >> 3) & 127) * K2_LD + ((v & 7) << 3);
-  } else if (k < 16) {               // -Kd^T hi, lo
-    const int v = u - 6144;
-    dst = (v >> 10 ? &sm.kd_lo[0][0] : &sm.kd_hi[0][0]) + ((v >> 3) & 127) * K2_LD + ((v & 7) << 3);
+  } else if (k < 8) {                // Tb [r][i] hi (k = 6), lo (k = 7)
+    dst = (k == 7 ? &sm.tb_lo[0][0] : &sm.tb_hi[0][0]) + (v >> 3) * K2_LD + ((v & 7) << 3);
+  } else if (k < 12) {               // scale Qd [r][c] hi, lo (into the Ke^T space)
+    dst = (v >> 10 ? &sm.r1.qd.lo[0][0] : &sm.r1.qd.hi[0][0]) + ((v >> 4) & 63) * QD_LD + ((v & 15) << 3);
+  } else if (k < 16) {               // -Kd [r][c] hi (k = 12, 13), lo (k = 14, 15)
+    dst = (k >= 14 ? &sm.kd_lo[0][0] : &sm.kd_hi[0][0]) + (v >> 4) * QD_LD + ((v & 15) << 3);
   } else {                           // e^(G_last), fp32 (32 units)
-    *reinterpret_cast<bf16x8*>(&sm.gam[4 * (u - 8192)]) = x;
+    *reinterpret_cast<bf16x8*>(&sm.gam[4 * t]) = x;
     return;
   }
   *reinterpret_cast<bf16x8*>(dst) = x;
@@ -453,11 +467,11 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   const int j0 = tile * VT;
   const int H = d.H;
   const int jD = t & 31, rD = 4 * (t >> 5);
-  const bf16* BP = reinterpret_cast<const bf16*>(sv.bwd_panels);
+  const bf16* BP = reinterpret_cast<const bf16*>(sv.panels);
 
-  const Panel KE{&sm.r1.ke.hi[0][0], &sm.r1.ke.lo[0][0], K1_LD};
-  const Panel QD{&sm.r1.qd.hi[0][0], &sm.r1.qd.lo[0][0], K2_LD};
-  const Panel KD{&sm.kd_hi[0][0], &sm.kd_lo[0][0], K2_LD};
+  const Panel KE{&sm.r1.ke.hi[0][0], &sm.r1.ke.lo[0][0], K2_LD};
+  const Panel QD{&sm.r1.qd.hi[0][0], &sm.r1.qd.lo[0][0], QD_LD};
+  const Panel KD{&sm.kd_hi[0][0], &sm.kd_lo[0][0], QD_LD};
   const Panel AQ{&sm.aq_hi[0][0], &sm.aq_lo[0][0], K2_LD};
   const Panel TB{&sm.tb_hi[0][0], &sm.tb_lo[0][0], K2_LD};
   const Panel DO{&sm.do_hi[0][0], nullptr, K2_LD};
@@ -473,11 +487,11 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   auto prefetch = [&](int cn) {
     pt0 = ct.tok[cn];
     pn = ct.len[cn];
-    const bf16* src = BP + ((int64_t)cn * H + h) * bwd_panel::ELEMS;
+    const bf16* src = BP + ((int64_t)cn * H + h) * fwd_panel::ELEMS + 8 * t;
 #pragma unroll
     for (int k = 0; k < BP_PER_THREAD; ++k)
       if (k < BP_PER_THREAD - 1 || t < BP_UNITS - NT_SCAN * (BP_PER_THREAD - 1))
-        pu[k] = *reinterpret_cast<const bf16x8*>(src + 8 * (t + NT_SCAN * k));
+        pu[k] = *reinterpret_cast<const bf16x8*>(src + bunit_src(k));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rr = rD + j, rc = rr < pn ? rr : pn - 1;
@@ -516,15 +530,15 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     __syncthreads();
     // ---- B. dU~ = scale A_qk^T dO + Ke dS_out   (tile rows 16 rb, cols 16 nw)
     f32x4 dU = zero4();
-    mma<SPLIT_A>(dU, AQ, 16 * rb, DO, 16 * nw, (16 * rb / 32) * 32, CL);
-    mma_k<SPLIT_BW, HD>(dU, KE, 16 * rb, DS, 16 * nw);
+    mma<SPLIT_A, true>(dU, AQ, 16 * rb, DO, 16 * nw, (16 * rb / 32) * 32, CL);
+    mma_k<SPLIT_BW, HD, true>(dU, KE, 16 * rb, DS, 16 * nw);
     *reinterpret_cast<f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)) = dU;
     store_tile_t(dU, DU, 16 * rb, 16 * nw);
     __syncthreads();
     // ---- C. dR = Tb^T dU~ (= dv); scale Qd^T into the Ke space
     {
       f32x4 acc = zero4();
-      mma<SPLIT_BW>(acc, TB, 16 * rb, DU, 16 * nw, (16 * rb / 32) * 32, CL);
+      mma<SPLIT_BW, true>(acc, TB, 16 * rb, DU, 16 * nw, (16 * rb / 32) * 32, CL);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + drow(i);
@@ -551,8 +565,8 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
 #pragma unroll
         for (int i = 0; i < 4; ++i) dS[nt][i] *= sm.gam[16 * w + drow(i)];
       }
-      mma_row<SPLIT_A, 2>(dS, QD, 16 * w, DO, 0, 0, CL);
-      mma_row<SPLIT_BW, 2>(dS, KD, 16 * w, DR, 0, 0, CL);
+      mma_row<SPLIT_A, 2, true>(dS, QD, 16 * w, DO, 0, 0, CL);
+      mma_row<SPLIT_BW, 2, true>(dS, KD, 16 * w, DR, 0, 0, CL);
     }
     __syncthreads();
 #pragma unroll
