@@ -28,7 +28,9 @@
  *    16-byte aligned. T = packed tokens, H = heads, D = 128.
  *      q, k, v, o, dO, dq, dk, dv           [T, H, 128] bf16
  *      beta, dbeta                          [T, H]      bf16
- *      gate form g:   g, dg                 [T, H, 128] fp32 (log of the forget gate)
+ *      gate form g:   g, dg                 [T, H, 128] fp32 (log of the forget gate,
+ *                                           g <= 0; a positive g gives unspecified
+ *                                           values, with every kernel in bounds)
  *      gate form raw: a, da                 [T, H, 128] bf16
  *                     A_log, dA_log         [H]         fp32
  *                     dt_bias, ddt_bias     [H, 128]    fp32
