@@ -30,6 +30,7 @@
 namespace kda {
 
 constexpr float SPAN_MAX = 120.f;
+constexpr int kPrepWorkgroups = 256;     // MI355X compute units
 
 #ifndef KDA_SPLIT_P1
 #define KDA_SPLIT_P1 SPLIT_AB    // A_kk = X_k Y^T, A_qk = X_q Y^T
@@ -140,44 +141,65 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
                                                             SavedSet sv, bf16* __restrict__ panels,
                                                             int with_lo) {
   __shared__ PrepSmem sm;
-  const int ci = blockIdx.x, h = blockIdx.y;
-  if (ci >= ct.doc_c0[d.N]) return;
-  const int64_t t0 = ct.tok[ci];
-  const int n = ct.len[ci];
+  const int h = blockIdx.y, nch = ct.doc_c0[d.N];
   const int t = threadIdx.x, w = wave_id(), l = lane_id();
   const int H = d.H;
-  const int64_t ch = (int64_t)ci * H + h;
   const bf16* q = reinterpret_cast<const bf16*>(in.q);
   const bf16* k = reinterpret_cast<const bf16*>(in.k);
   const bf16* beta = reinterpret_cast<const bf16*>(in.beta);
   const int rA = t >> 3, cA = 16 * (t & 7);
-  const bool okA = rA < n;
-  const int64_t baseA = ((t0 + (okA ? rA : n - 1)) * H + h) * HD + cA;
-
-  // ---- 1. loads (all issued before use). Thread t: q, k of row rA, channels
-  // cA .. cA+15; the gate of channel cG = t & 127, rows 16 qG .. 16 qG + 15.
-  const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(q + baseA);
-  const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(q + baseA + 8);
-  const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
-  const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
   const int cG = t & 127, qG = t >> 7;
+
+  // One chunk's raw inputs. Thread t: q, k of row rA, channels cA .. cA+15;
+  // the gate of channel cG = t & 127, rows 16 qG .. 16 qG + 15; beta of row t.
+  // The workgroup walks the chunks ci, ci + gridDim.x, ... of head h and loads
+  // the next chunk's inputs while it works on the current one.
+  bf16x8 q0, q1, k0, k1;
   float g[16], eg[16];
-  if (!d.raw) {
-    const float* gp = reinterpret_cast<const float*>(in.gate);
+  bf16 bt = f2bf(0.f);
+  auto load_raw = [&](int cn) {
+    const int64_t u0 = ct.tok[cn];
+    const int un = ct.len[cn];
+    const int64_t baseA = ((u0 + (rA < un ? rA : un - 1)) * H + h) * HD + cA;
+    q0 = *reinterpret_cast<const bf16x8*>(q + baseA);
+    q1 = *reinterpret_cast<const bf16x8*>(q + baseA + 8);
+    k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
+    k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
+    if (!d.raw) {
+      const float* gp = reinterpret_cast<const float*>(in.gate);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 16 * qG + j;
-      g[j] = gp[((t0 + (r < n ? r : n - 1)) * H + h) * HD + cG];
-    }
-  } else {
-    const bf16* ap = reinterpret_cast<const bf16*>(in.gate);
+      for (int j = 0; j < 16; ++j) {
+        const int r = 16 * qG + j;
+        g[j] = gp[((u0 + (r < un ? r : un - 1)) * H + h) * HD + cG];
+      }
+    } else {
+      const bf16* ap = reinterpret_cast<const bf16*>(in.gate);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 16 * qG + j;
-      g[j] = bf2f(ap[((t0 + (r < n ? r : n - 1)) * H + h) * HD + cG]);
+      for (int j = 0; j < 16; ++j) {
+        const int r = 16 * qG + j;
+        g[j] = bf2f(ap[((u0 + (r < un ? r : un - 1)) * H + h) * HD + cG]);
+      }
     }
-  }
-  if (t < CL) sm.beta[t] = t < n ? bf2f(beta[(t0 + (t < n ? t : n - 1)) * H + h]) : 0.f;
+    if (t < CL) bt = beta[(u0 + (t < un ? t : un - 1)) * H + h];
+  };
+  int ci = blockIdx.x;
+  if (ci >= nch) return;
+  load_raw(ci);
+  for (;;) {
+  // indices re-derived from an opaque copy of the thread id in every
+  // iteration: otherwise the unrolled phases' LDS addresses are hoisted out of
+  // the loop and held in registers across it
+  int tt = threadIdx.x;
+  asm volatile("" : "+v"(tt));
+  const int t = tt, w = tt >> 6, l = tt & 63;
+  const int rA = t >> 3, cA = 16 * (t & 7);
+  const int cG = t & 127, qG = t >> 7;
+  const int64_t t0 = ct.tok[ci];
+  const int n = ct.len[ci];
+  const int64_t ch = (int64_t)ci * H + h;
+
+  // ---- 1. this chunk's raw inputs into LDS, L2 partial sums
+  if (t < CL) sm.beta[t] = t < n ? bf2f(bt) : 0.f;
   *reinterpret_cast<bf16x8*>(&sm.qs[rA][cA]) = q0;
   *reinterpret_cast<bf16x8*>(&sm.qs[rA][cA + 8]) = q1;
   *reinterpret_cast<bf16x8*>(&sm.ks[rA][cA]) = k0;
@@ -261,10 +283,6 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     sm.Akk[16 * I + rr][16 * J + cc] = 0.f;
     sm.Aqk[16 * I + rr][16 * J + cc] = 0.f;
   }
-  // this thread's G (row rA, channels cA ..)
-  float Gv[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) Gv[j] = sm.G[rA][cA + j];
   __syncthreads();
 
   // ---- 3. decayed products of A_kk and A_qk, as work items spread over the
@@ -399,6 +417,9 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   }
   __syncthreads();
 
+  // the next chunk's raw inputs, in flight during the solve and the writes
+  if (ci + (int)gridDim.x < nch) load_raw(ci + gridDim.x);
+
   // ---- 4. T = (I + Diag(beta) A_kk)^-1 by 16x16 blocks, fp32
   float (*Tm)[F_LD] = sm.Tm;
   for (int e = t; e < CL * F_LD; e += NT_PREP) (&Tm[0][0])[e] = 0.f;
@@ -479,11 +500,15 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     // -Kd = -k^ e^G (hi) and scale Qd = scale q^ e^G (hi, lo): this thread's row
     const float rqA = sm.rq[rA], rkA = sm.rk[rA];
     bf16x8 kd[2], kl[2], qh[2], ql[2];
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.ks[rA][cA]);
+    const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&sm.ks[rA][cA + 8]);
+    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.qs[rA][cA]);
+    const bf16x8 qb = *reinterpret_cast<const bf16x8*>(&sm.qs[rA][cA + 8]);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float e1 = fexp(Gv[j]);
-      const float kx = -bf2f(j < 8 ? k0[j] : k1[j - 8]) * rkA * e1;
-      const float qx = bf2f(j < 8 ? q0[j] : q1[j - 8]) * rqA * e1 * d.scale;
+      const float e1 = fexp(sm.G[rA][cA + j]);
+      const float kx = -bf2f(j < 8 ? ka[j] : kb[j - 8]) * rkA * e1;
+      const float qx = bf2f(j < 8 ? qa[j] : qb[j - 8]) * rqA * e1 * d.scale;
       const bf16 hk = f2bf(kx);
       kd[j >> 3][j & 7] = hk;
       kl[j >> 3][j & 7] = f2bf(kx - bf2f(hk));
@@ -517,11 +542,17 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     }
     if (t < HD) reinterpret_cast<float*>(P + fwd_panel::GAM)[t] = fexp(sm.Gref[4][t]);
   }
+  ci += gridDim.x;
+  if (ci >= nch) break;
+  __syncthreads();     // the next chunk's first phase overwrites what was read above
+  }
 }
 
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
                            const SavedSet& sv, int with_bwd, hipStream_t s) {
-  hipLaunchKernelGGL(fwd_prep_kernel, dim3(d.NC, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
+  // about one workgroup per CU (the LDS allows one), each walking chunks of one head
+  const int gx = std::max(1, std::min(d.NC, (kPrepWorkgroups + d.H - 1) / d.H));
+  hipLaunchKernelGGL(fwd_prep_kernel, dim3(gx, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
                      reinterpret_cast<bf16*>(sv.panels), with_bwd);
   return hipGetLastError();
 }
