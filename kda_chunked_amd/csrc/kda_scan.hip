@@ -304,83 +304,116 @@ KDA_DEV bf16x8 gfrag(const bf16* p, int ld, int m0, int k) {
   return *reinterpret_cast<const bf16x8*>(p + (m0 + (l & 15)) * ld + k + ((l >> 4) << 3));
 }
 
+// One workgroup walks the chunks ci, ci + gridDim.x, ... of head h and loads
+// the next chunk's S_in, U~ tiles and Qd, A_qk fragments while it works on the
+// current one.
+constexpr int kOutWorkgroups = 256;     // about one per CU (the LDS allows one)
+
 __global__ __launch_bounds__(512) void fwd_out_kernel(Dims d, ChunkTable ct,
                                                        SavedSet sv,
                                                        const bf16* __restrict__ panels,
                                                        bf16* __restrict__ o) {
   __shared__ FwdOutSmem sm;
-  const int ci = blockIdx.x, h = blockIdx.y;
-  if (ci >= ct.doc_c0[d.N]) return;
-  const int64_t t0 = ct.tok[ci];
-  const int n = ct.len[ci];
-  const int t = threadIdx.x, w = wave_id();
-  const int rb = w & 3, chh = w >> 2;
+  const int h = blockIdx.y, nch = ct.doc_c0[d.N];
   const int H = d.H;
-  const int64_t ch = (int64_t)ci * H + h;
-  const bf16* P = panels + ch * fwd_panel::ELEMS;
   const Panel SP{&sm.s_hi[0][0], &sm.s_lo[0][0], K1_LD};
   const Panel UP{&sm.u_hi[0][0], &sm.u_lo[0][0], K2_LD};
-  // S_in [c][j] -> S_in^T panel: wave w stores tiles (c block w, all 8 j blocks)
-  {
-    const float* Sg = sv.S_in + ch * HD * HD;
-    const float* Ug = sv.U + ch * CL * HD;
-    f32x4 xs[8], xu[4];
+  const int w0 = wave_id(), rb0 = w0 & 3;
+  f32x4 xs[8], xu[4];               // S_in tiles (c block w, all j blocks), U~ tiles (i blocks, j block w)
+  bf16x8 fq[4][2], fa[2][2];        // scale Qd, scale A_qk fragments (hi, lo) of row block rb
+  auto load_chunk = [&](int cn) {
+    const int64_t cch = (int64_t)cn * H + h;
+    const float* Sg = sv.S_in + cch * HD * HD;
+    const float* Ug = sv.U + cch * CL * HD;
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) xs[jb] = *reinterpret_cast<const f32x4*>(Sg + tile_off(w, jb));
+    for (int jb = 0; jb < 8; ++jb) xs[jb] = *reinterpret_cast<const f32x4*>(Sg + tile_off(w0, jb));
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) xu[ib] = *reinterpret_cast<const f32x4*>(Ug + tile_off(ib, w));
+    for (int ib = 0; ib < 4; ++ib) xu[ib] = *reinterpret_cast<const f32x4*>(Ug + tile_off(ib, w0));
+    const bf16* P = panels + cch * fwd_panel::ELEMS;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      fq[kk][0] = gfrag(P + fwd_panel::QD, HD, 16 * rb0, 32 * kk);
+      fq[kk][1] = gfrag(P + fwd_panel::QD + CL * HD, HD, 16 * rb0, 32 * kk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      fa[kk][0] = gfrag(P + fwd_panel::AQ, CL, 16 * rb0, 32 * kk);
+      fa[kk][1] = gfrag(P + fwd_panel::AQ + CL * CL, CL, 16 * rb0, 32 * kk);
+    }
+  };
+  int ci = blockIdx.x;
+  if (ci >= nch) return;
+  load_chunk(ci);
+  for (;;) {
+    // indices from an opaque copy of the thread id in every iteration, so that
+    // LDS addresses are not hoisted out of the loop and held in registers
+    int tt = threadIdx.x;
+    asm volatile("" : "+v"(tt));
+    const int w = tt >> 6, rb = w & 3, chh = w >> 2;
+    const int64_t t0 = ct.tok[ci];
+    const int n = ct.len[ci];
+    // S_in [c][j] -> S_in^T panel; U~ [i][j] -> U~^T panel
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) store_tile_t(xs[jb], SP, 16 * w, 16 * jb);
-    // U~ [i][j] -> U~^T panel: wave w: j block w, i blocks 0..3
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) store_tile_t(xu[ib], UP, 16 * ib, 16 * w);
-  }
-  __syncthreads();
-  f32x4 acc[4];
+    bf16x8 aq[4][2], aa[2][2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
-  const bf16* qh = P + fwd_panel::QD;
-  const bf16* ql = qh + CL * HD;
+    for (int kk = 0; kk < 4; ++kk) aq[kk][0] = fq[kk][0], aq[kk][1] = fq[kk][1];
 #pragma unroll
-  for (int k = 0; k < HD; k += 32) {
-    const bf16x8 ah = gfrag(qh, HD, 16 * rb, k), al = gfrag(ql, HD, 16 * rb, k);
+    for (int kk = 0; kk < 2; ++kk) aa[kk][0] = fa[kk][0], aa[kk][1] = fa[kk][1];
+    __syncthreads();
+    const int cn = ci + gridDim.x;
+    if (cn < nch) load_chunk(cn);
+    f32x4 acc[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n0 = 64 * chh + 16 * nt;
-      const bf16x8 bh = frag(SP.hi, SP.ld, n0, k), bl = frag(SP.lo, SP.ld, n0, k);
-      acc[nt] = mfma16(al, bh, acc[nt]);
-      acc[nt] = mfma16(ah, bl, acc[nt]);
-      acc[nt] = mfma16(ah, bh, acc[nt]);
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 ah = aq[kk][0], al = aq[kk][1];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int n0 = 64 * chh + 16 * nt;
+        const bf16x8 bh = frag(SP.hi, SP.ld, n0, 32 * kk), bl = frag(SP.lo, SP.ld, n0, 32 * kk);
+        acc[nt] = mfma16(al, bh, acc[nt]);
+        acc[nt] = mfma16(ah, bl, acc[nt]);
+        acc[nt] = mfma16(ah, bh, acc[nt]);
+      }
     }
-  }
-  const bf16* aqh = P + fwd_panel::AQ;
-  const bf16* aql = aqh + CL * CL;
-  const int kend = ((16 * rb + 16 + 31) / 32) * 32;
-  for (int k = 0; k < kend; k += 32) {
-    const bf16x8 ah = gfrag(aqh, CL, 16 * rb, k), al = gfrag(aql, CL, 16 * rb, k);
+    // A_qk is lower triangular: K up to the end of the row block
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n0 = 64 * chh + 16 * nt;
-      const bf16x8 bh = frag(UP.hi, UP.ld, n0, k), bl = frag(UP.lo, UP.ld, n0, k);
-      acc[nt] = mfma16(al, bh, acc[nt]);
-      acc[nt] = mfma16(ah, bl, acc[nt]);
-      acc[nt] = mfma16(ah, bh, acc[nt]);
+    for (int kk = 0; kk < 2; ++kk) {
+      if (32 * kk < 16 * rb + 16) {
+        const bf16x8 ah = aa[kk][0], al = aa[kk][1];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int n0 = 64 * chh + 16 * nt;
+          const bf16x8 bh = frag(UP.hi, UP.ld, n0, 32 * kk), bl = frag(UP.lo, UP.ld, n0, 32 * kk);
+          acc[nt] = mfma16(al, bh, acc[nt]);
+          acc[nt] = mfma16(ah, bl, acc[nt]);
+          acc[nt] = mfma16(ah, bh, acc[nt]);
+        }
+      }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * rb + drow(i);
-    if (r < n) {
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + drow(i);
+      if (r < n) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        o[((t0 + r) * H + h) * HD + 64 * chh + 16 * nt + dcol()] = f2bf(acc[nt][i]);
+        for (int nt = 0; nt < 4; ++nt)
+          o[((t0 + r) * H + h) * HD + 64 * chh + 16 * nt + dcol()] = f2bf(acc[nt][i]);
+      }
     }
+    if (cn >= nch) break;
+    ci = cn;
+    __syncthreads();   // the next chunk's panels overwrite the ones read above
   }
 }
 
 hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& sv,
                           const void* panels, void* o, hipStream_t s) {
-  hipLaunchKernelGGL(fwd_out_kernel, dim3(d.NC, d.H), dim3(512), 0, s, d, ct, sv,
+  const int gx = std::max(1, std::min(d.NC, (kOutWorkgroups + d.H - 1) / d.H));
+  hipLaunchKernelGGL(fwd_out_kernel, dim3(gx, d.H), dim3(512), 0, s, d, ct, sv,
                      reinterpret_cast<const bf16*>(panels), reinterpret_cast<bf16*>(o));
   return hipGetLastError();
 }
