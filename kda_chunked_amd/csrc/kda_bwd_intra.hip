@@ -101,6 +101,8 @@ struct BwdIntraSmem {
     } p6;
     struct {
       float dG[CL][GS_LD];
+      float Pm[CL][GS_LD];          // aP rows, for their exclusive prefix sums
+      float totP[4][HD];
       float tot[4][HD];
       float red[2][4][HD];
       float rowp[2][2][CL];
@@ -112,7 +114,6 @@ struct BwdIntraSmem {
   float dbc[4][CL], dbr[2][CL];
   float GL[HD], gam[HD], dGL[HD], dgam[HD];
   float Gref[5][HD];       // G before block I (I = 0..3) and G_last (I = 4)
-  float dGLw[4][HD];
   int calm_blk[4];
   int calm_chunk;
 };
@@ -204,9 +205,13 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       if (sm.Gref[I][t] - sm.Gref[I + 1][t] > CALM_SPAN_B) sm.calm_blk[I] = 0;
   }
 
-  f32x4 adq[4], adk[4], adG[4];
+  // aP: the e^(G_last - G_r) terms of dKe, k^_r p3_r, which enter dg_j for
+  // every j > r; kept apart from adG so that P7 adds their exclusive prefix
+  // sum directly instead of the chunk total minus a suffix sum (which cancels
+  // badly when the decay across the chunk is steep)
+  f32x4 adq[4], adk[4], adG[4], aP[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) adq[nt] = adk[nt] = adG[nt] = zero4();
+  for (int nt = 0; nt < 4; ++nt) adq[nt] = adk[nt] = adG[nt] = aP[nt] = zero4();
 
   // ------------------------------------------------------------ P2: dQd, dKd
   // dR (= dv, fp32) from the reverse scan
@@ -306,24 +311,18 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int c = 64 * chh + 16 * nt + dcol();
-      float colp = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p3 = a[nt][i] * fexp(sm.GL[c] - eG[nt][i]);
         adk[nt][i] += p3;
-        adG[nt][i] -= p3 * EK(nt, i);
-        colp += p3 * EK(nt, i);
+        aP[nt][i] += p3 * EK(nt, i);
       }
-      colp += __shfl_xor(colp, 16);
-      colp += __shfl_xor(colp, 32);
-      if (l < 16) sm.dGLw[rb][c] = colp;
     }
     // dA_qk = scale dO U~^T: rows 16 rb, columns i in tiles 2 chh, 2 chh + 1
     dAq[0] = dAq[1] = zero4();
     mma_row<KDA_SPLIT_B5, 2>(dAq, DOP, 16 * rb, AP, 32 * chh, 0, HD);
     __syncthreads();
-    if (t < HD)
-      sm.dGL[t] = sm.dgam[t] * sm.gam[t] + ((sm.dGLw[0][t] + sm.dGLw[1][t]) + (sm.dGLw[2][t] + sm.dGLw[3][t]));
+    if (t < HD) sm.dGL[t] = sm.dgam[t] * sm.gam[t];
   }
 
   // ------------------------------------------------------------ P4: dTb = dU~ R^T
@@ -633,10 +632,14 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
             const float wgt = a * qv[r] + b * kv[r];
             sq[r] += a * ke;
             sk[r] += b * ke;
-            sg[r] += wgt * ke;
             const float s2 = wgt * E;
             sk[i] += s2;
-            sg[i] -= s2 * kv[i];
+            // a diagonal pair (i == r) enters dG_r with + and - and cancels
+            // exactly; adding both would leave the rounding of the larger term
+            if (i < r) {
+              sg[r] += wgt * ke;
+              sg[i] -= s2 * kv[i];
+            }
           }
         }
         // each thread overwrites only the entries it read
@@ -672,6 +675,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + drow(i), c = 64 * chh + 16 * nt + dcol();
         dG[r][c] = adG[nt][i] + (r == CL - 1 ? sm.dGL[c] : 0.f);
+        sm.u.p7.Pm[r][c] = aP[nt][i];
       }
     // L2 row dot products <x^, dx^> over the 128 channels
     if (d.l2norm) {
@@ -705,7 +709,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       for (int j = 0; j < 16; ++j) av[j] = bf2f(araw[rowidx(clampr(16 * I + j)) * HD + cc]);
     }
     __syncthreads();
-    // reverse cumsum inside the chunk: dg_j = sum_{r >= j} dG_r
+    // dg_j = sum_{r >= j} dG_r + sum_{r < j} aP_r: a reverse cumsum and an
+    // exclusive forward one inside the chunk, with the block carries
     float v[16];
     float run = 0.f;
 #pragma unroll
@@ -714,9 +719,18 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       v[j] = run;
     }
     sm.u.p7.tot[I][cc] = run;
+    float runp = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float x = sm.u.p7.Pm[16 * I + j][cc];
+      v[j] += runp;
+      runp += x;
+    }
+    sm.u.p7.totP[I][cc] = runp;
     __syncthreads();
     float carry = 0.f;
     for (int I2 = 3; I2 > I; --I2) carry += sm.u.p7.tot[I2][cc];
+    for (int I2 = 0; I2 < I; ++I2) carry += sm.u.p7.totP[I2][cc];
     float pdt = 0.f, pA = 0.f;
     const float ea = d.raw ? __expf(in.A_log[h]) : 0.f;
     const float dtb = d.raw ? in.dt_bias[h * HD + cc] : 0.f;
