@@ -114,6 +114,31 @@ KDA_DEV void offdiag_tile(int item, int& I, int& J) {
   J = item - I * (I - 1) / 2;
 }
 
+// The k and q fragments of one row share their factors e^(G - rho).
+KDA_DEV void decayed_frag2(const PrepSmem& sm, float rk, float rq, int row, int c,
+                           const float* ra, const float* rb, bf16x8& kh, bf16x8& kl,
+                           bf16x8& qh, bf16x8& ql) {
+  const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.G[row][c]);
+  const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.G[row][c + 4]);
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(ra + c);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(ra + c + 4);
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(rb + c);
+  const f32x4 b1 = *reinterpret_cast<const f32x4*>(rb + c + 4);
+  const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&sm.ks[row][c]);
+  const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&sm.qs[row][c]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float gj = j < 4 ? g0[j] : g1[j - 4];
+    const float rj = 0.5f * ((j < 4 ? a0[j] : a1[j - 4]) + (j < 4 ? b0[j] : b1[j - 4]));
+    const float e = fexp(gj - rj);
+    const float vk = bf2f(kv[j]) * rk * e, vq = bf2f(qv[j]) * rq * e;
+    kh[j] = f2bf(vk);
+    kl[j] = f2bf(vk - bf2f(kh[j]));
+    qh[j] = f2bf(vq);
+    ql[j] = f2bf(vq - bf2f(qh[j]));
+  }
+}
+
 // One 8-channel MFMA fragment of x e^(+-(G - rho)) for row `row`, channels
 // c .. c+7, split into hi and lo planes, with rho = (ra + rb) / 2 (exactly ra
 // when ra == rb). sgn = +1: x e^(G - rho); -1: x e^(rho - G).
@@ -328,8 +353,7 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       for (int ks = 0; ks < HD / 32; ++ks) {
         const int c = 32 * ks + 8 * (l >> 4);
         bf16x8 xk_h, xk_l, xq_h, xq_l, y_h, y_l;
-        decayed_frag(sm, sm.ks, rka, ra, c, refa, refb, 1.f, xk_h, xk_l);
-        decayed_frag(sm, sm.qs, rqa, ra, c, refa, refb, 1.f, xq_h, xq_l);
+        decayed_frag2(sm, rka, rqa, ra, c, refa, refb, xk_h, xk_l, xq_h, xq_l);
         decayed_frag(sm, sm.ks, rkb, rbw, c, refa, refb, -1.f, y_h, y_l);
         if (KDA_SPLIT_P1 & SPLIT_A) {
           akk = mfma16(xk_l, y_h, akk);
