@@ -383,20 +383,30 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
         i = second ? 15 - p : p;
         r = second ? st - 1 : p + st;
       };
-      float f[8];    // k_i rk_i e^(G_r - G_i), channels c .. c+7
+      float f[8] = {};    // k_i rk_i e^(G_r - G_i), channels c .. c+7
+      // the starting values k_i rk_i of both columns, so that a step is
+      // branch-free and the loads of later steps can be issued early
+      float kpf[8], kzf[8];
+      {
+        const bf16x8 kp = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + p][c]);
+        const bf16x8 kz = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + 15 - p][c]);
+        const float rkp = sm.rk[b0 + p], rkz = sm.rk[b0 + 15 - p];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          kpf[j] = bf2f(kp[j]) * rkp;
+          kzf[j] = bf2f(kz[j]) * rkz;
+        }
+      }
       auto step = [&](int st, float& skk, float& sqk) {
         int r, i;
         pair_of(st, r, i);
-        if (st == 0 || st == 16 - p) {
-          const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + i][c]);
-          const float rki = sm.rk[b0 + i];
+        const bool restart = st == 16 - p;       // first row of column 15 - p
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c]);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + 4]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) f[j] = bf2f(kv[j]) * rki;
-        } else {
-          const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c]);
-          const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + 4]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) f[j] *= j < 4 ? e0[j] : e1[j - 4];
+        for (int j = 0; j < 8; ++j) {
+          const float fm = f[j] * (j < 4 ? e0[j] : e1[j - 4]);
+          f[j] = st == 0 ? kpf[j] : restart ? kzf[j] : fm;
         }
         const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + r][c]);
         const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&sm.qs[b0 + r][c]);
