@@ -34,6 +34,8 @@ namespace kda {
 
 constexpr int NTHR = 512;
 constexpr int K1_LD = HD + 8;
+constexpr int T1_LD = HD + 16;      // [k][n] panels read by LDS transpose loads, 128 wide
+constexpr int T2_LD = CL + 8;       // the same, 64 wide
 constexpr int K2_LD = CL + 8;
 constexpr int X_LD = 32 + 8;
 constexpr int GS_LD = HD + 4;
@@ -66,14 +68,16 @@ constexpr float CALM_SPAN_B = 40.f;
 
 struct BwdIntraSmem {
   union {
+    // P2 .. P4 panels hold their operands transposed, K = j along the rows
+    // (8-byte stores of the D tiles, transpose loads of the fragments)
     struct {
-      bf16 s_hi[HD][K1_LD], s_lo[HD][K1_LD];       // S_in [c][j], then dS_out [c][j]
-      bf16 a_hi[CL][K1_LD], a_lo[CL][K1_LD];       // dR [r][j], then U~ [r][j]
+      bf16 s_hi[HD][T1_LD], s_lo[HD][T1_LD];       // S_in [j][c], then dS_out [j][c]
+      bf16 a_hi[HD][T2_LD], a_lo[HD][T2_LD];       // dR [j][r], then U~ [j][r]
       bf16 do_hi[CL][K1_LD];                       // dO [r][j]
     } p2;
     struct {
-      bf16 a_hi[CL][K1_LD], a_lo[CL][K1_LD];       // dU~ [r][j]
-      bf16 b_hi[CL][K1_LD], b_lo[CL][K1_LD];       // R [i][j]
+      bf16 a_hi[HD][T2_LD], a_lo[HD][T2_LD];       // dU~ [j][r]
+      bf16 b_hi[HD][T2_LD], b_lo[HD][T2_LD];       // R [j][i]
     } p4;
     struct {
       bf16 dt_hi[CL][K2_LD], dt_lo[CL][K2_LD];     // dT = dTb Diag(beta) [r][m]
@@ -215,8 +219,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 
   // ------------------------------------------------------------ P2: dQd, dKd
   // dR (= dv, fp32) from the reverse scan
-  const Panel SP{&sm.u.p2.s_hi[0][0], &sm.u.p2.s_lo[0][0], K1_LD};
-  const Panel AP{&sm.u.p2.a_hi[0][0], &sm.u.p2.a_lo[0][0], K1_LD};
+  const Panel SP{&sm.u.p2.s_hi[0][0], &sm.u.p2.s_lo[0][0], T1_LD};
+  const Panel AP{&sm.u.p2.a_hi[0][0], &sm.u.p2.a_lo[0][0], T2_LD};
   const Panel DOP{&sm.u.p2.do_hi[0][0], nullptr, K1_LD};
   auto load_state_panel = [&](const float* src) {
     // 128 x 128 fp32, tile order -> split panel [c][j]: wave w takes row
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) v[jb] = *reinterpret_cast<const f32x4*>(src + tile_off(w, jb));
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) store_tile_n(v[jb], SP, 16 * w, 16 * jb);
+    for (int jb = 0; jb < 8; ++jb) store_tile_t(v[jb], SP, 16 * w, 16 * jb);
   };
   {
     f32x4 dR[4];
@@ -243,16 +247,16 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       }
       *reinterpret_cast<bf16x8*>(&sm.u.p2.do_hi[r][j8]) = x;
     }
-    const Panel APd{AP.hi, (KDA_SPLIT_B2 & SPLIT_A) ? AP.lo : nullptr, K1_LD};
+    const Panel APd{AP.hi, (KDA_SPLIT_B2 & SPLIT_A) ? AP.lo : nullptr, T2_LD};
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) store_tile_n(dR[nt], APd, 16 * rb, 64 * chh + 16 * nt);
+    for (int nt = 0; nt < 4; ++nt) store_tile_t(dR[nt], APd, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
     load_epi();
     {
       f32x4 a[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
-      mma_row<KDA_SPLIT_B3, 4>(a, DOP, 16 * rb, SP, 64 * chh, 0, HD);
+      mma_row<KDA_SPLIT_B3, 4, false, true>(a, DOP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       f32x4 b[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) b[nt] = zero4();
-      mma_row<KDA_SPLIT_B2, 4>(b, AP, 16 * rb, SP, 64 * chh, 0, HD);
+      mma_row<KDA_SPLIT_B2, 4, true, true>(b, AP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -299,15 +303,15 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         sm.dgam[t] = (pg[0] + pg[HD]) + (pg[2 * HD] + pg[3 * HD]);
       }
 #pragma unroll
-      for (int jb = 0; jb < 8; ++jb) store_tile_n(v[jb], SP, 16 * w, 16 * jb);
+      for (int jb = 0; jb < 8; ++jb) store_tile_t(v[jb], SP, 16 * w, 16 * jb);
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) store_tile_n(U[nt], AP, 16 * rb, 64 * chh + 16 * nt);
+    for (int nt = 0; nt < 4; ++nt) store_tile_t(U[nt], AP, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
     f32x4 a[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
-    mma_row<KDA_SPLIT_B4, 4>(a, AP, 16 * rb, SP, 64 * chh, 0, HD);
+    mma_row<KDA_SPLIT_B4, 4, true, true>(a, AP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int c = 64 * chh + 16 * nt + dcol();
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     }
     // dA_qk = scale dO U~^T: rows 16 rb, columns i in tiles 2 chh, 2 chh + 1
     dAq[0] = dAq[1] = zero4();
-    mma_row<KDA_SPLIT_B5, 2>(dAq, DOP, 16 * rb, AP, 32 * chh, 0, HD);
+    mma_row<KDA_SPLIT_B5, 2, false, true>(dAq, DOP, 16 * rb, AP, 32 * chh, 0, HD);
     __syncthreads();
     if (t < HD) sm.dGL[t] = sm.dgam[t] * sm.gam[t];
   }
@@ -328,8 +332,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   // ------------------------------------------------------------ P4: dTb = dU~ R^T
   f32x4 dTb[2];
   {
-    const Panel DU{&sm.u.p4.a_hi[0][0], &sm.u.p4.a_lo[0][0], K1_LD};
-    const Panel RP{&sm.u.p4.b_hi[0][0], &sm.u.p4.b_lo[0][0], K1_LD};
+    const Panel DU{&sm.u.p4.a_hi[0][0], &sm.u.p4.a_lo[0][0], T2_LD};
+    const Panel RP{&sm.u.p4.b_hi[0][0], &sm.u.p4.b_lo[0][0], T2_LD};
     // dU~ and R, tile order: wave w takes row block w & 3, column blocks 4 (w >> 2) ..
     f32x4 va[4], vb[4];
 #pragma unroll
@@ -339,12 +343,12 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     }
 #pragma unroll
     for (int rep = 0; rep < 4; ++rep) {
-      store_tile_n(va[rep], DU, 16 * rb, 64 * chh + 16 * rep);
-      store_tile_n(vb[rep], RP, 16 * rb, 64 * chh + 16 * rep);
+      store_tile_t(va[rep], DU, 16 * rb, 64 * chh + 16 * rep);
+      store_tile_t(vb[rep], RP, 16 * rb, 64 * chh + 16 * rep);
     }
     __syncthreads();
     dTb[0] = dTb[1] = zero4();
-    mma_row<KDA_SPLIT_B6, 2>(dTb, DU, 16 * rb, RP, 32 * chh, 0, HD);
+    mma_row<KDA_SPLIT_B6, 2, true, true>(dTb, DU, 16 * rb, RP, 32 * chh, 0, HD);
     __syncthreads();
   }
 

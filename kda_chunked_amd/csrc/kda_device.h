@@ -140,8 +140,9 @@ KDA_DEV void mma_blk(f32x4 (&acc)[MT][NT], const Panel& A, int m0, const Panel& 
   }
 }
 
-// One row of tiles: acc[nt] += A[m0:m0+16] * B[n0 + 16 nt]^T.
-template <int SPLIT, int NT, bool AT = false>
+// One row of tiles: acc[nt] += A[m0:m0+16] * B[n0 + 16 nt]^T. AT / BT: the
+// panel stores its operand transposed, [k][m] / [k][n] (read by LDS transpose loads).
+template <int SPLIT, int NT, bool AT = false, bool BT = false>
 KDA_DEV void mma_row(f32x4 (&acc)[NT], const Panel& A, int m0, const Panel& B, int n0, int k0,
                      int k1) {
   for (int k = k0; k < k1; k += 32) {
@@ -151,8 +152,8 @@ KDA_DEV void mma_row(f32x4 (&acc)[NT], const Panel& A, int m0, const Panel& B, i
     bf16x8 bh[NT], bl[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      bh[nt] = frag(B.hi, B.ld, n0 + 16 * nt, k);
-      if (SPLIT & SPLIT_B) bl[nt] = frag(B.lo, B.ld, n0 + 16 * nt, k);
+      bh[nt] = afrag<BT>(B.hi, B.ld, n0 + 16 * nt, k);
+      if (SPLIT & SPLIT_B) bl[nt] = afrag<BT>(B.lo, B.ld, n0 + 16 * nt, k);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
