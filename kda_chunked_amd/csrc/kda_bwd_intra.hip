@@ -80,7 +80,7 @@ struct BwdIntraSmem {
       bf16 b_hi[HD][T2_LD], b_lo[HD][T2_LD];       // R [j][i]
     } p4;
     struct {
-      bf16 dt_hi[CL][K2_LD], dt_lo[CL][K2_LD];     // dT = dTb Diag(beta) [r][m]
+      bf16 dt_hi[CL][K2_LD], dt_lo[CL][K2_LD];     // dT = dTb Diag(beta), transposed [m][r]
       bf16 tn_hi[CL][K2_LD], tn_lo[CL][K2_LD];     // T [i][m]
       bf16 tt_hi[CL][K2_LD], tt_lo[CL][K2_LD];     // T^T [r][m]
       bf16 mt_hi[CL][K2_LD], mt_lo[CL][K2_LD];     // (dT T^T)^T [i][m]
@@ -89,8 +89,8 @@ struct BwdIntraSmem {
       struct {
         union {
           struct {                                 // part 1
-            bf16 dq_hi[CL][K2_LD], dq_lo[CL][K2_LD];   // dA_qk [r][i]
-            bf16 dk_hi[CL][K2_LD], dk_lo[CL][K2_LD];   // dA_kk [r][i]
+            bf16 dq_hi[CL][K2_LD], dq_lo[CL][K2_LD];   // dA_qk, transposed [i][r]
+            bf16 dk_hi[CL][K2_LD], dk_lo[CL][K2_LD];   // dA_kk, transposed [i][r]
             bf16 yt_hi[HD][K2_LD], yt_lo[HD][K2_LD];   // Y^T [c][i], Y = k^ times a decay factor
           } a;
           struct {                                 // part 2
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         x[i] = v * bm;
         cp += v * Tg[r * CL + m];
       }
-      store_tile_n(x, DT, 16 * rb, 32 * chh + 16 * nt);
+      store_tile_t(x, DT, 16 * rb, 32 * chh + 16 * nt);
       cp += __shfl_xor(cp, 16);
       cp += __shfl_xor(cp, 32);
       if (l < 16) sm.dbc[rb][m] = cp;
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     f32x4 tm[2];
     tm[0] = tm[1] = zero4();
     const int kend = ((min(16 * rb + 16, 32 * chh + 32) + 31) / 32) * 32;
-    mma_row<KDA_SPLIT_B8, 2>(tm, DT, 16 * rb, TN, 32 * chh, 0, kend);
+    mma_row<KDA_SPLIT_B8, 2, true>(tm, DT, 16 * rb, TN, 32 * chh, 0, kend);
     store_tile_t(tm[0], MT, 16 * rb, 32 * chh);
     store_tile_t(tm[1], MT, 16 * rb, 32 * chh + 16);
     __syncthreads();
@@ -443,8 +443,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     const bool blk_calm = sm.calm_blk[rb];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      store_tile_n(dAq[nt], DQ, 16 * rb, 32 * chh + 16 * nt);
-      store_tile_n(dAk[nt], DK, 16 * rb, 32 * chh + 16 * nt);
+      store_tile_t(dAq[nt], DQ, 16 * rb, 32 * chh + 16 * nt);
+      store_tile_t(dAk[nt], DK, 16 * rb, 32 * chh + 16 * nt);
       store_tile_t(dAq[nt], DAT, 32 * rb, 32 * chh + 16 * nt);
       store_tile_t(dAk[nt], DAT, 32 * rb + 16, 32 * chh + 16 * nt);
     }
@@ -475,8 +475,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       f32x4 aq[4], ak[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) aq[nt] = ak[nt] = zero4();
-      mma_row<KDA_SPLIT_B7, 4>(aq, DQ, 16 * rb, YT, 64 * chh, 0, kend);
-      mma_row<KDA_SPLIT_B7, 4>(ak, DK, 16 * rb, YT, 64 * chh, 0, kend);
+      mma_row<KDA_SPLIT_B7, 4, true>(aq, DQ, 16 * rb, YT, 64 * chh, 0, kend);
+      mma_row<KDA_SPLIT_B7, 4, true>(ak, DK, 16 * rb, YT, 64 * chh, 0, kend);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -508,8 +508,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
               ak[nt][i] *= dj;
             }
           }
-          mma_k16<KDA_SPLIT_B7>(aq[nt], DQ, 16 * rb, YT, 64 * chh + 16 * nt, 16 * J);
-          mma_k16<KDA_SPLIT_B7>(ak[nt], DK, 16 * rb, YT, 64 * chh + 16 * nt, 16 * J);
+          mma_k16<KDA_SPLIT_B7, true>(aq[nt], DQ, 16 * rb, YT, 64 * chh + 16 * nt, 16 * J);
+          mma_k16<KDA_SPLIT_B7, true>(ak[nt], DK, 16 * rb, YT, 64 * chh + 16 * nt, 16 * J);
         }
       }
 #pragma unroll

@@ -167,17 +167,29 @@ KDA_DEV void mma_row(f32x4 (&acc)[NT], const Panel& A, int m0, const Panel& B, i
 // acc += A[m0:m0+16, k0:k0+16] * B[n0:n0+16, k0:k0+16]^T: a K = 16 product on
 // the K = 32 instruction. Lanes 32..63 carry K = 16..31, which is zeroed (they
 // read the same in-range elements as lanes 0..31, then drop them).
-template <int SPLIT>
+// With AT the A panel stores A transposed, [k][m] (LDS transpose loads; lanes
+// 32..63 again address the rows of lanes 0..31).
+template <int SPLIT, bool AT = false>
 KDA_DEV void mma_k16(f32x4& acc, const Panel& A, int m0, const Panel& B, int n0, int k0) {
   const int l = lane_id();
   const bool on = l < 32;
   const int ko = k0 + ((l >> 4) & 1) * 8;
   const int ar = (m0 + (l & 15)) * A.ld + ko, br = (n0 + (l & 15)) * B.ld + ko;
   const bf16x8 z = {};
-  const bf16x8 ah = on ? *reinterpret_cast<const bf16x8*>(A.hi + ar) : z;
+  auto aload = [&](const bf16* p) -> bf16x8 {
+    if (!AT) return *reinterpret_cast<const bf16x8*>(p + ar);
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int s = l & 15;
+    const bf16* a = p + (k0 + 8 * ((l >> 4) & 1) + (s >> 2)) * A.ld + m0 + 4 * (s & 3);
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 4 * A.ld));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  const bf16x8 ah = on ? aload(A.hi) : z;
   const bf16x8 bh = on ? *reinterpret_cast<const bf16x8*>(B.hi + br) : z;
   if (SPLIT & SPLIT_A) {
-    const bf16x8 al = on ? *reinterpret_cast<const bf16x8*>(A.lo + ar) : z;
+    const bf16x8 al = on ? aload(A.lo) : z;
     acc = mfma16(al, bh, acc);
   }
   if (SPLIT & SPLIT_B) {
@@ -185,13 +197,6 @@ KDA_DEV void mma_k16(f32x4& acc, const Panel& A, int m0, const Panel& B, int n0,
     acc = mfma16(ah, bl, acc);
   }
   acc = mfma16(ah, bh, acc);
-}
-
-// Split-store one fp32 value into a panel.
-KDA_DEV void put(const Panel& P, int row, int col, float x) {
-  const bf16 h = f2bf(x);
-  P.hi[row * P.ld + col] = h;
-  if (P.lo) P.lo[row * P.ld + col] = f2bf(x - bf2f(h));
 }
 
 // Split-store 8 consecutive fp32 values (16-byte aligned destination).
@@ -219,18 +224,6 @@ KDA_DEV void store_tile_t(const f32x4& acc, const Panel& P, int m0, int n0) {
   const int off = (n0 + (l & 15)) * P.ld + m0 + 4 * (l >> 4);
   *reinterpret_cast<bf16x4*>(P.hi + off) = h;
   if (P.lo) *reinterpret_cast<bf16x4*>(P.lo + off) = w;
-}
-
-// D tile at (m0, n0) -> panel laid out [m][n].
-KDA_DEV void store_tile_n(const f32x4& acc, const Panel& P, int m0, int n0) {
-  const int l = lane_id();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) put(P, m0 + 4 * (l >> 4) + i, n0 + (l & 15), acc[i]);
-}
-
-// D tile at (m0, n0) -> panel [m][n] (row-major), hi and lo planes.
-KDA_DEV void store_tile_rowmajor(const f32x4& acc, const Panel& P, int m0, int n0) {
-  store_tile_n(acc, P, m0, n0);
 }
 
 // Split-store 4 consecutive fp32 values (8-byte aligned destination).
