@@ -499,7 +499,6 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   const int rb = w & 3, nw = w >> 2;
   const int j0 = tile * VT;
   const int H = d.H;
-  const int jD = t & 31, rD = 4 * (t >> 5);
   const bf16* BP = reinterpret_cast<const bf16*>(sv.panels);
 
   const Panel KE{&sm.r1.ke.hi[0][0], &sm.r1.ke.lo[0][0], K2_LD};
@@ -512,24 +511,47 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   const Panel DU{&sm.du_hi[0][0], &sm.du_lo[0][0], K2_LD};
   const Panel DR{&sm.dr_hi[0][0], &sm.dr_lo[0][0], K2_LD};
 
+  // Each operand is staged into LDS in the phase before its first use, and
+  // the next chunk's copy of it is requested right after staging, so the
+  // memory requests of a chunk are spread over the four phases of the
+  // previous one instead of queueing in one burst.
   bf16x8 pu[BP_PER_THREAD];
-  bf16 pdo[4];
+  bf16x4 pdo;          // dO, row rO, columns j0 + cO .. + 3
   f32x4 pS[2];         // S_in tiles (rows 16 w, this workgroup's 32 columns)
-  int64_t pt0 = 0;
-  int pn = 0;
-  auto prefetch = [&](int cn) {
-    pt0 = ct.tok[cn];
-    pn = ct.len[cn];
+  const int rO = t >> 3, cO = 4 * (t & 7);
+  // The chunks of a document are consecutive: first token and length follow
+  // from the document's first token and end.
+  int64_t tokA = 0, tEnd = 0;
+  if (c0 < c1) {
+    tokA = ct.tok[c0];
+    tEnd = (int64_t)ct.tok[c1 - 1] + ct.len[c1 - 1];
+  }
+  auto units = [&](int cn, int klo, int khi) {
     const bf16* src = BP + ((int64_t)cn * H + h) * fwd_panel::ELEMS + 8 * t;
 #pragma unroll
     for (int k = 0; k < BP_PER_THREAD; ++k)
-      if (k < BP_PER_THREAD - 1 || t < BP_UNITS - NT_SCAN * (BP_PER_THREAD - 1))
+      if (k >= klo && k < khi && (k < BP_PER_THREAD - 1 || t < BP_UNITS - NT_SCAN * (BP_PER_THREAD - 1)))
         pu[k] = *reinterpret_cast<const bf16x8*>(src + bunit_src(k));
+  };
+  auto stage = [&](int klo, int khi) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = rD + j, rc = rr < pn ? rr : pn - 1;
-      pdo[j] = dO[((pt0 + rc) * H + h) * HD + j0 + jD];
-    }
+    for (int k = 0; k < BP_PER_THREAD; ++k)
+      if (k >= klo && k < khi && (k < BP_PER_THREAD - 1 || t < BP_UNITS - NT_SCAN * (BP_PER_THREAD - 1)))
+        bstage_unit(sm, k, t, pu[k]);
+  };
+  auto rows_in = [&](int cn, int64_t& t0, int& n) {
+    t0 = tokA + (int64_t)CL * (cn - c0);
+    const int64_t left = tEnd - t0;
+    n = left < CL ? (int)left : CL;
+  };
+  auto load_dO = [&](int cn) {
+    int64_t t0;
+    int n;
+    rows_in(cn, t0, n);
+    const int rc = rO < n ? rO : n - 1;
+    pdo = *reinterpret_cast<const bf16x4*>(dO + ((t0 + rc) * H + h) * HD + j0 + cO);
+  };
+  auto load_S = [&](int cn) {
     const float* Sg = sv.S_in + ((int64_t)cn * H + h) * HD * HD;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -542,56 +564,69 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     (&sm.ds_hi[0][0])[e] = f2bf(0.f);
     (&sm.ds_lo[0][0])[e] = f2bf(0.f);
   }
-  if (c0 < c1) prefetch(c1 - 1);
+  // issued in the order of one step's requests, so that the waits counted
+  // for the first step are no stricter than for the later ones
+  if (c0 < c1) {
+    units(c1 - 1, 0, 6);
+    load_dO(c1 - 1);
+    units(c1 - 1, 6, 8);
+    units(c1 - 1, 8, 12);
+    units(c1 - 1, 12, BP_PER_THREAD);
+  }
 
   for (int ci = c1 - 1; ci >= c0; --ci) {
-    const int64_t t0 = pt0;
-    const int n = pn;
+    int64_t t0;
+    int n;
+    rows_in(ci, t0, n);
+    // the next copies are requested on every path (the last chunk reloads
+    // itself) so that the counted waits for them are the same on all paths
+    const int cp = ci > c0 ? ci - 1 : ci;
     const int64_t ch = (int64_t)ci * H + h;
-    // ---- A. operands of this chunk (scale Qd^T waits in registers)
+    // ---- A. Ke^T, A_qk, dO^T into LDS; their next copies requested
+    stage(0, 6);
 #pragma unroll
-    for (int k = 0; k < BP_PER_THREAD; ++k)
-      if ((k < 8 || k >= 12) && (k < BP_PER_THREAD - 1 || t < BP_UNITS - NT_SCAN * (BP_PER_THREAD - 1)))
-        bstage_unit(sm, k, t, pu[k]);
-    bf16x8 qdt[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) qdt[k] = pu[8 + k];
-    const f32x4 Sc0 = pS[0], Sc1 = pS[1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sm.do_hi[jD][rD + j] = (rD + j < n) ? pdo[j] : f2bf(0.f);
-    if (ci - 1 >= c0) prefetch(ci - 1);
+    for (int e = 0; e < 4; ++e) sm.do_hi[cO + e][rO] = rO < n ? pdo[e] : f2bf(0.f);
+    units(cp, 0, 6);
+    load_dO(cp);
     __syncthreads();
     // ---- B. dU~ = scale A_qk^T dO + Ke dS_out   (tile rows 16 rb, cols 16 nw)
-    f32x4 dU = zero4();
-    mma<SPLIT_A, true>(dU, AQ, 16 * rb, DO, 16 * nw, (16 * rb / 32) * 32, CL);
-    mma_k<SPLIT_BW, HD, true>(dU, KE, 16 * rb, DS, 16 * nw);
-    *reinterpret_cast<f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)) = dU;
-    store_tile_t(dU, DU, 16 * rb, 16 * nw);
+    {
+      f32x4 dU = zero4();
+      mma<SPLIT_A, true>(dU, AQ, 16 * rb, DO, 16 * nw, (16 * rb / 32) * 32, CL);
+      mma_k<SPLIT_BW, HD, true>(dU, KE, 16 * rb, DS, 16 * nw);
+      *reinterpret_cast<f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)) = dU;
+      store_tile_t(dU, DU, 16 * rb, 16 * nw);
+    }
+    stage(6, 8);                                   // Tb
+    units(cp, 6, 8);
+    load_S(ci);
     __syncthreads();
-    // ---- C. dR = Tb^T dU~ (= dv); scale Qd^T into the Ke space
+    // ---- C. dR = Tb^T dU~ (= dv); scale Qd, -Kd, e^(G_last) into LDS
     {
       f32x4 acc = zero4();
       mma<SPLIT_BW, true>(acc, TB, 16 * rb, DU, 16 * nw, (16 * rb / 32) * 32, CL);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + drow(i);
-        if (r < n) dv[((t0 + r) * H + h) * HD + j0 + 16 * nw + dcol()] = f2bf(acc[i]);
-      }
       *reinterpret_cast<f32x4*>(bw.dR + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)) = acc;
       store_tile_t(acc, DR, 16 * rb, 16 * nw);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) bstage_unit(sm, 8 + k, t, qdt[k]);
+    stage(8, BP_PER_THREAD);
+    units(cp, 8, 12);
     __syncthreads();
     // ---- D. dS_in = Diag(e^G_last) dS_out + scale Qd^T dO - Kd^T dR
     {
+      // dv = bf16(dR): row rO, columns j0 + cO .. + 3, from the hi plane of dR^T
+      if (rO < n) {
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = sm.dr_hi[cO + e][rO];
+        *reinterpret_cast<bf16x4*>(dv + ((t0 + rO) * H + h) * HD + j0 + cO) = x;
+      }
       float* dSg = bw.dS + ch * HD * HD;
       // d/d e^(G_last)[c] of this workgroup's columns: sum_j dS_out[c][j] S_in[c][j]
+      f32x4 pg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = row_sum16(dS[0][i] * Sc0[i] + dS[1][i] * Sc1[i]);
-        if (dcol() == 0) bw.dgam_part[(ch * NTILE + tile) * HD + 16 * w + drow(i)] = p;
-      }
+      for (int i = 0; i < 4; ++i) pg[i] = row_sum16(dS[0][i] * pS[0][i] + dS[1][i] * pS[1][i]);
+      if (dcol() == 0)
+        *reinterpret_cast<f32x4*>(bw.dgam_part + (ch * NTILE + tile) * HD + 16 * w + drow(0)) = pg;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         *reinterpret_cast<f32x4*>(dSg + tile_off(w, (j0 >> 4) + nt)) = dS[nt];
@@ -601,6 +636,7 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
       mma_row<SPLIT_A, 2, true>(dS, QD, 16 * w, DO, 0, 0, CL);
       mma_row<SPLIT_BW, 2, true>(dS, KD, 16 * w, DR, 0, 0, CL);
     }
+    units(cp, 12, BP_PER_THREAD);
     __syncthreads();
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) store_tile_t(dS[nt], DS, 16 * w, 16 * nt);
