@@ -77,9 +77,12 @@ KDA_DEV float bsel(bool ok, bf16 x) { return ok ? bf2f(x) : 0.f; }
 //   R = V - Kd S_in,  U~ = Tb R,  S_out = e^(G_last) * S_in + Ke^T U~,
 // exchanging operands only through its own LDS area (no barrier). The
 // chunk's shared operands (-Kd, Tb, Ke^T, e^(G_last): the first
-// fwd_panel::CHAIN elements of its panels) are copied global -> LDS with
-// asynchronous 16-byte DMA, one chunk ahead into the other of two buffers,
-// so the only barrier per chunk is the one that hands a buffer over.
+// fwd_panel::CHAIN elements of its panels) and its V rows are copied
+// global -> LDS with asynchronous 16-byte DMA, one chunk ahead into the other
+// of two buffers, so the only barrier per chunk is the one that hands a
+// buffer over. The copies are issued in three groups after the products that
+// read this wave's own B panels (the compiler then orders no LDS read behind
+// them), so that they queue behind compute instead of stalling it.
 // S_in, R (when saving for the backward) and U~ go to memory; the output
 // O = Qd S_in + A_qk U~ is formed afterwards by fwd_out_kernel, in parallel
 // over chunks.
@@ -97,6 +100,7 @@ struct __attribute__((aligned(16))) ChainBuf {
   bf16 tb[CL * CL];          // Tb   [r][i], row 128 B, chunk ^= (r >> 1) & 7
   bf16 ke[2][HD * CL];       // Ke^T [c][r] hi, lo, as tb
   float gam[HD];
+  bf16 v[CL * VT];           // V    [r][j] of the workgroup's 32 columns, row 64 B
 };
 struct __attribute__((aligned(16))) SliceBuf {            // one wave's B operands
   bf16 s_hi[16][K1_LD];                      // S^T [j][c]
@@ -120,12 +124,14 @@ KDA_DEV bf16x8 frag128(const bf16* p, int m0, int k) {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Asynchronous copy of chunk `src`'s chain operands into `dst` (this thread's
-// share: units t + 128 k). Lane l of each instruction lands at 16 l.
+// share: units t + 128 k, k in [KLO, KHI)). Lane l of each instruction lands
+// at 16 l.
+template <int KLO, int KHI>
 KDA_DEV void chain_dma(ChainBuf& dst, const bf16* __restrict__ src, int t) {
   char* base = reinterpret_cast<char*>(&dst);
   const int w = t >> 6;
 #pragma unroll
-  for (int k = 0; k < FS_PER_THREAD; ++k) {
+  for (int k = KLO; k < KHI; ++k) {
     const int u = t + FS_THREADS * k;
     int e;                                   // source element of the unit
     if (k < 8) {
@@ -144,6 +150,21 @@ KDA_DEV void chain_dma(ChainBuf& dst, const bf16* __restrict__ src, int t) {
       __builtin_amdgcn_global_load_lds(src + e,
                                        (lds_void*)(base + 16 * (FS_THREADS * k + 64 * w)), 16, 0,
                                        0);
+  }
+}
+
+// Asynchronous copy of V rows t0 .. t0 + 63 (rows from n on repeat row n - 1;
+// they are masked when read), columns j0 .. j0 + 31, into dst.v: unit
+// u = t + 128 k is row u / 4, columns j0 + 8 (u % 4) .. + 7.
+KDA_DEV void v_dma(ChainBuf& dst, const bf16* __restrict__ v, int64_t t0, int n, int H, int h,
+                   int j0, int t) {
+  char* base = reinterpret_cast<char*>(dst.v);
+  const int w = t >> 6;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = t + FS_THREADS * k, r = u >> 2, rc = r < n ? r : n - 1;
+    __builtin_amdgcn_global_load_lds(v + ((t0 + rc) * H + h) * HD + j0 + 8 * (u & 3),
+                                     (lds_void*)(base + 16 * (FS_THREADS * k + 64 * w)), 16, 0, 0);
   }
 }
 
@@ -171,42 +192,44 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
   f32x4 S[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) S[m] = zero4();
-  // V of the next chunk at this lane's R elements (rows 16 rb + drow(i))
-  bf16 pv[4][4];
-  int64_t pt0 = 0;
-  int pn = 0;
-  // V loads of chunk cn; its table entry (pt0, pn) must be in registers already
-  auto prefetch_v = [&](int cn) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + drow(i), rc = r < pn ? r : pn - 1;
-        pv[rb][i] = v[((pt0 + rc) * H + h) * HD + jv + dcol()];
-      }
+  // The chunks of a document are consecutive: first token and length follow
+  // from the document's first token and end.
+  int64_t tokA = 0, tEnd = 0;
+  if (c0 < c1) {
+    tokA = ct.tok[c0];
+    tEnd = (int64_t)ct.tok[c1 - 1] + ct.len[c1 - 1];
+  }
+  auto rows_in = [&](int cn, int64_t& t0, int& n) {
+    t0 = tokA + (int64_t)CL * (cn - c0);
+    const int64_t left = tEnd - t0;
+    n = left < CL ? (int)left : CL;
   };
   auto panel_of = [&](int cn) { return panels + ((int64_t)cn * H + h) * fwd_panel::ELEMS; };
 
   auto step = [&](ChainBuf& cur, ChainBuf& nxt, int ci) {
-    const int64_t t0 = pt0;
-    const int n = pn;
+    int64_t t0;
+    int n;
+    rows_in(ci, t0, n);
     const int64_t ch = (int64_t)ci * H + h;
-    f32x4 R[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) R[rb][i] = bsel(16 * rb + drow(i) < n, pv[rb][i]);
-    // the next chunk's table entry, read before the wait below so that no later
-    // wait for it also waits for the next chunk's copies
-    if (ci + 1 < c1) {
-      pt0 = ct.tok[ci + 1];
-      pn = ct.len[ci + 1];
-    }
+    const bool more = ci + 1 < c1;
+    const bf16* nsrc = panel_of(more ? ci + 1 : ci);
     __builtin_amdgcn_s_waitcnt(0);     // this thread's copies of `cur` have landed
     __syncthreads();                   // ... and the other wave's; `nxt` is free
-    if (ci + 1 < c1) {
-      chain_dma(nxt, panel_of(ci + 1), t);
-      prefetch_v(ci + 1);
+    // R starts as V (D layout) through transpose loads of cur.v
+    f32x4 R[4];
+    {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const int l = lane_id(), sl = l & 15;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int r0 = 16 * rb + 4 * (l >> 4);
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(cur.v + (r0 + (sl >> 2)) * VT + 16 * w + 4 * (sl & 3)));
+        const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) R[rb][i] = r0 + i < n ? bf2f(xb[i]) : 0.f;
+      }
     }
     // S_in: to memory and, as B operand, to this wave's LDS
     {
@@ -223,6 +246,13 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
       const bf16x8 b = frag(SB.hi, SB.ld, 0, k);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) R[rb] = mfma16(frag256(cur.kd, 16 * rb, k), b, R[rb]);
+    }
+    if (more) {
+      int64_t u0;
+      int un;
+      rows_in(ci + 1, u0, un);
+      v_dma(nxt, v, u0, un, H, h, tile * VT, t);
+      chain_dma<0, 12>(nxt, nsrc, t);
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -246,6 +276,7 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
         }
       }
     }
+    if (more) chain_dma<12, 22>(nxt, nsrc, t);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       *reinterpret_cast<f32x4*>(sv.U + ch * CL * HD + tile_off(rb, jv >> 4)) = U[rb];
@@ -268,14 +299,16 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
         S[m] = mfma16(ah, bl, S[m]);
         S[m] = mfma16(ah, bh, S[m]);
       }
+      if (k == 0 && more) chain_dma<22, FS_PER_THREAD>(nxt, nsrc, t);
     }
   };
 
   if (c0 < c1) {
-    pt0 = ct.tok[c0];
-    pn = ct.len[c0];
-    chain_dma(bufA, panel_of(c0), t);
-    prefetch_v(c0);
+    int64_t u0;
+    int un;
+    rows_in(c0, u0, un);
+    v_dma(bufA, v, u0, un, H, h, tile * VT, t);
+    chain_dma<0, FS_PER_THREAD>(bufA, panel_of(c0), t);
   }
   for (int ci = c0; ci < c1; ci += 2) {
     step(bufA, bufB, ci);
