@@ -72,21 +72,19 @@ KDA_DEV float bsel(bool ok, bf16 x) { return ok ? bf2f(x) : 0.f; }
 
 // ------------------------------------------------------------------ forward
 // The sequential state chain of one (document, head) and 32 state columns.
-// Two waves, one per 16-column slice: each wave runs the whole chain of its
-// slice by itself,
+// Two compute waves, one per 16-column slice: each runs the whole chain of
+// its slice by itself,
 //   R = V - Kd S_in,  U~ = Tb R,  S_out = e^(G_last) * S_in + Ke^T U~,
-// exchanging operands only through its own LDS area (no barrier). The
-// chunk's shared operands (-Kd, Tb, Ke^T, e^(G_last): the first
-// fwd_panel::CHAIN elements of its panels) and its V rows are copied
-// global -> LDS with asynchronous 16-byte DMA, one chunk ahead into the other
-// of two buffers, so the only barrier per chunk is the one that hands a
-// buffer over. The copies are issued in three groups after the products that
-// read this wave's own B panels (the compiler then orders no LDS read behind
-// them), so that they queue behind compute instead of stalling it.
+// exchanging operands only through its own LDS area. Two copy waves (on the
+// compute unit's other two SIMDs) bring the chunk's shared operands (-Kd, Tb,
+// Ke^T, e^(G_last): the first fwd_panel::CHAIN elements of its panels) and
+// its V rows global -> LDS with asynchronous 16-byte DMA, one chunk ahead into
+// the other of two buffers; the only barrier per chunk hands a buffer over.
+// The compute waves thus never wait behind the copies at instruction issue.
 // S_in, R (when saving for the backward) and U~ go to memory; the output
 // O = Qd S_in + A_qk U~ is formed afterwards by fwd_out_kernel, in parallel
 // over chunks.
-constexpr int FS_THREADS = 128;
+constexpr int FS_THREADS = 128;                       // copy waves (and compute waves)
 constexpr int FS_UNITS = fwd_panel::CHAIN / 8;          // 16-byte units: 3616
 constexpr int FS_PER_THREAD = (FS_UNITS + FS_THREADS - 1) / FS_THREADS;   // 29
 static_assert(fwd_panel::KD == 0 && fwd_panel::TB == 1024 * 8 && fwd_panel::KE == 1536 * 8 &&
@@ -168,7 +166,7 @@ KDA_DEV void v_dma(ChainBuf& dst, const bf16* __restrict__ v, int64_t t0, int n,
   }
 }
 
-__global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
+__global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
                                                                SavedSet sv,
                                                                const bf16* __restrict__ panels,
                                                                int save_R) {
@@ -180,10 +178,10 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
   const int doc = pair / d.H, h = pair % d.H;
   const int c0 = ct.doc_c0[doc], c1 = ct.doc_c0[doc + 1];
   const int t = threadIdx.x, w = wave_id();
-  const int jv = tile * VT + 16 * w;          // this wave's 16 state columns
+  const int jv = tile * VT + 16 * (w & 1);    // a compute wave's 16 state columns
   const int H = d.H;
   const bf16* v = reinterpret_cast<const bf16*>(in.v);
-  SliceBuf& sb = slice[w];
+  SliceBuf& sb = slice[w & 1];
   const Panel SB{&sb.s_hi[0][0], nullptr, K1_LD};
   const Panel RB{&sb.r_hi[0][0], &sb.r_lo[0][0], K2_LD};
   const Panel UB{&sb.u_hi[0][0], &sb.u_lo[0][0], K2_LD};
@@ -206,15 +204,12 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
   };
   auto panel_of = [&](int cn) { return panels + ((int64_t)cn * H + h) * fwd_panel::ELEMS; };
 
-  auto step = [&](ChainBuf& cur, ChainBuf& nxt, int ci) {
+  auto step = [&](ChainBuf& cur, int ci) {
     int64_t t0;
     int n;
     rows_in(ci, t0, n);
     const int64_t ch = (int64_t)ci * H + h;
-    const bool more = ci + 1 < c1;
-    const bf16* nsrc = panel_of(more ? ci + 1 : ci);
-    __builtin_amdgcn_s_waitcnt(0);     // this thread's copies of `cur` have landed
-    __syncthreads();                   // ... and the other wave's; `nxt` is free
+    __syncthreads();                   // `cur` has landed
     // R starts as V (D layout) through transpose loads of cur.v
     f32x4 R[4];
     {
@@ -247,13 +242,6 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) R[rb] = mfma16(frag256(cur.kd, 16 * rb, k), b, R[rb]);
     }
-    if (more) {
-      int64_t u0;
-      int un;
-      rows_in(ci + 1, u0, un);
-      v_dma(nxt, v, u0, un, H, h, tile * VT, t);
-      chain_dma<0, 12>(nxt, nsrc, t);
-    }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       if (save_R) *reinterpret_cast<f32x4*>(sv.R + ch * CL * HD + tile_off(rb, jv >> 4)) = R[rb];
@@ -276,7 +264,6 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
         }
       }
     }
-    if (more) chain_dma<12, 22>(nxt, nsrc, t);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       *reinterpret_cast<f32x4*>(sv.U + ch * CL * HD + tile_off(rb, jv >> 4)) = U[rb];
@@ -299,26 +286,40 @@ __global__ __launch_bounds__(FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in,
         S[m] = mfma16(ah, bl, S[m]);
         S[m] = mfma16(ah, bh, S[m]);
       }
-      if (k == 0 && more) chain_dma<22, FS_PER_THREAD>(nxt, nsrc, t);
     }
   };
 
-  if (c0 < c1) {
-    int64_t u0;
-    int un;
-    rows_in(c0, u0, un);
-    v_dma(bufA, v, u0, un, H, h, tile * VT, t);
-    chain_dma<0, FS_PER_THREAD>(bufA, panel_of(c0), t);
+  if (w >= 2) {
+    // copy waves: chunk ci + 1 into the buffer freed by the barrier of step ci
+    const int tp = t - FS_THREADS;
+    auto fill = [&](ChainBuf& dst, int cn) {
+      int64_t u0;
+      int un;
+      rows_in(cn, u0, un);
+      v_dma(dst, v, u0, un, H, h, tile * VT, tp);
+      chain_dma<0, FS_PER_THREAD>(dst, panel_of(cn), tp);
+      __builtin_amdgcn_s_waitcnt(0);
+    };
+    if (c0 < c1) fill(bufA, c0);
+    for (int ci = c0; ci < c1; ci += 2) {
+      __syncthreads();
+      if (ci + 1 < c1) fill(bufB, ci + 1);
+      if (ci + 1 < c1) {
+        __syncthreads();
+        if (ci + 2 < c1) fill(bufA, ci + 2);
+      }
+    }
+    return;
   }
   for (int ci = c0; ci < c1; ci += 2) {
-    step(bufA, bufB, ci);
-    if (ci + 1 < c1) step(bufB, bufA, ci + 1);
+    step(bufA, ci);
+    if (ci + 1 < c1) step(bufB, ci + 1);
   }
 }
 
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, const void* panels, int save_R, hipStream_t s) {
-  hipLaunchKernelGGL(fwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(FS_THREADS), 0, s, d, in,
+  hipLaunchKernelGGL(fwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(2 * FS_THREADS), 0, s, d, in,
                      ct, sv, reinterpret_cast<const bf16*>(panels), save_R);
   return hipGetLastError();
 }
