@@ -78,8 +78,9 @@ KDA_DEV float bsel(bool ok, bf16 x) { return ok ? bf2f(x) : 0.f; }
 // exchanging operands only through its own LDS area. Two copy waves (on the
 // compute unit's other two SIMDs) bring the chunk's shared operands (-Kd, Tb,
 // Ke^T, e^(G_last): the first fwd_panel::CHAIN elements of its panels) and
-// its V rows global -> LDS with asynchronous 16-byte DMA, one chunk ahead into
-// the other of two buffers; the only barrier per chunk hands a buffer over.
+// its V rows global -> registers -> LDS (16-byte units): registers two chunks
+// ahead, LDS one chunk ahead in the other of two buffers; the only barrier per
+// chunk hands a buffer over.
 // The compute waves thus never wait behind the copies at instruction issue.
 // S_in, R (when saving for the backward) and U~ go to memory; the output
 // O = Qd S_in + A_qk U~ is formed afterwards by fwd_out_kernel, in parallel
@@ -119,51 +120,22 @@ KDA_DEV bf16x8 frag128(const bf16* p, int m0, int k) {
   return *reinterpret_cast<const bf16x8*>(p + swz128(row, (k >> 3) + (l >> 4)));
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Asynchronous copy of chunk `src`'s chain operands into `dst` (this thread's
-// share: units t + 128 k, k in [KLO, KHI)). Lane l of each instruction lands
-// at 16 l.
-template <int KLO, int KHI>
-KDA_DEV void chain_dma(ChainBuf& dst, const bf16* __restrict__ src, int t) {
-  char* base = reinterpret_cast<char*>(&dst);
-  const int w = t >> 6;
-#pragma unroll
-  for (int k = KLO; k < KHI; ++k) {
-    const int u = t + FS_THREADS * k;
-    int e;                                   // source element of the unit
-    if (k < 8) {
-      const int row = u >> 4;
-      e = fwd_panel::KD + row * 128 + (((u & 15) ^ (row & 15)) << 3);
-    } else if (k < 12) {
-      const int v = u - 1024, row = v >> 3;
-      e = fwd_panel::TB + row * 64 + (((v & 7) ^ ((row >> 1) & 7)) << 3);
-    } else if (k < 28) {
-      const int v = u - 1536, pl = v >> 10, row = (v >> 3) & 127;
-      e = fwd_panel::KE + pl * (HD * CL) + row * 64 + (((v & 7) ^ ((row >> 1) & 7)) << 3);
-    } else {
-      e = fwd_panel::GAM + (u - 3584) * 8;
-    }
-    if (k < FS_PER_THREAD - 1 || u < FS_UNITS)
-      __builtin_amdgcn_global_load_lds(src + e,
-                                       (lds_void*)(base + 16 * (FS_THREADS * k + 64 * w)), 16, 0,
-                                       0);
+// Source element (in the chunk's panels) of chain unit u = t + 128 k; the
+// unit lands at byte 16 u of a ChainBuf.
+KDA_DEV int chain_src(int k, int u) {
+  if (k < 8) {
+    const int row = u >> 4;
+    return fwd_panel::KD + row * 128 + (((u & 15) ^ (row & 15)) << 3);
   }
-}
-
-// Asynchronous copy of V rows t0 .. t0 + 63 (rows from n on repeat row n - 1;
-// they are masked when read), columns j0 .. j0 + 31, into dst.v: unit
-// u = t + 128 k is row u / 4, columns j0 + 8 (u % 4) .. + 7.
-KDA_DEV void v_dma(ChainBuf& dst, const bf16* __restrict__ v, int64_t t0, int n, int H, int h,
-                   int j0, int t) {
-  char* base = reinterpret_cast<char*>(dst.v);
-  const int w = t >> 6;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int u = t + FS_THREADS * k, r = u >> 2, rc = r < n ? r : n - 1;
-    __builtin_amdgcn_global_load_lds(v + ((t0 + rc) * H + h) * HD + j0 + 8 * (u & 3),
-                                     (lds_void*)(base + 16 * (FS_THREADS * k + 64 * w)), 16, 0, 0);
+  if (k < 12) {
+    const int v = u - 1024, row = v >> 3;
+    return fwd_panel::TB + row * 64 + (((v & 7) ^ ((row >> 1) & 7)) << 3);
   }
+  if (k < 28) {
+    const int v = u - 1536, pl = v >> 10, row = (v >> 3) & 127;
+    return fwd_panel::KE + pl * (HD * CL) + row * 64 + (((v & 7) ^ ((row >> 1) & 7)) << 3);
+  }
+  return fwd_panel::GAM + (u - 3584) * 8;
 }
 
 __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
@@ -290,23 +262,59 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
   };
 
   if (w >= 2) {
-    // copy waves: chunk ci + 1 into the buffer freed by the barrier of step ci
+    // copy waves
     const int tp = t - FS_THREADS;
-    auto fill = [&](ChainBuf& dst, int cn) {
+    // Chunk cn + 1 is written from registers into the buffer freed at the
+    // start of step cn, then chunk cn + 2 is requested into the registers:
+    // each load has a whole step to arrive. V rows from n on repeat row n - 1
+    // (masked when read); V unit u is row u / 4, columns j0 + 8 (u % 4).
+    bf16x8 x[FS_PER_THREAD + 2];
+    auto load = [&](int cn) {
       int64_t u0;
       int un;
       rows_in(cn, u0, un);
-      v_dma(dst, v, u0, un, H, h, tile * VT, tp);
-      chain_dma<0, FS_PER_THREAD>(dst, panel_of(cn), tp);
-      __builtin_amdgcn_s_waitcnt(0);
+      const bf16* src = panel_of(cn);
+#pragma unroll
+      for (int k = 0; k < FS_PER_THREAD; ++k) {
+        const int u = tp + FS_THREADS * k;
+        if (k < FS_PER_THREAD - 1 || u < FS_UNITS)
+          x[k] = *reinterpret_cast<const bf16x8*>(src + chain_src(k, u));
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int u = tp + FS_THREADS * k, r = u >> 2, rc = r < un ? r : un - 1;
+        x[FS_PER_THREAD + k] =
+            *reinterpret_cast<const bf16x8*>(v + ((u0 + rc) * H + h) * HD + tile * VT + 8 * (u & 3));
+      }
     };
-    if (c0 < c1) fill(bufA, c0);
+    auto store = [&](ChainBuf& dst) {
+      char* base = reinterpret_cast<char*>(&dst);
+#pragma unroll
+      for (int k = 0; k < FS_PER_THREAD; ++k) {
+        const int u = tp + FS_THREADS * k;
+        if (k < FS_PER_THREAD - 1 || u < FS_UNITS)
+          *reinterpret_cast<bf16x8*>(base + 16 * u) = x[k];
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(dst.v) + 16 * (tp + FS_THREADS * k)) =
+            x[FS_PER_THREAD + k];
+    };
+    if (c0 < c1) {
+      load(c0);
+      store(bufA);
+    }
+    if (c0 + 1 < c1) load(c0 + 1);
     for (int ci = c0; ci < c1; ci += 2) {
       __syncthreads();
-      if (ci + 1 < c1) fill(bufB, ci + 1);
       if (ci + 1 < c1) {
+        store(bufB);
+        if (ci + 2 < c1) load(ci + 2);
         __syncthreads();
-        if (ci + 2 < c1) fill(bufA, ci + 2);
+        if (ci + 2 < c1) {
+          store(bufA);
+          if (ci + 3 < c1) load(ci + 3);
+        }
       }
     }
     return;
