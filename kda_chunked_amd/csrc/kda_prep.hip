@@ -473,27 +473,34 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     for (int r = 0; r < 16; ++r) Tm[16 * I + r][16 * I + j] = x[r];
   }
   __syncthreads();
+  // Off-diagonal blocks by distance: T_IJ = -T_II sum_{m = J .. I-1} B_Im T_mJ
+  // with B = Diag(beta) A_kk, one wave per block, on fp32 MFMA (exact
+  // products, fp32 sums). Z = sum B_Im T_mJ passes through the wave's own LDS
+  // rows to become the B operand of T_II Z.
+#pragma unroll
   for (int dist = 1; dist < 4; ++dist) {
-    // the (4 - dist) blocks of this distance in parallel, 256 threads each
-    const int nb = 4 - dist;
-    const int bsel = t >> 8, r = (t >> 4) & 15, j = t & 15;
-    for (int J0 = 0; J0 < nb; J0 += 2) {
-      const int J = J0 + bsel;
-      const int I = J + dist;
-      if (J < nb) {
-        float z = 0.f;
-        for (int m = 16 * J; m < 16 * I; ++m)
-          z += sm.beta[16 * I + r] * sm.Akk[16 * I + r][m] * Tm[m][16 * J + j];
-        sm.Z[bsel][r][j] = z;
+    if (w < 4 - dist) {
+      const int J = w, I = J + dist, lr = l & 15, lk = l >> 4;
+      const float bI = sm.beta[16 * I + lr];
+      f32x4 z = zero4();
+#pragma unroll
+      for (int s4 = 0; s4 < 4 * dist; ++s4) {
+        const int m = 16 * J + 4 * s4 + lk;
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(bI * sm.Akk[16 * I + lr][m], Tm[m][16 * J + lr], z,
+                                                 0, 0, 0);
       }
-      __syncthreads();
-      if (J < nb) {
-        float s2 = 0.f;
-        for (int m = 0; m < 16; ++m) s2 += Tm[16 * I + r][16 * I + m] * sm.Z[bsel][m][j];
-        Tm[16 * I + r][16 * J + j] = -s2;
-      }
-      __syncthreads();
+      float (*Zw)[17] = sm.Z[w];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Zw[4 * lk + i][lr] = z[i];
+      f32x4 x = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 16; kb += 4)
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(Tm[16 * I + lr][16 * I + kb + lk], Zw[kb + lk][lr], x,
+                                                 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tm[16 * I + 4 * lk + i][16 * J + lr] = -x[i];
     }
+    __syncthreads();
   }
 
   // ---- 5. saved matrices (fp32) and the forward scan's operand panels

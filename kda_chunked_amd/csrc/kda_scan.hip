@@ -679,9 +679,10 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
       mma_row<SPLIT_BW, 2, true>(dS, KD, 16 * w, DR, 0, 0, CL);
     }
     units(cp, 12, BP_PER_THREAD);
-    __syncthreads();
+    // dS^T is read only in phase B: its panel is written before the barrier
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) store_tile_t(dS[nt], DS, 16 * w, 16 * nt);
+    __syncthreads();
   }
 }
 
