@@ -161,6 +161,10 @@ KDA_DEV void decayed_frag(const PrepSmem& sm, const bf16 (*x)[XS_LD], float rx, 
   }
 }
 
+// RAW: the gate input is the raw a (bf16) of g = -exp(A_log) softplus(a + dt_bias)
+// rather than g itself (fp32); a template parameter so that neither form
+// carries the other's registers through the chunk loop.
+template <bool RAW>
 __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, ChunkTable ct,
                                                             float* __restrict__ G_out,
                                                             SavedSet sv, bf16* __restrict__ panels,
@@ -178,19 +182,20 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   // One chunk's raw inputs. Thread t: q, k of row rA, channels cA .. cA+15;
   // the gate of channel cG = t & 127, rows 16 qG .. 16 qG + 15; beta of row t.
   // The workgroup walks the chunks ci, ci + gridDim.x, ... of head h and loads
-  // the next chunk's inputs while it works on the current one.
+  // the next chunk's inputs while it works on the current one; the chunk
+  // table entries are read one chunk earlier still, and the raw gate stays
+  // bf16 until it is used, so that no wait follows the requests.
   bf16x8 q0, q1, k0, k1;
   float g[16], eg[16];
+  bf16 ga[16];
   bf16 bt = f2bf(0.f);
-  auto load_raw = [&](int cn) {
-    const int64_t u0 = ct.tok[cn];
-    const int un = ct.len[cn];
+  auto load_raw = [&](int64_t u0, int un) {
     const int64_t baseA = ((u0 + (rA < un ? rA : un - 1)) * H + h) * HD + cA;
     q0 = *reinterpret_cast<const bf16x8*>(q + baseA);
     q1 = *reinterpret_cast<const bf16x8*>(q + baseA + 8);
     k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
     k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
-    if (!d.raw) {
+    if (!RAW) {
       const float* gp = reinterpret_cast<const float*>(in.gate);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -202,14 +207,28 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = 16 * qG + j;
-        g[j] = bf2f(ap[((u0 + (r < un ? r : un - 1)) * H + h) * HD + cG]);
+        ga[j] = ap[((u0 + (r < un ? r : un - 1)) * H + h) * HD + cG];
       }
     }
     if (t < CL) bt = beta[(u0 + (t < un ? t : un - 1)) * H + h];
   };
   int ci = blockIdx.x;
   if (ci >= nch) return;
-  load_raw(ci);
+  const int gx = gridDim.x;
+  int64_t t0 = ct.tok[ci];
+  int n = ct.len[ci];
+  load_raw(t0, n);
+  // raw gate parameters of this head and thread channel cG
+  const float ea = RAW ? __expf(in.A_log[h]) : 0.f;
+  const float dtb = RAW ? in.dt_bias[h * HD + cG] : 0.f;
+  // table entry of the next chunk this workgroup takes (the last chunk when
+  // there is none: its loads are then repeated, never used)
+  int64_t nt0 = ct.tok[min(ci + gx, nch - 1)];
+  int nn = ct.len[min(ci + gx, nch - 1)];
+  // nothing is in flight when the loop is entered, so the waits counted at
+  // its top follow the steady state (loads requested before the stores of
+  // the previous chunk) and not the shorter entry path
+  __builtin_amdgcn_s_waitcnt(0);
   for (;;) {
   // indices re-derived from an opaque copy of the thread id in every
   // iteration: otherwise the unrolled phases' LDS addresses are hoisted out of
@@ -219,8 +238,6 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   const int t = tt, w = tt >> 6, l = tt & 63;
   const int rA = t >> 3, cA = 16 * (t & 7);
   const int cG = t & 127, qG = t >> 7;
-  const int64_t t0 = ct.tok[ci];
-  const int n = ct.len[ci];
   const int64_t ch = (int64_t)ci * H + h;
 
   // ---- 1. this chunk's raw inputs into LDS, L2 partial sums
@@ -244,13 +261,11 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   // ---- 2. chunk-local cumsum of g in registers (16 rows per thread), then
   // the carry of the earlier row quarters
   {
-    const float ea = d.raw ? __expf(in.A_log[h]) : 0.f;
-    const float dtb = d.raw ? in.dt_bias[h * HD + cG] : 0.f;
     float run = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      float x = g[j];
-      if (d.raw) x = -ea * softplus(x + dtb);
+      float x = RAW ? bf2f(ga[j]) : g[j];
+      if (RAW) x = -ea * softplus(x + dtb);
       x = (16 * qG + j < n) ? x : 0.f;
       run += x;
       g[j] = run;
@@ -451,8 +466,11 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   }
   __syncthreads();
 
-  // the next chunk's raw inputs, in flight during the solve and the writes
-  if (ci + (int)gridDim.x < nch) load_raw(ci + gridDim.x);
+  // the next chunk's raw inputs, in flight during the solve and the writes,
+  // and the table entry of the chunk after it
+  load_raw(nt0, nn);
+  const int64_t nt0b = ct.tok[min(ci + 2 * gx, nch - 1)];
+  const int nnb = ct.len[min(ci + 2 * gx, nch - 1)];
 
   // ---- 4. T = (I + Diag(beta) A_kk)^-1 by 16x16 blocks, fp32
   float (*Tm)[F_LD] = sm.Tm;
@@ -583,8 +601,12 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     }
     if (t < HD) reinterpret_cast<float*>(P + fwd_panel::GAM)[t] = fexp(sm.Gref[4][t]);
   }
-  ci += gridDim.x;
+  ci += gx;
   if (ci >= nch) break;
+  t0 = nt0;
+  n = nn;
+  nt0 = nt0b;
+  nn = nnb;
   __syncthreads();     // the next chunk's first phase overwrites what was read above
   }
 }
@@ -593,8 +615,12 @@ hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct
                            const SavedSet& sv, int with_bwd, hipStream_t s) {
   // about one workgroup per CU (the LDS allows one), each walking chunks of one head
   const int gx = std::max(1, std::min(d.NC, (kPrepWorkgroups + d.H - 1) / d.H));
-  hipLaunchKernelGGL(fwd_prep_kernel, dim3(gx, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
-                     reinterpret_cast<bf16*>(sv.panels), with_bwd);
+  if (d.raw)
+    hipLaunchKernelGGL(fwd_prep_kernel<true>, dim3(gx, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
+                       reinterpret_cast<bf16*>(sv.panels), with_bwd);
+  else
+    hipLaunchKernelGGL(fwd_prep_kernel<false>, dim3(gx, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
+                       reinterpret_cast<bf16*>(sv.panels), with_bwd);
   return hipGetLastError();
 }
 
