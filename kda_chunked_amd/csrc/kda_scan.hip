@@ -339,6 +339,7 @@ hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct
 struct FwdOutSmem {
   bf16 s_hi[HD][K1_LD], s_lo[HD][K1_LD];     // S_in^T [j][c]
   bf16 u_hi[HD][K2_LD], u_lo[HD][K2_LD];     // U~^T   [j][i]
+  bf16 ot[CL][K1_LD];                        // O [r][c] of the chunk, to rows of 16-byte stores
 };
 
 KDA_DEV bf16x8 gfrag(const bf16* p, int ld, int m0, int k) {
@@ -385,28 +386,51 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Dims d, ChunkTable ct,
   };
   int ci = blockIdx.x;
   if (ci >= nch) return;
-  load_chunk(ci);
-  for (;;) {
-    // indices from an opaque copy of the thread id in every iteration, so that
-    // LDS addresses are not hoisted out of the loop and held in registers
+  const int gx = gridDim.x;
+  int64_t t0 = ct.tok[ci];
+  int n = ct.len[ci];
+  // O of a chunk leaves through sm.ot after the barrier that follows its
+  // products: thread t writes row t / 8, columns 16 (t % 8) .. + 15
+  auto store_o = [&](int64_t ot0, int on) {
+    const int t = threadIdx.x, r = t >> 3, c = 16 * (t & 7);
+    if (r < on) {
+      bf16* dst = o + ((ot0 + r) * H + h) * HD + c;
+      *reinterpret_cast<bf16x8*>(dst) = *reinterpret_cast<const bf16x8*>(&sm.ot[r][c]);
+      *reinterpret_cast<bf16x8*>(dst + 8) = *reinterpret_cast<const bf16x8*>(&sm.ot[r][c + 8]);
+    }
+  };
+  // S_in [c][j] -> S_in^T panel, U~ [i][j] -> U~^T panel, A fragments to the
+  // registers the products read: the loaded values are consumed before the
+  // loop closes, so that no load is still in flight across its back edge
+  bf16x8 aq[4][2], aa[2][2];
+  auto stage = [&]() {
+    // indices from an opaque copy of the thread id, so that LDS addresses
+    // are not hoisted out of the loop and held in registers
     int tt = threadIdx.x;
     asm volatile("" : "+v"(tt));
-    const int w = tt >> 6, rb = w & 3, chh = w >> 2;
-    const int64_t t0 = ct.tok[ci];
-    const int n = ct.len[ci];
-    // S_in [c][j] -> S_in^T panel; U~ [i][j] -> U~^T panel
+    const int w = tt >> 6;
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) store_tile_t(xs[jb], SP, 16 * w, 16 * jb);
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) store_tile_t(xu[ib], UP, 16 * ib, 16 * w);
-    bf16x8 aq[4][2], aa[2][2];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) aq[kk][0] = fq[kk][0], aq[kk][1] = fq[kk][1];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) aa[kk][0] = fa[kk][0], aa[kk][1] = fa[kk][1];
-    __syncthreads();
-    const int cn = ci + gridDim.x;
-    if (cn < nch) load_chunk(cn);
+  };
+  load_chunk(ci);
+  stage();
+  __syncthreads();
+  for (;;) {
+    int tt = threadIdx.x;
+    asm volatile("" : "+v"(tt));
+    const int w = tt >> 6, rb = w & 3, chh = w >> 2;
+    // the next chunk's operands and table entry, requested on every path
+    // (the last chunk reloads itself)
+    const int cn = min(ci + gx, nch - 1);
+    const int64_t nt0 = ct.tok[cn];
+    const int nn = ct.len[cn];
+    load_chunk(cn);
     f32x4 acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
@@ -438,17 +462,17 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Dims d, ChunkTable ct,
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rb + drow(i);
-      if (r < n) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          o[((t0 + r) * H + h) * HD + 64 * chh + 16 * nt + dcol()] = f2bf(acc[nt][i]);
-      }
-    }
-    if (cn >= nch) break;
-    ci = cn;
-    __syncthreads();   // the next chunk's panels overwrite the ones read above
+      for (int nt = 0; nt < 4; ++nt) sm.ot[16 * rb + drow(i)][64 * chh + 16 * nt + dcol()] = f2bf(acc[nt][i]);
+    __syncthreads();   // the panels are free again and O is complete in sm.ot
+    store_o(t0, n);
+    if (ci + gx >= nch) break;
+    stage();
+    ci += gx;
+    t0 = nt0;
+    n = nn;
+    __syncthreads();
   }
 }
 
