@@ -136,6 +136,10 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   const int rb = w & 3, chh = w >> 2;          // row block, channel half
   const int64_t ch = (int64_t)ci * d.H + h;
   const int H = d.H;
+  // raw gate parameters of channel t & 127 (the last phase's column), read
+  // here so that no wait for them falls in that phase
+  const float ea7 = d.raw ? __expf(in.A_log[h]) : 0.f;
+  const float dtb7 = d.raw ? in.dt_bias[h * HD + (t & 127)] : 0.f;
   const bf16* q = reinterpret_cast<const bf16*>(in.q);
   const bf16* k = reinterpret_cast<const bf16*>(in.k);
   const bf16* beta = reinterpret_cast<const bf16*>(in.beta);
@@ -735,24 +739,31 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     float carry = 0.f;
     for (int I2 = 3; I2 > I; --I2) carry += sm.u.p7.tot[I2][cc];
     for (int I2 = 0; I2 < I; ++I2) carry += sm.u.p7.totP[I2][cc];
+    // every value first, then the stores: a store between two uses of the
+    // loaded a would make each use wait for it
     float pdt = 0.f, pA = 0.f;
-    const float ea = d.raw ? __expf(in.A_log[h]) : 0.f;
-    const float dtb = d.raw ? in.dt_bias[h * HD + cc] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float dg = 16 * I + j < n ? v[j] + carry : 0.f;
+      if (d.raw) {
+        const float z = av[j] + dtb7;
+        const float dz = dg * (-ea7) * sigmoid(z);
+        pdt += dz;
+        pA += dg * (-ea7 * softplus(z));
+        v[j] = dz;
+      } else {
+        v[j] = dg;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = 16 * I + j;
       if (r < n) {
-        const float dg = v[j] + carry;
         const int64_t idx = rowidx(r) * HD + cc;
-        if (d.raw) {
-          const float z = av[j] + dtb;
-          const float dz = dg * (-ea) * sigmoid(z);
-          reinterpret_cast<bf16*>(out.dgate)[idx] = f2bf(dz);
-          pdt += dz;
-          pA += dg * (-ea * softplus(z));
-        } else {
-          reinterpret_cast<float*>(out.dgate)[idx] = dg;
-        }
+        if (d.raw)
+          reinterpret_cast<bf16*>(out.dgate)[idx] = f2bf(v[j]);
+        else
+          reinterpret_cast<float*>(out.dgate)[idx] = v[j];
       }
     }
     if (d.raw) {
