@@ -3,7 +3,8 @@
 // reduction of the raw gate.
 //
 // Given the saved state S_in and U~ = Tb R (forward scan), and dS_out,
-// dU~ and dR = Tb^T dU~ (reverse scan), one workgroup per (chunk, head) forms
+// dU~ and dv = bf16(dR), dR = Tb^T dU~ (reverse scan), one workgroup per
+// (chunk, head) forms
 //   dQd = scale dO S_in^T,  dKd = -dR S_in^T,  dKe = U~ dS_out^T
 //   dA_qk = scale dO U~^T (i <= r),  dTb = dU~ R^T (i <= r)   (Tb = T Diag(beta))
 //   dT = dTb Diag(beta),  dX = -T^T dT T^T (i < r),  dA_kk = Diag(beta) dX
@@ -46,6 +47,9 @@ constexpr float CALM_SPAN_B = 40.f;
 #ifndef KDA_SPLIT_B2
 #define KDA_SPLIT_B2 SPLIT_B     // dKd = dR S_in^T
 #endif
+// dR enters dKd only through its bf16 rounding, which is the dv output of the
+// reverse scan; the kernel reads dv, so dR has no lo part to offer
+static_assert(!(KDA_SPLIT_B2 & SPLIT_A), "dKd reads dR as the bf16 dv");
 #ifndef KDA_SPLIT_B3
 #define KDA_SPLIT_B3 SPLIT_B     // dQd = dO S_in^T (dO exact)
 #endif
@@ -72,7 +76,11 @@ struct BwdIntraSmem {
     // (8-byte stores of the D tiles, transpose loads of the fragments)
     struct {
       bf16 s_hi[HD][T1_LD], s_lo[HD][T1_LD];       // S_in [j][c], then dS_out [j][c]
-      bf16 a_hi[HD][T2_LD], a_lo[HD][T2_LD];       // dR [j][r], then U~ [j][r]
+      bf16 a_hi[HD][T2_LD];                        // U~ [j][r]
+      union {
+        bf16 a_lo[HD][T2_LD];                      // U~ [j][r]
+        bf16 dv_hi[CL][K1_LD];                     // dv [r][j], before U~
+      };
       bf16 do_hi[CL][K1_LD];                       // dO [r][j]
     } p2;
     struct {
@@ -222,10 +230,11 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   for (int nt = 0; nt < 4; ++nt) adq[nt] = adk[nt] = adG[nt] = aP[nt] = zero4();
 
   // ------------------------------------------------------------ P2: dQd, dKd
-  // dR (= dv, fp32) from the reverse scan
+  // dR (= dv in fp32) enters as its bf16 rounding, the dv output of the reverse scan
   const Panel SP{&sm.u.p2.s_hi[0][0], &sm.u.p2.s_lo[0][0], T1_LD};
   const Panel AP{&sm.u.p2.a_hi[0][0], &sm.u.p2.a_lo[0][0], T2_LD};
   const Panel DOP{&sm.u.p2.do_hi[0][0], nullptr, K1_LD};
+  const Panel DVP{&sm.u.p2.dv_hi[0][0], nullptr, K1_LD};
   auto load_state_panel = [&](const float* src) {
     // 128 x 128 fp32, tile order -> split panel [c][j]: wave w takes row
     // block w, 8 tiles, all loads issued first
@@ -236,24 +245,20 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     for (int jb = 0; jb < 8; ++jb) store_tile_t(v[jb], SP, 16 * w, 16 * jb);
   };
   {
-    f32x4 dR[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)   // dR from the reverse scan (tile order)
-      dR[nt] = *reinterpret_cast<const f32x4*>(bw.dR + ch * CL * HD + tile_off(rb, 4 * chh + nt));
     load_state_panel(sv.S_in + ch * HD * HD);
+    const bf16* dv = reinterpret_cast<const bf16*>(out.dv);
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
       const int e = t + NTHR * rep, r = e >> 4, j8 = (e & 15) * 8;
       bf16x8 x = *reinterpret_cast<const bf16x8*>(dO + rowidx(clampr(r)) * HD + j8);
+      bf16x8 y = *reinterpret_cast<const bf16x8*>(dv + rowidx(clampr(r)) * HD + j8);
       if (r >= n) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) x[jj] = f2bf(0.f);
+        for (int jj = 0; jj < 8; ++jj) x[jj] = y[jj] = f2bf(0.f);
       }
       *reinterpret_cast<bf16x8*>(&sm.u.p2.do_hi[r][j8]) = x;
+      *reinterpret_cast<bf16x8*>(&sm.u.p2.dv_hi[r][j8]) = y;
     }
-    const Panel APd{AP.hi, (KDA_SPLIT_B2 & SPLIT_A) ? AP.lo : nullptr, T2_LD};
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) store_tile_t(dR[nt], APd, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
     load_epi();
     {
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       f32x4 b[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) b[nt] = zero4();
-      mma_row<KDA_SPLIT_B2, 4, true, true>(b, AP, 16 * rb, SP, 64 * chh, 0, HD);
+      mma_row<KDA_SPLIT_B2, 4, false, true>(b, DVP, 16 * rb, SP, 64 * chh, 0, HD);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -828,24 +833,49 @@ hipError_t launch_bwd_intra(const Dims& d, const Inputs& in, const ChunkTable& c
 }
 
 // Raw gate: dA_log[h] = sum over chunks of sum_{t,c} dg g, ddt_bias[h][c] =
-// sum over chunks of sum_t dz, both in chunk order (deterministic).
-__global__ __launch_bounds__(128) void finalize_kernel(Dims d, ChunkTable ct, BwdOut out,
-                                                        BwdWork bw) {
-  const int h = blockIdx.x, c = threadIdx.x;
+// sum over chunks of sum_t dz. One workgroup per head; thread (s, c) sums the
+// chunks ci = s, s + 8, ... in chunk order, and the eight slices are then
+// added by a fixed tree, so the result does not vary from run to run.
+constexpr int FIN_SL = 8;
+__global__ __launch_bounds__(FIN_SL * HD) void finalize_kernel(Dims d, ChunkTable ct, BwdOut out,
+                                                                BwdWork bw) {
+  __shared__ float rdt[FIN_SL][HD];
+  __shared__ float rA[FIN_SL * HD / 64];
+  const int h = blockIdx.x, t = threadIdx.x, c = t & (HD - 1), sl = t >> 7;
   const int nch = ct.doc_c0[d.N];
-  float s = 0.f;
-  for (int ci = 0; ci < nch; ++ci) s += bw.part_dt[((int64_t)ci * d.H + h) * HD + c];
-  out.ddt_bias[h * HD + c] = s;
-  if (c == 0) {
-    float a = 0.f;
-    for (int ci = 0; ci < nch; ++ci) a += bw.part_A[(int64_t)ci * d.H + h];
-    out.dA_log[h] = a;
+  const int64_t stride = (int64_t)FIN_SL * d.H * HD;
+  const float* p = bw.part_dt + ((int64_t)sl * d.H + h) * HD + c;
+  float s0 = 0.f, s1 = 0.f;
+  int ci = sl;
+  for (; ci + FIN_SL < nch; ci += 2 * FIN_SL, p += 2 * stride) {
+    s0 += p[0];
+    s1 += p[stride];
+  }
+  if (ci < nch) s0 += p[0];
+  rdt[sl][c] = s0 + s1;
+  // dA_log: thread t sums the chunks ci = t, t + 1024, ...
+  float a = 0.f;
+  for (int cj = t; cj < nch; cj += FIN_SL * HD) a += bw.part_A[(int64_t)cj * d.H + h];
+  a = row_sum16(a);
+  a += __shfl_xor(a, 16);
+  a += __shfl_xor(a, 32);
+  if ((t & 63) == 0) rA[t >> 6] = a;
+  __syncthreads();
+  if (t < HD) {
+    out.ddt_bias[h * HD + t] = ((rdt[0][t] + rdt[1][t]) + (rdt[2][t] + rdt[3][t])) +
+                               ((rdt[4][t] + rdt[5][t]) + (rdt[6][t] + rdt[7][t]));
+  }
+  if (t == HD) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < FIN_SL * HD / 64; ++i) s += rA[i];
+    out.dA_log[h] = s;
   }
 }
 
 hipError_t launch_finalize(const Dims& d, const ChunkTable& ct, const BwdOut& out,
                            const BwdWork& bw, hipStream_t s) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(d.H), dim3(HD), 0, s, d, ct, out, bw);
+  hipLaunchKernelGGL(finalize_kernel, dim3(d.H), dim3(FIN_SL * HD), 0, s, d, ct, out, bw);
   return hipGetLastError();
 }
 

@@ -38,11 +38,16 @@ constexpr int kPrepWorkgroups = 256;     // MI355X compute units
 
 __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
                                                         int64_t T, int NC, ChunkTable ct) {
-  __shared__ int32_t scan[256];
+  // documents are taken 256 at a time: a prefix sum of their chunk counts
+  // gives each its first chunk, then every thread fills chunk entries c,
+  // c + 256, ... of the batch, finding the document of entry c by a binary
+  // search over the batch's inclusive chunk ends
+  __shared__ int32_t scan[256], c_end[256], d_tok[256], d_end[256];
   const int t = threadIdx.x;
   int carry = 0;
   for (int base = 0; base < N; base += 256) {
     const int d = base + t;
+    const int nb = min(256, N - base);
     int a = 0, b = 0, cnt = 0;
     if (d < N) {
       int64_t ca = cu[d], cb = cu[d + 1];
@@ -62,13 +67,22 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
     }
     const int c0 = carry + scan[t] - cnt;
     const int total = scan[255];
-    if (d < N) {
-      ct.doc_c0[d] = min(c0, NC);
-      for (int c = 0; c < cnt && c0 + c < NC; ++c) {
-        const int tok = a + CL * c;
-        ct.tok[c0 + c] = tok;
-        ct.len[c0 + c] = min(CL, b - tok);
+    c_end[t] = carry + scan[t];
+    d_tok[t] = a - CL * c0;       // first token of chunk c of this document: d_tok + 64 c
+    d_end[t] = b;
+    if (d < N) ct.doc_c0[d] = min(c0, NC);
+    __syncthreads();
+    const int cstop = min(carry + total, NC);
+    for (int c = carry + t; c < cstop; c += 256) {
+      int lo = 0, hi = nb - 1;    // smallest document of the batch whose chunk end exceeds c
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (c_end[mid] > c) hi = mid;
+        else lo = mid + 1;
       }
+      const int tok = d_tok[lo] + CL * c;
+      ct.tok[c] = tok;
+      ct.len[c] = min(CL, d_end[lo] - tok);
     }
     carry += total;
     __syncthreads();

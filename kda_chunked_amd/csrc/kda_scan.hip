@@ -671,7 +671,6 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     {
       f32x4 acc = zero4();
       mma<SPLIT_BW, true>(acc, TB, 16 * rb, DU, 16 * nw, (16 * rb / 32) * 32, CL);
-      *reinterpret_cast<f32x4*>(bw.dR + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)) = acc;
       store_tile_t(acc, DR, 16 * rb, 16 * nw);
     }
     stage(8, BP_PER_THREAD);
