@@ -87,13 +87,12 @@ def algo_bytes_per_chunk_head(kernel: str, raw: bool) -> int:
         "fwd_scan": _FWD_CHAIN_B + 2 * _X + 4 * 128 * 128 + 2 * 4 * _X,
         # S_in, U~, scale Qd, scale A_qk -> o
         "fwd_out": 4 * 128 * 128 + 4 * _X + 2 * 2 * _X + 2 * 2 * 64 * 64 + 2 * _X,
-        # panels, dO, S_in -> dv, dU~ (fp32), dS (fp32), e^(G_last) gradient partials
-        "bwd_scan": _PANEL_B + 2 * _X + 4 * 128 * 128
-                    + 2 * _X + 4 * _X + 4 * 128 * 128 + 4 * 4 * 128,
-        # q, k, G, dO, dv, beta, rq, rk, S_in, dS, U~, R, dU~, T, A_kk, e^(G_last)
-        # gradient partials (+ a) -> dq, dk, dbeta, dgate
+        # panels, dO -> dv, dU~ (fp32), dS (fp32)
+        "bwd_scan": _PANEL_B + 2 * _X + 2 * _X + 4 * _X + 4 * 128 * 128,
+        # q, k, G, dO, dv, beta, rq, rk, S_in, dS, U~, R, dU~, T, A_kk (+ a)
+        # -> dq, dk, dbeta, dgate
         "bwd_intra": 2 * 2 * _X + 4 * _X + 2 * _X + 2 * _X + 128 + 512 + 2 * 4 * 128 * 128
-                     + 3 * 4 * _X + 2 * 4 * 64 * 64 + 4 * 4 * 128 + (2 * _X if raw else 0)
+                     + 3 * 4 * _X + 2 * 4 * 64 * 64 + (2 * _X if raw else 0)
                      + 2 * 2 * _X + 128 + gate_out,
     }[kernel]
 

@@ -83,7 +83,6 @@ kda::BwdWork carve_bwd(Carver& c, const Sizes& s) {
   kda::BwdWork bw;
   bw.dS = c.take<float>((size_t)s.NC * s.H * 128 * 128);
   bw.dU = c.take<float>((size_t)s.NC * s.H * 64 * 128);
-  bw.dgam_part = c.take<float>((size_t)s.NC * s.H * 4 * 128);
   bw.part_A = c.take<float>((size_t)s.NC * s.H);
   bw.part_dt = c.take<float>((size_t)s.NC * s.H * 128);
   return bw;

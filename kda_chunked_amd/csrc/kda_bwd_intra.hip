@@ -299,17 +299,29 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
       U[nt] = *reinterpret_cast<const f32x4*>(sv.U + ch * CL * HD + tile_off(rb, 4 * chh + nt));
-    // dS_out replaces S_in in the panel (wave w: row block w, 8 tiles);
-    // dgamma[c] = sum_j dS_out[c][j] S_in[c][j], from the reverse scan's
-    // partial sums over its four 32-column tiles
+    // dS_out replaces S_in in the panel (wave w: row block w, 8 tiles).
+    // dgamma[c] = sum_j dS_out[c][j] S_in[c][j]: each lane reads S_in (hi + lo)
+    // back from the panel positions it wrote in P2, which its dS_out tile
+    // then overwrites, so no other lane's data is involved before the barrier
     {
       const float* dSg = bw.dS + ch * HD * HD;
       f32x4 v[8];
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) v[jb] = *reinterpret_cast<const f32x4*>(dSg + tile_off(w, jb));
-      if (t < HD) {
-        const float* pg = bw.dgam_part + ch * 4 * HD + t;
-        sm.dgam[t] = (pg[0] + pg[HD]) + (pg[2 * HD] + pg[3 * HD]);
+      float pg[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) {
+        const int off = (16 * jb + dcol()) * T1_LD + 16 * w + 4 * (l >> 4);
+        const bf16x4 sh = *reinterpret_cast<const bf16x4*>(SP.hi + off);
+        const bf16x4 sl = *reinterpret_cast<const bf16x4*>(SP.lo + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pg[i] += v[jb][i] * (bf2f(sh[i]) + bf2f(sl[i]));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pg[i] = row_sum16(pg[i]);
+      if (dcol() == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.dgam[16 * w + drow(i)] = pg[i];
       }
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) store_tile_t(v[jb], SP, 16 * w, 16 * jb);

@@ -73,7 +73,6 @@ struct BwdOut {
 struct BwdWork {
   float* dS;          // [NC, H, 128 x 128] gradient w.r.t. the state after each chunk (tile order)
   float* dU;          // [NC, H, 64 x 128] gradient w.r.t. U~ (tile order, as SavedSet::R)
-  float* dgam_part;   // [NC, H, 4, 128] sum_j dS_out[c][j] S_in[c][j] over each 32-column tile
   float* part_A;      // [NC, H]      raw form: per-chunk sum of dg*g
   float* part_dt;     // [NC, H, 128] raw form: per-chunk sum of dz
 };

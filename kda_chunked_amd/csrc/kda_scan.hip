@@ -583,7 +583,6 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   // previous one instead of queueing in one burst.
   bf16x8 pu[BP_PER_THREAD];
   bf16x4 pdo;          // dO, row rO, columns j0 + cO .. + 3
-  f32x4 pS[2];         // S_in tiles (rows 16 w, this workgroup's 32 columns)
   const int rO = t >> 3, cO = 4 * (t & 7);
   // The chunks of a document are consecutive: first token and length follow
   // from the document's first token and end.
@@ -616,12 +615,6 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     rows_in(cn, t0, n);
     const int rc = rO < n ? rO : n - 1;
     pdo = *reinterpret_cast<const bf16x4*>(dO + ((t0 + rc) * H + h) * HD + j0 + cO);
-  };
-  auto load_S = [&](int cn) {
-    const float* Sg = sv.S_in + ((int64_t)cn * H + h) * HD * HD;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      pS[nt] = *reinterpret_cast<const f32x4*>(Sg + tile_off(w, (j0 >> 4) + nt));
   };
 
   f32x4 dS[2];
@@ -665,7 +658,6 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     }
     stage(6, 8);                                   // Tb
     units(cp, 6, 8);
-    load_S(ci);
     __syncthreads();
     // ---- C. dR = Tb^T dU~ (= dv); scale Qd, -Kd, e^(G_last) into LDS
     {
@@ -686,12 +678,6 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
         *reinterpret_cast<bf16x4*>(dv + ((t0 + rO) * H + h) * HD + j0 + cO) = x;
       }
       float* dSg = bw.dS + ch * HD * HD;
-      // d/d e^(G_last)[c] of this workgroup's columns: sum_j dS_out[c][j] S_in[c][j]
-      f32x4 pg;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pg[i] = row_sum16(dS[0][i] * pS[0][i] + dS[1][i] * pS[1][i]);
-      if (dcol() == 0)
-        *reinterpret_cast<f32x4*>(bw.dgam_part + (ch * NTILE + tile) * HD + 16 * w + drow(0)) = pg;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         *reinterpret_cast<f32x4*>(dSg + tile_off(w, (j0 >> 4) + nt)) = dS[nt];
