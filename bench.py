@@ -81,19 +81,18 @@ def algo_bytes_per_chunk_head(kernel: str, raw: bool) -> int:
     gate_in = 2 * _X if raw else 4 * _X            # a (bf16) or g (fp32)
     gate_out = 2 * _X + 512 + 4 if raw else 4 * _X  # da + part_dt + part_A, or dg
     return {
-        # q, k, gate, beta -> G, rq, rk, T, A_kk, operand panels
-        "fwd_prep": 2 * 2 * _X + gate_in + 128 + 4 * _X + 512 + 2 * 4 * 64 * 64 + _PANEL_B,
+        # q, k, gate, beta -> rq, rk, T, A_kk, operand panels
+        "fwd_prep": 2 * 2 * _X + gate_in + 128 + 512 + 2 * 4 * 64 * 64 + _PANEL_B,
         # chain panels, v -> S_in, R, U~ (fp32)
         "fwd_scan": _FWD_CHAIN_B + 2 * _X + 4 * 128 * 128 + 2 * 4 * _X,
         # S_in, U~, scale Qd, scale A_qk -> o
         "fwd_out": 4 * 128 * 128 + 4 * _X + 2 * 2 * _X + 2 * 2 * 64 * 64 + 2 * _X,
         # panels, dO -> dv, dU~ (fp32), dS (fp32)
         "bwd_scan": _PANEL_B + 2 * _X + 2 * _X + 4 * _X + 4 * 128 * 128,
-        # q, k, G, dO, dv, beta, rq, rk, S_in, dS, U~, R, dU~, T, A_kk (+ a)
+        # q, k, gate, dO, dv, beta, rq, rk, S_in, dS, U~, R, dU~, T, A_kk
         # -> dq, dk, dbeta, dgate
-        "bwd_intra": 2 * 2 * _X + 4 * _X + 2 * _X + 2 * _X + 128 + 512 + 2 * 4 * 128 * 128
-                     + 3 * 4 * _X + 2 * 4 * 64 * 64 + (2 * _X if raw else 0)
-                     + 2 * 2 * _X + 128 + gate_out,
+        "bwd_intra": 2 * 2 * _X + gate_in + 2 * _X + 2 * _X + 128 + 512 + 2 * 4 * 128 * 128
+                     + 3 * 4 * _X + 2 * 4 * 64 * 64 + 2 * 2 * _X + 128 + gate_out,
     }[kernel]
 
 

@@ -62,14 +62,13 @@ kda::ChunkTable carve_table(Carver& c, const Sizes& s) {
 }
 
 // with_states = 0 leaves out S_in and R (a forward that saves nothing).
-kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states, float** G) {
+kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states) {
   kda::SavedSet sv{};
   const size_t mat = (size_t)s.NC * s.H * 64 * 64;
   sv.Tm = c.take<float>(mat);
   sv.Akk = c.take<float>(mat);
   sv.rq = c.take<float>((size_t)s.T * s.H);
   sv.rk = c.take<float>((size_t)s.T * s.H);
-  *G = c.take<float>((size_t)s.T * s.H * 128);
   if (with_states) {
     sv.S_in = c.take<float>((size_t)s.NC * s.H * 128 * 128);
     sv.R = c.take<float>((size_t)s.NC * s.H * 64 * 128);
@@ -136,8 +135,7 @@ kda::Dims dims_of(const kda_problem* p) {
 size_t fwd_ws_bytes(const Sizes& s) {
   Carver c(nullptr);
   carve_table(c, s);
-  float* G;
-  carve_saved(c, s, 1, &G);   // used when the caller saves nothing
+  carve_saved(c, s, 1);   // used when the caller saves nothing
   return c.off;
 }
 
@@ -146,8 +144,7 @@ size_t bwd_ws_bytes(const Sizes& s, int replay) {
   carve_table(c, s);
   carve_bwd(c, s);
   if (replay) {
-    float* G;
-    carve_saved(c, s, 1, &G);
+    carve_saved(c, s, 1);
   }
   return c.off;
 }
@@ -171,8 +168,7 @@ extern "C" {
 size_t kda_saved_bytes(const kda_problem* p) {
   if (check_problem(p) != KDA_OK) return 0;
   Carver c(nullptr);
-  float* G;
-  carve_saved(c, sizes_of(p), 1, &G);
+  carve_saved(c, sizes_of(p), 1);
   return c.off;
 }
 
@@ -214,14 +210,13 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carver wc(workspace);
   const kda::ChunkTable ct = carve_table(wc, s);
-  float* G = nullptr;
-  kda::SavedSet sv = carve_saved(wc, s, 1, &G);   // used when nothing is saved
+  kda::SavedSet sv = carve_saved(wc, s, 1);   // used when nothing is saved
   if (saved) {
     Carver sc(saved);
-    sv = carve_saved(sc, s, 1, &G);
+    sv = carve_saved(sc, s, 1);
   }
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
-  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, saved != nullptr, hs));
+  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, saved != nullptr, hs));
   LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, saved != nullptr, hs));
   LAUNCH("fwd_out", kda::launch_fwd_out(d, ct, sv, sv.panels, o, hs));
   return KDA_OK;
@@ -273,22 +268,21 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   Carver wc(workspace);
   const kda::ChunkTable ct = carve_table(wc, s);
   const kda::BwdWork bw = carve_bwd(wc, s);
-  float* G = nullptr;
   kda::SavedSet sv;
   if (replay) {
-    sv = carve_saved(wc, s, 1, &G);
+    sv = carve_saved(wc, s, 1);
   } else {
     Carver sc(const_cast<void*>(saved));
-    sv = carve_saved(sc, s, 1, &G);
+    sv = carve_saved(sc, s, 1);
   }
   const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   if (replay) {
-    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, G, sv, 1, hs));
+    LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, 1, hs));
     LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, 1, hs));
   }
-  LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, G, sv, dO, dv, bw, hs));
-  LAUNCH("bwd_intra", kda::launch_bwd_intra(d, in, ct, G, sv, dO, out, bw, hs));
+  LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, sv, dO, dv, bw, hs));
+  LAUNCH("bwd_intra", kda::launch_bwd_intra(d, in, ct, sv, dO, out, bw, hs));
   if (p->gate == KDA_GATE_RAW) LAUNCH("finalize", kda::launch_finalize(d, ct, out, bw, hs));
   return KDA_OK;
 }

@@ -131,7 +131,6 @@ struct BwdIntraSmem {
 };
 
 __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                          const float* __restrict__ G,
                                                           SavedSet sv,
                                                           const bf16* __restrict__ dO,
                                                           BwdOut out, BwdWork bw) {
@@ -161,8 +160,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   float eG[4][4];
   bf16x2 eq2[4][2], ek2[4][2];     // raw q, k (bf16 pairs i = 2 m, 2 m + 1); q^ = q * rqr[i]
   float rqr[4], rkr[4];
-  // load G, q, k at this thread's elements once the first phase's panels
-  // are staged (they stay in registers through the epilogues of P2 .. P7)
+  // load q, k at this thread's elements once the first phase's panels are
+  // staged (they stay in registers through the epilogues of P2 .. P7)
   auto load_epi = [&]() {
     // addresses rebuilt from an opaque copy of the thread id, and pointers
     // made opaque, so that the loads are issued here and not hoisted above
@@ -170,7 +169,6 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     int tt = t;
     int64_t base = (t0 * H + h) * HD, rbase = t0 * H + h;
     asm volatile("" : "+v"(tt), "+s"(base), "+s"(rbase));
-    const float* Gp = G + base;
     const bf16* qp = q + base;
     const bf16* kp = k + base;
     const float* rqp = sv.rq + rbase;
@@ -183,7 +181,6 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       const int ro = r * rstride + cb;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        eG[nt][i] = Gp[ro + 16 * nt];
         eq2[nt][i >> 1][i & 1] = qp[ro + 16 * nt];
         ek2[nt][i >> 1][i & 1] = kp[ro + 16 * nt];
       }
@@ -202,13 +199,49 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     sm.rq[t] = ok ? a : 0.f;
     sm.rk[t] = ok ? c : 0.f;
   }
-  for (int e = t; e < 5 * HD; e += NTHR) {
-    const int I = e >> 7, c = e & 127;
-    const float v = I == 0 ? 0.f : G[rowidx(clampr(16 * I - 1)) * HD + c];
-    sm.Gref[I][c] = v;
-    if (I == 4) {
-      sm.GL[c] = v;
-      sm.gam[c] = fexp(v);
+  // G, the chunk-local inclusive cumsum of g, rebuilt from the gate input in
+  // the forward prep's order (so it is the same G, bit for bit): thread
+  // (I = t >> 7, c = t & 127) sums rows 16 I .. 16 I + 15 of channel c, then
+  // adds the totals of the earlier row blocks; rows >= n repeat G[n - 1]
+  {
+    // no fused multiply-adds here or in the prep's cumsum, so both round alike
+#pragma clang fp contract(off)
+    // an opaque copy of the thread id: the gate rows' addresses are not
+    // shared with the last phase's identical ones (they would stay live)
+    int tt = t;
+    asm volatile("" : "+v"(tt));
+    const int I = tt >> 7, c = tt & 127;
+    float gv[16];
+    if (d.raw) {
+      const bf16* ap = reinterpret_cast<const bf16*>(in.gate);
+      bf16 av[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) av[j] = ap[rowidx(clampr(16 * I + j)) * HD + c];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) gv[j] = -ea7 * softplus(bf2f(av[j]) + dtb7);
+    } else {
+      const float* gp = reinterpret_cast<const float*>(in.gate);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) gv[j] = gp[rowidx(clampr(16 * I + j)) * HD + c];
+    }
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      run += (16 * I + j < n) ? gv[j] : 0.f;
+      gv[j] = run;
+    }
+    sm.u.p7.tot[I][c] = run;
+    __syncthreads();
+    float carry = 0.f;
+    for (int j = 0; j < I; ++j) carry += sm.u.p7.tot[j][c];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sm.u.p7.dG[16 * I + j][c] = gv[j] + carry;
+    const float gl = gv[15] + carry;
+    if (I == 0) sm.Gref[0][c] = 0.f;
+    sm.Gref[I + 1][c] = gl;
+    if (I == 3) {
+      sm.GL[c] = gl;
+      sm.gam[c] = fexp(gl);
     }
   }
   if (t < 4) sm.calm_blk[t] = 1;
@@ -220,6 +253,12 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     for (int I = 0; I < 4; ++I)
       if (sm.Gref[I][t] - sm.Gref[I + 1][t] > CALM_SPAN_B) sm.calm_blk[I] = 0;
   }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eG[nt][i] = sm.u.p7.dG[16 * rb + drow(i)][64 * chh + 16 * nt + dcol()];
+  // the first phase's staging overwrites the G table
+  __syncthreads();
 
   // aP: the e^(G_last - G_r) terms of dKe, k^_r p3_r, which enter dg_j for
   // every j > r; kept apart from adG so that P7 adds their exclusive prefix
@@ -837,9 +876,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #undef EK
 
 hipError_t launch_bwd_intra(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                            const float* G, const SavedSet& sv, const void* dO,
-                            const BwdOut& out, const BwdWork& bw, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_intra_kernel, dim3(d.NC, d.H), dim3(NTHR), 0, s, d, in, ct, G, sv,
+                            const SavedSet& sv, const void* dO, const BwdOut& out,
+                            const BwdWork& bw, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_intra_kernel, dim3(d.NC, d.H), dim3(NTHR), 0, s, d, in, ct, sv,
                      reinterpret_cast<const bf16*>(dO), out, bw);
   return hipGetLastError();
 }

@@ -19,7 +19,7 @@ struct ChunkTable {
 };
 
 // Per-chunk matrices and states (the saved forward set), all fp32. The gate
-// cumsum G [T, H, 128] is carved right after rk.
+// cumsum G is not saved: the per-chunk backward rebuilds it from the gate input.
 //
 // S_in, R and U~ are stored per chunk-head in MFMA tile order: a 16 x 16 tile
 // (row block rb, column block cb) is 256 contiguous floats at
@@ -99,18 +99,18 @@ constexpr size_t BYTES = (size_t)ELEMS * 2;  // 131584, a multiple of 16
 
 hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
                             hipStream_t s);
-hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
+hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, int with_bwd, hipStream_t s);
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, const void* panels, int save_R, hipStream_t s);
 hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& sv,
                           const void* panels, void* o, hipStream_t s);
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                           const float* G, const SavedSet& sv, const void* dO, void* dv,
+                           const SavedSet& sv, const void* dO, void* dv,
                            const BwdWork& bw, hipStream_t s);
 hipError_t launch_bwd_intra(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                            const float* G, const SavedSet& sv, const void* dO,
-                            const BwdOut& out, const BwdWork& bw, hipStream_t s);
+                            const SavedSet& sv, const void* dO, const BwdOut& out,
+                            const BwdWork& bw, hipStream_t s);
 hipError_t launch_finalize(const Dims& d, const ChunkTable& ct, const BwdOut& out,
                            const BwdWork& bw, hipStream_t s);
 

@@ -180,7 +180,6 @@ KDA_DEV void decayed_frag(const PrepSmem& sm, const bf16 (*x)[XS_LD], float rx, 
 // carries the other's registers through the chunk loop.
 template <bool RAW>
 __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, ChunkTable ct,
-                                                            float* __restrict__ G_out,
                                                             SavedSet sv, bf16* __restrict__ panels,
                                                             int with_lo) {
   __shared__ PrepSmem sm;
@@ -275,6 +274,9 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   // ---- 2. chunk-local cumsum of g in registers (16 rows per thread), then
   // the carry of the earlier row quarters
   {
+    // no fused multiply-adds here: the per-chunk backward rebuilds G from the
+    // gate input with the same operations and must round alike
+#pragma clang fp contract(off)
     float run = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -297,7 +299,6 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       const int r = 16 * qG + j;
       const float Gx = g[j] + carry;
       sm.G[r][cG] = Gx;               // rows >= n hold G[n-1] (their g is 0)
-      if (r < n) G_out[((t0 + r) * H + h) * HD + cG] = Gx;
     }
     if (t < CL) {
       float a = 0.f, b = 0.f;
@@ -625,15 +626,15 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   }
 }
 
-hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct, float* G,
+hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, int with_bwd, hipStream_t s) {
   // about one workgroup per CU (the LDS allows one), each walking chunks of one head
   const int gx = std::max(1, std::min(d.NC, (kPrepWorkgroups + d.H - 1) / d.H));
   if (d.raw)
-    hipLaunchKernelGGL(fwd_prep_kernel<true>, dim3(gx, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
+    hipLaunchKernelGGL(fwd_prep_kernel<true>, dim3(gx, d.H), dim3(NT_PREP), 0, s, d, in, ct, sv,
                        reinterpret_cast<bf16*>(sv.panels), with_bwd);
   else
-    hipLaunchKernelGGL(fwd_prep_kernel<false>, dim3(gx, d.H), dim3(NT_PREP), 0, s, d, in, ct, G, sv,
+    hipLaunchKernelGGL(fwd_prep_kernel<false>, dim3(gx, d.H), dim3(NT_PREP), 0, s, d, in, ct, sv,
                        reinterpret_cast<bf16*>(sv.panels), with_bwd);
   return hipGetLastError();
 }

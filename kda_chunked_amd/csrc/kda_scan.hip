@@ -17,7 +17,7 @@
 // order; the 4 tiles of a head are mapped to one XCD so that they share the
 // chunk operands through that XCD's L2.
 //
-// Pipelining: the raw inputs of the next chunk (q, k, G, v, T, A_qk, ...)
+// Pipelining: the raw inputs of the next chunk (q, k, v, T, A_qk, ...)
 // are loaded into registers while the current chunk's products run, so the
 // only memory latency on the sequential path is the first chunk's.
 #include "kda_device.h"
@@ -696,9 +696,8 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
 }
 
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                           const float* G, const SavedSet& sv, const void* dO, void* dv,
+                           const SavedSet& sv, const void* dO, void* dv,
                            const BwdWork& bw, hipStream_t s) {
-  (void)G;
   hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(NT_SCAN), 0, s, d, in,
                      ct, sv, reinterpret_cast<const bf16*>(dO), reinterpret_cast<bf16*>(dv), bw);
   return hipGetLastError();

@@ -68,14 +68,14 @@ def test_parity_full_size_sampled_heads(name, heads, replay):
 
 
 def _saved_states(kda, w):
-    """The S_in block of the saved set (layout: Tm, Akk, rq, rk, G, S_in, ...,
+    """The S_in block of the saved set (layout: Tm, Akk, rq, rk, S_in, ...,
     each 256-byte aligned). S_in is stored in MFMA tile order: tile (rb, cb) of
     16 x 16 at (8 rb + cb) * 256 floats, element (4 g + i, c) of the tile at
     4 (16 g + c) + i."""
     up = lambda x: (x + 255) // 256 * 256
     NC = w.T // 64 + len(w.doc_lens)
     H, T = w.H, w.T
-    off = 2 * up(NC * H * 4096 * 4) + 2 * up(T * H * 4) + up(T * H * 128 * 4)
+    off = 2 * up(NC * H * 4096 * 4) + 2 * up(T * H * 4)
     n = NC * H * 128 * 128
     raw = kda.saved[off:off + 4 * n].view(torch.float32).view(NC, H, 8, 8, 4, 16, 4)
     return raw.permute(0, 1, 2, 4, 6, 3, 5).reshape(NC, H, 128, 128)
