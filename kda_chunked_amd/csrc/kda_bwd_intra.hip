@@ -191,38 +191,66 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   };
 #define EQ(nt, i) (bf2f(eq2[nt][(i) >> 1][(i) & 1]) * rqr[i])
 #define EK(nt, i) (bf2f(ek2[nt][(i) >> 1][(i) & 1]) * rkr[i])
-  if (t < CL) {
-    const int r = clampr(t);
-    const bool ok = t < n;
-    const float b = bf2f(beta[rowidx(r)]), a = sv.rq[rowidx(r)], c = sv.rk[rowidx(r)];
-    sm.beta[t] = ok ? b : 0.f;
-    sm.rq[t] = ok ? a : 0.f;
-    sm.rk[t] = ok ? c : 0.f;
-  }
+  // The setup's own loads go out first: memory counters complete in order,
+  // so P2's inputs, requested after them, stay in flight while it waits.
+  const int r64 = clampr(t & (CL - 1));
+  const bf16 ld_b = beta[rowidx(r64)];
+  const float ld_rq = sv.rq[rowidx(r64)], ld_rk = sv.rk[rowidx(r64)];
   // G, the chunk-local inclusive cumsum of g, rebuilt from the gate input in
   // the forward prep's order (so it is the same G, bit for bit): thread
   // (I = t >> 7, c = t & 127) sums rows 16 I .. 16 I + 15 of channel c, then
-  // adds the totals of the earlier row blocks; rows >= n repeat G[n - 1]
+  // adds the totals of the earlier row blocks; rows >= n repeat G[n - 1].
+  // An opaque copy of the thread id keeps the gate rows' addresses from
+  // being shared with the last phase's identical ones (they would stay live).
+  int tt = t;
+  asm volatile("" : "+v"(tt));
+  const int gI = tt >> 7, gc = tt & 127;
+  float gv[16];
+  bf16 av[16];
+  if (d.raw) {
+    const bf16* ap = reinterpret_cast<const bf16*>(in.gate);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) av[j] = ap[rowidx(clampr(16 * gI + j)) * HD + gc];
+  } else {
+    const float* gp = reinterpret_cast<const float*>(in.gate);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) gv[j] = gp[rowidx(clampr(16 * gI + j)) * HD + gc];
+  }
+  // Each phase's global inputs are requested one phase ahead (into
+  // registers), so that they arrive while the previous phase computes: P2's
+  // before the setup, P3's before P2's products, P4's before P3's products.
+  f32x4 pS[8];           // S_in tiles (row block w, all 8 column blocks)
+  bf16x8 pO[2], pV[2];   // dO, dv rows e >> 4, columns (e & 15) * 8, e = t + 512 rep
+  {
+    const float* src = sv.S_in + ch * HD * HD;
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) pS[jb] = *reinterpret_cast<const f32x4*>(src + tile_off(w, jb));
+    const bf16* dv = reinterpret_cast<const bf16*>(out.dv);
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int e = t + NTHR * rep, r = e >> 4, j8 = (e & 15) * 8;
+      pO[rep] = *reinterpret_cast<const bf16x8*>(dO + rowidx(clampr(r)) * HD + j8);
+      pV[rep] = *reinterpret_cast<const bf16x8*>(dv + rowidx(clampr(r)) * HD + j8);
+    }
+  }
+
+  if (t < CL) {
+    const bool ok = t < n;
+    sm.beta[t] = ok ? bf2f(ld_b) : 0.f;
+    sm.rq[t] = ok ? ld_rq : 0.f;
+    sm.rk[t] = ok ? ld_rk : 0.f;
+  }
   {
     // no fused multiply-adds here or in the prep's cumsum, so both round alike
 #pragma clang fp contract(off)
-    // an opaque copy of the thread id: the gate rows' addresses are not
-    // shared with the last phase's identical ones (they would stay live)
-    int tt = t;
-    asm volatile("" : "+v"(tt));
-    const int I = tt >> 7, c = tt & 127;
-    float gv[16];
-    if (d.raw) {
-      const bf16* ap = reinterpret_cast<const bf16*>(in.gate);
-      bf16 av[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) av[j] = ap[rowidx(clampr(16 * I + j)) * HD + c];
+    const int I = gI, c = gc;
+    // an opaque copy of the gate form: the two raw branches stay apart, so
+    // the gate's waits come after P2's requests
+    int raw = d.raw;
+    asm volatile("" : "+s"(raw));
+    if (raw) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) gv[j] = -ea7 * softplus(bf2f(av[j]) + dtb7);
-    } else {
-      const float* gp = reinterpret_cast<const float*>(in.gate);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) gv[j] = gp[rowidx(clampr(16 * I + j)) * HD + c];
     }
     float run = 0.f;
 #pragma unroll
@@ -274,23 +302,17 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   const Panel AP{&sm.u.p2.a_hi[0][0], &sm.u.p2.a_lo[0][0], T2_LD};
   const Panel DOP{&sm.u.p2.do_hi[0][0], nullptr, K1_LD};
   const Panel DVP{&sm.u.p2.dv_hi[0][0], nullptr, K1_LD};
-  auto load_state_panel = [&](const float* src) {
-    // 128 x 128 fp32, tile order -> split panel [c][j]: wave w takes row
-    // block w, 8 tiles, all loads issued first
-    f32x4 v[8];
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb) v[jb] = *reinterpret_cast<const f32x4*>(src + tile_off(w, jb));
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb) store_tile_t(v[jb], SP, 16 * w, 16 * jb);
-  };
+  f32x4 pU[4];           // U~ tiles (row block rb, column blocks 4 chh ..)
+  f32x4 pD[8];           // dS_out tiles (row block w, all 8 column blocks)
   {
-    load_state_panel(sv.S_in + ch * HD * HD);
-    const bf16* dv = reinterpret_cast<const bf16*>(out.dv);
+    // S_in (128 x 128 fp32, tile order) -> split panel [c][j]: wave w takes
+    // row block w, 8 tiles
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) store_tile_t(pS[jb], SP, 16 * w, 16 * jb);
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
       const int e = t + NTHR * rep, r = e >> 4, j8 = (e & 15) * 8;
-      bf16x8 x = *reinterpret_cast<const bf16x8*>(dO + rowidx(clampr(r)) * HD + j8);
-      bf16x8 y = *reinterpret_cast<const bf16x8*>(dv + rowidx(clampr(r)) * HD + j8);
+      bf16x8 x = pO[rep], y = pV[rep];
       if (r >= n) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) x[jj] = y[jj] = f2bf(0.f);
@@ -300,6 +322,14 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     }
     __syncthreads();
     load_epi();
+    {
+      const float* dSg = bw.dS + ch * HD * HD;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        pU[nt] = *reinterpret_cast<const f32x4*>(sv.U + ch * CL * HD + tile_off(rb, 4 * chh + nt));
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) pD[jb] = *reinterpret_cast<const f32x4*>(dSg + tile_off(w, jb));
+    }
     {
       f32x4 a[4];
 #pragma unroll
@@ -333,20 +363,14 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 
   // ------------------------------------------------------------ P3: dKe, dA_qk, dgamma
   f32x4 dAq[2];
+  f32x4 pA[4], pB[4];    // dU~ and R tiles (row block rb, column blocks 4 chh ..)
   {
-    f32x4 U[4];                                   // U~ from the forward scan (tile order)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      U[nt] = *reinterpret_cast<const f32x4*>(sv.U + ch * CL * HD + tile_off(rb, 4 * chh + nt));
     // dS_out replaces S_in in the panel (wave w: row block w, 8 tiles).
     // dgamma[c] = sum_j dS_out[c][j] S_in[c][j]: each lane reads S_in (hi + lo)
     // back from the panel positions it wrote in P2, which its dS_out tile
     // then overwrites, so no other lane's data is involved before the barrier
     {
-      const float* dSg = bw.dS + ch * HD * HD;
-      f32x4 v[8];
-#pragma unroll
-      for (int jb = 0; jb < 8; ++jb) v[jb] = *reinterpret_cast<const f32x4*>(dSg + tile_off(w, jb));
+      f32x4 (&v)[8] = pD;
       float pg[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) {
@@ -366,8 +390,13 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       for (int jb = 0; jb < 8; ++jb) store_tile_t(v[jb], SP, 16 * w, 16 * jb);
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) store_tile_t(U[nt], AP, 16 * rb, 64 * chh + 16 * nt);
+    for (int nt = 0; nt < 4; ++nt) store_tile_t(pU[nt], AP, 16 * rb, 64 * chh + 16 * nt);
     __syncthreads();
+#pragma unroll
+    for (int rep = 0; rep < 4; ++rep) {
+      pA[rep] = *reinterpret_cast<const f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, 4 * chh + rep));
+      pB[rep] = *reinterpret_cast<const f32x4*>(sv.R + ch * CL * HD + tile_off(rb, 4 * chh + rep));
+    }
     f32x4 a[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) a[nt] = zero4();
@@ -395,16 +424,10 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     const Panel DU{&sm.u.p4.a_hi[0][0], &sm.u.p4.a_lo[0][0], T2_LD};
     const Panel RP{&sm.u.p4.b_hi[0][0], &sm.u.p4.b_lo[0][0], T2_LD};
     // dU~ and R, tile order: wave w takes row block w & 3, column blocks 4 (w >> 2) ..
-    f32x4 va[4], vb[4];
 #pragma unroll
     for (int rep = 0; rep < 4; ++rep) {
-      va[rep] = *reinterpret_cast<const f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, 4 * chh + rep));
-      vb[rep] = *reinterpret_cast<const f32x4*>(sv.R + ch * CL * HD + tile_off(rb, 4 * chh + rep));
-    }
-#pragma unroll
-    for (int rep = 0; rep < 4; ++rep) {
-      store_tile_t(va[rep], DU, 16 * rb, 64 * chh + 16 * rep);
-      store_tile_t(vb[rep], RP, 16 * rb, 64 * chh + 16 * rep);
+      store_tile_t(pA[rep], DU, 16 * rb, 64 * chh + 16 * rep);
+      store_tile_t(pB[rep], RP, 16 * rb, 64 * chh + 16 * rep);
     }
     __syncthreads();
     dTb[0] = dTb[1] = zero4();
