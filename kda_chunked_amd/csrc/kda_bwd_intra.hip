@@ -216,6 +216,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int j = 0; j < 16; ++j) gv[j] = gp[rowidx(clampr(16 * gI + j)) * HD + gc];
   }
+  // q, k, rq, rk at this thread's elements, for the epilogues from P2 on
+  load_epi();
   // Each phase's global inputs are requested one phase ahead (into
   // registers), so that they arrive while the previous phase computes: P2's
   // before the setup, P3's before P2's products, P4's before P3's products.
@@ -321,7 +323,6 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       *reinterpret_cast<bf16x8*>(&sm.u.p2.dv_hi[r][j8]) = y;
     }
     __syncthreads();
-    load_epi();
     {
       const float* dSg = bw.dS + ch * HD * HD;
 #pragma unroll
@@ -420,6 +421,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 
   // ------------------------------------------------------------ P4: dTb = dU~ R^T
   f32x4 dTb[2];
+  f32x4 pT0, pT1;        // T row t >> 3, columns 8 (t & 7) .. + 7
+  float pTT[8];          // T column t & 63, rows 8 (t >> 6) .. + 7
+  float pTd[2][4], pAk[2][4];   // T and A_kk at this lane's dT / dX tile elements
   {
     const Panel DU{&sm.u.p4.a_hi[0][0], &sm.u.p4.a_lo[0][0], T2_LD};
     const Panel RP{&sm.u.p4.b_hi[0][0], &sm.u.p4.b_lo[0][0], T2_LD};
@@ -430,6 +434,23 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       store_tile_t(pB[rep], RP, 16 * rb, 64 * chh + 16 * rep);
     }
     __syncthreads();
+    // P5's reads of T and A_kk, requested before this phase's product
+    {
+      const int r = t >> 3, m8 = (t & 7) * 8;
+      pT0 = *reinterpret_cast<const f32x4*>(Tg + r * CL + m8);
+      pT1 = *reinterpret_cast<const f32x4*>(Tg + r * CL + m8 + 4);
+      const int r2 = t & 63, m82 = (t >> 6) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pTT[j] = Tg[(m82 + j) * CL + r2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 16 * rb + drow(i), m = 32 * chh + 16 * nt + dcol();
+          pTd[nt][i] = Tg[rr * CL + m];
+          pAk[nt][i] = Akk_g[rr * CL + m];
+        }
+    }
     dTb[0] = dTb[1] = zero4();
     mma_row<KDA_SPLIT_B6, 2, true, true>(dTb, DU, 16 * rb, RP, 32 * chh, 0, HD);
     __syncthreads();
@@ -446,17 +467,12 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     const Panel MT{&sm.u.p5.mt_hi[0][0], &sm.u.p5.mt_lo[0][0], K2_LD};
     {
       const int r = t >> 3, m8 = (t & 7) * 8;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(Tg + r * CL + m8);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(Tg + r * CL + m8 + 4);
-      const float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const float x[8] = {pT0[0], pT0[1], pT0[2], pT0[3], pT1[0], pT1[1], pT1[2], pT1[3]};
       put8(TN, r, m8, x);
     }
     {
       const int r = t & 63, m8 = (t >> 6) * 8;
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = Tg[(m8 + j) * CL + r];
-      put8(TT, r, m8, x);
+      put8(TT, r, m8, pTT);
     }
     // dT = dTb Diag(beta) (m <= r), and dbeta_m += sum_r dTb[r][m] T[r][m]
 #pragma unroll
@@ -470,7 +486,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         const int r = 16 * rb + drow(i);
         const float v = m <= r ? dTb[nt][i] : 0.f;
         x[i] = v * bm;
-        cp += v * Tg[r * CL + m];
+        cp += v * pTd[nt][i];
       }
       store_tile_t(x, DT, 16 * rb, 32 * chh + 16 * nt);
       cp += __shfl_xor(cp, 16);
@@ -496,7 +512,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + drow(i), c = 32 * chh + 16 * nt + dcol();
         const float v = c < r ? -dx[nt][i] : 0.f;
-        rp[i] += v * Akk_g[r * CL + c];
+        rp[i] += v * pAk[nt][i];
         dAk[nt][i] = sm.beta[r] * v;
         dAq[nt][i] = c <= r ? d.scale * dAq[nt][i] : 0.f;
       }
