@@ -431,11 +431,15 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
         int r, i;
         pair_of(st, r, i);
         const bool restart = st == 16 - p;       // first row of column 15 - p
-        const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c]);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + 4]);
+        // lanes cg >= 8 read their two halves in the other order, so that
+        // each 16-byte read of the 16 lanes touches every bank once
+        const int sw = (cg & 8) >> 1;
+        const f32x4 ea = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + sw]);
+        const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + 4 - sw]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float fm = f[j] * (j < 4 ? e0[j] : e1[j - 4]);
+          const float ej = sw ? (j < 4 ? eb[j] : ea[j - 4]) : (j < 4 ? ea[j] : eb[j - 4]);
+          const float fm = f[j] * ej;
           f[j] = st == 0 ? kpf[j] : restart ? kzf[j] : fm;
         }
         const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + r][c]);
