@@ -45,7 +45,9 @@
  *    and the workspace). The library allocates nothing and keeps no state
  *    between calls apart from its loaded code; calls are re-entrant. Calls
  *    that share a workspace or saved set must be ordered on one stream.
- *  - Outputs are overwritten, never accumulated.
+ *  - Outputs are overwritten, never accumulated. No output may overlap another
+ *    output, an input, the saved set or the workspace: kda_bwd reads dv back
+ *    after writing it (the per-chunk backward takes dR as the bf16 dv).
  *  - Errors: arguments are validated on the host before anything is
  *    enqueued; an invalid call returns a status and launches nothing. A
  *    launch failure returns KDA_ERR_DEVICE. kda_last_error() gives a
