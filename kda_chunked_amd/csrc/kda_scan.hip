@@ -203,7 +203,8 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
       float* Sg = sv.S_in + ch * HD * HD;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        *reinterpret_cast<f32x4*>(Sg + tile_off(m, jv >> 4)) = S[m];
+        // streamed out (non-temporal): read only by later kernels
+        __builtin_nontemporal_store(S[m], reinterpret_cast<f32x4*>(Sg + tile_off(m, jv >> 4)));
         store_tile_t(S[m], SB, 16 * m, 0);
       }
     }
@@ -216,7 +217,9 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      if (save_R) *reinterpret_cast<f32x4*>(sv.R + ch * CL * HD + tile_off(rb, jv >> 4)) = R[rb];
+      if (save_R)
+        __builtin_nontemporal_store(
+            R[rb], reinterpret_cast<f32x4*>(sv.R + ch * CL * HD + tile_off(rb, jv >> 4)));
       store_tile_t(R[rb], RB, 16 * rb, 0);
     }
     // U~ = Tb R (Tb lower triangular: K up to the end of the row block)
@@ -238,7 +241,8 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      *reinterpret_cast<f32x4*>(sv.U + ch * CL * HD + tile_off(rb, jv >> 4)) = U[rb];
+      __builtin_nontemporal_store(
+          U[rb], reinterpret_cast<f32x4*>(sv.U + ch * CL * HD + tile_off(rb, jv >> 4)));
       store_tile_t(U[rb], UB, 16 * rb, 0);
     }
     // S_out = e^(G_last) * S_in + Ke^T U~
@@ -653,7 +657,9 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
       f32x4 dU = zero4();
       mma<SPLIT_A, true>(dU, AQ, 16 * rb, DO, 16 * nw, (16 * rb / 32) * 32, CL);
       mma_k<SPLIT_BW, HD, true>(dU, KE, 16 * rb, DS, 16 * nw);
-      *reinterpret_cast<f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)) = dU;
+      // dU~ and dS_out are streamed out (non-temporal): read only by the next kernel
+      __builtin_nontemporal_store(
+          dU, reinterpret_cast<f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)));
       store_tile_t(dU, DU, 16 * rb, 16 * nw);
     }
     stage(6, 8);                                   // Tb
@@ -680,7 +686,8 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
       float* dSg = bw.dS + ch * HD * HD;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        *reinterpret_cast<f32x4*>(dSg + tile_off(w, (j0 >> 4) + nt)) = dS[nt];
+        __builtin_nontemporal_store(dS[nt],
+                                    reinterpret_cast<f32x4*>(dSg + tile_off(w, (j0 >> 4) + nt)));
 #pragma unroll
         for (int i = 0; i < 4; ++i) dS[nt][i] *= sm.gam[16 * w + drow(i)];
       }
