@@ -46,6 +46,10 @@ MUTANTS = {
     "raw_bwd_sigmoid": ("const double dz = dg[i * K + c] * (-ea) * sigmoid(z);",
                         "const double dz = dg[i * K + c] * (-ea) * sigmoid(-z);"),
     "dAlog_drop_g": ("dAlog += dg[i * K + c] * tk.g[i * K + c];", "dAlog += dg[i * K + c];"),
+    "softplus_large_drop_x": ("if (x > 30.0) return x + std::log1p(std::exp(-x));",
+                              "if (x > 30.0) return std::log1p(std::exp(-x));"),
+    "softplus_large_sign": ("if (x > 30.0) return x + std::log1p(std::exp(-x));",
+                            "if (x > 30.0) return -x + std::log1p(std::exp(-x));"),
 }
 
 
@@ -106,6 +110,20 @@ def battery(lib):
         o2 = s * (b[0] * (q[1] @ ka) * v[0] + b[1] * (q[1] @ k[1]) * u2)
         if not (rel_l2(o[0, 0], o1) < 1e-12 and rel_l2(o[1, 0], o2) < 1e-12):
             failed.append(f"two_tokens_{gate}_{l2}")
+    # closed form: two tokens, raw gate with softplus arguments around and
+    # above the large-argument branch point (30)
+    p = tiny_problem(rng, [2], 1, 5, 3, gate="raw")
+    p["dt_bias"] = np.zeros((1, 5))
+    p["gate"] = np.array([25.0, 29.5, 30.5, 38.0, 45.0])[None, None, :].repeat(2, axis=0)
+    p["A_log"] = np.array([-np.log(35.0)])
+    o = _run(lib, p)
+    q, k, v, b = p["q"][:, 0], p["k"][:, 0], p["v"][:, 0], p["beta"][:, 0]
+    a = np.exp(-np.exp(p["A_log"][0]) * np.logaddexp(0.0, p["gate"][:, 0]))
+    ka = a[1] * k[0]
+    u2 = v[1] - b[0] * (k[1] @ ka) * v[0]
+    o2 = 5 ** -0.5 * (b[0] * (q[1] @ ka) * v[0] + b[1] * (q[1] @ k[1]) * u2)
+    if not rel_l2(o[1, 0], o2) < 1e-12:
+        failed.append("two_tokens_raw_large")
     # finite differences
     for gate, l2 in (("g", False), ("raw", False), ("g", True), ("raw", True)):
         p = tiny_problem(rng, [3, 2], 1, 4, 3, gate=gate, l2norm=l2)

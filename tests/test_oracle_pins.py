@@ -127,6 +127,43 @@ def test_two_tokens_raw_gate():
         assert rel_l2(o[1, h], o2) < 1e-13
 
 
+def _large_argument_problem(seed):
+    """Two tokens with the raw gate's softplus argument a + dt_bias in
+    [25, 45]: both sides of the oracle's x > 30 branch. A_log = -log(35)
+    keeps g = -softplus(x)/35 near -1, so the decay is neither 0 nor 1 and
+    softplus(x) ~ x + e^-x is what the output depends on."""
+    rng = np.random.default_rng(seed)
+    K, V, H = 6, 3, 2
+    p = tiny_problem(rng, [2], H, K, V, gate="raw")
+    x = rng.uniform(25.0, 45.0, (2, H, K))
+    x[:, :, 0], x[:, :, 1] = 29.5, 30.5           # straddle the branch point
+    p["dt_bias"] = rng.normal(0.0, 0.5, (H, K))
+    p["gate"] = x - p["dt_bias"][None]
+    p["A_log"] = np.full(H, -np.log(35.0))
+    return p
+
+
+def test_two_tokens_raw_gate_large_arguments():
+    """softplus for a + dt_bias > 30: g = -exp(A_log) * (x + log1p(e^-x)),
+    checked against the closed form of two tokens (numpy's logaddexp as
+    softplus), and the backward against central differences."""
+    p = _large_argument_problem(17)
+    o = _fwd(p)
+    K = p["q"].shape[2]
+    for h in range(p["q"].shape[1]):
+        x = p["gate"][:, h] + p["dt_bias"][h]
+        assert np.all(x > 24.0) and np.any(x > 30.0) and np.any(x < 30.0)
+        g = -np.exp(p["A_log"][h]) * _softplus(x)
+        o1, o2 = _two_token_ref(p["q"][:, h], p["k"][:, h], p["v"][:, h], p["beta"][:, h],
+                                np.exp(g), K ** -0.5)
+        assert rel_l2(o[0, h], o1) < 1e-13
+        assert rel_l2(o[1, h], o2) < 1e-13
+    g = _bwd(p)
+    for inp, out in (("gate", "da"), ("A_log", "dA_log"), ("dt_bias", "ddt_bias")):
+        fd = _fd_grad(p, inp, h=1e-5)
+        assert rel_l2(g[out], fd) < 1e-6, (inp, rel_l2(g[out], fd))
+
+
 def test_two_tokens_l2_norm():
     """Fused L2 norm: q <- q (sum q^2 + eps)^-1/2, k likewise, before the rule."""
     rng = np.random.default_rng(8)
