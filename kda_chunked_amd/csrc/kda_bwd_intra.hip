@@ -126,6 +126,7 @@ struct BwdIntraSmem {
   float dbc[4][CL], dbr[2][CL];
   float GL[HD], gam[HD], dGL[HD], dgam[HD];
   float Gref[5][HD];       // G before block I (I = 0..3) and G_last (I = 4)
+  float accA[NTHR];        // raw form: each thread's share of the dA_log partial
   int calm_blk[4];
   int calm_chunk;
 };
@@ -297,6 +298,26 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   f32x4 adq[4], adk[4], adG[4], aP[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) adq[nt] = adk[nt] = adG[nt] = aP[nt] = zero4();
+  // Raw form: this thread's share of the chunk's dA_log partial
+  // sum_j g_j dg_j = sum_r dG_r G_r, taken term by term with bounded weights:
+  // a term of dG_r that carries e^(G_r) is weighted by G_r, the e^(G_last - G_r)
+  // terms by G_last - G_r, and a pair term p (entering dG_r with + and dG_i
+  // with -) by G_r - G_i, split as (G_r - rho) - (G_i - rho) around a
+  // reference rho shared by both members. Weighting dG_r by G_r directly
+  // would multiply the rounding of cancelling O(1) pair sums by |G|, which
+  // reaches 10^3 under fast decay.
+  // Each phase sums its terms in a register and adds them to the thread's
+  // LDS slot (no register stays live across phases for this).
+  const bool raw = d.raw;
+  float accA = 0.f;
+#define FLUSH_A()             \
+  do {                         \
+    if (raw) {                 \
+      sm.accA[t] += accA;      \
+      accA = 0.f;              \
+    }                          \
+  } while (0)
+  if (raw) sm.accA[t] = 0.f;
 
   // ------------------------------------------------------------ P2: dQd, dKd
   // dR (= dv in fp32) enters as its bf16 rounding, the dv output of the reverse scan
@@ -343,6 +364,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           const float p = d.scale * a[nt][i] * fexp(eG[nt][i]);
           adq[nt][i] += p;
           adG[nt][i] += p * EQ(nt, i);
+          
         }
     }
     {
@@ -357,6 +379,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           const float p2 = -b[nt][i] * fexp(eG[nt][i]);
           adk[nt][i] += p2;
           adG[nt][i] += p2 * EK(nt, i);
+          
         }
     }
     __syncthreads();
@@ -410,13 +433,18 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         const float p3 = a[nt][i] * fexp(sm.GL[c] - eG[nt][i]);
         adk[nt][i] += p3;
         aP[nt][i] += p3 * EK(nt, i);
+        if (raw) accA += p3 * EK(nt, i) * (sm.GL[c] - eG[nt][i]);
       }
     }
     // dA_qk = scale dO U~^T: rows 16 rb, columns i in tiles 2 chh, 2 chh + 1
     dAq[0] = dAq[1] = zero4();
     mma_row<KDA_SPLIT_B5, 2, false, true>(dAq, DOP, 16 * rb, AP, 32 * chh, 0, HD);
     __syncthreads();
-    if (t < HD) sm.dGL[t] = sm.dgam[t] * sm.gam[t];
+    if (t < HD) {
+      sm.dGL[t] = sm.dgam[t] * sm.gam[t];
+      if (raw) accA += sm.dGL[t] * sm.GL[t];
+    }
+    FLUSH_A();
   }
 
   // ------------------------------------------------------------ P4: dTb = dU~ R^T
@@ -528,6 +556,16 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
                  (sm.dbr[0][t] + sm.dbr[1][t]);
   }
 
+  // adG holds only the state terms of P2 so far (each carries e^(G_r)): weight G_r
+  if (raw) {
+    float sw = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sw += adG[nt][i] * eG[nt][i];
+    sm.accA[t] += sw;
+  }
+
   // ------------------------------------------------------------ P6: decayed-product backward
   // dq_r += sum_i dA_qk[r][i] k^_i e^(G_r - G_i),  dk_r += sum_i dA_kk[r][i] k^_i e^(G_r - G_i),
   // dk_i += sum_r (dA_qk[r][i] q^_r + dA_kk[r][i] k^_r) e^(G_r - G_i), with the matching
@@ -585,6 +623,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           adq[nt][i] += dqa;
           adk[nt][i] += dka;
           adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
+          // one reference (the chunk start, G = 0) for both members of every pair
+          if (raw) accA += (dqa * EQ(nt, i) + dka * EK(nt, i)) * eG[nt][i];
         }
     } else if (rb > 0 || blk_calm) {
       // Column blocks J = 0 .. jend (the diagonal block only when calm): the
@@ -613,7 +653,10 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const float ref = sm.Gref[jend + 1][64 * chh + 16 * nt + dcol()];
+        const int c = 64 * chh + 16 * nt + dcol();
+        const float ref = sm.Gref[jend + 1][c];
+        // pair reference: G before this row block (also the column side's)
+        const float rho = sm.Gref[rb][c];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e1 = fexp(eG[nt][i] - ref);
@@ -621,9 +664,11 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           adq[nt][i] += dqa;
           adk[nt][i] += dka;
           adG[nt][i] += dqa * EQ(nt, i) + dka * EK(nt, i);
+          if (raw) accA += (dqa * EQ(nt, i) + dka * EK(nt, i)) * (eG[nt][i] - rho);
         }
       }
     }
+    FLUSH_A();
     __syncthreads();
     // X^T [c][32 I + ...]: q^_r, k^_r times e^(G_r) or e^(G_r - rho_start(I)),
     // rho_start(I) = G before block I
@@ -654,6 +699,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
           const float dka = ac[nt][i] * fexp(-eG[nt][i]);
           adk[nt][i] += dka;
           adG[nt][i] -= dka * EK(nt, i);
+          if (raw) accA -= dka * EK(nt, i) * eG[nt][i];
         }
     } else if (rb < 3 || blk_calm) {
       // Row blocks I = 3 down to istart (the diagonal block only when calm):
@@ -674,7 +720,26 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
             for (int i = 0; i < 4; ++i) ac[nt][i] *= di;
           }
         }
+        // raw form: block I's pair terms take the reference rho = G before
+        // block I, as on the row side; their sum is the weighted running sum
+        // after block I's product minus the same sum before it (both bounded:
+        // every weight is x e^-x with x = G_i - rho)
+        auto weighted = [&]() -> float {
+          float sw = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const float rho = sm.Gref[I][64 * chh + 16 * nt + dcol()];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = eG[nt][i] - rho;
+              sw += ac[nt][i] * (fexp(-x) * EK(nt, i) * x);
+            }
+          }
+          return sw;
+        };
+        const float before = raw ? weighted() : 0.f;
         mma_row<KDA_SPLIT_B7, 4>(ac, DAT, 16 * rb, XT, 64 * chh, 32 * I, 32 * I + 32);
+        if (raw) accA -= weighted() - before;
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -687,6 +752,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         }
       }
     }
+    FLUSH_A();
     __syncthreads();
     if (!calm && !(sm.calm_blk[0] & sm.calm_blk[1] & sm.calm_blk[2] & sm.calm_blk[3])) {
       // Diagonal blocks too wide for one reference: every pair (r, i) of the
@@ -711,6 +777,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       const int I = t >> 7, c = t & 127;
       if (!sm.calm_blk[I]) {
         float g[16], qv[16], kv[16], sq[16], sk[16], sg[16];
+        float sa = 0.f;   // sum of the block's pair terms times G_r - G_i
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           g[j] = Xg[16 * I + j][c];
@@ -742,9 +809,11 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
             if (i < r) {
               sg[r] += wgt * ke;
               sg[i] -= s2 * kv[i];
+              sa += wgt * ke * (g[r] - g[i]);
             }
           }
         }
+        if (raw) accA += sa;
         // each thread overwrites only the entries it read
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -836,7 +905,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     for (int I2 = 0; I2 < I; ++I2) carry += sm.u.p7.totP[I2][cc];
     // every value first, then the stores: a store between two uses of the
     // loaded a would make each use wait for it
-    float pdt = 0.f, pA = 0.f;
+    float pdt = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float dg = 16 * I + j < n ? v[j] + carry : 0.f;
@@ -844,7 +913,6 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
         const float z = av[j] + dtb7;
         const float dz = dg * (-ea7) * sigmoid(z);
         pdt += dz;
-        pA += dg * (-ea7 * softplus(z));
         v[j] = dz;
       } else {
         v[j] = dg;
@@ -863,7 +931,7 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     }
     if (d.raw) {
       sm.u.p7.red[0][I][cc] = pdt;
-      sm.u.p7.red[1][I][cc] = pA;
+      sm.u.p7.red[1][I][cc] = sm.accA[t] + accA;
     }
     __syncthreads();
     if (d.raw) {
@@ -966,6 +1034,20 @@ __global__ __launch_bounds__(FIN_SL * HD) void finalize_kernel(Dims d, ChunkTabl
 hipError_t launch_finalize(const Dims& d, const ChunkTable& ct, const BwdOut& out,
                            const BwdWork& bw, hipStream_t s) {
   hipLaunchKernelGGL(finalize_kernel, dim3(d.H), dim3(FIN_SL * HD), 0, s, d, ct, out, bw);
+  return hipGetLastError();
+}
+
+// A plain fill kernel rather than a memset, so that the call also behaves in
+// a captured graph.
+__global__ __launch_bounds__(256) void zero_params_kernel(float* dA_log, float* ddt_bias, int H) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < H) dA_log[i] = 0.f;
+  if (i < H * HD) ddt_bias[i] = 0.f;
+}
+
+hipError_t launch_zero_params(const Dims& d, float* dA_log, float* ddt_bias, hipStream_t s) {
+  hipLaunchKernelGGL(zero_params_kernel, dim3((d.H * HD + 255) / 256), dim3(256), 0, s, dA_log,
+                     ddt_bias, d.H);
   return hipGetLastError();
 }
 

@@ -10,11 +10,10 @@ The gated delta rule and its chunked form are those of flashinfer PR #8909
 oracle is the FP64 token recurrence, on the same seeded inputs.
 
 dA_log[h] = sum_{t,c} dg g and ddt_bias[h,c] = sum_t da are sums whose terms
-cancel by factors of 10^2 .. 10^4 under fast decay (measured on the oracle),
-so their relative error is not a property of the kernels. For them the error
-is bounded by 1e-2 times the sum of the terms' magnitudes (sum |dg g| per head,
-sum |da| per head and channel), from the oracle: each term accurate to 1 %
-in aggregate. Every other output keeps the whole-tensor relative-L2 bound.
+cancel by factors of 10^2 .. 10^3 under fast decay (measured on the oracle).
+They keep the whole-vector relative-L2 bound of every gate gradient (1e-2);
+the error relative to the sum of the terms' magnitudes (sum |dg g| per head,
+sum |da| per head and channel, from the oracle) is printed beside it.
 """
 
 import numpy as np
@@ -30,7 +29,6 @@ CASES = [
     ("steep", (float(np.log(16.0)), float(np.log(64.0))), [200, 77, 300], False),
     ("near-calm", (float(np.log(2.0)), float(np.log(8.0))), [257, 130], True),
 ]
-SUM_TOL = 1e-2
 
 
 def _term_scales(inp, gref):
@@ -58,9 +56,8 @@ def test_fast_decay_parity(name, alog, docs, l2):
     sA, sdt = _term_scales(inp, gref)
     errs["dA_log/sum|terms|"] = float(np.max(np.abs(gg["dA_log"] - gref["dA_log"]) / sA))
     errs["ddt_bias/sum|terms|"] = float(np.max(np.abs(gg["ddt_bias"] - gref["ddt_bias"]) / sdt))
-    print(f"[parity] {name} " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items())
-          + f" (rel-L2 dA_log={rel_l2(gg['dA_log'], gref['dA_log']):.3e},"
-          f" ddt_bias={rel_l2(gg['ddt_bias'], gref['ddt_bias']):.3e})", flush=True)
-    tol = dict(TOL, **{"dA_log/sum|terms|": SUM_TOL, "ddt_bias/sum|terms|": SUM_TOL})
-    bad = {k: v for k, v in errs.items() if not v <= tol[k]}
+    errs["dA_log"] = rel_l2(gg["dA_log"], gref["dA_log"])
+    errs["ddt_bias"] = rel_l2(gg["ddt_bias"], gref["ddt_bias"])
+    print(f"[parity] {name} " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if k in TOL and not v <= TOL[k]}
     assert not bad, bad
