@@ -53,7 +53,9 @@
  *    launch failure returns KDA_ERR_DEVICE. kda_last_error() gives a
  *    thread-local message for the last failing call of the thread.
  *  - Stream: all work is enqueued on `stream` in order; nothing blocks the
- *    host. T == 0 returns KDA_OK without launching.
+ *    host. T == 0: kda_fwd launches nothing; kda_bwd in the raw gate form
+ *    writes zeros to dA_log and ddt_bias (sums over no tokens) with one small
+ *    fill kernel and launches nothing else.
  *  - Determinism: no floating-point atomics; results are bitwise identical
  *    run to run, and the replay backward is bitwise identical to the saved
  *    backward of the same inputs.
@@ -73,7 +75,8 @@ extern "C" {
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARGUMENT = 1,   /* bad scalar, null or misaligned pointer */
-  KDA_ERR_UNSUPPORTED = 2,        /* a valid request this build does not serve (dk, dv != 128) */
+  KDA_ERR_UNSUPPORTED = 2,        /* a valid request this build does not serve: dk, dv != 128,
+                                     H > 65535, or more than 2^29 (document, head) pairs */
   KDA_ERR_WORKSPACE_TOO_SMALL = 3,
   KDA_ERR_DEVICE = 4              /* a HIP call failed; see kda_last_error() */
 } kda_status;
@@ -93,28 +96,49 @@ typedef struct {
 
 /* Size in bytes of the saved forward set of a problem: what kda_fwd writes
  * when `saved` is non-NULL and what kda_bwd reads. Opaque to the caller;
- * reusable across calls of problems with the same T, H and num_seqs. */
+ * reusable across calls of problems with the same T, H and num_seqs.
+ * Defined by the saved backward path of the KDA training package (PR #8909,
+ * opening section: the backward either uses the saved forward set or replays
+ * the forward from a checkpoint). Returns 0 for an invalid problem. */
 size_t kda_saved_bytes(const kda_problem* p);
 
-/* Size in bytes of the scratch workspace a call needs.
- *   backward = 0: kda_fwd;  backward = 1: kda_bwd.
- *   replay   = 1 with backward = 1: kda_bwd called with saved == NULL. */
+/* Size in bytes of the scratch workspace a call needs. The caller allocates
+ * it; a workspace may be reused by later calls ordered on the same stream
+ * (workspace reuse across calls as in PR #7774's test list).
+ *   backward = 0, replay = 0: kda_fwd with saved != NULL;
+ *   backward = 0, replay = 1: kda_fwd with saved == NULL (the forward half of
+ *                             a replay pair; it needs private room for the
+ *                             per-chunk states);
+ *   backward = 1, replay = 0: kda_bwd with saved != NULL;
+ *   backward = 1, replay = 1: kda_bwd with saved == NULL.
+ * Returns 0 for an invalid problem. */
 size_t kda_workspace_bytes(const kda_problem* p, int backward, int replay);
 
-/* Forward. Writes o, and the saved forward set when `saved` is non-NULL.
+/* Forward (PR #8909, opening section: the package's forward over the gate
+ * forms g / raw and the optional fused Q/K L2 norm; PR #7176, opening
+ * section: documents packed into one sequence, state reset at each document
+ * start). Writes o, and the saved forward set when `saved` is non-NULL.
  * g_or_a is g (fp32) for KDA_GATE_G or a (bf16) for KDA_GATE_RAW; A_log and
- * dt_bias are read only for KDA_GATE_RAW (may be NULL otherwise). */
+ * dt_bias are read only for KDA_GATE_RAW (may be NULL otherwise).
+ * workspace_bytes must be at least kda_workspace_bytes(p, 0, saved == NULL).
+ * Errors: KDA_ERR_INVALID_ARGUMENT (bad scalar, NULL or misaligned pointer),
+ * KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, all before any launch;
+ * KDA_ERR_DEVICE if a launch fails. */
 kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
                    const void* beta, const void* g_or_a, const float* A_log,
                    const float* dt_bias, const int32_t* cu_seqlens, void* o, void* saved,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward of L = sum <o, dO>. With saved != NULL it reads the set written
+/* Backward of L = sum <o, dO> (PR #8909, opening section: the saved and
+ * replay backward paths, and the gate gradients dg, dA_log and dt_bias that
+ * its accuracy fix is about). With saved != NULL it reads the set written
  * by kda_fwd for the same inputs; with saved == NULL it first recomputes the
  * forward state from q, k, v, beta and the gate (replay; o is not written).
  * Writes dq, dk, dv, dbeta and, for KDA_GATE_G, dg_or_da = dg (fp32); for
  * KDA_GATE_RAW, dg_or_da = da (bf16), dA_log and ddt_bias. With the fused L2
- * norm, dq and dk are gradients with respect to the raw (unnormalised) q, k. */
+ * norm, dq and dk are gradients with respect to the raw (unnormalised) q, k.
+ * workspace_bytes must be at least kda_workspace_bytes(p, 1, saved == NULL).
+ * Errors as for kda_fwd. */
 kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
                    const void* beta, const void* g_or_a, const float* A_log,
                    const float* dt_bias, const int32_t* cu_seqlens, const void* dO,
@@ -130,6 +154,8 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
 typedef void (*kda_launch_hook)(void* user, const char* kernel, int end, void* stream);
 void kda_set_launch_hook(kda_launch_hook hook, void* user);
 
+/* Error reporting (PR #7774's review: invalid requests such as a head count
+ * below one are rejected with a clear validation error). */
 const char* kda_status_string(kda_status s);
 const char* kda_last_error(void);   /* thread-local; "" if none */
 int kda_abi_version(void);          /* KDA_ABI_VERSION */

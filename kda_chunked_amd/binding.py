@@ -194,7 +194,7 @@ class KDA:
         self.p = problem(T, H, num_seqs, gate, l2norm, scale, l2_eps)
         self.gate = gate
         self.device = torch.device(device)
-        nbytes = max(workspace_bytes(self.p, False), workspace_bytes(self.p, True, True))
+        nbytes = max(workspace_bytes(self.p, False, True), workspace_bytes(self.p, True, True))
         u8 = dict(dtype=torch.uint8, device=self.device)
         self.workspace = torch.empty(max(nbytes, 1), **u8)
         self.saved = torch.empty(max(saved_bytes(self.p), 1), **u8)

@@ -61,20 +61,18 @@ kda::ChunkTable carve_table(Carver& c, const Sizes& s) {
   return ct;
 }
 
-// with_states = 0 leaves out S_in and R (a forward that saves nothing).
-kda::SavedSet carve_saved(Carver& c, const Sizes& s, int with_states) {
+// The saved forward set: per-chunk matrices, L2 scalars, states and panels.
+kda::SavedSet carve_saved(Carver& c, const Sizes& s) {
   kda::SavedSet sv{};
   const size_t mat = (size_t)s.NC * s.H * 64 * 64;
   sv.Tm = c.take<float>(mat);
   sv.Akk = c.take<float>(mat);
   sv.rq = c.take<float>((size_t)s.T * s.H);
   sv.rk = c.take<float>((size_t)s.T * s.H);
-  if (with_states) {
-    sv.S_in = c.take<float>((size_t)s.NC * s.H * 128 * 128);
-    sv.R = c.take<float>((size_t)s.NC * s.H * 64 * 128);
-    sv.U = c.take<float>((size_t)s.NC * s.H * 64 * 128);
-    sv.panels = c.take<uint16_t>((size_t)s.NC * s.H * kda::fwd_panel::ELEMS);
-  }
+  sv.S_in = c.take<float>((size_t)s.NC * s.H * 128 * 128);
+  sv.R = c.take<float>((size_t)s.NC * s.H * 64 * 128);
+  sv.U = c.take<float>((size_t)s.NC * s.H * 64 * 128);
+  sv.panels = c.take<uint16_t>((size_t)s.NC * s.H * kda::fwd_panel::ELEMS);
   return sv;
 }
 
@@ -100,6 +98,17 @@ kda_status check_problem(const kda_problem* p) {
                 p->num_seqs);
   if (p->num_seqs > (1 << 24))
     return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = %d is too large", p->num_seqs);
+  if (p->H > 65535)
+    return fail(KDA_ERR_UNSUPPORTED, "H = %d exceeds 65535 heads (a launch grid dimension)",
+                p->H);
+  {
+    // the scans launch one workgroup per (document, head, column tile), with
+    // the pairs rounded up to a multiple of 8: 4 * ceil8(N * H) must fit an int
+    const int64_t pairs = (int64_t)p->num_seqs * p->H;
+    if (4 * ((pairs + 7) / 8 * 8) >= ((int64_t)1 << 31))
+      return fail(KDA_ERR_UNSUPPORTED, "num_seqs * H = %lld (document, head) pairs exceeds 2^29",
+                  (long long)pairs);
+  }
   if (p->dk != 128 || p->dv != 128)
     return fail(KDA_ERR_UNSUPPORTED, "dk = %d, dv = %d: this build serves 128, 128", p->dk,
                 p->dv);
@@ -132,10 +141,11 @@ kda::Dims dims_of(const kda_problem* p) {
   return d;
 }
 
-size_t fwd_ws_bytes(const Sizes& s) {
+// A forward that saves nothing keeps its per-chunk set in the workspace.
+size_t fwd_ws_bytes(const Sizes& s, int nosave) {
   Carver c(nullptr);
   carve_table(c, s);
-  carve_saved(c, s, 1);   // used when the caller saves nothing
+  if (nosave) carve_saved(c, s);
   return c.off;
 }
 
@@ -143,9 +153,7 @@ size_t bwd_ws_bytes(const Sizes& s, int replay) {
   Carver c(nullptr);
   carve_table(c, s);
   carve_bwd(c, s);
-  if (replay) {
-    carve_saved(c, s, 1);
-  }
+  if (replay) carve_saved(c, s);
   return c.off;
 }
 
@@ -168,14 +176,14 @@ extern "C" {
 size_t kda_saved_bytes(const kda_problem* p) {
   if (check_problem(p) != KDA_OK) return 0;
   Carver c(nullptr);
-  carve_saved(c, sizes_of(p), 1);
+  carve_saved(c, sizes_of(p));
   return c.off;
 }
 
 size_t kda_workspace_bytes(const kda_problem* p, int backward, int replay) {
   if (check_problem(p) != KDA_OK) return 0;
   const Sizes s = sizes_of(p);
-  return backward ? bwd_ws_bytes(s, replay) : fwd_ws_bytes(s);
+  return backward ? bwd_ws_bytes(s, replay != 0) : fwd_ws_bytes(s, replay != 0);
 }
 
 kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
@@ -200,7 +208,7 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   if (saved && !aligned(saved)) return fail(KDA_ERR_INVALID_ARGUMENT, "saved is not 16-byte aligned");
   REQUIRE_PTR(workspace, "workspace");
   const Sizes s = sizes_of(p);
-  const size_t need = fwd_ws_bytes(s);
+  const size_t need = fwd_ws_bytes(s, saved == nullptr);
   if (workspace_bytes < need)
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
                 workspace_bytes, need);
@@ -210,10 +218,12 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   hipStream_t hs = static_cast<hipStream_t>(stream);
   Carver wc(workspace);
   const kda::ChunkTable ct = carve_table(wc, s);
-  kda::SavedSet sv = carve_saved(wc, s, 1);   // used when nothing is saved
+  kda::SavedSet sv;
   if (saved) {
     Carver sc(saved);
-    sv = carve_saved(sc, s, 1);
+    sv = carve_saved(sc, s);
+  } else {
+    sv = carve_saved(wc, s);   // private per-chunk set in the workspace
   }
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, saved != nullptr, hs));
@@ -232,7 +242,14 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   kda_status st = check_problem(p);
   if (st != KDA_OK) return st;
   if (p->T == 0) {
-    // no tokens: the parameter gradients are zero sums; leave them to the caller
+    // no tokens: the raw form's parameter gradients are sums over nothing
+    if (p->gate == KDA_GATE_RAW) {
+      REQUIRE_PTR(dA_log, "dA_log");
+      REQUIRE_PTR(ddt_bias, "ddt_bias");
+      const kda::Dims d = dims_of(p);
+      hipStream_t hs = static_cast<hipStream_t>(stream);
+      LAUNCH("zero_params", kda::launch_zero_params(d, dA_log, ddt_bias, hs));
+    }
     return KDA_OK;
   }
   REQUIRE_PTR(q, "q");
@@ -270,10 +287,10 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   const kda::BwdWork bw = carve_bwd(wc, s);
   kda::SavedSet sv;
   if (replay) {
-    sv = carve_saved(wc, s, 1);
+    sv = carve_saved(wc, s);
   } else {
     Carver sc(const_cast<void*>(saved));
-    sv = carve_saved(sc, s, 1);
+    sv = carve_saved(sc, s);
   }
   const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));

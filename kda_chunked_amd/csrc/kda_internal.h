@@ -113,5 +113,7 @@ hipError_t launch_bwd_intra(const Dims& d, const Inputs& in, const ChunkTable& c
                             const BwdWork& bw, hipStream_t s);
 hipError_t launch_finalize(const Dims& d, const ChunkTable& ct, const BwdOut& out,
                            const BwdWork& bw, hipStream_t s);
+// Raw form with T == 0: dA_log[H] and ddt_bias[H, 128] are sums over no tokens.
+hipError_t launch_zero_params(const Dims& d, float* dA_log, float* ddt_bias, hipStream_t s);
 
 }  // namespace kda

@@ -60,6 +60,9 @@ def test_sizes():
     assert s >= nc * 4 * 128 * 128 * 4 + 3 * nc * 4 * 64 * 64 * 4
     assert B.workspace_bytes(p, True, True) > B.workspace_bytes(p, True, False)
     assert B.workspace_bytes(p, False) > 0
+    # a saving forward keeps its per-chunk set in `saved`, not in the workspace
+    assert B.workspace_bytes(p, False, True) >= B.workspace_bytes(p, False, False) + s
+    assert B.workspace_bytes(p, False, False) < 4096
     # invalid problems size to zero
     assert B.saved_bytes(_p(H=0)) == 0
     assert B.workspace_bytes(_p(dk=64), False) == 0
@@ -84,6 +87,8 @@ def _fwd_status(p, **ptrs):
     (dict(T=-1), 1, "negative"),
     (dict(dk=64), 2, "128"),
     (dict(dv=256), 2, "128"),
+    (dict(H=65536), 2, "65535"),
+    (dict(H=65535, num_seqs=1 << 14), 2, "2^29"),
 ])
 def test_invalid_problem_rejected_before_launch(kw, status, msg):
     rc, err = _fwd_status(_p(**kw))
@@ -106,6 +111,37 @@ def test_small_workspace_rejected():
 
 def test_zero_tokens_is_a_no_op():
     rc, _ = _fwd_status(_p(T=0), q=None, k=None, v=None)
+    assert rc == 0
+
+
+def test_saving_forward_needs_no_private_set():
+    p = _p()
+    small = B.workspace_bytes(p, False, False)
+    rc, err = _fwd_status(p, saved=16, ws_bytes=small)
+    assert rc == 0 or "workspace" not in err
+    rc, err = _fwd_status(p, saved=None, ws_bytes=small)
+    assert rc == 3 and "workspace" in err
+
+
+def _bwd_status(p, **ptrs):
+    lib = B.lib()
+    args = dict(dA_log=16, ddt_bias=16)
+    args.update(ptrs)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    rc = lib.kda_bwd(ctypes.byref(p), *([None] * 10), None, None, None, None, None,
+                     vp(args["dA_log"]), vp(args["ddt_bias"]), None, 0, None)
+    return rc, lib.kda_last_error().decode()
+
+
+def test_zero_tokens_raw_backward_validates_parameter_gradients():
+    """With T == 0 the raw form's dA_log and ddt_bias are zero sums that the
+    library writes; their pointers are checked on the host first (the write
+    itself needs a GPU and is covered by the GPU tests)."""
+    rc, err = _bwd_status(_p(T=0, gate="raw"), dA_log=None)
+    assert rc == 1 and "dA_log" in err
+    rc, err = _bwd_status(_p(T=0, gate="raw"), ddt_bias=18)
+    assert rc == 1 and "ddt_bias" in err
+    rc, _ = _bwd_status(_p(T=0, gate="g"), dA_log=None, ddt_bias=None)
     assert rc == 0
 
 
