@@ -8,21 +8,27 @@ flashinfer PR #8909, timing tables). Inputs are seeded synthetic data that is
 resident in HBM before the timed region starts.
 
 Prints one JSON line: throughput in tokens/s (packed tokens x all heads per
-step), the roofline of the dominant kernel (timed live with HIP events on
-the stream the library launches on, through the library's launch hook), and
-the FP64 oracle timed on the host on a bounded sample of the same workload.
+step); the roofline of the dominant contraction kernel (the longest MFMA
+kernel of the step, timed live with HIP events on the stream the library
+launches on, through the library's launch hook) as its algorithmic FLOP rate
+against the dense bf16 MFMA peak, with its compulsory HBM bytes and the
+measured HBM traffic beside it; the whole step on the method's own work and
+compulsory bytes; and the FP64 oracle timed on the host on a bounded sample of
+the same workload.
 
 Besides the timed steps it times, outside the timed region, the units of the
 deterministic package's protocol: fwd alone, bwd alone and the replay pair
 (forward without saving, backward recomputing the forward), each the median
-of 15 samples of 20 back-to-back calls.
+of 15 samples of 20 back-to-back calls; and the same units for the package's
+other timing rows that this repository reproduces (4doc saved and replay, R2,
+m2), as extra keys.
 
 HBM traffic and MFMA utilisation come from rocprofv3 counter runs whose
 summaries sit in profiles/; they are reported only while the kernel sources
 still hash to the fingerprint recorded with them (else null).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 1doc]
-                       [--no-cpu] [--no-units] [--calibrate-copy MIB]
+                       [--no-cpu] [--no-units] [--no-rows] [--calibrate-copy MIB]
        python bench.py --pmc-summary DIR     (tabulate a rocprofv3 --pmc run)
        python bench.py --trace-summary DIR   (tabulate a rocprofv3 --kernel-trace run)
        python bench.py --fingerprint         (hash of the kernel sources)
@@ -50,8 +56,8 @@ METRIC = "KDA fwd+bwd ms & tokens/s, 16384 tok x 64 heads, d=128; MFMA util %"
 CSRC = os.path.join(ROOT, "kda_chunked_amd", "csrc")
 # fwd+bwd ms per row on NVIDIA GB300 ("after head" column of the GB300 timing
 # table on flashinfer PR #8909): another machine's numbers, context only.
-PAGE_FWD_BWD_MS = {"1doc:g:fused": 4.4696, "4doc:raw:off": 4.2789, "R2:raw:off": 0.6658,
-                   "m2:g:off": 0.5285}
+PAGE_FWD_BWD_MS = {"1doc:g:fused": 4.4696, "4doc:raw:off": 4.2789,
+                   "4doc:raw:off:replay": 5.0539, "R2:raw:off": 0.6658, "m2:g:off": 0.5285}
 PROFILES = os.path.join(ROOT, "profiles")
 
 # Algorithmic multiply-adds per full 64-token chunk and head, per kernel: the
@@ -96,23 +102,57 @@ def algo_bytes_per_chunk_head(kernel: str, raw: bool) -> int:
     }[kernel]
 
 
+# The method's own work and compulsory HBM traffic per token-head (one token
+# of one head), independent of this design's intermediates:
+# * FLOP: a full 64-token chunk-head takes 4.51 M multiply-adds forward
+#   (A_kk 0.26 M, A_qk 0.27 M, UT solve 0.04 M, W 0.27 M, U 0.27 M, W S 1.05 M,
+#   K_dec^T U~ 1.05 M, O 1.31 M) and 11.17 M backward (reverse state scan
+#   3.41 M, intra-chunk gradients 5.6 M, recomputing A_kk, A_qk, T and U~
+#   2.15 M): 141 k + 349 k FLOP per token-head.
+# * Bytes: every input read once and every output written once at its storage
+#   precision. Gate form g: forward reads q, k, v (bf16), beta (bf16), g (fp32)
+#   and writes o; backward reads those and dO and writes dq, dk, dv, dbeta, dg.
+#   The raw form replaces the fp32 g / dg with a bf16 a / da (A_log, dt_bias
+#   and their gradients are per head, negligible).
+FLOP_PER_TOKEN_HEAD = {"fwd": 2 * 4.51e6 / 64, "bwd": 2 * 11.17e6 / 64}
+COMPULSORY_BYTES_PER_TOKEN_HEAD = {
+    False: {"fwd": 3 * 256 + 2 + 512 + 256, "bwd": 3 * 256 + 2 + 512 + 256 + 3 * 256 + 2 + 512},
+    True: {"fwd": 3 * 256 + 2 + 256 + 256, "bwd": 3 * 256 + 2 + 256 + 256 + 3 * 256 + 2 + 256},
+}
+# The per-chunk backward's own compulsory I/O: q, k, gate, beta, dO in;
+# dq, dk, dbeta, dgate out (dv leaves the reverse scan).
+BWD_INTRA_COMPULSORY_BYTES_PER_TOKEN_HEAD = {
+    False: 256 + 256 + 512 + 2 + 256 + 256 + 256 + 2 + 512,
+    True: 256 + 256 + 256 + 2 + 256 + 256 + 256 + 2 + 256,
+}
+MFMA_KERNELS = ("fwd_prep", "fwd_scan", "fwd_out", "bwd_scan", "bwd_intra")
+
+
 def kernel_roofline(kernel: str, ms: float, chunk_heads: float, raw: bool) -> dict:
-    """The kernel's bound (whichever of its algorithmic FLOP at the bf16 MFMA
-    peak or its algorithmic bytes at the HBM peak takes longer) and the
-    fraction of that peak it reaches."""
+    """A contraction kernel against the dense bf16 MFMA peak: its algorithmic
+    FLOP per launch (the method's products, triangles on their nonzero half,
+    split terms not counted) over its average launch time. The HBM view of the
+    same launch (this design's stored bytes at 8 TB/s) is secondary."""
     flop = 2.0 * MAC_PER_CHUNK_HEAD[kernel] * chunk_heads
     nbytes = float(algo_bytes_per_chunk_head(kernel, raw)) * chunk_heads
-    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
-    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
-    if t_hbm >= t_mfma:
-        ach = nbytes / (ms * 1e-3) / 1e9
-        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": nbytes,
-                "algorithmic_flop_per_launch": flop}
     ach = flop / (ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "algorithmic_bytes_per_launch": nbytes, "algorithmic_flop_per_launch": flop}
+            "algorithmic_flop_per_launch": flop, "design_bytes_per_launch": nbytes,
+            "design_bytes_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def end_to_end(ms_step: float, T: int, H: int, raw: bool) -> dict:
+    """The whole fwd+bwd step on the method's own work and compulsory bytes."""
+    th = float(T) * H
+    flop = th * (FLOP_PER_TOKEN_HEAD["fwd"] + FLOP_PER_TOKEN_HEAD["bwd"])
+    cb = COMPULSORY_BYTES_PER_TOKEN_HEAD[raw]
+    nbytes = th * (cb["fwd"] + cb["bwd"])
+    sec = ms_step * 1e-3
+    return {"algorithmic_flop": flop, "tflops": round(flop / sec / 1e12, 2),
+            "mfma_frac": round(flop / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "compulsory_bytes": nbytes, "gbs": round(nbytes / sec / 1e9, 1),
+            "hbm_frac": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 class HipEvents:
@@ -289,6 +329,72 @@ def cpu_baseline(w, inp, threads):
                       f"{sec:.1f} s on {threads} threads; value scaled to all heads"}
 
 
+def make_runner(w, torch):
+    """Device inputs and output buffers of workload w, and closures that run
+    one fwd (saving or not), one bwd (saved or replay), one step and one
+    replay pair on the current stream."""
+    from kda_chunked_amd.binding import KDA
+    inp, dev = make_device_inputs(w, torch)
+    kda = KDA(w.T, w.H, len(w.doc_lens), gate=w.gate, l2norm=w.l2norm)
+    A_log, dt_bias = dev.get("A_log"), dev.get("dt_bias")
+    grads = dict(dq=torch.empty_like(dev["q"]), dk=torch.empty_like(dev["k"]),
+                 dv=torch.empty_like(dev["v"]), dbeta=torch.empty_like(dev["beta"]),
+                 dgate=torch.empty_like(dev["gate"]))
+    if w.gate == "raw":
+        grads.update(dA_log=torch.empty_like(A_log), ddt_bias=torch.empty_like(dt_bias))
+    o = torch.empty_like(dev["v"])
+    args_in = (dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], dev["cu"])
+
+    def fwd(save=True):
+        kda.forward(*args_in, A_log, dt_bias, save=save, o=o)
+
+    def bwd(replay=False):
+        kda.backward(*args_in, dev["dO"], A_log, dt_bias, replay=replay, out=grads)
+
+    def step():
+        fwd()
+        bwd()
+
+    def replay_pair():
+        fwd(save=False)
+        bwd(replay=True)
+
+    return inp, {"fwd": fwd, "bwd": bwd, "step": step, "replay_pair": replay_pair,
+                 "kda": kda, "dev": dev, "grads": grads, "o": o}
+
+
+# The other rows of the deterministic package's timing table that this
+# repository's workloads reproduce (flashinfer PR #8909, timing tables): timed
+# with the pages' protocol outside the timed region, as extra keys.
+SECONDARY_ROWS = (("4doc", False), ("4doc", True), ("R2", False), ("m2", False), ("1doc", False))
+
+
+def time_row(w, replay, torch) -> dict:
+    """fwd, bwd and fwd+bwd ms (median of 15 samples of 20 back-to-back calls)
+    of one row; replay rows time the pair fwd(no save) + bwd(replay)."""
+    _, run = make_runner(w, torch)
+    for _ in range(3):
+        (run["replay_pair"] if replay else run["step"])()
+    torch.cuda.synchronize()
+    key = f"{w.key}:{'replay' if replay else 'saved'}"
+    if replay:
+        out = {"fwd_ms": time_unit(torch, lambda: run["fwd"](save=False)),
+               "bwd_ms": time_unit(torch, lambda: run["bwd"](replay=True)),
+               "fwd_bwd_ms": time_unit(torch, run["replay_pair"])}
+    else:
+        out = {"fwd_ms": time_unit(torch, run["fwd"]), "bwd_ms": time_unit(torch, run["bwd"]),
+               "fwd_bwd_ms": time_unit(torch, run["step"])}
+    out = {k: round(v, 4) for k, v in out.items()}
+    out["tokens_per_s"] = round(w.T / (out["fwd_bwd_ms"] * 1e-3), 1)
+    page = PAGE_FWD_BWD_MS.get(w.key + (":replay" if replay else ""))
+    out["page_gb300_fwd_bwd_ms"] = page
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    print(f"[bench] row {key}: {out}", file=sys.stderr, flush=True)
+    return {key: out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,6 +404,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-units", action="store_true",
                     help="skip the fwd / bwd / replay unit timings")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other workloads' rows (4doc saved and replay, R2, m2)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the steps, copy MIB MiB device to device once (a plain copy "
                          "kernel of known size, for scaling HBM byte counters)")
@@ -333,34 +441,12 @@ def main():
 
     import torch
     from kda_chunked_amd import inputs as I
-    from kda_chunked_amd.binding import KDA, lib, set_launch_hook
+    from kda_chunked_amd.binding import lib, set_launch_hook
 
     lib()
     w = I.BY_NAME[args.workload]
-    inp, dev = make_device_inputs(w, torch)
-    kda = KDA(w.T, w.H, len(w.doc_lens), gate=w.gate, l2norm=w.l2norm)
-    A_log, dt_bias = dev.get("A_log"), dev.get("dt_bias")
-    grads = dict(dq=torch.empty_like(dev["q"]), dk=torch.empty_like(dev["k"]),
-                 dv=torch.empty_like(dev["v"]), dbeta=torch.empty_like(dev["beta"]),
-                 dgate=torch.empty_like(dev["gate"]))
-    if w.gate == "raw":
-        grads.update(dA_log=torch.empty_like(A_log), ddt_bias=torch.empty_like(dt_bias))
-    o = torch.empty_like(dev["v"])
-    args_in = (dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], dev["cu"])
-
-    def fwd(save=True):
-        kda.forward(*args_in, A_log, dt_bias, save=save, o=o)
-
-    def bwd(replay=False):
-        kda.backward(*args_in, dev["dO"], A_log, dt_bias, replay=replay, out=grads)
-
-    def step():
-        fwd()
-        bwd()
-
-    def replay_pair():
-        fwd(save=False)
-        bwd(replay=True)
+    inp, run = make_runner(w, torch)
+    step, fwd, bwd, replay_pair = run["step"], run["fwd"], run["bwd"], run["replay_pair"]
 
     for _ in range(args.warmup):
         step()
@@ -404,25 +490,35 @@ def main():
     raw = w.gate == "raw"
     per_kernel = {k: kernel_roofline(k, kern_avg[k], chunk_heads, raw)
                   for k in kern_avg if k in MAC_PER_CHUNK_HEAD}
-    dom = max(per_kernel, key=lambda k: kern_avg[k])
+    # the dominant contraction kernel: the longest MFMA kernel of the step
+    dom = max((k for k in per_kernel if k in MFMA_KERNELS), key=lambda k: kern_avg[k])
     fp = fingerprint()
     fig = profile_figures(w.name, dom, fp)
     r = per_kernel[dom]
-    roofline = {"bound": r["bound"], "kernel": dom, "achieved": r["achieved"], "peak": r["peak"],
-                "unit": r["unit"], "frac": r["frac"],
-                "traffic": fig["traffic_bytes"] if fig else None,
-                "algorithmic_bytes_per_launch": r["algorithmic_bytes_per_launch"],
+    sec = kern_avg[dom] * 1e-3
+    comp = float(BWD_INTRA_COMPULSORY_BYTES_PER_TOKEN_HEAD[raw]) * w.T * w.H \
+        if dom == "bwd_intra" else None
+    traffic = fig["traffic_bytes"] if fig else None
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": r["achieved"], "peak": r["peak"],
+                "unit": r["unit"], "frac": r["frac"], "traffic": traffic,
                 "algorithmic_flop_per_launch": r["algorithmic_flop_per_launch"],
                 "avg_launch_ms": round(kern_avg[dom], 4)}
-    # the MFMA view of the same kernel (its algorithmic FLOP at the bf16 peak)
-    roofline["mfma_frac"] = round(r["algorithmic_flop_per_launch"] / (kern_avg[dom] * 1e-3)
-                                  / 1e12 / PEAK_BF16_TFLOPS, 4)
+    if comp is not None:
+        roofline["compulsory_bytes_per_launch"] = comp
+        roofline["compulsory_hbm_frac"] = round(comp / sec / 1e9 / PEAK_HBM_GBS, 4)
+        roofline["traffic_over_compulsory"] = round(traffic / comp, 3) if traffic else None
     if fig:
         roofline["mfma_busy_pct"] = fig.get("mfma_busy_pct")
         roofline["executed_mfma_tflops"] = round(
-            fig["mfma_flop"] / (kern_avg[dom] * 1e-3) / 1e12, 2) if "mfma_flop" in fig else None
+            fig["mfma_flop"] / sec / 1e12, 2) if "mfma_flop" in fig else None
 
-    total_flop = 2.0 * sum(MAC_PER_CHUNK_HEAD.values()) * chunk_heads
+    rows = {}
+    if not args.no_rows:
+        for name, replay in SECONDARY_ROWS:
+            if name == w.name:
+                continue
+            rows.update(time_row(I.BY_NAME[name], replay, torch))
+
     line = {
         "metric": METRIC,
         "value": round(w.T / (ms_step * 1e-3), 1),
@@ -442,15 +538,18 @@ def main():
         "config": {"workload": w.key + ":saved", "tokens": w.T, "heads": w.H, "head_dim": 128,
                    "docs": list(w.doc_lens), "chunk": 64},
         "roofline": roofline,
+        "end_to_end": end_to_end(ms_step, w.T, w.H, raw),
         "token_heads_per_s": round(w.T * w.H / (ms_step * 1e-3), 1),
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kern_avg.items())},
-        "kernels_roofline": {k: {"bound": v["bound"], "frac": v["frac"]}
+        "kernels_roofline": {k: {"bound": v["bound"], "frac": v["frac"],
+                                 "design_bytes_frac": v["design_bytes_frac"]}
                              for k, v in sorted(per_kernel.items())},
-        "algorithmic_tflops": round(total_flop / (ms_step * 1e-3) / 1e12, 2),
         "wall_s_timed": round(wall, 3),
         "source_fingerprint": fp,
     }
     line.update(units)
+    if rows:
+        line["rows"] = rows
     if not args.no_cpu:
         from oracle import kda_oracle as ko
         line["cpu_baseline"] = cpu_baseline(w, inp, ko.default_threads())

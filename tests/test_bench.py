@@ -40,16 +40,41 @@ def test_byte_model_matches_panel_layout():
     assert bench._FWD_CHAIN_B == 2 * p["CHAIN"]
 
 
+def test_method_work_and_compulsory_bytes():
+    """The method's own figures per token-head: 4.51 M + 11.17 M multiply-adds
+    per 64-token chunk-head (141 k + 349 k FLOP per token-head), and every
+    input read and output written once (g form 1538 + 2820 B, raw 1282 +
+    2308 B). 1doc fwd+bwd is then 5.14e11 FLOP and 4.57 GB."""
+    f = bench.FLOP_PER_TOKEN_HEAD
+    assert f["fwd"] == pytest.approx(141e3, rel=1e-3)
+    assert f["bwd"] == pytest.approx(349e3, rel=1e-3)
+    fwd_mac = 258048 + 266240 + 64 ** 3 / 6 + 3 * 266240 + 2 * 64 * 128 * 128 + 64 * 128 * 128
+    assert fwd_mac == pytest.approx(4.51e6, rel=1e-3)
+    cb = bench.COMPULSORY_BYTES_PER_TOKEN_HEAD
+    assert (cb[False]["fwd"], cb[False]["bwd"]) == (1538, 2820)
+    assert (cb[True]["fwd"], cb[True]["bwd"]) == (1282, 2308)
+    e = bench.end_to_end(1.0, 16384, 64, False)
+    assert e["algorithmic_flop"] == pytest.approx(5.14e11, rel=2e-3)
+    assert e["compulsory_bytes"] == pytest.approx(4.57e9, rel=2e-3)
+    assert e["mfma_frac"] == pytest.approx(e["algorithmic_flop"] / 1e-3 / 2.5e15, rel=1e-3)
+    assert e["hbm_frac"] == pytest.approx(e["compulsory_bytes"] / 1e-3 / 8e12, rel=1e-3)
+    # the per-chunk backward's own I/O: q, k, g, beta, dO in; dq, dk, dbeta, dg out
+    assert bench.BWD_INTRA_COMPULSORY_BYTES_PER_TOKEN_HEAD[False] * 16384 * 64 == \
+        pytest.approx(2.42e9, rel=2e-3)
+
+
 @pytest.mark.parametrize("raw", [False, True])
-def test_every_kernel_is_hbm_bound(raw):
-    # the path's intensity is far below the MI355X ridge (2.5 PFLOP/s / 8 TB/s)
+def test_contraction_kernels_report_against_the_mfma_peak(raw):
     for k in KERNELS:
-        r = bench.kernel_roofline(k, 1.0, CHUNK_HEADS, raw)
-        assert r["bound"] == "hbm", k
-        flop = 2.0 * bench.MAC_PER_CHUNK_HEAD[k]
-        assert flop / bench.algo_bytes_per_chunk_head(k, raw) < 312 / 4
-        assert r["achieved"] == pytest.approx(r["algorithmic_bytes_per_launch"] / 1e-3 / 1e9, rel=1e-3)
-        assert r["frac"] == pytest.approx(r["achieved"] / bench.PEAK_HBM_GBS, abs=1e-4)
+        r = bench.kernel_roofline(k, 2.0, CHUNK_HEADS, raw)
+        assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+        flop = 2.0 * bench.MAC_PER_CHUNK_HEAD[k] * CHUNK_HEADS
+        assert r["achieved"] == pytest.approx(flop / 2e-3 / 1e12, rel=1e-3)
+        assert r["frac"] == pytest.approx(r["achieved"] / 2500.0, abs=1e-4)
+    # the per-chunk backward at 1doc: 1.766e11 FLOP, here timed at 2.2273 ms
+    r = bench.kernel_roofline("bwd_intra", 2.2273, CHUNK_HEADS, raw)
+    assert r["algorithmic_flop_per_launch"] == pytest.approx(1.766e11, rel=1e-3)
+    assert r["frac"] == pytest.approx(0.0317, abs=2e-4)
 
 
 @pytest.mark.parametrize("workload,raw", [("1doc", False), ("4doc", True)])
