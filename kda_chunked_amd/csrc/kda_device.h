@@ -289,11 +289,19 @@ KDA_DEV float row_transpose_sum16(float* x, int j) {
   return x[0];
 }
 
-// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^-|x|), on the hardware
-// base-2 exponential and logarithm.
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|), on the hardware
+// base-2 exponential and logarithm. log1p(y) is taken as log(u) y / (u - 1)
+// with u = 1 + y rounded (y itself when u rounds to 1): the rounding of u
+// cancels between log(u) and u - 1, so small y (x far below zero) keeps its
+// relative accuracy instead of losing it to 1 + y (D. Goldberg, "What every
+// computer scientist should know about floating-point arithmetic", 1991).
 KDA_DEV float softplus(float x) {
   const float y = __builtin_amdgcn_exp2f(-fabsf(x) * LOG2E);
-  return fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + y) * 0.6931471805599453f;
+  const float u = 1.f + y;
+  const float l1p = u == 1.f ? y
+                             : __builtin_amdgcn_logf(u) * 0.6931471805599453f *
+                                   (y * __builtin_amdgcn_rcpf(u - 1.f));
+  return fmaxf(x, 0.f) + l1p;
 }
 KDA_DEV float sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * LOG2E));
