@@ -146,6 +146,24 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
                    void* dg_or_da, float* dA_log, float* ddt_bias, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): kda_fwd
+ * with its workspace taken from a fixed scratch array that the library holds
+ * on each GPU it runs on (KDA_NOALLOC_SCRATCH_BYTES per GPU, from module load
+ * until the process ends) instead of a caller buffer. Inputs, o and the saved
+ * set are the caller's, as for kda_fwd; results are identical to kda_fwd's.
+ * It allocates nothing. A call whose workspace would exceed the scratch
+ * (kda_workspace_bytes(p, 0, saved == NULL) > KDA_NOALLOC_SCRATCH_BYTES: a
+ * forward without a saved set beyond a few hundred chunk-heads) returns
+ * KDA_ERR_WORKSPACE_TOO_SMALL before any launch. Every call on one GPU uses
+ * the same array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must not be issued. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+kda_status kda_fwd_noalloc(const kda_problem* p, const void* q, const void* k, const void* v,
+                           const void* beta, const void* g_or_a, const float* A_log,
+                           const float* dt_bias, const int32_t* cu_seqlens, void* o,
+                           void* saved, void* stream);
+
 /* Instrumentation for callers that time the library's kernels (for example
  * with HIP events): when set, `hook` is called on the host immediately before
  * (end = 0) and after (end = 1) every kernel launch, with the kernel's name

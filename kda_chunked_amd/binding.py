@@ -42,8 +42,9 @@ class kda_problem(ctypes.Structure):
 
 
 _lib = None
-EXPORTS = ("kda_saved_bytes", "kda_workspace_bytes", "kda_fwd", "kda_bwd",
+EXPORTS = ("kda_saved_bytes", "kda_workspace_bytes", "kda_fwd", "kda_bwd", "kda_fwd_noalloc",
            "kda_set_launch_hook", "kda_status_string", "kda_last_error", "kda_abi_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES in kda.h
 LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int,
                                ctypes.c_void_p)
 
@@ -66,6 +67,8 @@ def lib():
         L.kda_fwd.restype = ctypes.c_int
         L.kda_bwd.argtypes = [pp] + [vp] * 18 + [sz, vp]
         L.kda_bwd.restype = ctypes.c_int
+        L.kda_fwd_noalloc.argtypes = [pp] + [vp] * 11
+        L.kda_fwd_noalloc.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -164,6 +167,17 @@ def kda_fwd(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, o, saved, work
                            _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(o), _ptr(saved),
                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                            _stream(dev))
+    _check(rc)
+
+
+def kda_fwd_noalloc(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, o, saved):
+    """kda_fwd without a workspace argument (the library's fixed per-GPU
+    scratch serves instead); enqueued on the current stream of q's device."""
+    dev = _dev(p, (q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, o, saved))
+    with _device_ctx(dev):
+        rc = lib().kda_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                   _ptr(g_or_a), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens),
+                                   _ptr(o), _ptr(saved), _stream(dev))
     _check(rc)
 
 

@@ -11,11 +11,12 @@
 #include "kda_internal.h"
 
 namespace {
-
 // Message of the calling thread's last failed call (plain storage: no
 // dynamic initialisation or destructor in the thread-local block).
 thread_local char g_last_error[512];
+}  // namespace
 
+namespace kda {
 kda_status fail(kda_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -23,6 +24,10 @@ kda_status fail(kda_status s, const char* fmt, ...) {
   va_end(ap);
   return s;
 }
+}  // namespace kda
+
+namespace {
+using kda::fail;
 
 constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

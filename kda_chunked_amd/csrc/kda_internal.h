@@ -5,7 +5,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
+
+// Records a printf-style message as the calling thread's kda_last_error()
+// and returns s.
+__attribute__((visibility("hidden"))) kda_status fail(kda_status s, const char* fmt, ...);
 
 // Device-side chunk table built from cu_seqlens by the chunk-map kernel.
 // Chunks are 64 tokens long and restart at every document start; chunk ids

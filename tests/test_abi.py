@@ -15,7 +15,8 @@ HEADER = os.path.join(ROOT, "include", "kda.h")
 
 
 def header_symbols():
-    text = open(HEADER).read()
+    import glob
+    text = "".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     return sorted(set(re.findall(r"^\S.*?\b(kda_[a-z_]+)\s*\(", text, flags=re.M)))
 
 
@@ -172,3 +173,23 @@ def test_host_tensors_refused_for_a_valid_problem():
     t = torch.zeros(16, dtype=torch.uint8)
     with pytest.raises(ValueError):
         B.kda_fwd(p, t, t, t, t, t, None, None, t, t, None, t)
+
+
+def _noalloc_status(p, saved=None):
+    lib = B.lib()
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    rc = lib.kda_fwd_noalloc(ctypes.byref(p), *([vp(16)] * 8), vp(16), vp(saved), None)
+    return rc, lib.kda_last_error().decode()
+
+
+def test_noalloc_forward_rejects_calls_beyond_its_scratch():
+    """The no-alloc forward checks its fixed scratch size on the host before it
+    looks up the device array or launches anything."""
+    big = _p(T=16384, H=4, num_seqs=3)
+    assert B.workspace_bytes(big, False, True) > B.NOALLOC_SCRATCH_BYTES
+    rc, err = _noalloc_status(big, saved=None)
+    assert rc == 3 and "scratch" in err
+    rc, err = _noalloc_status(_p(H=0))
+    assert rc == 1 and "head" in err
+    # with a saved set the workspace is the chunk table only, far below the scratch
+    assert B.workspace_bytes(big, False, False) < 1 << 20
