@@ -19,9 +19,9 @@ the same workload.
 Besides the timed steps it times, outside the timed region, the units of the
 deterministic package's protocol: fwd alone, bwd alone and the replay pair
 (forward without saving, backward recomputing the forward), each the median
-of 15 samples of 20 back-to-back calls; and the same units for the package's
+of 15 samples of 20 back-to-back calls; the same units for the package's
 other timing rows that this repository reproduces (4doc saved and replay, R2,
-m2), as extra keys.
+m2); and the conv1d + SiLU op that precedes the state passing, as extra keys.
 
 HBM traffic and MFMA utilisation come from rocprofv3 counter runs whose
 summaries sit in profiles/; they are reported only while the kernel sources
@@ -395,6 +395,44 @@ def time_row(w, replay, torch) -> dict:
     return {key: out}
 
 
+def time_conv(torch) -> dict:
+    """The width-4 causal conv1d + SiLU op on the 4doc layout (16384 tokens,
+    the q, k, v channels of 64 heads x 128 = 24576, halo on): fwd and bwd ms
+    with the pages' protocol, against the HBM peak on its compulsory bytes
+    (fwd reads x and writes y; bwd reads x and dy and writes dx; bf16)."""
+    import numpy as np
+    from kda_chunked_amd import inputs as I
+    from kda_chunked_amd.binding import ConvSiLU
+    w = I.CONV_BY_NAME["conv_4doc"]
+    inp = I.make_conv_inputs(w)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    x, dy, halo = bf(inp["x"]), bf(inp["dy"]), bf(inp["halo"])
+    wt = torch.from_numpy(inp["w"]).cuda()
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    op = ConvSiLU(w.T, w.D, len(w.doc_lens), bias=w.bias, halo=w.halo)
+    y = torch.empty_like(x)
+    out = dict(dx=torch.empty_like(x), dw=torch.empty_like(wt), dhalo=torch.empty_like(halo))
+    fwd = lambda: op.forward(x, wt, cu, None, halo, y=y)
+    bwd = lambda: op.backward(x, wt, cu, dy, None, halo, out=out)
+    for _ in range(3):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    f_ms, b_ms = time_unit(torch, fwd), time_unit(torch, bwd)
+    n = float(w.T) * w.D
+    fb, bb = 4.0 * n, 6.0 * n
+    res = {"workload": f"conv_4doc: {w.T} tokens x {w.D} channels, width 4, halo",
+           "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+           "fwd": {"bound": "hbm", "achieved": round(fb / (f_ms * 1e-3) / 1e9, 1),
+                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(fb / (f_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+           "bwd": {"bound": "hbm", "achieved": round(bb / (b_ms * 1e-3) / 1e9, 1),
+                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(bb / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    print(f"[bench] conv: {res}", file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -513,11 +551,13 @@ def main():
             fig["mfma_flop"] / sec / 1e12, 2) if "mfma_flop" in fig else None
 
     rows = {}
+    conv = None
     if not args.no_rows:
         for name, replay in SECONDARY_ROWS:
             if name == w.name:
                 continue
             rows.update(time_row(I.BY_NAME[name], replay, torch))
+        conv = time_conv(torch)
 
     line = {
         "metric": METRIC,
@@ -550,6 +590,8 @@ def main():
     line.update(units)
     if rows:
         line["rows"] = rows
+    if conv:
+        line["conv1d_silu"] = conv
     if not args.no_cpu:
         from oracle import kda_oracle as ko
         line["cpu_baseline"] = cpu_baseline(w, inp, ko.default_threads())

@@ -41,9 +41,21 @@ class kda_problem(ctypes.Structure):
     ]
 
 
+class kda_conv_problem(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("D", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("width", ctypes.c_int32),
+        ("has_bias", ctypes.c_int32),
+        ("has_halo", ctypes.c_int32),
+    ]
+
+
 _lib = None
 EXPORTS = ("kda_saved_bytes", "kda_workspace_bytes", "kda_fwd", "kda_bwd", "kda_fwd_noalloc",
-           "kda_set_launch_hook", "kda_status_string", "kda_last_error", "kda_abi_version")
+           "kda_set_launch_hook", "kda_status_string", "kda_last_error", "kda_abi_version",
+           "kda_conv_workspace_bytes", "kda_conv_silu_fwd", "kda_conv_silu_bwd")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES in kda.h
 LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int,
                                ctypes.c_void_p)
@@ -69,6 +81,13 @@ def lib():
         L.kda_bwd.restype = ctypes.c_int
         L.kda_fwd_noalloc.argtypes = [pp] + [vp] * 11
         L.kda_fwd_noalloc.restype = ctypes.c_int
+        cp = ctypes.POINTER(kda_conv_problem)
+        L.kda_conv_workspace_bytes.argtypes = [cp, ctypes.c_int]
+        L.kda_conv_workspace_bytes.restype = sz
+        L.kda_conv_silu_fwd.argtypes = [cp] + [vp] * 7 + [sz, vp]
+        L.kda_conv_silu_fwd.restype = ctypes.c_int
+        L.kda_conv_silu_bwd.argtypes = [cp] + [vp] * 11 + [sz, vp]
+        L.kda_conv_silu_bwd.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -232,4 +251,76 @@ class KDA:
         kda_bwd(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, dO,
                 None if replay else self.saved, out["dq"], out["dk"], out["dv"], out["dbeta"],
                 out["dgate"], out.get("dA_log"), out.get("ddt_bias"), self.workspace)
+        return out
+
+
+# ---------------------------------------------------------------- conv1d + SiLU
+
+def conv_problem(T, D, num_seqs, bias=False, halo=False, width=4):
+    return kda_conv_problem(int(T), int(D), int(num_seqs), int(width), int(bool(bias)),
+                            int(bool(halo)))
+
+
+def conv_workspace_bytes(p: kda_conv_problem, backward: bool) -> int:
+    return int(lib().kda_conv_workspace_bytes(ctypes.byref(p), int(bool(backward))))
+
+
+def conv_silu_fwd(p, x, w, b, halo, cu_seqlens, y, workspace=None):
+    """Enqueue the conv1d + SiLU forward on the current stream of x's device."""
+    dev = _dev_conv(p, (x, w, b, halo, cu_seqlens, y, workspace))
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with _device_ctx(dev):
+        rc = lib().kda_conv_silu_fwd(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(b), _ptr(halo),
+                                     _ptr(cu_seqlens), _ptr(y), _ptr(workspace), nbytes,
+                                     _stream(dev))
+    _check(rc)
+
+
+def conv_silu_bwd(p, x, w, b, halo, cu_seqlens, dy, dx, dw, db, dhalo, workspace):
+    """Enqueue the conv1d + SiLU backward on the current stream of x's device."""
+    dev = _dev_conv(p, (x, w, b, halo, cu_seqlens, dy, dx, dw, db, dhalo, workspace))
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with _device_ctx(dev):
+        rc = lib().kda_conv_silu_bwd(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(b), _ptr(halo),
+                                     _ptr(cu_seqlens), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
+                                     _ptr(dhalo), _ptr(workspace), nbytes, _stream(dev))
+    _check(rc)
+
+
+def _dev_conv(p, tensors):
+    ts = [t for t in tensors if t is not None]
+    if ts and all(t.is_cuda for t in ts):
+        return ts[0].device
+    if lib().kda_conv_workspace_bytes(ctypes.byref(p), 0) != 0 or \
+            lib().kda_conv_workspace_bytes(ctypes.byref(p), 1) != 0:
+        raise ValueError("every tensor passed to the conv op must be on the GPU")
+    return None
+
+
+class ConvSiLU:
+    """Width-4 causal conv1d + SiLU over packed documents (optionally after a
+    halo of the 3 tokens preceding x[0] in document 0). x, dy [T, D] bf16;
+    w [D, 4] fp32; b [D] fp32; halo [3, D] bf16; cu_seqlens [N+1] int32."""
+
+    def __init__(self, T, D, num_seqs, bias=False, halo=False, device="cuda"):
+        self.p = conv_problem(T, D, num_seqs, bias, halo)
+        self.device = torch.device(device)
+        n = max(conv_workspace_bytes(self.p, True), 16)
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def forward(self, x, w, cu_seqlens, b=None, halo=None, y=None):
+        if y is None:
+            y = torch.empty_like(x)
+        conv_silu_fwd(self.p, x, w, b, halo, cu_seqlens, y)
+        return y
+
+    def backward(self, x, w, cu_seqlens, dy, b=None, halo=None, out=None):
+        if out is None:
+            out = dict(dx=torch.empty_like(x), dw=torch.empty_like(w))
+            if self.p.has_bias:
+                out["db"] = torch.empty_like(b)
+            if self.p.has_halo:
+                out["dhalo"] = torch.empty_like(halo)
+        conv_silu_bwd(self.p, x, w, b, halo, cu_seqlens, dy, out["dx"], out["dw"], out.get("db"),
+                      out.get("dhalo"), self.workspace)
         return out

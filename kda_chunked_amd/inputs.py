@@ -151,3 +151,59 @@ def as_f64(inp: dict) -> dict:
             out[key] = inp[key].astype(np.float64)
     out["cu_seqlens"] = inp["cu_seqlens"].astype(np.int64)
     return out
+
+
+# ---------------------------------------------------------------- conv1d + SiLU
+#
+# The width-4 causal conv1d + SiLU that precedes the state passing in the KDA
+# module forward (flashinfer PR #7176, description): x is the packed [T, D]
+# projection input (D = q, k and v channels of every head), with the recipe
+# x, dy ~ N(0, 1) rounded to bf16; taps w ~ U(-1/2, 1/2) and bias
+# b ~ U(-1/2, 1/2) in float32 (the uniform bound 1/sqrt(fan_in) of a width-4
+# depthwise conv); halo ~ N(0, 1) bf16, the 3 tokens before x[0] of a
+# fragment that continues a document. Draw order: x, dy, w, b, halo.
+
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    doc_lens: tuple
+    D: int
+    bias: bool
+    halo: bool
+    seed: int = 0
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.doc_lens))
+
+    @property
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.doc_lens)]).astype(np.int32)
+
+
+CONV_WORKLOADS = [
+    ConvWorkload("conv_tiny", (200, 56), 256, True, True, seed=10),
+    ConvWorkload("conv_ragged", (2, 0, 1, 70, 3, 0, 64, 130), 512, True, True, seed=11),
+    # the 4doc layout with the q, k, v channels of 64 heads x 128, as a context
+    # fragment that continues its first document (halo on), no bias
+    ConvWorkload("conv_4doc", (8192, 4096, 3072, 1024), 3 * 64 * 128, False, True, seed=12),
+]
+CONV_BY_NAME = {w.name: w for w in CONV_WORKLOADS}
+
+
+def make_conv_inputs(w: ConvWorkload, seed: int | None = None) -> dict:
+    """x, dy, halo (uint16 bf16 bits), w, b (float32), cu_seqlens (int32)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    T, D = w.T, w.D
+    out = {"cu_seqlens": w.cu_seqlens,
+           "x": f32_to_bf16(rng.standard_normal((T, D), dtype=np.float32)),
+           "dy": f32_to_bf16(rng.standard_normal((T, D), dtype=np.float32)),
+           "w": rng.uniform(-0.5, 0.5, (D, 4)).astype(np.float32)}
+    b = rng.uniform(-0.5, 0.5, D).astype(np.float32)
+    halo = f32_to_bf16(rng.standard_normal((3, D), dtype=np.float32))
+    if w.bias:
+        out["b"] = b
+    if w.halo:
+        out["halo"] = halo
+    return out
