@@ -20,6 +20,12 @@
 // decays e^(g_r), r = i+1 .. 15, which never exceeds 1 and underflows
 // gracefully.
 //
+// A calm chunk (span at most SPAN_MAX in every channel) uses one reference
+// for all of its tiles, rho = G_last / 2, so both factors lie within
+// e^(+-SPAN_MAX/2): the k operand k^ e^(rho - G) is built once per row into an
+// LDS panel and each wave builds its rows' x operands for half of the channels
+// once, then runs every tile of its row block.
+//
 // Besides the saved fp32 matrices, the kernel writes the operand panels (-Kd,
 // scale Qd, Ke^T, Tb, scale A_qk as bf16 hi/lo planes and e^(G_last)) that the
 // two state scans and the output kernel stream; the lo planes of -Kd and Tb
@@ -117,10 +123,17 @@ struct PrepSmem {
       float nrm[2][8][CL]; // L2 partial sums
     } s;
     float E[CL][HD];       // e^(g) per row and channel, once the above are dead
+    bf16 Y[2][CL * HD];    // calm chunk: k^ e^(rho - G), hi and lo, rows of 16-byte
+                           // chunks XOR-swizzled by row
   } u;
   float rq[CL], rk[CL], beta[CL];
   int wide[4];             // diagonal block I has a span > SPAN_MAX
+  int notcalm;             // some channel's chunk span exceeds SPAN_MAX
 };
+
+// Element offset of (row, channel c) in a swizzled 64 x 128 bf16 plane: 16-byte
+// chunk c / 8 of the row sits at position (c / 8) ^ (row & 15).
+KDA_DEV int yswz(int row, int c) { return row * HD + ((((c >> 3) ^ (row & 15))) << 3) + (c & 7); }
 
 // Off-diagonal tile (I, J), J < I, of the lower triangle of 16 x 16 blocks.
 KDA_DEV void offdiag_tile(int item, int& I, int& J) {
@@ -290,6 +303,7 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     sm.u.s.qtot[qG][cG] = run;
   }
   if (t < 4) sm.wide[t] = 0;
+  if (t == 4) sm.notcalm = 0;
   __syncthreads();
   {
     float carry = 0.f;
@@ -300,6 +314,8 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       const float Gx = g[j] + carry;
       sm.G[r][cG] = Gx;               // rows >= n hold G[n-1] (their g is 0)
     }
+    // the chunk's span in this channel: 0 (before the first row) minus G_last
+    if (qG == 3 && -(g[15] + carry) > SPAN_MAX) sm.notcalm = 1;
     if (t < CL) {
       float a = 0.f, b = 0.f;
 #pragma unroll
@@ -328,8 +344,28 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
     for (int I = 0; I < 4; ++I)
       if ((I == 0 ? 0.f : sm.G[16 * I - 1][t]) - sm.G[16 * I + 15][t] > SPAN_MAX) sm.wide[I] = 1;
   }
+  const bool calm = !sm.notcalm;
+  if (!calm) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) sm.u.E[16 * qG + j][cG] = eg[j];
+    for (int j = 0; j < 16; ++j) sm.u.E[16 * qG + j][cG] = eg[j];
+  } else {
+    // Y = k^ e^(rho - G), rho = G_last / 2: thread t, row rA, channels cA .. cA + 15
+    const float rkA = sm.rk[rA];
+#pragma unroll
+    for (int u2 = 0; u2 < 2; ++u2) {
+      const int c = cA + 8 * u2;
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&sm.ks[rA][c]);
+      bf16x8 yh, yl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float y = bf2f(kv[j]) * rkA * fexp(0.5f * sm.G[CL - 1][c + j] - sm.G[rA][c + j]);
+        yh[j] = f2bf(y);
+        yl[j] = f2bf(y - bf2f(yh[j]));
+      }
+      *reinterpret_cast<bf16x8*>(&sm.u.Y[0][yswz(rA, c)]) = yh;
+      *reinterpret_cast<bf16x8*>(&sm.u.Y[1][yswz(rA, c)]) = yl;
+    }
+  }
   // zero the strictly-upper 16 x 16 tiles of A_kk and A_qk
   for (int e = t; e < 6 * 256; e += NT_PREP) {
     const int tile = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
@@ -344,142 +380,223 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   // 8 waves: each off-diagonal tile and each calm diagonal tile is one MFMA
   // product of bf16 hi/lo operands; each wide diagonal tile is two
   // running-product units (unit u: columns p and 15 - p, p = 4u .. 4u + 3).
-  int wide[4], n_wide = 0;
+  if (calm) {
+    // One reference for the whole chunk: wave w takes row block I = w & 3 and
+    // channels 64 kh .. 64 kh + 63 (kh = w >> 2) of every tile (I, J <= I);
+    // its x operands x^ e^(G - rho) are built once, the k operands come from
+    // the Y panel. The two channel halves meet in LDS in a fixed order.
+    const int I = w & 3, kh = w >> 2, ra = 16 * I + (l & 15);
+    const float rqa = sm.rq[ra], rka = sm.rk[ra];
+    f32x4 akk[4], aqk[4];
 #pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    wide[I] = __builtin_amdgcn_readfirstlane(sm.wide[I]);
-    n_wide += wide[I];
-  }
-  for (int item = w; item < 10 + n_wide; item += 8) {
-    int I = 3, J, unit = -1;
-    if (item < 6) {
-      offdiag_tile(item, I, J);
-    } else {
-      int rem = item - 6;
-      bool found = false;
+    for (int J = 0; J < 4; ++J) akk[J] = aqk[J] = zero4();
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int cnt = 1 + wide[b];
-        if (!found && rem < cnt) {
-          I = b;
-          unit = wide[b] ? rem : -1;
-          found = true;
-        } else if (!found) {
-          rem -= cnt;
-        }
-      }
-      J = I;
-    }
-    if (unit < 0) {
-      // rho: G at the end of block J (off-diagonal), else the midpoint of G
-      // before block I and G at its last row
-      const bool diag = I == J;
-      const float* refa = diag ? sm.Gref[I] : sm.Gref[J + 1];
-      const float* refb = sm.Gref[J + 1];
-      const int ra = 16 * I + (l & 15), rbw = 16 * J + (l & 15);
-      const float rqa = sm.rq[ra], rka = sm.rk[ra], rkb = sm.rk[rbw];
-      f32x4 akk = zero4(), aqk = zero4();
-#pragma unroll
-      for (int ks = 0; ks < HD / 32; ++ks) {
-        const int c = 32 * ks + 8 * (l >> 4);
-        bf16x8 xk_h, xk_l, xq_h, xq_l, y_h, y_l;
-        decayed_frag2(sm, rka, rqa, ra, c, refa, refb, xk_h, xk_l, xq_h, xq_l);
-        decayed_frag(sm, sm.ks, rkb, rbw, c, refa, refb, -1.f, y_h, y_l);
-        if (KDA_SPLIT_P1 & SPLIT_A) {
-          akk = mfma16(xk_l, y_h, akk);
-          aqk = mfma16(xq_l, y_h, aqk);
-        }
-        if (KDA_SPLIT_P1 & SPLIT_B) {
-          akk = mfma16(xk_h, y_l, akk);
-          aqk = mfma16(xq_h, y_l, aqk);
-        }
-        akk = mfma16(xk_h, y_h, akk);
-        aqk = mfma16(xq_h, y_h, aqk);
-      }
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r = 16 * I + drow(i4), i = 16 * J + dcol();
-        sm.Akk[r][i] = (i < r) ? akk[i4] : 0.f;
-        sm.Aqk[r][i] = (i <= r) ? aqk[i4] : 0.f;
-      }
-    } else {
-      // Lane (lg, cg): column pair p = 4 unit + lg, channels 8 cg .. + 7.
-      // Step st walks column p for rows p .. 15 (st = 0 .. 15 - p), then
-      // column 15 - p for rows 15 - p .. 15: 17 (r, i) pairs per lane group.
-      const int lg = l >> 4, cg = l & 15, c = 8 * cg, b0 = 16 * I;
-      const int p = 4 * unit + lg;
-      auto pair_of = [&](int st, int& r, int& i) {
-        const bool second = st > 15 - p;
-        i = second ? 15 - p : p;
-        r = second ? st - 1 : p + st;
-      };
-      float f[8] = {};    // k_i rk_i e^(G_r - G_i), channels c .. c+7
-      // the starting values k_i rk_i of both columns, so that a step is
-      // branch-free and the loads of later steps can be issued early
-      float kpf[8], kzf[8];
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 64 * kh + 32 * ks + 8 * (l >> 4);
+      bf16x8 xk_h, xk_l, xq_h, xq_l;
       {
-        const bf16x8 kp = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + p][c]);
-        const bf16x8 kz = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + 15 - p][c]);
-        const float rkp = sm.rk[b0 + p], rkz = sm.rk[b0 + 15 - p];
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.G[ra][c]);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.G[ra][c + 4]);
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sm.G[CL - 1][c]);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sm.G[CL - 1][c + 4]);
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&sm.ks[ra][c]);
+        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&sm.qs[ra][c]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          kpf[j] = bf2f(kp[j]) * rkp;
-          kzf[j] = bf2f(kz[j]) * rkz;
+          const float gj = j < 4 ? g0[j] : g1[j - 4];
+          const float rj = 0.5f * (j < 4 ? e0[j] : e1[j - 4]);
+          const float e = fexp(gj - rj);
+          const float vk = bf2f(kv[j]) * rka * e, vq = bf2f(qv[j]) * rqa * e;
+          xk_h[j] = f2bf(vk);
+          xk_l[j] = f2bf(vk - bf2f(xk_h[j]));
+          xq_h[j] = f2bf(vq);
+          xq_l[j] = f2bf(vq - bf2f(xq_h[j]));
         }
       }
-      auto step = [&](int st, float& skk, float& sqk) {
-        int r, i;
-        pair_of(st, r, i);
-        const bool restart = st == 16 - p;       // first row of column 15 - p
-        // lanes cg >= 8 read their two halves in the other order, so that
-        // each 16-byte read of the 16 lanes touches every bank once
-        const int sw = (cg & 8) >> 1;
-        const f32x4 ea = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + sw]);
-        const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + 4 - sw]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float ej = sw ? (j < 4 ? eb[j] : ea[j - 4]) : (j < 4 ? ea[j] : eb[j - 4]);
-          const float fm = f[j] * ej;
-          f[j] = st == 0 ? kpf[j] : restart ? kzf[j] : fm;
+      for (int J = 0; J < 4; ++J) {
+        if (J <= I) {
+          const int yo = yswz(16 * J + (l & 15), c);
+          const bf16x8 y_h = *reinterpret_cast<const bf16x8*>(&sm.u.Y[0][yo]);
+          const bf16x8 y_l = *reinterpret_cast<const bf16x8*>(&sm.u.Y[1][yo]);
+          if (KDA_SPLIT_P1 & SPLIT_A) {
+            akk[J] = mfma16(xk_l, y_h, akk[J]);
+            aqk[J] = mfma16(xq_l, y_h, aqk[J]);
+          }
+          if (KDA_SPLIT_P1 & SPLIT_B) {
+            akk[J] = mfma16(xk_h, y_l, akk[J]);
+            aqk[J] = mfma16(xq_h, y_l, aqk[J]);
+          }
+          akk[J] = mfma16(xk_h, y_h, akk[J]);
+          aqk[J] = mfma16(xq_h, y_h, aqk[J]);
         }
-        const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + r][c]);
-        const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&sm.qs[b0 + r][c]);
-        skk = sqk = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          skk += bf2f(kr[j]) * f[j];
-          sqk += bf2f(qr[j]) * f[j];
-        }
-      };
-      // the sums of step st (kind 0: A_kk, 1: A_qk), mirrored zero above the diagonal
-      auto store = [&](int st, int kind, float v) {
-        int r, i;
-        pair_of(st, r, i);
-        if (kind == 0) {
-          sm.Akk[b0 + r][b0 + i] = r > i ? v * sm.rk[b0 + r] : 0.f;
-          if (r > i) sm.Akk[b0 + i][b0 + r] = 0.f;
-        } else {
-          sm.Aqk[b0 + r][b0 + i] = v * sm.rq[b0 + r];
-          if (r > i) sm.Aqk[b0 + i][b0 + r] = 0.f;
-        }
-      };
-      // steps 0..15 in two groups of 8: the 16 sums of a group are reduced
-      // over the 16 channel-group lanes (one DPP row), after which lane cg
-      // holds the total of value cg (step cg / 2, kind cg % 2)
-#pragma unroll
-      for (int gq = 0; gq < 2; ++gq) {
-        float x[16];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) step(8 * gq + e, x[2 * e], x[2 * e + 1]);
-        store(8 * gq + (cg >> 1), cg & 1, row_transpose_sum16(x, cg));
       }
-      float skk, sqk;
-      step(16, skk, sqk);
-      skk = row_sum16(skk);
-      sqk = row_sum16(sqk);
-      if (cg == 0) {
-        store(16, 0, skk);
-        store(16, 1, sqk);
+    }
+    // channels 0..63 (kh = 0) first, then kh = 1 adds channels 64..127 and masks
+    if (kh == 0) {
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J <= I) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int r = 16 * I + drow(i4), i = 16 * J + dcol();
+            sm.Akk[r][i] = akk[J][i4];
+            sm.Aqk[r][i] = aqk[J][i4];
+          }
+        }
+    }
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J <= I) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int r = 16 * I + drow(i4), i = 16 * J + dcol();
+            const float vk = sm.Akk[r][i] + akk[J][i4], vq = sm.Aqk[r][i] + aqk[J][i4];
+            sm.Akk[r][i] = (i < r) ? vk : 0.f;
+            sm.Aqk[r][i] = (i <= r) ? vq : 0.f;
+          }
+        }
+    }
+  } else {
+    int wide[4], n_wide = 0;
+  #pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      wide[I] = __builtin_amdgcn_readfirstlane(sm.wide[I]);
+      n_wide += wide[I];
+    }
+    for (int item = w; item < 10 + n_wide; item += 8) {
+      int I = 3, J, unit = -1;
+      if (item < 6) {
+        offdiag_tile(item, I, J);
+      } else {
+        int rem = item - 6;
+        bool found = false;
+  #pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int cnt = 1 + wide[b];
+          if (!found && rem < cnt) {
+            I = b;
+            unit = wide[b] ? rem : -1;
+            found = true;
+          } else if (!found) {
+            rem -= cnt;
+          }
+        }
+        J = I;
+      }
+      if (unit < 0) {
+        // rho: G at the end of block J (off-diagonal), else the midpoint of G
+        // before block I and G at its last row
+        const bool diag = I == J;
+        const float* refa = diag ? sm.Gref[I] : sm.Gref[J + 1];
+        const float* refb = sm.Gref[J + 1];
+        const int ra = 16 * I + (l & 15), rbw = 16 * J + (l & 15);
+        const float rqa = sm.rq[ra], rka = sm.rk[ra], rkb = sm.rk[rbw];
+        f32x4 akk = zero4(), aqk = zero4();
+  #pragma unroll
+        for (int ks = 0; ks < HD / 32; ++ks) {
+          const int c = 32 * ks + 8 * (l >> 4);
+          bf16x8 xk_h, xk_l, xq_h, xq_l, y_h, y_l;
+          decayed_frag2(sm, rka, rqa, ra, c, refa, refb, xk_h, xk_l, xq_h, xq_l);
+          decayed_frag(sm, sm.ks, rkb, rbw, c, refa, refb, -1.f, y_h, y_l);
+          if (KDA_SPLIT_P1 & SPLIT_A) {
+            akk = mfma16(xk_l, y_h, akk);
+            aqk = mfma16(xq_l, y_h, aqk);
+          }
+          if (KDA_SPLIT_P1 & SPLIT_B) {
+            akk = mfma16(xk_h, y_l, akk);
+            aqk = mfma16(xq_h, y_l, aqk);
+          }
+          akk = mfma16(xk_h, y_h, akk);
+          aqk = mfma16(xq_h, y_h, aqk);
+        }
+  #pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r = 16 * I + drow(i4), i = 16 * J + dcol();
+          sm.Akk[r][i] = (i < r) ? akk[i4] : 0.f;
+          sm.Aqk[r][i] = (i <= r) ? aqk[i4] : 0.f;
+        }
+      } else {
+        // Lane (lg, cg): column pair p = 4 unit + lg, channels 8 cg .. + 7.
+        // Step st walks column p for rows p .. 15 (st = 0 .. 15 - p), then
+        // column 15 - p for rows 15 - p .. 15: 17 (r, i) pairs per lane group.
+        const int lg = l >> 4, cg = l & 15, c = 8 * cg, b0 = 16 * I;
+        const int p = 4 * unit + lg;
+        auto pair_of = [&](int st, int& r, int& i) {
+          const bool second = st > 15 - p;
+          i = second ? 15 - p : p;
+          r = second ? st - 1 : p + st;
+        };
+        float f[8] = {};    // k_i rk_i e^(G_r - G_i), channels c .. c+7
+        // the starting values k_i rk_i of both columns, so that a step is
+        // branch-free and the loads of later steps can be issued early
+        float kpf[8], kzf[8];
+        {
+          const bf16x8 kp = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + p][c]);
+          const bf16x8 kz = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + 15 - p][c]);
+          const float rkp = sm.rk[b0 + p], rkz = sm.rk[b0 + 15 - p];
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            kpf[j] = bf2f(kp[j]) * rkp;
+            kzf[j] = bf2f(kz[j]) * rkz;
+          }
+        }
+        auto step = [&](int st, float& skk, float& sqk) {
+          int r, i;
+          pair_of(st, r, i);
+          const bool restart = st == 16 - p;       // first row of column 15 - p
+          // lanes cg >= 8 read their two halves in the other order, so that
+          // each 16-byte read of the 16 lanes touches every bank once
+          const int sw = (cg & 8) >> 1;
+          const f32x4 ea = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + sw]);
+          const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.u.E[b0 + r][c + 4 - sw]);
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float ej = sw ? (j < 4 ? eb[j] : ea[j - 4]) : (j < 4 ? ea[j] : eb[j - 4]);
+            const float fm = f[j] * ej;
+            f[j] = st == 0 ? kpf[j] : restart ? kzf[j] : fm;
+          }
+          const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&sm.ks[b0 + r][c]);
+          const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&sm.qs[b0 + r][c]);
+          skk = sqk = 0.f;
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            skk += bf2f(kr[j]) * f[j];
+            sqk += bf2f(qr[j]) * f[j];
+          }
+        };
+        // the sums of step st (kind 0: A_kk, 1: A_qk), mirrored zero above the diagonal
+        auto store = [&](int st, int kind, float v) {
+          int r, i;
+          pair_of(st, r, i);
+          if (kind == 0) {
+            sm.Akk[b0 + r][b0 + i] = r > i ? v * sm.rk[b0 + r] : 0.f;
+            if (r > i) sm.Akk[b0 + i][b0 + r] = 0.f;
+          } else {
+            sm.Aqk[b0 + r][b0 + i] = v * sm.rq[b0 + r];
+            if (r > i) sm.Aqk[b0 + i][b0 + r] = 0.f;
+          }
+        };
+        // steps 0..15 in two groups of 8: the 16 sums of a group are reduced
+        // over the 16 channel-group lanes (one DPP row), after which lane cg
+        // holds the total of value cg (step cg / 2, kind cg % 2)
+  #pragma unroll
+        for (int gq = 0; gq < 2; ++gq) {
+          float x[16];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) step(8 * gq + e, x[2 * e], x[2 * e + 1]);
+          store(8 * gq + (cg >> 1), cg & 1, row_transpose_sum16(x, cg));
+        }
+        float skk, sqk;
+        step(16, skk, sqk);
+        skk = row_sum16(skk);
+        sqk = row_sum16(sqk);
+        if (cg == 0) {
+          store(16, 0, skk);
+          store(16, 1, sqk);
+        }
       }
     }
   }
