@@ -47,7 +47,22 @@ struct Carver {
 
 struct Sizes {
   int64_t T, H, N, NC;
+  int64_t L, NS;    // segment length (chunks; 0: whole documents), segment upper bound
 };
+
+// Segment length of the segment-parallel scans, from sizes the host knows
+// (document lengths stay on the device). With few chains (documents x heads x
+// 4 column tiles well below the 256 compute units) and documents that average
+// at least two segments, each document is cut into segments of L chunks,
+// about 64 chains over the heads, at least 16 chunks long; otherwise 0 (one
+// chain per document: the summaries and walks would cost more than they save).
+int64_t seg_len(int64_t T, int64_t H, int64_t N) {
+  const int64_t NC = T / 64 + N;
+  if (N * H * 4 >= 192) return 0;
+  int64_t L = (NC * H + 63) / 64;
+  if (L < 16) L = 16;
+  return 2 * L * N > NC ? 0 : L;
+}
 
 Sizes sizes_of(const kda_problem* p) {
   Sizes s;
@@ -55,6 +70,9 @@ Sizes sizes_of(const kda_problem* p) {
   s.H = p->H;
   s.N = p->num_seqs;
   s.NC = p->T / 64 + p->num_seqs;
+  s.L = seg_len(s.T, s.H, s.N);
+  // document d has ceil(n_d / L) <= n_d / L + 1 segments
+  s.NS = s.L > 0 ? s.NC / s.L + s.N : s.N;
   return s;
 }
 
@@ -63,8 +81,13 @@ kda::ChunkTable carve_table(Carver& c, const Sizes& s) {
   ct.doc_c0 = c.take<int32_t>(s.N + 1);
   ct.tok = c.take<int32_t>(s.NC);
   ct.len = c.take<int32_t>(s.NC);
+  ct.seg_doc0 = c.take<int32_t>(s.N + 1);
+  ct.seg_doc = c.take<int32_t>(s.NS);
   return ct;
 }
+
+// One fp32 128 x 128 matrix per (segment, head).
+float* take_seg(Carver& c, const Sizes& s) { return c.take<float>((size_t)s.NS * s.H * 128 * 128); }
 
 // The saved forward set: per-chunk matrices, L2 scalars, states and panels.
 kda::SavedSet carve_saved(Carver& c, const Sizes& s) {
@@ -78,6 +101,7 @@ kda::SavedSet carve_saved(Carver& c, const Sizes& s) {
   sv.R = c.take<float>((size_t)s.NC * s.H * 64 * 128);
   sv.U = c.take<float>((size_t)s.NC * s.H * 64 * 128);
   sv.panels = c.take<uint16_t>((size_t)s.NC * s.H * kda::fwd_panel::ELEMS);
+  sv.Mseg = s.L > 0 ? take_seg(c, s) : nullptr;
   return sv;
 }
 
@@ -139,6 +163,9 @@ kda::Dims dims_of(const kda_problem* p) {
   d.H = p->H;
   d.N = p->num_seqs;
   d.NC = (int)(p->T / 64 + p->num_seqs);
+  const Sizes s = sizes_of(p);
+  d.L = (int)s.L;
+  d.NS = (int)s.NS;
   d.raw = p->gate == KDA_GATE_RAW;
   d.l2norm = p->l2norm;
   d.scale = p->scale;
@@ -146,11 +173,38 @@ kda::Dims dims_of(const kda_problem* p) {
   return d;
 }
 
+// Segment summaries and walk results. The forward takes B and S0 (M lives in
+// the saved set); the backward B' and D0, which a replay also lends to its
+// forward as B and S0 (the forward is done with them before the backward's
+// summary pass writes B').
+kda::SegWork carve_seg_fwd(Carver& c, const Sizes& s, const kda::SavedSet& sv) {
+  kda::SegWork sg{};
+  if (s.L > 0) {
+    sg.M = sv.Mseg;
+    sg.B = take_seg(c, s);
+    sg.S0 = take_seg(c, s);
+  }
+  return sg;
+}
+kda::SegWork carve_seg_bwd(Carver& c, const Sizes& s, const kda::SavedSet& sv) {
+  kda::SegWork sg{};
+  if (s.L > 0) {
+    sg.M = sv.Mseg;
+    sg.Brev = take_seg(c, s);
+    sg.D0 = take_seg(c, s);
+    sg.B = sg.Brev;
+    sg.S0 = sg.D0;
+  }
+  return sg;
+}
+
 // A forward that saves nothing keeps its per-chunk set in the workspace.
 size_t fwd_ws_bytes(const Sizes& s, int nosave) {
   Carver c(nullptr);
   carve_table(c, s);
-  if (nosave) carve_saved(c, s);
+  kda::SavedSet sv{};
+  if (nosave) sv = carve_saved(c, s);
+  carve_seg_fwd(c, s, sv);
   return c.off;
 }
 
@@ -158,7 +212,9 @@ size_t bwd_ws_bytes(const Sizes& s, int replay) {
   Carver c(nullptr);
   carve_table(c, s);
   carve_bwd(c, s);
-  if (replay) carve_saved(c, s);
+  kda::SavedSet sv{};
+  if (replay) sv = carve_saved(c, s);
+  carve_seg_bwd(c, s, sv);
   return c.off;
 }
 
@@ -230,9 +286,17 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   } else {
     sv = carve_saved(wc, s);   // private per-chunk set in the workspace
   }
+  const kda::SegWork sg = carve_seg_fwd(wc, s, sv);
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
+  LAUNCH("seg_map", kda::launch_seg_map(d, ct, hs));
   LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, saved != nullptr, hs));
-  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, saved != nullptr, hs));
+  if (d.L > 0) {
+    LAUNCH("fwd_scan_summary", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, 0, sg,
+                                                    kda::SCAN_SUMMARY, hs));
+    LAUNCH("walk", kda::launch_walk(d, ct, sg, 0, hs));
+  }
+  LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, saved != nullptr, sg,
+                                          kda::SCAN_FINISH, hs));
   LAUNCH("fwd_out", kda::launch_fwd_out(d, ct, sv, sv.panels, o, hs));
   return KDA_OK;
 }
@@ -298,12 +362,25 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
     sv = carve_saved(sc, s);
   }
   const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
+  const kda::SegWork sg = carve_seg_bwd(wc, s, sv);
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
+  LAUNCH("seg_map", kda::launch_seg_map(d, ct, hs));
   if (replay) {
     LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, 1, hs));
-    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, 1, hs));
+    if (d.L > 0) {
+      LAUNCH("fwd_scan_summary", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, 0, sg,
+                                                      kda::SCAN_SUMMARY, hs));
+      LAUNCH("walk", kda::launch_walk(d, ct, sg, 0, hs));
+    }
+    LAUNCH("fwd_scan", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, 1, sg, kda::SCAN_FINISH,
+                                            hs));
   }
-  LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, sv, dO, dv, bw, hs));
+  if (d.L > 0) {
+    LAUNCH("bwd_scan_summary", kda::launch_bwd_scan(d, in, ct, sv, dO, dv, bw, sg,
+                                                    kda::SCAN_SUMMARY, hs));
+    LAUNCH("walk_rev", kda::launch_walk(d, ct, sg, 1, hs));
+  }
+  LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, sv, dO, dv, bw, sg, kda::SCAN_FINISH, hs));
   LAUNCH("bwd_intra", kda::launch_bwd_intra(d, in, ct, sv, dO, out, bw, hs));
   if (p->gate == KDA_GATE_RAW) LAUNCH("finalize", kda::launch_finalize(d, ct, out, bw, hs));
   return KDA_OK;

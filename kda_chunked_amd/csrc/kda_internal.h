@@ -22,6 +22,11 @@ struct ChunkTable {
   int32_t* doc_c0;   // [N+1]: chunks of document d are [doc_c0[d], doc_c0[d+1])
   int32_t* tok;      // [n_chunks_max]: first token of the chunk
   int32_t* len;      // [n_chunks_max]: tokens in the chunk (1..64)
+  // Segments: each document's chunks cut into runs of Dims::L chunks (one
+  // segment per document when L = 0), numbered in document order. Segment s
+  // of document d is its k-th, k = s - seg_doc0[d].
+  int32_t* seg_doc0; // [N+1]: segments of document d are [seg_doc0[d], seg_doc0[d+1])
+  int32_t* seg_doc;  // [n_segments_max]: document of segment s
 };
 
 // Per-chunk matrices and states (the saved forward set), all fp32. The gate
@@ -42,13 +47,30 @@ struct SavedSet {
   float* rq;     // [T, H]           L2 scalars (1 without the fused norm)
   float* rk;     // [T, H]
   void* panels;  // [NC, H, fwd_panel::ELEMS] bf16 operand panels (also the reverse scan's)
+  float* Mseg;   // [NS, H, 128 x 128] homogeneous part of each segment's state map (L > 0)
 };
+
+// Segment-parallel scans (L > 0): the state map of a segment of chunks is
+// affine, S_out = M S_in + B, and its reverse is dS_in = M^T dS_out + B'.
+// fp32, tile order as SavedSet::S_in.
+struct SegWork {
+  float* M;      // [NS, H, 128 x 128] M of each segment (the saved set's Mseg)
+  float* B;      // [NS, H, 128 x 128] B: the state after the segment from a zero state
+  float* S0;     // [NS, H, 128 x 128] state entering each segment (forward walk)
+  float* Brev;   // [NS, H, 128 x 128] B': dS at the segment start from a zero dS at its end
+  float* D0;     // [NS, H, 128 x 128] dS at each segment's end (reverse walk)
+};
+// Scan passes: per-chunk outputs from the walk's segment states, or the
+// segment summaries only.
+enum : int { SCAN_FINISH = 0, SCAN_SUMMARY = 1 };
 
 struct Dims {
   int64_t T;
   int H;
   int N;        // documents
   int NC;       // n_chunks_max
+  int L;        // chunks per segment of the segment-parallel scans (0: whole documents)
+  int NS;       // n_segments_max
   int raw;      // gate form raw
   int l2norm;
   float scale;
@@ -105,15 +127,19 @@ constexpr size_t BYTES = (size_t)ELEMS * 2;  // 131584, a multiple of 16
 
 hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
                             hipStream_t s);
+hipError_t launch_seg_map(const Dims& d, const ChunkTable& ct, hipStream_t s);
+hipError_t launch_walk(const Dims& d, const ChunkTable& ct, const SegWork& sg, int reverse,
+                       hipStream_t s);
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, int with_bwd, hipStream_t s);
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                           const SavedSet& sv, const void* panels, int save_R, hipStream_t s);
+                           const SavedSet& sv, const void* panels, int save_R,
+                           const SegWork& sg, int mode, hipStream_t s);
 hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& sv,
                           const void* panels, void* o, hipStream_t s);
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, const void* dO, void* dv,
-                           const BwdWork& bw, hipStream_t s);
+                           const BwdWork& bw, const SegWork& sg, int mode, hipStream_t s);
 hipError_t launch_bwd_intra(const Dims& d, const Inputs& in, const ChunkTable& ct,
                             const SavedSet& sv, const void* dO, const BwdOut& out,
                             const BwdWork& bw, hipStream_t s);

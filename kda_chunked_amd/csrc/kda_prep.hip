@@ -102,6 +102,56 @@ hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& 
   return hipGetLastError();
 }
 
+// Segments: document d's chunks [doc_c0[d], doc_c0[d+1]) cut into runs of L
+// chunks (one segment per document, empty or not, when L = 0). Documents are
+// taken 256 at a time as in the chunk map: a prefix sum of their segment
+// counts gives each its first segment, then segment entries are filled by a
+// binary search over the batch's inclusive segment ends.
+__global__ __launch_bounds__(256) void seg_map_kernel(int N, int L, int NS, ChunkTable ct) {
+  __shared__ int32_t scan[256], s_end[256];
+  const int t = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < N; base += 256) {
+    const int d = base + t;
+    const int nb = min(256, N - base);
+    int cnt = 0;
+    if (d < N) {
+      const int nch = max(0, ct.doc_c0[d + 1] - ct.doc_c0[d]);
+      cnt = L > 0 ? (nch + L - 1) / L : 1;
+    }
+    scan[t] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = t >= off ? scan[t - off] : 0;
+      __syncthreads();
+      scan[t] += v;
+      __syncthreads();
+    }
+    const int total = scan[255];
+    s_end[t] = carry + scan[t];
+    if (d < N) ct.seg_doc0[d] = min(carry + scan[t] - cnt, NS);
+    __syncthreads();
+    const int sstop = min(carry + total, NS);
+    for (int sg = carry + t; sg < sstop; sg += 256) {
+      int lo = 0, hi = nb - 1;      // first document of the batch whose segment end exceeds sg
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_end[mid] > sg) hi = mid;
+        else lo = mid + 1;
+      }
+      ct.seg_doc[sg] = base + lo;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (t == 0) ct.seg_doc0[N] = min(carry, NS);
+}
+
+hipError_t launch_seg_map(const Dims& d, const ChunkTable& ct, hipStream_t s) {
+  hipLaunchKernelGGL(seg_map_kernel, dim3(1), dim3(256), 0, s, d.N, d.L, d.NS, ct);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // The prep kernel: 512 threads (8 waves). For loads and the elementwise
 // panels, thread t owns row rA = t >> 3 and channels cA .. cA+15 (cA = 16 (t & 7)).

@@ -138,17 +138,32 @@ KDA_DEV int chain_src(int k, int u) {
   return fwd_panel::GAM + (u - 3584) * 8;
 }
 
+// One chain is a segment of one head (a whole document when the scans are not
+// segmented). MODE = SCAN_FINISH: the chain starts from the segment's entering
+// state (zero at a document start, else the forward walk's) and stores the
+// per-chunk S_in, R and U~. MODE = SCAN_SUMMARY (segments of documents with
+// more than one segment): variant 0 starts from the identity with V = 0 and
+// ends at the segment's M; variant 1 starts from zero and ends at its B.
+template <int MODE>
 __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
                                                                SavedSet sv,
                                                                const bf16* __restrict__ panels,
-                                                               int save_R) {
+                                                               int save_R, SegWork sg) {
   __shared__ ChainBuf bufA;
   __shared__ ChainBuf bufB;
   __shared__ SliceBuf slice[2];
-  int pair, tile;
-  if (!scan_coords(d.N * d.H, pair, tile)) return;
-  const int doc = pair / d.H, h = pair % d.H;
-  const int c0 = ct.doc_c0[doc], c1 = ct.doc_c0[doc + 1];
+  int chain, tile;
+  if (!scan_coords((MODE == SCAN_SUMMARY ? 2 : 1) * d.NS * d.H, chain, tile)) return;
+  const int var = MODE == SCAN_SUMMARY ? chain & 1 : 0;
+  const int sh = MODE == SCAN_SUMMARY ? chain >> 1 : chain;
+  const int seg = sh / d.H, h = sh % d.H;
+  if (seg >= ct.seg_doc0[d.N]) return;
+  const int doc = ct.seg_doc[seg];
+  const int sfirst = ct.seg_doc0[doc], slast = ct.seg_doc0[doc + 1] - 1;
+  if (MODE == SCAN_SUMMARY && sfirst == slast) return;
+  const int dc1 = ct.doc_c0[doc + 1];
+  const int c0 = d.L > 0 ? ct.doc_c0[doc] + d.L * (seg - sfirst) : ct.doc_c0[doc];
+  const int c1 = d.L > 0 ? min(dc1, c0 + d.L) : dc1;
   const int t = threadIdx.x, w = wave_id();
   const int jv = tile * VT + 16 * (w & 1);    // a compute wave's 16 state columns
   const int H = d.H;
@@ -160,8 +175,18 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
 
   // state slice: tile m holds rows 16 m .. 16 m + 15 (D layout)
   f32x4 S[8];
+  const int64_t segoff = ((int64_t)seg * H + h) * HD * HD;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) S[m] = zero4();
+  for (int m = 0; m < 8; ++m) {
+    if (MODE == SCAN_FINISH && seg != sfirst && w < 2) {
+      S[m] = *reinterpret_cast<const f32x4*>(sg.S0 + segoff + tile_off(m, jv >> 4));
+    } else if (MODE == SCAN_SUMMARY && var == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[m][i] = 16 * m + drow(i) == jv + dcol() ? 1.f : 0.f;
+    } else {
+      S[m] = zero4();
+    }
+  }
   // The chunks of a document are consecutive: first token and length follow
   // from the document's first token and end.
   int64_t tokA = 0, tEnd = 0;
@@ -194,8 +219,10 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(cur.v + (r0 + (sl >> 2)) * VT + 16 * w + 4 * (sl & 3)));
         const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
+        // the identity variant of a segment summary takes V = 0
+        const bool vz = MODE == SCAN_SUMMARY && var == 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[rb][i] = r0 + i < n ? bf2f(xb[i]) : 0.f;
+        for (int i = 0; i < 4; ++i) R[rb][i] = r0 + i < n && !vz ? bf2f(xb[i]) : 0.f;
       }
     }
     // S_in: to memory and, as B operand, to this wave's LDS
@@ -204,7 +231,8 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         // streamed out (non-temporal): read only by later kernels
-        __builtin_nontemporal_store(S[m], reinterpret_cast<f32x4*>(Sg + tile_off(m, jv >> 4)));
+        if (MODE == SCAN_FINISH)
+          __builtin_nontemporal_store(S[m], reinterpret_cast<f32x4*>(Sg + tile_off(m, jv >> 4)));
         store_tile_t(S[m], SB, 16 * m, 0);
       }
     }
@@ -217,7 +245,7 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      if (save_R)
+      if (MODE == SCAN_FINISH && save_R)
         __builtin_nontemporal_store(
             R[rb], reinterpret_cast<f32x4*>(sv.R + ch * CL * HD + tile_off(rb, jv >> 4)));
       store_tile_t(R[rb], RB, 16 * rb, 0);
@@ -241,8 +269,9 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      __builtin_nontemporal_store(
-          U[rb], reinterpret_cast<f32x4*>(sv.U + ch * CL * HD + tile_off(rb, jv >> 4)));
+      if (MODE == SCAN_FINISH)
+        __builtin_nontemporal_store(
+            U[rb], reinterpret_cast<f32x4*>(sv.U + ch * CL * HD + tile_off(rb, jv >> 4)));
       store_tile_t(U[rb], UB, 16 * rb, 0);
     }
     // S_out = e^(G_last) * S_in + Ke^T U~
@@ -327,12 +356,23 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
     step(bufA, ci);
     if (ci + 1 < c1) step(bufB, ci + 1);
   }
+  if (MODE == SCAN_SUMMARY) {
+    float* dst = (var == 0 ? sg.M : sg.B) + segoff;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) *reinterpret_cast<f32x4*>(dst + tile_off(m, jv >> 4)) = S[m];
+  }
 }
 
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
-                           const SavedSet& sv, const void* panels, int save_R, hipStream_t s) {
-  hipLaunchKernelGGL(fwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(2 * FS_THREADS), 0, s, d, in,
-                     ct, sv, reinterpret_cast<const bf16*>(panels), save_R);
+                           const SavedSet& sv, const void* panels, int save_R,
+                           const SegWork& sg, int mode, hipStream_t s) {
+  const bf16* pn = reinterpret_cast<const bf16*>(panels);
+  if (mode == SCAN_SUMMARY)
+    hipLaunchKernelGGL(fwd_scan_kernel<SCAN_SUMMARY>, dim3(scan_grid(2 * d.NS * d.H)),
+                       dim3(2 * FS_THREADS), 0, s, d, in, ct, sv, pn, save_R, sg);
+  else
+    hipLaunchKernelGGL(fwd_scan_kernel<SCAN_FINISH>, dim3(scan_grid(d.NS * d.H)),
+                       dim3(2 * FS_THREADS), 0, s, d, in, ct, sv, pn, save_R, sg);
   return hipGetLastError();
 }
 
@@ -556,15 +596,30 @@ KDA_DEV void bstage_unit(BwdScanSmem& sm, int k, int t, const bf16x8& x) {
   *reinterpret_cast<bf16x8*>(dst) = x;
 }
 
+// One chain is a segment of one head, walked from its last chunk to its
+// first. MODE = SCAN_FINISH: dS starts from the segment's exit value (zero at a
+// document end, else the reverse walk's) and the per-chunk dU~, dS_out and dv
+// are stored. MODE = SCAN_SUMMARY (segments of documents with more than one
+// segment): dS starts from zero and only the dS reached at the segment start
+// (its B') is stored.
+template <int MODE>
 __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, ChunkTable ct,
                                                             SavedSet sv,
                                                             const bf16* __restrict__ dO,
-                                                            bf16* __restrict__ dv, BwdWork bw) {
+                                                            bf16* __restrict__ dv, BwdWork bw,
+                                                            SegWork sg) {
   __shared__ BwdScanSmem sm;
-  int pair, tile;
-  if (!scan_coords(d.N * d.H, pair, tile)) return;
-  const int doc = pair / d.H, h = pair % d.H;
-  const int c0 = ct.doc_c0[doc], c1 = ct.doc_c0[doc + 1];
+  int chain, tile;
+  if (!scan_coords(d.NS * d.H, chain, tile)) return;
+  const int seg = chain / d.H, h = chain % d.H;
+  if (seg >= ct.seg_doc0[d.N]) return;
+  const int doc = ct.seg_doc[seg];
+  const int sfirst = ct.seg_doc0[doc], slast = ct.seg_doc0[doc + 1] - 1;
+  if (MODE == SCAN_SUMMARY && sfirst == slast) return;
+  const int dc1 = ct.doc_c0[doc + 1];
+  const int c0 = d.L > 0 ? ct.doc_c0[doc] + d.L * (seg - sfirst) : ct.doc_c0[doc];
+  const int c1 = d.L > 0 ? min(dc1, c0 + d.L) : dc1;
+  const int64_t segoff = ((int64_t)seg * d.H + h) * HD * HD;
   const int t = threadIdx.x, w = wave_id();
   const int rb = w & 3, nw = w >> 2;
   const int j0 = tile * VT;
@@ -627,6 +682,15 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     (&sm.ds_hi[0][0])[e] = f2bf(0.f);
     (&sm.ds_lo[0][0])[e] = f2bf(0.f);
   }
+  if (MODE == SCAN_FINISH && seg != slast) {
+    // the dS leaving this segment, from the reverse walk (rows 16 w, this tile's columns)
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      dS[nt] = *reinterpret_cast<const f32x4*>(sg.D0 + segoff + tile_off(w, (j0 >> 4) + nt));
+      store_tile_t(dS[nt], DS, 16 * w, 16 * nt);
+    }
+  }
   // issued in the order of one step's requests, so that the waits counted
   // for the first step are no stricter than for the later ones
   if (c0 < c1) {
@@ -658,8 +722,9 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
       mma<SPLIT_A, true>(dU, AQ, 16 * rb, DO, 16 * nw, (16 * rb / 32) * 32, CL);
       mma_k<SPLIT_BW, HD, true>(dU, KE, 16 * rb, DS, 16 * nw);
       // dU~ and dS_out are streamed out (non-temporal): read only by the next kernel
-      __builtin_nontemporal_store(
-          dU, reinterpret_cast<f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)));
+      if (MODE == SCAN_FINISH)
+        __builtin_nontemporal_store(
+            dU, reinterpret_cast<f32x4*>(bw.dU + ch * CL * HD + tile_off(rb, (j0 >> 4) + nw)));
       store_tile_t(dU, DU, 16 * rb, 16 * nw);
     }
     stage(6, 8);                                   // Tb
@@ -677,7 +742,7 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     // ---- D. dS_in = Diag(e^G_last) dS_out + scale Qd^T dO - Kd^T dR
     {
       // dv = bf16(dR): row rO, columns j0 + cO .. + 3, from the hi plane of dR^T
-      if (rO < n) {
+      if (MODE == SCAN_FINISH && rO < n) {
         bf16x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = sm.dr_hi[cO + e][rO];
@@ -686,8 +751,9 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
       float* dSg = bw.dS + ch * HD * HD;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        __builtin_nontemporal_store(dS[nt],
-                                    reinterpret_cast<f32x4*>(dSg + tile_off(w, (j0 >> 4) + nt)));
+        if (MODE == SCAN_FINISH)
+          __builtin_nontemporal_store(dS[nt],
+                                      reinterpret_cast<f32x4*>(dSg + tile_off(w, (j0 >> 4) + nt)));
 #pragma unroll
         for (int i = 0; i < 4; ++i) dS[nt][i] *= sm.gam[16 * w + drow(i)];
       }
@@ -700,13 +766,24 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     for (int nt = 0; nt < 2; ++nt) store_tile_t(dS[nt], DS, 16 * w, 16 * nt);
     __syncthreads();
   }
+  if (MODE == SCAN_SUMMARY) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      *reinterpret_cast<f32x4*>(sg.Brev + segoff + tile_off(w, (j0 >> 4) + nt)) = dS[nt];
+  }
 }
 
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
                            const SavedSet& sv, const void* dO, void* dv,
-                           const BwdWork& bw, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_grid(d.N * d.H)), dim3(NT_SCAN), 0, s, d, in,
-                     ct, sv, reinterpret_cast<const bf16*>(dO), reinterpret_cast<bf16*>(dv), bw);
+                           const BwdWork& bw, const SegWork& sg, int mode, hipStream_t s) {
+  const bf16* pdo = reinterpret_cast<const bf16*>(dO);
+  bf16* pdv = reinterpret_cast<bf16*>(dv);
+  if (mode == SCAN_SUMMARY)
+    hipLaunchKernelGGL(bwd_scan_kernel<SCAN_SUMMARY>, dim3(scan_grid(d.NS * d.H)), dim3(NT_SCAN),
+                       0, s, d, in, ct, sv, pdo, pdv, bw, sg);
+  else
+    hipLaunchKernelGGL(bwd_scan_kernel<SCAN_FINISH>, dim3(scan_grid(d.NS * d.H)), dim3(NT_SCAN),
+                       0, s, d, in, ct, sv, pdo, pdv, bw, sg);
   return hipGetLastError();
 }
 

@@ -63,7 +63,15 @@ def test_sizes():
     assert B.workspace_bytes(p, False) > 0
     # a saving forward keeps its per-chunk set in `saved`, not in the workspace
     assert B.workspace_bytes(p, False, True) >= B.workspace_bytes(p, False, False) + s
-    assert B.workspace_bytes(p, False, False) < 4096
+    wide = _p(T=1000, H=64)          # enough chains: one per document, no segment buffers
+    assert B.workspace_bytes(wide, False, False) < 4096
+    # few chains (2 documents x 4 heads): 64-chunk documents are cut into
+    # segments of 16 chunks, whose summaries need two 128 x 128 fp32 buffers
+    seg = _p(T=8192, H=4)
+    ns = (8192 // 64 + 2) // 16 + 2
+    assert B.workspace_bytes(seg, False, False) >= 2 * ns * 4 * 128 * 128 * 4
+    # documents averaging fewer than two segments are not cut
+    assert B.workspace_bytes(_p(T=3548, H=4), False, False) < 4096
     # invalid problems size to zero
     assert B.saved_bytes(_p(H=0)) == 0
     assert B.workspace_bytes(_p(dk=64), False) == 0
@@ -191,5 +199,6 @@ def test_noalloc_forward_rejects_calls_beyond_its_scratch():
     assert rc == 3 and "scratch" in err
     rc, err = _noalloc_status(_p(H=0))
     assert rc == 1 and "head" in err
-    # with a saved set the workspace is the chunk table only, far below the scratch
-    assert B.workspace_bytes(big, False, False) < 1 << 20
+    # with a saved set the workspace is the chunk table and, for few chains,
+    # the segment summaries (at most about 112 chain matrices): below the scratch
+    assert B.workspace_bytes(big, False, False) < 16 << 20 < B.NOALLOC_SCRATCH_BYTES
