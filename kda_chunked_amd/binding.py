@@ -41,6 +41,18 @@ class kda_problem(ctypes.Structure):
     ]
 
 
+class kda_attn_problem(ctypes.Structure):
+    _fields_ = [
+        ("Tq", ctypes.c_int64),
+        ("Tk", ctypes.c_int64),
+        ("num_seqs", ctypes.c_int32),
+        ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
 class kda_conv_problem(ctypes.Structure):
     _fields_ = [
         ("T", ctypes.c_int64),
@@ -55,7 +67,9 @@ class kda_conv_problem(ctypes.Structure):
 _lib = None
 EXPORTS = ("kda_saved_bytes", "kda_workspace_bytes", "kda_fwd", "kda_bwd", "kda_fwd_noalloc",
            "kda_set_launch_hook", "kda_status_string", "kda_last_error", "kda_abi_version",
-           "kda_conv_workspace_bytes", "kda_conv_silu_fwd", "kda_conv_silu_bwd")
+           "kda_conv_workspace_bytes", "kda_conv_silu_fwd", "kda_conv_silu_bwd",
+           "kda_attn_workspace_bytes", "kda_attn_fwd", "kda_attn_bwd")
+ATTN_DKV_BF16, ATTN_DKV_F32, ATTN_DKV_F32_ADD = 0, 1, 2   # kda_attn.h
 NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES in kda.h
 LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int,
                                ctypes.c_void_p)
@@ -88,6 +102,14 @@ def lib():
         L.kda_conv_silu_fwd.restype = ctypes.c_int
         L.kda_conv_silu_bwd.argtypes = [cp] + [vp] * 11 + [sz, vp]
         L.kda_conv_silu_bwd.restype = ctypes.c_int
+        ap = ctypes.POINTER(kda_attn_problem)
+        L.kda_attn_workspace_bytes.argtypes = [ap, ctypes.c_int, ctypes.c_int64]
+        L.kda_attn_workspace_bytes.restype = sz
+        L.kda_attn_fwd.argtypes = [ap] + [vp] * 8 + [sz, vp]
+        L.kda_attn_fwd.restype = ctypes.c_int
+        L.kda_attn_bwd.argtypes = ([ap] + [vp] * 11 + [ctypes.c_int, vp, ctypes.c_int64, vp, sz,
+                                                       vp])
+        L.kda_attn_bwd.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.argtypes = []
@@ -324,3 +346,86 @@ class ConvSiLU:
         conv_silu_bwd(self.p, x, w, b, halo, cu_seqlens, dy, out["dx"], out["dw"], out.get("db"),
                       out.get("dhalo"), self.workspace)
         return out
+
+
+# ---------------------------------------------------------------- GQA attention
+
+def attn_problem(Tq, Tk, num_seqs, Hq, Hkv, D=256, scale=None):
+    scale = D ** -0.5 if scale is None else scale
+    return kda_attn_problem(int(Tq), int(Tk), int(num_seqs), int(Hq), int(Hkv), int(D),
+                            float(scale))
+
+
+def attn_workspace_bytes(p: kda_attn_problem, stage: int, dst_rows: int = 0) -> int:
+    return int(lib().kda_attn_workspace_bytes(ctypes.byref(p), int(stage), int(dst_rows)))
+
+
+def _dev_attn(p, tensors):
+    ts = [t for t in tensors if t is not None]
+    if ts and all(t.is_cuda for t in ts):
+        return ts[0].device
+    if attn_workspace_bytes(p, 0) != 0:
+        raise ValueError("every tensor passed to the attention op must be on the GPU")
+    return None
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def attn_fwd(p, q, k, v, cu_q, cu_k, o, lse, workspace):
+    """Enqueue the attention forward on the current stream of q's device."""
+    dev = _dev_attn(p, (q, k, v, cu_q, cu_k, o, lse, workspace))
+    with _device_ctx(dev):
+        rc = lib().kda_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_q),
+                                _ptr(cu_k), _ptr(o), _ptr(lse), _ptr(workspace),
+                                _nbytes(workspace), _stream(dev))
+    _check(rc)
+
+
+def attn_bwd(p, q, k, v, cu_q, cu_k, o, lse, dO, dq, dk, dv, form, row_map, dst_rows,
+             workspace):
+    """Enqueue the attention backward on the current stream of q's device."""
+    dev = _dev_attn(p, (q, k, v, cu_q, cu_k, o, lse, dO, dq, dk, dv, row_map, workspace))
+    with _device_ctx(dev):
+        rc = lib().kda_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_q),
+                                _ptr(cu_k), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk),
+                                _ptr(dv), int(form), _ptr(row_map), int(dst_rows),
+                                _ptr(workspace), _nbytes(workspace), _stream(dev))
+    _check(rc)
+
+
+class GQAAttention:
+    """Packed-varlen causal GQA attention, head dim 256: q [Tq, Hq, 256] and
+    k, v [Tk, Hkv, 256] bf16; cu_q, cu_k [num_seqs + 1] int32 on the device.
+    One workspace serves the forward and every backward form; a larger one
+    serves smaller problems too."""
+
+    def __init__(self, Tq, Tk, num_seqs, Hq, Hkv, scale=None, dst_rows=None, device="cuda"):
+        self.p = attn_problem(Tq, Tk, num_seqs, Hq, Hkv, 256, scale)
+        self.device = torch.device(device)
+        stage = 2 if dst_rows is not None else 1
+        n = max(attn_workspace_bytes(self.p, stage, dst_rows or 0), 16)
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def forward(self, q, k, v, cu_q, cu_k, o=None, lse=None, with_lse=True):
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None and with_lse:
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        attn_fwd(self.p, q, k, v, cu_q, cu_k, o, lse, self.workspace)
+        return o, lse
+
+    def backward(self, q, k, v, cu_q, cu_k, o, lse, dO, form=ATTN_DKV_BF16, dk=None, dv=None,
+                 row_map=None, dst_rows=0, dq=None):
+        """dq, dk, dv. Form ATTN_DKV_F32_ADD adds into the given fp32 dk, dv
+        [dst_rows, Hkv, 256] through row_map [Tk] int32."""
+        if dq is None:
+            dq = torch.empty_like(q)
+        if form != ATTN_DKV_F32_ADD:
+            dt = torch.bfloat16 if form == ATTN_DKV_BF16 else torch.float32
+            dk = torch.empty(k.shape, dtype=dt, device=k.device) if dk is None else dk
+            dv = torch.empty(v.shape, dtype=dt, device=v.device) if dv is None else dv
+        attn_bwd(self.p, q, k, v, cu_q, cu_k, o, lse, dO, dq, dk, dv, form, row_map, dst_rows,
+                 self.workspace)
+        return dq, dk, dv

@@ -20,7 +20,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 
 SOURCES = ["kda_api.cpp", "kda_prep.hip", "kda_scan.hip", "kda_bwd_intra.hip",
-           "kda_noalloc.hip", "conv_silu.hip", "kda_walk.hip"]
+           "kda_noalloc.hip", "conv_silu.hip", "kda_walk.hip", "attn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

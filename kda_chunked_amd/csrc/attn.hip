@@ -1,0 +1,827 @@
+// Packed-varlen causal GQA training attention, head dimension 256 (flashinfer
+// PR #7774, description and commit notes: bottom-right causal alignment per
+// segment, natural-log LSE, dK / dV as FP32 sums over each key head's query
+// heads in three output forms, BF16 in and out with FP32 accumulation).
+//
+// Every product runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation. A
+// workgroup is 4 waves over a 64-row block; a wave owns 16 rows.
+//   forward:  per (query block, HPW query heads of one group), key blocks of
+//             64 in order with an online softmax in base 2: S = Q K^T,
+//             P = exp2(S scale log2 e - m), O += P V, then O / l and
+//             lse = (m + log2 l) ln 2. The heads of a workgroup share each
+//             staged K / V block and every operand fragment read from it.
+//   delta:    Delta_i = <dO_i, o_i> per (row, head).
+//   dq:       per (query block, query head): S, P from the lse, dP = dO V^T,
+//             dS = P (dP - Delta), dq += dS K.
+//   dk, dv:   per (key block, key head): for each query head of the group in
+//             order and each query block that sees the keys, P^T and dS^T,
+//             dv += P^T dO, dk += dS^T Q; the fixed order makes the sums over
+//             the group's heads the same bits every run.
+//   row map:  the fp32 window sums go to their destination rows through a
+//             sort of (row, key) pairs, so that the keys sharing a row are
+//             summed in ascending key order.
+// P and dS enter their products as bf16. Rows past a block's end are loaded
+// from the block's last row and masked out.
+#include <cmath>
+#include <utility>
+
+#include "kda_attn.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace attn {
+
+constexpr int AD = 256;           // head dimension
+constexpr int BR = 64;            // rows of a query or key block
+constexpr int A_LD = AD + 8;      // 528-byte rows of a staged block
+constexpr int P_LD = BR + 8;      // 144-byte rows of a wave's P / dS block
+constexpr float LOG2E_F = 1.4426950408889634f;
+constexpr float LN2_F = 0.6931471805599453f;
+
+struct Dims {
+  int64_t Tq, Tk;
+  int S, Hq, Hkv, grp;
+  int NCq, NCk;                   // 64-row blocks, upper bounds
+  float scale;
+};
+
+// The segment of block ci: the last s with c0[s] <= ci (an empty segment
+// shares its first block index with the next one).
+KDA_DEV int seg_of(const int32_t* c0, int S, int ci) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (c0[mid] <= ci) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Segment bounds, clamped into the packed tensors.
+KDA_DEV void seg_bounds(const int32_t* cu, int s, int64_t T, int64_t& a, int64_t& n) {
+  int64_t x = cu[s], y = cu[s + 1];
+  x = x < 0 ? 0 : (x > T ? T : x);
+  y = y < x ? x : (y > T ? T : y);
+  a = x;
+  n = y - x;
+}
+
+KDA_DEV float row_max16(float v) {
+  v = fmaxf(v, row_xor<1>(v));
+  v = fmaxf(v, row_xor<3>(v));
+  v = fmaxf(v, row_xor<7>(v));
+  return fmaxf(v, row_xor<15>(v));
+}
+
+// 64 rows of one head of a [T, H, 256] bf16 tensor into an LDS block; rows
+// from n on repeat row n - 1 (their results are masked).
+KDA_DEV void stage_rows(bf16 (*dst)[A_LD], const bf16* src, int64_t row0, int n, int H, int h) {
+  for (int u = threadIdx.x; u < BR * AD / 8; u += 256) {
+    const int r = u >> 5, c8 = (u & 31) * 8;
+    const int rr = r < n ? r : n - 1;
+    *reinterpret_cast<bf16x8*>(&dst[r][c8]) =
+        *reinterpret_cast<const bf16x8*>(src + ((row0 + rr) * H + h) * AD + c8);
+  }
+}
+
+// A wave's 16 x 256 fp32 tiles (D layout, 16 column tiles) to rows of a
+// [T, H, 256] bf16 tensor through the wave's 16 rows of an LDS block.
+KDA_DEV void write_rows_bf16(bf16 (*stage)[A_LD], const f32x4 (&acc)[16], float mul, bf16* dst,
+                             int64_t row0, int nvalid, int H, int h) {
+  const int w = wave_id(), l = lane_id();
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[16 * w + drow(i)][16 * dt + dcol()] = f2bf(acc[dt][i] * mul);
+  __builtin_amdgcn_s_waitcnt(0xc07f);     // this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  for (int u = l; u < 16 * AD / 8; u += 64) {
+    const int r = u >> 5, c8 = (u & 31) * 8, row = 16 * w + r;
+    if (row < nvalid)
+      *reinterpret_cast<bf16x8*>(dst + ((row0 + row) * H + h) * AD + c8) =
+          *reinterpret_cast<const bf16x8*>(&stage[row][c8]);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);     // reads done before the rows are staged again
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The same through fp32 LDS rows (all waves together; the caller brackets the
+// call with barriers).
+KDA_DEV void write_rows_f32(float (*stage)[AD + 4], const f32x4 (&acc)[16], float mul, float* dst,
+                            int64_t row0, int nvalid, int H, int h) {
+  const int w = wave_id();
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[16 * w + drow(i)][16 * dt + dcol()] = acc[dt][i] * mul;
+  __syncthreads();
+  for (int e = threadIdx.x; e < BR * AD / 4; e += 256) {
+    const int r = e >> 6, c4 = (e & 63) * 4;
+    if (r < nvalid)
+      *reinterpret_cast<f32x4*>(dst + ((row0 + r) * H + h) * AD + c4) =
+          *reinterpret_cast<const f32x4*>(&stage[r][c4]);
+  }
+}
+
+// ------------------------------------------------------------------ forward
+template <int HPW>
+struct FwdSmem {
+  bf16 k[BR][A_LD];
+  bf16 v[BR][A_LD];
+  bf16 p[4][HPW][16][P_LD];
+};
+
+template <int HPW>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(Dims a, ChunkTable qt,
+                                                      const int32_t* __restrict__ cuq,
+                                                      const int32_t* __restrict__ cuk,
+                                                      const bf16* __restrict__ q,
+                                                      const bf16* __restrict__ k,
+                                                      const bf16* __restrict__ v,
+                                                      bf16* __restrict__ o, float* __restrict__ lse) {
+  __shared__ FwdSmem<HPW> sm;
+  const int ci = blockIdx.x, h0 = blockIdx.y * HPW;
+  if (ci >= qt.doc_c0[a.S]) return;
+  const int s = seg_of(qt.doc_c0, a.S, ci);
+  int64_t qs, Lq, ks, Lk;
+  seg_bounds(cuq, s, a.Tq, qs, Lq);
+  seg_bounds(cuk, s, a.Tk, ks, Lk);
+  const int64_t t0 = qt.tok[ci];
+  const int nq = qt.len[ci];
+  const int64_t i0 = t0 - qs, off = Lk - Lq;
+  const int g = h0 / a.grp, w = wave_id(), l = lane_id();
+  const float c2 = a.scale * LOG2E_F;
+
+  bf16x8 qf[HPW][8];
+  {
+    const int r = 16 * w + (l & 15), rr = r < nq ? r : nq - 1;
+#pragma unroll
+    for (int hp = 0; hp < HPW; ++hp) {
+      const bf16* src = q + ((t0 + rr) * a.Hq + h0 + hp) * AD + 8 * (l >> 4);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) qf[hp][kk] = *reinterpret_cast<const bf16x8*>(src + 32 * kk);
+    }
+  }
+  float m[HPW][4], ls[HPW][4];
+  f32x4 O[HPW][16];
+#pragma unroll
+  for (int hp = 0; hp < HPW; ++hp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[hp][i] = -INFINITY, ls[hp][i] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) O[hp][dt] = zero4();
+  }
+  int64_t kend = i0 + nq + off;             // keys [0, kend) can be seen by the block
+  kend = kend < 0 ? 0 : (kend > Lk ? Lk : kend);
+  for (int64_t kb0 = 0; kb0 < kend; kb0 += BR) {
+    const int nk = (int)(kend - kb0 < BR ? kend - kb0 : BR);
+    __syncthreads();
+    stage_rows(sm.k, k, ks + kb0, nk, a.Hkv, g);
+    stage_rows(sm.v, v, ks + kb0, nk, a.Hkv, g);
+    __syncthreads();
+    f32x4 S[HPW][4];
+#pragma unroll
+    for (int hp = 0; hp < HPW; ++hp)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) S[hp][nt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const bf16x8 kb = frag(&sm.k[0][0], A_LD, 16 * nt, 32 * kk);
+#pragma unroll
+        for (int hp = 0; hp < HPW; ++hp) S[hp][nt] = mfma16(qf[hp][kk], kb, S[hp][nt]);
+      }
+    // base-2 logits, masked; the running max and sum per row
+#pragma unroll
+    for (int hp = 0; hp < HPW; ++hp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + drow(i);
+        const int64_t qi = i0 + r;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int jl = 16 * nt + dcol();
+          const bool vis = r < nq && jl < nk && kb0 + jl <= qi + off;
+          S[hp][nt][i] = vis ? S[hp][nt][i] * c2 : -INFINITY;
+          mx = fmaxf(mx, S[hp][nt][i]);
+        }
+        mx = row_max16(mx);
+        const float mn = fmaxf(m[hp][i], mx);
+        const float corr = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[hp][i] - mn);
+        float sum = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float pv = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S[hp][nt][i] - mn);
+          S[hp][nt][i] = pv;
+          sum += pv;
+        }
+        sum = row_sum16(sum);
+        ls[hp][i] = ls[hp][i] * corr + sum;
+        m[hp][i] = mn;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) O[hp][dt][i] *= corr;
+      }
+#pragma unroll
+    for (int hp = 0; hp < HPW; ++hp)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.p[w][hp][drow(i)][16 * nt + dcol()] = f2bf(S[hp][nt][i]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 pa[HPW];
+#pragma unroll
+      for (int hp = 0; hp < HPW; ++hp) pa[hp] = frag(&sm.p[w][hp][0][0], P_LD, 0, 32 * kk);
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        const bf16x8 vb = fragT(&sm.v[0][0], A_LD, 16 * dt, 32 * kk);
+#pragma unroll
+        for (int hp = 0; hp < HPW; ++hp) O[hp][dt] = mfma16(pa[hp], vb, O[hp][dt]);
+      }
+    }
+  }
+  __syncthreads();                          // the K block is free: O leaves through it
+#pragma unroll
+  for (int hp = 0; hp < HPW; ++hp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + drow(i);
+      const bool seen = ls[hp][i] > 0.f;
+      const float inv = seen ? 1.f / ls[hp][i] : 0.f;
+      if (lse && dcol() == 0 && r < nq)
+        lse[(t0 + r) * a.Hq + h0 + hp] =
+            seen ? (m[hp][i] + __builtin_amdgcn_logf(ls[hp][i])) * LN2_F : -INFINITY;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) O[hp][dt][i] *= inv;
+    }
+    write_rows_bf16(sm.k, O[hp], 1.f, o, t0, nq, a.Hq, h0 + hp);
+  }
+}
+
+// ------------------------------------------------------------------ delta
+// Delta[row, h] = <dO, o> over the 256 channels: one wave per (row, head).
+__global__ __launch_bounds__(256) void attn_delta_kernel(int64_t n, const bf16* __restrict__ o,
+                                                        const bf16* __restrict__ dO,
+                                                        float* __restrict__ delta) {
+  const int l = lane_id();
+  for (int64_t e = (int64_t)blockIdx.x * 4 + wave_id(); e < n; e += (int64_t)gridDim.x * 4) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(o + e * AD + 4 * l);
+    const bf16x4 y = *reinterpret_cast<const bf16x4*>(dO + e * AD + 4 * l);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += bf2f(x[i]) * bf2f(y[i]);
+    s = row_sum16(s);
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (l == 0) delta[e] = s;
+  }
+}
+
+// ------------------------------------------------------------------ dq
+struct DqSmem {
+  bf16 k[BR][A_LD];
+  bf16 v[BR][A_LD];
+  bf16 p[4][16][P_LD];
+};
+
+__global__ __launch_bounds__(256) void attn_dq_kernel(Dims a, ChunkTable qt,
+                                                     const int32_t* __restrict__ cuq,
+                                                     const int32_t* __restrict__ cuk,
+                                                     const bf16* __restrict__ q,
+                                                     const bf16* __restrict__ k,
+                                                     const bf16* __restrict__ v,
+                                                     const bf16* __restrict__ dO,
+                                                     const float* __restrict__ lse,
+                                                     const float* __restrict__ delta,
+                                                     bf16* __restrict__ dq) {
+  __shared__ DqSmem sm;
+  const int ci = blockIdx.x, h = blockIdx.y;
+  if (ci >= qt.doc_c0[a.S]) return;
+  const int s = seg_of(qt.doc_c0, a.S, ci);
+  int64_t qs, Lq, ks, Lk;
+  seg_bounds(cuq, s, a.Tq, qs, Lq);
+  seg_bounds(cuk, s, a.Tk, ks, Lk);
+  const int64_t t0 = qt.tok[ci];
+  const int nq = qt.len[ci];
+  const int64_t i0 = t0 - qs, off = Lk - Lq;
+  const int g = h / a.grp, w = wave_id(), l = lane_id();
+  const float c2 = a.scale * LOG2E_F;
+
+  bf16x8 qf[8], df[8];
+  {
+    const int r = 16 * w + (l & 15), rr = r < nq ? r : nq - 1;
+    const int64_t base = ((t0 + rr) * a.Hq + h) * AD + 8 * (l >> 4);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(q + base + 32 * kk);
+      df[kk] = *reinterpret_cast<const bf16x8*>(dO + base + 32 * kk);
+    }
+  }
+  float lb[4], dl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + drow(i), rr = r < nq ? r : nq - 1;
+    lb[i] = lse[(t0 + rr) * a.Hq + h] * LOG2E_F;
+    dl[i] = delta[(t0 + rr) * a.Hq + h];
+  }
+  f32x4 dQ[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) dQ[dt] = zero4();
+  int64_t kend = i0 + nq + off;
+  kend = kend < 0 ? 0 : (kend > Lk ? Lk : kend);
+  for (int64_t kb0 = 0; kb0 < kend; kb0 += BR) {
+    const int nk = (int)(kend - kb0 < BR ? kend - kb0 : BR);
+    __syncthreads();
+    stage_rows(sm.k, k, ks + kb0, nk, a.Hkv, g);
+    stage_rows(sm.v, v, ks + kb0, nk, a.Hkv, g);
+    __syncthreads();
+    f32x4 S[4], dP[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) S[nt] = dP[nt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        S[nt] = mfma16(qf[kk], frag(&sm.k[0][0], A_LD, 16 * nt, 32 * kk), S[nt]);
+        dP[nt] = mfma16(df[kk], frag(&sm.v[0][0], A_LD, 16 * nt, 32 * kk), dP[nt]);
+      }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + drow(i), jl = 16 * nt + dcol();
+        const bool vis = r < nq && jl < nk && kb0 + jl <= i0 + r + off;
+        const float p = vis ? __builtin_amdgcn_exp2f(S[nt][i] * c2 - lb[i]) : 0.f;
+        sm.p[w][drow(i)][jl] = f2bf(p * (dP[nt][i] - dl[i]));
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 da = frag(&sm.p[w][0][0], P_LD, 0, 32 * kk);
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt)
+        dQ[dt] = mfma16(da, fragT(&sm.k[0][0], A_LD, 16 * dt, 32 * kk), dQ[dt]);
+    }
+  }
+  __syncthreads();
+  write_rows_bf16(sm.k, dQ, a.scale, dq, t0, nq, a.Hq, h);
+}
+
+// ------------------------------------------------------------------ dk, dv
+struct KvSmem {
+  bf16 k[BR][A_LD];
+  bf16 v[BR][A_LD];
+  union {
+    struct {
+      bf16 q[BR][A_LD];
+      bf16 dO[BR][A_LD];
+    } in;
+    float out[BR][AD + 4];        // fp32 results on their way out
+  } u;
+  bf16 p[4][16][P_LD];            // P^T of the wave's keys
+  bf16 ds[4][16][P_LD];           // dS^T of the wave's keys
+  float lb[BR], dl[BR];           // lse log2 e and Delta of the staged queries
+};
+
+// F32: fp32 rows (window gradients, or the row-map form's staging), else bf16.
+template <bool F32>
+__global__ __launch_bounds__(256) void attn_dkdv_kernel(Dims a, ChunkTable qt, ChunkTable kt,
+                                                       const int32_t* __restrict__ cuq,
+                                                       const int32_t* __restrict__ cuk,
+                                                       const bf16* __restrict__ q,
+                                                       const bf16* __restrict__ k,
+                                                       const bf16* __restrict__ v,
+                                                       const bf16* __restrict__ dO,
+                                                       const float* __restrict__ lse,
+                                                       const float* __restrict__ delta,
+                                                       void* __restrict__ dk, void* __restrict__ dv) {
+  __shared__ KvSmem sm;
+  const int cj = blockIdx.x, g = blockIdx.y;
+  if (cj >= kt.doc_c0[a.S]) return;
+  const int s = seg_of(kt.doc_c0, a.S, cj);
+  int64_t qs, Lq, ks, Lk;
+  seg_bounds(cuq, s, a.Tq, qs, Lq);
+  seg_bounds(cuk, s, a.Tk, ks, Lk);
+  const int64_t u0 = kt.tok[cj];
+  const int nk = kt.len[cj];
+  const int64_t j0 = u0 - ks, off = Lk - Lq;
+  const int w = wave_id();
+  const float c2 = a.scale * LOG2E_F;
+  // query blocks of the segment that see some of these keys: i + off >= j0
+  const int qc0 = qt.doc_c0[s], qc1 = qt.doc_c0[s + 1];
+  int64_t ifirst = j0 - off;
+  ifirst = ifirst < 0 ? 0 : ifirst;
+  const int64_t qf64 = qc0 + ifirst / BR;
+  const int qfirst = qf64 < qc1 ? (int)qf64 : qc1;
+
+  stage_rows(sm.k, k, u0, nk, a.Hkv, g);
+  stage_rows(sm.v, v, u0, nk, a.Hkv, g);
+  f32x4 dK[16], dV[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) dK[dt] = dV[dt] = zero4();
+  for (int hh = 0; hh < a.grp; ++hh) {
+    const int h = g * a.grp + hh;
+    for (int qc = qfirst; qc < qc1; ++qc) {
+      const int64_t t0 = qt.tok[qc];
+      const int nq = qt.len[qc];
+      const int64_t i0 = t0 - qs;
+      __syncthreads();
+      stage_rows(sm.u.in.q, q, t0, nq, a.Hq, h);
+      stage_rows(sm.u.in.dO, dO, t0, nq, a.Hq, h);
+      if (threadIdx.x < BR) {
+        const int r = threadIdx.x, rr = r < nq ? r : nq - 1;
+        sm.lb[r] = lse[(t0 + rr) * a.Hq + h] * LOG2E_F;
+        sm.dl[r] = delta[(t0 + rr) * a.Hq + h];
+      }
+      __syncthreads();
+      f32x4 S[4], dP[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) S[nt] = dP[nt] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 ka = frag(&sm.k[0][0], A_LD, 16 * w, 32 * kk);
+        const bf16x8 va = frag(&sm.v[0][0], A_LD, 16 * w, 32 * kk);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          S[nt] = mfma16(ka, frag(&sm.u.in.q[0][0], A_LD, 16 * nt, 32 * kk), S[nt]);
+          dP[nt] = mfma16(va, frag(&sm.u.in.dO[0][0], A_LD, 16 * nt, 32 * kk), dP[nt]);
+        }
+      }
+      // S^T[key][query]: keys are rows 16 w + drow(i), queries columns 16 nt + dcol()
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int jr = 16 * w + drow(i), qcol = 16 * nt + dcol();
+          const bool vis = jr < nk && qcol < nq && j0 + jr <= i0 + qcol + off;
+          const float p = vis ? __builtin_amdgcn_exp2f(S[nt][i] * c2 - sm.lb[qcol]) : 0.f;
+          sm.p[w][drow(i)][qcol] = f2bf(p);
+          sm.ds[w][drow(i)][qcol] = f2bf(p * (dP[nt][i] - sm.dl[qcol]));
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 pa = frag(&sm.p[w][0][0], P_LD, 0, 32 * kk);
+        const bf16x8 da = frag(&sm.ds[w][0][0], P_LD, 0, 32 * kk);
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) {
+          dV[dt] = mfma16(pa, fragT(&sm.u.in.dO[0][0], A_LD, 16 * dt, 32 * kk), dV[dt]);
+          dK[dt] = mfma16(da, fragT(&sm.u.in.q[0][0], A_LD, 16 * dt, 32 * kk), dK[dt]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (!F32) {
+    write_rows_bf16(sm.u.in.q, dK, a.scale, reinterpret_cast<bf16*>(dk), u0, nk, a.Hkv, g);
+    write_rows_bf16(sm.u.in.dO, dV, 1.f, reinterpret_cast<bf16*>(dv), u0, nk, a.Hkv, g);
+  } else {
+    write_rows_f32(sm.u.out, dK, a.scale, reinterpret_cast<float*>(dk), u0, nk, a.Hkv, g);
+    __syncthreads();
+    write_rows_f32(sm.u.out, dV, 1.f, reinterpret_cast<float*>(dv), u0, nk, a.Hkv, g);
+  }
+}
+
+// ------------------------------------------------------------------ row map
+// Pairs (destination row, key) packed as row << 32 | key; a key whose row is
+// outside [0, R) gets row R and sorts last. Keys are distinct, so the order
+// is total and every sort gives the same sequence.
+constexpr int SORT_TILE = 2048;
+
+__global__ __launch_bounds__(256) void rowmap_keys_kernel(int64_t n, const int32_t* __restrict__ map,
+                                                         int64_t R, uint64_t* __restrict__ out) {
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (int64_t)gridDim.x * 256) {
+    const int64_t r = map[j];
+    const uint64_t rr = (r >= 0 && r < R) ? (uint64_t)r : (uint64_t)R;
+    out[j] = rr << 32 | (uint64_t)j;
+  }
+}
+
+// Bitonic sort of each tile of SORT_TILE pairs in LDS (the tail padded with
+// the largest value and not written back).
+__global__ __launch_bounds__(256) void rowmap_tile_sort_kernel(int64_t n, uint64_t* __restrict__ x) {
+  __shared__ uint64_t t[SORT_TILE];
+  const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
+  for (int i = threadIdx.x; i < SORT_TILE; i += 256)
+    t[i] = base + i < n ? x[base + i] : ~(uint64_t)0;
+  __syncthreads();
+  for (int size = 2; size <= SORT_TILE; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < SORT_TILE / 2; i += 256) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t a = t[lo], b = t[hi];
+        if ((a > b) == up) t[lo] = b, t[hi] = a;
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < SORT_TILE; i += 256)
+    if (base + i < n) x[base + i] = t[i];
+}
+
+// One merge pass: sorted runs of `width` become runs of 2 width. Each element
+// finds its place by counting the smaller elements of the other run.
+__global__ __launch_bounds__(256) void rowmap_merge_kernel(int64_t n, int64_t width,
+                                                          const uint64_t* __restrict__ x,
+                                                          uint64_t* __restrict__ y) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t pair0 = e / (2 * width) * (2 * width);
+    const int64_t a0 = pair0, a1 = pair0 + width < n ? pair0 + width : n;
+    const int64_t b0 = a1, b1 = pair0 + 2 * width < n ? pair0 + 2 * width : n;
+    const uint64_t key = x[e];
+    const bool inA = e < a1;
+    int64_t lo = inA ? b0 : a0, hi = inA ? b1 : a1;     // first element >= key in the other run
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (x[mid] < key) lo = mid + 1;
+      else hi = mid;
+    }
+    const int64_t pos = pair0 + (inA ? e - a0 : e - b0) + (lo - (inA ? b0 : a0));
+    y[pos] = key;
+  }
+}
+
+// Per run of one destination row in the sorted pairs: the window rows of its
+// keys summed in key order, added once to the destination. A thread owns four
+// channels of one key head.
+__global__ __launch_bounds__(256) void rowmap_add_kernel(int64_t n, int64_t R, int Hkv,
+                                                        const uint64_t* __restrict__ x,
+                                                        const float* __restrict__ wk,
+                                                        const float* __restrict__ wv,
+                                                        float* __restrict__ dk,
+                                                        float* __restrict__ dv) {
+  const int64_t cols = (int64_t)Hkv * (AD / 4);
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n * cols;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t p = e / cols, c = e - p * cols;
+    const int64_t r = (int64_t)(x[p] >> 32);
+    if (r >= R || (p > 0 && (int64_t)(x[p - 1] >> 32) == r)) continue;
+    f32x4 sk = zero4(), sv = zero4();
+    for (int64_t u = p; u < n && (int64_t)(x[u] >> 32) == r; ++u) {
+      const int64_t j = (int64_t)(x[u] & 0xffffffffu);
+      sk += *reinterpret_cast<const f32x4*>(wk + j * cols * 4 + 4 * c);
+      sv += *reinterpret_cast<const f32x4*>(wv + j * cols * 4 + 4 * c);
+    }
+    f32x4* pk = reinterpret_cast<f32x4*>(dk + r * cols * 4 + 4 * c);
+    f32x4* pv = reinterpret_cast<f32x4*>(dv + r * cols * 4 + 4 * c);
+    *pk = *pk + sk;
+    *pv = *pv + sv;
+  }
+}
+
+}  // namespace attn
+}  // namespace kda
+
+// ------------------------------------------------------------------ host
+namespace {
+
+using kda::fail;
+namespace A = kda::attn;
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+constexpr int64_t MAX_BLOCKS = (int64_t)1 << 24;    // 64-row blocks of Tq or Tk, with segments
+
+kda_status check(const kda_attn_problem* p) {
+  if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->Tq < 0 || p->Tk < 0 || p->Tq > ((int64_t)1 << 30) || p->Tk > ((int64_t)1 << 30))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "Tq = %lld, Tk = %lld outside [0, 2^30]",
+                (long long)p->Tq, (long long)p->Tk);
+  if (p->num_seqs < 1 || p->num_seqs > (1 << 24))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = %d outside [1, 2^24]", p->num_seqs);
+  if (p->Hq < 1 || p->Hkv < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "Hq = %d, Hkv = %d: need at least one head", p->Hq, p->Hkv);
+  if (p->Hq % p->Hkv)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "Hq = %d is not a multiple of Hkv = %d", p->Hq, p->Hkv);
+  if (p->Hq > 65535) return fail(KDA_ERR_UNSUPPORTED, "Hq = %d: more than 65535 heads", p->Hq);
+  if (p->D != 256) return fail(KDA_ERR_UNSUPPORTED, "D = %d: this build serves 256", p->D);
+  if (!std::isfinite(p->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (p->Tq / 64 + p->num_seqs > MAX_BLOCKS || p->Tk / 64 + p->num_seqs > MAX_BLOCKS)
+    return fail(KDA_ERR_UNSUPPORTED, "more than 2^24 row blocks");
+  return KDA_OK;
+}
+
+#define REQ(ptr, name)                                                                  \
+  do {                                                                                  \
+    if (!(ptr)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", name);              \
+    if (!al16(ptr)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct Layout {
+  A::Dims d;
+  size_t q_tab, k_tab, delta, fwd_end, bwd_end;
+  size_t win_k, win_v, keys0, keys1, map_end;
+};
+
+Layout layout_of(const kda_attn_problem* p) {
+  Layout L;
+  L.d.Tq = p->Tq;
+  L.d.Tk = p->Tk;
+  L.d.S = p->num_seqs;
+  L.d.Hq = p->Hq;
+  L.d.Hkv = p->Hkv;
+  L.d.grp = p->Hq / p->Hkv;
+  L.d.NCq = (int)(p->Tq / 64 + p->num_seqs);
+  L.d.NCk = (int)(p->Tk / 64 + p->num_seqs);
+  L.d.scale = p->scale;
+  auto tab = [&](int nc) { return up256(4 * (size_t)(p->num_seqs + 1)) + 2 * up256(4 * (size_t)nc); };
+  L.q_tab = 0;
+  L.k_tab = tab(L.d.NCq);
+  L.fwd_end = L.k_tab;
+  L.delta = L.k_tab + tab(L.d.NCk);
+  L.bwd_end = L.delta + up256(4 * (size_t)p->Tq * p->Hq);
+  const size_t win = up256(4 * (size_t)p->Tk * p->Hkv * A::AD);
+  L.win_k = L.bwd_end;
+  L.win_v = L.win_k + win;
+  L.keys0 = L.win_v + win;
+  L.keys1 = L.keys0 + up256(8 * (size_t)p->Tk);
+  L.map_end = L.keys1 + up256(8 * (size_t)p->Tk);
+  return L;
+}
+
+kda::ChunkTable table_at(char* base, int S, int nc) {
+  kda::ChunkTable ct{};
+  ct.doc_c0 = reinterpret_cast<int32_t*>(base);
+  ct.tok = reinterpret_cast<int32_t*>(base + up256(4 * (size_t)(S + 1)));
+  ct.len = reinterpret_cast<int32_t*>(base + up256(4 * (size_t)(S + 1)) + up256(4 * (size_t)nc));
+  return ct;
+}
+
+kda::Dims map_dims(int64_t T, int S, int nc) {
+  kda::Dims d{};
+  d.T = T;
+  d.N = S;
+  d.NC = nc;
+  return d;
+}
+
+unsigned grid_for(int64_t items) {
+  const int64_t b = (items + 255) / 256;
+  return (unsigned)(b < 1 ? 1 : (b > 65536 ? 65536 : b));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_attn_workspace_bytes(const kda_attn_problem* p, int stage, int64_t dkv_dst_rows) {
+  if (check(p) != KDA_OK) return 0;
+  const Layout L = layout_of(p);
+  switch (stage) {
+    case 0: return L.fwd_end;
+    case 1: return L.bwd_end;
+    case 2: return (dkv_dst_rows >= 0 && dkv_dst_rows < ((int64_t)1 << 31)) ? L.map_end : 0;
+    default: return 0;
+  }
+}
+
+kda_status kda_attn_fwd(const kda_attn_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  kda_status st = check(p);
+  if (st != KDA_OK) return st;
+  if (p->Tq == 0) return KDA_OK;
+  REQ(q, "q");
+  REQ(cu_seqlens_q, "cu_seqlens_q");
+  REQ(cu_seqlens_k, "cu_seqlens_k");
+  REQ(o, "o");
+  if (lse && !al16(lse)) return fail(KDA_ERR_INVALID_ARGUMENT, "lse is not 16-byte aligned");
+  if (p->Tk > 0) {
+    REQ(k, "k");
+    REQ(v, "v");
+  }
+  REQ(workspace, "workspace");
+  const Layout L = layout_of(p);
+  if (workspace_bytes < L.fwd_end)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                L.fwd_end);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const kda::ChunkTable qt = table_at(ws + L.q_tab, p->num_seqs, L.d.NCq);
+  hipError_t e = kda::launch_chunk_map(map_dims(p->Tq, p->num_seqs, L.d.NCq), cu_seqlens_q, qt, hs);
+  if (e == hipSuccess) {
+    const auto* qb = static_cast<const kda::bf16*>(q);
+    const auto* kb = static_cast<const kda::bf16*>(k);
+    const auto* vb = static_cast<const kda::bf16*>(v);
+    auto* ob = static_cast<kda::bf16*>(o);
+    if (L.d.grp % 2 == 0)
+      hipLaunchKernelGGL(A::attn_fwd_kernel<2>, dim3(L.d.NCq, p->Hq / 2), dim3(256), 0, hs, L.d,
+                         qt, cu_seqlens_q, cu_seqlens_k, qb, kb, vb, ob, lse);
+    else
+      hipLaunchKernelGGL(A::attn_fwd_kernel<1>, dim3(L.d.NCq, p->Hq), dim3(256), 0, hs, L.d, qt,
+                         cu_seqlens_q, cu_seqlens_k, qb, kb, vb, ob, lse);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess)
+    return fail(KDA_ERR_DEVICE, "attention forward launch failed: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+kda_status kda_attn_bwd(const kda_attn_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const void* o,
+                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                        int dkv_form, const int32_t* dkv_row_map, int64_t dkv_dst_rows,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  kda_status st = check(p);
+  if (st != KDA_OK) return st;
+  if (dkv_form != KDA_ATTN_DKV_BF16 && dkv_form != KDA_ATTN_DKV_F32 &&
+      dkv_form != KDA_ATTN_DKV_F32_ADD)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dkv_form = %d is not one of 0, 1, 2", dkv_form);
+  const bool add = dkv_form == KDA_ATTN_DKV_F32_ADD;
+  if (add && (dkv_dst_rows < 0 || dkv_dst_rows >= ((int64_t)1 << 31)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dkv_dst_rows = %lld outside [0, 2^31)",
+                (long long)dkv_dst_rows);
+  if (p->Tq == 0 && p->Tk == 0) return KDA_OK;
+  REQ(cu_seqlens_q, "cu_seqlens_q");
+  REQ(cu_seqlens_k, "cu_seqlens_k");
+  if (p->Tq > 0) {
+    REQ(q, "q");
+    REQ(o, "o");
+    REQ(lse, "lse");
+    REQ(dO, "dO");
+    REQ(dq, "dq");
+  }
+  const bool keys = p->Tk > 0 && (!add || dkv_dst_rows > 0);
+  if (p->Tk > 0) {
+    REQ(k, "k");
+    REQ(v, "v");
+  }
+  if (keys) {
+    REQ(dk, "dk");
+    REQ(dv, "dv");
+    if (add) REQ(dkv_row_map, "dkv_row_map");
+  }
+  REQ(workspace, "workspace");
+  const Layout L = layout_of(p);
+  const size_t need = add ? L.map_end : L.bwd_end;
+  if (workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                need);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const kda::ChunkTable qt = table_at(ws + L.q_tab, p->num_seqs, L.d.NCq);
+  const kda::ChunkTable kt = table_at(ws + L.k_tab, p->num_seqs, L.d.NCk);
+  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  const auto* qb = static_cast<const kda::bf16*>(q);
+  const auto* kb = static_cast<const kda::bf16*>(k);
+  const auto* vb = static_cast<const kda::bf16*>(v);
+  const auto* dob = static_cast<const kda::bf16*>(dO);
+  hipError_t e = kda::launch_chunk_map(map_dims(p->Tq, p->num_seqs, L.d.NCq), cu_seqlens_q, qt, hs);
+  if (e == hipSuccess)
+    e = kda::launch_chunk_map(map_dims(p->Tk, p->num_seqs, L.d.NCk), cu_seqlens_k, kt, hs);
+  if (e == hipSuccess && p->Tq > 0) {
+    const int64_t rows = p->Tq * p->Hq;
+    hipLaunchKernelGGL(A::attn_delta_kernel, dim3(grid_for(rows * 64)), dim3(256), 0, hs, rows,
+                       static_cast<const kda::bf16*>(o), dob, delta);
+    hipLaunchKernelGGL(A::attn_dq_kernel, dim3(L.d.NCq, p->Hq), dim3(256), 0, hs, L.d, qt,
+                       cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta,
+                       static_cast<kda::bf16*>(dq));
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && keys) {
+    void* wk = add ? ws + L.win_k : dk;
+    void* wv = add ? ws + L.win_v : dv;
+    if (dkv_form == KDA_ATTN_DKV_BF16)
+      hipLaunchKernelGGL(A::attn_dkdv_kernel<false>, dim3(L.d.NCk, p->Hkv), dim3(256), 0, hs, L.d,
+                         qt, kt, cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wk, wv);
+    else
+      hipLaunchKernelGGL(A::attn_dkdv_kernel<true>, dim3(L.d.NCk, p->Hkv), dim3(256), 0, hs, L.d,
+                         qt, kt, cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wk, wv);
+    e = hipGetLastError();
+    if (e == hipSuccess && add) {
+      const int64_t n = p->Tk;
+      auto* x0 = reinterpret_cast<uint64_t*>(ws + L.keys0);
+      auto* x1 = reinterpret_cast<uint64_t*>(ws + L.keys1);
+      hipLaunchKernelGGL(A::rowmap_keys_kernel, dim3(grid_for(n)), dim3(256), 0, hs, n, dkv_row_map,
+                         dkv_dst_rows, x0);
+      hipLaunchKernelGGL(A::rowmap_tile_sort_kernel,
+                         dim3((unsigned)((n + A::SORT_TILE - 1) / A::SORT_TILE)), dim3(256), 0, hs,
+                         n, x0);
+      for (int64_t width = A::SORT_TILE; width < n; width *= 2) {
+        hipLaunchKernelGGL(A::rowmap_merge_kernel, dim3(grid_for(n)), dim3(256), 0, hs, n, width,
+                           x0, x1);
+        std::swap(x0, x1);
+      }
+      hipLaunchKernelGGL(A::rowmap_add_kernel, dim3(grid_for(n * p->Hkv * (A::AD / 4))), dim3(256),
+                         0, hs, n, dkv_dst_rows, p->Hkv, x0,
+                         reinterpret_cast<const float*>(ws + L.win_k),
+                         reinterpret_cast<const float*>(ws + L.win_v), static_cast<float*>(dk),
+                         static_cast<float*>(dv));
+      e = hipGetLastError();
+    }
+  }
+  if (e != hipSuccess)
+    return fail(KDA_ERR_DEVICE, "attention backward launch failed: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -207,3 +207,82 @@ def make_conv_inputs(w: ConvWorkload, seed: int | None = None) -> dict:
     if w.halo:
         out["halo"] = halo
     return out
+
+
+# ---------------------------------------------------------------- GQA attention
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Packed-varlen causal GQA attention, head dim 256: segment s has
+    q_lens[s] queries and k_lens[s] keys (the causal mask is aligned to the
+    bottom right of each segment)."""
+    name: str
+    q_lens: tuple
+    k_lens: tuple
+    Hq: int
+    Hkv: int
+    seed: int = 0
+    D: int = 256
+
+    @property
+    def Tq(self) -> int:
+        return int(sum(self.q_lens))
+
+    @property
+    def Tk(self) -> int:
+        return int(sum(self.k_lens))
+
+    @property
+    def cu_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
+
+    @property
+    def cu_k(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.k_lens)]).astype(np.int32)
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs the mask lets through, per head."""
+        n = 0
+        for lq, lk in zip(self.q_lens, self.k_lens):
+            i = np.arange(lq)
+            n += int(np.clip(i + (lk - lq) + 1, 0, lk).sum())
+        return n
+
+
+# The 16461-query, 24693-key layout of 8 segments with 24 query and 4 key
+# heads of the pages' training-attention table; segment lengths are a fixed
+# synthetic split (every segment has at least as many keys as queries).
+_CP1_Q = (3150, 2604, 1987, 2411, 1503, 2216, 1330, 1260)
+_CP1_EXTRA = (1024, 2048, 0, 1536, 517, 1024, 1059, 1024)
+
+ATTN_WORKLOADS = [
+    # small and ragged: a one-token segment, a segment without queries, one
+    # with fewer keys than queries (its first rows see no key), one without keys
+    AttnWorkload("attn_tiny", (70, 1, 0, 130, 5, 64), (100, 1, 5, 64, 0, 64), 4, 2, seed=20),
+    # an odd group size (3 query heads per key head) over several blocks
+    AttnWorkload("attn_grp3", (200, 65, 129), (300, 65, 200), 6, 2, seed=21),
+    AttnWorkload("attn_cp1_16461", _CP1_Q, tuple(a + b for a, b in zip(_CP1_Q, _CP1_EXTRA)),
+                 24, 4, seed=22),
+]
+ATTN_BY_NAME = {w.name: w for w in ATTN_WORKLOADS}
+
+
+def make_attn_inputs(w: AttnWorkload, seed: int | None = None) -> dict:
+    """q, k, v, dO as uint16 bf16 bits (standard normal), cu_q, cu_k (int32)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    return {"cu_q": w.cu_q, "cu_k": w.cu_k,
+            "q": f32_to_bf16(rng.standard_normal((w.Tq, w.Hq, w.D), dtype=np.float32)),
+            "k": f32_to_bf16(rng.standard_normal((w.Tk, w.Hkv, w.D), dtype=np.float32)),
+            "v": f32_to_bf16(rng.standard_normal((w.Tk, w.Hkv, w.D), dtype=np.float32)),
+            "dO": f32_to_bf16(rng.standard_normal((w.Tq, w.Hq, w.D), dtype=np.float32))}
+
+
+def make_row_map(Tk: int, dst_rows: int, seed: int) -> np.ndarray:
+    """A key-to-destination row map with repeated rows, dropped keys (-1) and
+    out-of-range rows (dropped too)."""
+    rng = np.random.default_rng(seed)
+    m = rng.integers(0, max(dst_rows, 1), Tk).astype(np.int32)
+    drop = rng.random(Tk)
+    m[drop < 0.05] = -1
+    m[(drop >= 0.05) & (drop < 0.07)] = dst_rows + 3
+    return m

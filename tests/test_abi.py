@@ -202,3 +202,78 @@ def test_noalloc_forward_rejects_calls_beyond_its_scratch():
     # with a saved set the workspace is the chunk table and, for few chains,
     # the segment summaries (at most about 112 chain matrices): below the scratch
     assert B.workspace_bytes(big, False, False) < 16 << 20 < B.NOALLOC_SCRATCH_BYTES
+
+
+# ---------------------------------------------------------------- GQA attention
+
+def _attn(**kw):
+    a = dict(Tq=1000, Tk=1500, num_seqs=3, Hq=24, Hkv=4, D=256, scale=None)
+    a.update(kw)
+    return B.attn_problem(**a)
+
+
+def _attn_bwd_status(p, form=0, ws_bytes=1 << 30, dst_rows=0, **ptrs):
+    base = dict(q=256, k=512, v=768, cu_q=1024, cu_k=1280, o=1536, lse=1792, dO=2048, dq=2304,
+                dk=2560, dv=2816, row_map=3072, ws=4096)
+    base.update(ptrs)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = B.lib().kda_attn_bwd(ctypes.byref(p), *(vp(base[n]) for n in (
+        "q", "k", "v", "cu_q", "cu_k", "o", "lse", "dO", "dq", "dk", "dv")), form,
+        vp(base["row_map"]), dst_rows, vp(base["ws"]), ws_bytes, None)
+    return rc, B.lib().kda_last_error().decode()
+
+
+def test_attn_workspace_sizes():
+    p = _attn()
+    fwd, bwd = B.attn_workspace_bytes(p, 0), B.attn_workspace_bytes(p, 1)
+    add = B.attn_workspace_bytes(p, 2, 700)
+    assert 0 < fwd < bwd < add
+    # the row-map form keeps two fp32 windows [Tk, Hkv, 256] and two key arrays
+    assert add - bwd >= 2 * 4 * 1500 * 4 * 256 + 2 * 8 * 1500
+    assert B.attn_workspace_bytes(p, 3) == 0
+    assert B.attn_workspace_bytes(_attn(Hq=6, Hkv=4), 0) == 0
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hq=6, Hkv=4), 1, "multiple"),
+    (dict(Hkv=0), 1, "at least one head"),
+    (dict(D=128), 2, "256"),
+    (dict(num_seqs=0), 1, "num_seqs"),
+    (dict(Tq=-1), 1, "Tq"),
+    (dict(scale=float("nan")), 1, "scale"),
+])
+def test_attn_invalid_problem_rejected(kw, status, msg):
+    rc, err = _attn_bwd_status(_attn(**kw))
+    assert rc == status and msg in err
+
+
+def test_attn_argument_checks():
+    p = _attn()
+    rc, err = _attn_bwd_status(p, form=3)
+    assert rc == 1 and "dkv_form" in err
+    rc, err = _attn_bwd_status(p, dq=None)
+    assert rc == 1 and "dq is NULL" in err
+    rc, err = _attn_bwd_status(p, form=2, dst_rows=10, row_map=None)
+    assert rc == 1 and "dkv_row_map" in err
+    rc, err = _attn_bwd_status(p, form=2, dst_rows=-1)
+    assert rc == 1 and "dkv_dst_rows" in err
+    rc, err = _attn_bwd_status(p, k=520)
+    assert rc == 1 and "aligned" in err
+    rc, err = _attn_bwd_status(p, ws_bytes=B.attn_workspace_bytes(p, 1) - 1)
+    assert rc == 3
+    rc, err = _attn_bwd_status(p, form=2, dst_rows=10, ws_bytes=B.attn_workspace_bytes(p, 1))
+    assert rc == 3
+    # nothing to do: no launch, no pointer needed
+    rc, _ = _attn_bwd_status(_attn(Tq=0, Tk=0), q=None, k=None, v=None, ws=None)
+    assert rc == 0
+
+
+def test_attn_fwd_binding_signature():
+    p = _attn(D=64)
+    vp = ctypes.c_void_p
+    rc = B.lib().kda_attn_fwd(ctypes.byref(p), *(vp(256 * i) for i in range(1, 9)), 1 << 20, None)
+    assert rc == 2 and "256" in B.lib().kda_last_error().decode()
+    with pytest.raises(ValueError):     # host tensors for a valid problem
+        import torch
+        t = torch.zeros(16, dtype=torch.uint8)
+        B.attn_fwd(_attn(), t, t, t, t, t, t, None, t)

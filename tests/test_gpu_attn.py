@@ -1,0 +1,187 @@
+"""GPU parity of packed-varlen causal GQA training attention, head dim 256
+(flashinfer PR #7774, description and commit notes: bottom-right causal mask
+per segment, natural-log LSE, dK / dV summed over each key head's query heads
+as BF16, FP32 window gradients, or an FP32 add through a row map with repeated
+destination rows) against the FP64 oracle on the same seeded bits.
+
+Bounds, relative L2 in float64, derived from the arithmetic: rounding a
+tensor of such values to bf16 costs about 1.7e-3 of its norm. o is one such
+rounding of an fp32 sum whose P factors were rounded to bf16 too (that error
+averages over many keys): 2.5e-3. dq, dk, dv are sums of products with one
+bf16-rounded factor (dS, or P for dv) whose terms have mixed signs, so that
+rounding adds about another 1.7e-3 in quadrature (2.4e-3), with Delta taken
+from the bf16 o below that: 4e-3. lse within 1e-4 absolute (fp32 sums of fp32
+exponentials). Rows that see no key must give o = 0, lse = -inf and dq = 0
+exactly. Two runs must agree bit for bit in every output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import bf16_tensor, f64, rel_l2
+from kda_chunked_amd import inputs as I
+from kda_chunked_amd.binding import (ATTN_DKV_BF16, ATTN_DKV_F32, ATTN_DKV_F32_ADD,
+                                     GQAAttention)
+from oracle import attn_oracle as ao
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"o": 2.5e-3, "dq": 4e-3, "dk": 4e-3, "dv": 4e-3}
+LSE_ABS = 1e-4
+
+
+def _dev(inp):
+    out = {k: bf16_tensor(inp[k]) for k in ("q", "k", "v", "dO")}
+    out["cu_q"] = torch.from_numpy(inp["cu_q"].astype(np.int32)).cuda()
+    out["cu_k"] = torch.from_numpy(inp["cu_k"].astype(np.int32)).cuda()
+    return out
+
+
+def _op(w, dst_rows=None):
+    return GQAAttention(w.Tq, w.Tk, len(w.q_lens), w.Hq, w.Hkv, dst_rows=dst_rows)
+
+
+def _run(w, d, form=ATTN_DKV_BF16, op=None):
+    op = op or _op(w)
+    o, lse = op.forward(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"])
+    dq, dk, dv = op.backward(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], o, lse, d["dO"], form)
+    torch.cuda.synchronize()
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+
+
+def _f64(inp, key, heads=None):
+    a = I.bf16_to_f32(inp[key]).astype(np.float64)
+    return np.ascontiguousarray(a[:, heads]) if heads is not None else a
+
+
+def _oracle(inp, qheads=None, kheads=None):
+    cu_q, cu_k = inp["cu_q"].astype(np.int64), inp["cu_k"].astype(np.int64)
+    q, k, v, dO = (_f64(inp, "q", qheads), _f64(inp, "k", kheads), _f64(inp, "v", kheads),
+                   _f64(inp, "dO", qheads))
+    o, lse = ao.attn_fwd(cu_q, cu_k, q, k, v)
+    g = ao.attn_bwd(cu_q, cu_k, q, k, v, dO)
+    return dict(o=o, lse=lse, **g)
+
+
+def _check_lse(lse, ref):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.all(lse[~fin] == -np.inf)
+    err = float(np.max(np.abs(lse[fin] - ref[fin]))) if fin.any() else 0.0
+    assert err <= LSE_ABS, err
+    return err
+
+
+def _keyless(ref_lse):
+    return ~np.isfinite(ref_lse)
+
+
+@pytest.mark.parametrize("name", ["attn_tiny", "attn_grp3"])
+@pytest.mark.parametrize("form", [ATTN_DKV_BF16, ATTN_DKV_F32], ids=["bf16", "f32"])
+def test_small_full_parity(name, form):
+    w = I.ATTN_BY_NAME[name]
+    print(f"[case] attn {name} form={form} q={w.q_lens} k={w.k_lens}", flush=True)
+    inp = I.make_attn_inputs(w)
+    d = _dev(inp)
+    got = _run(w, d, form)
+    ref = _oracle(inp)
+    errs = {k: rel_l2(f64(got[k]), ref[k]) for k in ("o", "dq", "dk", "dv")}
+    errs["lse"] = _check_lse(f64(got["lse"]), ref["lse"])
+    print("[parity] attn " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    assert all(errs[k] <= TOL[k] for k in ("o", "dq", "dk", "dv")), errs
+    kl = _keyless(ref["lse"])
+    if kl.any():
+        assert np.all(f64(got["o"])[kl] == 0) and np.all(f64(got["dq"])[kl] == 0)
+    # reproducible bit for bit
+    again = _run(w, d, form)
+    for k in got:
+        assert torch.equal(got[k].view(torch.uint8), again[k].view(torch.uint8)), k
+
+
+def test_row_map_add_form():
+    """dk, dv added in fp32 into destinations through a row map with repeated
+    rows, dropped keys (-1) and out-of-range rows; rows no key names stay."""
+    w = I.ATTN_BY_NAME["attn_grp3"]
+    dst_rows = w.Tk // 2 + 7
+    inp = I.make_attn_inputs(w)
+    d = _dev(inp)
+    rmap = I.make_row_map(w.Tk, dst_rows, seed=5)
+    rng = np.random.default_rng(6)
+    init_k = rng.standard_normal((dst_rows, w.Hkv, 256)).astype(np.float32)
+    init_v = rng.standard_normal((dst_rows, w.Hkv, 256)).astype(np.float32)
+    op = _op(w, dst_rows=dst_rows)
+    o, lse = op.forward(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"])
+    outs = []
+    for _ in range(2):
+        dk = torch.from_numpy(init_k).cuda()
+        dv = torch.from_numpy(init_v).cuda()
+        op.backward(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], o, lse, d["dO"],
+                    ATTN_DKV_F32_ADD, dk=dk, dv=dv, row_map=torch.from_numpy(rmap).cuda(),
+                    dst_rows=dst_rows)
+        torch.cuda.synchronize()
+        outs.append((dk.cpu().numpy(), dv.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    ref = _oracle(inp)
+    valid = (rmap >= 0) & (rmap < dst_rows)
+    for n, init, got in (("dk", init_k, outs[0][0]), ("dv", init_v, outs[0][1])):
+        add = np.zeros((dst_rows, w.Hkv, 256))
+        np.add.at(add, rmap[valid], ref[n][valid])
+        named = np.zeros(dst_rows, bool)
+        named[rmap[valid]] = True
+        assert np.array_equal(got[~named], init[~named]), n
+        err = rel_l2(got[named].astype(np.float64) - init[named], add[named])
+        print(f"[parity] attn row map {n}={err:.3e}", flush=True)
+        assert err <= TOL[n], (n, err)
+
+
+def test_empty_sides():
+    """No keys at all: o = 0, lse = -inf, dq = 0. No queries: dk = dv = 0."""
+    d = {}
+    wq = I.AttnWorkload("attn_nokeys", (40, 3), (0, 0), 2, 1, seed=30)
+    inp = I.make_attn_inputs(wq)
+    d = _dev(inp)
+    got = _run(wq, d, ATTN_DKV_F32)
+    assert torch.all(got["o"] == 0) and torch.all(got["dq"] == 0)
+    assert torch.all(torch.isneginf(got["lse"]))
+    wk = I.AttnWorkload("attn_noqueries", (0, 0), (33, 70), 2, 2, seed=31)
+    inp = I.make_attn_inputs(wk)
+    d = _dev(inp)
+    op = _op(wk)
+    dk = torch.full((wk.Tk, 2, 256), 7.0, device="cuda")
+    dv = torch.full((wk.Tk, 2, 256), 7.0, device="cuda")
+    e = torch.empty(0, 2, 256, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(0, 2, device="cuda")
+    op.backward(e, d["k"], d["v"], d["cu_q"], d["cu_k"], e, lse, e, ATTN_DKV_F32, dk=dk, dv=dv,
+                dq=e)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_full_size_sampled_heads():
+    """The 16461-query, 24693-key, 8-segment layout with 24 / 4 heads, in the
+    launch configuration the benchmark times: o, lse and dq of query heads 0
+    and 23, dk and dv of key head 1 (its 6 query heads) against the oracle;
+    every output reproducible bit for bit."""
+    w = I.ATTN_BY_NAME["attn_cp1_16461"]
+    print(f"[case] attn {w.name} Tq={w.Tq} Tk={w.Tk}", flush=True)
+    inp = I.make_attn_inputs(w)
+    d = _dev(inp)
+    op = _op(w)
+    got = _run(w, d, ATTN_DKV_BF16, op)
+    again = _run(w, d, ATTN_DKV_BF16, op)
+    for k in got:
+        assert torch.equal(got[k].view(torch.uint8), again[k].view(torch.uint8)), k
+    errs = {}
+    for h in (0, 23):
+        g = h // (w.Hq // w.Hkv)
+        ref = _oracle(inp, qheads=[h], kheads=[g])
+        errs[f"o{h}"] = rel_l2(f64(got["o"][:, h]), ref["o"][:, 0])
+        errs[f"dq{h}"] = rel_l2(f64(got["dq"][:, h]), ref["dq"][:, 0])
+        errs[f"lse{h}"] = _check_lse(f64(got["lse"][:, h]), ref["lse"][:, 0])
+    ref = _oracle(inp, qheads=list(range(6, 12)), kheads=[1])
+    errs["dk1"] = rel_l2(f64(got["dk"][:, 1]), ref["dk"][:, 0])
+    errs["dv1"] = rel_l2(f64(got["dv"][:, 1]), ref["dv"][:, 0])
+    print("[parity] attn full " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+    assert all(v <= TOL[k.rstrip("0123456789")] for k, v in errs.items()
+               if not k.startswith("lse")), errs
