@@ -21,7 +21,8 @@ deterministic package's protocol: fwd alone, bwd alone and the replay pair
 (forward without saving, backward recomputing the forward), each the median
 of 15 samples of 20 back-to-back calls; the same units for the package's
 other timing rows that this repository reproduces (4doc saved and replay, R2,
-m2); and the conv1d + SiLU op that precedes the state passing, as extra keys.
+m2); the conv1d + SiLU op that precedes the state passing; and the packed-varlen
+causal GQA attention of the same family (2 x forward + backward), as extra keys.
 
 HBM traffic and MFMA utilisation come from rocprofv3 counter runs whose
 summaries sit in profiles/; they are reported only while the kernel sources
@@ -209,7 +210,10 @@ def fingerprint() -> str:
 
 
 def _short(kernel_name: str) -> str:
-    for k in ("chunk_map", "fwd_prep", "fwd_scan", "fwd_out", "bwd_scan", "bwd_intra", "finalize"):
+    for k in ("chunk_map", "seg_map", "fwd_prep", "fwd_scan", "fwd_out", "bwd_scan", "bwd_intra",
+              "finalize", "zero_params", "walk", "conv_fwd", "conv_bwd", "conv_reduce", "conv_zero",
+              "attn_fwd", "attn_delta", "attn_dq", "attn_dkdv", "rowmap_keys", "rowmap_tile_sort",
+              "rowmap_merge", "rowmap_add"):
         if k + "_kernel" in kernel_name:
             return k
     return "copy" if "copyBuffer" in kernel_name else kernel_name[:40]
@@ -433,6 +437,56 @@ def time_conv(torch) -> dict:
     return res
 
 
+PAGE_ATTN_STEP_MS = 4.527      # flashinfer PR #7774, GB200 table: zz_cp1_r0_16461 (Cake)
+
+
+def time_attn(torch) -> dict:
+    """Packed-varlen causal GQA attention (head dim 256) on the 16461-query,
+    24693-key, 8-segment layout with 24 query and 4 key heads: forward,
+    backward (bf16 dk, dv) and the pages' training step of one layer under
+    activation checkpointing (2 x forward + backward), median of HIP-event
+    timings, against the bf16 MFMA peak on the algorithmic FLOP (4 D per
+    visible (query, key) pair and query head forward, 10 D backward)."""
+    import numpy as np
+    from kda_chunked_amd import inputs as I
+    from kda_chunked_amd.binding import ATTN_DKV_BF16, GQAAttention
+    w = I.ATTN_BY_NAME["attn_cp1_16461"]
+    inp = I.make_attn_inputs(w)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, dO = bf(inp["q"]), bf(inp["k"]), bf(inp["v"]), bf(inp["dO"])
+    cq, ck = torch.from_numpy(inp["cu_q"]).cuda(), torch.from_numpy(inp["cu_k"]).cuda()
+    op = GQAAttention(w.Tq, w.Tk, len(w.q_lens), w.Hq, w.Hkv)
+    o, lse = op.forward(q, k, v, cq, ck)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fwd = lambda: op.forward(q, k, v, cq, ck, o=o, lse=lse)
+    bwd = lambda: op.backward(q, k, v, cq, ck, o, lse, dO, ATTN_DKV_BF16, dk=dk, dv=dv, dq=dq)
+
+    def step():
+        fwd()
+        fwd()
+        bwd()
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    f_ms = time_unit(torch, fwd, samples=7, calls=5)
+    b_ms = time_unit(torch, bwd, samples=7, calls=3)
+    s_ms = time_unit(torch, step, samples=5, calls=2)
+    pairs = float(w.visible_pairs()) * w.Hq
+    ff, bf_ = 4.0 * w.D * pairs, 10.0 * w.D * pairs
+    rate = lambda fl, ms: round(fl / (ms * 1e-3) / 1e12, 1)
+    res = {"workload": (f"attn_cp1_16461: Tq {w.Tq}, Tk {w.Tk}, {len(w.q_lens)} segments, "
+                        f"Hq {w.Hq}, Hkv {w.Hkv}, D {w.D}, bottom-right causal"),
+           "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4), "step_ms": round(s_ms, 4),
+           "page_gb200_step_ms": PAGE_ATTN_STEP_MS,
+           "fwd": {"bound": "mfma", "achieved": rate(ff, f_ms), "peak": PEAK_BF16_TFLOPS,
+                   "unit": "TFLOP/s", "frac": round(ff / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+           "bwd": {"bound": "mfma", "achieved": rate(bf_, b_ms), "peak": PEAK_BF16_TFLOPS,
+                   "unit": "TFLOP/s",
+                   "frac": round(bf_ / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+    print(f"[bench] attn: {res}", file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -551,13 +605,14 @@ def main():
             fig["mfma_flop"] / sec / 1e12, 2) if "mfma_flop" in fig else None
 
     rows = {}
-    conv = None
+    conv = attn = None
     if not args.no_rows:
         for name, replay in SECONDARY_ROWS:
             if name == w.name:
                 continue
             rows.update(time_row(I.BY_NAME[name], replay, torch))
         conv = time_conv(torch)
+        attn = time_attn(torch)
 
     line = {
         "metric": METRIC,
@@ -592,6 +647,8 @@ def main():
         line["rows"] = rows
     if conv:
         line["conv1d_silu"] = conv
+    if attn:
+        line["gqa_attention"] = attn
     if not args.no_cpu:
         from oracle import kda_oracle as ko
         line["cpu_baseline"] = cpu_baseline(w, inp, ko.default_threads())

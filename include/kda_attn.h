@@ -40,7 +40,7 @@ typedef struct {
   int32_t num_seqs;   /* segments, >= 1 */
   int32_t Hq, Hkv;    /* query and key heads; Hq a multiple of Hkv */
   int32_t D;          /* head dimension; this build serves 256 */
-  float scale;        /* softmax scale, usually 1/sqrt(D) */
+  float scale;        /* softmax scale, finite and > 0; usually 1/sqrt(D) */
 } kda_attn_problem;
 
 /* Forms of the key and value gradients written by kda_attn_bwd. */

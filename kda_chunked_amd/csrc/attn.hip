@@ -35,14 +35,13 @@ namespace attn {
 constexpr int AD = 256;           // head dimension
 constexpr int BR = 64;            // rows of a query or key block
 constexpr int A_LD = AD + 8;      // 528-byte rows of a staged block
-constexpr int P_LD = BR + 8;      // 144-byte rows of a wave's P / dS block
 constexpr float LOG2E_F = 1.4426950408889634f;
 constexpr float LN2_F = 0.6931471805599453f;
 
 struct Dims {
   int64_t Tq, Tk;
   int S, Hq, Hkv, grp;
-  int NCq, NCk;                   // 64-row blocks, upper bounds
+  int NCq, NCk;                   // 64-query and 128-key blocks, upper bounds
   float scale;
 };
 
@@ -74,74 +73,97 @@ KDA_DEV float row_max16(float v) {
   return fmaxf(v, row_xor<15>(v));
 }
 
-// 64 rows of one head of a [T, H, 256] bf16 tensor into an LDS block; rows
-// from n on repeat row n - 1 (their results are masked).
-KDA_DEV void stage_rows(bf16 (*dst)[A_LD], const bf16* src, int64_t row0, int n, int H, int h) {
-  for (int u = threadIdx.x; u < BR * AD / 8; u += 256) {
-    const int r = u >> 5, c8 = (u & 31) * 8;
-    const int rr = r < n ? r : n - 1;
-    *reinterpret_cast<bf16x8*>(&dst[r][c8]) =
-        *reinterpret_cast<const bf16x8*>(src + ((row0 + rr) * H + h) * AD + c8);
+// ------------------------------------------------------------------ helpers
+// 64 rows of one head of a [T, H, 256] bf16 tensor into a padded LDS block
+// (rows of A_LD = 264 elements: 33 chunks of 16 bytes, the last one padding)
+// by direct global-to-LDS loads, which use no registers. Wave instruction
+// `ins` fills the 64 chunks (1 KiB) from chunk 64 ins on, lane L the one at
+// 64 ins + L; a padding chunk gets a copy of its row's last chunk. NW waves
+// share the 33 instructions. Rows from n on repeat row n - 1. The caller
+// waits for the loads (vmcnt) and then for the other waves.
+template <int NW>
+KDA_DEV void dma_rows(bf16 (*blk)[A_LD], const bf16* src, int64_t row0, int n, int H, int h) {
+  typedef __attribute__((address_space(1))) const void* gptr;
+  typedef __attribute__((address_space(3))) void* lptr;
+  constexpr int CPR = A_LD / 8, INS = BR * CPR / 64;    // 33 chunks per row, 33 instructions
+  static_assert(BR * CPR % 64 == 0, "whole wave instructions");
+  const int w = wave_id(), l = lane_id();
+  bf16* base = &blk[0][0];
+#pragma unroll
+  for (int j = 0; j < (INS + NW - 1) / NW; ++j) {
+    const int ins = w + NW * j;
+    if (ins < INS) {
+      const int qc = 64 * ins + l, r = qc / CPR, c = qc - r * CPR;
+      const int cc = c < AD / 8 ? c : AD / 8 - 1, rr = r < n ? r : n - 1;
+      __builtin_amdgcn_global_load_lds((gptr)(src + ((row0 + rr) * H + h) * AD + 8 * cc),
+                                       (lptr)(base + 512 * ins), 16, 0, 0);
+    }
   }
 }
 
-// A wave's 16 x 256 fp32 tiles (D layout, 16 column tiles) to rows of a
-// [T, H, 256] bf16 tensor through the wave's 16 rows of an LDS block.
-KDA_DEV void write_rows_bf16(bf16 (*stage)[A_LD], const f32x4 (&acc)[16], float mul, bf16* dst,
-                             int64_t row0, int nvalid, int H, int h) {
-  const int w = wave_id(), l = lane_id();
+// Wait for this wave's direct loads, then for every wave.
+KDA_DEV void dma_join() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// A wave's 16 x 256 fp32 tiles (D layout) to bf16 rows of a [T, H, 256]
+// tensor through rows 16 wr .. + 15 of an LDS block.
+KDA_DEV void write_rows_bf16(bf16 (*stage)[A_LD], int wr, const f32x4 (&acc)[16], float mul,
+                             bf16* dst, int64_t row0, int nvalid, int H, int h) {
+  const int l = lane_id();
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) stage[16 * w + drow(i)][16 * dt + dcol()] = f2bf(acc[dt][i] * mul);
+    for (int i = 0; i < 4; ++i) stage[16 * wr + drow(i)][16 * dt + dcol()] = f2bf(acc[dt][i] * mul);
   __builtin_amdgcn_s_waitcnt(0xc07f);     // this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
   for (int u = l; u < 16 * AD / 8; u += 64) {
-    const int r = u >> 5, c8 = (u & 31) * 8, row = 16 * w + r;
+    const int r = u >> 5, c8 = (u & 31) * 8, row = 16 * wr + r;
     if (row < nvalid)
       *reinterpret_cast<bf16x8*>(dst + ((row0 + row) * H + h) * AD + c8) =
           *reinterpret_cast<const bf16x8*>(&stage[row][c8]);
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);     // reads done before the rows are staged again
-  __builtin_amdgcn_wave_barrier();
 }
 
-// The same through fp32 LDS rows (all waves together; the caller brackets the
-// call with barriers).
-KDA_DEV void write_rows_f32(float (*stage)[AD + 4], const f32x4 (&acc)[16], float mul, float* dst,
-                            int64_t row0, int nvalid, int H, int h) {
-  const int w = wave_id();
+// ------------------------------------------------------------------ P panels
+// A wave's P (or dS) block goes through LDS transposed, as [64][16]: the
+// four D-layout values a lane holds for one column (rows 4 (l / 16) .. + 3)
+// are one 8-byte store, and the MFMA A operand comes back through the
+// transpose loads. Rows of the panel are the block's 64 columns.
+constexpr int PT_LD = 16;
+
+KDA_DEV void put_pt(bf16* pt, int nt, const f32x4& x) {
+  bf16x4 v;
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) stage[16 * w + drow(i)][16 * dt + dcol()] = acc[dt][i] * mul;
-  __syncthreads();
-  for (int e = threadIdx.x; e < BR * AD / 4; e += 256) {
-    const int r = e >> 6, c4 = (e & 63) * 4;
-    if (r < nvalid)
-      *reinterpret_cast<f32x4*>(dst + ((row0 + r) * H + h) * AD + c4) =
-          *reinterpret_cast<const f32x4*>(&stage[r][c4]);
-  }
+  for (int i = 0; i < 4; ++i) v[i] = f2bf(x[i]);
+  *reinterpret_cast<bf16x4*>(pt + (16 * nt + dcol()) * PT_LD + 4 * (lane_id() >> 4)) = v;
 }
+
+// Slack of the running maximum, in log2 units: the stored maximum moves only
+// when a row's new maximum exceeds it by more than this, so P stays below
+// 2^8 and the O rescale is skipped whenever no row of the wave moved.
+constexpr float M_SLACK = 8.f;
 
 // ------------------------------------------------------------------ forward
+// Workgroup: one 64-row query block of HPW query heads of one group, 4 waves
+// per head (wave w: head h0 + w / 4, rows 16 (w % 4) .. + 15). The heads
+// share every staged K / V block.
 template <int HPW>
 struct FwdSmem {
   bf16 k[BR][A_LD];
   bf16 v[BR][A_LD];
-  bf16 p[4][HPW][16][P_LD];
+  bf16 pt[4 * HPW][BR * PT_LD];
 };
 
 template <int HPW>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(Dims a, ChunkTable qt,
-                                                      const int32_t* __restrict__ cuq,
-                                                      const int32_t* __restrict__ cuk,
-                                                      const bf16* __restrict__ q,
-                                                      const bf16* __restrict__ k,
-                                                      const bf16* __restrict__ v,
-                                                      bf16* __restrict__ o, float* __restrict__ lse) {
+__global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attn_fwd_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
+                const int32_t* __restrict__ cuk, const bf16* __restrict__ q,
+                const bf16* __restrict__ k, const bf16* __restrict__ v, bf16* __restrict__ o,
+                float* __restrict__ lse) {
   __shared__ FwdSmem<HPW> sm;
-  const int ci = blockIdx.x, h0 = blockIdx.y * HPW;
+  const int ci = blockIdx.x;
   if (ci >= qt.doc_c0[a.S]) return;
   const int s = seg_of(qt.doc_c0, a.S, ci);
   int64_t qs, Lq, ks, Lk;
@@ -150,117 +172,98 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Dims a, ChunkTable qt,
   const int64_t t0 = qt.tok[ci];
   const int nq = qt.len[ci];
   const int64_t i0 = t0 - qs, off = Lk - Lq;
-  const int g = h0 / a.grp, w = wave_id(), l = lane_id();
+  const int w = wave_id(), wr = w & 3, l = lane_id();
+  const int h = blockIdx.y * HPW + (w >> 2), g = h / a.grp;
   const float c2 = a.scale * LOG2E_F;
 
-  bf16x8 qf[HPW][8];
+  bf16x8 qf[8];
   {
-    const int r = 16 * w + (l & 15), rr = r < nq ? r : nq - 1;
+    const int r = 16 * wr + (l & 15), rr = r < nq ? r : nq - 1;
+    const bf16* src = q + ((t0 + rr) * a.Hq + h) * AD + 8 * (l >> 4);
 #pragma unroll
-    for (int hp = 0; hp < HPW; ++hp) {
-      const bf16* src = q + ((t0 + rr) * a.Hq + h0 + hp) * AD + 8 * (l >> 4);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qf[hp][kk] = *reinterpret_cast<const bf16x8*>(src + 32 * kk);
-    }
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(src + 32 * kk);
   }
-  float m[HPW][4], ls[HPW][4];
-  f32x4 O[HPW][16];
+  // m: stored row maximum (scaled, log2 units); ls: this lane's partial row
+  // sum over its columns, reduced across the row once at the end
+  float m[4], ls[4];
+  f32x4 O[16];
 #pragma unroll
-  for (int hp = 0; hp < HPW; ++hp) {
+  for (int i = 0; i < 4; ++i) m[i] = -INFINITY, ls[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m[hp][i] = -INFINITY, ls[hp][i] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt) O[hp][dt] = zero4();
-  }
+  for (int dt = 0; dt < 16; ++dt) O[dt] = zero4();
   int64_t kend = i0 + nq + off;             // keys [0, kend) can be seen by the block
   kend = kend < 0 ? 0 : (kend > Lk ? Lk : kend);
   for (int64_t kb0 = 0; kb0 < kend; kb0 += BR) {
     const int nk = (int)(kend - kb0 < BR ? kend - kb0 : BR);
-    __syncthreads();
-    stage_rows(sm.k, k, ks + kb0, nk, a.Hkv, g);
-    stage_rows(sm.v, v, ks + kb0, nk, a.Hkv, g);
-    __syncthreads();
-    f32x4 S[HPW][4];
+    __syncthreads();                        // every wave is done with the previous block
+    dma_rows<4 * HPW>(sm.k, k, ks + kb0, nk, a.Hkv, g);
+    dma_rows<4 * HPW>(sm.v, v, ks + kb0, nk, a.Hkv, g);
+    dma_join();
+    f32x4 S[4];
 #pragma unroll
-    for (int hp = 0; hp < HPW; ++hp)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) S[hp][nt] = zero4();
+    for (int nt = 0; nt < 4; ++nt) S[nt] = zero4();
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const bf16x8 kb = frag(&sm.k[0][0], A_LD, 16 * nt, 32 * kk);
-#pragma unroll
-        for (int hp = 0; hp < HPW; ++hp) S[hp][nt] = mfma16(qf[hp][kk], kb, S[hp][nt]);
-      }
-    // base-2 logits, masked; the running max and sum per row
-#pragma unroll
-    for (int hp = 0; hp < HPW; ++hp)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i);
-        const int64_t qi = i0 + r;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int jl = 16 * nt + dcol();
-          const bool vis = r < nq && jl < nk && kb0 + jl <= qi + off;
-          S[hp][nt][i] = vis ? S[hp][nt][i] * c2 : -INFINITY;
-          mx = fmaxf(mx, S[hp][nt][i]);
-        }
-        mx = row_max16(mx);
-        const float mn = fmaxf(m[hp][i], mx);
-        const float corr = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[hp][i] - mn);
-        float sum = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float pv = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S[hp][nt][i] - mn);
-          S[hp][nt][i] = pv;
-          sum += pv;
-        }
-        sum = row_sum16(sum);
-        ls[hp][i] = ls[hp][i] * corr + sum;
-        m[hp][i] = mn;
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt) O[hp][dt][i] *= corr;
-      }
-#pragma unroll
-    for (int hp = 0; hp < HPW; ++hp)
+      for (int nt = 0; nt < 4; ++nt)
+        S[nt] = mfma16(qf[kk], frag(&sm.k[0][0], A_LD, 16 * nt, 32 * kk), S[nt]);
+    // every row of the block sees every key of this key block
+    const bool full = nk == BR && nq == BR && kb0 + BR - 1 <= i0 + off;
+    if (!full) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.p[w][hp][drow(i)][16 * nt + dcol()] = f2bf(S[hp][nt][i]);
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * wr + drow(i), jl = 16 * nt + dcol();
+          if (!(r < nq && jl < nk && kb0 + jl <= i0 + r + off)) S[nt][i] = -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = fmaxf(fmaxf(S[0][i], S[1][i]), fmaxf(S[2][i], S[3][i]));
+      mx = row_max16(mx) * c2;
+      const bool up = mx > m[i] + M_SLACK;
+      // O rows move only when one of the four rows i of the wave moved
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float corr = up ? __builtin_amdgcn_exp2f(m[i] - mx) : 1.f;
+        ls[i] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) O[dt][i] *= corr;
+      }
+      m[i] = up ? mx : m[i];
+      const float sub = m[i] == -INFINITY ? 0.f : m[i];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[nt][i], c2, -sub));
+        S[nt][i] = p;
+        ls[i] += p;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) put_pt(sm.pt[w], nt, S[nt]);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 pa[HPW];
+      const bf16x8 pa = fragT(sm.pt[w], PT_LD, 0, 32 * kk);
 #pragma unroll
-      for (int hp = 0; hp < HPW; ++hp) pa[hp] = frag(&sm.p[w][hp][0][0], P_LD, 0, 32 * kk);
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) {
-        const bf16x8 vb = fragT(&sm.v[0][0], A_LD, 16 * dt, 32 * kk);
-#pragma unroll
-        for (int hp = 0; hp < HPW; ++hp) O[hp][dt] = mfma16(pa[hp], vb, O[hp][dt]);
-      }
+      for (int dt = 0; dt < 16; ++dt)
+        O[dt] = mfma16(pa, fragT(&sm.v[0][0], A_LD, 16 * dt, 32 * kk), O[dt]);
     }
   }
-  __syncthreads();                          // the K block is free: O leaves through it
+  __syncthreads();                          // K and V are free: O leaves through them
 #pragma unroll
-  for (int hp = 0; hp < HPW; ++hp) {
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wr + drow(i);
+    const float tot = row_sum16(ls[i]);
+    const bool seen = tot > 0.f;
+    const float inv = seen ? 1.f / tot : 0.f;
+    if (lse && dcol() == 0 && r < nq)
+      lse[(t0 + r) * a.Hq + h] = seen ? (m[i] + __builtin_amdgcn_logf(tot)) * LN2_F : -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + drow(i);
-      const bool seen = ls[hp][i] > 0.f;
-      const float inv = seen ? 1.f / ls[hp][i] : 0.f;
-      if (lse && dcol() == 0 && r < nq)
-        lse[(t0 + r) * a.Hq + h0 + hp] =
-            seen ? (m[hp][i] + __builtin_amdgcn_logf(ls[hp][i])) * LN2_F : -INFINITY;
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) O[hp][dt][i] *= inv;
-    }
-    write_rows_bf16(sm.k, O[hp], 1.f, o, t0, nq, a.Hq, h0 + hp);
+    for (int dt = 0; dt < 16; ++dt) O[dt][i] *= inv;
   }
+  write_rows_bf16((w >> 2) ? sm.v : sm.k, wr, O, 1.f, o, t0, nq, a.Hq, h);
 }
 
 // ------------------------------------------------------------------ delta
@@ -283,24 +286,23 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(int64_t n, const bf16* 
 }
 
 // ------------------------------------------------------------------ dq
+// Workgroup as in the forward: one query block of HPW heads of one group.
+template <int HPW>
 struct DqSmem {
   bf16 k[BR][A_LD];
   bf16 v[BR][A_LD];
-  bf16 p[4][16][P_LD];
+  bf16 pt[4 * HPW][BR * PT_LD];
 };
 
-__global__ __launch_bounds__(256) void attn_dq_kernel(Dims a, ChunkTable qt,
-                                                     const int32_t* __restrict__ cuq,
-                                                     const int32_t* __restrict__ cuk,
-                                                     const bf16* __restrict__ q,
-                                                     const bf16* __restrict__ k,
-                                                     const bf16* __restrict__ v,
-                                                     const bf16* __restrict__ dO,
-                                                     const float* __restrict__ lse,
-                                                     const float* __restrict__ delta,
-                                                     bf16* __restrict__ dq) {
-  __shared__ DqSmem sm;
-  const int ci = blockIdx.x, h = blockIdx.y;
+template <int HPW>
+__global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attn_dq_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
+               const int32_t* __restrict__ cuk, const bf16* __restrict__ q,
+               const bf16* __restrict__ k, const bf16* __restrict__ v,
+               const bf16* __restrict__ dO, const float* __restrict__ lse,
+               const float* __restrict__ delta, bf16* __restrict__ dq) {
+  __shared__ DqSmem<HPW> sm;
+  const int ci = blockIdx.x;
   if (ci >= qt.doc_c0[a.S]) return;
   const int s = seg_of(qt.doc_c0, a.S, ci);
   int64_t qs, Lq, ks, Lk;
@@ -309,12 +311,13 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(Dims a, ChunkTable qt,
   const int64_t t0 = qt.tok[ci];
   const int nq = qt.len[ci];
   const int64_t i0 = t0 - qs, off = Lk - Lq;
-  const int g = h / a.grp, w = wave_id(), l = lane_id();
+  const int w = wave_id(), wr = w & 3, l = lane_id();
+  const int h = blockIdx.y * HPW + (w >> 2), g = h / a.grp;
   const float c2 = a.scale * LOG2E_F;
 
   bf16x8 qf[8], df[8];
   {
-    const int r = 16 * w + (l & 15), rr = r < nq ? r : nq - 1;
+    const int r = 16 * wr + (l & 15), rr = r < nq ? r : nq - 1;
     const int64_t base = ((t0 + rr) * a.Hq + h) * AD + 8 * (l >> 4);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(Dims a, ChunkTable qt,
   float lb[4], dl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 16 * w + drow(i), rr = r < nq ? r : nq - 1;
+    const int r = 16 * wr + drow(i), rr = r < nq ? r : nq - 1;
     lb[i] = lse[(t0 + rr) * a.Hq + h] * LOG2E_F;
     dl[i] = delta[(t0 + rr) * a.Hq + h];
   }
@@ -337,9 +340,9 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(Dims a, ChunkTable qt,
   for (int64_t kb0 = 0; kb0 < kend; kb0 += BR) {
     const int nk = (int)(kend - kb0 < BR ? kend - kb0 : BR);
     __syncthreads();
-    stage_rows(sm.k, k, ks + kb0, nk, a.Hkv, g);
-    stage_rows(sm.v, v, ks + kb0, nk, a.Hkv, g);
-    __syncthreads();
+    dma_rows<4 * HPW>(sm.k, k, ks + kb0, nk, a.Hkv, g);
+    dma_rows<4 * HPW>(sm.v, v, ks + kb0, nk, a.Hkv, g);
+    dma_join();
     f32x4 S[4], dP[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) S[nt] = dP[nt] = zero4();
@@ -350,57 +353,60 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(Dims a, ChunkTable qt,
         S[nt] = mfma16(qf[kk], frag(&sm.k[0][0], A_LD, 16 * nt, 32 * kk), S[nt]);
         dP[nt] = mfma16(df[kk], frag(&sm.v[0][0], A_LD, 16 * nt, 32 * kk), dP[nt]);
       }
+    const bool full = nk == BR && nq == BR && kb0 + BR - 1 <= i0 + off;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4 ds;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + drow(i), jl = 16 * nt + dcol();
-        const bool vis = r < nq && jl < nk && kb0 + jl <= i0 + r + off;
-        const float p = vis ? __builtin_amdgcn_exp2f(S[nt][i] * c2 - lb[i]) : 0.f;
-        sm.p[w][drow(i)][jl] = f2bf(p * (dP[nt][i] - dl[i]));
+        const int r = 16 * wr + drow(i), jl = 16 * nt + dcol();
+        const bool vis = full || (r < nq && jl < nk && kb0 + jl <= i0 + r + off);
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[nt][i], c2, -lb[i])) : 0.f;
+        ds[i] = p * (dP[nt][i] - dl[i]);
       }
+      put_pt(sm.pt[w], nt, ds);
+    }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 da = frag(&sm.p[w][0][0], P_LD, 0, 32 * kk);
+      const bf16x8 da = fragT(sm.pt[w], PT_LD, 0, 32 * kk);
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt)
         dQ[dt] = mfma16(da, fragT(&sm.k[0][0], A_LD, 16 * dt, 32 * kk), dQ[dt]);
     }
   }
   __syncthreads();
-  write_rows_bf16(sm.k, dQ, a.scale, dq, t0, nq, a.Hq, h);
+  write_rows_bf16((w >> 2) ? sm.v : sm.k, wr, dQ, a.scale, dq, t0, nq, a.Hq, h);
 }
 
 // ------------------------------------------------------------------ dk, dv
+// Workgroup: one 128-key block (BK) of one key head, 8 waves of 16 keys that
+// share each staged query block. K and V never enter LDS: they are only the
+// A operands of a wave's own keys and stay in registers. dv and dk are two
+// launches of one kernel (WANT_DK false / true): holding both accumulators
+// would leave no registers for a second wave per SIMD; the dk pass recomputes
+// the S^T that the dv pass also forms.
+constexpr int BK = 128;
+
 struct KvSmem {
-  bf16 k[BR][A_LD];
-  bf16 v[BR][A_LD];
   union {
     struct {
       bf16 q[BR][A_LD];
       bf16 dO[BR][A_LD];
+      bf16 pt[8][BR * PT_LD];       // P^T (dv pass) or dS^T (dk pass), stored [query][key]
     } in;
-    float out[BR][AD + 4];        // fp32 results on their way out
+    float out[BR][AD + 4];          // fp32 results of four waves on their way out
   } u;
-  bf16 p[4][16][P_LD];            // P^T of the wave's keys
-  bf16 ds[4][16][P_LD];           // dS^T of the wave's keys
-  float lb[BR], dl[BR];           // lse log2 e and Delta of the staged queries
 };
 
 // F32: fp32 rows (window gradients, or the row-map form's staging), else bf16.
-template <bool F32>
-__global__ __launch_bounds__(256) void attn_dkdv_kernel(Dims a, ChunkTable qt, ChunkTable kt,
-                                                       const int32_t* __restrict__ cuq,
-                                                       const int32_t* __restrict__ cuk,
-                                                       const bf16* __restrict__ q,
-                                                       const bf16* __restrict__ k,
-                                                       const bf16* __restrict__ v,
-                                                       const bf16* __restrict__ dO,
-                                                       const float* __restrict__ lse,
-                                                       const float* __restrict__ delta,
-                                                       void* __restrict__ dk, void* __restrict__ dv) {
+template <bool WANT_DK, bool F32>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_dkdv_kernel(
+    Dims a, ChunkTable qt, ChunkTable kt, const int32_t* __restrict__ cuq,
+    const int32_t* __restrict__ cuk, const bf16* __restrict__ q, const bf16* __restrict__ k,
+    const bf16* __restrict__ v, const bf16* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ delta, void* __restrict__ out) {
   __shared__ KvSmem sm;
   const int cj = blockIdx.x, g = blockIdx.y;
   if (cj >= kt.doc_c0[a.S]) return;
@@ -411,7 +417,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(Dims a, ChunkTable qt, C
   const int64_t u0 = kt.tok[cj];
   const int nk = kt.len[cj];
   const int64_t j0 = u0 - ks, off = Lk - Lq;
-  const int w = wave_id();
+  const int w = wave_id(), l = lane_id();
+  const int jw = 16 * w;                // the wave's first key in the block
   const float c2 = a.scale * LOG2E_F;
   // query blocks of the segment that see some of these keys: i + off >= j0
   const int qc0 = qt.doc_c0[s], qc1 = qt.doc_c0[s + 1];
@@ -420,72 +427,102 @@ __global__ __launch_bounds__(256) void attn_dkdv_kernel(Dims a, ChunkTable qt, C
   const int64_t qf64 = qc0 + ifirst / BR;
   const int qfirst = qf64 < qc1 ? (int)qf64 : qc1;
 
-  stage_rows(sm.k, k, u0, nk, a.Hkv, g);
-  stage_rows(sm.v, v, u0, nk, a.Hkv, g);
-  f32x4 dK[16], dV[16];
+  bf16x8 kf[8], vf[WANT_DK ? 8 : 1];  // A fragments of the wave's 16 keys
+  {
+    const int r = jw + (l & 15), rr = r < nk ? r : nk - 1;
+    const int64_t base = ((u0 + rr) * a.Hkv + g) * AD + 8 * (l >> 4);
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) dK[dt] = dV[dt] = zero4();
-  for (int hh = 0; hh < a.grp; ++hh) {
-    const int h = g * a.grp + hh;
-    for (int qc = qfirst; qc < qc1; ++qc) {
-      const int64_t t0 = qt.tok[qc];
-      const int nq = qt.len[qc];
-      const int64_t i0 = t0 - qs;
-      __syncthreads();
-      stage_rows(sm.u.in.q, q, t0, nq, a.Hq, h);
-      stage_rows(sm.u.in.dO, dO, t0, nq, a.Hq, h);
-      if (threadIdx.x < BR) {
-        const int r = threadIdx.x, rr = r < nq ? r : nq - 1;
-        sm.lb[r] = lse[(t0 + rr) * a.Hq + h] * LOG2E_F;
-        sm.dl[r] = delta[(t0 + rr) * a.Hq + h];
+    for (int kk = 0; kk < 8; ++kk) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(k + base + 32 * kk);
+      if (WANT_DK) vf[kk] = *reinterpret_cast<const bf16x8*>(v + base + 32 * kk);
+    }
+  }
+  f32x4 acc[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) acc[dt] = zero4();
+  const int nqb = qc1 - qfirst, items = a.grp * nqb;
+  // the (query head, query block) items in a fixed order: heads outer
+  for (int it = 0; it < items; ++it) {
+    const int h = g * a.grp + it / nqb, qc = qfirst + it % nqb;
+    const int64_t t0 = qt.tok[qc];
+    const int nq = qt.len[qc];
+    const int64_t i0 = t0 - qs;
+    float lbq[4], dlq[4];             // lse log2 e and Delta of this lane's query columns
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int qcol = 16 * nt + dcol(), qq = qcol < nq ? qcol : nq - 1;
+      lbq[nt] = lse[(t0 + qq) * a.Hq + h] * LOG2E_F;
+      dlq[nt] = WANT_DK ? delta[(t0 + qq) * a.Hq + h] : 0.f;
+    }
+    __syncthreads();                  // every wave is done with the previous item's panels
+    dma_rows<8>(sm.u.in.q, q, t0, nq, a.Hq, h);
+    dma_rows<8>(sm.u.in.dO, dO, t0, nq, a.Hq, h);
+    dma_join();
+    // a wave whose keys no query of this block sees skips the item
+    if (jw >= nk || j0 + jw > i0 + nq - 1 + off) continue;
+    f32x4 S[4], dP[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) S[nt] = dP[nt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        S[nt] = mfma16(kf[kk], frag(&sm.u.in.q[0][0], A_LD, 16 * nt, 32 * kk), S[nt]);
+        if (WANT_DK)
+          dP[nt] = mfma16(vf[kk], frag(&sm.u.in.dO[0][0], A_LD, 16 * nt, 32 * kk), dP[nt]);
       }
-      __syncthreads();
-      f32x4 S[4], dP[4];
+    // S^T[key][query]: keys are rows jw + drow(i), queries columns 16 nt + dcol()
+    const bool full = jw + 16 <= nk && nq == BR && j0 + jw + 15 <= i0 + off;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) S[nt] = dP[nt] = zero4();
+    for (int nt = 0; nt < 4; ++nt) {
+      const int qcol = 16 * nt + dcol();
+      f32x4 x;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ka = frag(&sm.k[0][0], A_LD, 16 * w, 32 * kk);
-        const bf16x8 va = frag(&sm.v[0][0], A_LD, 16 * w, 32 * kk);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          S[nt] = mfma16(ka, frag(&sm.u.in.q[0][0], A_LD, 16 * nt, 32 * kk), S[nt]);
-          dP[nt] = mfma16(va, frag(&sm.u.in.dO[0][0], A_LD, 16 * nt, 32 * kk), dP[nt]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int jr = jw + drow(i);
+        const bool vis = full || (jr < nk && qcol < nq && j0 + jr <= i0 + qcol + off);
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[nt][i], c2, -lbq[nt])) : 0.f;
+        x[i] = WANT_DK ? p * (dP[nt][i] - dlq[nt]) : p;
       }
-      // S^T[key][query]: keys are rows 16 w + drow(i), queries columns 16 nt + dcol()
+      put_pt(sm.u.in.pt[w], nt, x);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // dv += P^T dO, or dk += dS^T Q
+    const bf16* bpan = WANT_DK ? &sm.u.in.q[0][0] : &sm.u.in.dO[0][0];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 pa = fragT(sm.u.in.pt[w], PT_LD, 0, 32 * kk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int jr = 16 * w + drow(i), qcol = 16 * nt + dcol();
-          const bool vis = jr < nk && qcol < nq && j0 + jr <= i0 + qcol + off;
-          const float p = vis ? __builtin_amdgcn_exp2f(S[nt][i] * c2 - sm.lb[qcol]) : 0.f;
-          sm.p[w][drow(i)][qcol] = f2bf(p);
-          sm.ds[w][drow(i)][qcol] = f2bf(p * (dP[nt][i] - sm.dl[qcol]));
-        }
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 pa = frag(&sm.p[w][0][0], P_LD, 0, 32 * kk);
-        const bf16x8 da = frag(&sm.ds[w][0][0], P_LD, 0, 32 * kk);
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt) {
-          dV[dt] = mfma16(pa, fragT(&sm.u.in.dO[0][0], A_LD, 16 * dt, 32 * kk), dV[dt]);
-          dK[dt] = mfma16(da, fragT(&sm.u.in.q[0][0], A_LD, 16 * dt, 32 * kk), dK[dt]);
-        }
-      }
+      for (int dt = 0; dt < 16; ++dt) acc[dt] = mfma16(pa, fragT(bpan, A_LD, 16 * dt, 32 * kk), acc[dt]);
     }
   }
   __syncthreads();
+  const float mul = WANT_DK ? a.scale : 1.f;
   if (!F32) {
-    write_rows_bf16(sm.u.in.q, dK, a.scale, reinterpret_cast<bf16*>(dk), u0, nk, a.Hkv, g);
-    write_rows_bf16(sm.u.in.dO, dV, 1.f, reinterpret_cast<bf16*>(dv), u0, nk, a.Hkv, g);
+    // waves 0-3 through the q block, 4-7 through the dO block
+    write_rows_bf16(w < 4 ? sm.u.in.q : sm.u.in.dO, w & 3, acc, mul, reinterpret_cast<bf16*>(out),
+                    u0 + 64 * (w >> 2), nk - 64 * (w >> 2), a.Hkv, g);
   } else {
-    write_rows_f32(sm.u.out, dK, a.scale, reinterpret_cast<float*>(dk), u0, nk, a.Hkv, g);
-    __syncthreads();
-    write_rows_f32(sm.u.out, dV, 1.f, reinterpret_cast<float*>(dv), u0, nk, a.Hkv, g);
+    // the two halves of the block in turn through the fp32 rows
+    for (int half = 0; half < 2; ++half) {
+      if (half) __syncthreads();
+      if ((w >> 2) == half)
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sm.u.out[16 * (w & 3) + drow(i)][16 * dt + dcol()] = acc[dt][i] * mul;
+      __syncthreads();
+      const int nv = nk - 64 * half;
+      for (int e = threadIdx.x; e < BR * AD / 4; e += 512) {
+        const int r = e >> 6, c4 = (e & 63) * 4;
+        if (r < nv)
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) +
+                                    ((u0 + 64 * half + r) * a.Hkv + g) * AD + c4) =
+              *reinterpret_cast<const f32x4*>(&sm.u.out[r][c4]);
+      }
+    }
   }
 }
 
@@ -587,7 +624,7 @@ namespace A = kda::attn;
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-constexpr int64_t MAX_BLOCKS = (int64_t)1 << 24;    // 64-row blocks of Tq or Tk, with segments
+constexpr int64_t MAX_BLOCKS = (int64_t)1 << 22;    // row blocks of a launch (x 512 threads < 2^32)
 
 kda_status check(const kda_attn_problem* p) {
   if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "problem is NULL");
@@ -602,9 +639,10 @@ kda_status check(const kda_attn_problem* p) {
     return fail(KDA_ERR_INVALID_ARGUMENT, "Hq = %d is not a multiple of Hkv = %d", p->Hq, p->Hkv);
   if (p->Hq > 65535) return fail(KDA_ERR_UNSUPPORTED, "Hq = %d: more than 65535 heads", p->Hq);
   if (p->D != 256) return fail(KDA_ERR_UNSUPPORTED, "D = %d: this build serves 256", p->D);
-  if (!std::isfinite(p->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!(std::isfinite(p->scale) && p->scale > 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite and positive");
   if (p->Tq / 64 + p->num_seqs > MAX_BLOCKS || p->Tk / 64 + p->num_seqs > MAX_BLOCKS)
-    return fail(KDA_ERR_UNSUPPORTED, "more than 2^24 row blocks");
+    return fail(KDA_ERR_UNSUPPORTED, "more than 2^22 row blocks");
   return KDA_OK;
 }
 
@@ -631,7 +669,7 @@ Layout layout_of(const kda_attn_problem* p) {
   L.d.Hkv = p->Hkv;
   L.d.grp = p->Hq / p->Hkv;
   L.d.NCq = (int)(p->Tq / 64 + p->num_seqs);
-  L.d.NCk = (int)(p->Tk / 64 + p->num_seqs);
+  L.d.NCk = (int)(p->Tk / A::BK + p->num_seqs);
   L.d.scale = p->scale;
   auto tab = [&](int nc) { return up256(4 * (size_t)(p->num_seqs + 1)) + 2 * up256(4 * (size_t)nc); };
   L.q_tab = 0;
@@ -714,7 +752,7 @@ kda_status kda_attn_fwd(const kda_attn_problem* p, const void* q, const void* k,
     const auto* vb = static_cast<const kda::bf16*>(v);
     auto* ob = static_cast<kda::bf16*>(o);
     if (L.d.grp % 2 == 0)
-      hipLaunchKernelGGL(A::attn_fwd_kernel<2>, dim3(L.d.NCq, p->Hq / 2), dim3(256), 0, hs, L.d,
+      hipLaunchKernelGGL(A::attn_fwd_kernel<2>, dim3(L.d.NCq, p->Hq / 2), dim3(512), 0, hs, L.d,
                          qt, cu_seqlens_q, cu_seqlens_k, qb, kb, vb, ob, lse);
     else
       hipLaunchKernelGGL(A::attn_fwd_kernel<1>, dim3(L.d.NCq, p->Hq), dim3(256), 0, hs, L.d, qt,
@@ -777,25 +815,36 @@ kda_status kda_attn_bwd(const kda_attn_problem* p, const void* q, const void* k,
   const auto* dob = static_cast<const kda::bf16*>(dO);
   hipError_t e = kda::launch_chunk_map(map_dims(p->Tq, p->num_seqs, L.d.NCq), cu_seqlens_q, qt, hs);
   if (e == hipSuccess)
-    e = kda::launch_chunk_map(map_dims(p->Tk, p->num_seqs, L.d.NCk), cu_seqlens_k, kt, hs);
+    e = kda::launch_chunk_map(map_dims(p->Tk, p->num_seqs, L.d.NCk), cu_seqlens_k, kt, hs, A::BK);
   if (e == hipSuccess && p->Tq > 0) {
     const int64_t rows = p->Tq * p->Hq;
     hipLaunchKernelGGL(A::attn_delta_kernel, dim3(grid_for(rows * 64)), dim3(256), 0, hs, rows,
                        static_cast<const kda::bf16*>(o), dob, delta);
-    hipLaunchKernelGGL(A::attn_dq_kernel, dim3(L.d.NCq, p->Hq), dim3(256), 0, hs, L.d, qt,
-                       cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta,
-                       static_cast<kda::bf16*>(dq));
+    if (L.d.grp % 2 == 0)
+      hipLaunchKernelGGL(A::attn_dq_kernel<2>, dim3(L.d.NCq, p->Hq / 2), dim3(512), 0, hs, L.d, qt,
+                         cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta,
+                         static_cast<kda::bf16*>(dq));
+    else
+      hipLaunchKernelGGL(A::attn_dq_kernel<1>, dim3(L.d.NCq, p->Hq), dim3(256), 0, hs, L.d, qt,
+                         cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta,
+                         static_cast<kda::bf16*>(dq));
     e = hipGetLastError();
   }
   if (e == hipSuccess && keys) {
     void* wk = add ? ws + L.win_k : dk;
     void* wv = add ? ws + L.win_v : dv;
-    if (dkv_form == KDA_ATTN_DKV_BF16)
-      hipLaunchKernelGGL(A::attn_dkdv_kernel<false>, dim3(L.d.NCk, p->Hkv), dim3(256), 0, hs, L.d,
-                         qt, kt, cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wk, wv);
-    else
-      hipLaunchKernelGGL(A::attn_dkdv_kernel<true>, dim3(L.d.NCk, p->Hkv), dim3(256), 0, hs, L.d,
-                         qt, kt, cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wk, wv);
+    const dim3 grid(L.d.NCk, p->Hkv);
+    if (dkv_form == KDA_ATTN_DKV_BF16) {
+      hipLaunchKernelGGL((A::attn_dkdv_kernel<false, false>), grid, dim3(512), 0, hs, L.d, qt, kt,
+                         cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wv);
+      hipLaunchKernelGGL((A::attn_dkdv_kernel<true, false>), grid, dim3(512), 0, hs, L.d, qt, kt,
+                         cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wk);
+    } else {
+      hipLaunchKernelGGL((A::attn_dkdv_kernel<false, true>), grid, dim3(512), 0, hs, L.d, qt, kt,
+                         cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wv);
+      hipLaunchKernelGGL((A::attn_dkdv_kernel<true, true>), grid, dim3(512), 0, hs, L.d, qt, kt,
+                         cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wk);
+    }
     e = hipGetLastError();
     if (e == hipSuccess && add) {
       const int64_t n = p->Tk;

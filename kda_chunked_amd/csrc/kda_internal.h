@@ -125,8 +125,9 @@ constexpr int ELEMS = TBL + 64 * 64;         // 65792 bf16 elements per chunk-he
 constexpr size_t BYTES = (size_t)ELEMS * 2;  // 131584, a multiple of 16
 }  // namespace fwd_panel
 
+// Blocks of `block` tokens per document (64: the chunks of the method).
 hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
-                            hipStream_t s);
+                            hipStream_t s, int block = 64);
 hipError_t launch_seg_map(const Dims& d, const ChunkTable& ct, hipStream_t s);
 hipError_t launch_walk(const Dims& d, const ChunkTable& ct, const SegWork& sg, int reverse,
                        hipStream_t s);

@@ -43,7 +43,7 @@ constexpr int kPrepWorkgroups = 256;     // MI355X compute units
 #endif
 
 __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restrict__ cu, int N,
-                                                        int64_t T, int NC, ChunkTable ct) {
+                                                        int64_t T, int NC, int cl, ChunkTable ct) {
   // documents are taken 256 at a time: a prefix sum of their chunk counts
   // gives each its first chunk, then every thread fills chunk entries c,
   // c + 256, ... of the batch, finding the document of entry c by a binary
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
       cb = cb < ca ? ca : (cb > T ? T : cb);
       a = (int)ca;
       b = (int)cb;
-      cnt = (b - a + CL - 1) / CL;
+      cnt = (b - a + cl - 1) / cl;
     }
     scan[t] = cnt;
     __syncthreads();
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
     const int c0 = carry + scan[t] - cnt;
     const int total = scan[255];
     c_end[t] = carry + scan[t];
-    d_tok[t] = a - CL * c0;       // first token of chunk c of this document: d_tok + 64 c
+    d_tok[t] = a - cl * c0;       // first token of chunk c of this document: d_tok + cl c
     d_end[t] = b;
     if (d < N) ct.doc_c0[d] = min(c0, NC);
     __syncthreads();
@@ -86,9 +86,9 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
         if (c_end[mid] > c) hi = mid;
         else lo = mid + 1;
       }
-      const int tok = d_tok[lo] + CL * c;
+      const int tok = d_tok[lo] + cl * c;
       ct.tok[c] = tok;
-      ct.len[c] = min(CL, d_end[lo] - tok);
+      ct.len[c] = min(cl, d_end[lo] - tok);
     }
     carry += total;
     __syncthreads();
@@ -97,8 +97,8 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
 }
 
 hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
-                            hipStream_t s) {
-  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, s, cu, d.N, d.T, d.NC, ct);
+                            hipStream_t s, int block) {
+  hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, s, cu, d.N, d.T, d.NC, block, ct);
   return hipGetLastError();
 }
 
