@@ -34,7 +34,7 @@ namespace attn {
 
 constexpr int AD = 256;           // head dimension
 constexpr int BR = 64;            // rows of a query or key block
-constexpr int A_LD = AD + 8;      // 528-byte rows of a staged block
+constexpr int A_LD = AD + 16;     // 544-byte rows of a staged block (conflict-free 16-byte reads)
 constexpr float LOG2E_F = 1.4426950408889634f;
 constexpr float LN2_F = 0.6931471805599453f;
 
@@ -75,17 +75,17 @@ KDA_DEV float row_max16(float v) {
 
 // ------------------------------------------------------------------ helpers
 // 64 rows of one head of a [T, H, 256] bf16 tensor into a padded LDS block
-// (rows of A_LD = 264 elements: 33 chunks of 16 bytes, the last one padding)
+// (rows of A_LD = 272 elements: 34 chunks of 16 bytes, the last two padding)
 // by direct global-to-LDS loads, which use no registers. Wave instruction
 // `ins` fills the 64 chunks (1 KiB) from chunk 64 ins on, lane L the one at
 // 64 ins + L; a padding chunk gets a copy of its row's last chunk. NW waves
-// share the 33 instructions. Rows from n on repeat row n - 1. The caller
+// share the 34 instructions. Rows from n on repeat row n - 1. The caller
 // waits for the loads (vmcnt) and then for the other waves.
 template <int NW>
 KDA_DEV void dma_rows(bf16 (*blk)[A_LD], const bf16* src, int64_t row0, int n, int H, int h) {
   typedef __attribute__((address_space(1))) const void* gptr;
   typedef __attribute__((address_space(3))) void* lptr;
-  constexpr int CPR = A_LD / 8, INS = BR * CPR / 64;    // 33 chunks per row, 33 instructions
+  constexpr int CPR = A_LD / 8, INS = BR * CPR / 64;    // 34 chunks per row, 34 instructions
   static_assert(BR * CPR % 64 == 0, "whole wave instructions");
   const int w = wave_id(), l = lane_id();
   bf16* base = &blk[0][0];
