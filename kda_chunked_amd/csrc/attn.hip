@@ -101,6 +101,29 @@ KDA_DEV void dma_rows(bf16 (*blk)[A_LD], const bf16* src, int64_t row0, int n, i
   }
 }
 
+// A thread's share of 64 rows of one head of a [T, H, 256] bf16 tensor when
+// NW waves stage a block (2048 chunks of 16 bytes): requested into registers
+// one block ahead of its use, so that the loads fly while the current block
+// is computed. Rows from n on repeat row n - 1.
+template <int NW>
+KDA_DEV void pre_load(bf16x8 (&x)[32 / NW], const bf16* src, int64_t row0, int n, int H, int h) {
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int u = threadIdx.x + 64 * NW * i, r = u >> 5, c = u & 31;
+    const int rr = r < n ? r : n - 1;
+    x[i] = *reinterpret_cast<const bf16x8*>(src + ((row0 + rr) * H + h) * AD + 8 * c);
+  }
+}
+
+template <int NW>
+KDA_DEV void pre_store(bf16 (*blk)[A_LD], const bf16x8 (&x)[32 / NW]) {
+#pragma unroll
+  for (int i = 0; i < 32 / NW; ++i) {
+    const int u = threadIdx.x + 64 * NW * i;
+    *reinterpret_cast<bf16x8*>(&blk[u >> 5][8 * (u & 31)]) = x[i];
+  }
+}
+
 // Wait for this wave's direct loads, then for every wave.
 KDA_DEV void dma_join() {
   __builtin_amdgcn_s_waitcnt(0);
@@ -193,12 +216,35 @@ attn_fwd_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
   for (int dt = 0; dt < 16; ++dt) O[dt] = zero4();
   int64_t kend = i0 + nq + off;             // keys [0, kend) can be seen by the block
   kend = kend < 0 ? 0 : (kend > Lk ? Lk : kend);
+  // eight waves prefetch the next K / V block into registers (32 each);
+  // four load theirs directly into LDS and rely on a second workgroup
+  constexpr int NW = 4 * HPW;
+  bf16x8 pk[32 / NW], pv[32 / NW];
+  if constexpr (HPW == 2) {
+    if (kend > 0) {
+      const int n0 = (int)(kend < BR ? kend : BR);
+      pre_load<NW>(pk, k, ks, n0, a.Hkv, g);
+      pre_load<NW>(pv, v, ks, n0, a.Hkv, g);
+    }
+  }
   for (int64_t kb0 = 0; kb0 < kend; kb0 += BR) {
     const int nk = (int)(kend - kb0 < BR ? kend - kb0 : BR);
     __syncthreads();                        // every wave is done with the previous block
-    dma_rows<4 * HPW>(sm.k, k, ks + kb0, nk, a.Hkv, g);
-    dma_rows<4 * HPW>(sm.v, v, ks + kb0, nk, a.Hkv, g);
-    dma_join();
+    if constexpr (HPW == 2) {
+      pre_store<NW>(sm.k, pk);
+      pre_store<NW>(sm.v, pv);
+      __syncthreads();
+      if (kb0 + BR < kend) {
+        const int64_t nb = kb0 + BR;
+        const int n1 = (int)(kend - nb < BR ? kend - nb : BR);
+        pre_load<NW>(pk, k, ks + nb, n1, a.Hkv, g);
+        pre_load<NW>(pv, v, ks + nb, n1, a.Hkv, g);
+      }
+    } else {
+      dma_rows<NW>(sm.k, k, ks + kb0, nk, a.Hkv, g);
+      dma_rows<NW>(sm.v, v, ks + kb0, nk, a.Hkv, g);
+      dma_join();
+    }
     f32x4 S[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) S[nt] = zero4();
@@ -382,11 +428,12 @@ attn_dq_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
 
 // ------------------------------------------------------------------ dk, dv
 // Workgroup: one 128-key block (BK) of one key head, 8 waves of 16 keys that
-// share each staged query block. K and V never enter LDS: they are only the
-// A operands of a wave's own keys and stay in registers. dv and dk are two
-// launches of one kernel (WANT_DK false / true): holding both accumulators
-// would leave no registers for a second wave per SIMD; the dk pass recomputes
-// the S^T that the dv pass also forms.
+// share each staged query block; the next item's q and dO are requested into
+// registers while the current one is computed. K is the A operand of a
+// wave's own keys and stays in registers; V (dk pass) is read from LDS. dv
+// and dk are two launches of one kernel (WANT_DK false / true): holding both
+// accumulators would leave no registers for a second wave per SIMD; the dk
+// pass recomputes the S^T that the dv pass also forms.
 constexpr int BK = 128;
 
 struct KvSmem {
@@ -398,6 +445,7 @@ struct KvSmem {
     } in;
     float out[BR][AD + 4];          // fp32 results of four waves on their way out
   } u;
+  bf16 vb[BK][A_LD];                // the block's V rows (dk pass: A operand of dP^T)
 };
 
 // F32: fp32 rows (window gradients, or the row-map form's staging), else bf16.
@@ -427,37 +475,54 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t qf64 = qc0 + ifirst / BR;
   const int qfirst = qf64 < qc1 ? (int)qf64 : qc1;
 
-  bf16x8 kf[8], vf[WANT_DK ? 8 : 1];  // A fragments of the wave's 16 keys
+  bf16x8 kf[8];                       // A fragments of the wave's 16 keys
   {
     const int r = jw + (l & 15), rr = r < nk ? r : nk - 1;
     const int64_t base = ((u0 + rr) * a.Hkv + g) * AD + 8 * (l >> 4);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      kf[kk] = *reinterpret_cast<const bf16x8*>(k + base + 32 * kk);
-      if (WANT_DK) vf[kk] = *reinterpret_cast<const bf16x8*>(v + base + 32 * kk);
-    }
+    for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(k + base + 32 * kk);
+  }
+  if (WANT_DK) {
+    // the block's V rows, 128 of them (rows past nk repeat the last key)
+    dma_rows<8>(reinterpret_cast<bf16 (*)[A_LD]>(&sm.vb[0][0]), v, u0, nk, a.Hkv, g);
+    dma_rows<8>(reinterpret_cast<bf16 (*)[A_LD]>(&sm.vb[BR][0]), v, u0 + BR, nk - BR, a.Hkv, g);
   }
   f32x4 acc[16];
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) acc[dt] = zero4();
   const int nqb = qc1 - qfirst, items = a.grp * nqb;
-  // the (query head, query block) items in a fixed order: heads outer
-  for (int it = 0; it < items; ++it) {
+  // the (query head, query block) items in a fixed order, heads outer; each
+  // item's q, dO, lse and Delta are requested one item ahead
+  bf16x8 pq[4], pd[4];
+  float plb[4], pdl[4];
+  auto fetch = [&](int it) {
     const int h = g * a.grp + it / nqb, qc = qfirst + it % nqb;
+    const int64_t t0 = qt.tok[qc];
+    const int nq = qt.len[qc];
+    pre_load<8>(pq, q, t0, nq, a.Hq, h);
+    pre_load<8>(pd, dO, t0, nq, a.Hq, h);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int qcol = 16 * nt + dcol(), qq = qcol < nq ? qcol : nq - 1;
+      plb[nt] = lse[(t0 + qq) * a.Hq + h];
+      pdl[nt] = WANT_DK ? delta[(t0 + qq) * a.Hq + h] : 0.f;
+    }
+  };
+  if (items > 0) fetch(0);
+  __builtin_amdgcn_s_waitcnt(0);      // the V rows (and the first item) have landed
+  for (int it = 0; it < items; ++it) {
+    const int qc = qfirst + it % nqb;
     const int64_t t0 = qt.tok[qc];
     const int nq = qt.len[qc];
     const int64_t i0 = t0 - qs;
     float lbq[4], dlq[4];             // lse log2 e and Delta of this lane's query columns
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int qcol = 16 * nt + dcol(), qq = qcol < nq ? qcol : nq - 1;
-      lbq[nt] = lse[(t0 + qq) * a.Hq + h] * LOG2E_F;
-      dlq[nt] = WANT_DK ? delta[(t0 + qq) * a.Hq + h] : 0.f;
-    }
+    for (int nt = 0; nt < 4; ++nt) lbq[nt] = plb[nt] * LOG2E_F, dlq[nt] = pdl[nt];
     __syncthreads();                  // every wave is done with the previous item's panels
-    dma_rows<8>(sm.u.in.q, q, t0, nq, a.Hq, h);
-    dma_rows<8>(sm.u.in.dO, dO, t0, nq, a.Hq, h);
-    dma_join();
+    pre_store<8>(sm.u.in.q, pq);
+    pre_store<8>(sm.u.in.dO, pd);
+    __syncthreads();
+    if (it + 1 < items) fetch(it + 1);
     // a wave whose keys no query of this block sees skips the item
     if (jw >= nk || j0 + jw > i0 + nq - 1 + off) continue;
     f32x4 S[4], dP[4];
@@ -469,7 +534,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int nt = 0; nt < 4; ++nt) {
         S[nt] = mfma16(kf[kk], frag(&sm.u.in.q[0][0], A_LD, 16 * nt, 32 * kk), S[nt]);
         if (WANT_DK)
-          dP[nt] = mfma16(vf[kk], frag(&sm.u.in.dO[0][0], A_LD, 16 * nt, 32 * kk), dP[nt]);
+          dP[nt] = mfma16(frag(&sm.vb[0][0], A_LD, jw, 32 * kk),
+                          frag(&sm.u.in.dO[0][0], A_LD, 16 * nt, 32 * kk), dP[nt]);
       }
     // S^T[key][query]: keys are rows jw + drow(i), queries columns 16 nt + dcol()
     const bool full = jw + 16 <= nk && nq == BR && j0 + jw + 15 <= i0 + off;
