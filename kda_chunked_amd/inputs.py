@@ -261,6 +261,12 @@ ATTN_WORKLOADS = [
     AttnWorkload("attn_tiny", (70, 1, 0, 130, 5, 64), (100, 1, 5, 64, 0, 64), 4, 2, seed=20),
     # an odd group size (3 query heads per key head) over several blocks
     AttnWorkload("attn_grp3", (200, 65, 129), (300, 65, 200), 6, 2, seed=21),
+    # plain multi-head (one query head per key head); a short query block
+    # against five key blocks; a group of 4 sharing one key head
+    AttnWorkload("attn_mha", (129, 3), (200, 3), 2, 2, seed=23),
+    AttnWorkload("attn_longkeys", (5, 64, 1), (300, 64, 130), 4, 1, seed=24),
+    # 5200 keys: the row map's sort takes three tiles and two merge passes
+    AttnWorkload("attn_rowmap", (300, 200), (3000, 2200), 2, 1, seed=25),
     AttnWorkload("attn_cp1_16461", _CP1_Q, tuple(a + b for a, b in zip(_CP1_Q, _CP1_EXTRA)),
                  24, 4, seed=22),
 ]

@@ -77,7 +77,7 @@ def _keyless(ref_lse):
     return ~np.isfinite(ref_lse)
 
 
-@pytest.mark.parametrize("name", ["attn_tiny", "attn_grp3"])
+@pytest.mark.parametrize("name", ["attn_tiny", "attn_grp3", "attn_mha", "attn_longkeys"])
 @pytest.mark.parametrize("form", [ATTN_DKV_BF16, ATTN_DKV_F32], ids=["bf16", "f32"])
 def test_small_full_parity(name, form):
     w = I.ATTN_BY_NAME[name]
@@ -99,10 +99,13 @@ def test_small_full_parity(name, form):
         assert torch.equal(got[k].view(torch.uint8), again[k].view(torch.uint8)), k
 
 
-def test_row_map_add_form():
+@pytest.mark.parametrize("name", ["attn_grp3", "attn_rowmap"])
+def test_row_map_add_form(name):
     """dk, dv added in fp32 into destinations through a row map with repeated
-    rows, dropped keys (-1) and out-of-range rows; rows no key names stay."""
-    w = I.ATTN_BY_NAME["attn_grp3"]
+    rows, dropped keys (-1) and out-of-range rows; rows no key names stay.
+    attn_rowmap's 5200 keys take the sort through three tiles and two merge
+    passes."""
+    w = I.ATTN_BY_NAME[name]
     dst_rows = w.Tk // 2 + 7
     inp = I.make_attn_inputs(w)
     d = _dev(inp)
