@@ -768,8 +768,10 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       *reinterpret_cast<bf16x8*>(P + fwd_panel::QD + rA * HD + cA + 8 * u) = qh[u];
       *reinterpret_cast<bf16x8*>(P + fwd_panel::QD + CL * HD + rA * HD + cA + 8 * u) = ql[u];
     }
-    // Ke^T [c][r] = k^_r e^(G_last - G_r): thread (c, rows 16 b .. 16 b + 15)
-    const int c = t & 127, b = t >> 7;
+    // Ke^T [c][r] = k^_r e^(G_last - G_r): thread (c, rows 16 b .. 16 b + 15),
+    // four consecutive threads per row c, so that a wave writes 16 whole
+    // 128-byte rows of each plane
+    const int c = t >> 2, b = t & 3;
     const float gl = sm.Gref[4][c];
     bf16x8 eh[2], el[2];
 #pragma unroll
