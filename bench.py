@@ -505,6 +505,8 @@ def main():
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="tabulate a rocprofv3 --kernel-trace run and exit")
     ap.add_argument("--fingerprint", action="store_true", help="print the source hash and exit")
+    ap.add_argument("--leg", choices=("kda", "conv", "attn"), default="kda",
+                    help="time only the conv1d + SiLU or the attention leg (for profiling runs)")
     args = ap.parse_args()
     if args.fingerprint:
         print(fingerprint())
@@ -536,6 +538,13 @@ def main():
     from kda_chunked_amd.binding import lib, set_launch_hook
 
     lib()
+    if args.leg != "kda":
+        if args.calibrate_copy:
+            src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda")
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps(time_conv(torch) if args.leg == "conv" else time_attn(torch)), flush=True)
+        return
     w = I.BY_NAME[args.workload]
     inp, run = make_runner(w, torch)
     step, fwd, bwd, replay_pair = run["step"], run["fwd"], run["bwd"], run["replay_pair"]

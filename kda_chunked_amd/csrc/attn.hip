@@ -66,6 +66,17 @@ KDA_DEV void seg_bounds(const int32_t* cu, int s, int64_t T, int64_t& a, int64_t
   n = y - x;
 }
 
+// Workgroup x of a (query block, HPW query heads) launch: key heads vary
+// fastest, then the HPW-head slices of the group, then the query block, so
+// that the XCDs (dealt workgroups round robin) each see few key heads and the
+// heads of one query block start together.
+template <int HPW>
+KDA_DEV void qblock_heads(const Dims& a, int x, int& ci, int& h0) {
+  const int slices = a.grp / HPW, g = x % a.Hkv, rest = x / a.Hkv;
+  ci = rest / slices;
+  h0 = g * a.grp + (rest % slices) * HPW;
+}
+
 KDA_DEV float row_max16(float v) {
   v = fmaxf(v, row_xor<1>(v));
   v = fmaxf(v, row_xor<3>(v));
@@ -186,7 +197,8 @@ attn_fwd_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
                 const bf16* __restrict__ k, const bf16* __restrict__ v, bf16* __restrict__ o,
                 float* __restrict__ lse) {
   __shared__ FwdSmem<HPW> sm;
-  const int ci = blockIdx.x;
+  int ci, h0;
+  qblock_heads<HPW>(a, blockIdx.x, ci, h0);
   if (ci >= qt.doc_c0[a.S]) return;
   const int s = seg_of(qt.doc_c0, a.S, ci);
   int64_t qs, Lq, ks, Lk;
@@ -196,7 +208,7 @@ attn_fwd_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
   const int nq = qt.len[ci];
   const int64_t i0 = t0 - qs, off = Lk - Lq;
   const int w = wave_id(), wr = w & 3, l = lane_id();
-  const int h = blockIdx.y * HPW + (w >> 2), g = h / a.grp;
+  const int h = h0 + (w >> 2), g = h / a.grp;
   const float c2 = a.scale * LOG2E_F;
 
   bf16x8 qf[8];
@@ -348,7 +360,8 @@ attn_dq_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
                const bf16* __restrict__ dO, const float* __restrict__ lse,
                const float* __restrict__ delta, bf16* __restrict__ dq) {
   __shared__ DqSmem<HPW> sm;
-  const int ci = blockIdx.x;
+  int ci, h0;
+  qblock_heads<HPW>(a, blockIdx.x, ci, h0);
   if (ci >= qt.doc_c0[a.S]) return;
   const int s = seg_of(qt.doc_c0, a.S, ci);
   int64_t qs, Lq, ks, Lk;
@@ -358,7 +371,7 @@ attn_dq_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
   const int nq = qt.len[ci];
   const int64_t i0 = t0 - qs, off = Lk - Lq;
   const int w = wave_id(), wr = w & 3, l = lane_id();
-  const int h = blockIdx.y * HPW + (w >> 2), g = h / a.grp;
+  const int h = h0 + (w >> 2), g = h / a.grp;
   const float c2 = a.scale * LOG2E_F;
 
   bf16x8 qf[8], df[8];
@@ -456,7 +469,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16* __restrict__ v, const bf16* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ delta, void* __restrict__ out) {
   __shared__ KvSmem sm;
-  const int cj = blockIdx.x, g = blockIdx.y;
+  // key heads vary fastest: neighbouring workgroups (which the dispatcher
+  // deals round robin over the XCDs) take the same key block of every head,
+  // so that each XCD sees the key heads congruent to it and the heavy early
+  // blocks of a segment start together
+  const int cj = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
   if (cj >= kt.doc_c0[a.S]) return;
   const int s = seg_of(kt.doc_c0, a.S, cj);
   int64_t qs, Lq, ks, Lk;
@@ -690,7 +707,7 @@ namespace A = kda::attn;
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-constexpr int64_t MAX_BLOCKS = (int64_t)1 << 22;    // row blocks of a launch (x 512 threads < 2^32)
+constexpr int64_t MAX_BLOCKS = (int64_t)1 << 22;    // workgroups of a launch (x 512 threads < 2^32)
 
 kda_status check(const kda_attn_problem* p) {
   if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "problem is NULL");
@@ -707,8 +724,9 @@ kda_status check(const kda_attn_problem* p) {
   if (p->D != 256) return fail(KDA_ERR_UNSUPPORTED, "D = %d: this build serves 256", p->D);
   if (!(std::isfinite(p->scale) && p->scale > 0.f))
     return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite and positive");
-  if (p->Tq / 64 + p->num_seqs > MAX_BLOCKS || p->Tk / 64 + p->num_seqs > MAX_BLOCKS)
-    return fail(KDA_ERR_UNSUPPORTED, "more than 2^22 row blocks");
+  if ((p->Tq / 64 + p->num_seqs) * (int64_t)p->Hq > MAX_BLOCKS ||
+      (p->Tk / 128 + p->num_seqs) * (int64_t)p->Hkv > MAX_BLOCKS)
+    return fail(KDA_ERR_UNSUPPORTED, "more than 2^22 workgroups (row blocks x heads)");
   return KDA_OK;
 }
 
@@ -818,10 +836,10 @@ kda_status kda_attn_fwd(const kda_attn_problem* p, const void* q, const void* k,
     const auto* vb = static_cast<const kda::bf16*>(v);
     auto* ob = static_cast<kda::bf16*>(o);
     if (L.d.grp % 2 == 0)
-      hipLaunchKernelGGL(A::attn_fwd_kernel<2>, dim3(L.d.NCq, p->Hq / 2), dim3(512), 0, hs, L.d,
+      hipLaunchKernelGGL(A::attn_fwd_kernel<2>, dim3(L.d.NCq * (p->Hq / 2)), dim3(512), 0, hs, L.d,
                          qt, cu_seqlens_q, cu_seqlens_k, qb, kb, vb, ob, lse);
     else
-      hipLaunchKernelGGL(A::attn_fwd_kernel<1>, dim3(L.d.NCq, p->Hq), dim3(256), 0, hs, L.d, qt,
+      hipLaunchKernelGGL(A::attn_fwd_kernel<1>, dim3(L.d.NCq * p->Hq), dim3(256), 0, hs, L.d, qt,
                          cu_seqlens_q, cu_seqlens_k, qb, kb, vb, ob, lse);
     e = hipGetLastError();
   }
@@ -887,11 +905,11 @@ kda_status kda_attn_bwd(const kda_attn_problem* p, const void* q, const void* k,
     hipLaunchKernelGGL(A::attn_delta_kernel, dim3(grid_for(rows * 64)), dim3(256), 0, hs, rows,
                        static_cast<const kda::bf16*>(o), dob, delta);
     if (L.d.grp % 2 == 0)
-      hipLaunchKernelGGL(A::attn_dq_kernel<2>, dim3(L.d.NCq, p->Hq / 2), dim3(512), 0, hs, L.d, qt,
+      hipLaunchKernelGGL(A::attn_dq_kernel<2>, dim3(L.d.NCq * (p->Hq / 2)), dim3(512), 0, hs, L.d, qt,
                          cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta,
                          static_cast<kda::bf16*>(dq));
     else
-      hipLaunchKernelGGL(A::attn_dq_kernel<1>, dim3(L.d.NCq, p->Hq), dim3(256), 0, hs, L.d, qt,
+      hipLaunchKernelGGL(A::attn_dq_kernel<1>, dim3(L.d.NCq * p->Hq), dim3(256), 0, hs, L.d, qt,
                          cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta,
                          static_cast<kda::bf16*>(dq));
     e = hipGetLastError();
@@ -899,7 +917,7 @@ kda_status kda_attn_bwd(const kda_attn_problem* p, const void* q, const void* k,
   if (e == hipSuccess && keys) {
     void* wk = add ? ws + L.win_k : dk;
     void* wv = add ? ws + L.win_v : dv;
-    const dim3 grid(L.d.NCk, p->Hkv);
+    const dim3 grid((unsigned)((int64_t)L.d.NCk * p->Hkv));
     if (dkv_form == KDA_ATTN_DKV_BF16) {
       hipLaunchKernelGGL((A::attn_dkdv_kernel<false, false>), grid, dim3(512), 0, hs, L.d, qt, kt,
                          cu_seqlens_q, cu_seqlens_k, qb, kb, vb, dob, lse, delta, wv);
