@@ -201,6 +201,9 @@ attn_fwd_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
   qblock_heads<HPW>(a, blockIdx.x, ci, h0);
   if (ci >= qt.doc_c0[a.S]) return;
   const int s = seg_of(qt.doc_c0, a.S, ci);
+  // a segment's query blocks in reverse: the late ones see the most keys and
+  // start first
+  ci = qt.doc_c0[s] + qt.doc_c0[s + 1] - 1 - ci;
   int64_t qs, Lq, ks, Lk;
   seg_bounds(cuq, s, a.Tq, qs, Lq);
   seg_bounds(cuk, s, a.Tk, ks, Lk);
@@ -364,6 +367,9 @@ attn_dq_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
   qblock_heads<HPW>(a, blockIdx.x, ci, h0);
   if (ci >= qt.doc_c0[a.S]) return;
   const int s = seg_of(qt.doc_c0, a.S, ci);
+  // a segment's query blocks in reverse: the late ones see the most keys and
+  // start first
+  ci = qt.doc_c0[s] + qt.doc_c0[s + 1] - 1 - ci;
   int64_t qs, Lq, ks, Lk;
   seg_bounds(cuq, s, a.Tq, qs, Lq);
   seg_bounds(cuk, s, a.Tk, ks, Lk);
