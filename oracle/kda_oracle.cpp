@@ -16,7 +16,9 @@
 //   chunked form (per-chunk affine state map S_out = M*S_in + B, PR #7176
 //   opening section) is an acceleration of:
 //
-//     S_0 = 0 at every document start
+//     S_0 = 0 at every document start, except that document 0 may enter with a
+//         given state S_init (one rank's share of a sequence split over ranks,
+//         PR #7176 opening section: the state passed between fragments)
 //     S'_t = Diag(exp(g_t)) S_{t-1}               (decay each key row c)
 //     u_t  = v_t - S'_t^T k_t
 //     S_t  = S'_t + beta_t k_t u_t^T              (= (I - b k k^T) Diag(e^g) S + b k v^T)
@@ -24,6 +26,10 @@
 //
 //   gate form "raw": g[t,h,c] = -exp(A_log[h]) * softplus(a[t,h,c] + dt_bias[h,c])
 //   fused L2 norm:   q <- q * (sum_c q_c^2 + eps)^(-1/2), same for k
+//
+// The state after the last document may be returned as S_final, and the
+// backward may take dS_final, the gradient of the loss with respect to it, and
+// return dS_init, the gradient with respect to S_init.
 //
 // The backward is the reverse-mode derivative of the loss L = sum_t <o_t, dO_t>,
 // derived by hand from the recurrence above (token by token, in reverse), with
@@ -76,6 +82,14 @@ double sigmoid(double x) {
   double e = std::exp(x);
   return e / (1.0 + e);
 }
+
+// States at the ends of the packed sequence, each [H, K, V] (nullable).
+struct Boundary {
+  const double* s_init;    // state entering document 0
+  double* s_final;         // state leaving the last document
+  const double* ds_final;  // gradient with respect to s_final
+  double* ds_init;         // gradient with respect to s_init
+};
 
 // Per-token quantities of one (document, head) job, after the gate transform
 // and the optional L2 norm.
@@ -152,7 +166,7 @@ void step_fwd(int K, int V, const Token& tk, int64_t i, std::vector<double>& S,
   if (u) std::memcpy(u, ut.data(), sizeof(double) * V);
 }
 
-void fwd_job(const Problem& P, const Inputs& in, int d, int h, double* o,
+void fwd_job(const Problem& P, const Inputs& in, const Boundary& bd, int d, int h, double* o,
              double* states, const int64_t* chunk_base, int chunk) {
   Token tk;
   load_job(P, in, d, h, tk);
@@ -160,6 +174,7 @@ void fwd_job(const Problem& P, const Inputs& in, int d, int h, double* o,
   const int64_t n = in.cu[d + 1] - t0;
   const int K = P.K, V = P.V, H = P.H;
   std::vector<double> S(K * V, 0.0);
+  if (d == 0 && bd.s_init) std::memcpy(S.data(), bd.s_init + (int64_t)h * K * V, sizeof(double) * K * V);
   for (int64_t i = 0; i < n; ++i) {
     if (states && i % chunk == 0) {
       double* dst = states + ((chunk_base[d] + i / chunk) * H + h) * K * V;
@@ -176,6 +191,8 @@ void fwd_job(const Problem& P, const Inputs& in, int d, int h, double* o,
       }
     }
   }
+  if (d == P.N - 1 && bd.s_final)
+    std::memcpy(bd.s_final + (int64_t)h * K * V, S.data(), sizeof(double) * K * V);
 }
 
 struct Grads {
@@ -188,8 +205,8 @@ struct Grads {
   double* ddt_bias_part;  // [N,H,K] per-job partial (raw only)
 };
 
-void bwd_job(const Problem& P, const Inputs& in, const double* dO, const Grads& G,
-             int d, int h) {
+void bwd_job(const Problem& P, const Inputs& in, const Boundary& bd, const double* dO,
+             const Grads& G, int d, int h) {
   Token tk;
   load_job(P, in, d, h, tk);
   const int64_t t0 = in.cu[d];
@@ -202,13 +219,17 @@ void bwd_job(const Problem& P, const Inputs& in, const double* dO, const Grads& 
   std::vector<double> ckpt(nblk * K * V, 0.0);
   {
     std::vector<double> S(K * V, 0.0);
+    if (d == 0 && bd.s_init) std::memcpy(S.data(), bd.s_init + (int64_t)h * K * V, sizeof(double) * K * V);
     for (int64_t i = 0; i < n; ++i) {
       if (i % B == 0) std::memcpy(&ckpt[(i / B) * K * V], S.data(), sizeof(double) * K * V);
       step_fwd(K, V, tk, i, S, nullptr, nullptr);
     }
   }
 
-  std::vector<double> dS(K * V, 0.0);  // gradient w.r.t. S_t; zero after the document
+  // gradient w.r.t. S_t; zero after a document, dS_final after the last one
+  std::vector<double> dS(K * V, 0.0);
+  if (d == P.N - 1 && bd.ds_final)
+    std::memcpy(dS.data(), bd.ds_final + (int64_t)h * K * V, sizeof(double) * K * V);
   std::vector<double> Sp_blk(B * K * V), St_blk(B * K * V), u_blk(B * V);
   std::vector<double> dqh(n * K, 0.0), dkh(n * K, 0.0), dg(n * K, 0.0);
   std::vector<double> du(V), dSp(K * V);
@@ -271,6 +292,10 @@ void bwd_job(const Problem& P, const Inputs& in, const double* dO, const Grads& 
       for (int j = 0; j < V; ++j) G.dv[(t * H + h) * V + j] = du[j];
     }
   }
+
+  // dS now holds the gradient w.r.t. the state entering the document
+  if (d == 0 && bd.ds_init)
+    std::memcpy(bd.ds_init + (int64_t)h * K * V, dS.data(), sizeof(double) * K * V);
 
   // Chain rule through the L2 norm and the gate transform.
   double dAlog = 0;
@@ -357,10 +382,12 @@ extern "C" {
 // `chunk` tokens, chunks restarting at each document start, ordered by
 // document then chunk: [n_chunks, H, K, V] with n_chunks = sum_d ceil(len_d/chunk).
 // Returns 0 on success, 1 on invalid arguments.
+// s_init, s_final (nullable, [H,K,V]): the state entering document 0 and the
+// state leaving the last document.
 int kda_oracle_fwd(const Problem* P, const int64_t* cu, const double* q, const double* k,
                    const double* v, const double* beta, const double* gate,
-                   const double* A_log, const double* dt_bias, double* o, double* states,
-                   int chunk, int nthreads) {
+                   const double* A_log, const double* dt_bias, const double* s_init,
+                   double* o, double* s_final, double* states, int chunk, int nthreads) {
   if (check(P, cu)) return 1;
   if (P->gate_raw && (!A_log || !dt_bias)) return 1;
   if (states && chunk < 1) return 1;
@@ -370,25 +397,33 @@ int kda_oracle_fwd(const Problem* P, const int64_t* cu, const double* q, const d
     int64_t len = cu[d + 1] - cu[d];
     base[d + 1] = base[d] + (states ? (len + chunk - 1) / chunk : 0);
   }
+  const Boundary bd{s_init, s_final, nullptr, nullptr};
+  if (s_final && P->N == 0) return 1;
   run_jobs(*P, cu, nthreads,
-           [&](int d, int h) { fwd_job(*P, in, d, h, o, states, base.data(), chunk); });
+           [&](int d, int h) { fwd_job(*P, in, bd, d, h, o, states, base.data(), chunk); });
   return 0;
 }
 
 // Backward of L = sum <o, dO>. dgate receives dg (g form) or da (raw form).
 // Raw form also writes dA_log [H] and ddt_bias [H,K], summed over documents
 // in document order.
+// s_init (nullable): as for the forward; ds_final (nullable): gradient of the
+// loss w.r.t. the state leaving the last document; ds_init (nullable) receives
+// the gradient w.r.t. s_init.
 int kda_oracle_bwd(const Problem* P, const int64_t* cu, const double* q, const double* k,
                    const double* v, const double* beta, const double* gate,
-                   const double* A_log, const double* dt_bias, const double* dO, double* dq,
-                   double* dk, double* dv, double* dbeta, double* dgate, double* dA_log,
-                   double* ddt_bias, int nthreads) {
+                   const double* A_log, const double* dt_bias, const double* s_init,
+                   const double* dO, const double* ds_final, double* dq, double* dk, double* dv,
+                   double* dbeta, double* dgate, double* dA_log, double* ddt_bias,
+                   double* ds_init, int nthreads) {
   if (check(P, cu)) return 1;
   if (P->gate_raw && (!A_log || !dt_bias || !dA_log || !ddt_bias)) return 1;
   Inputs in{cu, q, k, v, beta, gate, A_log, dt_bias};
   std::vector<double> pA((size_t)P->N * P->H, 0.0), pdt((size_t)P->N * P->H * P->K, 0.0);
   Grads G{dq, dk, dv, dbeta, dgate, pA.data(), pdt.data()};
-  run_jobs(*P, cu, nthreads, [&](int d, int h) { bwd_job(*P, in, dO, G, d, h); });
+  const Boundary bd{s_init, nullptr, ds_final, ds_init};
+  if (ds_init && P->N == 0) return 1;
+  run_jobs(*P, cu, nthreads, [&](int d, int h) { bwd_job(*P, in, bd, dO, G, d, h); });
   if (P->gate_raw) {
     for (int h = 0; h < P->H; ++h) {
       double s = 0;
@@ -404,6 +439,6 @@ int kda_oracle_bwd(const Problem* P, const int64_t* cu, const double* q, const d
   return 0;
 }
 
-int kda_oracle_version(void) { return 1; }
+int kda_oracle_version(void) { return 2; }
 
 }  // extern "C"

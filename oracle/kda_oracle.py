@@ -69,9 +69,9 @@ def open_library(path: str):
     dp = ctypes.POINTER(ctypes.c_double)
     lp = ctypes.POINTER(ctypes.c_int64)
     pp = ctypes.POINTER(_Problem)
-    lib.kda_oracle_fwd.argtypes = [pp, lp] + [dp] * 9 + [ctypes.c_int, ctypes.c_int]
+    lib.kda_oracle_fwd.argtypes = [pp, lp] + [dp] * 11 + [ctypes.c_int, ctypes.c_int]
     lib.kda_oracle_fwd.restype = ctypes.c_int
-    lib.kda_oracle_bwd.argtypes = [pp, lp] + [dp] * 15 + [ctypes.c_int]
+    lib.kda_oracle_bwd.argtypes = [pp, lp] + [dp] * 18 + [ctypes.c_int]
     lib.kda_oracle_bwd.restype = ctypes.c_int
     return lib
 
@@ -133,11 +133,23 @@ class _Args:
         self.raw = raw
 
 
+def _state(x, a):
+    if x is None:
+        return None
+    x = _f64(x)
+    if x.shape != (a.H, a.K, a.V):
+        raise ValueError("a boundary state must be [H,K,V]")
+    return x
+
+
 def fwd(cu_seqlens, q, k, v, beta, gate, A_log=None, dt_bias=None, *, gate_form="g",
-        l2norm=False, scale=None, l2_eps=1e-6, chunk=None, threads=None, lib=None):
+        l2norm=False, scale=None, l2_eps=1e-6, chunk=None, threads=None, lib=None,
+        s_init=None, final_state=False):
     """Forward. Returns o [T,H,V] (float64), and with ``chunk`` also the
     state at the start of every chunk: [n_chunks, H, K, V], chunks restarting
-    at each document start, ordered by document then chunk."""
+    at each document start, ordered by document then chunk. ``s_init``
+    [H,K,V] is the state entering document 0 (zero if None); with
+    ``final_state`` the state leaving the last document is returned last."""
     a = _Args(cu_seqlens, q, k, v, beta, gate, A_log, dt_bias, gate_form, l2norm, scale, l2_eps)
     o = np.zeros((a.T, a.H, a.V))
     states = None
@@ -145,20 +157,26 @@ def fwd(cu_seqlens, q, k, v, beta, gate, A_log=None, dt_bias=None, *, gate_form=
         lens = np.diff(a.cu)
         nch = int(np.sum((lens + chunk - 1) // chunk))
         states = np.zeros((nch, a.H, a.K, a.V))
+    s_in = _state(s_init, a)
+    s_fin = np.zeros((a.H, a.K, a.V)) if final_state else None
     lib = _load(lib)
     rc = lib.kda_oracle_fwd(ctypes.byref(a.P), a.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                             _ptr(a.q), _ptr(a.k), _ptr(a.v), _ptr(a.beta), _ptr(a.gate),
-                            _ptr(a.A_log), _ptr(a.dt_bias), _ptr(o), _ptr(states),
-                            int(chunk or 0), int(threads or default_threads()))
+                            _ptr(a.A_log), _ptr(a.dt_bias), _ptr(s_in), _ptr(o), _ptr(s_fin),
+                            _ptr(states), int(chunk or 0), int(threads or default_threads()))
     if rc != 0:
         raise ValueError("kda_oracle_fwd rejected its arguments")
-    return (o, states) if chunk else o
+    out = (o,) + ((states,) if chunk else ()) + ((s_fin,) if final_state else ())
+    return out if len(out) > 1 else o
 
 
 def bwd(cu_seqlens, q, k, v, beta, gate, dO, A_log=None, dt_bias=None, *, gate_form="g",
-        l2norm=False, scale=None, l2_eps=1e-6, threads=None, lib=None):
-    """Backward of L = sum(o * dO). Returns a dict with dq, dk, dv, dbeta and
-    dg (g form) or da, dA_log, ddt_bias (raw form), all float64."""
+        l2norm=False, scale=None, l2_eps=1e-6, threads=None, lib=None, s_init=None,
+        ds_final=None):
+    """Backward of L = sum(o * dO) + <S_final, ds_final>. Returns a dict with
+    dq, dk, dv, dbeta and dg (g form) or da, dA_log, ddt_bias (raw form), and,
+    when s_init or ds_final is given, ds_init (the gradient w.r.t. the state
+    entering document 0, [H,K,V]), all float64."""
     a = _Args(cu_seqlens, q, k, v, beta, gate, A_log, dt_bias, gate_form, l2norm, scale, l2_eps)
     dO = _f64(dO)
     if dO.shape != (a.T, a.H, a.V):
@@ -170,15 +188,19 @@ def bwd(cu_seqlens, q, k, v, beta, gate, dO, A_log=None, dt_bias=None, *, gate_f
     dgate = np.zeros((a.T, a.H, a.K))
     dA_log = np.zeros(a.H) if a.raw else None
     ddt = np.zeros((a.H, a.K)) if a.raw else None
+    s_in, ds_fin = _state(s_init, a), _state(ds_final, a)
+    ds_init = np.zeros((a.H, a.K, a.V)) if a.P.N > 0 else None
     lib = _load(lib)
     rc = lib.kda_oracle_bwd(ctypes.byref(a.P), a.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                             _ptr(a.q), _ptr(a.k), _ptr(a.v), _ptr(a.beta), _ptr(a.gate),
-                            _ptr(a.A_log), _ptr(a.dt_bias), _ptr(dO), _ptr(dq), _ptr(dk),
-                            _ptr(dv), _ptr(dbeta), _ptr(dgate), _ptr(dA_log), _ptr(ddt),
-                            int(threads or default_threads()))
+                            _ptr(a.A_log), _ptr(a.dt_bias), _ptr(s_in), _ptr(dO), _ptr(ds_fin),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dgate), _ptr(dA_log),
+                            _ptr(ddt), _ptr(ds_init), int(threads or default_threads()))
     if rc != 0:
         raise ValueError("kda_oracle_bwd rejected its arguments")
     out = {"dq": dq, "dk": dk, "dv": dv, "dbeta": dbeta}
+    if s_init is not None or ds_final is not None:
+        out["ds_init"] = ds_init
     if a.raw:
         out.update(da=dgate, dA_log=dA_log, ddt_bias=ddt)
     else:

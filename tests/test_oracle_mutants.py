@@ -50,6 +50,13 @@ MUTANTS = {
                               "if (x > 30.0) return std::log1p(std::exp(-x));"),
     "softplus_large_sign": ("if (x > 30.0) return x + std::log1p(std::exp(-x));",
                             "if (x > 30.0) return -x + std::log1p(std::exp(-x));"),
+    # boundary states of a split sequence
+    "s_init_dropped_bwd": ("    if (d == 0 && bd.s_init) std::memcpy(S.data()",
+                           "    if (false && bd.s_init) std::memcpy(S.data()"),
+    "s_final_wrong_doc": ("if (d == P.N - 1 && bd.s_final)", "if (d == 0 && bd.s_final)"),
+    "ds_final_wrong_doc": ("if (d == P.N - 1 && bd.ds_final)", "if (d == 0 && bd.ds_final)"),
+    "ds_init_before_decay": ("std::memcpy(bd.ds_init + (int64_t)h * K * V, dS.data()",
+                             "std::memcpy(bd.ds_init + (int64_t)h * K * V, dSp.data()"),
 }
 
 
@@ -59,10 +66,10 @@ def _run(lib, p, **kw):
                   threads=1, **kw)
 
 
-def _grad(lib, p):
+def _grad(lib, p, **kw):
     return ko.bwd(p["cu"], p["q"], p["k"], p["v"], p["beta"], p["gate"], p["dO"],
                   p.get("A_log"), p.get("dt_bias"), gate_form=p["gate_form"],
-                  l2norm=p["l2norm"], lib=lib, threads=1)
+                  l2norm=p["l2norm"], lib=lib, threads=1, **kw)
 
 
 def _fd_ok(lib, p, tol=1e-6, h=1e-6):
@@ -140,6 +147,21 @@ def battery(lib):
                           5 ** -0.5, 3)
     if not all(rel_l2(gr[n], gc[n]) < 1e-12 for n in gc):
         failed.append("chunked_bwd")
+    # a sequence split inside its second document, run fragment by fragment
+    # with the state handed over, gives the unsplit outputs and gradients
+    from test_oracle_state import split
+    p = tiny_problem(rng, [4, 6, 3], 1, 4, 3)
+    o, g = _run(lib, p), _grad(lib, p)
+    A, B = split(p, 7)
+    oA, SA = _run(lib, A, final_state=True)
+    oB = _run(lib, B, s_init=SA)
+    gB = _grad(lib, B, s_init=SA, ds_final=np.zeros_like(SA))
+    gA = _grad(lib, A, ds_final=gB["ds_init"])
+    if not rel_l2(np.concatenate([oA, oB]), o) < 1e-12:
+        failed.append("split_fwd")
+    if not all(rel_l2(np.concatenate([gA[n], gB[n]]), g[n]) < 1e-11
+               for n in ("dq", "dk", "dv", "dbeta", "dg")):
+        failed.append("split_bwd")
     return failed
 
 
