@@ -487,6 +487,73 @@ def time_attn(torch) -> dict:
     return res
 
 
+def time_cp(torch, ranks=4) -> dict:
+    """One rank's share of the 1doc sequence split contiguously over `ranks`
+    ranks (the last rank: its fragment continues the document), with the
+    exchange between ranks left out: the state summary (prep kept in the
+    saved set), ranks - 1 transfer steps, the forward from the walked state,
+    the gradient summary, ranks - 1 transposed transfer steps and the
+    backward; against the plain forward + backward of the same fragment."""
+    import numpy as np
+    from kda_chunked_amd import inputs as I
+    from kda_chunked_amd.binding import KDA, kda_state_apply
+    w = I.BY_NAME["1doc"]
+    inp = I.make_inputs(w)
+    T = w.T // ranks
+    a0 = w.T - T
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x[a0:]).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    q, k, v, beta, dO = (bf(inp[n]) for n in ("q", "k", "v", "beta", "dO"))
+    g = torch.from_numpy(np.ascontiguousarray(inp["gate"][a0:])).cuda()
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    kda = KDA(T, w.H, 1, gate=w.gate, l2norm=w.l2norm)
+    args = (q, k, v, beta, g, cu)
+    st = lambda: torch.zeros(w.H, 128, 128, dtype=torch.float32, device="cuda")
+    S_init, s_fin, dS, ds_in, y = st(), st(), st(), st(), st()
+    o = torch.empty_like(v)
+    M, B = kda.state_summary(*args, keep_prep=True)
+    kda.forward(*args, o=o, s_init=S_init, s_final=s_fin, prep_done=True)
+    grads = kda.backward(*args, dO, s_init=S_init, ds_final=dS, ds_init=ds_in)
+
+    def share():
+        kda.state_summary(*args, keep_prep=True)
+        for _ in range(ranks - 1):
+            kda_state_apply(M, S_init, B, y=y)
+        kda.forward(*args, o=o, s_init=S_init, s_final=s_fin, prep_done=True)
+        kda.state_grad_summary(*args, dO)
+        for _ in range(ranks - 1):
+            kda_state_apply(M, dS, B, transpose=True, y=y)
+        kda.backward(*args, dO, s_init=S_init, ds_final=dS, ds_init=ds_in, out=grads)
+
+    def plain():
+        kda.forward(*args, o=o)
+        kda.backward(*args, dO, out=grads)
+    for _ in range(2):
+        share()
+        plain()
+    torch.cuda.synchronize()
+    parts = {
+        "summary_ms": lambda: kda.state_summary(*args, keep_prep=True),
+        "apply_ms": lambda: kda_state_apply(M, S_init, B, y=y),
+        "fwd_state_ms": lambda: kda.forward(*args, o=o, s_init=S_init, s_final=s_fin,
+                                            prep_done=True),
+        "grad_summary_ms": lambda: kda.state_grad_summary(*args, dO),
+        "bwd_state_ms": lambda: kda.backward(*args, dO, s_init=S_init, ds_final=dS,
+                                             ds_init=ds_in, out=grads),
+    }
+    res = {"workload": (f"1doc split over {ranks} ranks, last rank's share: {T} tokens x "
+                        f"{w.H} heads, one continuing document, gate {w.gate}, "
+                        f"L2 {'fused' if w.l2norm else 'off'}")}
+    for name, fn in parts.items():
+        res[name] = round(time_unit(torch, fn, samples=7, calls=5), 4)
+    res["share_step_ms"] = round(time_unit(torch, share, samples=7, calls=3), 4)
+    res["plain_step_ms"] = round(time_unit(torch, plain, samples=7, calls=3), 4)
+    res["overhead"] = round(res["share_step_ms"] / res["plain_step_ms"], 3)
+    res["share_tokens_per_s"] = round(T / (res["share_step_ms"] * 1e-3), 1)
+    print(f"[bench] cp: {res}", file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -505,8 +572,9 @@ def main():
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="tabulate a rocprofv3 --kernel-trace run and exit")
     ap.add_argument("--fingerprint", action="store_true", help="print the source hash and exit")
-    ap.add_argument("--leg", choices=("kda", "conv", "attn"), default="kda",
-                    help="time only the conv1d + SiLU or the attention leg (for profiling runs)")
+    ap.add_argument("--leg", choices=("kda", "conv", "attn", "cp"), default="kda",
+                    help="time only the conv1d + SiLU leg, the attention leg, or one rank's "
+                         "share of a sequence split over ranks (for profiling runs)")
     args = ap.parse_args()
     if args.fingerprint:
         print(fingerprint())
@@ -543,7 +611,8 @@ def main():
             src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda")
             torch.empty_like(src).copy_(src)
             torch.cuda.synchronize()
-        print(json.dumps(time_conv(torch) if args.leg == "conv" else time_attn(torch)), flush=True)
+        legs = {"conv": time_conv, "attn": time_attn, "cp": time_cp}
+        print(json.dumps(legs[args.leg](torch)), flush=True)
         return
     w = I.BY_NAME[args.workload]
     inp, run = make_runner(w, torch)

@@ -68,7 +68,9 @@ _lib = None
 EXPORTS = ("kda_saved_bytes", "kda_workspace_bytes", "kda_fwd", "kda_bwd", "kda_fwd_noalloc",
            "kda_set_launch_hook", "kda_status_string", "kda_last_error", "kda_abi_version",
            "kda_conv_workspace_bytes", "kda_conv_silu_fwd", "kda_conv_silu_bwd",
-           "kda_attn_workspace_bytes", "kda_attn_fwd", "kda_attn_bwd")
+           "kda_attn_workspace_bytes", "kda_attn_fwd", "kda_attn_bwd",
+           "kda_fwd_state", "kda_bwd_state", "kda_state_summary_workspace_bytes",
+           "kda_state_summary", "kda_state_grad_summary", "kda_state_apply")
 ATTN_DKV_BF16, ATTN_DKV_F32, ATTN_DKV_F32_ADD = 0, 1, 2   # kda_attn.h
 NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES in kda.h
 LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int,
@@ -102,6 +104,18 @@ def lib():
         L.kda_conv_silu_fwd.restype = ctypes.c_int
         L.kda_conv_silu_bwd.argtypes = [cp] + [vp] * 11 + [sz, vp]
         L.kda_conv_silu_bwd.restype = ctypes.c_int
+        L.kda_fwd_state.argtypes = [pp] + [vp] * 12 + [ctypes.c_int, vp, sz, vp]
+        L.kda_fwd_state.restype = ctypes.c_int
+        L.kda_bwd_state.argtypes = [pp] + [vp] * 21 + [sz, vp]
+        L.kda_bwd_state.restype = ctypes.c_int
+        L.kda_state_summary_workspace_bytes.argtypes = [pp]
+        L.kda_state_summary_workspace_bytes.restype = sz
+        L.kda_state_summary.argtypes = [pp] + [vp] * 12 + [sz, vp]
+        L.kda_state_summary.restype = ctypes.c_int
+        L.kda_state_grad_summary.argtypes = [pp] + [vp] * 12 + [sz, vp]
+        L.kda_state_grad_summary.restype = ctypes.c_int
+        L.kda_state_apply.argtypes = [ctypes.c_int32, vp, ctypes.c_int, vp, vp, vp, vp]
+        L.kda_state_apply.restype = ctypes.c_int
         ap = ctypes.POINTER(kda_attn_problem)
         L.kda_attn_workspace_bytes.argtypes = [ap, ctypes.c_int, ctypes.c_int64]
         L.kda_attn_workspace_bytes.restype = sz
@@ -237,6 +251,87 @@ def kda_bwd(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, dO, saved, dq,
     _check(rc)
 
 
+FWD_PREP_DONE = 1   # kda_fwd_state: the saved set holds kda_state_summary's prep
+
+
+def kda_fwd_state(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, s_init, o, s_final,
+                  saved, workspace, flags=0):
+    """kda_fwd with the state entering document 0 (s_init, None: zero) and the
+    state leaving the last document written to s_final (None: not written);
+    states fp32 [H,128,128]."""
+    dev = _dev(p, (q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, s_init, o, s_final, saved,
+                   workspace))
+    with _device_ctx(dev):
+        rc = lib().kda_fwd_state(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                 _ptr(g_or_a), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens),
+                                 _ptr(s_init), _ptr(o), _ptr(s_final), _ptr(saved), int(flags),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(dev))
+    _check(rc)
+
+
+def kda_bwd_state(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, s_init, dO, ds_final,
+                  saved, dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias, ds_init, workspace):
+    """kda_bwd of sum <o, dO> + <s_final, ds_final>, writing ds_init."""
+    dev = _dev(p, (q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, s_init, dO, ds_final,
+                   saved, dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias, ds_init, workspace))
+    with _device_ctx(dev):
+        rc = lib().kda_bwd_state(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                 _ptr(g_or_a), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens),
+                                 _ptr(s_init), _ptr(dO), _ptr(ds_final), _ptr(saved), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg_or_da), _ptr(dA_log),
+                                 _ptr(ddt_bias), _ptr(ds_init), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+
+
+def state_summary_workspace_bytes(p) -> int:
+    return int(lib().kda_state_summary_workspace_bytes(ctypes.byref(p)))
+
+
+def _nbytes_or0(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def kda_state_summary(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, M, B, workspace,
+                      saved=None):
+    """The fragment's map s_final = M s_init + B (M, B fp32 [H,128,128] or None);
+    saved, when given, receives the prep for kda_fwd_state(flags=FWD_PREP_DONE)."""
+    dev = _dev(p, (q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, M, B, saved, workspace))
+    with _device_ctx(dev):
+        rc = lib().kda_state_summary(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                     _ptr(g_or_a), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens),
+                                     _ptr(M), _ptr(B), _ptr(saved), _ptr(workspace),
+                                     _nbytes_or0(workspace), _stream(dev))
+    _check(rc)
+
+
+def kda_state_grad_summary(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, dO, saved, dB,
+                           workspace):
+    """dB fp32 [H,128,128]: the gradient w.r.t. s_init with a zero gradient of
+    s_final (saved: the saving forward's set, or None to rebuild its panels)."""
+    dev = _dev(p, (q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, dO, saved, dB, workspace))
+    with _device_ctx(dev):
+        rc = lib().kda_state_grad_summary(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                          _ptr(g_or_a), _ptr(A_log), _ptr(dt_bias),
+                                          _ptr(cu_seqlens), _ptr(dO), _ptr(saved), _ptr(dB),
+                                          _ptr(workspace), _nbytes_or0(workspace), _stream(dev))
+    _check(rc)
+
+
+def kda_state_apply(M, x, B=None, transpose=False, y=None):
+    """y = M x + B (or M^T x + B) per head; M, x, B fp32 [H,128,128] on one GPU."""
+    if y is None:
+        y = torch.empty_like(x)
+    if not (M.is_cuda and x.is_cuda and y.is_cuda and (B is None or B.is_cuda)):
+        raise ValueError("kda_state_apply takes GPU tensors")
+    with _device_ctx(x.device):
+        rc = lib().kda_state_apply(int(x.shape[0]), _ptr(M), int(bool(transpose)), _ptr(B),
+                                   _ptr(x), _ptr(y), _stream(x.device))
+    _check(rc)
+    return y
+
+
 class KDA:
     """Holds the buffers of one problem shape and runs forward / backward.
 
@@ -253,27 +348,77 @@ class KDA:
         u8 = dict(dtype=torch.uint8, device=self.device)
         self.workspace = torch.empty(max(nbytes, 1), **u8)
         self.saved = torch.empty(max(saved_bytes(self.p), 1), **u8)
+        self.summary_ws = None     # the state summaries' workspace, made on first use
 
     def forward(self, q, k, v, beta, gate, cu_seqlens, A_log=None, dt_bias=None, save=True,
-                o=None):
+                o=None, s_init=None, s_final=None, prep_done=False):
+        """o; with s_init / s_final (fp32 [H,128,128]) document 0 enters from
+        s_init and the state leaving the last document goes to s_final;
+        prep_done: the saved set holds state_summary(keep_prep=True)'s prep."""
         if o is None:
             o = torch.empty_like(v)
-        kda_fwd(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, o,
-                self.saved if save else None, self.workspace)
+        saved = self.saved if save else None
+        if prep_done:
+            kda_fwd_state(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, s_init, o,
+                          s_final, saved, self.workspace, flags=FWD_PREP_DONE)
+        elif s_init is None and s_final is None:
+            kda_fwd(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, o, saved,
+                    self.workspace)
+        else:
+            kda_fwd_state(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, s_init, o,
+                          s_final, saved, self.workspace)
         return o
 
     def backward(self, q, k, v, beta, gate, cu_seqlens, dO, A_log=None, dt_bias=None,
-                 replay=False, out=None):
+                 replay=False, out=None, s_init=None, ds_final=None, ds_init=None):
+        """Gradients; with s_init / ds_final / ds_init the boundary-state form
+        (ds_init, when given, receives the gradient w.r.t. s_init)."""
         if out is None:
             out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                        dbeta=torch.empty_like(beta), dgate=torch.empty_like(gate))
             if self.gate == "raw":
                 out["dA_log"] = torch.empty_like(A_log)
                 out["ddt_bias"] = torch.empty_like(dt_bias)
-        kda_bwd(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, dO,
-                None if replay else self.saved, out["dq"], out["dk"], out["dv"], out["dbeta"],
-                out["dgate"], out.get("dA_log"), out.get("ddt_bias"), self.workspace)
+        saved = None if replay else self.saved
+        if s_init is None and ds_final is None and ds_init is None:
+            kda_bwd(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, dO, saved,
+                    out["dq"], out["dk"], out["dv"], out["dbeta"], out["dgate"],
+                    out.get("dA_log"), out.get("ddt_bias"), self.workspace)
+        else:
+            kda_bwd_state(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, s_init, dO,
+                          ds_final, saved, out["dq"], out["dk"], out["dv"], out["dbeta"],
+                          out["dgate"], out.get("dA_log"), out.get("ddt_bias"), ds_init,
+                          self.workspace)
+            if ds_init is not None:
+                out["ds_init"] = ds_init
         return out
+
+    def _summary_ws(self, device):
+        if self.summary_ws is None:
+            n = max(state_summary_workspace_bytes(self.p), 16)
+            self.summary_ws = torch.empty(n, dtype=torch.uint8, device=device)
+        return self.summary_ws
+
+    def state_summary(self, q, k, v, beta, gate, cu_seqlens, A_log=None, dt_bias=None,
+                      want_M=True, want_B=True, keep_prep=False):
+        """(M, B) fp32 [H,128,128] (None where not wanted): s_final = M s_init + B.
+        keep_prep: the prep goes to this object's saved set, for a following
+        forward(..., prep_done=True) on the same inputs."""
+        st = lambda: torch.empty(self.p.H, 128, 128, dtype=torch.float32, device=q.device)
+        M = st() if want_M else None
+        B = st() if want_B else None
+        kda_state_summary(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, M, B,
+                          self._summary_ws(q.device), self.saved if keep_prep else None)
+        return M, B
+
+    def state_grad_summary(self, q, k, v, beta, gate, cu_seqlens, dO, A_log=None, dt_bias=None,
+                           replay=False):
+        """dB fp32 [H,128,128]: ds_init with a zero ds_final, from this object's
+        saved set (a saving forward ran last) or, with replay, rebuilt."""
+        dB = torch.empty(self.p.H, 128, 128, dtype=torch.float32, device=q.device)
+        kda_state_grad_summary(self.p, q, k, v, beta, gate, A_log, dt_bias, cu_seqlens, dO,
+                               None if replay else self.saved, dB, self._summary_ws(q.device))
+        return dB
 
 
 # ---------------------------------------------------------------- conv1d + SiLU

@@ -8,6 +8,7 @@
 #include <cstdio>
 
 #include "kda.h"
+#include "kda_state.h"
 #include "kda_internal.h"
 
 namespace {
@@ -102,6 +103,18 @@ kda::SavedSet carve_saved(Carver& c, const Sizes& s) {
   sv.U = c.take<float>((size_t)s.NC * s.H * 64 * 128);
   sv.panels = c.take<uint16_t>((size_t)s.NC * s.H * kda::fwd_panel::ELEMS);
   sv.Mseg = s.L > 0 ? take_seg(c, s) : nullptr;
+  return sv;
+}
+
+// What the prep writes (the state summaries store nothing per chunk beyond it).
+kda::SavedSet carve_prep(Carver& c, const Sizes& s) {
+  kda::SavedSet sv{};
+  const size_t mat = (size_t)s.NC * s.H * 64 * 64;
+  sv.Tm = c.take<float>(mat);
+  sv.Akk = c.take<float>(mat);
+  sv.rq = c.take<float>((size_t)s.T * s.H);
+  sv.rk = c.take<float>((size_t)s.T * s.H);
+  sv.panels = c.take<uint16_t>((size_t)s.NC * s.H * kda::fwd_panel::ELEMS);
   return sv;
 }
 
@@ -247,14 +260,42 @@ size_t kda_workspace_bytes(const kda_problem* p, int backward, int replay) {
   return backward ? bwd_ws_bytes(s, replay != 0) : fwd_ws_bytes(s, replay != 0);
 }
 
-kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
-                   const void* beta, const void* g_or_a, const float* A_log,
-                   const float* dt_bias, const int32_t* cu_seqlens, void* o, void* saved,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+#define OPT_PTR(ptr, name)                                                               \
+  do {                                                                                   \
+    if ((ptr) && !aligned(ptr))                                                          \
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);          \
+  } while (0)
+
+// kda_fwd and kda_fwd_state: s_init, s_final as in kda_fwd_state (nullable).
+kda_status fwd_impl(const kda_problem* p, const void* q, const void* k, const void* v,
+                    const void* beta, const void* g_or_a, const float* A_log,
+                    const float* dt_bias, const int32_t* cu_seqlens, const float* s_init,
+                    void* o, float* s_final, void* saved, int flags, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   kda_status st = check_problem(p);
   if (st != KDA_OK) return st;
-  if (p->T == 0) return KDA_OK;
+  OPT_PTR(s_init, "s_init");
+  OPT_PTR(s_final, "s_final");
+  if (flags & ~KDA_FWD_PREP_DONE) return fail(KDA_ERR_INVALID_ARGUMENT, "unknown flags %d", flags);
+  const bool prep_done = (flags & KDA_FWD_PREP_DONE) != 0;
+  if (prep_done && !saved)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "KDA_FWD_PREP_DONE needs the saved set");
+  if (p->T == 0) {
+    // no tokens: the last document is empty; it is document 0 (entering
+    // with s_init) only when there is one document
+    if (s_final) {
+      hipStream_t hs = static_cast<hipStream_t>(stream);
+      LAUNCH("fill_states", kda::launch_fill_states(p->H, s_final, s_init,
+                                                    p->num_seqs == 1 ? kda::FILL_COPY
+                                                                     : kda::FILL_ZERO, hs));
+    }
+    return KDA_OK;
+  }
   REQUIRE_PTR(q, "q");
   REQUIRE_PTR(k, "k");
   REQUIRE_PTR(v, "v");
@@ -286,10 +327,15 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   } else {
     sv = carve_saved(wc, s);   // private per-chunk set in the workspace
   }
-  const kda::SegWork sg = carve_seg_fwd(wc, s, sv);
+  kda::SegWork sg = carve_seg_fwd(wc, s, sv);
+  sg.s_init = s_init;
+  sg.s_final = s_final;
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   LAUNCH("seg_map", kda::launch_seg_map(d, ct, hs));
-  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, saved != nullptr, hs));
+  if (!prep_done) LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, saved != nullptr, hs));
+  // an empty last document has no chain when documents are cut into
+  // segments: its leaving state is the zero it starts from
+  if (s_final) LAUNCH("fill_states", kda::launch_fill_states(p->H, s_final, nullptr, kda::FILL_ZERO, hs));
   if (d.L > 0) {
     LAUNCH("fwd_scan_summary", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, 0, sg,
                                                     kda::SCAN_SUMMARY, hs));
@@ -301,24 +347,34 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
   return KDA_OK;
 }
 
-kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
-                   const void* beta, const void* g_or_a, const float* A_log,
-                   const float* dt_bias, const int32_t* cu_seqlens, const void* dO,
-                   const void* saved, void* dq, void* dk, void* dv, void* dbeta,
-                   void* dg_or_da, float* dA_log, float* ddt_bias, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+// kda_bwd and kda_bwd_state: s_init, ds_final, ds_init as in kda_bwd_state.
+kda_status bwd_impl(const kda_problem* p, const void* q, const void* k, const void* v,
+                    const void* beta, const void* g_or_a, const float* A_log,
+                    const float* dt_bias, const int32_t* cu_seqlens, const float* s_init,
+                    const void* dO, const float* ds_final, const void* saved, void* dq,
+                    void* dk, void* dv, void* dbeta, void* dg_or_da, float* dA_log,
+                    float* ddt_bias, float* ds_init, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   g_last_error[0] = 0;
   kda_status st = check_problem(p);
   if (st != KDA_OK) return st;
+  OPT_PTR(s_init, "s_init");
+  OPT_PTR(ds_final, "ds_final");
+  OPT_PTR(ds_init, "ds_init");
   if (p->T == 0) {
+    hipStream_t hs = static_cast<hipStream_t>(stream);
     // no tokens: the raw form's parameter gradients are sums over nothing
     if (p->gate == KDA_GATE_RAW) {
       REQUIRE_PTR(dA_log, "dA_log");
       REQUIRE_PTR(ddt_bias, "ddt_bias");
       const kda::Dims d = dims_of(p);
-      hipStream_t hs = static_cast<hipStream_t>(stream);
       LAUNCH("zero_params", kda::launch_zero_params(d, dA_log, ddt_bias, hs));
     }
+    // the state passes through an empty document 0 only when it is the last
+    if (ds_init)
+      LAUNCH("fill_states", kda::launch_fill_states(p->H, ds_init, ds_final,
+                                                    p->num_seqs == 1 ? kda::FILL_COPY
+                                                                     : kda::FILL_ZERO, hs));
     return KDA_OK;
   }
   REQUIRE_PTR(q, "q");
@@ -362,9 +418,14 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
     sv = carve_saved(sc, s);
   }
   const kda::BwdOut out{dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias};
-  const kda::SegWork sg = carve_seg_bwd(wc, s, sv);
+  kda::SegWork sg = carve_seg_bwd(wc, s, sv);
+  sg.s_init = s_init;
+  sg.ds_final = ds_final;
+  sg.ds_init = ds_init;
   LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
   LAUNCH("seg_map", kda::launch_seg_map(d, ct, hs));
+  // an empty document 0 has no chain when documents are cut into segments
+  if (ds_init) LAUNCH("fill_states", kda::launch_fill_states(p->H, ds_init, nullptr, kda::FILL_ZERO, hs));
   if (replay) {
     LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, 1, hs));
     if (d.L > 0) {
@@ -383,6 +444,219 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   LAUNCH("bwd_scan", kda::launch_bwd_scan(d, in, ct, sv, dO, dv, bw, sg, kda::SCAN_FINISH, hs));
   LAUNCH("bwd_intra", kda::launch_bwd_intra(d, in, ct, sv, dO, out, bw, hs));
   if (p->gate == KDA_GATE_RAW) LAUNCH("finalize", kda::launch_finalize(d, ct, out, bw, hs));
+  return KDA_OK;
+}
+
+// The state summaries' workspace: their own chunk table and the prep's
+// outputs, with the documents never cut into segments.
+Sizes map_sizes(const kda_problem* p) {
+  Sizes s = sizes_of(p);
+  s.L = 0;
+  s.NS = s.N;
+  return s;
+}
+
+size_t table_bytes(const Sizes& s) {
+  Carver c(nullptr);
+  carve_table(c, s);
+  return c.off;
+}
+
+size_t map_ws_bytes(const Sizes& s) {
+  Carver c(nullptr);
+  carve_table(c, s);
+  carve_prep(c, s);
+  return c.off;
+}
+
+kda::Dims map_dims(const kda_problem* p) {
+  kda::Dims d = dims_of(p);
+  d.L = 0;
+  d.NS = d.N;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                   const void* beta, const void* g_or_a, const float* A_log,
+                   const float* dt_bias, const int32_t* cu_seqlens, void* o, void* saved,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, nullptr, o, nullptr,
+                  saved, 0, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_fwd_state(const kda_problem* p, const void* q, const void* k, const void* v,
+                         const void* beta, const void* g_or_a, const float* A_log,
+                         const float* dt_bias, const int32_t* cu_seqlens, const float* s_init,
+                         void* o, float* s_final, void* saved, int flags, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return fwd_impl(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, s_init, o, s_final,
+                  saved, flags, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                   const void* beta, const void* g_or_a, const float* A_log,
+                   const float* dt_bias, const int32_t* cu_seqlens, const void* dO,
+                   const void* saved, void* dq, void* dk, void* dv, void* dbeta,
+                   void* dg_or_da, float* dA_log, float* ddt_bias, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, nullptr, dO, nullptr,
+                  saved, dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias, nullptr, workspace,
+                  workspace_bytes, stream);
+}
+
+kda_status kda_bwd_state(const kda_problem* p, const void* q, const void* k, const void* v,
+                         const void* beta, const void* g_or_a, const float* A_log,
+                         const float* dt_bias, const int32_t* cu_seqlens, const float* s_init,
+                         const void* dO, const float* ds_final, const void* saved, void* dq,
+                         void* dk, void* dv, void* dbeta, void* dg_or_da, float* dA_log,
+                         float* ddt_bias, float* ds_init, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens, s_init, dO, ds_final,
+                  saved, dq, dk, dv, dbeta, dg_or_da, dA_log, ddt_bias, ds_init, workspace,
+                  workspace_bytes, stream);
+}
+
+size_t kda_state_summary_workspace_bytes(const kda_problem* p) {
+  if (check_problem(p) != KDA_OK) return 0;
+  return map_ws_bytes(map_sizes(p));
+}
+
+kda_status kda_state_summary(const kda_problem* p, const void* q, const void* k, const void* v,
+                             const void* beta, const void* g_or_a, const float* A_log,
+                             const float* dt_bias, const int32_t* cu_seqlens, float* M, float* B,
+                             void* saved, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_last_error[0] = 0;
+  kda_status st = check_problem(p);
+  if (st != KDA_OK) return st;
+  OPT_PTR(M, "M");
+  OPT_PTR(B, "B");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // more than one document: the last one starts inside the sequence from
+  // zero and does not see the entering state (M = 0); no tokens: the state
+  // passes through one document unchanged (M = I) and nothing is added
+  const int fill_M = p->num_seqs > 1 ? kda::FILL_ZERO : kda::FILL_IDENTITY;
+  if (p->T == 0) {
+    if (M) LAUNCH("fill_states", kda::launch_fill_states(p->H, M, nullptr, fill_M, hs));
+    if (B) LAUNCH("fill_states", kda::launch_fill_states(p->H, B, nullptr, kda::FILL_ZERO, hs));
+    return KDA_OK;
+  }
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(beta, "beta");
+  REQUIRE_PTR(g_or_a, "g_or_a");
+  REQUIRE_PTR(cu_seqlens, "cu_seqlens");
+  if (p->gate == KDA_GATE_RAW) {
+    REQUIRE_PTR(A_log, "A_log");
+    REQUIRE_PTR(dt_bias, "dt_bias");
+  }
+  if (saved && !aligned(saved)) return fail(KDA_ERR_INVALID_ARGUMENT, "saved is not 16-byte aligned");
+  REQUIRE_PTR(workspace, "workspace");
+  const Sizes s = map_sizes(p);
+  const size_t need = saved ? table_bytes(s) : map_ws_bytes(s);
+  if (workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+                workspace_bytes, need);
+  if (M && p->num_seqs > 1)
+    LAUNCH("fill_states", kda::launch_fill_states(p->H, M, nullptr, fill_M, hs));
+  if (!(M && p->num_seqs == 1) && !B && !saved) return KDA_OK;
+  const kda::Dims d = map_dims(p);
+  const kda::Inputs in{q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens};
+  Carver wc(workspace);
+  const kda::ChunkTable ct = carve_table(wc, s);
+  kda::SavedSet sv;
+  if (saved) {
+    // the prep goes into the caller's saved set (with the backward's panels),
+    // in the layout of kda_fwd, for a kda_fwd_state with KDA_FWD_PREP_DONE
+    Carver sc(saved);
+    sv = carve_saved(sc, sizes_of(p));
+  } else {
+    sv = carve_prep(wc, s);
+  }
+  kda::SegWork sg{};
+  sg.map_M = p->num_seqs == 1 ? M : nullptr;
+  sg.map_B = B;
+  LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
+  LAUNCH("seg_map", kda::launch_seg_map(d, ct, hs));
+  LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, saved != nullptr, hs));
+  if (!(M && p->num_seqs == 1) && !B) return KDA_OK;
+  LAUNCH("fwd_scan_map", kda::launch_fwd_scan(d, in, ct, sv, sv.panels, 0, sg, kda::SCAN_MAP, hs));
+  return KDA_OK;
+}
+
+kda_status kda_state_grad_summary(const kda_problem* p, const void* q, const void* k,
+                                  const void* v, const void* beta, const void* g_or_a,
+                                  const float* A_log, const float* dt_bias,
+                                  const int32_t* cu_seqlens, const void* dO, const void* saved,
+                                  float* dB, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  g_last_error[0] = 0;
+  kda_status st = check_problem(p);
+  if (st != KDA_OK) return st;
+  REQUIRE_PTR(dB, "dB");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // no tokens: no dO reaches the entering state
+  if (p->T == 0) {
+    LAUNCH("fill_states", kda::launch_fill_states(p->H, dB, nullptr, kda::FILL_ZERO, hs));
+    return KDA_OK;
+  }
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(beta, "beta");
+  REQUIRE_PTR(g_or_a, "g_or_a");
+  REQUIRE_PTR(cu_seqlens, "cu_seqlens");
+  REQUIRE_PTR(dO, "dO");
+  if (p->gate == KDA_GATE_RAW) {
+    REQUIRE_PTR(A_log, "A_log");
+    REQUIRE_PTR(dt_bias, "dt_bias");
+  }
+  if (saved && !aligned(saved)) return fail(KDA_ERR_INVALID_ARGUMENT, "saved is not 16-byte aligned");
+  REQUIRE_PTR(workspace, "workspace");
+  const Sizes s = map_sizes(p);
+  const size_t need = saved ? table_bytes(s) : map_ws_bytes(s);
+  if (workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+                workspace_bytes, need);
+  const kda::Dims d = map_dims(p);
+  const kda::Inputs in{q, k, v, beta, g_or_a, A_log, dt_bias, cu_seqlens};
+  Carver wc(workspace);
+  const kda::ChunkTable ct = carve_table(wc, s);
+  kda::SavedSet sv;
+  if (saved) {
+    // the saving forward's set, in its own layout
+    Carver sc(const_cast<void*>(saved));
+    sv = carve_saved(sc, sizes_of(p));
+  } else {
+    sv = carve_prep(wc, s);
+  }
+  kda::SegWork sg{};
+  sg.ds_init = dB;
+  LAUNCH("chunk_map", kda::launch_chunk_map(d, cu_seqlens, ct, hs));
+  LAUNCH("seg_map", kda::launch_seg_map(d, ct, hs));
+  if (!saved) LAUNCH("fwd_prep", kda::launch_fwd_prep(d, in, ct, sv, 1, hs));
+  LAUNCH("bwd_scan_map", kda::launch_bwd_scan(d, in, ct, sv, dO, nullptr, kda::BwdWork{}, sg,
+                                              kda::SCAN_MAP, hs));
+  return KDA_OK;
+}
+
+kda_status kda_state_apply(int32_t H, const float* M, int transpose, const float* B,
+                           const float* x, float* y, void* stream) {
+  g_last_error[0] = 0;
+  if (H < 1 || H > 65535) return fail(KDA_ERR_INVALID_ARGUMENT, "H = %d outside [1, 65535]", H);
+  if (transpose != 0 && transpose != 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "transpose must be 0 or 1");
+  REQUIRE_PTR(M, "M");
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(y, "y");
+  OPT_PTR(B, "B");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  LAUNCH("state_apply", kda::launch_state_apply(H, M, transpose, B, x, y, hs));
   return KDA_OK;
 }
 

@@ -59,10 +59,25 @@ struct SegWork {
   float* S0;     // [NS, H, 128 x 128] state entering each segment (forward walk)
   float* Brev;   // [NS, H, 128 x 128] B': dS at the segment start from a zero dS at its end
   float* D0;     // [NS, H, 128 x 128] dS at each segment's end (reverse walk)
+  // Boundary states of the packed sequence, caller layout [H][128][128]
+  // row-major (key row, value column), all nullable: the state entering
+  // document 0, the state leaving the last document, the gradient with
+  // respect to the latter, and the gradient with respect to the former.
+  const float* s_init;
+  float* s_final;
+  const float* ds_final;
+  float* ds_init;
+  // The affine map of the whole sequence, s_final = M s_init + B (caller
+  // layout, nullable): written by the forward scan in mode SCAN_MAP.
+  float* map_M;
+  float* map_B;
 };
-// Scan passes: per-chunk outputs from the walk's segment states, or the
-// segment summaries only.
-enum : int { SCAN_FINISH = 0, SCAN_SUMMARY = 1 };
+// Scan passes: per-chunk outputs from the walk's segment states, the segment
+// summaries only, or (SCAN_MAP, whole documents, nothing per chunk stored)
+// the summary of the whole sequence: forward map_M and map_B, reverse the
+// gradient entering document 0 from a zero gradient leaving the sequence,
+// written to ds_init.
+enum : int { SCAN_FINISH = 0, SCAN_SUMMARY = 1, SCAN_MAP = 2 };
 
 struct Dims {
   int64_t T;
@@ -129,6 +144,13 @@ constexpr size_t BYTES = (size_t)ELEMS * 2;  // 131584, a multiple of 16
 hipError_t launch_chunk_map(const Dims& d, const int32_t* cu, const ChunkTable& ct,
                             hipStream_t s, int block = 64);
 hipError_t launch_seg_map(const Dims& d, const ChunkTable& ct, hipStream_t s);
+// H states of 128 x 128 (caller layout): FILL_ZERO, FILL_IDENTITY, or
+// FILL_COPY of src (zero when src is null).
+enum : int { FILL_ZERO = 0, FILL_IDENTITY = 1, FILL_COPY = 2 };
+hipError_t launch_fill_states(int H, float* dst, const float* src, int mode, hipStream_t s);
+// y = (M or M^T) x + B per head (B nullable), caller layout.
+hipError_t launch_state_apply(int H, const float* M, int transpose, const float* B,
+                              const float* x, float* y, hipStream_t s);
 hipError_t launch_walk(const Dims& d, const ChunkTable& ct, const SegWork& sg, int reverse,
                        hipStream_t s);
 hipError_t launch_fwd_prep(const Dims& d, const Inputs& in, const ChunkTable& ct,

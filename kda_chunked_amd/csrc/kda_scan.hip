@@ -153,14 +153,23 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
   __shared__ ChainBuf bufB;
   __shared__ SliceBuf slice[2];
   int chain, tile;
-  if (!scan_coords((MODE == SCAN_SUMMARY ? 2 : 1) * d.NS * d.H, chain, tile)) return;
-  const int var = MODE == SCAN_SUMMARY ? chain & 1 : 0;
-  const int sh = MODE == SCAN_SUMMARY ? chain >> 1 : chain;
+  // summaries run two chains per segment: var 0 from the identity with V = 0
+  // (ending at M), var 1 from zero (ending at B)
+  constexpr bool TWO = MODE == SCAN_SUMMARY || MODE == SCAN_MAP;
+  if (!scan_coords((TWO ? 2 : 1) * d.NS * d.H, chain, tile)) return;
+  const int var = TWO ? chain & 1 : 0;
+  const bool ident = TWO && var == 0;
+  const int sh = TWO ? chain >> 1 : chain;
   const int seg = sh / d.H, h = sh % d.H;
   if (seg >= ct.seg_doc0[d.N]) return;
   const int doc = ct.seg_doc[seg];
   const int sfirst = ct.seg_doc0[doc], slast = ct.seg_doc0[doc + 1] - 1;
   if (MODE == SCAN_SUMMARY && sfirst == slast) return;
+  // the map of a whole sequence: M from document 0 when it is the only one
+  // (else M = 0, written by the host), B from the last document
+  if (MODE == SCAN_MAP &&
+      (var == 0 ? doc != 0 || d.N != 1 || !sg.map_M : doc != d.N - 1 || !sg.map_B))
+    return;
   const int dc1 = ct.doc_c0[doc + 1];
   const int c0 = d.L > 0 ? ct.doc_c0[doc] + d.L * (seg - sfirst) : ct.doc_c0[doc];
   const int c1 = d.L > 0 ? min(dc1, c0 + d.L) : dc1;
@@ -180,7 +189,12 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
   for (int m = 0; m < 8; ++m) {
     if (MODE == SCAN_FINISH && seg != sfirst && w < 2) {
       S[m] = *reinterpret_cast<const f32x4*>(sg.S0 + segoff + tile_off(m, jv >> 4));
-    } else if (MODE == SCAN_SUMMARY && var == 0) {
+    } else if (MODE == SCAN_FINISH && doc == 0 && sg.s_init && w < 2) {
+      // the caller's state entering document 0 (row-major [H][128][128])
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[m][i] = sg.s_init[((int64_t)h * HD + 16 * m + drow(i)) * HD + jv + dcol()];
+    } else if (ident) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[m][i] = 16 * m + drow(i) == jv + dcol() ? 1.f : 0.f;
     } else {
@@ -219,8 +233,8 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(cur.v + (r0 + (sl >> 2)) * VT + 16 * w + 4 * (sl & 3)));
         const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
-        // the identity variant of a segment summary takes V = 0
-        const bool vz = MODE == SCAN_SUMMARY && var == 0;
+        // the identity variant of a segment summary (and the map) takes V = 0
+        const bool vz = ident;
 #pragma unroll
         for (int i = 0; i < 4; ++i) R[rb][i] = r0 + i < n && !vz ? bf2f(xb[i]) : 0.f;
       }
@@ -361,6 +375,17 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
 #pragma unroll
     for (int m = 0; m < 8; ++m) *reinterpret_cast<f32x4*>(dst + tile_off(m, jv >> 4)) = S[m];
   }
+  // the state leaving the last document, or the sequence map's M or B, in
+  // the caller layout
+  float* leave = MODE == SCAN_MAP ? (var == 0 ? sg.map_M : sg.map_B)
+               : MODE == SCAN_FINISH && doc == d.N - 1 && seg == slast ? sg.s_final : nullptr;
+  if (leave) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        leave[((int64_t)h * HD + 16 * m + drow(i)) * HD + jv + dcol()] = S[m][i];
+  }
 }
 
 hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
@@ -369,6 +394,9 @@ hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct
   const bf16* pn = reinterpret_cast<const bf16*>(panels);
   if (mode == SCAN_SUMMARY)
     hipLaunchKernelGGL(fwd_scan_kernel<SCAN_SUMMARY>, dim3(scan_grid(2 * d.NS * d.H)),
+                       dim3(2 * FS_THREADS), 0, s, d, in, ct, sv, pn, save_R, sg);
+  else if (mode == SCAN_MAP)
+    hipLaunchKernelGGL(fwd_scan_kernel<SCAN_MAP>, dim3(scan_grid(2 * d.NS * d.H)),
                        dim3(2 * FS_THREADS), 0, s, d, in, ct, sv, pn, save_R, sg);
   else
     hipLaunchKernelGGL(fwd_scan_kernel<SCAN_FINISH>, dim3(scan_grid(d.NS * d.H)),
@@ -616,6 +644,8 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   const int doc = ct.seg_doc[seg];
   const int sfirst = ct.seg_doc0[doc], slast = ct.seg_doc0[doc + 1] - 1;
   if (MODE == SCAN_SUMMARY && sfirst == slast) return;
+  // the gradient summary of a whole sequence: document 0 only
+  if (MODE == SCAN_MAP && doc != 0) return;
   const int dc1 = ct.doc_c0[doc + 1];
   const int c0 = d.L > 0 ? ct.doc_c0[doc] + d.L * (seg - sfirst) : ct.doc_c0[doc];
   const int c1 = d.L > 0 ? min(dc1, c0 + d.L) : dc1;
@@ -682,12 +712,21 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     (&sm.ds_hi[0][0])[e] = f2bf(0.f);
     (&sm.ds_lo[0][0])[e] = f2bf(0.f);
   }
-  if (MODE == SCAN_FINISH && seg != slast) {
-    // the dS leaving this segment, from the reverse walk (rows 16 w, this tile's columns)
+  const bool tail_in = MODE == SCAN_FINISH && doc == d.N - 1 && seg == slast && sg.ds_final;
+  if (MODE == SCAN_FINISH && (seg != slast || tail_in)) {
+    // the dS leaving this segment (rows 16 w, this tile's columns): from the
+    // reverse walk, or the caller's gradient of the state leaving the last
+    // document (row-major [H][128][128])
     __syncthreads();
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      dS[nt] = *reinterpret_cast<const f32x4*>(sg.D0 + segoff + tile_off(w, (j0 >> 4) + nt));
+      if (seg != slast) {
+        dS[nt] = *reinterpret_cast<const f32x4*>(sg.D0 + segoff + tile_off(w, (j0 >> 4) + nt));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dS[nt][i] = sg.ds_final[((int64_t)h * HD + 16 * w + drow(i)) * HD + j0 + 16 * nt + dcol()];
+      }
       store_tile_t(dS[nt], DS, 16 * w, 16 * nt);
     }
   }
@@ -771,6 +810,15 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
     for (int nt = 0; nt < 2; ++nt)
       *reinterpret_cast<f32x4*>(sg.Brev + segoff + tile_off(w, (j0 >> 4) + nt)) = dS[nt];
   }
+  // the gradient with respect to the state entering document 0 (with a zero
+  // gradient leaving the sequence: its B')
+  if (MODE != SCAN_SUMMARY && doc == 0 && seg == sfirst && sg.ds_init) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sg.ds_init[((int64_t)h * HD + 16 * w + drow(i)) * HD + j0 + 16 * nt + dcol()] = dS[nt][i];
+  }
 }
 
 hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct,
@@ -781,6 +829,9 @@ hipError_t launch_bwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct
   if (mode == SCAN_SUMMARY)
     hipLaunchKernelGGL(bwd_scan_kernel<SCAN_SUMMARY>, dim3(scan_grid(d.NS * d.H)), dim3(NT_SCAN),
                        0, s, d, in, ct, sv, pdo, pdv, bw, sg);
+  else if (mode == SCAN_MAP)      // the chains of document 0 are the first H
+    hipLaunchKernelGGL(bwd_scan_kernel<SCAN_MAP>, dim3(scan_grid(d.H)), dim3(NT_SCAN), 0, s, d,
+                       in, ct, sv, pdo, pdv, bw, sg);
   else
     hipLaunchKernelGGL(bwd_scan_kernel<SCAN_FINISH>, dim3(scan_grid(d.NS * d.H)), dim3(NT_SCAN),
                        0, s, d, in, ct, sv, pdo, pdv, bw, sg);

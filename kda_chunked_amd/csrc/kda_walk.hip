@@ -72,6 +72,23 @@ KDA_DEV void stage_x(WalkSmem& sm, const f32x4 (&X)[8]) {
   }
 }
 
+// Rows 16 m + drow(i), column 16 cb + dcol() of head h's 128 x 128 state in
+// the caller layout (row-major), as D-layout tiles; zero when x is null.
+KDA_DEV void load_state(f32x4 (&X)[8], const float* x, int h, int cb) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      X[m][i] = x ? x[((int64_t)h * HD + 16 * m + drow(i)) * HD + 16 * cb + dcol()] : 0.f;
+}
+
+KDA_DEV void store_state(const f32x4 (&X)[8], float* x, int h, int cb) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[((int64_t)h * HD + 16 * m + drow(i)) * HD + 16 * cb + dcol()] = X[m][i];
+}
+
 // acc[m] += (M or M^T)[16 m .., :] X[:, this wave's columns], six split terms.
 template <bool TRANS>
 KDA_DEV void walk_product(const WalkSmem& sm, f32x4 (&acc)[8]) {
@@ -111,10 +128,12 @@ __global__ __launch_bounds__(WK_THREADS) void walk_kernel(Dims d, ChunkTable ct,
   const int cb = 4 * half + w;             // this wave's 16-column block of the state
   auto off = [&](int s) { return ((int64_t)s * d.H + h) * HD * HD; };
   f32x4 X[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) X[m] = zero4();
+  // the walk starts from zero, or from the caller's boundary state: the state
+  // entering document 0 (forward) or the gradient leaving the last document
+  const float* x0 = REV ? (doc == d.N - 1 ? sg.ds_final : nullptr) : (doc == 0 ? sg.s_init : nullptr);
+  load_state(X, x0, h, cb);
   if (!REV) {
-    // S entering segment s0 is zero; S entering s + 1 = M_s S + B_s
+    // S entering segment s0 is zero (or s_init); S entering s + 1 = M_s S + B_s
     for (int s = s0; s < s1; ++s) {
       float* dst = sg.S0 + off(s);
 #pragma unroll
@@ -130,7 +149,7 @@ __global__ __launch_bounds__(WK_THREADS) void walk_kernel(Dims d, ChunkTable ct,
       walk_product<false>(sm, X);
     }
   } else {
-    // dS leaving the last segment is zero; dS leaving s - 1 = M_s^T dS + B'_s
+    // dS leaving the last segment is zero (or ds_final); dS leaving s - 1 = M_s^T dS + B'_s
     for (int s = s1 - 1; s > s0; --s) {
       __syncthreads();
       stage_m(sm, sg.M + off(s));
@@ -145,6 +164,59 @@ __global__ __launch_bounds__(WK_THREADS) void walk_kernel(Dims d, ChunkTable ct,
       for (int m = 0; m < 8; ++m) *reinterpret_cast<f32x4*>(dst + tile_off(m, cb)) = X[m];
     }
   }
+}
+
+// y = (M or M^T) x + B for the 128 x 128 states of H heads in the caller
+// layout: the transfer step of a sequence split over ranks (flashinfer PR
+// #7176, opening section: S_out = M S_in + B, and in the backward
+// dS_in = M^T dS_out + B'), on the same six-term split products as the walks.
+// Block b: head b >> 1, column half b & 1. Every block reads its columns of x
+// and B before it writes those of y, so y may alias x or B.
+template <bool TRANS>
+__global__ __launch_bounds__(WK_THREADS) void state_apply_kernel(const float* M, const float* B,
+                                                                 const float* x, float* y) {
+  __shared__ WalkSmem sm;
+  const int h = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int cb = 4 * half + wave_id();
+  for (int v = threadIdx.x; v < HD * HD / 4; v += WK_THREADS) {
+    const int r = v >> 5, c4 = (v & 31) * 4;
+    const f32x4 t = *reinterpret_cast<const f32x4*>(M + ((int64_t)h * HD + r) * HD + c4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split3(t[i], sm.m[0][r][c4 + i], sm.m[1][r][c4 + i], sm.m[2][r][c4 + i]);
+  }
+  f32x4 X[8], acc[8];
+  load_state(X, x, h, cb);
+  load_state(acc, B, h, cb);
+  stage_x(sm, X);
+  __syncthreads();
+  walk_product<TRANS>(sm, acc);
+  store_state(acc, y, h, cb);
+}
+
+// Boundary-state fills: zero, identity, or a copy (zero from a null source).
+__global__ __launch_bounds__(256) void fill_states_kernel(int64_t n, float* dst, const float* src,
+                                                          int mode) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int r = (int)((e / HD) % HD), c = (int)(e % HD);
+    dst[e] = mode == FILL_IDENTITY ? (r == c ? 1.f : 0.f) : (mode == FILL_COPY && src ? src[e] : 0.f);
+  }
+}
+
+hipError_t launch_fill_states(int H, float* dst, const float* src, int mode, hipStream_t s) {
+  const int64_t n = (int64_t)H * HD * HD;
+  const int64_t b = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_states_kernel, dim3((unsigned)(b < 4096 ? b : 4096)), dim3(256), 0, s, n,
+                     dst, src, mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_apply(int H, const float* M, int transpose, const float* B,
+                              const float* x, float* y, hipStream_t s) {
+  if (transpose)
+    hipLaunchKernelGGL(state_apply_kernel<true>, dim3(2 * H), dim3(WK_THREADS), 0, s, M, B, x, y);
+  else
+    hipLaunchKernelGGL(state_apply_kernel<false>, dim3(2 * H), dim3(WK_THREADS), 0, s, M, B, x, y);
+  return hipGetLastError();
 }
 
 hipError_t launch_walk(const Dims& d, const ChunkTable& ct, const SegWork& sg, int reverse,

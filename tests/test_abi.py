@@ -277,3 +277,56 @@ def test_attn_fwd_binding_signature():
         import torch
         t = torch.zeros(16, dtype=torch.uint8)
         B.attn_fwd(_attn(), t, t, t, t, t, t, None, t)
+
+
+def test_state_entry_points_validate_on_the_host():
+    """The boundary-state calls of a sequence split over ranks reject bad
+    arguments before anything is enqueued (no GPU needed for these paths)."""
+    lib = B.lib()
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    err = lambda: lib.kda_last_error().decode()
+    # kda_state_apply: head count, transpose flag, pointers
+    assert lib.kda_state_apply(0, vp(16), 0, None, vp(16), vp(16), None) == 1 and "H" in err()
+    assert lib.kda_state_apply(65536, vp(16), 0, None, vp(16), vp(16), None) == 1
+    assert lib.kda_state_apply(2, vp(16), 2, None, vp(16), vp(16), None) == 1
+    assert "transpose" in err()
+    assert lib.kda_state_apply(2, None, 0, None, vp(16), vp(16), None) == 1 and "M is NULL" in err()
+    assert lib.kda_state_apply(2, vp(16), 1, vp(24), vp(16), vp(16), None) == 1
+    assert "B is not 16-byte aligned" in err()
+    # kda_state_summary / kda_state_grad_summary: problem, outputs, workspace
+    assert B.state_summary_workspace_bytes(_p(H=0)) == 0
+    assert B.state_summary_workspace_bytes(_p()) > 0
+    ptrs = [vp(16)] * 8
+    summ = lambda p, *a: lib.kda_state_summary(ctypes.byref(p), *a)
+    assert summ(_p(H=0), *ptrs, vp(16), vp(16), None, vp(16), 1 << 40, None) == 1
+    assert summ(_p(), *ptrs, vp(20), None, None, vp(16), 1 << 40, None) == 1
+    assert "M is not 16-byte aligned" in err()
+    assert summ(_p(), *ptrs, vp(16), vp(16), None, vp(16), 100, None) == 3 and "workspace" in err()
+    assert summ(_p(), *ptrs, vp(16), vp(16), vp(40), vp(16), 100, None) == 1 and "saved" in err()
+    rc = summ(_p(), *([vp(16)] * 7), None, vp(16), vp(16), None, vp(16), 1 << 40, None)
+    assert rc == 1 and "cu_seqlens is NULL" in err()
+    rc = lib.kda_state_grad_summary(ctypes.byref(_p()), *ptrs, vp(16), None, None, vp(16),
+                                    1 << 40, None)
+    assert rc == 1 and "dB is NULL" in err()
+    rc = lib.kda_state_grad_summary(ctypes.byref(_p()), *ptrs, None, None, vp(16), vp(16),
+                                    1 << 40, None)
+    assert rc == 1 and "dO is NULL" in err()
+    rc = lib.kda_state_grad_summary(ctypes.byref(_p()), *ptrs, vp(16), vp(24), vp(16), vp(16),
+                                    1 << 40, None)
+    assert rc == 1 and "saved" in err()
+    rc = lib.kda_state_grad_summary(ctypes.byref(_p()), *ptrs, vp(16), None, vp(16), vp(16), 64,
+                                    None)
+    assert rc == 3 and "workspace" in err()
+    # kda_fwd_state / kda_bwd_state: the boundary states' alignment
+    fs = lambda *a: lib.kda_fwd_state(ctypes.byref(_p()), *ptrs, *a)
+    assert fs(vp(40), vp(16), vp(16), vp(16), 0, vp(16), 1 << 40, None) == 1 and "s_init" in err()
+    assert fs(None, vp(16), vp(20), vp(16), 0, vp(16), 1 << 40, None) == 1 and "s_final" in err()
+    assert fs(None, vp(16), None, vp(16), 4, vp(16), 1 << 40, None) == 1 and "flags" in err()
+    assert fs(None, vp(16), None, None, 1, vp(16), 1 << 40, None) == 1 and "saved" in err()
+    bw = [vp(16)] * 8
+    rc = lib.kda_bwd_state(ctypes.byref(_p()), *bw, None, vp(16), vp(36), None, *([vp(16)] * 7),
+                           None, vp(16), 1 << 40, None)
+    assert rc == 1 and "ds_final" in err()
+    rc = lib.kda_bwd_state(ctypes.byref(_p()), *bw, None, vp(16), None, None, *([vp(16)] * 7),
+                           vp(52), vp(16), 1 << 40, None)
+    assert rc == 1 and "ds_init" in err()
