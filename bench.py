@@ -157,7 +157,10 @@ def end_to_end(ms_step: float, T: int, H: int, raw: bool) -> dict:
 
 
 class HipEvents:
-    """Per-kernel HIP event pairs recorded from the library's launch hook."""
+    """Per-kernel HIP event pairs recorded from the library's launch hook.
+    The events are created beforehand (`reserve`): creating one can take long
+    enough, on some hosts, for the launching thread to fall behind the GPU
+    inside the timed region."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
@@ -169,12 +172,19 @@ class HipEvents:
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.records = []      # (kernel, start_event, end_event)
         self.open = {}
+        self.pool = []
 
-    def _event(self):
+    def _create(self):
         e = ctypes.c_void_p()
         if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
             raise RuntimeError("hipEventCreate failed")
         return e
+
+    def reserve(self, n):
+        self.pool.extend(self._create() for _ in range(n))
+
+    def _event(self):
+        return self.pool.pop() if self.pool else self._create()
 
     def hook(self, name, end, stream):
         ev = self._event()
@@ -195,7 +205,20 @@ class HipEvents:
             self.hip.hipEventDestroy(a)
             self.hip.hipEventDestroy(b)
         self.records = []
+        for e in self.pool:
+            self.hip.hipEventDestroy(e)
+        self.pool = []
         return out
+
+
+class LaunchCounter:
+    """Counts the library's launches (a hook that records nothing)."""
+
+    def __init__(self):
+        self.n = 0
+
+    def hook(self, name, end, stream):
+        self.n += 1
 
 
 def fingerprint() -> str:
@@ -623,7 +646,13 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, per-kernel HIP events from the hook
+    counter = LaunchCounter()
+    set_launch_hook(counter.hook)
+    step()
+    set_launch_hook(None)
+    torch.cuda.synchronize()
     ev = HipEvents()
+    ev.reserve(counter.n * args.steps + 16)
     set_launch_hook(ev.hook)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
