@@ -712,7 +712,7 @@ def main():
             fig["mfma_flop"] / sec / 1e12, 2) if "mfma_flop" in fig else None
 
     rows = {}
-    conv = attn = None
+    conv = attn = cp = None
     if not args.no_rows:
         for name, replay in SECONDARY_ROWS:
             if name == w.name:
@@ -720,6 +720,7 @@ def main():
             rows.update(time_row(I.BY_NAME[name], replay, torch))
         conv = time_conv(torch)
         attn = time_attn(torch)
+        cp = time_cp(torch)
 
     line = {
         "metric": METRIC,
@@ -756,6 +757,8 @@ def main():
         line["conv1d_silu"] = conv
     if attn:
         line["gqa_attention"] = attn
+    if cp:
+        line["kda_cp_rank_share"] = cp
     if not args.no_cpu:
         from oracle import kda_oracle as ko
         line["cpu_baseline"] = cpu_baseline(w, inp, ko.default_threads())
