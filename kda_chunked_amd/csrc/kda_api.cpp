@@ -151,6 +151,13 @@ kda_status check_problem(const kda_problem* p) {
       return fail(KDA_ERR_UNSUPPORTED, "num_seqs * H = %lld (document, head) pairs exceeds 2^29",
                   (long long)pairs);
   }
+  {
+    // the per-chunk backward launches one workgroup per (chunk, head)
+    const int64_t chunk_heads = (p->T / 64 + p->num_seqs) * (int64_t)p->H;
+    if (chunk_heads >= ((int64_t)1 << 31))
+      return fail(KDA_ERR_UNSUPPORTED, "%lld (chunk, head) pairs exceed 2^31 workgroups",
+                  (long long)chunk_heads);
+  }
   if (p->dk != 128 || p->dv != 128)
     return fail(KDA_ERR_UNSUPPORTED, "dk = %d, dv = %d: this build serves 128, 128", p->dk,
                 p->dv);

@@ -136,7 +136,14 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
                                                           const bf16* __restrict__ dO,
                                                           BwdOut out, BwdWork bw) {
   __shared__ BwdIntraSmem sm;
-  const int ci = blockIdx.x, h = blockIdx.y;
+  // Workgroup b: chunk b / H, head b % H. With the heads fastest, the
+  // workgroups resident at one time cover a few whole chunks of every head,
+  // so their rows of the [T, H, .] tensors and their blocks of the per
+  // chunk-head sets are contiguous in memory (with the chunks fastest they
+  // were 16 KiB to 4 MiB apart): 2.16 -> 1.90 ms at 16384 tokens x 64 heads.
+  // readfirstlane keeps the quotient in scalar registers.
+  const int ci = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)d.H));
+  const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x - (unsigned)ci * (unsigned)d.H));
   if (ci >= ct.doc_c0[d.N]) return;
   const int64_t t0 = ct.tok[ci];
   const int n = ct.len[ci];
@@ -985,7 +992,8 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 hipError_t launch_bwd_intra(const Dims& d, const Inputs& in, const ChunkTable& ct,
                             const SavedSet& sv, const void* dO, const BwdOut& out,
                             const BwdWork& bw, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_intra_kernel, dim3(d.NC, d.H), dim3(NTHR), 0, s, d, in, ct, sv,
+  hipLaunchKernelGGL(bwd_intra_kernel, dim3((unsigned)((int64_t)d.NC * d.H)), dim3(NTHR), 0, s,
+                     d, in, ct, sv,
                      reinterpret_cast<const bf16*>(dO), out, bw);
   return hipGetLastError();
 }

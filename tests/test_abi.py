@@ -98,6 +98,7 @@ def _fwd_status(p, **ptrs):
     (dict(dv=256), 2, "128"),
     (dict(H=65536), 2, "65535"),
     (dict(H=65535, num_seqs=1 << 14), 2, "2^29"),
+    (dict(T=1 << 30, H=1024), 2, "2^31"),
 ])
 def test_invalid_problem_rejected_before_launch(kw, status, msg):
     rc, err = _fwd_status(_p(**kw))
