@@ -75,7 +75,8 @@ KDA_DEV float bsel(bool ok, bf16 x) { return ok ? bf2f(x) : 0.f; }
 // Two compute waves, one per 16-column slice: each runs the whole chain of
 // its slice by itself,
 //   R = V - Kd S_in,  U~ = Tb R,  S_out = e^(G_last) * S_in + Ke^T U~,
-// exchanging operands only through its own LDS area. Two copy waves (on the
+// with the right operands of its products in registers (fragK*). Two copy
+// waves (on the
 // compute unit's other two SIMDs) bring the chunk's shared operands (-Kd, Tb,
 // Ke^T, e^(G_last): the first fwd_panel::CHAIN elements of its panels) and
 // its V rows global -> registers -> LDS (16-byte units): registers two chunks
@@ -101,11 +102,6 @@ struct __attribute__((aligned(16))) ChainBuf {
   float gam[HD];
   bf16 v[CL * VT];           // V    [r][j] of the workgroup's 32 columns, row 64 B
 };
-struct __attribute__((aligned(16))) SliceBuf {            // one wave's B operands
-  bf16 s_hi[16][K1_LD];                      // S^T [j][c]
-  bf16 r_hi[16][K2_LD], r_lo[16][K2_LD];     // R^T [j][r]
-  bf16 u_hi[16][K2_LD], u_lo[16][K2_LD];     // U~^T [j][r]
-};
 
 KDA_DEV int swz256(int row, int kc) { return row * 128 + ((kc ^ (row & 15)) << 3); }
 KDA_DEV int swz128(int row, int kc) { return row * 64 + ((kc ^ ((row >> 1) & 7)) << 3); }
@@ -118,6 +114,45 @@ KDA_DEV bf16x8 frag256(const bf16* p, int m0, int k) {
 KDA_DEV bf16x8 frag128(const bf16* p, int m0, int k) {
   const int l = lane_id(), row = m0 + (l & 15);
   return *reinterpret_cast<const bf16x8*>(p + swz128(row, (k >> 3) + (l >> 4)));
+}
+
+// The chain's B operands stay in registers. A 32-row K block of a product is
+// two D tiles of the right operand, and lane l holds rows 4 (l / 16) .. + 3 of
+// each: taken as they are, lane group g supplies K slots 8 g .. 8 g + 7 =
+// rows k + 4 g .. + 3 of the first tile and k + 16 + 4 g .. + 3 of the second.
+// The A fragment is read in that K order (two 8-byte pieces per lane), so the
+// products are the same sums, formed without an LDS round trip.
+KDA_DEV bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+KDA_DEV bf16x8 fragK256(const bf16* p, int m0, int k) {
+  const int l = lane_id(), row = m0 + (l & 15), c0 = k + 4 * (l >> 4), c1 = c0 + 16;
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p + swz256(row, c0 >> 3) + (c0 & 7));
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + swz256(row, c1 >> 3) + (c1 & 7));
+  return cat44(a, b);
+}
+KDA_DEV bf16x8 fragK128(const bf16* p, int m0, int k) {
+  const int l = lane_id(), row = m0 + (l & 15), c0 = k + 4 * (l >> 4), c1 = c0 + 16;
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p + swz128(row, c0 >> 3) + (c0 & 7));
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + swz128(row, c1 >> 3) + (c1 & 7));
+  return cat44(a, b);
+}
+// B operand of the K block made of D tiles x0 (first 16 rows) and x1: hi
+// planes, and the lo planes (x - hi) when wanted.
+KDA_DEV bf16x8 bpair_hi(const f32x4& x0, const f32x4& x1) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = f2bf(x0[i]), r[4 + i] = f2bf(x1[i]);
+  return r;
+}
+KDA_DEV void bpair(const f32x4& x0, const f32x4& x1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = f2bf(x0[i]);
+    hi[4 + i] = f2bf(x1[i]);
+    lo[i] = f2bf(x0[i] - bf2f(hi[i]));
+    lo[4 + i] = f2bf(x1[i] - bf2f(hi[4 + i]));
+  }
 }
 
 // Source element (in the chunk's panels) of chain unit u = t + 128 k; the
@@ -151,7 +186,6 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
                                                                int save_R, SegWork sg) {
   __shared__ ChainBuf bufA;
   __shared__ ChainBuf bufB;
-  __shared__ SliceBuf slice[2];
   int chain, tile;
   // summaries run two chains per segment: var 0 from the identity with V = 0
   // (ending at M), var 1 from zero (ending at B)
@@ -177,10 +211,6 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
   const int jv = tile * VT + 16 * (w & 1);    // a compute wave's 16 state columns
   const int H = d.H;
   const bf16* v = reinterpret_cast<const bf16*>(in.v);
-  SliceBuf& sb = slice[w & 1];
-  const Panel SB{&sb.s_hi[0][0], nullptr, K1_LD};
-  const Panel RB{&sb.r_hi[0][0], &sb.r_lo[0][0], K2_LD};
-  const Panel UB{&sb.u_hi[0][0], &sb.u_lo[0][0], K2_LD};
 
   // state slice: tile m holds rows 16 m .. 16 m + 15 (D layout)
   f32x4 S[8];
@@ -239,54 +269,48 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
         for (int i = 0; i < 4; ++i) R[rb][i] = r0 + i < n && !vz ? bf2f(xb[i]) : 0.f;
       }
     }
-    // S_in: to memory and, as B operand, to this wave's LDS
-    {
+    // S_in to memory (streamed out, non-temporal: read only by later kernels)
+    if (MODE == SCAN_FINISH) {
       float* Sg = sv.S_in + ch * HD * HD;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        // streamed out (non-temporal): read only by later kernels
-        if (MODE == SCAN_FINISH)
-          __builtin_nontemporal_store(S[m], reinterpret_cast<f32x4*>(Sg + tile_off(m, jv >> 4)));
-        store_tile_t(S[m], SB, 16 * m, 0);
-      }
+      for (int m = 0; m < 8; ++m)
+        __builtin_nontemporal_store(S[m], reinterpret_cast<f32x4*>(Sg + tile_off(m, jv >> 4)));
     }
     // R = V - Kd S_in (the panel holds -Kd)
 #pragma unroll
-    for (int k = 0; k < HD; k += 32) {
-      const bf16x8 b = frag(SB.hi, SB.ld, 0, k);
+    for (int kb = 0; kb < HD / 32; ++kb) {
+      const bf16x8 b = bpair_hi(S[2 * kb], S[2 * kb + 1]);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) R[rb] = mfma16(frag256(cur.kd, 16 * rb, k), b, R[rb]);
+      for (int rb = 0; rb < 4; ++rb) R[rb] = mfma16(fragK256(cur.kd, 16 * rb, 32 * kb), b, R[rb]);
     }
+    if (MODE == SCAN_FINISH && save_R) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if (MODE == SCAN_FINISH && save_R)
+      for (int rb = 0; rb < 4; ++rb)
         __builtin_nontemporal_store(
             R[rb], reinterpret_cast<f32x4*>(sv.R + ch * CL * HD + tile_off(rb, jv >> 4)));
-      store_tile_t(R[rb], RB, 16 * rb, 0);
     }
     // U~ = Tb R (Tb lower triangular: K up to the end of the row block)
     f32x4 U[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) U[rb] = zero4();
 #pragma unroll
-    for (int k = 0; k < CL; k += 32) {
-      const bf16x8 bh = frag(RB.hi, RB.ld, 0, k);
-      const bf16x8 bl = frag(RB.lo, RB.ld, 0, k);
+    for (int kb = 0; kb < CL / 32; ++kb) {
+      bf16x8 bh, bl;
+      bpair(R[2 * kb], R[2 * kb + 1], bh, bl);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        if (k < 16 * rb + 16) {
-          const bf16x8 a = frag128(cur.tb, 16 * rb, k);
+        if (32 * kb < 16 * rb + 16) {
+          const bf16x8 a = fragK128(cur.tb, 16 * rb, 32 * kb);
           U[rb] = mfma16(a, bl, U[rb]);
           U[rb] = mfma16(a, bh, U[rb]);
         }
       }
     }
+    if (MODE == SCAN_FINISH) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if (MODE == SCAN_FINISH)
+      for (int rb = 0; rb < 4; ++rb)
         __builtin_nontemporal_store(
             U[rb], reinterpret_cast<f32x4*>(sv.U + ch * CL * HD + tile_off(rb, jv >> 4)));
-      store_tile_t(U[rb], UB, 16 * rb, 0);
     }
     // S_out = e^(G_last) * S_in + Ke^T U~
 #pragma unroll
@@ -294,13 +318,13 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[m][i] *= cur.gam[16 * m + drow(i)];
 #pragma unroll
-    for (int k = 0; k < CL; k += 32) {
-      const bf16x8 bh = frag(UB.hi, UB.ld, 0, k);
-      const bf16x8 bl = frag(UB.lo, UB.ld, 0, k);
+    for (int kb = 0; kb < CL / 32; ++kb) {
+      bf16x8 bh, bl;
+      bpair(U[2 * kb], U[2 * kb + 1], bh, bl);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const bf16x8 ah = frag128(cur.ke[0], 16 * m, k);
-        const bf16x8 al = frag128(cur.ke[1], 16 * m, k);
+        const bf16x8 ah = fragK128(cur.ke[0], 16 * m, 32 * kb);
+        const bf16x8 al = fragK128(cur.ke[1], 16 * m, 32 * kb);
         S[m] = mfma16(al, bh, S[m]);
         S[m] = mfma16(ah, bl, S[m]);
         S[m] = mfma16(ah, bh, S[m]);
