@@ -144,9 +144,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   // readfirstlane keeps the quotient in scalar registers.
   const int ci = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)d.H));
   const int h = __builtin_amdgcn_readfirstlane((int)(blockIdx.x - (unsigned)ci * (unsigned)d.H));
-  if (ci >= ct.doc_c0[d.N]) return;
-  const int64_t t0 = ct.tok[ci];
-  const int n = ct.len[ci];
+  if (ci >= ld_const(ct.doc_c0, d.N)) return;
+  const int64_t t0 = ld_const(ct.tok, ci);
+  const int n = ld_const(ct.len, ci);
   const int t = threadIdx.x, w = wave_id(), l = lane_id();
   const int rb = w & 3, chh = w >> 2;          // row block, channel half
   const int64_t ch = (int64_t)ci * d.H + h;
@@ -1008,7 +1008,7 @@ __global__ __launch_bounds__(FIN_SL * HD) void finalize_kernel(Dims d, ChunkTabl
   __shared__ float rdt[FIN_SL][HD];
   __shared__ float rA[FIN_SL * HD / 64];
   const int h = blockIdx.x, t = threadIdx.x, c = t & (HD - 1), sl = t >> 7;
-  const int nch = ct.doc_c0[d.N];
+  const int nch = ld_const(ct.doc_c0, d.N);
   const int64_t stride = (int64_t)FIN_SL * d.H * HD;
   const float* p = bw.part_dt + ((int64_t)sl * d.H + h) * HD + c;
   float s0 = 0.f, s1 = 0.f;

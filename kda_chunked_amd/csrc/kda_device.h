@@ -48,6 +48,25 @@ KDA_DEV bf16 f2bf(float x) { return (bf16)x; }  // round to nearest even
 // exp(x) through the hardware base-2 exponential.
 KDA_DEV float fexp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 
+// A global load at a 32-bit byte offset from a base pointer that is the same
+// for every lane: the address is the base (scalar registers) plus the
+// zero-extended offset, so a lane needs no 64-bit multiply for it. Offsets
+// within one chunk's rows of a [T, H, 128] tensor stay below 2^32 bytes for
+// every head count the library accepts (at most 65535).
+template <class T>
+KDA_DEV T ld_at(const T* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+// A read of data that no kernel in flight writes (the chunk table), through
+// the constant address space: at a uniform index it becomes a scalar load,
+// whose value lands in scalar registers without a wait on the vector memory
+// counter (which would also wait for every vector load issued before it).
+template <class T>
+KDA_DEV T ld_const(const T* p, int i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 // An LDS operand panel: hi and lo bf16 planes, `ld` elements per row.
 struct Panel {
   bf16* hi;

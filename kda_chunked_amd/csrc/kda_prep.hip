@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
                                                             SavedSet sv, bf16* __restrict__ panels,
                                                             int with_lo) {
   __shared__ PrepSmem sm;
-  const int h = blockIdx.y, nch = ct.doc_c0[d.N];
+  const int h = blockIdx.y, nch = ld_const(ct.doc_c0, d.N);
   const int t = threadIdx.x, w = wave_id(), l = lane_id();
   const int H = d.H;
   const bf16* q = reinterpret_cast<const bf16*>(in.q);
@@ -265,42 +265,42 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   float g[16], eg[16];
   bf16 ga[16];
   bf16 bt = f2bf(0.f);
+  // Addresses: the chunk's first row is a base common to the workgroup; a
+  // lane adds its row (clamped to the last one) times the row stride H * HD as
+  // a 32-bit byte offset, so the 16 gate rows cost an add and a min each.
   auto load_raw = [&](int64_t u0, int un) {
-    const int64_t baseA = ((u0 + (rA < un ? rA : un - 1)) * H + h) * HD + cA;
-    q0 = *reinterpret_cast<const bf16x8*>(q + baseA);
-    q1 = *reinterpret_cast<const bf16x8*>(q + baseA + 8);
-    k0 = *reinterpret_cast<const bf16x8*>(k + baseA);
-    k1 = *reinterpret_cast<const bf16x8*>(k + baseA + 8);
+    const int64_t cbase = (u0 * H + h) * HD;
+    const uint32_t rs = (uint32_t)H * HD;     // elements from one row to the next
+    const uint32_t oA = ((uint32_t)(rA < un ? rA : un - 1) * rs + cA) * 2u;
+    q0 = ld_at(reinterpret_cast<const bf16x8*>(q + cbase), oA);
+    q1 = ld_at(reinterpret_cast<const bf16x8*>(q + cbase), oA + 16u);
+    k0 = ld_at(reinterpret_cast<const bf16x8*>(k + cbase), oA);
+    k1 = ld_at(reinterpret_cast<const bf16x8*>(k + cbase), oA + 16u);
+    const uint32_t o0 = 16u * qG * rs + cG, olast = (uint32_t)(un - 1) * rs + cG;
     if (!RAW) {
-      const float* gp = reinterpret_cast<const float*>(in.gate);
+      const float* gp = reinterpret_cast<const float*>(in.gate) + cbase;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = 16 * qG + j;
-        g[j] = gp[((u0 + (r < un ? r : un - 1)) * H + h) * HD + cG];
-      }
+      for (int j = 0; j < 16; ++j) g[j] = ld_at(gp, 4u * min(o0 + j * rs, olast));
     } else {
-      const bf16* ap = reinterpret_cast<const bf16*>(in.gate);
+      const bf16* ap = reinterpret_cast<const bf16*>(in.gate) + cbase;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = 16 * qG + j;
-        ga[j] = ap[((u0 + (r < un ? r : un - 1)) * H + h) * HD + cG];
-      }
+      for (int j = 0; j < 16; ++j) ga[j] = ld_at(ap, 2u * min(o0 + j * rs, olast));
     }
-    if (t < CL) bt = beta[(u0 + (t < un ? t : un - 1)) * H + h];
+    if (t < CL) bt = ld_at(beta + u0 * H + h, 2u * (uint32_t)(t < un ? t : un - 1) * (uint32_t)H);
   };
   int ci = blockIdx.x;
   if (ci >= nch) return;
   const int gx = gridDim.x;
-  int64_t t0 = ct.tok[ci];
-  int n = ct.len[ci];
+  int64_t t0 = ld_const(ct.tok, ci);
+  int n = ld_const(ct.len, ci);
   load_raw(t0, n);
   // raw gate parameters of this head and thread channel cG
   const float ea = RAW ? __expf(in.A_log[h]) : 0.f;
   const float dtb = RAW ? in.dt_bias[h * HD + cG] : 0.f;
   // table entry of the next chunk this workgroup takes (the last chunk when
   // there is none: its loads are then repeated, never used)
-  int64_t nt0 = ct.tok[min(ci + gx, nch - 1)];
-  int nn = ct.len[min(ci + gx, nch - 1)];
+  int64_t nt0 = ld_const(ct.tok, min(ci + gx, nch - 1));
+  int nn = ld_const(ct.len, min(ci + gx, nch - 1));
   // nothing is in flight when the loop is entered, so the waits counted at
   // its top follow the steady state (loads requested before the stores of
   // the previous chunk) and not the shorter entry path
@@ -655,8 +655,8 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   // the next chunk's raw inputs, in flight during the solve and the writes,
   // and the table entry of the chunk after it
   load_raw(nt0, nn);
-  const int64_t nt0b = ct.tok[min(ci + 2 * gx, nch - 1)];
-  const int nnb = ct.len[min(ci + 2 * gx, nch - 1)];
+  const int64_t nt0b = ld_const(ct.tok, min(ci + 2 * gx, nch - 1));
+  const int nnb = ld_const(ct.len, min(ci + 2 * gx, nch - 1));
 
   // ---- 4. T = (I + Diag(beta) A_kk)^-1 by 16x16 blocks, fp32
   float (*Tm)[F_LD] = sm.Tm;

@@ -195,17 +195,17 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
   const bool ident = TWO && var == 0;
   const int sh = TWO ? chain >> 1 : chain;
   const int seg = sh / d.H, h = sh % d.H;
-  if (seg >= ct.seg_doc0[d.N]) return;
-  const int doc = ct.seg_doc[seg];
-  const int sfirst = ct.seg_doc0[doc], slast = ct.seg_doc0[doc + 1] - 1;
+  if (seg >= ld_const(ct.seg_doc0, d.N)) return;
+  const int doc = ld_const(ct.seg_doc, seg);
+  const int sfirst = ld_const(ct.seg_doc0, doc), slast = ld_const(ct.seg_doc0, doc + 1) - 1;
   if (MODE == SCAN_SUMMARY && sfirst == slast) return;
   // the map of a whole sequence: M from document 0 when it is the only one
   // (else M = 0, written by the host), B from the last document
   if (MODE == SCAN_MAP &&
       (var == 0 ? doc != 0 || d.N != 1 || !sg.map_M : doc != d.N - 1 || !sg.map_B))
     return;
-  const int dc1 = ct.doc_c0[doc + 1];
-  const int c0 = d.L > 0 ? ct.doc_c0[doc] + d.L * (seg - sfirst) : ct.doc_c0[doc];
+  const int dc1 = ld_const(ct.doc_c0, doc + 1);
+  const int c0 = ld_const(ct.doc_c0, doc) + (d.L > 0 ? d.L * (seg - sfirst) : 0);
   const int c1 = d.L > 0 ? min(dc1, c0 + d.L) : dc1;
   const int t = threadIdx.x, w = wave_id();
   const int jv = tile * VT + 16 * (w & 1);    // a compute wave's 16 state columns
@@ -235,8 +235,8 @@ __global__ __launch_bounds__(2 * FS_THREADS) void fwd_scan_kernel(Dims d, Inputs
   // from the document's first token and end.
   int64_t tokA = 0, tEnd = 0;
   if (c0 < c1) {
-    tokA = ct.tok[c0];
-    tEnd = (int64_t)ct.tok[c1 - 1] + ct.len[c1 - 1];
+    tokA = ld_const(ct.tok, c0);
+    tEnd = (int64_t)ld_const(ct.tok, c1 - 1) + ld_const(ct.len, c1 - 1);
   }
   auto rows_in = [&](int cn, int64_t& t0, int& n) {
     t0 = tokA + (int64_t)CL * (cn - c0);
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Dims d, ChunkTable ct,
                                                        const bf16* __restrict__ panels,
                                                        bf16* __restrict__ o) {
   __shared__ FwdOutSmem sm;
-  const int h = blockIdx.y, nch = ct.doc_c0[d.N];
+  const int h = blockIdx.y, nch = ld_const(ct.doc_c0, d.N);
   const int H = d.H;
   const Panel SP{&sm.s_hi[0][0], &sm.s_lo[0][0], K1_LD};
   const Panel UP{&sm.u_hi[0][0], &sm.u_lo[0][0], K2_LD};
@@ -483,8 +483,8 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Dims d, ChunkTable ct,
   int ci = blockIdx.x;
   if (ci >= nch) return;
   const int gx = gridDim.x;
-  int64_t t0 = ct.tok[ci];
-  int n = ct.len[ci];
+  int64_t t0 = ld_const(ct.tok, ci);
+  int n = ld_const(ct.len, ci);
   // O of a chunk leaves through sm.ot after the barrier that follows its
   // products: thread t writes row t / 8, columns 16 (t % 8) .. + 15
   auto store_o = [&](int64_t ot0, int on) {
@@ -524,8 +524,8 @@ __global__ __launch_bounds__(512) void fwd_out_kernel(Dims d, ChunkTable ct,
     // the next chunk's operands and table entry, requested on every path
     // (the last chunk reloads itself)
     const int cn = min(ci + gx, nch - 1);
-    const int64_t nt0 = ct.tok[cn];
-    const int nn = ct.len[cn];
+    const int64_t nt0 = ld_const(ct.tok, cn);
+    const int nn = ld_const(ct.len, cn);
     load_chunk(cn);
     f32x4 acc[4];
 #pragma unroll
@@ -664,14 +664,14 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   int chain, tile;
   if (!scan_coords(d.NS * d.H, chain, tile)) return;
   const int seg = chain / d.H, h = chain % d.H;
-  if (seg >= ct.seg_doc0[d.N]) return;
-  const int doc = ct.seg_doc[seg];
-  const int sfirst = ct.seg_doc0[doc], slast = ct.seg_doc0[doc + 1] - 1;
+  if (seg >= ld_const(ct.seg_doc0, d.N)) return;
+  const int doc = ld_const(ct.seg_doc, seg);
+  const int sfirst = ld_const(ct.seg_doc0, doc), slast = ld_const(ct.seg_doc0, doc + 1) - 1;
   if (MODE == SCAN_SUMMARY && sfirst == slast) return;
   // the gradient summary of a whole sequence: document 0 only
   if (MODE == SCAN_MAP && doc != 0) return;
-  const int dc1 = ct.doc_c0[doc + 1];
-  const int c0 = d.L > 0 ? ct.doc_c0[doc] + d.L * (seg - sfirst) : ct.doc_c0[doc];
+  const int dc1 = ld_const(ct.doc_c0, doc + 1);
+  const int c0 = ld_const(ct.doc_c0, doc) + (d.L > 0 ? d.L * (seg - sfirst) : 0);
   const int c1 = d.L > 0 ? min(dc1, c0 + d.L) : dc1;
   const int64_t segoff = ((int64_t)seg * d.H + h) * HD * HD;
   const int t = threadIdx.x, w = wave_id();
@@ -701,8 +701,8 @@ __global__ __launch_bounds__(NT_SCAN) void bwd_scan_kernel(Dims d, Inputs in, Ch
   // from the document's first token and end.
   int64_t tokA = 0, tEnd = 0;
   if (c0 < c1) {
-    tokA = ct.tok[c0];
-    tEnd = (int64_t)ct.tok[c1 - 1] + ct.len[c1 - 1];
+    tokA = ld_const(ct.tok, c0);
+    tEnd = (int64_t)ld_const(ct.tok, c1 - 1) + ld_const(ct.len, c1 - 1);
   }
   auto units = [&](int cn, int klo, int khi) {
     const bf16* src = BP + ((int64_t)cn * H + h) * fwd_panel::ELEMS + 8 * t;

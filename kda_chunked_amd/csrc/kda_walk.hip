@@ -122,7 +122,7 @@ __global__ __launch_bounds__(WK_THREADS) void walk_kernel(Dims d, ChunkTable ct,
   const int half = blockIdx.x & 1, pair = blockIdx.x >> 1;
   const int doc = pair / d.H, h = pair % d.H;
   if (doc >= d.N) return;
-  const int s0 = ct.seg_doc0[doc], s1 = ct.seg_doc0[doc + 1];
+  const int s0 = ld_const(ct.seg_doc0, doc), s1 = ld_const(ct.seg_doc0, doc + 1);
   if (s1 - s0 < 2) return;
   const int w = wave_id();
   const int cb = 4 * half + w;             // this wave's 16-column block of the state
