@@ -162,6 +162,13 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   const float* Akk_g = sv.Akk + ch * CL * CL;
   auto rowidx = [&](int r) -> int64_t { return (t0 + r) * H + h; };
   auto clampr = [&](int r) -> int { return r < n ? r : n - 1; };
+  // Row addressing of the [T, H, 128] tensors: the chunk's first row of this
+  // head is a base common to the workgroup (scalar registers); a lane adds
+  // row r times the stride H * 128 as a 32-bit element offset (below 2^31
+  // for every head count the library accepts), so no lane does 64-bit math.
+  const int64_t row0 = (t0 * H + h) * HD;
+  const uint32_t rs = (uint32_t)H * HD;
+  auto eoff = [&](int r, int c) -> uint32_t { return (uint32_t)r * rs + (uint32_t)c; };
 
   // ------------------------------------------------------------ P0: setup
   // this thread's elements: rows er(i) = 16 rb + drow(i), channels ec(nt) = 64 chh + 16 nt + dcol()
@@ -202,8 +209,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   // The setup's own loads go out first: memory counters complete in order,
   // so P2's inputs, requested after them, stay in flight while it waits.
   const int r64 = clampr(t & (CL - 1));
-  const bf16 ld_b = beta[rowidx(r64)];
-  const float ld_rq = sv.rq[rowidx(r64)], ld_rk = sv.rk[rowidx(r64)];
+  const uint32_t ob = (uint32_t)r64 * (uint32_t)H;
+  const bf16 ld_b = ld_at(beta + rowidx(0), 2u * ob);
+  const float ld_rq = ld_at(sv.rq + rowidx(0), 4u * ob), ld_rk = ld_at(sv.rk + rowidx(0), 4u * ob);
   // G, the chunk-local inclusive cumsum of g, rebuilt from the gate input in
   // the forward prep's order (so it is the same G, bit for bit): thread
   // (I = t >> 7, c = t & 127) sums rows 16 I .. 16 I + 15 of channel c, then
@@ -215,14 +223,19 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
   const int gI = tt >> 7, gc = tt & 127;
   float gv[16];
   bf16 av[16];
-  if (d.raw) {
-    const bf16* ap = reinterpret_cast<const bf16*>(in.gate);
+  {
+    // rows 16 gI + j, clamped to the last: min() on the offsets, as the
+    // stride is positive
+    const uint32_t o0 = eoff(16 * gI, gc), olast = eoff(n - 1, gc);
+    if (d.raw) {
+      const bf16* ap = reinterpret_cast<const bf16*>(in.gate) + row0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) av[j] = ap[rowidx(clampr(16 * gI + j)) * HD + gc];
-  } else {
-    const float* gp = reinterpret_cast<const float*>(in.gate);
+      for (int j = 0; j < 16; ++j) av[j] = ld_at(ap, 2u * min(o0 + j * rs, olast));
+    } else {
+      const float* gp = reinterpret_cast<const float*>(in.gate) + row0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) gv[j] = gp[rowidx(clampr(16 * gI + j)) * HD + gc];
+      for (int j = 0; j < 16; ++j) gv[j] = ld_at(gp, 4u * min(o0 + j * rs, olast));
+    }
   }
   // q, k, rq, rk at this thread's elements, for the epilogues from P2 on
   load_epi();
@@ -239,8 +252,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
       const int e = t + NTHR * rep, r = e >> 4, j8 = (e & 15) * 8;
-      pO[rep] = *reinterpret_cast<const bf16x8*>(dO + rowidx(clampr(r)) * HD + j8);
-      pV[rep] = *reinterpret_cast<const bf16x8*>(dv + rowidx(clampr(r)) * HD + j8);
+      const uint32_t o = 2u * eoff(clampr(r), j8);
+      pO[rep] = ld_at(reinterpret_cast<const bf16x8*>(dO + row0), o);
+      pV[rep] = ld_at(reinterpret_cast<const bf16x8*>(dv + row0), o);
     }
   }
 
@@ -884,8 +898,9 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     const bf16* araw = reinterpret_cast<const bf16*>(in.gate);
     float av[16];
     if (d.raw) {
+      const uint32_t o0 = eoff(16 * I, cc), olast = eoff(n - 1, cc);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) av[j] = bf2f(araw[rowidx(clampr(16 * I + j)) * HD + cc]);
+      for (int j = 0; j < 16; ++j) av[j] = bf2f(ld_at(araw + row0, 2u * min(o0 + j * rs, olast)));
     }
     __syncthreads();
     // dg_j = sum_{r >= j} dG_r + sum_{r < j} aP_r: a reverse cumsum and an
@@ -929,11 +944,11 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
     for (int j = 0; j < 16; ++j) {
       const int r = 16 * I + j;
       if (r < n) {
-        const int64_t idx = rowidx(r) * HD + cc;
+        const uint32_t o = eoff(r, cc);
         if (d.raw)
-          reinterpret_cast<bf16*>(out.dgate)[idx] = f2bf(v[j]);
+          (reinterpret_cast<bf16*>(out.dgate) + row0)[o] = f2bf(v[j]);
         else
-          reinterpret_cast<float*>(out.dgate)[idx] = v[j];
+          (reinterpret_cast<float*>(out.dgate) + row0)[o] = v[j];
       }
     }
     if (d.raw) {
@@ -971,18 +986,18 @@ __global__ __launch_bounds__(NTHR) void bwd_intra_kernel(Dims d, Inputs in, Chun
       if (r < n) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const int64_t idx = rowidx(r) * HD + 64 * chh + 16 * nt + dcol();
+          const uint32_t idx = eoff(r, 64 * chh + 16 * nt + dcol());
           float gq = adq[nt][i], gk = adk[nt][i];
           if (d.l2norm) {
             gq = sm.rq[r] * (gq - EQ(nt, i) * tq);
             gk = sm.rk[r] * (gk - EK(nt, i) * tk);
           }
-          dq[idx] = f2bf(gq);
-          dk[idx] = f2bf(gk);
+          dq[row0 + idx] = f2bf(gq);
+          dk[row0 + idx] = f2bf(gk);
         }
       }
     }
-    if (t < n) reinterpret_cast<bf16*>(out.dbeta)[rowidx(t)] = f2bf(sm.db[t]);
+    if (t < n) (reinterpret_cast<bf16*>(out.dbeta) + rowidx(0))[(uint32_t)t * (uint32_t)H] = f2bf(sm.db[t]);
   }
 }
 

@@ -659,18 +659,26 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   const int nnb = ld_const(ct.len, min(ci + 2 * gx, nch - 1));
 
   // ---- 4. T = (I + Diag(beta) A_kk)^-1 by 16x16 blocks, fp32
+  // (its strictly-upper 16 x 16 blocks are never written or read here: they
+  // leave as zeros)
   float (*Tm)[F_LD] = sm.Tm;
-  for (int e = t; e < CL * F_LD; e += NT_PREP) (&Tm[0][0])[e] = 0.f;
-  __syncthreads();
   if (w < 4 && l < 16) {
-    // wave w inverts diagonal block w; lane = column j
+    // wave w inverts diagonal block w by forward substitution, lane j taking
+    // column j. Lane j first reads row j of the block of Diag(beta) A_kk into
+    // registers; step r takes row r from lane r (readlane), so that no LDS
+    // read waits inside the dependent chain.
     const int I = w, j = l;
+    float brow[16];
+    const float bj = sm.beta[16 * I + j];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) brow[i] = bj * sm.Akk[16 * I + j][16 * I + i];
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float s2 = (r == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s2 -= sm.beta[16 * I + r] * sm.Akk[16 * I + r][16 * I + i] * x[i];
+      for (int i = 0; i < r; ++i)
+        s2 -= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(brow[i]), r)) * x[i];
       x[r] = s2;
     }
 #pragma unroll
@@ -714,9 +722,10 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   {
     const int r = t >> 3, i8 = 8 * (t & 7);
     float tv[8], kv[8], qv[8];
+    const bool upper = (i8 >> 4) > (r >> 4);    // a strictly-upper block of T
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      tv[j] = Tm[r][i8 + j];
+      tv[j] = upper ? 0.f : Tm[r][i8 + j];
       kv[j] = sm.Akk[r][i8 + j];
       qv[j] = sm.Aqk[r][i8 + j];
     }
