@@ -70,7 +70,7 @@ static_assert(!(KDA_SPLIT_B2 & SPLIT_A), "dKd reads dR as the bf16 dv");
 #define KDA_SPLIT_B8 SPLIT_AB    // WY / UT backward: dT T^T, T^T tmp
 #endif
 
-struct BwdIntraSmem {
+struct __attribute__((aligned(16))) BwdIntraSmem {
   union {
     // P2 .. P4 panels hold their operands transposed, K = j along the rows
     // (8-byte stores of the D tiles, transpose loads of the fragments)

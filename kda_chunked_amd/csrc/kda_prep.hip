@@ -160,7 +160,7 @@ constexpr int GP_LD = HD + 4;     // fp32 rows of G (16-byte aligned rows)
 constexpr int XS_LD = HD + 8;     // bf16 rows of the raw q, k
 constexpr int F_LD = CL + 1;      // fp32 64 x 64 matrices
 
-struct PrepSmem {
+struct __attribute__((aligned(16))) PrepSmem {
   float G[CL][GP_LD];
   bf16 qs[CL][XS_LD], ks[CL][XS_LD];   // raw q, k (rows >= n repeat row n - 1)
   float Akk[CL][F_LD], Aqk[CL][F_LD];
@@ -416,14 +416,8 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
       *reinterpret_cast<bf16x8*>(&sm.u.Y[1][yswz(rA, c)]) = yl;
     }
   }
-  // zero the strictly-upper 16 x 16 tiles of A_kk and A_qk
-  for (int e = t; e < 6 * 256; e += NT_PREP) {
-    const int tile = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-    const int I = tile < 3 ? 0 : tile < 5 ? 1 : 2;
-    const int J = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
-    sm.Akk[16 * I + rr][16 * J + cc] = 0.f;
-    sm.Aqk[16 * I + rr][16 * J + cc] = 0.f;
-  }
+  // (the strictly-upper 16 x 16 tiles of A_kk and A_qk are never written or
+  // read: they leave as zeros)
   __syncthreads();
 
   // ---- 3. decayed products of A_kk and A_qk, as work items spread over the
@@ -431,11 +425,12 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   // product of bf16 hi/lo operands; each wide diagonal tile is two
   // running-product units (unit u: columns p and 15 - p, p = 4u .. 4u + 3).
   if (calm) {
-    // One reference for the whole chunk: wave w takes row block I = w & 3 and
-    // channels 64 kh .. 64 kh + 63 (kh = w >> 2) of every tile (I, J <= I);
-    // its x operands x^ e^(G - rho) are built once, the k operands come from
-    // the Y panel. The two channel halves meet in LDS in a fixed order.
-    const int I = w & 3, kh = w >> 2, ra = 16 * I + (l & 15);
+    // One reference for the whole chunk: each wave takes one row block I and
+    // channels 64 kh .. 64 kh + 63 of every tile (I, J <= I); its x operands
+    // x^ e^(G - rho) are built once, the k operands come from the Y panel.
+    // The two channel halves meet in LDS in a fixed order. Waves w and w + 4
+    // share a SIMD: they take row blocks I and 3 - I, 5 tiles per SIMD.
+    const int I = w < 4 ? (w & 1) : 3 - (w & 1), kh = (w >> 1) & 1, ra = 16 * I + (l & 15);
     const float rqa = sm.rq[ra], rka = sm.rk[ra];
     f32x4 akk[4], aqk[4];
 #pragma unroll
@@ -722,12 +717,12 @@ __global__ __launch_bounds__(NT_PREP) void fwd_prep_kernel(Dims d, Inputs in, Ch
   {
     const int r = t >> 3, i8 = 8 * (t & 7);
     float tv[8], kv[8], qv[8];
-    const bool upper = (i8 >> 4) > (r >> 4);    // a strictly-upper block of T
+    const bool upper = (i8 >> 4) > (r >> 4);    // a strictly-upper 16 x 16 block
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       tv[j] = upper ? 0.f : Tm[r][i8 + j];
-      kv[j] = sm.Akk[r][i8 + j];
-      qv[j] = sm.Aqk[r][i8 + j];
+      kv[j] = upper ? 0.f : sm.Akk[r][i8 + j];
+      qv[j] = upper ? 0.f : sm.Aqk[r][i8 + j];
     }
     *reinterpret_cast<f32x4*>(Tg + r * CL + i8) = f32x4{tv[0], tv[1], tv[2], tv[3]};
     *reinterpret_cast<f32x4*>(Tg + r * CL + i8 + 4) = f32x4{tv[4], tv[5], tv[6], tv[7]};

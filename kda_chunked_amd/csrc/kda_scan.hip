@@ -432,7 +432,7 @@ hipError_t launch_fwd_scan(const Dims& d, const Inputs& in, const ChunkTable& ct
 // and the output panels (scale folded in). 8 waves: rows 16 (w & 3), columns
 // 64 (w >> 2) .. + 63. A operands are read from memory as MFMA fragments; the
 // B operands S_in^T and U~^T are split into LDS panels.
-struct FwdOutSmem {
+struct __attribute__((aligned(16))) FwdOutSmem {
   bf16 s_hi[HD][K1_LD], s_lo[HD][K1_LD];     // S_in^T [j][c]
   bf16 u_hi[HD][K2_LD], u_lo[HD][K2_LD];     // U~^T   [j][i]
   bf16 ot[CL][K1_LD];                        // O [r][c] of the chunk, to rows of 16-byte stores
@@ -589,7 +589,7 @@ hipError_t launch_fwd_out(const Dims& d, const ChunkTable& ct, const SavedSet& s
 // prefetched into registers one chunk ahead; scale Qd shares its LDS space
 // with Ke^T and is staged once Ke^T has been consumed.
 constexpr int QD_LD = HD + 16;       // 144: rows of 288 bytes
-struct BwdScanSmem {
+struct __attribute__((aligned(16))) BwdScanSmem {
   union {
     struct { bf16 hi[HD][K2_LD], lo[HD][K2_LD]; } ke;      // Ke^T         [c][r]
     struct { bf16 hi[CL][QD_LD], lo[CL][QD_LD]; } qd;      // scale*Qd     [r][c]
