@@ -51,7 +51,7 @@ KDA_DEV int seg_of(const int32_t* c0, int S, int ci) {
   int lo = 0, hi = S - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (c0[mid] <= ci) lo = mid;
+    if (ld_const(c0, mid) <= ci) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -59,7 +59,7 @@ KDA_DEV int seg_of(const int32_t* c0, int S, int ci) {
 
 // Segment bounds, clamped into the packed tensors.
 KDA_DEV void seg_bounds(const int32_t* cu, int s, int64_t T, int64_t& a, int64_t& n) {
-  int64_t x = cu[s], y = cu[s + 1];
+  int64_t x = ld_const(cu, s), y = ld_const(cu, s + 1);
   x = x < 0 ? 0 : (x > T ? T : x);
   y = y < x ? x : (y > T ? T : y);
   a = x;
@@ -100,13 +100,20 @@ KDA_DEV void dma_rows(bf16 (*blk)[A_LD], const bf16* src, int64_t row0, int n, i
   static_assert(BR * CPR % 64 == 0, "whole wave instructions");
   const int w = wave_id(), l = lane_id();
   bf16* base = &blk[0][0];
+  // row addresses: the first row read (common to the workgroup) plus a 32-bit
+  // byte offset per lane. With n <= 0 every row is row0 + n - 1 (the row
+  // before the block), which then is that first row.
+  const int64_t rfirst = n > 0 ? row0 : row0 + n - 1;
+  const int nn = n > 0 ? n : 1;
+  const char* src0 = reinterpret_cast<const char*>(src + (rfirst * H + h) * AD);
+  const uint32_t rs = 2u * (uint32_t)H * AD;
 #pragma unroll
   for (int j = 0; j < (INS + NW - 1) / NW; ++j) {
     const int ins = w + NW * j;
     if (ins < INS) {
       const int qc = 64 * ins + l, r = qc / CPR, c = qc - r * CPR;
-      const int cc = c < AD / 8 ? c : AD / 8 - 1, rr = r < n ? r : n - 1;
-      __builtin_amdgcn_global_load_lds((gptr)(src + ((row0 + rr) * H + h) * AD + 8 * cc),
+      const int cc = c < AD / 8 ? c : AD / 8 - 1, rr = r < nn ? r : nn - 1;
+      __builtin_amdgcn_global_load_lds((gptr)(src0 + ((uint32_t)rr * rs + 16u * (uint32_t)cc)),
                                        (lptr)(base + 512 * ins), 16, 0, 0);
     }
   }
@@ -118,11 +125,16 @@ KDA_DEV void dma_rows(bf16 (*blk)[A_LD], const bf16* src, int64_t row0, int n, i
 // is computed. Rows from n on repeat row n - 1.
 template <int NW>
 KDA_DEV void pre_load(bf16x8 (&x)[32 / NW], const bf16* src, int64_t row0, int n, int H, int h) {
+  // (as in dma_rows: the first row read is the base; n <= 0 reads row0 + n - 1)
+  const int64_t rfirst = n > 0 ? row0 : row0 + n - 1;
+  const int nn = n > 0 ? n : 1;
+  const bf16x8* src0 = reinterpret_cast<const bf16x8*>(src + (rfirst * H + h) * AD);
+  const uint32_t rs = 2u * (uint32_t)H * AD;
 #pragma unroll
   for (int i = 0; i < 32 / NW; ++i) {
     const int u = threadIdx.x + 64 * NW * i, r = u >> 5, c = u & 31;
-    const int rr = r < n ? r : n - 1;
-    x[i] = *reinterpret_cast<const bf16x8*>(src + ((row0 + rr) * H + h) * AD + 8 * c);
+    const int rr = r < nn ? r : nn - 1;
+    x[i] = ld_at(src0, (uint32_t)rr * rs + 16u * (uint32_t)c);
   }
 }
 
@@ -152,10 +164,11 @@ KDA_DEV void write_rows_bf16(bf16 (*stage)[A_LD], int wr, const f32x4 (&acc)[16]
     for (int i = 0; i < 4; ++i) stage[16 * wr + drow(i)][16 * dt + dcol()] = f2bf(acc[dt][i] * mul);
   __builtin_amdgcn_s_waitcnt(0xc07f);     // this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
+  bf16* dst0 = dst + (row0 * H + h) * AD;
   for (int u = l; u < 16 * AD / 8; u += 64) {
     const int r = u >> 5, c8 = (u & 31) * 8, row = 16 * wr + r;
     if (row < nvalid)
-      *reinterpret_cast<bf16x8*>(dst + ((row0 + row) * H + h) * AD + c8) =
+      *reinterpret_cast<bf16x8*>(dst0 + ((uint32_t)row * (uint32_t)H * AD + c8)) =
           *reinterpret_cast<const bf16x8*>(&stage[row][c8]);
   }
 }
@@ -199,16 +212,16 @@ attn_fwd_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
   __shared__ FwdSmem<HPW> sm;
   int ci, h0;
   qblock_heads<HPW>(a, blockIdx.x, ci, h0);
-  if (ci >= qt.doc_c0[a.S]) return;
+  if (ci >= ld_const(qt.doc_c0, a.S)) return;
   const int s = seg_of(qt.doc_c0, a.S, ci);
   // a segment's query blocks in reverse: the late ones see the most keys and
   // start first
-  ci = qt.doc_c0[s] + qt.doc_c0[s + 1] - 1 - ci;
+  ci = ld_const(qt.doc_c0, s) + ld_const(qt.doc_c0, s + 1) - 1 - ci;
   int64_t qs, Lq, ks, Lk;
   seg_bounds(cuq, s, a.Tq, qs, Lq);
   seg_bounds(cuk, s, a.Tk, ks, Lk);
-  const int64_t t0 = qt.tok[ci];
-  const int nq = qt.len[ci];
+  const int64_t t0 = ld_const(qt.tok, ci);
+  const int nq = ld_const(qt.len, ci);
   const int64_t i0 = t0 - qs, off = Lk - Lq;
   const int w = wave_id(), wr = w & 3, l = lane_id();
   const int h = h0 + (w >> 2), g = h / a.grp;
@@ -365,16 +378,16 @@ attn_dq_kernel(Dims a, ChunkTable qt, const int32_t* __restrict__ cuq,
   __shared__ DqSmem<HPW> sm;
   int ci, h0;
   qblock_heads<HPW>(a, blockIdx.x, ci, h0);
-  if (ci >= qt.doc_c0[a.S]) return;
+  if (ci >= ld_const(qt.doc_c0, a.S)) return;
   const int s = seg_of(qt.doc_c0, a.S, ci);
   // a segment's query blocks in reverse: the late ones see the most keys and
   // start first
-  ci = qt.doc_c0[s] + qt.doc_c0[s + 1] - 1 - ci;
+  ci = ld_const(qt.doc_c0, s) + ld_const(qt.doc_c0, s + 1) - 1 - ci;
   int64_t qs, Lq, ks, Lk;
   seg_bounds(cuq, s, a.Tq, qs, Lq);
   seg_bounds(cuk, s, a.Tk, ks, Lk);
-  const int64_t t0 = qt.tok[ci];
-  const int nq = qt.len[ci];
+  const int64_t t0 = ld_const(qt.tok, ci);
+  const int nq = ld_const(qt.len, ci);
   const int64_t i0 = t0 - qs, off = Lk - Lq;
   const int w = wave_id(), wr = w & 3, l = lane_id();
   const int h = h0 + (w >> 2), g = h / a.grp;
@@ -480,19 +493,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // so that each XCD sees the key heads congruent to it and the heavy early
   // blocks of a segment start together
   const int cj = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
-  if (cj >= kt.doc_c0[a.S]) return;
+  if (cj >= ld_const(kt.doc_c0, a.S)) return;
   const int s = seg_of(kt.doc_c0, a.S, cj);
   int64_t qs, Lq, ks, Lk;
   seg_bounds(cuq, s, a.Tq, qs, Lq);
   seg_bounds(cuk, s, a.Tk, ks, Lk);
-  const int64_t u0 = kt.tok[cj];
-  const int nk = kt.len[cj];
+  const int64_t u0 = ld_const(kt.tok, cj);
+  const int nk = ld_const(kt.len, cj);
   const int64_t j0 = u0 - ks, off = Lk - Lq;
   const int w = wave_id(), l = lane_id();
   const int jw = 16 * w;                // the wave's first key in the block
   const float c2 = a.scale * LOG2E_F;
   // query blocks of the segment that see some of these keys: i + off >= j0
-  const int qc0 = qt.doc_c0[s], qc1 = qt.doc_c0[s + 1];
+  const int qc0 = ld_const(qt.doc_c0, s), qc1 = ld_const(qt.doc_c0, s + 1);
   int64_t ifirst = j0 - off;
   ifirst = ifirst < 0 ? 0 : ifirst;
   const int64_t qf64 = qc0 + ifirst / BR;
@@ -520,23 +533,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float plb[4], pdl[4];
   auto fetch = [&](int it) {
     const int h = g * a.grp + it / nqb, qc = qfirst + it % nqb;
-    const int64_t t0 = qt.tok[qc];
-    const int nq = qt.len[qc];
+    const int64_t t0 = ld_const(qt.tok, qc);
+    const int nq = ld_const(qt.len, qc);
     pre_load<8>(pq, q, t0, nq, a.Hq, h);
     pre_load<8>(pd, dO, t0, nq, a.Hq, h);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int qcol = 16 * nt + dcol(), qq = qcol < nq ? qcol : nq - 1;
-      plb[nt] = lse[(t0 + qq) * a.Hq + h];
-      pdl[nt] = WANT_DK ? delta[(t0 + qq) * a.Hq + h] : 0.f;
+      const uint32_t o = 4u * (uint32_t)qq * (uint32_t)a.Hq;
+      plb[nt] = ld_at(lse + t0 * a.Hq + h, o);
+      pdl[nt] = WANT_DK ? ld_at(delta + t0 * a.Hq + h, o) : 0.f;
     }
   };
   if (items > 0) fetch(0);
   __builtin_amdgcn_s_waitcnt(0);      // the V rows (and the first item) have landed
   for (int it = 0; it < items; ++it) {
     const int qc = qfirst + it % nqb;
-    const int64_t t0 = qt.tok[qc];
-    const int nq = qt.len[qc];
+    const int64_t t0 = ld_const(qt.tok, qc);
+    const int nq = ld_const(qt.len, qc);
     const int64_t i0 = t0 - qs;
     float lbq[4], dlq[4];             // lse log2 e and Delta of this lane's query columns
 #pragma unroll
