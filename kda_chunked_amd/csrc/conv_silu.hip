@@ -8,10 +8,10 @@
 //   dw[c, j] = sum_t dz[t] xx(t - 3 + j),  db[c] = sum_t dz[t]
 //
 // The op streams a [T, D] bf16 tensor once each way, so it is bound by HBM:
-// lanes own 8 consecutive channels (one 16-byte vector) and a run of tokens,
-// keep the 3-token window in registers, and a wave moves 1 KiB per token row.
-// A workgroup is 4 waves on the same 512 channels and 4 consecutive 64-token
-// runs; the backward adds its 4 runs' dw and db partials in LDS in a fixed
+// lanes own VEC consecutive channels (8 forward, 4 backward: one 16- or
+// 8-byte vector) and a run of tokens, keep the 3-token window in registers,
+// and a wave moves 64 VEC channels of each token row. A workgroup is 4 waves
+// on the same 64 VEC channels and 4 consecutive 64-token runs; the backward adds its 4 runs' dw and db partials in LDS in a fixed
 // order and a second kernel adds the workgroup rows in order, so the sums are
 // the same bits every run.
 #include "kda_conv.h"
@@ -22,24 +22,30 @@ namespace kda {
 namespace conv {
 
 constexpr int W = 4;          // conv width
-constexpr int VEC = 8;        // channels per lane
+constexpr int VEC_FWD = 8;    // channels per lane, forward
+constexpr int VEC_BWD = 4;    // channels per lane, backward (half the registers of 8:
+                              // four waves per SIMD keep twice the loads in flight)
 constexpr int CG = 64;        // lanes per wave: channel groups of a workgroup
 constexpr int SUB = 4;        // waves per workgroup: token runs
 constexpr int RUN = 64;       // tokens per run
 constexpr int ROWS = SUB * RUN;
 constexpr int NP = W + 1;     // partial sums per channel: dw[0..3], db
 
-KDA_DEV void load8(const bf16* p, float* v) {
-  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+template <int V>
+KDA_DEV void loadv(const bf16* p, float* v) {
+  typedef __bf16 vec __attribute__((ext_vector_type(V)));
+  const vec a = *reinterpret_cast<const vec*>(p);
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) v[i] = bf2f(a[i]);
+  for (int i = 0; i < V; ++i) v[i] = bf2f(a[i]);
 }
 
-KDA_DEV void store8(bf16* p, const float* v) {
-  bf16x8 a;
+template <int V>
+KDA_DEV void storev(bf16* p, const float* v) {
+  typedef __bf16 vec __attribute__((ext_vector_type(V)));
+  vec a;
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) a[i] = f2bf(v[i]);
-  *reinterpret_cast<bf16x8*>(p) = a;
+  for (int i = 0; i < V; ++i) a[i] = f2bf(v[i]);
+  *reinterpret_cast<vec*>(p) = a;
 }
 
 KDA_DEV float sigm(float z) {
@@ -60,13 +66,15 @@ KDA_DEV int doc_of(const int32_t* cu, int N, int64_t t) {
 
 // The lane's view of its run: taps, bias, document bounds and the window
 // xx(t0 - 3), xx(t0 - 2), xx(t0 - 1).
+template <int VEC>
 struct Lane {
   float wk[W][VEC], bb[VEC];
   int d;
   int64_t s, e;
 };
 
-KDA_DEV void setup(Lane& L, float (&xm)[3][VEC], int64_t T, int D, int N, const bf16* x,
+template <int VEC>
+KDA_DEV void setup(Lane<VEC>& L, float (&xm)[3][VEC], int64_t T, int D, int N, const bf16* x,
                    const float* w, const float* b, const bf16* halo, const int32_t* cu, int c0,
                    int64_t t0) {
 #pragma unroll
@@ -86,9 +94,9 @@ KDA_DEV void setup(Lane& L, float (&xm)[3][VEC], int64_t T, int D, int N, const 
     const int64_t u = t0 - k;
     float* v = xm[3 - k];
     if (u >= L.s) {
-      load8(x + u * D + c0, v);
+      loadv<VEC>(x + u * D + c0, v);
     } else if (L.d == 0 && halo) {
-      load8(halo + (3 + (u - L.s)) * D + c0, v);
+      loadv<VEC>(halo + (3 + (u - L.s)) * D + c0, v);
     } else {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) v[i] = 0.f;
@@ -97,13 +105,15 @@ KDA_DEV void setup(Lane& L, float (&xm)[3][VEC], int64_t T, int D, int N, const 
 }
 
 // Moves to the document that contains t (t reached the current one's end).
-KDA_DEV void next_doc(Lane& L, int64_t T, int N, const int32_t* cu, int64_t t) {
+template <int VEC>
+KDA_DEV void next_doc(Lane<VEC>& L, int64_t T, int N, const int32_t* cu, int64_t t) {
   while (L.d + 1 < N && cu[L.d + 1] <= t) ++L.d;
   L.s = t;
   const int64_t e = cu[L.d + 1];
   L.e = e <= t ? t + 1 : (e > T ? T : e);
 }
 
+template <int VEC>
 __global__ __launch_bounds__(CG * SUB) void conv_fwd_kernel(int64_t T, int D, int N,
                                                             const bf16* __restrict__ x,
                                                             const float* __restrict__ w,
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(CG * SUB) void conv_fwd_kernel(int64_t T, int D, in
   const int64_t t0 = (int64_t)blockIdx.y * ROWS + sub * RUN;
   if (c0 >= D || t0 >= T) return;
   const int64_t t1 = t0 + RUN < T ? t0 + RUN : T;
-  Lane L;
+  Lane<VEC> L;
   float xm[3][VEC];
   setup(L, xm, T, D, N, x, w, b, halo, cu, c0, t0);
   for (int64_t t = t0; t < t1; ++t) {
@@ -128,7 +138,7 @@ __global__ __launch_bounds__(CG * SUB) void conv_fwd_kernel(int64_t T, int D, in
         for (int i = 0; i < VEC; ++i) xm[k][i] = 0.f;
     }
     float xt[VEC], yv[VEC];
-    load8(x + t * D + c0, xt);
+    loadv<VEC>(x + t * D + c0, xt);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
       const float z = L.bb[i] + L.wk[0][i] * xm[0][i] + L.wk[1][i] * xm[1][i] +
@@ -138,13 +148,14 @@ __global__ __launch_bounds__(CG * SUB) void conv_fwd_kernel(int64_t T, int D, in
       xm[1][i] = xm[2][i];
       xm[2][i] = xt[i];
     }
-    store8(y + t * D + c0, yv);
+    storev<VEC>(y + t * D + c0, yv);
   }
 }
 
 // Backward of one run: dz for the run's tokens and up to 3 tokens past it
 // (they reach back into the run through dx); dx of the run's tokens; the
 // run's dw and db partials; dhalo from the run that starts at token 0.
+template <int VEC>
 __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
     int64_t T, int D, int N, const bf16* __restrict__ x, const float* __restrict__ w,
     const float* __restrict__ b, const bf16* __restrict__ halo, const int32_t* __restrict__ cu,
@@ -165,7 +176,7 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
   if (on) {
     const int64_t t1 = t0 + RUN < T ? t0 + RUN : T;
     const int64_t tend = t1 + 3 < T ? t1 + 3 : T;
-    Lane L;
+    Lane<VEC> L;
     float xm[3][VEC];
     setup(L, xm, T, D, N, x, w, b, halo, cu, c0, t0);
     const bool with_halo = halo && dhalo && t0 == 0;
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
     }
     // dx of token u, complete: stored when it belongs to this run and document
     auto put = [&](int64_t u, const float* v) {
-      if (u >= t0 && u < t1 && u >= L.s) store8(dx + u * D + c0, v);
+      if (u >= t0 && u < t1 && u >= L.s) storev<VEC>(dx + u * D + c0, v);
     };
     for (int64_t t = t0; t < tend; ++t) {
       if (t >= L.e) {
@@ -198,8 +209,8 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
         }
       }
       float xt[VEC], gy[VEC], dz[VEC];
-      load8(x + t * D + c0, xt);
-      load8(dy + t * D + c0, gy);
+      loadv<VEC>(x + t * D + c0, xt);
+      loadv<VEC>(dy + t * D + c0, gy);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         const float z = L.bb[i] + L.wk[0][i] * xm[0][i] + L.wk[1][i] * xm[1][i] +
@@ -255,7 +266,7 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
     }
     if (with_halo) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) store8(dhalo + (int64_t)k * D + c0, dh[k]);
+      for (int k = 0; k < 3; ++k) storev<VEC>(dhalo + (int64_t)k * D + c0, dh[k]);
     }
   }
   // the workgroup's 4 runs added in a fixed order
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
     red[sub][W][lane * VEC + i] = pb[i];
   }
   __syncthreads();
-  // NP * CG * VEC = 2560 sums over the 4 runs, spread over the 256 threads
+  // NP * CG * VEC sums over the 4 runs, spread over the 256 threads
   const int cbase = blockIdx.x * CG * VEC;
   for (int e = threadIdx.x; e < NP * CG * VEC; e += CG * SUB) {
     const int k = e / (CG * VEC), cc = e % (CG * VEC);
@@ -340,8 +351,8 @@ size_t bwd_ws(const kda_conv_problem* p) {
   return (size_t)kda::conv::part_rows(p->T) * kda::conv::NP * p->D * sizeof(float);
 }
 
-dim3 grid_of(const kda_conv_problem* p) {
-  return dim3((p->D / kda::conv::VEC + kda::conv::CG - 1) / kda::conv::CG,
+dim3 grid_of(const kda_conv_problem* p, int vec) {
+  return dim3((p->D / vec + kda::conv::CG - 1) / kda::conv::CG,
               (unsigned)kda::conv::part_rows(p->T));
 }
 
@@ -369,7 +380,8 @@ kda_status kda_conv_silu_fwd(const kda_conv_problem* p, const void* x, const flo
   if (p->has_bias) REQ(b, "b");
   if (p->has_halo) REQ(halo, "halo");
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(kda::conv::conv_fwd_kernel, grid_of(p), dim3(kda::conv::CG * kda::conv::SUB),
+  hipLaunchKernelGGL(kda::conv::conv_fwd_kernel<kda::conv::VEC_FWD>,
+                     grid_of(p, kda::conv::VEC_FWD), dim3(kda::conv::CG * kda::conv::SUB),
                      0, hs, p->T, p->D, p->num_seqs, static_cast<const kda::bf16*>(x), w,
                      p->has_bias ? b : nullptr,
                      p->has_halo ? static_cast<const kda::bf16*>(halo) : nullptr, cu_seqlens,
@@ -409,7 +421,8 @@ kda_status kda_conv_silu_bwd(const kda_conv_problem* p, const void* x, const flo
       return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
                   workspace_bytes, need);
     float* part = static_cast<float*>(workspace);
-    hipLaunchKernelGGL(kda::conv::conv_bwd_kernel, grid_of(p),
+    hipLaunchKernelGGL(kda::conv::conv_bwd_kernel<kda::conv::VEC_BWD>,
+                       grid_of(p, kda::conv::VEC_BWD),
                        dim3(kda::conv::CG * kda::conv::SUB), 0, hs, p->T, p->D, p->num_seqs,
                        static_cast<const kda::bf16*>(x), w, p->has_bias ? b : nullptr,
                        p->has_halo ? static_cast<const kda::bf16*>(halo) : nullptr, cu_seqlens,
