@@ -185,6 +185,9 @@ class ConvWorkload:
 CONV_WORKLOADS = [
     ConvWorkload("conv_tiny", (200, 56), 256, True, True, seed=10),
     ConvWorkload("conv_ragged", (2, 0, 1, 70, 3, 0, 64, 130), 512, True, True, seed=11),
+    # a channel count that is no multiple of a workgroup's channels (256 or 512):
+    # workgroups with idle lanes
+    ConvWorkload("conv_narrow", (1, 66, 0, 190), 136, True, True, seed=13),
     # the 4doc layout with the q, k, v channels of 64 heads x 128, as a context
     # fragment that continues its first document (halo on), no bias
     ConvWorkload("conv_4doc", (8192, 4096, 3072, 1024), 3 * 64 * 128, False, True, seed=12),

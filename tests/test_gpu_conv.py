@@ -68,7 +68,7 @@ def _compare(tag, y, g, yref, gref, cols=None):
     assert not bad, f"{tag}: over tolerance {bad}"
 
 
-@pytest.mark.parametrize("name", ["conv_tiny", "conv_ragged"])
+@pytest.mark.parametrize("name", ["conv_tiny", "conv_ragged", "conv_narrow"])
 def test_conv_parity_full(name):
     w = I.CONV_BY_NAME[name]
     print(f"[case] {name} T={w.T} D={w.D} docs={w.doc_lens}", flush=True)
