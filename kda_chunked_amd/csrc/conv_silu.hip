@@ -162,6 +162,9 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
     const bf16* __restrict__ dy, bf16* __restrict__ dx, bf16* __restrict__ dhalo,
     float* __restrict__ part) {
   __shared__ float red[SUB][NP][CG * VEC];
+  // dhalo sums of the run that starts at token 0, in LDS rather than in 12
+  // registers that every other run would hold too (each lane owns its slots)
+  __shared__ float dhs[3][CG * VEC];
   const int lane = threadIdx.x & (CG - 1), sub = threadIdx.x / CG;
   const int c0 = (blockIdx.x * CG + lane) * VEC;
   const int64_t t0 = (int64_t)blockIdx.y * ROWS + sub * RUN;
@@ -180,13 +183,16 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
     float xm[3][VEC];
     setup(L, xm, T, D, N, x, w, b, halo, cu, c0, t0);
     const bool with_halo = halo && dhalo && t0 == 0;
-    float dh[3][VEC];
+    if (with_halo) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) dhs[k][lane * VEC + i] = 0.f;
+    }
     // acc[k]: dx of token t - 3 + k while token t is processed
     float acc[4][VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-#pragma unroll
-      for (int k = 0; k < 3; ++k) dh[k][i] = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc[k][i] = 0.f;
     }
@@ -194,7 +200,18 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
     auto put = [&](int64_t u, const float* v) {
       if (u >= t0 && u < t1 && u >= L.s) storev<VEC>(dx + u * D + c0, v);
     };
+    // x and dy rows requested two tokens ahead (rows past tend repeat the
+    // last one): the row a token uses was requested two iterations earlier
+    typedef __bf16 vec __attribute__((ext_vector_type(VEC)));
+    auto row_x = [&](int64_t u) {
+      return *reinterpret_cast<const vec*>(x + (u < tend ? u : tend - 1) * D + c0);
+    };
+    auto row_dy = [&](int64_t u) {
+      return *reinterpret_cast<const vec*>(dy + (u < tend ? u : tend - 1) * D + c0);
+    };
+    vec cx = row_x(t0), cg = row_dy(t0), nx = row_x(t0 + 1), ng = row_dy(t0 + 1);
     for (int64_t t = t0; t < tend; ++t) {
+      const vec fx = row_x(t + 2), fg = row_dy(t + 2);
       if (t >= L.e) {
         // the document ended: tokens t-3 .. t-1 receive nothing more
 #pragma unroll
@@ -209,8 +226,9 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
         }
       }
       float xt[VEC], gy[VEC], dz[VEC];
-      loadv<VEC>(x + t * D + c0, xt);
-      loadv<VEC>(dy + t * D + c0, gy);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) xt[i] = bf2f(cx[i]), gy[i] = bf2f(cg[i]);
+      cx = nx, cg = ng, nx = fx, ng = fg;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         const float z = L.bb[i] + L.wk[0][i] * xm[0][i] + L.wk[1][i] * xm[1][i] +
@@ -239,12 +257,7 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
         } else if (with_halo && L.d == 0) {
           const int r = (int)(3 + (u - L.s));
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            const float v = L.wk[j][i] * dz[i];
-            if (r == 0) dh[0][i] += v;
-            else if (r == 1) dh[1][i] += v;
-            else dh[2][i] += v;
-          }
+          for (int i = 0; i < VEC; ++i) dhs[r][lane * VEC + i] += L.wk[j][i] * dz[i];
         }
       }
       put(t - 3, acc[0]);
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(CG * SUB) void conv_bwd_kernel(
     }
     if (with_halo) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) storev<VEC>(dhalo + (int64_t)k * D + c0, dh[k]);
+      for (int k = 0; k < 3; ++k) storev<VEC>(dhalo + (int64_t)k * D + c0, &dhs[k][lane * VEC]);
     }
   }
   // the workgroup's 4 runs added in a fixed order
