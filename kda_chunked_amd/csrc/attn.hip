@@ -157,6 +157,9 @@ KDA_DEV void dma_join() {
 // tensor through rows 16 wr .. + 15 of an LDS block.
 KDA_DEV void write_rows_bf16(bf16 (*stage)[A_LD], int wr, const f32x4 (&acc)[16], float mul,
                              bf16* dst, int64_t row0, int nvalid, int H, int h) {
+  // (no valid row: row0 may lie past the tensor, and nothing is written; the
+  // staging below is this wave's own)
+  if (nvalid <= 0) return;
   const int l = lane_id();
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt)
